@@ -1,0 +1,214 @@
+"""Python face of the CPU oracle (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this module.  It loads ``liboracle.so`` (plain C, see
+``sage_oracle.c``) through ctypes and adds the fp64 exact-attention reference
+used for the accuracy check.  It imports nothing from the GPU package.
+
+Arrays are numpy.  Inputs Q, K, V are passed as the raw 16-bit patterns of
+float16 / bfloat16 tensors of shape [B, H, N, d] (``uint16``), with
+``dtype`` 0 for float16 and 1 for bfloat16.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+F16, BF16 = 0, 1
+#: width of the KV tile over which the online softmax updates its running max
+#: and the inner FP8 P~V block is accumulated (the kernel's tile width).
+KV_TILE = 64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode.argtypes = [f32]
+        L.oracle_e4m3_encode_n.argtypes = [P, P, i64]
+        L.oracle_e4m3_decode_n.argtypes = [P, P, i64]
+        L.oracle_x2.restype = f32
+        L.oracle_x2.argtypes = [f32]
+        L.oracle_x2_n.argtypes = [P, P, i64]
+        L.oracle_x2_c1.restype = f32
+        L.oracle_x2_c2.restype = f32
+        L.oracle_kmean.restype = i32
+        L.oracle_kmean.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.oracle_quantize_qk.restype = i32
+        L.oracle_quantize_qk.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_quantize_v.restype = i32
+        L.oracle_quantize_v.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.oracle_qk_int32.restype = None
+        L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, P, i32, P]
+        L.oracle_attn_rows.restype = i32
+        L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, P, i32, P, P]
+        L.oracle_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------- primitives
+def e4m3_encode(x):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e4m3_encode_n(_p(x), _p(out), x.size)
+    return out
+
+
+def e4m3_decode(c):
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_decode_n(_p(c), _p(out), c.size)
+    return out
+
+
+def x2(t):
+    t = _c(t, np.float32)
+    out = np.empty(t.shape, np.float32)
+    lib().oracle_x2_n(_p(t), _p(out), t.size)
+    return out
+
+
+def x2_coefficients():
+    return float(lib().oracle_x2_c1()), float(lib().oracle_x2_c2())
+
+
+def num_threads():
+    return int(lib().oracle_num_threads())
+
+
+# ---------------------------------------------------------------- the method
+def kmean(K_bits, dtype):
+    K_bits = _c(K_bits, np.uint16)
+    B, H, N, d = K_bits.shape
+    mu = np.empty((B, H, d), np.float32)
+    sums = np.empty((B, H, d), np.int64)
+    rc = lib().oracle_kmean(_p(K_bits), dtype, B * H, N, d, _p(mu), _p(sums))
+    assert rc == 0
+    return mu, sums
+
+
+def quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k):
+    Q_bits = _c(Q_bits, np.uint16)
+    K_bits = _c(K_bits, np.uint16)
+    B, H, N, d = Q_bits.shape
+    assert K_bits.shape == Q_bits.shape
+    qc = np.empty((B, H, N, d), np.int8)
+    kc = np.empty((B, H, N, d), np.int8)
+    qs = np.empty((B, H, N // blk_q), np.float32)
+    ks = np.empty((B, H, N // blk_k), np.float32)
+    mu = np.empty((B, H, d), np.float32)
+    rc = lib().oracle_quantize_qk(_p(Q_bits), _p(K_bits), dtype, B * H, N, d, blk_q, blk_k,
+                                  _p(qc), _p(qs), _p(kc), _p(ks), _p(mu))
+    if rc != 0:
+        raise ValueError("oracle_quantize_qk: unsupported shape")
+    return dict(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks, k_mean=mu)
+
+
+def quantize_v(V_bits, dtype):
+    """Returns (v_codes [B,H,N,d] e4m3 in natural token-major layout, v_scale [B,H,d])."""
+    V_bits = _c(V_bits, np.uint16)
+    B, H, N, d = V_bits.shape
+    vc = np.empty((B, H, N, d), np.uint8)
+    vs = np.empty((B, H, d), np.float32)
+    rc = lib().oracle_quantize_v(_p(V_bits), dtype, B * H, N, d, _p(vc), _p(vs))
+    assert rc == 0
+    return vc, vs
+
+
+def qk_int32(q_codes, k_codes, rows):
+    q_codes = _c(q_codes, np.int8)
+    k_codes = _c(k_codes, np.int8)
+    B, H, N, d = q_codes.shape
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, N), np.int32)
+    lib().oracle_qk_int32(_p(q_codes), _p(k_codes), B * H, N, d, _p(rows), rows.size, _p(out))
+    return out
+
+
+def attn_rows(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, rows=None, kv_tile=KV_TILE,
+              want_p=False):
+    """Oracle attention for flat query rows ``bh*N + i`` (all rows when None).
+
+    ``qk`` is the dict returned by :func:`quantize_qk`; ``v_codes`` is in the
+    natural [B,H,N,d] layout.  Returns O [nrows, d] fp32 (and the FP8 codes of
+    P~ [nrows, N] when ``want_p``).
+    """
+    qc = _c(qk["q_codes"], np.int8)
+    kc = _c(qk["k_codes"], np.int8)
+    qs = _c(qk["q_scale"], np.float32)
+    ks = _c(qk["k_scale"], np.float32)
+    vc = _c(v_codes, np.uint8)
+    vs = _c(v_scale, np.float32)
+    B, H, N, d = qc.shape
+    if rows is None:
+        rows = np.arange(B * H * N, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, d), np.float32)
+    p = np.empty((rows.size, N), np.uint8) if want_p else None
+    rc = lib().oracle_attn_rows(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B * H, N, d, blk_q, blk_k,
+                                kv_tile, int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows: unsupported arguments")
+    return (out, p) if want_p else out
+
+
+def run(Q_bits, K_bits, V_bits, dtype, blk_q, blk_k, causal, sm_scale, rows=None, kv_tile=KV_TILE,
+        want_p=False):
+    """The whole path on the CPU: quantize Q, K, V, then attention for ``rows``."""
+    qk = quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k)
+    vc, vs = quantize_v(V_bits, dtype)
+    res = attn_rows(qk, vc, vs, blk_q, blk_k, causal, sm_scale, rows=rows, kv_tile=kv_tile, want_p=want_p)
+    return qk, (vc, vs), res
+
+
+# ---------------------------------------------------------------- exact reference
+def exact_attention(Q, K, V, causal, sm_scale, rows=None, chunk=256):
+    """softmax(Q K^T * sm_scale [+ causal mask]) V in fp64 from float inputs [B,H,N,d].
+
+    Plain definition, evaluated in row chunks so that long sequences fit in memory.
+    Returns [nrows, d] for flat rows ``bh*N + i`` (all rows when None).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, H, N, d = Q.shape
+    Qf, Kf, Vf = Q.reshape(B * H, N, d), K.reshape(B * H, N, d), V.reshape(B * H, N, d)
+    if rows is None:
+        rows = np.arange(B * H * N, dtype=np.int64)
+    rows = np.asarray(rows, np.int64)
+    out = np.empty((rows.size, d), np.float64)
+    for s in range(0, rows.size, chunk):
+        r = rows[s:s + chunk]
+        bh, i = r // N, r % N
+        for h in np.unique(bh):
+            sel = np.nonzero(bh == h)[0]
+            qi = i[sel]
+            logits = (Qf[h][qi] @ Kf[h].T) * sm_scale
+            if causal:
+                logits = np.where(np.arange(N)[None, :] <= qi[:, None], logits, -np.inf)
+            logits -= logits.max(axis=1, keepdims=True)
+            w = np.exp(logits)
+            w /= w.sum(axis=1, keepdims=True)
+            out[s + sel] = w @ Vf[h]
+    return out

@@ -1,0 +1,373 @@
+/*
+ * sage_oracle.c -- plain, slow CPU oracle for the SageAttention-style quantized
+ * attention forward (INT8 per-block Q/K with K smoothing, INT8 QK^T with int32
+ * accumulation, fp32 online softmax, FP8 (e4m3) P~ and per-channel-scaled FP8 V,
+ * two-level P~V accumulation).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference the GPU path is checked
+ * against.  Only the test suite, the package smoke check and the benchmark's CPU
+ * baseline leg may load it.  It shares no code, header, table or constant
+ * generator with the HIP implementation; the shared exp2 polynomial below is a
+ * written specification that both sides restate independently.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [SA]   "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ *         Acceleration", abstract (8-bit quantized attention).
+ *  [SA2]  "SageAttention2", abstract: (P~, V) quantized to FP8 and a two-level
+ *         accumulation strategy for P~V.
+ *  [BLOG] "Flash Attention vs Sage Attention: Kernel Comparison", sections
+ *         "How FlashAttention reduces memory traffic" (tiled online softmax) and
+ *         "How SageAttention uses quantization for more throughput" (Q, K to
+ *         8-bit before the matmul, then precision-aware scaling); "A handful of
+ *         variables swing rankings hard" (causal masking changes which blocks are
+ *         skipped).
+ * The concrete arithmetic (K smoothing by the per-channel mean, INT8 per-block
+ * Q/K, int32 QK^T, fp32 online softmax, FP8 V with per-channel scales, two-level
+ * accumulation) is the method statement this build implements; every rounding
+ * step that the pages leave open is a stated reading, listed with the design
+ * notes.
+ *
+ * Arithmetic hygiene: build with -ffp-contract=off and without -ffast-math.
+ * fp32 operations are IEEE binary32 round-to-nearest-even; the only fused
+ * multiply-adds are the explicit fmaf() calls.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Input decoding: IEEE binary16 and bfloat16 to binary32 (both exact).      */
+/* ------------------------------------------------------------------------ */
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+static float half_to_float(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  float v;
+  if (e == 0) v = ldexpf((float)m, -24);                 /* zero / subnormal: m * 2^-24 */
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexpf((float)(1024 + m), e - 25);             /* (1 + m/1024) * 2^(e-15) */
+  return s ? -v : v;
+}
+static float bf16_to_float(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* dtype: 0 = float16, 1 = bfloat16 */
+static float load_in(const uint16_t* x, size_t idx, int dtype) {
+  return dtype == 0 ? half_to_float(x[idx]) : bf16_to_float(x[idx]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3 ("e4m3fn"): sign, 4-bit exponent (bias 7), 3-bit mantissa;   */
+/* normals (1 + m/8) 2^(e-7), subnormals (m/8) 2^-6, no infinities, S.1111.111 */
+/* is NaN, largest finite 448.  Encoding: round to nearest, ties to even,     */
+/* saturating to +-448.  ([SA2] abstract: P~ and V are quantized to FP8.)     */
+/* ------------------------------------------------------------------------ */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(8.0 + m, e - 10);
+  return s ? -v : v;
+}
+
+uint8_t oracle_e4m3_encode(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (isnan(x)) return 0x7F;
+  if (a >= 448.0) return sign | 0x7E;                     /* saturate to the largest finite */
+  if (a < 0x1p-6) {
+    /* subnormal range: grid step 2^-9; r = 8 lands on the smallest normal 0x08 */
+    double r = rint(a * 512.0);                            /* exact scaling, ties to even */
+    return sign | (uint8_t)r;
+  }
+  int ex;
+  frexp(a, &ex);                                           /* a = fr * 2^ex, fr in [0.5, 1) */
+  int k = ex - 1;                                          /* a in [2^k, 2^(k+1)), k >= -6 */
+  double r = rint(ldexp(a, 3 - k));                        /* significand in eighths: 8..16 */
+  if (r == 16.0) { k += 1; r = 8.0; }                      /* rounded up into the next binade */
+  return sign | (uint8_t)(((k + 7) << 3) | ((int)r - 8));
+}
+
+/* batch helpers for tests */
+void oracle_e4m3_encode_n(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_encode(x[i]);
+}
+void oracle_e4m3_decode_n(const uint8_t* c, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Shared exp2 X2(t), the exponential of the fp32 online softmax.            */
+/* Written specification (the kernel restates it independently):            */
+/*   n = round-to-nearest-even(t)            (exact)                         */
+/*   f = t - n                               (exact, |f| <= 1/2)             */
+/*   p = fma(fma(C2, f, C1), f, 1)           (two fp32 fused multiply-adds)  */
+/*   X2 = p * 2^n                            (exact scaling; only a result   */
+/*                                            below 2^-126 rounds, and any  */
+/*                                            n < -200 gives 0)             */
+/* C1 = 0x1.6a7dc6p-1, C2 = 0x1.fbcaa2p-3: relative minimax fit of 2^f on    */
+/* [-1/2, 1/2] with the constant term fixed to 1 and continuity across the  */
+/* reduction boundary (p(1/2) = 2 p(-1/2)); max relative error 2.9e-3,      */
+/* ten times below the e4m3 half-spacing.  X2(0) = 1 exactly.               */
+/* ------------------------------------------------------------------------ */
+static const float X2_C1 = 0x1.6a7dc6p-1f;
+static const float X2_C2 = 0x1.fbcaa2p-3f;
+
+float oracle_x2(float t) {
+  float n = rintf(t);
+  float f = t - n;
+  float p = fmaf(fmaf(X2_C2, f, X2_C1), f, 1.0f);
+  if (n < -200.0f) return 0.0f * p;
+  return ldexpf(p, (int)n);
+}
+
+void oracle_x2_n(const float* t, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_x2(t[i]);
+}
+float oracle_x2_c1(void) { return X2_C1; }
+float oracle_x2_c2(void) { return X2_C2; }
+
+/* ------------------------------------------------------------------------ */
+/* Step 1: per-channel mean of K over all N tokens of a head (smoothing K).  */
+/* Fixed point, order-free: s = sum_t trunc(clamp(k, +-2^20) * 2^24) in      */
+/* int64, mu = float(double(s) * 2^-24 / N).  Exact for float16 inputs;      */
+/* for bfloat16 only bits below 2^-24 of tiny elements are dropped.  Any     */
+/* shift vector leaves softmax(QK^T) unchanged; the fixed-point sum makes     */
+/* the vector independent of summation order.                                */
+/* ------------------------------------------------------------------------ */
+static const double KMEAN_CLAMP = 1048576.0;  /* 2^20 */
+
+static void kmean_head(const uint16_t* K, int dtype, int N, int d, float* mu, int64_t* sums_out) {
+  for (int c = 0; c < d; c++) {
+    int64_t s = 0;
+    for (int t = 0; t < N; t++) {
+      double x = (double)load_in(K, (size_t)t * d + c, dtype);
+      if (x > KMEAN_CLAMP) x = KMEAN_CLAMP;
+      if (x < -KMEAN_CLAMP) x = -KMEAN_CLAMP;
+      s += (int64_t)trunc(x * 16777216.0);
+    }
+    if (sums_out) sums_out[c] = s;
+    mu[c] = (float)(((double)s * 0x1p-24) / (double)N);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 2: symmetric INT8 block quantizer ([SA] abstract; [BLOG] "How        */
+/* SageAttention uses quantization").  One scale per block of tokens:        */
+/*   a = max |x| over the block; if a < 2^-120 the block is zero (d=r=0);     */
+/*   delta = RN(a / 127), r = RN(127 / a), code = rint(RN(x * r)) in [-127,127]*/
+/* ------------------------------------------------------------------------ */
+static void quant_block_i8(const float* x, size_t n, int8_t* codes, float* delta) {
+  float a = 0.0f;
+  for (size_t k = 0; k < n; k++) { float v = fabsf(x[k]); if (v > a) a = v; }
+  if (a < 0x1p-120f) {
+    *delta = 0.0f;
+    for (size_t k = 0; k < n; k++) codes[k] = 0;
+    return;
+  }
+  float dl = a / 127.0f;
+  float r = 127.0f / a;
+  *delta = dl;
+  for (size_t k = 0; k < n; k++) {
+    float y = rintf(x[k] * r);
+    if (y > 127.0f) y = 127.0f;
+    if (y < -127.0f) y = -127.0f;
+    codes[k] = (int8_t)y;
+  }
+}
+
+/* Q, K: [BH, N, d] (float16/bfloat16 raw bits).  Outputs: q_codes, k_codes
+ * [BH, N, d] int8; q_scale [BH, N/blk_q]; k_scale [BH, N/blk_k]; k_mean [BH, d].
+ * Returns 0, or -1 for a shape the method does not define. */
+int oracle_quantize_qk(const uint16_t* Q, const uint16_t* K, int dtype, int BH, int N, int d,
+                       int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                       float* k_scale, float* k_mean) {
+  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1 || N % blk_q || N % blk_k) return -1;
+  int nbq = N / blk_q, nbk = N / blk_k;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    const uint16_t* Qh = Q + (size_t)bh * N * d;
+    const uint16_t* Kh = K + (size_t)bh * N * d;
+    float* mu = k_mean + (size_t)bh * d;
+    kmean_head(Kh, dtype, N, d, mu, NULL);
+    float* buf = (float*)malloc(sizeof(float) * (size_t)(blk_q > blk_k ? blk_q : blk_k) * d);
+    for (int b = 0; b < nbq; b++) {
+      for (size_t k = 0; k < (size_t)blk_q * d; k++) buf[k] = load_in(Qh, (size_t)b * blk_q * d + k, dtype);
+      quant_block_i8(buf, (size_t)blk_q * d, q_codes + (size_t)bh * N * d + (size_t)b * blk_q * d,
+                     q_scale + (size_t)bh * nbq + b);
+    }
+    for (int b = 0; b < nbk; b++) {
+      for (int t = 0; t < blk_k; t++)
+        for (int c = 0; c < d; c++) {
+          size_t idx = (size_t)(b * blk_k + t) * d + c;
+          buf[(size_t)t * d + c] = load_in(Kh, idx, dtype) - mu[c];   /* smoothed K, fp32 */
+        }
+      quant_block_i8(buf, (size_t)blk_k * d, k_codes + (size_t)bh * N * d + (size_t)b * blk_k * d,
+                     k_scale + (size_t)bh * nbk + b);
+    }
+    free(buf);
+  }
+  return 0;
+}
+
+/* exported for tests: the int64 fixed-point channel sums and the mean */
+int oracle_kmean(const uint16_t* K, int dtype, int BH, int N, int d, float* mu, int64_t* sums) {
+  if (BH < 1 || N < 1 || d < 1) return -1;
+  for (int bh = 0; bh < BH; bh++)
+    kmean_head(K + (size_t)bh * N * d, dtype, N, d, mu + (size_t)bh * d, sums ? sums + (size_t)bh * d : NULL);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 3: V to FP8 with per-channel scales over all tokens of a head        */
+/* ([SA2] abstract: V quantized to FP8).                                     */
+/*   a_c = max_t |v[t,c]| (a_c < 2^-120: channel is zero),                   */
+/*   delta_c = RN(a_c / 448), r_c = RN(448 / a_c), code = E(RN(v * r_c)).    */
+/* Output codes in natural layout [BH, N, d].                                */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_v(const uint16_t* V, int dtype, int BH, int N, int d, uint8_t* v_codes, float* v_scale) {
+  if (BH < 1 || N < 1 || d < 1) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    const uint16_t* Vh = V + (size_t)bh * N * d;
+    for (int c = 0; c < d; c++) {
+      float a = 0.0f;
+      for (int t = 0; t < N; t++) { float v = fabsf(load_in(Vh, (size_t)t * d + c, dtype)); if (v > a) a = v; }
+      float dl = 0.0f, r = 0.0f;
+      if (a >= 0x1p-120f) { dl = a / 448.0f; r = 448.0f / a; }
+      v_scale[(size_t)bh * d + c] = dl;
+      for (int t = 0; t < N; t++) {
+        float v = load_in(Vh, (size_t)t * d + c, dtype);
+        v_codes[(size_t)bh * N * d + (size_t)t * d + c] = (a >= 0x1p-120f) ? oracle_e4m3_encode(v * r) : 0;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 4 (diagnostic): exact int32 S = q_codes . k_codes over d for chosen   */
+/* query rows against every key of the same head.  rows[] are flat indices   */
+/* bh*N + i.  out: [nrows, N].                                               */
+/* ------------------------------------------------------------------------ */
+void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int BH, int N, int d,
+                     const int64_t* rows, int nrows, int32_t* out) {
+  (void)BH;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < nrows; r++) {
+    int64_t bh = rows[r] / N, i = rows[r] % N;
+    const int8_t* q = q_codes + ((size_t)bh * N + i) * d;
+    for (int j = 0; j < N; j++) {
+      const int8_t* k = k_codes + ((size_t)bh * N + j) * d;
+      int32_t s = 0;
+      for (int c = 0; c < d; c++) s += (int32_t)q[c] * (int32_t)k[c];
+      out[(size_t)r * N + j] = s;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps 4-8: attention for chosen query rows.  For row i of head bh, KV      */
+/* tiles of kv_tile keys are visited in ascending order, one pass, as in the */
+/* tiled online softmax ([BLOG] "How FlashAttention reduces memory            */
+/* traffic"); tiles with no visible key (causal) are skipped ([BLOG] causal   */
+/* masking changes which blocks are skipped).  Per tile:                     */
+/*   S_j   = sum_c q_c k_c                       (int32, exact)              */
+/*   c2_j  = RN(RN(dQ * dK_j) * s2),  s2 = RN(sm_scale * log2 e)             */
+/*   u_j   = RN(float(S_j) * c2_j);  m' = max(m, max_j u_j)                  */
+/*   alpha = X2(RN(m - m'))   (0 on the first visited tile)                  */
+/*   P~_j  = X2(fma(float(S_j), c2_j, -RN(m' - 8)))   (P~ scaled by 2^8)     */
+/*   l     = fma(alpha, l, sum_j P~_j)               (fp32 state)            */
+/*   P^_j  = E(P~_j)                                 (FP8 e4m3)              */
+/*   Oblk_c = sum_j dec(P^_j) dec(v^_jc)             (inner level; exact     */
+/*                                                    products, summed in    */
+/*                                                    fp64, rounded to fp32) */
+/*   Oacc_c = fma(alpha, Oacc_c, Oblk_c)             (outer fp32 level)      */
+/*   m = m'                                                                  */
+/* O_c = Oacc_c * deltaV_c / l.  ([SA2] abstract: two-level accumulation of  */
+/* FP8 P~V.)  rows[] are flat indices bh*N + i; out: [nrows, d] fp32;        */
+/* p_codes (optional): [nrows, N], 0 where a key is not visible.             */
+/* ------------------------------------------------------------------------ */
+static const float LOG2E_F = 0x1.715476p+0f;   /* RN(log2 e) */
+
+int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                     const float* k_scale, const uint8_t* v_codes, const float* v_scale, int BH, int N,
+                     int d, int blk_q, int blk_k, int kv_tile, int causal, float sm_scale,
+                     const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1 || kv_tile < 1) return -1;
+  if (N % blk_q || N % blk_k || N % kv_tile) return -1;
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return -1;
+  const float s2 = sm_scale * LOG2E_F;
+  const int nbq = N / blk_q, nbk = N / blk_k;
+  double vdec[256];
+  for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
+  for (int r = 0; r < nrows; r++)
+    if (rows[r] < 0 || rows[r] >= (int64_t)BH * N) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int r = 0; r < nrows; r++) {
+    int64_t bh = rows[r] / N, i = rows[r] % N;
+    const int8_t* q = q_codes + ((size_t)bh * N + i) * d;
+    const float dq = q_scale[(size_t)bh * nbq + i / blk_q];
+    int32_t* S = (int32_t*)malloc(sizeof(int32_t) * kv_tile);
+    float* c2 = (float*)malloc(sizeof(float) * kv_tile);
+    float* pt = (float*)malloc(sizeof(float) * kv_tile);
+    uint8_t* ph = (uint8_t*)malloc(kv_tile);
+    float* oacc = (float*)calloc(d, sizeof(float));
+    double* oblk = (double*)malloc(sizeof(double) * d);
+    float m = 0.0f, l = 0.0f;
+    int first = 1;
+    if (p_codes) memset(p_codes + (size_t)r * N, 0, N);
+    for (int j0 = 0; j0 < N; j0 += kv_tile) {
+      int nvis = kv_tile;
+      if (causal) { if (j0 > i) break; if (i - j0 + 1 < nvis) nvis = (int)(i - j0 + 1); }
+      /* scores of the visible keys j0 .. j0+nvis-1 */
+      float mt = -INFINITY;
+      for (int jj = 0; jj < nvis; jj++) {
+        int j = j0 + jj;
+        const int8_t* k = k_codes + ((size_t)bh * N + j) * d;
+        int32_t s = 0;
+        for (int c = 0; c < d; c++) s += (int32_t)q[c] * (int32_t)k[c];
+        S[jj] = s;
+        c2[jj] = (dq * k_scale[(size_t)bh * nbk + j / blk_k]) * s2;
+        float u = (float)s * c2[jj];
+        if (u > mt) mt = u;
+      }
+      float mnew = first ? mt : (mt > m ? mt : m);
+      float alpha = first ? 0.0f : oracle_x2(m - mnew);
+      float mm = mnew - 8.0f;
+      float rowsum = 0.0f;
+      for (int jj = 0; jj < nvis; jj++) {
+        pt[jj] = oracle_x2(fmaf((float)S[jj], c2[jj], -mm));
+        rowsum += pt[jj];
+        ph[jj] = oracle_e4m3_encode(pt[jj]);
+        if (p_codes) p_codes[(size_t)r * N + j0 + jj] = ph[jj];
+      }
+      for (int c = 0; c < d; c++) {
+        double acc = 0.0;
+        for (int jj = 0; jj < nvis; jj++)
+          acc += vdec[ph[jj]] * vdec[v_codes[((size_t)bh * N + j0 + jj) * d + c]];
+        oblk[c] = acc;
+      }
+      for (int c = 0; c < d; c++) oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);
+      l = fmaf(alpha, l, rowsum);
+      m = mnew;
+      first = 0;
+    }
+    for (int c = 0; c < d; c++)
+      out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bh * d + c]) / (double)l);
+    free(S); free(c2); free(pt); free(ph); free(oacc); free(oblk);
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

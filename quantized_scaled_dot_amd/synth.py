@@ -1,0 +1,97 @@
+"""Seeded synthetic inputs for the quantized attention forward.
+
+This module only draws random tensors; it holds none of the method's
+arithmetic.  The oracle and the GPU path receive the same tensors from it.
+
+Recipe (for every workload): ``numpy.random.default_rng(seed)`` (PCG64),
+float32 standard normals drawn in the order Q, K, per-channel K bias, V,
+then the V outlier channels; K gets a bias drawn per (b, h, channel) with the
+stated variance and added to every token (channel outliers that smoothing
+removes); optionally a fixed number of V channels per (b, h), chosen without
+replacement, are multiplied by a factor; finally the tensors are rounded to
+float16 / bfloat16 with round-to-nearest-even.  Shapes follow the workloads
+the method is aimed at: LLM prefill, ViT, video DiT and long-context prefill.
+"""
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "float16" or "bfloat16"
+    causal: bool
+    blk_q: int
+    blk_k: int
+    bias_var: float
+    sm_scale: float
+    v_outlier_channels: int = 0
+    v_outlier_scale: float = 1.0
+    seed: int = 0
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "float16" else torch.bfloat16
+
+    @property
+    def dtype_code(self):
+        return 0 if self.dtype == "float16" else 1
+
+    @property
+    def ops(self):
+        """Attention operation count 4*B*H*N^2*d, halved for causal masking."""
+        o = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return o / 2 if self.causal else o
+
+    def with_(self, **kw):
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+def _rsqrt32(x):
+    return float(np.float32(1.0 / math.sqrt(x)))
+
+
+WORKLOADS = {
+    "tiny-f16-256": Workload("tiny-f16-256", 1, 2, 256, 64, "float16", False, 64, 64, 4.0, 0.125),
+    "llm-prefill-4k-causal": Workload("llm-prefill-4k-causal", 4, 32, 4096, 128, "bfloat16", True, 128, 64,
+                                      4.0, _rsqrt32(128)),
+    "vit-2k-f16": Workload("vit-2k-f16", 16, 16, 2048, 64, "float16", False, 128, 64, 2.0, 0.125),
+    "video-dit-32k": Workload("video-dit-32k", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0, _rsqrt32(128)),
+    "long-prefill-128k-causal": Workload("long-prefill-128k-causal", 1, 8, 131072, 128, "bfloat16", True, 128, 64,
+                                         4.0, _rsqrt32(128), v_outlier_channels=13, v_outlier_scale=8.0),
+}
+
+
+def make_inputs(w: Workload, seed=None, device="cpu"):
+    """Return Q, K, V as torch tensors [B, H, N, d] of ``w.dtype`` on ``device``."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    bias = rng.standard_normal((w.B, w.H, 1, w.d), dtype=np.float32) * np.float32(math.sqrt(w.bias_var))
+    k += bias
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if w.v_outlier_channels:
+        for b in range(w.B):
+            for h in range(w.H):
+                ch = rng.choice(w.d, size=w.v_outlier_channels, replace=False)
+                v[b, h][:, ch] *= np.float32(w.v_outlier_scale)
+    out = []
+    for a in (q, k, v):
+        t = torch.from_numpy(a).to(w.torch_dtype)
+        out.append(t.to(device) if device != "cpu" else t)
+    return tuple(out)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of a float16/bfloat16 CPU tensor as a uint16 array."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself (brute force, an independent library routine, exact rationals, a closed
+form, or an invariance the mathematics fixes), so that a dropped term, a wrong
+sign or index, or a transposed operand fails at least one of them."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from quantized_scaled_dot_amd import synth
+
+
+def _f16_bits(a):
+    return synth.bits(torch.from_numpy(np.asarray(a, np.float32)).to(torch.float16))
+
+
+def _bf16_bits(a):
+    return synth.bits(torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16))
+
+
+def _f16_vals(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.float16).float().numpy()
+
+
+# ------------------------------------------------------------------ e4m3 codec
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def _nearest_even_bruteforce(x):
+    """Nearest finite e4m3 value by exhaustive search; ties to the even code."""
+    codes = np.arange(0, 127, dtype=np.uint8)  # positive finite codes
+    vals = orc.e4m3_decode(codes)
+    a = abs(float(x))
+    if a >= 448.0:
+        c = 0x7E
+    else:
+        dist = np.abs(vals - a)
+        best = np.flatnonzero(dist == dist.min())
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+    return c | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+
+def test_e4m3_encode_midpoints_ties_to_even_and_saturation():
+    vals = orc.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    xs = []
+    for k in range(126):
+        mid = np.float32((vals[k] + vals[k + 1]) / 2)
+        v = np.float32(vals[k])
+        xs += [v, np.nextafter(v, np.float32(1e30)), np.nextafter(v, np.float32(-1e30)),
+               mid, np.nextafter(mid, np.float32(1e30)), np.nextafter(mid, np.float32(-1e30))]
+    xs += [np.float32(v) for v in (448, 449, 463.99, 464, 1e6, 3e38, 0, 2 ** -10, 3 * 2 ** -11, 2 ** -11, 1e-30)]
+    xs = np.array(xs, np.float32)
+    xs = np.concatenate([xs, -xs])
+    got = orc.e4m3_encode(xs)
+    ref = np.array([_nearest_even_bruteforce(float(x)) for x in xs], np.uint8)
+    assert np.array_equal(got, ref)
+    assert orc.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * 40,
+                        rng.uniform(-448, 448, 200000).astype(np.float32),
+                        (rng.standard_normal(100000) * 1e-2).astype(np.float32)])
+    ours = orc.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------ shared exp2
+def test_x2_accuracy_and_exact_points():
+    t = np.concatenate([np.linspace(-126, 8.5, 2_000_001), np.linspace(-1, 1, 100001)]).astype(np.float32)
+    got = orc.x2(t).astype(np.float64)
+    ref = np.exp2(t.astype(np.float64))
+    rel = np.abs(got / ref - 1)
+    assert rel.max() < 3.0e-3
+    ints = np.arange(-126, 9, dtype=np.float32)
+    assert np.array_equal(orc.x2(ints), np.exp2(ints.astype(np.float64)).astype(np.float32))
+    assert orc.x2(np.array([0.0], np.float32))[0] == 1.0
+    assert orc.x2(np.array([8.0], np.float32))[0] == 256.0
+
+
+def test_x2_monotone_and_underflow():
+    t = np.linspace(-20, 8.5, 3_000_001).astype(np.float32)
+    y = orc.x2(t)
+    d = np.diff(y.astype(np.float64))
+    # non-decreasing up to one fp32 ulp at the half-integer reduction boundaries
+    ulp = np.spacing(y[:-1]).astype(np.float64)
+    assert (d >= -ulp).all()
+    assert orc.x2(np.array([-150, -1e4, -1e30, -3.0e38], np.float32)).tolist() == [0, 0, 0, 0]
+    # subnormal results are correctly rounded scalings of the polynomial
+    p = orc.x2(np.array([-130.0], np.float32))[0]
+    assert p == np.float32(2.0 ** -130)
+
+
+def test_x2_coefficients_are_the_specified_literals():
+    c1, c2 = orc.x2_coefficients()
+    assert c1 == float.fromhex("0x1.6a7dc6p-1") and c2 == float.fromhex("0x1.fbcaa2p-3")
+
+
+# ------------------------------------------------------------------ int32 QK^T
+def test_qk_int32_against_bigint_bruteforce():
+    rng = np.random.default_rng(2)
+    B, H, N, d = 1, 2, 8, 64
+    qc = rng.integers(-127, 128, (B, H, N, d), dtype=np.int8)
+    kc = rng.integers(-127, 128, (B, H, N, d), dtype=np.int8)
+    qc[0, 1, 3] = 127
+    kc[0, 1, 5] = -127  # extreme products
+    rows = np.array([0, 3, 7, N + 3, 2 * N - 1], np.int64)
+    got = orc.qk_int32(qc, kc, rows)
+    for r, row in enumerate(rows):
+        bh, i = divmod(int(row), N)
+        b, h = divmod(bh, H)
+        for j in range(N):
+            s = sum(int(qc[b, h, i, c]) * int(kc[b, h, j, c]) for c in range(d))
+            assert got[r, j] == s
+
+
+# ------------------------------------------------------------------ K mean
+def test_kmean_equals_exact_rational_mean_f16():
+    rng = np.random.default_rng(3)
+    B, H, N, d = 1, 2, 96, 16
+    k = rng.standard_normal((B, H, N, d)).astype(np.float32) * 3 + 1.5
+    kb = _f16_bits(k)
+    kv = _f16_vals(k)
+    mu, sums = orc.kmean(kb, 0)
+    for b in range(B):
+        for h in range(H):
+            for c in range(d):
+                exact = sum(Fraction(float(x)) for x in kv[b, h, :, c])
+                # every float16 is a multiple of 2^-24: the fixed-point sum is the exact sum
+                assert Fraction(int(sums[b, h, c]), 2 ** 24) == exact
+                m = exact / N
+                rn = np.float32(float(m))  # round the exact mean once (via double)
+                assert abs(Fraction(float(mu[b, h, c])) - m) <= Fraction(float(np.spacing(rn)))
+                assert mu[b, h, c] == np.float32(np.float64(float(exact)) / N)
+
+
+def test_kmean_constant_channels_and_bf16_tiny_values():
+    B, H, N, d = 1, 1, 64, 8
+    k = np.tile(np.array([0.5, -3.25, 1024.0, 0, 7.0, -0.125, 2.0 ** -20, 96.0], np.float32), (B, H, N, 1))
+    for conv, dt in ((_f16_bits, 0), (_bf16_bits, 1)):
+        mu, _ = orc.kmean(conv(k), dt)
+        kv = torch.from_numpy(k).to(torch.float16 if dt == 0 else torch.bfloat16).float().numpy()
+        expect = kv[0, 0, 0].copy()
+        if dt == 1:  # bfloat16 values below 2^-24 granularity are truncated in the fixed-point sum
+            expect[6] = np.float32(0.0) if kv[0, 0, 0, 6] < 2.0 ** -24 else expect[6]
+        assert np.array_equal(mu[0, 0], expect)
+
+
+# ------------------------------------------------------------------ Q/K block quantizer
+def _quantize(B=2, H=2, N=256, d=64, blk_q=64, blk_k=64, seed=4, dtype=0, scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, N, d)).astype(np.float32) * scale
+    k = (rng.standard_normal((B, H, N, d)) + rng.standard_normal((B, H, 1, d)) * 2).astype(np.float32) * scale
+    conv = _f16_bits if dtype == 0 else _bf16_bits
+    return q, k, orc.quantize_qk(conv(q), conv(k), dtype, blk_q, blk_k)
+
+
+def test_quantizer_roundtrip_bound_and_full_range():
+    for dtype in (0, 1):
+        q, k, r = _quantize(dtype=dtype)
+        tdt = torch.float16 if dtype == 0 else torch.bfloat16
+        qv = torch.from_numpy(q).to(tdt).float().numpy()
+        kv = torch.from_numpy(k).to(tdt).float().numpy()
+        ks = kv - r["k_mean"][:, :, None, :]  # smoothed K in fp32 (exact per element rounding)
+        for x, codes, scale, blk in ((qv, r["q_codes"], r["q_scale"], 64), (ks, r["k_codes"], r["k_scale"], 64)):
+            B, H, N, d = x.shape
+            xb = x.reshape(B, H, N // blk, blk * d).astype(np.float64)
+            cb = codes.reshape(B, H, N // blk, blk * d).astype(np.float64)
+            dl = scale.astype(np.float64)[..., None]
+            assert np.abs(codes).max() <= 127
+            assert (np.abs(cb).max(axis=-1) == 127).all()  # every nonzero block uses the full range
+            err = np.abs(xb - cb * dl)
+            assert (err <= dl / 2 + 127 * dl * 2.0 ** -21).all()
+            a = np.abs(xb).max(axis=-1, keepdims=True)
+            assert np.array_equal(dl.astype(np.float32), (a.astype(np.float32) / np.float32(127)))
+
+
+def test_quantizer_power_of_two_metamorphic():
+    _, _, r0 = _quantize(seed=5)
+    _, _, r1 = _quantize(seed=5, scale=8.0)
+    _, _, r2 = _quantize(seed=5, scale=1 / 16)
+    for r in (r1, r2):
+        assert np.array_equal(r["q_codes"], r0["q_codes"]) and np.array_equal(r["k_codes"], r0["k_codes"])
+    assert np.array_equal(r1["q_scale"], r0["q_scale"] * 8) and np.array_equal(r1["k_scale"], r0["k_scale"] * 8)
+    assert np.array_equal(r2["q_scale"], r0["q_scale"] / 16)
+
+
+def test_zero_block_gives_zero_scale_and_codes():
+    B, H, N, d = 1, 1, 128, 64
+    q = np.zeros((B, H, N, d), np.float32)
+    q[0, 0, 64:] = 1.0
+    k = np.ones((B, H, N, d), np.float32) * 3  # constant K: smoothed K is exactly 0
+    r = orc.quantize_qk(_f16_bits(q), _f16_bits(k), 0, 64, 64)
+    assert r["q_scale"][0, 0, 0] == 0 and (r["q_codes"][0, 0, :64] == 0).all()
+    assert (r["q_codes"][0, 0, 64:] == 127).all()
+    assert (r["k_scale"] == 0).all() and (r["k_codes"] == 0).all() and (r["k_mean"] == 3).all()
+
+
+# ------------------------------------------------------------------ V quantizer
+def test_v_quantizer_roundtrip_and_scales():
+    rng = np.random.default_rng(6)
+    B, H, N, d = 1, 2, 128, 32
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    v[0, 1, :, 5] *= 8
+    vv = _f16_vals(v).astype(np.float64)
+    vc, vs = orc.quantize_v(_f16_bits(v), 0)
+    a = np.abs(vv).max(axis=2)
+    assert np.array_equal(vs, (a.astype(np.float32) / np.float32(448)))
+    deq = orc.e4m3_decode(vc) * vs[:, :, None, :].astype(np.float64)
+    err = np.abs(deq - vv)
+    normal = np.abs(orc.e4m3_decode(vc)) >= 2.0 ** -6
+    tol_norm = 2.0 ** -4 * np.abs(vv) * (1 + 2.0 ** -20)
+    tol_sub = 2.0 ** -10 * np.broadcast_to(vs[:, :, None, :], vv.shape) * (1 + 2.0 ** -20)
+    assert (err[normal] <= tol_norm[normal] + 1e-30).all()
+    assert (err[~normal] <= tol_sub[~normal]).all()
+    # each channel's largest magnitude maps to the top code
+    assert (np.abs(orc.e4m3_decode(vc)).max(axis=2) == 448).all()
+
+
+# ------------------------------------------------------------------ attention
+def _small(w_kw, seed=0):
+    w = synth.WORKLOADS["tiny-f16-256"].with_(**w_kw)
+    Q, K, V = synth.make_inputs(w, seed=seed)
+    return w, Q, K, V
+
+
+def _run(w, Q, K, V, **kw):
+    return orc.run(synth.bits(Q), synth.bits(K), synth.bits(V), w.dtype_code, w.blk_q, w.blk_k, w.causal,
+                   w.sm_scale, **kw)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(causal=True), dict(d=128, blk_q=128, dtype="bfloat16", causal=True),
+                                dict(N=512, v_outlier_channels=6, v_outlier_scale=8.0, causal=True)])
+def test_oracle_close_to_exact_fp64_attention(kw):
+    w, Q, K, V = _small(kw)
+    _, _, O = _run(w, Q, K, V)
+    ref = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
+    O = O.astype(np.float64)
+    cos = (O * ref).sum() / np.sqrt((O * O).sum() * (ref * ref).sum())
+    assert cos >= 0.995
+    # a dropped term or a wrong index moves the result far beyond FP8 noise
+    assert np.abs(O - ref).max() < 0.25 * np.abs(ref).max()
+
+
+def test_softmax_invariant_to_subtracting_the_k_mean_fp64():
+    w, Q, K, V = _small({})
+    mu, _ = orc.kmean(synth.bits(K), 0)
+    Qf, Kf, Vf = (t.double().numpy() for t in (Q, K, V))
+    a = orc.exact_attention(Qf, Kf, Vf, False, w.sm_scale)
+    b = orc.exact_attention(Qf, Kf - mu[:, :, None, :].astype(np.float64), Vf, False, w.sm_scale)
+    assert np.abs(a - b).max() < 1e-12
+
+
+def test_k_bias_invariance_bit_exact_on_dyadic_grid():
+    """On a dyadic grid the smoothing step removes a per-channel K bias exactly,
+    so every code, scale and output is bit-identical with and without it."""
+    rng = np.random.default_rng(7)
+    B, H, N, d = 1, 2, 256, 64
+    q = rng.integers(-512, 513, (B, H, N, d)) / 256.0
+    k = rng.integers(-512, 513, (B, H, N, d)) / 256.0
+    v = rng.integers(-512, 513, (B, H, N, d)) / 256.0
+    bias = rng.integers(-900, 901, (B, H, 1, d)) / 256.0
+    args = dict(dtype=0, blk_q=64, blk_k=64, causal=True, sm_scale=0.125)
+    r0 = orc.run(_f16_bits(q), _f16_bits(k), _f16_bits(v), want_p=True, **args)
+    r1 = orc.run(_f16_bits(q), _f16_bits(k + bias), _f16_bits(v), want_p=True, **args)
+    assert np.array_equal(r1[0]["k_mean"], r0[0]["k_mean"] + bias[:, :, 0, :].astype(np.float32))
+    for key in ("k_codes", "k_scale", "q_codes", "q_scale"):
+        assert np.array_equal(r0[0][key], r1[0][key])
+    assert np.array_equal(r0[2][1], r1[2][1])  # FP8 codes of P~
+    assert np.array_equal(r0[2][0], r1[2][0])  # O bit for bit
+
+
+def test_zero_q_gives_mean_of_dequantized_v():
+    for causal in (False, True):
+        w, Q, K, V = _small(dict(causal=causal))
+        Q = torch.zeros_like(Q)
+        qk, (vc, vs), (O, P) = _run(w, Q, K, V, want_p=True)
+        assert (qk["q_codes"] == 0).all() and (qk["q_scale"] == 0).all()
+        deq = orc.e4m3_decode(vc) * vs[:, :, None, :].astype(np.float64)  # [B,H,N,d]
+        B, H, N, d = deq.shape
+        if causal:
+            ref = np.cumsum(deq, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+            vis = np.tril(np.ones((N, N), bool))
+        else:
+            ref = np.broadcast_to(deq.mean(axis=2, keepdims=True), deq.shape)
+            vis = np.ones((N, N), bool)
+        assert np.allclose(O.reshape(B, H, N, d), ref, rtol=2e-6, atol=1e-6)
+        P = P.reshape(B, H, N, N)
+        assert (P[:, :, vis] == 0x78).all() and (P[:, :, ~vis] == 0).all()  # every P~ = 2^8 exactly
+
+
+def test_causal_first_row_is_first_value_row():
+    w, Q, K, V = _small(dict(causal=True))
+    qk, (vc, vs), O = _run(w, Q, K, V)
+    B, H, N, d = vc.shape
+    O = O.reshape(B, H, N, d)
+    expect = (orc.e4m3_decode(vc[:, :, 0, :]) * vs.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(O[:, :, 0, :], expect)
+
+
+def test_v_power_of_two_scales_output_exactly():
+    w, Q, K, V = _small(dict(causal=True))
+    _, (vc0, vs0), O0 = _run(w, Q, K, V)
+    _, (vc1, vs1), O1 = _run(w, Q, K, V * 4)
+    assert np.array_equal(vc0, vc1) and np.array_equal(vs1, vs0 * 4)
+    assert np.array_equal(O1, O0 * 4)
+
+
+def test_head_permutation_equivariance():
+    w, Q, K, V = _small(dict(B=2, H=3, N=128))
+    perm = torch.tensor([4, 0, 5, 2, 1, 3])
+    def flat(t):
+        return t.reshape(6, *t.shape[2:])
+    def unflat(t):
+        return t.reshape(2, 3, *t.shape[1:])
+    Qp, Kp, Vp = (unflat(flat(t)[perm]) for t in (Q, K, V))
+    _, _, O = _run(w, Q, K, V)
+    _, _, Op = _run(w, Qp, Kp, Vp)
+    N, d = 128, w.d
+    assert np.array_equal(Op.reshape(6, N, d), O.reshape(6, N, d)[perm.numpy()])
+
+
+def test_row_subset_matches_full_run():
+    w, Q, K, V = _small(dict(causal=True))
+    qk, (vc, vs), (O, P) = _run(w, Q, K, V, want_p=True)
+    rows = np.array([0, 5, 63, 64, 255, 256, 300, 511], np.int64)
+    Os, Ps = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, True, w.sm_scale, rows=rows, want_p=True)
+    assert np.array_equal(Os, O[rows]) and np.array_equal(Ps, P[rows])
+
+
+def test_exact_attention_reference_against_python_loops():
+    rng = np.random.default_rng(8)
+    B, H, N, d = 1, 1, 5, 3
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    got = orc.exact_attention(Q, K, V, True, 0.7)
+    for i in range(N):
+        logits = [sum(Q[0, 0, i, c] * K[0, 0, j, c] for c in range(d)) * 0.7 for j in range(i + 1)]
+        mx = max(logits)
+        w = [math.exp(x - mx) for x in logits]
+        s = sum(w)
+        for c in range(d):
+            assert abs(got[i, c] - sum(w[j] * V[0, 0, j, c] for j in range(i + 1)) / s) < 1e-12
+
+
+def test_online_softmax_matches_single_tile_reference_in_the_exact_limit():
+    """With the KV tile as wide as the sequence, one tile holds every key: the
+    result is softmax with the exact row max.  Narrow tiles must agree within
+    FP8 noise, and both must track the fp64 reference."""
+    w, Q, K, V = _small({})
+    qk, (vc, vs), O64 = _run(w, Q, K, V, kv_tile=64)
+    O256 = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, False, w.sm_scale, kv_tile=256)
+    assert np.abs(O64 - O256).max() < 0.05
