@@ -1,0 +1,159 @@
+/*
+ * sage.h -- C ABI of libsage.so, the MI355X (gfx950) quantized attention
+ * forward: K smoothing, INT8 per-block Q/K, INT8 QK^T with int32 accumulation,
+ * fp32 online softmax, FP8 (OCP e4m3) P~ and per-channel-scaled FP8 V, and a
+ * two-level P~V accumulation (an FP8 matrix-core inner block added into an fp32
+ * running accumulator).
+ *
+ * Method sources (web pages, by title and section):
+ *  - "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ *    Acceleration", abstract (dblp author listing on taxoreview.com): attention
+ *    with 8-bit quantized Q and K.
+ *  - The SageAttention2 abstract (same listing): P~
+ *    and V quantized to FP8, and a two-level accumulation strategy for P~V.
+ *  - "Flash Attention vs Sage Attention: Kernel Comparison", sections "How
+ *    SageAttention uses quantization for more throughput" (Q, K to 8-bit before
+ *    the matrix multiply, then precision-aware scaling), "How FlashAttention
+ *    reduces memory traffic" (tiled online softmax) and the list of variables
+ *    under "Attention kernel benchmarks" (causal masking changes which blocks are
+ *    skipped).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers owned by the caller; the library allocates
+ *    nothing and keeps no state between calls.  Every pointer must be 16-byte
+ *    aligned; outputs must not alias inputs.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work on it and return; no host synchronisation happens inside.
+ *  - Return value: a sage_status.  Argument errors are detected before any work
+ *    is enqueued; then no output is touched.  A failed kernel launch returns
+ *    SAGE_ERR_HIP.  Faults during execution surface at the caller's next
+ *    synchronisation, as for any HIP work.
+ *  - Tensors are contiguous, row-major, self-attention shaped [B, H, N, d]
+ *    (the layout of PyTorch's scaled_dot_product_attention).
+ *  - Supported: d in {64, 128}; N a multiple of 128 with 128 <= N <= 524288;
+ *    blk_q in {64, 128}; blk_k = 64; B*H >= 1; sm_scale finite and > 0;
+ *    inputs finite.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad dtype, bad sm_scale */
+  SAGE_ERR_UNSUPPORTED = 2,   /* shape outside the supported set above */
+  SAGE_ERR_MISALIGNED = 3,    /* a pointer is not 16-byte aligned */
+  SAGE_ERR_HIP = 4,           /* a HIP call failed (launch error) */
+  SAGE_ERR_WORKSPACE = 5      /* workspace too small */
+};
+
+enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 };
+
+/* Human-readable text of a status code (static storage). */
+const char* sage_status_string(int status);
+
+/* Width, in keys, of the KV tile of the online softmax: the running max is
+ * updated and one FP8 inner P~V block is accumulated per tile. */
+int sage_kv_tile(void);
+
+/* Bytes of scratch memory sage_quantize_qk needs (int64 per-channel partial
+ * sums of K, one row of d per 256 tokens of every head). */
+size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * sage_quantize_qk -- smooth K and quantize Q and K to INT8 per block.
+ * (SageAttention abstract; blog section "How SageAttention uses quantization
+ * for more throughput".)
+ *   k_mean[b,h,c] = mean over all N tokens of K[b,h,:,c], computed from the
+ *     exact int64 sum of trunc(clamp(k, +-2^20) * 2^24) (order-free), divided in
+ *     fp64 and rounded to fp32.
+ *   Smoothed K: ks = fp32(k) - k_mean (fp32).
+ *   Blocks of blk_q tokens of Q / blk_k tokens of ks, all d channels: a = max|x|;
+ *     scale = a/127, r = 127/a (fp32, correctly rounded), code = rint(x*r)
+ *     (ties to even) in [-127, 127]; a block with a < 2^-120 gets scale 0 and
+ *     all-zero codes.
+ * In:  Q, K        [B,H,N,d] float16 (in_dtype SAGE_F16) or bfloat16 (SAGE_BF16).
+ * Out: q_codes     [B,H,N,d] int8;  q_scale [B,H,N/blk_q] fp32;
+ *      k_codes     [B,H,N,d] int8;  k_scale [B,H,N/blk_k] fp32;
+ *      k_mean      [B,H,d] fp32.
+ * workspace: device scratch of at least sage_quantize_qk_workspace_bytes(...);
+ *      contents on entry are ignored.
+ */
+int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, int N, int d, int blk_q,
+                     int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
+                     float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch memory sage_quantize_v needs (fp32 per-channel partial
+ * maxima, one row of d per 256 tokens of every head, plus one row per head). */
+size_t sage_quantize_v_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * sage_quantize_v -- V to FP8 e4m3 with one scale per channel of each head.
+ * (SageAttention2 abstract: V quantized to FP8.)
+ *   a_c = max over all N tokens of |V[b,h,:,c]|; v_scale = a_c/448,
+ *   r_c = 448/a_c; code = e4m3(rn(v * r_c)) with round-to-nearest-even
+ *   (a channel with a_c < 2^-120 gets scale 0 and zero codes).
+ * In:  V       [B,H,N,d] float16 / bfloat16.
+ * Out: v_codes e4m3 bytes in KV-tile channel-major order: for head (b,h),
+ *              tile t of 64 consecutive tokens and channel c, the 64 codes of
+ *              tokens 64t..64t+63 are contiguous at byte offset
+ *              (((b*H + h)*(N/64) + t)*d + c)*64.
+ *      v_scale [B,H,d] fp32.
+ */
+int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_attn_fwd -- attention forward on the quantized operands.
+ * (Tiled online softmax: blog section "How FlashAttention reduces memory
+ * traffic"; FP8 P~ and two-level P~V accumulation: SageAttention2 abstract;
+ * causal block skipping: blog, variables under "Attention kernel benchmarks".)
+ * For query row i, KV tiles of sage_kv_tile() keys are visited in ascending
+ * order (causal: only tiles holding a key j <= i; key j is visible iff j <= i):
+ *   S_j    = sum_c q_codes[i,c] k_codes[j,c]               (int32, exact)
+ *   c2     = (q_scale * k_scale_j) * (sm_scale * log2 e)   (fp32, in this order)
+ *   m'     = max(m, max_j fp32(S_j) * c2)
+ *   alpha  = X2(m - m')   (0 on the first tile)
+ *   P~_j   = X2(fma(fp32(S_j), c2, -(m' - 8)))             (P~ scaled by 2^8)
+ *   l      = fma(alpha, l, sum_j P~_j)
+ *   O_blk  = sum_j e4m3(P~_j) * v_code_j                   (FP8 matrix cores)
+ *   O_acc  = fma(alpha, O_acc, O_blk);  m = m'
+ *   O[i,c] = O_acc[c] * v_scale[c] / l
+ * X2(t) = p(f) * 2^n with n = rint(t), f = t - n,
+ *   p(f) = fma(fma(0x1.fbcaa2p-3, f, 0x1.6a7dc6p-1), f, 1).
+ * In:  the outputs of sage_quantize_qk (q_codes, q_scale, k_codes, k_scale)
+ *      and sage_quantize_v (v_codes, v_scale), same B, H, N, d, blk_q, blk_k.
+ * Out: O [B,H,N,d] of out_dtype (SAGE_F32, SAGE_F16 or SAGE_BF16; rounded to
+ *      nearest even from fp32).
+ */
+int sage_attn_fwd(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                  const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
+                  int blk_q, int blk_k, int causal, float sm_scale, void* stream);
+
+/*
+ * sage_attn_fwd_dump -- sage_attn_fwd through the same kernel code, which in
+ * addition writes the int32 scores and the FP8 codes of P~ of selected
+ * 128-query tiles (test and diagnostic use).
+ * sel:    n_sel device int32 ids (b*H + h) * (N/128) + qt of query tiles.
+ * s_dump: [n_sel, 128, N] int32; entry (k, r, j) = S for query qt*128 + r and
+ *         key j, for every key of every KV tile the kernel computed for that
+ *         query's 32-row group (other entries are left untouched).
+ * p_dump: [n_sel, 128, N] uint8 e4m3 codes of P~ (0 for keys not visible),
+ *         same coverage.
+ */
+int sage_attn_fwd_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                       const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N,
+                       int d, int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel,
+                       int32_t* s_dump, uint8_t* p_dump, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */

@@ -12,9 +12,10 @@
  *
  * Sources (web pages, cited by title and section):
  *  [SA]   "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
- *         Acceleration", abstract (8-bit quantized attention).
- *  [SA2]  "SageAttention2", abstract: (P~, V) quantized to FP8 and a two-level
- *         accumulation strategy for P~V.
+ *         Acceleration", abstract on the dblp author listing (taxoreview.com):
+ *         8-bit quantized attention.
+ *  [SA2]  The SageAttention2 abstract on the same listing: (P~, V) quantized to
+ *         FP8 and a two-level accumulation strategy for P~V.
  *  [BLOG] "Flash Attention vs Sage Attention: Kernel Comparison", sections
  *         "How FlashAttention reduces memory traffic" (tiled online softmax) and
  *         "How SageAttention uses quantization for more throughput" (Q, K to

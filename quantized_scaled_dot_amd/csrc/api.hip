@@ -1,0 +1,145 @@
+// C ABI of libsage.so: argument validation, then kernel launches on the
+// caller's stream.  No allocation, no host synchronisation, no global state.
+#include <math.h>
+
+#include "../../include/sage.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return SAGE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (N % sage::kQTile != 0 || N > (1 << 19)) return SAGE_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  // flattened 1-D grids: (N/64) * B*H workgroups must fit in a grid dimension
+  if (bh * (N / sage::kKTile) > 0x7fffffffLL) return SAGE_ERR_UNSUPPORTED;
+  return SAGE_OK;
+}
+
+int check_in_dtype(int dt) { return (dt == SAGE_F16 || dt == SAGE_BF16) ? SAGE_OK : SAGE_ERR_INVALID_ARG; }
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+#define SAGE_TRY(x)          \
+  do {                       \
+    int _s = (x);            \
+    if (_s != SAGE_OK) return _s; \
+  } while (0)
+
+#define SAGE_PTR(p)                                    \
+  do {                                                 \
+    if ((p) == nullptr) return SAGE_ERR_INVALID_ARG;   \
+    if (!aligned16(p)) return SAGE_ERR_MISALIGNED;     \
+  } while (0)
+
+int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
+                int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump,
+                uint8_t* p_dump, bool dump, void* stream) {
+  SAGE_TRY(check_shape(B, H, N, d));
+  if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
+  if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O);
+  if (dump) {
+    if (n_sel < 0) return SAGE_ERR_INVALID_ARG;
+    if (n_sel > 0) { SAGE_PTR(sel); SAGE_PTR(s_dump); SAGE_PTR(p_dump); }
+  }
+  sage::AttnArgs a;
+  a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
+  a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype;
+  a.BH = B * H; a.N = N; a.d = d; a.blk_q = blk_q; a.causal = causal;
+  a.s2 = sm_scale * sage::kLog2e;
+  a.sel = dump ? sel : nullptr; a.n_sel = dump ? n_sel : 0; a.s_dump = s_dump; a.p_dump = p_dump;
+  (void)hipGetLastError();
+  sage::launch_attn_fwd(a, dump, (hipStream_t)stream);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG: null pointer, bad size, dtype or sm_scale";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N % 128 == 0, N <= 2^19, blk_q in {64,128}, blk_k == 64";
+    case SAGE_ERR_MISALIGNED: return "SAGE_ERR_MISALIGNED: pointer not 16-byte aligned";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP: kernel launch failed";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
+    default: return "SAGE_ERR_UNKNOWN";
+  }
+}
+
+int sage_kv_tile(void) { return sage::kKTile; }
+
+size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != SAGE_OK) return 0;
+  return sage::quantize_qk_workspace(B * H, N, d);
+}
+
+size_t sage_quantize_v_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != SAGE_OK) return 0;
+  return sage::quantize_v_workspace(B * H, N, d);
+}
+
+int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, int N, int d, int blk_q, int blk_k,
+                     int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale, float* k_mean, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shape(B, H, N, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
+  if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
+  SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  SAGE_PTR(k_mean); SAGE_PTR(workspace);
+  if (workspace_bytes < sage::quantize_qk_workspace(B * H, N, d)) return SAGE_ERR_WORKSPACE;
+  sage::QuantQKArgs a;
+  a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.BH = B * H; a.N = N; a.d = d; a.blk_q = blk_q;
+  a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale; a.k_mean = k_mean;
+  a.workspace = workspace;
+  (void)hipGetLastError();
+  sage::launch_quantize_qk(a, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shape(B, H, N, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_PTR(V); SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(workspace);
+  if (workspace_bytes < sage::quantize_v_workspace(B * H, N, d)) return SAGE_ERR_WORKSPACE;
+  sage::QuantVArgs a;
+  a.V = V; a.is_bf16 = in_dtype == SAGE_BF16; a.BH = B * H; a.N = N; a.d = d;
+  a.v_codes = v_codes; a.v_scale = v_scale; a.workspace = workspace;
+  (void)hipGetLastError();
+  sage::launch_quantize_v(a, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sage_attn_fwd(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                  const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
+                  int blk_q, int blk_k, int causal, float sm_scale, void* stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
+                     causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream);
+}
+
+int sage_attn_fwd_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                       const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
+                       int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump,
+                       uint8_t* p_dump, void* stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
+                     causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Fused quantized attention forward for gfx950 (CDNA4).
+//
+// One workgroup = 128 query rows of one head (4 waves x 32 rows); KV tiles of
+// 64 keys are staged in LDS and visited in ascending order.
+//
+// Per wave and KV tile:
+//   S^T[64 keys x 32 queries] = K_tile . Q^T          2 x (d/32) v_mfma_i32_32x32x32_i8
+//   (transposed so that each lane holds one query row: lane l owns query l%32
+//    and 32 of the 64 keys; lanes l and l^32 share a row)
+//   row max on the int32 scores, dequantisation c2 = dQ*dK*sm_scale*log2e,
+//   P~ = X2(S*c2 - (m' - 8)) on the VALU, packed to FP8 e4m3 in registers
+//   O_blk^T[32 ch x 32 q] = V^T_tile . P^T              d/32 v_mfma_scale_f32_32x32x64_f8f6f4
+//   O_acc = fma(alpha, O_acc, O_blk)                   (outer fp32 level)
+//
+// Register layout chaining: the int8 MFMA output places key
+// 32*g + 16*h + v in register v of half h of lane group g = lane/32 when K
+// row sigma_h(m) feeds MFMA row m (sigma is applied when K is staged into LDS,
+// "MFMA order").  Packing those 32 values in register order gives exactly the
+// FP8 B operand whose byte b of lane group g is key 32*g + b, which pairs with
+// byte b of the V^T operand = the 32 contiguous channel-major codes of keys
+// 32*g .. 32*g+31.  No register shuffles are needed between the two MFMAs.
+#include "common.h"
+#include "launch.h"
+
+namespace sage {
+
+struct AttnK {
+  const int8_t* q_codes;
+  const float* q_scale;
+  const int8_t* k_codes;
+  const float* k_scale;
+  const uint8_t* v_codes;
+  const float* v_scale;
+  void* O;
+  int N, nqt, nbq, blk_q;
+  float s2;
+  const int32_t* sel;
+  int n_sel;
+  int32_t* s_dump;
+  uint8_t* p_dump;
+};
+
+// LDS row of key kappa (0..63) of a KV tile: 32*h + m with m the MFMA row
+// m = 8*(v/4) + 4*g + v%4 for kappa = 32*g + 16*h + v.
+__device__ __forceinline__ int k_lds_row(int kap) {
+  const int g = kap >> 5, h = (kap >> 4) & 1, v = kap & 15;
+  return 32 * h + 8 * (v >> 2) + 4 * g + (v & 3);
+}
+// 16-byte chunk swizzles (XOR of the chunk index) against LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int k_swz(int ell) { return D == 128 ? (ell & 7) : (ell & 3); }
+__device__ __forceinline__ int v_swz(int r) { return (r >> 1) & 3; }
+
+template <int OUT>
+__device__ __forceinline__ void store4(void* O, size_t idx, v4f v) {
+  if (OUT == 2) {
+    *(v4f*)((float*)O + idx) = v;
+  } else if (OUT == 1) {
+    unsigned u[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) u[e] = bf16_bits_rne(v[e]);
+    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
+    *(v2i*)((uint16_t*)O + idx) = w;
+  } else {
+    unsigned u[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) u[e] = f16_bits_rne(v[e]);
+    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
+    *(v2i*)((uint16_t*)O + idx) = w;
+  }
+}
+
+template <int D, bool CAUSAL, int OUT, bool DUMP>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
+  constexpr int KS = D / 32;   // k-steps of the int8 MFMA over d
+  constexpr int CT = D / 32;   // 32-channel tiles of the FP8 MFMA
+  __shared__ __attribute__((aligned(16))) int8_t sK[kKTile * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[D * kKTile];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, lg = lane >> 5;
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of (head, query tile) so one head's K/V stays in one L2.
+  const int G = gridDim.x, b = blockIdx.x;
+  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int bh = L / p.nqt;
+  int qt = L % p.nqt;
+  if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
+  const int N = p.N;
+  const int q0 = qt * kQTile, qrow0 = q0 + wave * 32, row = qrow0 + li;
+
+  int dump_idx = -1;
+  if (DUMP) {
+    for (int k = 0; k < p.n_sel; k++)
+      if (p.sel[k] == bh * p.nqt + qt) { dump_idx = k; break; }
+  }
+
+  v4i qreg[KS];
+  {
+    const int8_t* qp = p.q_codes + ((size_t)bh * N + row) * D + 16 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; s++) qreg[s] = *(const v4i*)(qp + 32 * s);
+  }
+  const float dq = p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
+
+  v16f oacc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
+  float m = -1e30f, lpart = 0.0f;
+  const v16f zero16 = {};
+
+  const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
+  const int8_t* gK = p.k_codes + (size_t)bh * N * D;
+  const uint8_t* gV = p.v_codes + (size_t)bh * N * D;
+  const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
+
+  for (int tt = 0; tt < ntiles; tt++) {
+    const int kv0 = tt * kKTile;
+    __syncthreads();
+    for (int c = tid; c < kKTile * D / 16; c += 256) {
+      const int kap = c / (D / 16), c16 = c % (D / 16);
+      const v4i val = *(const v4i*)(gK + (size_t)(kv0 + kap) * D + c16 * 16);
+      const int ell = k_lds_row(kap);
+      *(v4i*)(sK + ell * D + 16 * (c16 ^ k_swz<D>(ell))) = val;
+    }
+    for (int c = tid; c < D * kKTile / 16; c += 256) {
+      const int r = c >> 2, c16 = c & 3;
+      const v4i val = *(const v4i*)(gV + (size_t)tt * D * kKTile + r * kKTile + c16 * 16);
+      *(v4i*)(sV + r * kKTile + 16 * (c16 ^ v_swz(r))) = val;
+    }
+    __syncthreads();
+    if (CAUSAL && kv0 > qrow0 + 31) continue;   // every key of the tile is after every row of this wave
+
+    // ---- S^T = K . Q^T (int32) ----
+    v16i acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      const int e0 = li, e1 = 32 + li;
+      const v4i a0 = *(const v4i*)(sK + e0 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e0)));
+      const v4i a1 = *(const v4i*)(sK + e1 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e1)));
+      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[s], acc1, 0, 0, 0);
+    }
+    const int keyb = kv0 + 32 * lg;   // acc0[v] is key keyb + v, acc1[v] is key keyb + 16 + v
+    if (DUMP && dump_idx >= 0) {
+      int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+#pragma unroll
+      for (int v = 0; v < 16; v++) { sd[v] = acc0[v]; sd[16 + v] = acc1[v]; }
+    }
+    const bool diag = CAUSAL && (kv0 + kKTile - 1 > qrow0);
+    if (diag) {
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        if (keyb + v > row) acc0[v] = INT32_MIN;
+        if (keyb + 16 + v > row) acc1[v] = INT32_MIN;
+      }
+    }
+    // ---- online softmax state ----
+    int smax = INT32_MIN;
+#pragma unroll
+    for (int v = 0; v < 16; v++) smax = max(smax, max(acc0[v], acc1[v]));
+    smax = pair_max_i32(smax);
+    const float c2 = (dq * kscale[tt]) * p.s2;
+    float ustar = (float)smax * c2;
+    if (CAUSAL && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
+    const float mnew = fmaxf(m, ustar);
+    const float mm = mnew - 8.0f;
+    const float alpha = (tt == 0) ? 0.0f : exp2_softmax(m - mnew);
+
+    // ---- P~ (fp32) -> FP8 B operand ----
+    float rs = 0.0f;
+    v8i pb;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int sv = h == 0 ? acc0[4 * q + e] : acc1[4 * q + e];
+          float t = exp2_softmax(__builtin_fmaf((float)sv, c2, -mm));
+          if (diag && keyb + 16 * h + 4 * q + e > row) t = 0.0f;
+          pv[e] = t;
+          rs += t;
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+        pb[4 * h + q] = w;
+      }
+    }
+    if (DUMP && dump_idx >= 0) {
+      uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+#pragma unroll
+      for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
+    }
+
+    // ---- O_blk^T = V^T . P^T (FP8 inner block), O_acc = alpha*O_acc + O_blk ----
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) {
+      const int r = 32 * ct + li;
+      const v4i v0 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg) ^ v_swz(r)));
+      const v4i v1 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg + 1) ^ v_swz(r)));
+      const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const v16f ob = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, zero16, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int e = 0; e < 16; e++) oacc[ct][e] = __builtin_fmaf(alpha, oacc[ct][e], ob[e]);
+    }
+    lpart = __builtin_fmaf(alpha, lpart, rs);
+    m = mnew;
+  }
+
+  // ---- epilogue: O = O_acc * v_scale / l ----
+  const float lt = pair_sum_f32(lpart);
+  const float inv = 1.0f / lt;
+  const float* vs = p.v_scale + (size_t)bh * D;
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int c0 = 32 * ct + 8 * q + 4 * lg;   // O^T register 4q+e holds channel c0 + e
+      const v4f sc = *(const v4f*)(vs + c0);
+      v4f o;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[e] = oacc[ct][4 * q + e] * (sc[e] * inv);
+      store4<OUT>(p.O, ((size_t)bh * N + row) * D + c0, o);
+    }
+  }
+}
+
+template <int D, bool CAUSAL, int OUT>
+static void launch3(const AttnK& k, int grid, bool dump, hipStream_t st) {
+  if (dump) hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, OUT, true>), dim3(grid), dim3(256), 0, st, k);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, OUT, false>), dim3(grid), dim3(256), 0, st, k);
+}
+template <int D, bool CAUSAL>
+static void launch2(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
+  if (out == 2) launch3<D, CAUSAL, 2>(k, grid, dump, st);
+  else if (out == 1) launch3<D, CAUSAL, 1>(k, grid, dump, st);
+  else launch3<D, CAUSAL, 0>(k, grid, dump, st);
+}
+
+void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
+  AttnK k;
+  k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
+  k.v_codes = a.v_codes; k.v_scale = a.v_scale; k.O = a.O;
+  k.N = a.N; k.nqt = a.N / kQTile; k.nbq = a.N / a.blk_q; k.blk_q = a.blk_q; k.s2 = a.s2;
+  k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
+  const int grid = a.BH * k.nqt;
+  if (a.d == 128) {
+    if (a.causal) launch2<128, true>(k, grid, a.out_dtype, dump, st);
+    else launch2<128, false>(k, grid, a.out_dtype, dump, st);
+  } else {
+    if (a.causal) launch2<64, true>(k, grid, a.out_dtype, dump, st);
+    else launch2<64, false>(k, grid, a.out_dtype, dump, st);
+  }
+}
+
+}  // namespace sage

@@ -1,0 +1,55 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+struct QuantQKArgs {
+  const void* Q;
+  const void* K;
+  int is_bf16;
+  int BH, N, d, blk_q;
+  int8_t* q_codes;
+  float* q_scale;
+  int8_t* k_codes;
+  float* k_scale;
+  float* k_mean;
+  void* workspace;
+};
+
+struct QuantVArgs {
+  const void* V;
+  int is_bf16;
+  int BH, N, d;
+  uint8_t* v_codes;
+  float* v_scale;
+  void* workspace;
+};
+
+struct AttnArgs {
+  const int8_t* q_codes;
+  const float* q_scale;
+  const int8_t* k_codes;
+  const float* k_scale;
+  const uint8_t* v_codes;
+  const float* v_scale;
+  void* O;
+  int out_dtype;
+  int BH, N, d, blk_q, causal;
+  float s2;   // fp32(sm_scale * log2 e)
+  // dump (test) mode
+  const int32_t* sel;
+  int n_sel;
+  int32_t* s_dump;
+  uint8_t* p_dump;
+};
+
+void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st);
+void launch_quantize_v(const QuantVArgs& a, hipStream_t st);
+void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st);
+size_t quantize_qk_workspace(int BH, int N, int d);
+size_t quantize_v_workspace(int BH, int N, int d);
+
+}  // namespace sage

@@ -1,0 +1,200 @@
+"""Thin Python binding of libsage.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; PyTorch only
+provides device memory and the current HIP stream.  Importing this module
+fails loudly if the library has not been built: there is no fallback path.
+
+The ``sage_*`` functions mirror the C ABI in ``include/sage.h`` one to one and
+take raw integers (device pointers, sizes, stream handle).  The tensor-level
+helpers below them allocate outputs with torch and call the C entry points.
+"""
+import ctypes
+import math
+import os
+
+import torch  # loads torch's HIP runtime first, so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage.so")
+
+SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_MISALIGNED, SAGE_ERR_HIP, SAGE_ERR_WORKSPACE = range(6)
+SAGE_F16, SAGE_BF16, SAGE_F32 = 0, 1, 2
+#: exported symbols, in header order
+SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_bytes", "sage_quantize_qk",
+           "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_dump")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "(hipcc, gfx950); there is no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+_lib.sage_status_string.restype = ctypes.c_char_p
+_lib.sage_status_string.argtypes = [_I]
+_lib.sage_kv_tile.restype = _I
+_lib.sage_kv_tile.argtypes = []
+_lib.sage_quantize_qk_workspace_bytes.restype = _SZ
+_lib.sage_quantize_qk_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.sage_quantize_v_workspace_bytes.restype = _SZ
+_lib.sage_quantize_v_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.sage_quantize_qk.restype = _I
+_lib.sage_quantize_qk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.sage_quantize_v.restype = _I
+_lib.sage_quantize_v.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]
+_lib.sage_attn_fwd.restype = _I
+_lib.sage_attn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.sage_attn_fwd_dump.restype = _I
+_lib.sage_attn_fwd_dump.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _P]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(sage_status_string(status))
+
+
+def _check(status):
+    if status != SAGE_OK:
+        raise SageError(status)
+
+
+# ---------------------------------------------------------------- C ABI, 1:1
+def sage_status_string(status):
+    return _lib.sage_status_string(status).decode()
+
+
+def sage_kv_tile():
+    return _lib.sage_kv_tile()
+
+
+def sage_quantize_qk_workspace_bytes(B, H, N, d):
+    return _lib.sage_quantize_qk_workspace_bytes(B, H, N, d)
+
+
+def sage_quantize_v_workspace_bytes(B, H, N, d):
+    return _lib.sage_quantize_v_workspace_bytes(B, H, N, d)
+
+
+def sage_quantize_qk(Q, K, in_dtype, B, H, N, d, blk_q, blk_k, q_codes, q_scale, k_codes, k_scale, k_mean,
+                     workspace, workspace_bytes, stream):
+    return _lib.sage_quantize_qk(Q, K, in_dtype, B, H, N, d, blk_q, blk_k, q_codes, q_scale, k_codes, k_scale, k_mean,
+                                 workspace, workspace_bytes, stream)
+
+
+def sage_quantize_v(V, in_dtype, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes, stream):
+    return _lib.sage_quantize_v(V, in_dtype, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes, stream)
+
+
+def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
+                  causal, sm_scale, stream):
+    return _lib.sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q,
+                              blk_k, causal, sm_scale, stream)
+
+
+def sage_attn_fwd_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
+                       causal, sm_scale, sel, n_sel, s_dump, p_dump, stream):
+    return _lib.sage_attn_fwd_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d,
+                                   blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
+
+
+# ---------------------------------------------------------------- tensor helpers
+_DT = {torch.float16: SAGE_F16, torch.bfloat16: SAGE_BF16, torch.float32: SAGE_F32}
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _shape4(x):
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("expected a contiguous CUDA tensor [B, H, N, d]")
+    return x.shape
+
+
+def quantize_qk(Q, K, blk_q=128, blk_k=64, workspace=None, stream=None):
+    """INT8 per-block Q and smoothed K.  Returns a dict of device tensors."""
+    B, H, N, d = _shape4(Q)
+    if K.shape != Q.shape or K.dtype != Q.dtype:
+        raise ValueError("Q and K must have the same shape and dtype")
+    _shape4(K)
+    dev = Q.device
+    out = dict(q_codes=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, H, N // blk_q), dtype=torch.float32, device=dev),
+               k_codes=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, H, N // blk_k), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    wsb = sage_quantize_qk_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(sage_quantize_qk(_ptr(Q), _ptr(K), _DT.get(Q.dtype, -1), B, H, N, d, blk_q, blk_k, _ptr(out["q_codes"]),
+                            _ptr(out["q_scale"]), _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    out.update(blk_q=blk_q, blk_k=blk_k)
+    return out
+
+
+def quantize_v(V, workspace=None, stream=None):
+    """FP8 e4m3 V with per-channel scales.  Returns (v_codes, v_scale); v_codes
+    is in KV-tile channel-major order (see ``v_codes_to_natural``)."""
+    B, H, N, d = _shape4(V)
+    dev = V.device
+    v_codes = torch.empty((B, H, N // sage_kv_tile(), d, sage_kv_tile()), dtype=torch.uint8, device=dev)
+    v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    wsb = sage_quantize_v_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(sage_quantize_v(_ptr(V), _DT.get(V.dtype, -1), B, H, N, d, _ptr(v_codes), _ptr(v_scale), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return v_codes, v_scale
+
+
+def v_codes_to_natural(v_codes):
+    """[B, H, N/64, d, 64] tile layout -> [B, H, N, d] token-major (a view permutation)."""
+    B, H, T, d, kt = v_codes.shape
+    return v_codes.permute(0, 1, 2, 4, 3).reshape(B, H, T * kt, d)
+
+
+def default_sm_scale(d):
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=None, stream=None, dump=None):
+    """Attention on quantized operands.  ``qk`` from quantize_qk, ``v`` = (v_codes, v_scale).
+    ``dump`` = (sel int32 tensor, s_dump, p_dump) routes through sage_attn_fwd_dump."""
+    B, H, N, d = qk["q_codes"].shape
+    v_codes, v_scale = v
+    if sm_scale is None:
+        sm_scale = default_sm_scale(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=qk["q_codes"].device)
+    args = (_ptr(qk["q_codes"]), _ptr(qk["q_scale"]), _ptr(qk["k_codes"]), _ptr(qk["k_scale"]), _ptr(v_codes),
+            _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), B, H, N, d, qk["blk_q"], qk["blk_k"], int(bool(causal)),
+            float(sm_scale))
+    if dump is None:
+        _check(sage_attn_fwd(*args, _stream(stream)))
+    else:
+        sel, s_dump, p_dump = dump
+        _check(sage_attn_fwd_dump(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
+    return out
+
+
+def attention(q, k, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, out_dtype=None, stream=None):
+    """Drop-in quantized attention forward for [B, H, N, d] float16/bfloat16 inputs."""
+    qk = quantize_qk(q, k, blk_q, blk_k, stream=stream)
+    vq = quantize_v(v, stream=stream)
+    return attn_fwd(qk, vq, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or q.dtype, stream=stream)
+
+
+def loaded_hip_runtimes():
+    """Paths of libamdhip64 mapped into this process (must be exactly one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)

@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/sage.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_scaled_dot_amd import sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "sage.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sage_\w+)\s*\(", src, flags=re.M)
+
+
+def test_every_declared_symbol_is_exported():
+    names = _header_functions()
+    assert len(names) == 8 and set(names) == set(sage.SYMBOLS)
+    lib = ctypes.CDLL(sage.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_constants():
+    assert sage.sage_status_string(0) == "SAGE_OK"
+    for s in range(1, 6):
+        assert sage.sage_status_string(s).startswith("SAGE_ERR_")
+    assert sage.sage_kv_tile() == 64
+
+
+def test_workspace_sizes():
+    assert sage.sage_quantize_qk_workspace_bytes(1, 24, 32768, 128) == 24 * 128 * 128 * 8
+    assert sage.sage_quantize_v_workspace_bytes(1, 2, 256, 64) == (2 * 1 * 64 + 2 * 64) * 4
+    assert sage.sage_quantize_qk_workspace_bytes(1, 1, 100, 64) == 0   # unsupported N
+
+
+A = 4096  # a fake 16-byte aligned address; never dereferenced because validation fails first
+
+
+def _qk(**kw):
+    args = dict(Q=A, K=A, in_dtype=1, B=1, H=1, N=256, d=128, blk_q=128, blk_k=64, q_codes=A, q_scale=A,
+                k_codes=A, k_scale=A, k_mean=A, workspace=A, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return sage.sage_quantize_qk(**args)
+
+
+def _v(**kw):
+    args = dict(V=A, in_dtype=0, B=1, H=1, N=256, d=64, v_codes=A, v_scale=A, workspace=A, workspace_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return sage.sage_quantize_v(**args)
+
+
+def _attn(**kw):
+    args = dict(q_codes=A, q_scale=A, k_codes=A, k_scale=A, v_codes=A, v_scale=A, O=A, out_dtype=2, B=1, H=1, N=256,
+                d=128, blk_q=128, blk_k=64, causal=0, sm_scale=0.125, stream=None)
+    args.update(kw)
+    return sage.sage_attn_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), sage.SAGE_ERR_UNSUPPORTED), (dict(N=200), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(N=1 << 20), sage.SAGE_ERR_UNSUPPORTED), (dict(B=0), sage.SAGE_ERR_INVALID_ARG),
+    (dict(H=-1), sage.SAGE_ERR_INVALID_ARG), (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG),
+    (dict(in_dtype=7), sage.SAGE_ERR_INVALID_ARG), (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(blk_k=128), sage.SAGE_ERR_UNSUPPORTED), (dict(Q=None), sage.SAGE_ERR_INVALID_ARG),
+    (dict(k_mean=None), sage.SAGE_ERR_INVALID_ARG), (dict(K=A + 8), sage.SAGE_ERR_MISALIGNED),
+    (dict(workspace=None), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=16), sage.SAGE_ERR_WORKSPACE),
+])
+def test_quantize_qk_rejects(kw, status):
+    assert _qk(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=32), sage.SAGE_ERR_UNSUPPORTED), (dict(N=64), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(V=None), sage.SAGE_ERR_INVALID_ARG), (dict(v_codes=A + 4), sage.SAGE_ERR_MISALIGNED),
+    (dict(in_dtype=-1), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=0), sage.SAGE_ERR_WORKSPACE),
+])
+def test_quantize_v_rejects(kw, status):
+    assert _v(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=256), sage.SAGE_ERR_UNSUPPORTED), (dict(N=192), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(blk_q=256), sage.SAGE_ERR_UNSUPPORTED), (dict(blk_k=32), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), sage.SAGE_ERR_INVALID_ARG), (dict(causal=2), sage.SAGE_ERR_INVALID_ARG),
+    (dict(sm_scale=0.0), sage.SAGE_ERR_INVALID_ARG), (dict(sm_scale=-1.0), sage.SAGE_ERR_INVALID_ARG),
+    (dict(sm_scale=float("inf")), sage.SAGE_ERR_INVALID_ARG), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
+    (dict(O=None), sage.SAGE_ERR_INVALID_ARG), (dict(v_scale=A + 2), sage.SAGE_ERR_MISALIGNED),
+    (dict(q_codes=None), sage.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_rejects(kw, status):
+    assert _attn(**kw) == status
+
+
+def test_attn_fwd_dump_rejects_bad_selection():
+    r = sage.sage_attn_fwd_dump(A, A, A, A, A, A, A, 2, 1, 1, 256, 128, 128, 64, 0, 0.125, None, 1, A, A, None)
+    assert r == sage.SAGE_ERR_INVALID_ARG
+    r = sage.sage_attn_fwd_dump(A, A, A, A, A, A, A, 2, 1, 1, 256, 128, 128, 64, 0, 0.125, A, -1, A, A, None)
+    assert r == sage.SAGE_ERR_INVALID_ARG
+
+
+def test_python_helpers_validate_shapes():
+    import torch
+    with pytest.raises(ValueError):
+        sage.quantize_qk(torch.zeros(2, 2), torch.zeros(2, 2))

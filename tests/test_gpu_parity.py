@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: bit-exact K means, INT8 Q/K codes and scales, FP8 V codes and scales,
+int32 QK^T tiles and FP8 codes of P~; fp32 O within max-abs 2e-3 of the
+oracle; cosine similarity to fp64 exact attention >= 0.995.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from quantized_scaled_dot_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+S_SENTINEL = np.iinfo(np.int32).min
+P_SENTINEL = 0x7F
+
+
+def _sage():
+    from quantized_scaled_dot_amd import sage
+    return sage
+
+
+def run_gpu(w, Q, K, V, out_dtype=torch.float32, dump_tiles=(), check_runtime=True):
+    sage = _sage()
+    if check_runtime:
+        assert len(sage.loaded_hip_runtimes()) == 1, sage.loaded_hip_runtimes()
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    qk = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k)
+    vq = sage.quantize_v(Vd)
+    dump = None
+    if dump_tiles:
+        sel = torch.tensor(list(dump_tiles), dtype=torch.int32, device=dev)
+        s_d = torch.full((len(dump_tiles), 128, w.N), S_SENTINEL, dtype=torch.int32, device=dev)
+        p_d = torch.full((len(dump_tiles), 128, w.N), P_SENTINEL, dtype=torch.uint8, device=dev)
+        dump = (sel, s_d, p_d)
+    O = sage.attn_fwd(qk, vq, causal=w.causal, sm_scale=w.sm_scale, out_dtype=out_dtype, dump=dump)
+    torch.cuda.synchronize()
+    res = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in qk.items()}
+    res["v_codes"] = sage.v_codes_to_natural(vq[0]).cpu().numpy()
+    res["v_codes_tiled"] = vq[0]
+    res["v_scale"] = vq[1].cpu().numpy()
+    res["O"] = O.float().cpu().numpy()
+    res["O_dev"] = O
+    res["qk_dev"], res["vq_dev"] = qk, vq
+    if dump:
+        res["s_dump"], res["p_dump"] = dump[1].cpu().numpy(), dump[2].cpu().numpy()
+    return res
+
+
+def run_oracle_quant(w, Q, K, V):
+    qk = orc.quantize_qk(synth.bits(Q), synth.bits(K), w.dtype_code, w.blk_q, w.blk_k)
+    vc, vs = orc.quantize_v(synth.bits(V), w.dtype_code)
+    return qk, vc, vs
+
+
+def check_quant_bit_exact(g, qk, vc, vs):
+    for key in ("k_mean", "q_scale", "k_scale"):
+        assert np.array_equal(g[key].view(np.uint32), qk[key].view(np.uint32)), key
+    for key in ("q_codes", "k_codes"):
+        if not np.array_equal(g[key], qk[key]):
+            bad = np.argwhere(g[key] != qk[key])
+            raise AssertionError(f"{key}: {len(bad)} mismatches, first at {bad[0]}")
+    assert np.array_equal(g["v_scale"].view(np.uint32), vs.view(np.uint32))
+    if not np.array_equal(g["v_codes"], vc):
+        bad = np.argwhere(g["v_codes"] != vc)
+        raise AssertionError(f"v_codes: {len(bad)} mismatches, first at {bad[0]}")
+
+
+def check_dump(w, g, qk, tiles):
+    nqt = w.N // 128
+    for k, tid in enumerate(tiles):
+        bh, qt = divmod(tid, nqt)
+        rows = bh * w.N + qt * 128 + np.arange(128)
+        s_ref = orc.qk_int32(qk["q_codes"], qk["k_codes"], rows)
+        s_got = g["s_dump"][k]
+        written = s_got != S_SENTINEL
+        i = qt * 128 + np.arange(128)[:, None]
+        j = np.arange(w.N)[None, :]
+        visible = (j <= i) if w.causal else np.ones_like(written)
+        assert written[visible].all(), "a visible score was not computed"
+        assert np.array_equal(s_got[written], s_ref[written]), "int32 QK^T mismatch"
+        yield rows, g["p_dump"][k], visible
+
+
+def cosine(a, b):
+    a = a.astype(np.float64).ravel()
+    b = b.astype(np.float64).ravel()
+    return float(a @ b / np.sqrt((a @ a) * (b @ b)))
+
+
+# ------------------------------------------------------------------ small cases: every row
+SMALL = {
+    "tiny-f16-256": dict(),
+    "causal-bf16-d128-N1024": dict(base="llm-prefill-4k-causal", B=1, H=2, N=1024),
+    "vit-f16-d64-N512": dict(base="vit-2k-f16", B=2, H=2, N=512),
+    "outliers-causal-N2048": dict(base="long-prefill-128k-causal", H=2, N=2048),
+    "blkq64-causal-f16-N384": dict(base="llm-prefill-4k-causal", B=1, H=3, N=384, blk_q=64, dtype="float16"),
+    "min-N128-causal-d64-bf16": dict(base="vit-2k-f16", B=2, H=1, N=128, causal=True, dtype="bfloat16"),
+    "noncausal-bf16-d128-blkq64": dict(base="video-dit-32k", H=2, N=768, blk_q=64),
+}
+
+
+def small_workload(name):
+    kw = dict(SMALL[name])
+    base = kw.pop("base", name)
+    return synth.WORKLOADS[base].with_(name=name, **kw)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name):
+    w = small_workload(name)
+    Q, K, V = synth.make_inputs(w)
+    nqt = w.N // 128
+    tiles = sorted({0, nqt - 1, (w.B * w.H - 1) * nqt + nqt // 2})
+    g = run_gpu(w, Q, K, V, dump_tiles=tiles)
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, want_p=True)
+    for rows, p_got, visible in check_dump(w, g, qk, tiles):
+        written = p_got != P_SENTINEL
+        assert written[visible].all()
+        assert np.array_equal(p_got[written], P_ref[rows][written]), "FP8 P~ code mismatch"
+    O = g["O"].reshape(-1, w.d)
+    err = np.abs(O - O_ref)
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {np.unravel_index(err.argmax(), err.shape)}"
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
+    assert cosine(O, ex) >= 0.995
+
+
+def test_output_dtypes_round_the_fp32_result():
+    w = small_workload("causal-bf16-d128-N1024")
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu(w, Q, K, V)
+    sage = _sage()
+    ref = torch.from_numpy(g["O"])
+    for dt in (torch.bfloat16, torch.float16):
+        o = sage.attn_fwd(g["qk_dev"], g["vq_dev"], causal=w.causal, sm_scale=w.sm_scale, out_dtype=dt)
+        torch.cuda.synchronize()
+        got, exp = o.cpu(), ref.to(dt)
+        bad = (got.view(torch.int16) != exp.view(torch.int16)).nonzero()
+        if len(bad):
+            i = tuple(bad[0].tolist())
+            raise AssertionError(f"{dt}: {len(bad)} mismatches; first {i}: fp32 {ref[i].item()!r} "
+                                 f"got {got[i].item()!r} expected {exp[i].item()!r}")
+
+
+def test_repeat_runs_are_bit_identical():
+    w = small_workload("outliers-causal-N2048")
+    Q, K, V = synth.make_inputs(w)
+    g1 = run_gpu(w, Q, K, V)
+    g2 = run_gpu(w, Q, K, V)
+    for key in ("q_codes", "k_codes", "v_codes", "k_mean", "q_scale", "k_scale", "v_scale", "O"):
+        assert np.array_equal(g1[key], g2[key]), key
+
+
+def test_drop_in_attention_matches_separate_calls():
+    sage = _sage()
+    w = small_workload("vit-f16-d64-N512")
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu(w, Q, K, V, out_dtype=torch.float16)
+    o = sage.attention(Q.cuda(), K.cuda(), V.cuda(), causal=w.causal, sm_scale=w.sm_scale, blk_q=w.blk_q)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16 and torch.equal(o.cpu(), g["O_dev"].cpu())
+
+
+# ------------------------------------------------------------------ edge cases
+def _edge_inputs(w, kind):
+    Q, K, V = synth.make_inputs(w)
+    if kind == "zero-q":
+        Q = torch.zeros_like(Q)
+    elif kind == "constant-k":
+        K = torch.ones_like(K) * 3
+    elif kind == "zero-v-channel":
+        V = V.clone()
+        V[..., 5] = 0
+    elif kind == "large":
+        Q, K, V = Q * 64, K * 64, V * 1000
+    elif kind == "tiny":
+        Q, K, V = Q * 2 ** -10, K * 2 ** -10, V * 2 ** -10
+    elif kind == "zero-q-block":
+        Q = Q.clone()
+        Q[:, :, 128:256] = 0
+    return Q, K, V
+
+
+@pytest.mark.parametrize("kind", ["zero-q", "constant-k", "zero-v-channel", "large", "tiny", "zero-q-block"])
+def test_edge_cases(kind):
+    w = small_workload("blkq64-causal-f16-N384") if kind != "large" else small_workload("causal-bf16-d128-N1024")
+    Q, K, V = _edge_inputs(w, kind)
+    g = run_gpu(w, Q, K, V, dump_tiles=(1,))
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, want_p=True)
+    for rows, p_got, visible in check_dump(w, g, qk, (1,)):
+        written = p_got != P_SENTINEL
+        assert np.array_equal(p_got[written], P_ref[rows][written])
+    O = g["O"].reshape(-1, w.d)
+    tol = O_TOL * (1000 if kind == "large" else 1)  # V scaled by 1000: same relative bar
+    assert np.abs(O - O_ref).max() <= tol
+    assert np.isfinite(O).all()
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+def _sample_rows(w, rng, n_rand=24):
+    BH, N = w.B * w.H, w.N
+    first = np.arange(16)                                   # early causal rows: few keys, big weights
+    last = (BH - 1) * N + N - 1 - np.arange(8)
+    rand = rng.integers(0, BH * N, n_rand)
+    return np.unique(np.concatenate([first, last, rand])).astype(np.int64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_full_size_workload(name):
+    w = synth.WORKLOADS[name]
+    Q, K, V = synth.make_inputs(w)
+    nqt = w.N // 128
+    tiles = (0, w.B * w.H * nqt - 1)
+    g = run_gpu(w, Q, K, V, dump_tiles=tiles)
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    rows = _sample_rows(w, np.random.default_rng(123))
+    dump_rows = np.concatenate([np.arange(128), (w.B * w.H - 1) * w.N + (nqt - 1) * 128 + np.arange(128)])
+    O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale,
+                                 rows=np.concatenate([rows, dump_rows]), want_p=True)
+    for k, (r, p_got, visible) in enumerate(check_dump(w, g, qk, tiles)):
+        written = p_got != P_SENTINEL
+        ref = P_ref[len(rows) + 128 * k: len(rows) + 128 * (k + 1)]
+        assert np.array_equal(p_got[written], ref[written])
+    O = g["O"].reshape(-1, w.d)
+    err = np.abs(O[rows] - O_ref[:len(rows)])
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
+    assert cosine(O[rows], ex) >= 0.995
