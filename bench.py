@@ -1,0 +1,184 @@
+"""Benchmark of the quantized attention forward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input: quantize Q and K
+(K smoothing, INT8 per block), quantize V (FP8, per-channel scales), then the
+fused attention kernel.  Inputs are resident in HBM before timing starts.
+
+Metric: attention TOPS = 4*B*H*N^2*d / t (halved for causal) with t the
+wall-clock time of one step.  The JSON line also carries the attention
+kernel's own rate against the dense INT8/FP8 matrix-core peak (roofline) and
+the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from quantized_scaled_dot_amd import synth  # noqa: E402
+
+MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 = dense FP8 = 5.0 P op/s
+DEFAULT_WORKLOAD = "video-dit-32k"
+METRIC = "attention TOPS (4·B·H·N²·d/t) at 1 MI355X; % of INT8/FP8 MFMA peak"
+KERNEL_SOURCES = ("quantized_scaled_dot_amd/csrc/attn.hip", "quantized_scaled_dot_amd/csrc/common.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_kernel.{workload}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, Q, K, V, budget_s=20.0):
+    """The oracle as it stands, on the host cores: full quantization of Q, K, V,
+    then attention for a bounded sample of query rows; extrapolated to the step."""
+    from oracle import oracle as orc
+
+    qb, kb, vb = synth.bits(Q), synth.bits(K), synth.bits(V)
+    t0 = time.perf_counter()
+    qk = orc.quantize_qk(qb, kb, w.dtype_code, w.blk_q, w.blk_k)
+    vc, vs = orc.quantize_v(vb, w.dtype_code)
+    t_quant = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    total_rows = w.B * w.H * w.N
+    # calibrate with a small batch, then size the sample to the budget
+    rows = rng.choice(total_rows, 64, replace=False).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
+    per_row = (time.perf_counter() - t0) / len(rows)
+    n = int(max(64, min(total_rows, (budget_s - t_quant) / max(per_row, 1e-9))))
+    rows = rng.choice(total_rows, n, replace=False).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
+    t_rows = time.perf_counter() - t0
+    t_step = t_quant + t_rows * total_rows / n
+    return {"value": round(w.ops / t_step / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"oracle quantization of all of Q, K, V ({t_quant:.1f} s) plus attention for {n} random query "
+                      f"rows of {total_rows} ({t_rows:.1f} s), extrapolated linearly to the full step "
+                      f"({t_step:.0f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (scale reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path shards over (batch, head) with no "
+              "communication, and this build runs and reports the single-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    from quantized_scaled_dot_amd import sage
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    if args.pmc_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
+
+    B, H, N, d = w.B, w.H, w.N, w.d
+    ws_qk = torch.empty(max(sage.sage_quantize_qk_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(max(sage.sage_quantize_v_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, N, d), dtype=w.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
+        v = sage.quantize_v(Vd, workspace=ws_v)
+        if ev is not None:
+            ev[0].record(stream)
+        sage.attn_fwd(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = t * 1e3 / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    value = w.ops / (ms_step * 1e-3) / 1e12
+    attn_tops = w.ops / (attn_avg * 1e-3) / 1e12
+    log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel avg {attn_avg:.3f} ms "
+        f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
+        f"{100 * attn_tops / MFMA_PEAK_TOPS:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)...")
+        cpu = cpu_baseline(w, Q, K, V, budget_s=args.cpu_budget)
+        log(f"[bench] CPU oracle: {cpu}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+fp8 (fp32 softmax)", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "in_dtype": w.dtype,
+                   "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_tile": sage.sage_kv_tile(), "parallelism": "none (1 GPU)"},
+        "attn_kernel_ms": round(attn_avg, 4),
+        "attn_kernel_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),
+        "attn_tops": round(attn_tops, 3),
+        "frac_of_mfma_peak_step": round(value / MFMA_PEAK_TOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 3),
+                     "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / MFMA_PEAK_TOPS, 4),
+                     "traffic": measured_traffic(w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
