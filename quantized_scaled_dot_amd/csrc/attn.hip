@@ -9,8 +9,10 @@
 //    and 32 of the 64 keys; lanes l and l^32 share a row)
 //   row max on the int32 scores, dequantisation c2 = dQ*dK*sm_scale*log2e,
 //   P~ = X2(S*c2 - (m' - 8)) on the VALU, packed to FP8 e4m3 in registers
-//   O_blk^T[32 ch x 32 q] = V^T_tile . P^T              d/32 v_mfma_scale_f32_32x32x64_f8f6f4
-//   O_acc = fma(alpha, O_acc, O_blk)                   (outer fp32 level)
+//   O_acc^T[32 ch x 32 q] += V^T_tile . P^T             d/32 v_mfma_scale_f32_32x32x64_f8f6f4
+//   (inner level: the instruction's 64-product block sum; outer level: the
+//    exact fp32 accumulate into its C operand; O_acc is rescaled by alpha
+//    first whenever a row's running max grew)
 //
 // Register layout chaining: the int8 MFMA output places key
 // 32*g + 16*h + v in register v of half h of lane group g = lane/32 when K
@@ -109,7 +111,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
 #pragma unroll
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
-  const v16f zero16 = {};
 
   const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
   const int8_t* gK = p.k_codes + (size_t)bh * N * D;
@@ -160,14 +161,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
     // ---- online softmax state ----
     int smax = INT32_MIN;
 #pragma unroll
-    for (int v = 0; v < 16; v++) smax = max(smax, max(acc0[v], acc1[v]));
+    for (int v = 0; v < 16; v++) smax = max(max(smax, acc0[v]), acc1[v]);   // v_max3_i32 chain
     smax = pair_max_i32(smax);
     const float c2 = (dq * kscale[tt]) * p.s2;
     float ustar = (float)smax * c2;
     if (CAUSAL && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
     const float mnew = fmaxf(m, ustar);
     const float mm = mnew - 8.0f;
-    const float alpha = (tt == 0) ? 0.0f : exp2_softmax(m - mnew);
+    // Rescale the running state only when some row of this wave got a larger
+    // max (alpha = X2(0) = 1 exactly for the others); on the first tile the
+    // state is still zero.
+    float alpha = 1.0f;
+    if (tt > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
+      alpha = exp2_softmax(m - mnew);
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
+    }
 
     // ---- P~ (fp32) -> FP8 B operand ----
     float rs = 0.0f;
@@ -196,16 +207,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
       for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
     }
 
-    // ---- O_blk^T = V^T . P^T (FP8 inner block), O_acc = alpha*O_acc + O_blk ----
+    // ---- two-level P~V: the matrix core sums the 64 FP8 products of this KV
+    // tile (inner level) and adds that block sum into the fp32 accumulator
+    // O_acc passed as its C operand (outer level; the C addition is an fp32
+    // add outside the instruction's product-alignment window) ----
 #pragma unroll
     for (int ct = 0; ct < CT; ct++) {
       const int r = 32 * ct + li;
       const v4i v0 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg) ^ v_swz(r)));
       const v4i v1 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg + 1) ^ v_swz(r)));
       const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      const v16f ob = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, zero16, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int e = 0; e < 16; e++) oacc[ct][e] = __builtin_fmaf(alpha, oacc[ct][e], ob[e]);
+      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
     }
     lpart = __builtin_fmaf(alpha, lpart, rs);
     m = mnew;
