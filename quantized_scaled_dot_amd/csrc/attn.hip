@@ -48,10 +48,15 @@ __device__ __forceinline__ int k_lds_row(int kap) {
   const int g = kap >> 5, h = (kap >> 4) & 1, v = kap & 15;
   return 32 * h + 8 * (v >> 2) + 4 * g + (v & 3);
 }
-// 16-byte chunk swizzles (XOR of the chunk index) against LDS bank conflicts.
+// XOR swizzles of the 16-byte chunk index within an LDS row.  The matrix-core
+// operand reads (ds_read_b128) touch one chunk of 8 or 16 consecutive rows;
+// these maps give those rows distinct banks whether the LDS serves 8 lanes
+// (128 bytes) or 16 lanes (256 bytes) per cycle.
 template <int D>
-__device__ __forceinline__ int k_swz(int ell) { return D == 128 ? (ell & 7) : (ell & 3); }
-__device__ __forceinline__ int v_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int k_swz(int ell) {
+  return D == 128 ? (((ell >> 1) & 7) ^ ((ell & 1) << 2)) : (((ell >> 1) ^ (ell >> 3)) & 3);
+}
+__device__ __forceinline__ int v_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <int OUT>
 __device__ __forceinline__ void store4(void* O, size_t idx, v4f v) {
@@ -72,12 +77,20 @@ __device__ __forceinline__ void store4(void* O, size_t idx, v4f v) {
   }
 }
 
+// Buffer resource for raw 16-byte loads of one head's codes (out-of-range
+// offsets read zero; every offset used here is in range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int D, bool CAUSAL, int OUT, bool DUMP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
-  constexpr int KS = D / 32;   // k-steps of the int8 MFMA over d
-  constexpr int CT = D / 32;   // 32-channel tiles of the FP8 MFMA
-  __shared__ __attribute__((aligned(16))) int8_t sK[kKTile * D];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[D * kKTile];
+  constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
+  constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
+  constexpr int TILE = kKTile * D;             // bytes of one K tile = one V tile
+  constexpr int CPT = TILE / 16 / 256;         // 16-byte chunks per thread per tile (2 or 1)
+  __shared__ __attribute__((aligned(16))) int8_t sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, lg = lane >> 5;
@@ -105,122 +118,150 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnK p) {
   }
   const float dq = p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
 
+  // ---- staging: every thread moves CPT 16-byte chunks of each tile ----
+  // K and V tiles are contiguous TILE-byte blocks in HBM (K: 64 rows of d
+  // codes; V: d rows of 64 codes).  Chunk c of the K tile is key c/(d/16),
+  // chunk c%(d/16); chunk c of the V tile is channel c/4, chunk c%4.  The
+  // global offsets and LDS destinations are fixed per thread; only the tile
+  // offset (a scalar) changes from tile to tile.
+  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bh * N * D, (uint32_t)(N * D));
+  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bh * N * D, (uint32_t)(N * D));
+  int k_dst[CPT], v_dst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; i++) {
+    const int c = tid + 256 * i;
+    const int kap = c / (D / 16), c16 = c % (D / 16);
+    const int ell = k_lds_row(kap);
+    k_dst[i] = ell * D + 16 * (c16 ^ k_swz<D>(ell));
+    const int r = c >> 2, v16 = c & 3;
+    v_dst[i] = r * kKTile + 16 * (v16 ^ v_swz(r));
+  }
+  v4i stK[CPT], stV[CPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+      stK[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rK, (tid + 256 * i) * 16, t * TILE, 0));
+      stV[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rV, (tid + 256 * i) * 16, t * TILE, 0));
+    }
+  };
+  auto deposit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+      *(v4i*)(&sK[buf][k_dst[i]]) = stK[i];
+      *(v4i*)(&sV[buf][v_dst[i]]) = stV[i];
+    }
+  };
+
   v16f oacc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++)
 #pragma unroll
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
+  v8i pb = {};
 
   const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
-  const int8_t* gK = p.k_codes + (size_t)bh * N * D;
-  const uint8_t* gV = p.v_codes + (size_t)bh * N * D;
   const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
 
+  fetch(0);
+  deposit(0);
   for (int tt = 0; tt < ntiles; tt++) {
-    const int kv0 = tt * kKTile;
-    __syncthreads();
-    for (int c = tid; c < kKTile * D / 16; c += 256) {
-      const int kap = c / (D / 16), c16 = c % (D / 16);
-      const v4i val = *(const v4i*)(gK + (size_t)(kv0 + kap) * D + c16 * 16);
-      const int ell = k_lds_row(kap);
-      *(v4i*)(sK + ell * D + 16 * (c16 ^ k_swz<D>(ell))) = val;
-    }
-    for (int c = tid; c < D * kKTile / 16; c += 256) {
-      const int r = c >> 2, c16 = c & 3;
-      const v4i val = *(const v4i*)(gV + (size_t)tt * D * kKTile + r * kKTile + c16 * 16);
-      *(v4i*)(sV + r * kKTile + 16 * (c16 ^ v_swz(r))) = val;
-    }
-    __syncthreads();
-    if (CAUSAL && kv0 > qrow0 + 31) continue;   // every key of the tile is after every row of this wave
+    const int kv0 = tt * kKTile, buf = tt & 1;
+    __syncthreads();                            // tile tt staged; tile tt-1 fully consumed
+    const bool more = tt + 1 < ntiles;
+    if (more) fetch(tt + 1);                    // in flight while tile tt is computed
+    const int8_t* sKb = sK[buf];
+    const uint8_t* sVb = sV[buf];
 
-    // ---- S^T = K . Q^T (int32) ----
-    v16i acc0 = {}, acc1 = {};
+    // every key of the tile is after every row of this wave: nothing to do
+    if (!(CAUSAL && kv0 > qrow0 + 31)) {
+      // ---- S^T = K . Q^T (int32) ----
+      v16i acc0 = {}, acc1 = {};
 #pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const int e0 = li, e1 = 32 + li;
-      const v4i a0 = *(const v4i*)(sK + e0 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e0)));
-      const v4i a1 = *(const v4i*)(sK + e1 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e1)));
-      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[s], acc1, 0, 0, 0);
-    }
-    const int keyb = kv0 + 32 * lg;   // acc0[v] is key keyb + v, acc1[v] is key keyb + 16 + v
-    if (DUMP && dump_idx >= 0) {
-      int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
-#pragma unroll
-      for (int v = 0; v < 16; v++) { sd[v] = acc0[v]; sd[16 + v] = acc1[v]; }
-    }
-    const bool diag = CAUSAL && (kv0 + kKTile - 1 > qrow0);
-    if (diag) {
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        if (keyb + v > row) acc0[v] = INT32_MIN;
-        if (keyb + 16 + v > row) acc1[v] = INT32_MIN;
+      for (int s = 0; s < KS; s++) {
+        const int e0 = li, e1 = 32 + li;
+        const v4i a0 = *(const v4i*)(sKb + e0 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e0)));
+        const v4i a1 = *(const v4i*)(sKb + e1 * D + 16 * ((2 * s + lg) ^ k_swz<D>(e1)));
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[s], acc1, 0, 0, 0);
       }
-    }
-    // ---- online softmax state ----
-    int smax = INT32_MIN;
+      const int keyb = kv0 + 32 * lg;   // acc0[v] is key keyb + v, acc1[v] is key keyb + 16 + v
+      if (DUMP && dump_idx >= 0) {
+        int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
 #pragma unroll
-    for (int v = 0; v < 16; v++) smax = max(max(smax, acc0[v]), acc1[v]);   // v_max3_i32 chain
-    smax = pair_max_i32(smax);
-    const float c2 = (dq * kscale[tt]) * p.s2;
-    float ustar = (float)smax * c2;
-    if (CAUSAL && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
-    const float mnew = fmaxf(m, ustar);
-    const float mm = mnew - 8.0f;
-    // Rescale the running state only when some row of this wave got a larger
-    // max (alpha = X2(0) = 1 exactly for the others); on the first tile the
-    // state is still zero.
-    float alpha = 1.0f;
-    if (tt > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
-      alpha = exp2_softmax(m - mnew);
+        for (int v = 0; v < 16; v++) { sd[v] = acc0[v]; sd[16 + v] = acc1[v]; }
+      }
+      const bool diag = CAUSAL && (kv0 + kKTile - 1 > qrow0);
+      if (diag) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
-    }
-
-    // ---- P~ (fp32) -> FP8 B operand ----
-    float rs = 0.0f;
-    v8i pb;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        float pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int sv = h == 0 ? acc0[4 * q + e] : acc1[4 * q + e];
-          float t = exp2_softmax(__builtin_fmaf((float)sv, c2, -mm));
-          if (diag && keyb + 16 * h + 4 * q + e > row) t = 0.0f;
-          pv[e] = t;
-          rs += t;
+        for (int v = 0; v < 16; v++) {
+          if (keyb + v > row) acc0[v] = INT32_MIN;
+          if (keyb + 16 + v > row) acc1[v] = INT32_MIN;
         }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
-        pb[4 * h + q] = w;
       }
-    }
-    if (DUMP && dump_idx >= 0) {
-      uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+      // ---- online softmax state ----
+      int smax = INT32_MIN;
 #pragma unroll
-      for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
-    }
+      for (int v = 0; v < 16; v++) smax = max(max(smax, acc0[v]), acc1[v]);   // v_max3_i32 chain
+      smax = pair_max_i32(smax);
+      const float c2 = (dq * kscale[tt]) * p.s2;
+      float ustar = (float)smax * c2;
+      if (CAUSAL && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
+      const float mnew = fmaxf(m, ustar);
+      const float mm = mnew - 8.0f;
+      // Rescale the running state only when some row of this wave got a larger
+      // max (alpha = X2(0) = 1 exactly for the others); on the first tile the
+      // state is still zero.
+      float alpha = 1.0f;
+      if (tt > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
+        alpha = exp2_softmax(m - mnew);
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
+      }
 
-    // ---- two-level P~V: the matrix core sums the 64 FP8 products of this KV
-    // tile (inner level) and adds that block sum into the fp32 accumulator
-    // O_acc passed as its C operand (outer level; the C addition is an fp32
-    // add outside the instruction's product-alignment window) ----
+      // ---- P~ (fp32) -> FP8 B operand, packed in place ----
+      float rs = 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < CT; ct++) {
-      const int r = 32 * ct + li;
-      const v4i v0 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg) ^ v_swz(r)));
-      const v4i v1 = *(const v4i*)(sV + r * kKTile + 16 * ((2 * lg + 1) ^ v_swz(r)));
-      const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
+      for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int sv = h == 0 ? acc0[4 * q + e] : acc1[4 * q + e];
+            float t = exp2_softmax(__builtin_fmaf((float)sv, c2, -mm));
+            if (diag && keyb + 16 * h + 4 * q + e > row) t = 0.0f;
+            pv[e] = t;
+            rs += t;
+          }
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pb[4 * h + q], false);
+          pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+        }
+      }
+      if (DUMP && dump_idx >= 0) {
+        uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+#pragma unroll
+        for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
+      }
+
+      // ---- two-level P~V: the matrix core sums the 64 FP8 products of this KV
+      // tile (inner level) and adds that block sum into the fp32 accumulator
+      // O_acc passed as its C operand (outer level; the C addition is an fp32
+      // add outside the instruction's product-alignment window) ----
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) {
+        const int r = 32 * ct + li;
+        const v4i v0 = *(const v4i*)(sVb + r * kKTile + 16 * ((2 * lg) ^ v_swz(r)));
+        const v4i v1 = *(const v4i*)(sVb + r * kKTile + 16 * ((2 * lg + 1) ^ v_swz(r)));
+        const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
+      }
+      lpart = __builtin_fmaf(alpha, lpart, rs);
+      m = mnew;
     }
-    lpart = __builtin_fmaf(alpha, lpart, rs);
-    m = mnew;
+    if (more) deposit(buf ^ 1);                 // other buffer: last read in iteration tt-1
   }
 
   // ---- epilogue: O = O_acc * v_scale / l ----
