@@ -47,27 +47,22 @@ __device__ __forceinline__ uint32_t f16_bits_rne(float x) {
   return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 16777216.0f);
 }
 
-// v_cvt_i32_f32: rounds toward zero and saturates out-of-range inputs to the
-// int32 limits (the hardware definition), unlike a C++ cast.
-__device__ __forceinline__ int cvt_i32_sat(float x) {
-  int r;
-  asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
 // Exponential of the fp32 online softmax: X2(t) = p(f) * 2^n, n = rint(t),
 // f = t - n (exact, |f| <= 1/2), p(f) = fma(fma(C2, f, C1), f, 1) with
 // C1 = 0x1.6a7dc6p-1, C2 = 0x1.fbcaa2p-3 (relative minimax of 2^f on
 // [-1/2, 1/2], constant term 1, continuous across the reduction boundary;
 // max relative error 2.9e-3).  Scaling by 2^n is v_ldexp_f32 (exact unless the
-// result is subnormal; 0 for n far below the fp32 range).  Six VALU ops and no
-// transcendental unit, and reproducible bit for bit on any IEEE fp32 machine.
+// result is subnormal; 0 once n is far below the fp32 range).  Six VALU ops,
+// no transcendental unit, reproducible bit for bit on any IEEE fp32 machine.
+// Requires |t| < 2^31 (the float-to-int conversion); exp2_softmax_clamped
+// accepts any finite t and returns the same values (X2(t) = 0 for t < -200).
 __device__ __forceinline__ float exp2_softmax(float t) {
   float n = __builtin_rintf(t);
   float f = t - n;
   float p = __builtin_fmaf(__builtin_fmaf(0x1.fbcaa2p-3f, f, 0x1.6a7dc6p-1f), f, 1.0f);
-  return __builtin_amdgcn_ldexpf(p, cvt_i32_sat(n));
+  return __builtin_amdgcn_ldexpf(p, (int)n);
 }
+__device__ __forceinline__ float exp2_softmax_clamped(float t) { return exp2_softmax(fmaxf(t, -256.0f)); }
 
 // Exchange with the lane 32 apart (same query row, other half of the keys /
 // channels): v_permlane32_swap returns {x[l], x[l^32]} in some order for every
