@@ -1,61 +1,18 @@
 // Quantization kernels (gfx950): K smoothing + INT8 per-block Q/K, FP8 V with
-// per-channel scales.  All passes are HBM-bound streams with 16-byte coalesced
-// loads; every reduction is order-free (int64 sums, max), so results do not
-// depend on launch geometry.
+// per-channel scales.  All passes stream HBM with 16-byte loads; every
+// reduction is order-free (exact integer sums, max), so results do not depend
+// on launch geometry.
+//
+// quantize_qk: pass 1 = {INT8 blocks of Q} + {per-chunk K channel sums} in one
+//              launch; finalize = per-head K mean; pass 2 = INT8 blocks of the
+//              smoothed K.
+// quantize_v:  pass 1 = per-chunk V channel maxima; finalize = per-channel
+//              scales and reciprocals; pass 2 = FP8 codes, transposed in
+//              registers into the KV-tile channel-major layout.
 #include "common.h"
 #include "launch.h"
 
 namespace sage {
-
-// ---------------------------------------------------------------------------
-// Per-channel fixed-point sums of K over one chunk of kStatChunk tokens:
-// s_c = sum_t trunc(clamp(k, +-2^20) * 2^24) (int64, exact).
-// Grid: (nchunk * BH).  Block: 256 threads, each owning 8 channels of every
-// RPP-th token of the chunk.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void k_colsum_kernel(const uint16_t* __restrict__ K, int is_bf16, int N,
-                                                        int nchunk, long long* __restrict__ partial) {
-  constexpr int TPR = D / 8;        // threads per token row
-  constexpr int RPP = 256 / TPR;    // token rows per pass
-  const int chunk = blockIdx.x % nchunk, bh = blockIdx.x / nchunk;
-  const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
-  const int n0 = chunk * kStatChunk;
-  const int nrows = min(kStatChunk, N - n0);
-  long long s[8];
-#pragma unroll
-  for (int e = 0; e < 8; e++) s[e] = 0;
-  const uint16_t* base = K + ((size_t)bh * N + n0) * D + cg * 8;
-  for (int r = r0; r < nrows; r += RPP) {
-    v4i raw = *(const v4i*)(base + (size_t)r * D);
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      float x = load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16);
-      x = fminf(fmaxf(x, -1048576.0f), 1048576.0f);
-      s[e] += (long long)(x * 16777216.0f);   // exact product; truncation toward zero
-    }
-  }
-  __shared__ long long red[RPP][D];
-#pragma unroll
-  for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = s[e];
-  __syncthreads();
-  for (int c = t; c < D; c += 256) {
-    long long tot = 0;
-    for (int r = 0; r < RPP; r++) tot += red[r][c];
-    partial[((size_t)bh * nchunk + chunk) * D + c] = tot;
-  }
-}
-
-// mean_c = fp32(fp64(sum_chunks s_c) * 2^-24 / N).  Grid: BH.  Block: 128.
-__global__ __launch_bounds__(128) void k_mean_kernel(const long long* __restrict__ partial, int nchunk, int N, int D,
-                                                      float* __restrict__ k_mean) {
-  const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    long long s = 0;
-    for (int ch = 0; ch < nchunk; ch++) s += partial[((size_t)bh * nchunk + ch) * D + c];
-    k_mean[(size_t)bh * D + c] = (float)(((double)s * 0x1p-24) / (double)N);
-  }
-}
 
 __device__ __forceinline__ float block_max_256(float a, float* red4) {
 #pragma unroll
@@ -65,20 +22,24 @@ __device__ __forceinline__ float block_max_256(float a, float* red4) {
   return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
 }
 
+__device__ __forceinline__ float half_of(const v4i& raw, int e, int is_bf16) {
+  return load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16);
+}
+
 // ---------------------------------------------------------------------------
 // Symmetric INT8 quantization of one block of BLK tokens x D channels:
 // a = max|x| (x = K - mean when SMOOTH), scale = a/127, r = 127/a,
 // code = rint(x * r) in [-127, 127]; a < 2^-120 gives scale 0 and zero codes.
-// Grid: (nblk * BH).  Block: 256 threads holding BLK*D/256 values each.
+// 256 threads hold BLK*D/256 values each.
 // ---------------------------------------------------------------------------
 template <int D, int BLK, bool SMOOTH>
-__global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ X, int is_bf16, int N,
-                                                           const float* __restrict__ mean, int8_t* __restrict__ codes,
-                                                           float* __restrict__ scale) {
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int is_bf16, int N,
+                                            const float* __restrict__ mean, int8_t* __restrict__ codes,
+                                            float* __restrict__ scale, int lin, float* red4) {
   constexpr int EPT = BLK * D / 256;   // values per thread
   constexpr int LPT = EPT / 8;         // 16-byte loads per thread
   const int nblk = N / BLK;
-  const int blk = blockIdx.x % nblk, bh = blockIdx.x / nblk;
+  const int blk = lin % nblk, bh = lin / nblk;
   const int t = threadIdx.x;
   const size_t off = ((size_t)bh * N + (size_t)blk * BLK) * D;
   const uint16_t* src = X + off;
@@ -98,13 +59,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
     }
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      float v = load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16);
+      float v = half_of(raw, e, is_bf16);
       if (SMOOTH) v = v - mu[e];
       x[l * 8 + e] = v;
       a = fmaxf(a, fabsf(v));
     }
   }
-  __shared__ float red4[4];
   a = block_max_256(a, red4);
   const bool zero = !(a >= 0x1p-120f);
   const float dl = zero ? 0.0f : a / 127.0f;
@@ -127,7 +87,86 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Per-channel maxima of |V| over one chunk of tokens.  Grid: (nchunk * BH).
+// Per-channel fixed-point sums of K over one chunk of kStatChunk tokens:
+// s_c = sum_t trunc(clamp(k, +-2^20) * 2^24).  Each term is an integer below
+// 2^44; a thread adds at most 32 of them in fp64 (exact below 2^53), converts
+// once to int64, and the threads' int64 sums are combined through LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_bf16, int N, int nchunk, int lin,
+                                         long long* __restrict__ partial, long long (*red)[D]) {
+  constexpr int TPR = D / 8;        // threads per token row
+  constexpr int RPP = 256 / TPR;    // token rows per pass
+  const int chunk = lin % nchunk, bh = lin / nchunk;
+  const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
+  const int n0 = chunk * kStatChunk;
+  const int nrows = min(kStatChunk, N - n0);
+  double s[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) s[e] = 0.0;
+  const uint16_t* base = K + ((size_t)bh * N + n0) * D + cg * 8;
+#pragma unroll 4
+  for (int r = r0; r < nrows; r += RPP) {
+    v4i raw = *(const v4i*)(base + (size_t)r * D);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float x = fminf(fmaxf(half_of(raw, e, is_bf16), -1048576.0f), 1048576.0f);
+      s[e] += (double)__builtin_truncf(x * 16777216.0f);   // exact product, exact sum
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = (long long)s[e];
+  __syncthreads();
+  for (int c = t; c < D; c += 256) {
+    long long tot = 0;
+    for (int r = 0; r < RPP; r++) tot += red[r][c];
+    partial[((size_t)bh * nchunk + chunk) * D + c] = tot;
+  }
+}
+
+// Pass 1 of quantize_qk.  Grid: BH*N/BLKQ Q blocks followed by BH*nchunk K chunks.
+template <int D, int BLKQ>
+__global__ __launch_bounds__(256) void qk_pass1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                        int is_bf16, int N, int nq, int nchunk,
+                                                        int8_t* __restrict__ q_codes, float* __restrict__ q_scale,
+                                                        long long* __restrict__ partial) {
+  __shared__ long long red[256 / (D / 8)][D];
+  __shared__ float red4[4];
+  const int b = blockIdx.x;
+  if (b < nq) quant_block<D, BLKQ, false>(Q, is_bf16, N, nullptr, q_codes, q_scale, b, red4);
+  else k_colsum<D>(K, is_bf16, N, nchunk, b - nq, partial, red);
+}
+
+// mean_c = fp32(fp64(sum_chunks s_c) * 2^-24 / N).  Grid: BH * D/16; a block
+// of 256 = 16 channels x 16 chunk lanes.
+__global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict__ partial, int nchunk, int N, int D,
+                                                      float* __restrict__ k_mean) {
+  const int ng = D / 16, g = blockIdx.x % ng, bh = blockIdx.x / ng;
+  const int cl = threadIdx.x & 15, j = threadIdx.x >> 4;
+  const int c = g * 16 + cl;
+  long long s = 0;
+  for (int ch = j; ch < nchunk; ch += 16) s += partial[((size_t)bh * nchunk + ch) * D + c];
+  __shared__ long long red[16][16];
+  red[j][cl] = s;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    long long tot = 0;
+    for (int k = 0; k < 16; k++) tot += red[k][threadIdx.x];
+    k_mean[(size_t)bh * D + g * 16 + threadIdx.x] = (float)(((double)tot * 0x1p-24) / (double)N);
+  }
+}
+
+// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: BH*N/64.
+template <int D>
+__global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, int N,
+                                                       const float* __restrict__ k_mean, int8_t* __restrict__ k_codes,
+                                                       float* __restrict__ k_scale) {
+  __shared__ float red4[4];
+  quant_block<D, 64, true>(K, is_bf16, N, k_mean, k_codes, k_scale, blockIdx.x, red4);
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel maxima of |V| over one chunk of tokens.  Grid: nchunk * BH.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ V, int is_bf16, int N, int nchunk,
@@ -142,11 +181,11 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
 #pragma unroll
   for (int e = 0; e < 8; e++) s[e] = 0.0f;
   const uint16_t* base = V + ((size_t)bh * N + n0) * D + cg * 8;
+#pragma unroll 4
   for (int r = r0; r < nrows; r += RPP) {
     v4i raw = *(const v4i*)(base + (size_t)r * D);
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-      s[e] = fmaxf(s[e], fabsf(load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16)));
+    for (int e = 0; e < 8; e++) s[e] = fmaxf(s[e], fabsf(half_of(raw, e, is_bf16)));
   }
   __shared__ float red[RPP][D];
 #pragma unroll
@@ -159,16 +198,25 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
   }
 }
 
-// scale_c = a_c / 448, r_c = 448 / a_c (0 and 0 when a_c < 2^-120).  Grid: BH.
-__global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ partial, int nchunk, int D,
+// scale_c = a_c / 448, r_c = 448 / a_c (0 and 0 when a_c < 2^-120).
+// Grid: BH * D/16; a block of 256 = 16 channels x 16 chunk lanes.
+__global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ partial, int nchunk, int D,
                                                        float* __restrict__ v_scale, float* __restrict__ v_recip) {
-  const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float a = 0.0f;
-    for (int ch = 0; ch < nchunk; ch++) a = fmaxf(a, partial[((size_t)bh * nchunk + ch) * D + c]);
-    const bool zero = !(a >= 0x1p-120f);
-    v_scale[(size_t)bh * D + c] = zero ? 0.0f : a / 448.0f;
-    v_recip[(size_t)bh * D + c] = zero ? 0.0f : 448.0f / a;
+  const int ng = D / 16, g = blockIdx.x % ng, bh = blockIdx.x / ng;
+  const int cl = threadIdx.x & 15, j = threadIdx.x >> 4;
+  const int c = g * 16 + cl;
+  float a = 0.0f;
+  for (int ch = j; ch < nchunk; ch += 16) a = fmaxf(a, partial[((size_t)bh * nchunk + ch) * D + c]);
+  __shared__ float red[16][16];
+  red[j][cl] = a;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float m = 0.0f;
+    for (int k = 0; k < 16; k++) m = fmaxf(m, red[k][threadIdx.x]);
+    const bool zero = !(m >= 0x1p-120f);
+    const size_t o = (size_t)bh * D + g * 16 + threadIdx.x;
+    v_scale[o] = zero ? 0.0f : m / 448.0f;
+    v_recip[o] = zero ? 0.0f : 448.0f / m;
   }
 }
 
@@ -176,64 +224,61 @@ __global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ 
 // FP8 codes of one KV tile of 64 tokens, written channel-major: the 64 codes of
 // channel c are contiguous (the layout the attention kernel stages into LDS).
 // code = e4m3(clamp(rn(v * r_c), +-448)), round to nearest even; zero channels
-// give code 0.  Grid: (N/64 * BH).  Transposed through LDS.
+// give code 0.  A thread converts 4 consecutive tokens x 8 channels and packs
+// each channel's 4 codes into one dword, so the transpose happens in registers
+// and every channel row is written as 16 consecutive dwords.
+// Grid: BH * N/64.  Block: 16 * D/8 threads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, int N,
-                                                       const float* __restrict__ v_recip, uint8_t* __restrict__ v_codes) {
-  constexpr int ROW = kKTile + 16;   // padded LDS row: 64 codes + 16 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t sT[D * ROW];
+__global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, int N,
+                                                              const float* __restrict__ v_recip,
+                                                              uint8_t* __restrict__ v_codes) {
   const int ntile = N / kKTile;
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
-  const int t = threadIdx.x;
-  const uint16_t* src = V + ((size_t)bh * N + (size_t)tile * kKTile) * D;
-  constexpr int CHUNKS = kKTile * D / 8;
-  for (int ch = t; ch < CHUNKS; ch += 256) {
-    const int tok = ch / (D / 8), c0 = (ch % (D / 8)) * 8;
-    v4i raw = *(const v4i*)(src + (size_t)ch * 8);
-    v4f r0 = *(const v4f*)(v_recip + (size_t)bh * D + c0);
-    v4f r1 = *(const v4f*)(v_recip + (size_t)bh * D + c0 + 4);
-    float y[8];
+  const int t = threadIdx.x, cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
+  const uint16_t* src = V + ((size_t)bh * N + (size_t)tile * kKTile + 4 * tg) * D + 8 * cg;
+  const v4f r0 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg);
+  const v4f r1 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg + 4);
+  float r[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const float r = e < 4 ? r0[e] : r1[e - 4];
-      float v = load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16) * r;
-      y[e] = fminf(fmaxf(v, -448.0f), 448.0f);
-    }
+  for (int e = 0; e < 4; e++) { r[e] = r0[e]; r[e + 4] = r1[e]; }
+  float y[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[e], y[e + 1], 0, false);
-      const float ra = e < 4 ? r0[e] : r1[e - 4], rb = e < 4 ? r0[e + 1] : r1[e - 3];
-      sT[(c0 + e) * ROW + tok] = ra == 0.0f ? 0 : (uint8_t)(pk & 0xFF);
-      sT[(c0 + e + 1) * ROW + tok] = rb == 0.0f ? 0 : (uint8_t)((pk >> 8) & 0xFF);
-    }
+  for (int i = 0; i < 4; i++) {
+    const v4i raw = *(const v4i*)(src + (size_t)i * D);
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[i][e] = fminf(fmaxf(half_of(raw, e, is_bf16) * r[e], -448.0f), 448.0f);
   }
-  __syncthreads();
-  uint8_t* dst = v_codes + ((size_t)bh * ntile + tile) * (size_t)(D * kKTile);
-  for (int ch = t; ch < D * (kKTile / 16); ch += 256) {
-    const int c = ch / (kKTile / 16), part = ch % (kKTile / 16);
-    *(v4i*)(dst + (size_t)c * kKTile + part * 16) = *(const v4i*)(sT + c * ROW + part * 16);
+  uint8_t* dst = v_codes + ((size_t)bh * ntile + tile) * (size_t)(D * kKTile) + (size_t)(8 * cg) * kKTile + 4 * tg;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][e], y[1][e], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][e], y[3][e], w, true);
+    *(int*)(dst + (size_t)e * kKTile) = r[e] == 0.0f ? 0 : w;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
+static inline int stat_chunks(int N) { return (N + kStatChunk - 1) / kStatChunk; }
+
 template <int D>
 static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
-  const int nchunk = (a.N + kStatChunk - 1) / kStatChunk;
+  const int nchunk = stat_chunks(a.N);
   long long* partial = (long long*)a.workspace;
-  hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(nchunk * a.BH), dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, a.N,
-                     nchunk, partial);
-  hipLaunchKernelGGL(k_mean_kernel, dim3(a.BH), dim3(128), 0, st, (const long long*)partial, nchunk, a.N, D, a.k_mean);
+  const int nq = a.BH * (a.N / a.blk_q);
+  const int grid1 = nq + a.BH * nchunk;
   if (a.blk_q == 128)
-    hipLaunchKernelGGL((quant_block_kernel<D, 128, false>), dim3(a.N / 128 * a.BH), dim3(256), 0, st,
-                       (const uint16_t*)a.Q, a.is_bf16, a.N, (const float*)nullptr, a.q_codes, a.q_scale);
+    hipLaunchKernelGGL((qk_pass1_kernel<D, 128>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
+                       (const uint16_t*)a.K, a.is_bf16, a.N, nq, nchunk, a.q_codes, a.q_scale, partial);
   else
-    hipLaunchKernelGGL((quant_block_kernel<D, 64, false>), dim3(a.N / 64 * a.BH), dim3(256), 0, st,
-                       (const uint16_t*)a.Q, a.is_bf16, a.N, (const float*)nullptr, a.q_codes, a.q_scale);
-  hipLaunchKernelGGL((quant_block_kernel<D, 64, true>), dim3(a.N / 64 * a.BH), dim3(256), 0, st, (const uint16_t*)a.K,
-                     a.is_bf16, a.N, (const float*)a.k_mean, a.k_codes, a.k_scale);
+    hipLaunchKernelGGL((qk_pass1_kernel<D, 64>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
+                       (const uint16_t*)a.K, a.is_bf16, a.N, nq, nchunk, a.q_codes, a.q_scale, partial);
+  hipLaunchKernelGGL(k_mean_kernel, dim3(a.BH * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.N,
+                     D, a.k_mean);
+  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(a.BH * (a.N / 64)), dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16,
+                     a.N, (const float*)a.k_mean, a.k_codes, a.k_scale);
 }
 
 void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {
@@ -243,14 +288,15 @@ void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {
 
 template <int D>
 static void launch_v_d(const QuantVArgs& a, hipStream_t st) {
-  const int nchunk = (a.N + kStatChunk - 1) / kStatChunk;
+  const int nchunk = stat_chunks(a.N);
   float* partial = (float*)a.workspace;
   float* recip = partial + (size_t)a.BH * nchunk * D;
   hipLaunchKernelGGL(v_colmax_kernel<D>, dim3(nchunk * a.BH), dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, a.N,
                      nchunk, partial);
-  hipLaunchKernelGGL(v_scale_kernel, dim3(a.BH), dim3(128), 0, st, (const float*)partial, nchunk, D, a.v_scale, recip);
-  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(a.N / kKTile * a.BH), dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16,
-                     a.N, (const float*)recip, a.v_codes);
+  hipLaunchKernelGGL(v_scale_kernel, dim3(a.BH * (D / 16)), dim3(256), 0, st, (const float*)partial, nchunk, D,
+                     a.v_scale, recip);
+  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(a.N / kKTile * a.BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
+                     a.is_bf16, a.N, (const float*)recip, a.v_codes);
 }
 
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {
@@ -259,12 +305,10 @@ void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {
 }
 
 size_t quantize_qk_workspace(int BH, int N, int d) {
-  const size_t nchunk = (size_t)(N + kStatChunk - 1) / kStatChunk;
-  return (size_t)BH * nchunk * d * sizeof(long long);
+  return (size_t)BH * stat_chunks(N) * d * sizeof(long long);
 }
 size_t quantize_v_workspace(int BH, int N, int d) {
-  const size_t nchunk = (size_t)(N + kStatChunk - 1) / kStatChunk;
-  return ((size_t)BH * nchunk * d + (size_t)BH * d) * sizeof(float);
+  return ((size_t)BH * stat_chunks(N) * d + (size_t)BH * d) * sizeof(float);
 }
 
 }  // namespace sage

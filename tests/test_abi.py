@@ -33,7 +33,7 @@ def test_status_strings_and_constants():
 
 
 def test_workspace_sizes():
-    assert sage.sage_quantize_qk_workspace_bytes(1, 24, 32768, 128) == 24 * 128 * 128 * 8
+    assert sage.sage_quantize_qk_workspace_bytes(1, 24, 32768, 128) == 24 * 128 * 128 * 8   # 256-token chunks
     assert sage.sage_quantize_v_workspace_bytes(1, 2, 256, 64) == (2 * 1 * 64 + 2 * 64) * 4
     assert sage.sage_quantize_qk_workspace_bytes(1, 1, 100, 64) == 0   # unsupported N
 
