@@ -167,9 +167,11 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
   const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
   const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
 
-  fetch(0);
-  deposit(0);
-  for (int tt = 0; tt < ntiles; tt++) {
+  // One KV tile.  DIAG: the tile may hold keys after some row of this
+  // workgroup (causal diagonal region): waves skip a tile entirely in their
+  // future and mask partially visible ones.  Interior tiles need neither.
+  auto tile_step = [&](const int tt, auto diag_tag) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     const int kv0 = tt * kKTile, buf = tt & 1;
     __syncthreads();                            // tile tt staged; tile tt-1 fully consumed
     const bool more = tt + 1 < ntiles;
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
     const uint8_t* sVb = sV[buf];
 
     // every key of the tile is after every row of this wave: nothing to do
-    if (!(CAUSAL && kv0 > qrow0 + 31)) {
+    if (!(DIAG && kv0 > qrow0 + 31)) {
       // ---- S^T = K . Q^T (int32) ----
       v16i acc0 = {}, acc1 = {};
 #pragma unroll
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
 #pragma unroll
         for (int v = 0; v < 16; v++) { sd[v] = acc0[v]; sd[16 + v] = acc1[v]; }
       }
-      const bool diag = CAUSAL && (kv0 + kKTile - 1 > qrow0);
+      const bool diag = DIAG && (kv0 + kKTile - 1 > qrow0);
       // ---- online softmax state (the max runs over visible keys only) ----
       int smax = INT32_MIN;
       if (diag) {
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
       smax = pair_max_i32(smax);
       const float c2 = (dq * kscale[tt]) * p.s2;
       float ustar = (float)smax * c2;
-      if (CAUSAL && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
+      if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
       const float mnew = fmaxf(m, ustar);
       const float mm = mnew - 8.0f;
       // Rescale the running state only when some row of this wave got a larger
@@ -228,8 +230,9 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
       // |S| <= 127^2 * d < 2^21, so every argument is inside +-2^30 when
       // c2 < 256 and |m' - 8| < 2^29 on all lanes: then the plain conversion
       // in X2 is exact; otherwise (extreme inputs) the clamped form is used.
+      // Masked (future) keys get the argument -256, for which X2 is exactly 0.
       float rs = 0.0f;
-      auto softmax_tile = [&](auto clamped) {
+      auto softmax_tile = [&](auto clamped, auto masked) {
 #pragma unroll
         for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -238,9 +241,9 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
 #pragma unroll
             for (int e = 0; e < 4; e++) {
               const int sv = h == 0 ? acc0[4 * q + e] : acc1[4 * q + e];
-              const float arg = __builtin_fmaf((float)sv, c2, -mm);
-              float t = decltype(clamped)::value ? exp2_softmax_clamped(arg) : exp2_softmax(arg);
-              if (diag && keyb + 16 * h + 4 * q + e > row) t = 0.0f;
+              float arg = __builtin_fmaf((float)sv, c2, -mm);
+              if (decltype(masked)::value && diag && keyb + 16 * h + 4 * q + e > row) arg = -256.0f;
+              const float t = decltype(clamped)::value ? exp2_softmax_clamped(arg) : exp2_softmax(arg);
               pv[e] = t;
               rs += t;
             }
@@ -249,9 +252,9 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
           }
         }
       };
-      const bool in_range = c2 < 256.0f && fabsf(mm) < 0x1p29f;
-      if (__builtin_amdgcn_ballot_w64(!in_range) == 0) softmax_tile(std::false_type{});
-      else softmax_tile(std::true_type{});
+      const bool fast = __builtin_amdgcn_ballot_w64(!(c2 < 256.0f && fabsf(mm) < 0x1p29f)) == 0;
+      if (fast) softmax_tile(std::false_type{}, diag_tag);
+      else softmax_tile(std::true_type{}, diag_tag);
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
 #pragma unroll
@@ -274,7 +277,14 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
       m = mnew;
     }
     if (more) deposit(buf ^ 1);                 // other buffer: last read in iteration tt-1
-  }
+  };
+
+  fetch(0);
+  deposit(0);
+  const int nint = CAUSAL ? 2 * qt : ntiles;   // tiles before the diagonal region
+  int tt = 0;
+  for (; tt < nint; tt++) tile_step(tt, std::false_type{});
+  for (; tt < ntiles; tt++) tile_step(tt, std::integral_constant<bool, CAUSAL>{});
 
   // ---- epilogue: O = O_acc * v_scale / l ----
   const float lt = pair_sum_f32(lpart);
