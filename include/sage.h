@@ -125,8 +125,8 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
  *   O_blk  = sum_j e4m3(P~_j) * v_code_j                   (FP8 matrix cores)
  *   O_acc  = fma(alpha, O_acc, O_blk);  m = m'
  *   O[i,c] = O_acc[c] * v_scale[c] / l
- * X2(t) = p(f) * 2^n with n = rint(t), f = t - n,
- *   p(f) = fma(fma(0x1.fbcaa2p-3, f, 0x1.6a7dc6p-1), f, 1).
+ * X2(t) = p(f) * 2^n with n = floor(t), f = min(t - n, 1 - 2^-24) (fp32),
+ *   p(f) = fma(fma(0x1.5beb9ep-2, f, 0x1.520a3p-1), f, 1).
  * In:  the outputs of sage_quantize_qk (q_codes, q_scale, k_codes, k_scale)
  *      and sage_quantize_v (v_codes, v_scale), same B, H, N, d, blk_q, blk_k.
  * Out: O [B,H,N,d] of out_dtype (SAGE_F32, SAGE_F16 or SAGE_BF16; rounded to

@@ -104,23 +104,23 @@ void oracle_e4m3_decode_n(const uint8_t* c, double* out, int64_t n) {
 /* ------------------------------------------------------------------------ */
 /* Shared exp2 X2(t), the exponential of the fp32 online softmax.            */
 /* Written specification (the kernel restates it independently):            */
-/*   n = round-to-nearest-even(t)            (exact)                         */
-/*   f = t - n                               (exact, |f| <= 1/2)             */
-/*   p = fma(fma(C2, f, C1), f, 1)           (two fp32 fused multiply-adds)  */
-/*   X2 = p * 2^n                            (exact scaling; only a result   */
-/*                                            below 2^-126 rounds, and any  */
-/*                                            n < -200 gives 0)             */
-/* C1 = 0x1.6a7dc6p-1, C2 = 0x1.fbcaa2p-3: relative minimax fit of 2^f on    */
-/* [-1/2, 1/2] with the constant term fixed to 1 and continuity across the  */
-/* reduction boundary (p(1/2) = 2 p(-1/2)); max relative error 2.9e-3,      */
-/* ten times below the e4m3 half-spacing.  X2(0) = 1 exactly.               */
+/*   n = floor(t)                                                            */
+/*   f = min(t - n, 1 - 2^-24)         (fp32 difference: exact except for    */
+/*                                      t in (-1, 0), where it rounds)       */
+/*   p = fma(fma(C2, f, C1), f, 1)     (two fp32 fused multiply-adds)        */
+/*   X2 = p * 2^n                      (exact scaling; only a result below   */
+/*                                      2^-126 rounds, and n < -200 gives 0) */
+/* C1 = 0x1.520a3p-1, C2 = 0x1.5beb9ep-2: relative minimax fit of 2^f on     */
+/* [0, 1) with p(0) = 1 and p(1) = 2 (X2 is continuous at every integer);    */
+/* max relative error 2.68e-3, ten times below the e4m3 half-spacing.        */
+/* X2(k) = 2^k exactly for integers k.                                       */
 /* ------------------------------------------------------------------------ */
-static const float X2_C1 = 0x1.6a7dc6p-1f;
-static const float X2_C2 = 0x1.fbcaa2p-3f;
+static const float X2_C1 = 0x1.520a3p-1f;
+static const float X2_C2 = 0x1.5beb9ep-2f;
 
 float oracle_x2(float t) {
-  float n = rintf(t);
-  float f = t - n;
+  float n = floorf(t);
+  float f = fminf(t - n, 0x1.fffffep-1f);
   float p = fmaf(fmaf(X2_C2, f, X2_C1), f, 1.0f);
   if (n < -200.0f) return 0.0f * p;
   return ldexpf(p, (int)n);
