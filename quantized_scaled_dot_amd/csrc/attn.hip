@@ -99,13 +99,24 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, lg = lane >> 5;
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of (head, query tile) so one head's K/V stays in one L2.
+  // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
+  // on XCD b % 8).  When the heads divide evenly, XCD x owns heads x, x+8, ...
+  // so each head's K/V stays in one L2.  Non-causal: an XCD walks its heads
+  // one after another.  Causal (work grows with the query tile): an XCD walks
+  // its query tiles heaviest first across all of its heads, so the long
+  // tiles never start last.
   const int G = gridDim.x, b = blockIdx.x;
-  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  const int bh = L / p.nqt;
-  int qt = L % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
+  const int BH = G / p.nqt;
+  int bh, qt;
+  if (BH % 8 == 0) {
+    const int x = b % 8, j = b / 8, hpx = BH / 8;   // XCD, its j-th item, heads per XCD
+    if (CAUSAL) { bh = (j % hpx) * 8 + x; qt = p.nqt - 1 - j / hpx; }
+    else { bh = (j / p.nqt) * 8 + x; qt = j % p.nqt; }
+  } else if (CAUSAL) {
+    bh = b % BH; qt = p.nqt - 1 - b / BH;           // heaviest first overall
+  } else {
+    bh = b / p.nqt; qt = b % p.nqt;
+  }
   const int N = p.N;
   const int q0 = qt * kQTile, qrow0 = q0 + wave * 32, row = qrow0 + li;
 

@@ -105,14 +105,22 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
 #pragma unroll
   for (int e = 0; e < 8; e++) s[e] = 0.0;
   const uint16_t* base = K + ((size_t)bh * N + n0) * D + cg * 8;
-#pragma unroll 4
-  for (int r = r0; r < nrows; r += RPP) {
-    v4i raw = *(const v4i*)(base + (size_t)r * D);
+  auto add_row = [&](const v4i& raw) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const float x = fminf(fmaxf(half_of(raw, e, is_bf16), -1048576.0f), 1048576.0f);
       s[e] += (double)__builtin_truncf(x * 16777216.0f);   // exact product, exact sum
     }
+  };
+  if (nrows == kStatChunk) {   // full chunk: issue every row load of this thread first
+    constexpr int RPT = kStatChunk / RPP;
+    v4i raw[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * D);
+#pragma unroll
+    for (int i = 0; i < RPT; i++) add_row(raw[i]);
+  } else {
+    for (int r = r0; r < nrows; r += RPP) add_row(*(const v4i*)(base + (size_t)r * D));
   }
 #pragma unroll
   for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = (long long)s[e];
@@ -181,11 +189,19 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
 #pragma unroll
   for (int e = 0; e < 8; e++) s[e] = 0.0f;
   const uint16_t* base = V + ((size_t)bh * N + n0) * D + cg * 8;
-#pragma unroll 4
-  for (int r = r0; r < nrows; r += RPP) {
-    v4i raw = *(const v4i*)(base + (size_t)r * D);
+  auto max_row = [&](const v4i& raw) {
 #pragma unroll
     for (int e = 0; e < 8; e++) s[e] = fmaxf(s[e], fabsf(half_of(raw, e, is_bf16)));
+  };
+  if (nrows == kStatChunk) {   // full chunk: issue every row load of this thread first
+    constexpr int RPT = kStatChunk / RPP;
+    v4i raw[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * D);
+#pragma unroll
+    for (int i = 0; i < RPT; i++) max_row(raw[i]);
+  } else {
+    for (int r = r0; r < nrows; r += RPP) max_row(*(const v4i*)(base + (size_t)r * D));
   }
   __shared__ float red[RPP][D];
 #pragma unroll
