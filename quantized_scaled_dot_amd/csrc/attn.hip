@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
 #pragma unroll
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
-  v8i pb = {};
+  v8i pb;
 
   const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
   const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
@@ -258,7 +258,9 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
               pv[e] = t;
               rs += t;
             }
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], pb[4 * h + q], false);
+            // the low-half convert's "old" operand is a register that dies here
+            // (its high half is overwritten by the second convert)
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[0]), false);
             pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
           }
         }
