@@ -39,11 +39,9 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [f32]
         L.oracle_e4m3_encode_n.argtypes = [P, P, i64]
         L.oracle_e4m3_decode_n.argtypes = [P, P, i64]
-        L.oracle_x2.restype = f32
-        L.oracle_x2.argtypes = [f32]
-        L.oracle_x2_n.argtypes = [P, P, i64]
-        L.oracle_x2_c1.restype = f32
-        L.oracle_x2_c2.restype = f32
+        L.oracle_exp2f.restype = f32
+        L.oracle_exp2f.argtypes = [f32]
+        L.oracle_exp2f_n.argtypes = [P, P, i64]
         L.oracle_kmean.restype = i32
         L.oracle_kmean.argtypes = [P, i32, i32, i32, i32, P, P]
         L.oracle_quantize_qk.restype = i32
@@ -82,15 +80,12 @@ def e4m3_decode(c):
     return out
 
 
-def x2(t):
+def exp2f(t):
+    """The softmax exponential: 2^t of fp32 t, evaluated in double, rounded once to fp32."""
     t = _c(t, np.float32)
     out = np.empty(t.shape, np.float32)
-    lib().oracle_x2_n(_p(t), _p(out), t.size)
+    lib().oracle_exp2f_n(_p(t), _p(out), t.size)
     return out
-
-
-def x2_coefficients():
-    return float(lib().oracle_x2_c1()), float(lib().oracle_x2_c2())
 
 
 def num_threads():

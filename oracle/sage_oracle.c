@@ -7,8 +7,7 @@
  * TEST INFRASTRUCTURE ONLY.  This file is the reference the GPU path is checked
  * against.  Only the test suite, the package smoke check and the benchmark's CPU
  * baseline leg may load it.  It shares no code, header, table or constant
- * generator with the HIP implementation; the shared exp2 polynomial below is a
- * written specification that both sides restate independently.
+ * generator with the HIP implementation.
  *
  * Sources (web pages, cited by title and section):
  *  [SA]   "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
@@ -102,35 +101,18 @@ void oracle_e4m3_decode_n(const uint8_t* c, double* out, int64_t n) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* Shared exp2 X2(t), the exponential of the fp32 online softmax.            */
-/* Written specification (the kernel restates it independently):            */
-/*   n = floor(t)                                                            */
-/*   f = min(t - n, 1 - 2^-24)         (fp32 difference: exact except for    */
-/*                                      t in (-1, 0), where it rounds)       */
-/*   p = fma(fma(C2, f, C1), f, 1)     (two fp32 fused multiply-adds)        */
-/*   X2 = p * 2^n                      (exact scaling; only a result below   */
-/*                                      2^-126 rounds, and n < -200 gives 0) */
-/* C1 = 0x1.520a3p-1, C2 = 0x1.5beb9ep-2: relative minimax fit of 2^f on     */
-/* [0, 1) with p(0) = 1 and p(1) = 2 (X2 is continuous at every integer);    */
-/* max relative error 2.68e-3, ten times below the e4m3 half-spacing.        */
-/* X2(k) = 2^k exactly for integers k.                                       */
+/* exp2 of the fp32 online softmax ([BLOG] "How FlashAttention reduces       */
+/* memory traffic": the softmax is evaluated tile by tile in fp32; folding  */
+/* log2 e into the score scale turns exp into exp2).  The argument is an    */
+/* fp32 value; 2^t is evaluated in double precision and rounded once to     */
+/* fp32 (a result below the fp32 subnormal range rounds to 0, -inf gives    */
+/* 0).  The pages fix no cheaper approximation, so none is taken here.      */
 /* ------------------------------------------------------------------------ */
-static const float X2_C1 = 0x1.520a3p-1f;
-static const float X2_C2 = 0x1.5beb9ep-2f;
+float oracle_exp2f(float t) { return (float)exp2((double)t); }
 
-float oracle_x2(float t) {
-  float n = floorf(t);
-  float f = fminf(t - n, 0x1.fffffep-1f);
-  float p = fmaf(fmaf(X2_C2, f, X2_C1), f, 1.0f);
-  if (n < -200.0f) return 0.0f * p;
-  return ldexpf(p, (int)n);
+void oracle_exp2f_n(const float* t, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_exp2f(t[i]);
 }
-
-void oracle_x2_n(const float* t, float* out, int64_t n) {
-  for (int64_t i = 0; i < n; i++) out[i] = oracle_x2(t[i]);
-}
-float oracle_x2_c1(void) { return X2_C1; }
-float oracle_x2_c2(void) { return X2_C2; }
 
 /* ------------------------------------------------------------------------ */
 /* Step 1: per-channel mean of K over all N tokens of a head (smoothing K).  */
@@ -280,8 +262,8 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int BH, int N
 /*   S_j   = sum_c q_c k_c                       (int32, exact)              */
 /*   c2_j  = RN(RN(dQ * dK_j) * s2),  s2 = RN(sm_scale * log2 e)             */
 /*   u_j   = RN(float(S_j) * c2_j);  m' = max(m, max_j u_j)                  */
-/*   alpha = X2(RN(m - m'))   (0 on the first visited tile)                  */
-/*   P~_j  = X2(fma(float(S_j), c2_j, -RN(m' - 8)))   (P~ scaled by 2^8)     */
+/*   alpha = exp2f(RN(m - m'))   (0 on the first visited tile)               */
+/*   P~_j  = exp2f(fma(float(S_j), c2_j, -RN(m' - 8)))  (P~ scaled by 2^8)  */
 /*   l     = fma(alpha, l, sum_j P~_j)               (fp32 state)            */
 /*   P^_j  = E(P~_j)                                 (FP8 e4m3)              */
 /*   Oblk_c = sum_j dec(P^_j) dec(v^_jc)             (inner level; exact     */
@@ -338,11 +320,11 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
         if (u > mt) mt = u;
       }
       float mnew = first ? mt : (mt > m ? mt : m);
-      float alpha = first ? 0.0f : oracle_x2(m - mnew);
+      float alpha = first ? 0.0f : oracle_exp2f(m - mnew);
       float mm = mnew - 8.0f;
       float rowsum = 0.0f;
       for (int jj = 0; jj < nvis; jj++) {
-        pt[jj] = oracle_x2(fmaf((float)S[jj], c2[jj], -mm));
+        pt[jj] = oracle_exp2f(fmaf((float)S[jj], c2[jj], -mm));
         rowsum += pt[jj];
         ph[jj] = oracle_e4m3_encode(pt[jj]);
         if (p_codes) p_codes[(size_t)r * N + j0 + jj] = ph[jj];

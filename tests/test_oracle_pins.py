@@ -78,35 +78,44 @@ def test_e4m3_encode_matches_torch_in_range():
     assert np.array_equal(ours, ref)
 
 
-# ------------------------------------------------------------------ shared exp2
-def test_x2_accuracy_and_exact_points():
-    t = np.concatenate([np.linspace(-126, 8.5, 2_000_001), np.linspace(-1, 1, 100001)]).astype(np.float32)
-    got = orc.x2(t).astype(np.float64)
-    ref = np.exp2(t.astype(np.float64))
-    rel = np.abs(got / ref - 1)
-    assert rel.max() < 3.0e-3
-    ints = np.arange(-126, 9, dtype=np.float32)
-    assert np.array_equal(orc.x2(ints), np.exp2(ints.astype(np.float64)).astype(np.float32))
-    assert orc.x2(np.array([0.0], np.float32))[0] == 1.0
-    assert orc.x2(np.array([8.0], np.float32))[0] == 256.0
+# ------------------------------------------------------------------ softmax exp2
+def test_exp2_exact_points():
+    # powers of two are exact, down to the smallest subnormal; below it, zero
+    ints = np.arange(-149, 128, dtype=np.float32)
+    assert [float(v) for v in orc.exp2f(ints)] == [2.0 ** int(k) for k in ints]
+    assert orc.exp2f(np.array([-150.5, -1e4, -1e30, -np.inf], np.float32)).tolist() == [0, 0, 0, 0]
+    assert orc.exp2f(np.array([0.0, -0.0], np.float32)).tolist() == [1.0, 1.0]
 
 
-def test_x2_monotone_and_underflow():
-    t = np.linspace(-20, 8.5, 3_000_001).astype(np.float32)
-    y = orc.x2(t)
-    d = np.diff(y.astype(np.float64))
-    # non-decreasing up to one fp32 ulp (the polynomial meets 2 at f = 1)
-    ulp = np.spacing(y[:-1]).astype(np.float64)
-    assert (d >= -ulp).all()
-    assert orc.x2(np.array([-150, -1e4, -1e30, -3.0e38], np.float32)).tolist() == [0, 0, 0, 0]
-    # subnormal results are correctly rounded scalings of the polynomial
-    p = orc.x2(np.array([-130.0], np.float32))[0]
-    assert p == np.float32(2.0 ** -130)
+def test_exp2_against_square_roots_and_logs():
+    # 2^(1/2) and 2^(-1/2) are sqrt(2) and 1/sqrt(2), correctly rounded
+    got = orc.exp2f(np.array([0.5, -0.5, 8.5], np.float32))
+    assert got[0] == np.float32(np.sqrt(2.0)) and got[1] == np.float32(np.sqrt(0.5))
+    assert got[2] == np.float32(256.0 * np.sqrt(2.0))
+    # 2^(log2 x) returns x up to the rounding of log2 x to fp32 (|dt| <= 2^-24 |t|)
+    x = np.array([3.0, 5.0, 10.0, 0.1, 1e-3, 200.0])
+    t = np.log2(x).astype(np.float32)
+    rel = np.abs(orc.exp2f(t) / x - 1)
+    assert (rel <= np.abs(t) * 2.0 ** -24 * np.log(2) + 2.0 ** -24).all()
 
 
-def test_x2_coefficients_are_the_specified_literals():
-    c1, c2 = orc.x2_coefficients()
-    assert c1 == float.fromhex("0x1.520a3p-1") and c2 == float.fromhex("0x1.5beb9ep-2")
+def test_exp2_shift_by_one_is_doubling_and_monotone():
+    rng = np.random.default_rng(5)
+    t = rng.uniform(-120, 120, 200_000).astype(np.float32)
+    t1 = t + np.float32(1)
+    keep = t1.astype(np.float64) - t.astype(np.float64) == 1.0   # t + 1 exact in fp32
+    t, t1 = t[keep], t1[keep]
+    assert t.size > 100_000
+    a, b = orc.exp2f(t), orc.exp2f(t1)
+    assert np.array_equal(b, a * np.float32(2))
+    s = np.sort(rng.uniform(-30, 9, 500_000).astype(np.float32))
+    y = orc.exp2f(s)
+    assert (np.diff(y.astype(np.float64)) >= 0).all()
+    # within half an fp32 ulp of the exact value (a spot check in long double)
+    u = np.array([-0.3, 0.7, -17.123, 7.999], np.float32)
+    exact = np.array([np.exp2(np.longdouble(v)) for v in u])
+    err = np.abs(orc.exp2f(u).astype(np.longdouble) - exact)
+    assert (err <= np.spacing(orc.exp2f(u)).astype(np.longdouble) / 2 * (1 + 1e-9)).all()
 
 
 # ------------------------------------------------------------------ int32 QK^T
