@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   constexpr int CPT = TILE / 16 / 256;         // 16-byte chunks per thread per tile (2 or 1)
   constexpr int RK = kRowK<D>;
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][D * kRowV];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, lg = lane >> 5;
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   // codes; V: d rows of 64 codes).  Chunk c of the K tile is key c/(d/16),
   // chunk c%(d/16); chunk c of the V tile is channel c/4, chunk c%4.  The
   // global offsets and LDS destinations are fixed per thread; only the tile
-  // offset (a scalar) changes from tile to tile.  K tile t lives in sK[t&1],
-  // V tile t in sV[t&1]; K is staged one tile ahead of V (see the loop).
+  // offset (a scalar) changes from tile to tile.  K tile t lives in sK[t%2],
+  // V tile t in sV[t%3]; K is staged one tile ahead of V (see the loop).
   const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bh * N * D, (uint32_t)(N * D));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bh * N * D, (uint32_t)(N * D));
   int k_dst[CPT], v_dst[CPT];
@@ -194,25 +194,69 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
     }
   };
+  // ---- two-level P~V for the tile whose V codes are in slot vslot: the
+  // matrix core sums the 64 FP8 products of the tile (inner level) and adds
+  // that block sum into the fp32 accumulator O_acc passed as its C operand
+  // (outer level; the C addition is an fp32 add outside the instruction's
+  // product-alignment window) ----
+  auto pv = [&](const v8i& pb, int vslot) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) {
+      const uint8_t* vb = sV[vslot] + (32 * ct + li) * kRowV + 32 * lg;   // channel row, keys 32*lg..
+      const v4i v0 = *(const v4i*)(vb);
+      const v4i v1 = *(const v4i*)(vb + 16);
+      const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
+    }
+  };
   // whole tile t after every row of this wave (causal): nothing to compute
   auto future = [&](int t) { return CAUSAL && t * kKTile > qrow0 + 31; };
 
-  // One KV tile t whose scores sc0/sc1 were issued earlier.  While its
-  // softmax runs on the VALU, the matrix core computes the scores of tile t+1
-  // into nx0/nx1 (when NEXT), so the two units overlap within the wave.
+  // P~ codes of the last visited tile whose P~V is still to be issued, and
+  // that tile's rescale of the running state (alpha_prev, applied before
+  // the pending P~V when some row of the wave got a larger max).
+  v8i pprev;
+  bool pend = false, grew = false;
+  float alpha_prev = 1.0f;
+  float ks_next = kscale[0];   // K scale of the tile whose softmax comes next
+  auto rescale = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha_prev;
+  };
+
+  // One KV tile t whose scores sc0/sc1 were issued in the previous step.
+  // The step issues the P~V of the previous tile and the scores of tile t+1
+  // (when NEXT) between the VALU instructions of tile t's softmax, so the
+  // matrix core runs while the VALU computes.  The previous tile's rescale
+  // comes first: after the P~V of the tile before it (issued one step
+  // earlier) and before its own, so O_t = alpha_t * O_{t-1} + P~_t V_t holds
+  // exactly as in the sequential form.
   // DIAG: the tile may hold keys after some row (causal diagonal region).
-  auto tile_step = [&](const int t, v16i& sc0, v16i& sc1, v16i& nx0, v16i& nx1, auto diag_tag, bool next) {
+  // HAD: 1 = a P~V is pending (every step after the first in the interior),
+  // 0 = none (first step), 2 = decided at run time (causal diagonal steps).
+  auto tile_step = [&](const int t, v16i& sc0, v16i& sc1, v16i& nx0, v16i& nx1, auto diag_tag, auto had_tag,
+                       bool next) {
     constexpr bool DIAG = decltype(diag_tag)::value;
+    constexpr int HAD = decltype(had_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();          // K_{t+1}, V_t staged; every wave is done with tile t-1
     __builtin_amdgcn_sched_barrier(0);
+    const bool had = HAD == 2 ? pend : HAD == 1;
+    if (had && grew) rescale();   // rare
+    // The K scale of tile t+1 is read one step ahead, before the tile
+    // copies, so waiting for it never waits for them.
+    const float ks = ks_next;
+    ks_next = kscale[min(t + 1, ntiles - 1)];
     // In flight while tile t is computed.  Past the last tile the index is
     // clamped: the extra copy lands in a slot that is never read again.
     fetchK(min(t + 2, ntiles - 1));
     fetchV(min(t + 1, ntiles - 1));
-    const uint8_t* sVb = sV[t & 1];
+    __builtin_amdgcn_sched_barrier(0);   // issue the copies first
     const int kv0 = t * kKTile;
     const int keyb = kv0 + 32 * lg;   // sc0[v] is key keyb + v, sc1[v] is key keyb + 16 + v
+    if (had) pv(pprev, (t + 2) % 3);   // slot of tile t-1
 
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
@@ -232,22 +276,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
         for (int v = 0; v < 16; v++) smax = max(max(smax, sc0[v]), sc1[v]);   // v_max3_i32 chain
       }
       smax = pair_max_i32(smax);
-      const float c2 = (dq * kscale[t]) * p.s2;
+      const float c2 = (dq * ks) * p.s2;
       float ustar = (float)smax * c2;
       if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
       const float mnew = fmaxf(m, ustar);
       const float mm = mnew - 8.0f;
-      // Rescale the running state only when some row of this wave got a larger
-      // max (alpha = exp2(0) = 1 exactly for the others); on the first tile
-      // the state is still zero.
-      float alpha = 1.0f;
-      if (t > 0 && __builtin_amdgcn_ballot_w64(mnew > m) != 0) {
-        alpha = __builtin_amdgcn_exp2f(m - mnew);
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-          for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
-      }
       if (next) qk(t + 1, nx0, nx1);
 
       // ---- P~ (fp32) -> FP8 B operand, packed in place ----
@@ -259,61 +292,48 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       for (int h = 0; h < 2; h++) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          float pv[4];
+          float pv4[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
             float arg = __builtin_fmaf((float)sv, c2, -mm);
             if (diag && keyb + 16 * h + 4 * q + e > row) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
-            pv[e] = x;
+            pv4[e] = x;
             rs += x;
           }
           // the low-half convert's "old" operand is a register that dies here
           // (its high half is overwritten by the second convert)
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[0]), false);
-          pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w, true);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[0], pv4[1], __float_as_int(pv4[0]), false);
+          pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[2], pv4[3], w, true);
         }
       }
+      // keep the softmax in this block: without a use here the compiler
+      // moves it below the rescale branch, away from the MFMAs it should
+      // overlap (an empty statement that reads the packed codes and the sum)
+      asm volatile("" : "+v"(pb), "+v"(rs));
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
 #pragma unroll
         for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
       }
-
-      // ---- two-level P~V: the matrix core sums the 64 FP8 products of this KV
-      // tile (inner level) and adds that block sum into the fp32 accumulator
-      // O_acc passed as its C operand (outer level; the C addition is an fp32
-      // add outside the instruction's product-alignment window) ----
-#pragma unroll
-      for (int ct = 0; ct < CT; ct++) {
-        const uint8_t* vb = sVb + (32 * ct + li) * kRowV + 32 * lg;   // channel row, keys 32*lg..
-        const v4i v0 = *(const v4i*)(vb);
-        const v4i v1v = *(const v4i*)(vb + 16);
-        const v8i av = {v0[0], v0[1], v0[2], v0[3], v1v[0], v1v[1], v1v[2], v1v[3]};
-        oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
-      }
+      // alpha = exp2(m - m'): 1 exactly where the max did not grow, 0 on the
+      // first visited tile (m = -1e30, the state is still zero)
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       lpart = __builtin_fmaf(alpha, lpart, rs);
+      grew = __builtin_amdgcn_ballot_w64(mnew > m) != 0;
+      alpha_prev = alpha;
       m = mnew;
-      if (next) {
-        // Interleave the next tile's score MFMAs with this tile's softmax:
-        // one MFMA, one operand read, then a batch of VALU work, so the
-        // matrix core runs while the VALU computes.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // first K operands
-#pragma unroll
-        for (int i = 0; i < 2 * KS; i++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-          __builtin_amdgcn_sched_group_barrier(0x402, 64 / KS, 0);   // VALU incl. exp
-        }
-      }
-    } else if (next) {
-      qk(t + 1, nx0, nx1);
+      pprev = pb;
+      pend = true;
+    } else {
+      if (next) qk(t + 1, nx0, nx1);
+      pend = false;
     }
-    // K_{t+2} replaces K_t (last read before this tile's barrier), V_{t+1}
-    // replaces V_{t-1} (read by the previous tile's P~V)
+    // K_{t+2} replaces K_t (read by the previous step's score MFMAs); V_{t+1}
+    // replaces V_{t-2} (read by the previous step's P~V)
     depositK(t & 1);
-    depositV((t + 1) & 1);
+    depositV((t + 1) % 3);
   };
 
   // prologue: K_0, V_0, K_1 staged, scores of tile 0 issued
@@ -330,15 +350,28 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   // their count is even (N is a multiple of 128).  The pipelined step always
   // computes the next tile's scores there: after the last tile of a
   // non-causal pass that reads a stale (but in-bounds) K slot and is unused.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   const int nint = CAUSAL ? 2 * qt : ntiles;
   int t = 0;
-  for (; t < nint; t += 2) {
-    tile_step(t, sa0, sa1, sb0, sb1, std::false_type{}, true);
-    tile_step(t + 1, sb0, sb1, sa0, sa1, std::false_type{}, true);
+  if (nint > 0) {
+    tile_step(0, sa0, sa1, sb0, sb1, std::false_type{}, I0{}, true);
+    for (t = 1; t + 1 < nint; t += 2) {
+      tile_step(t, sb0, sb1, sa0, sa1, std::false_type{}, I1{}, true);
+      tile_step(t + 1, sa0, sa1, sb0, sb1, std::false_type{}, I1{}, true);
+    }
+    tile_step(t, sb0, sb1, sa0, sa1, std::false_type{}, I1{}, true);   // t = nint - 1
+    t = nint;
   }
-  if (CAUSAL) {   // the two diagonal tiles 2*qt and 2*qt + 1
-    tile_step(t, sa0, sa1, sb0, sb1, std::integral_constant<bool, CAUSAL>{}, !future(t + 1));
-    tile_step(t + 1, sb0, sb1, sa0, sa1, std::integral_constant<bool, CAUSAL>{}, false);
+  if (CAUSAL) {   // the two diagonal tiles 2*qt and 2*qt + 1 (scores of tile t are in sa)
+    tile_step(t, sa0, sa1, sb0, sb1, std::integral_constant<bool, CAUSAL>{}, I2{}, !future(t + 1));
+    tile_step(t + 1, sb0, sb1, sa0, sa1, std::integral_constant<bool, CAUSAL>{}, I2{}, false);
+    t += 2;
+  }
+  if (pend) {   // the last visited tile is t-1
+    if (grew) rescale();
+    pv(pprev, (t + 2) % 3);
   }
 
   // ---- epilogue: O = O_acc * v_scale / l ----
