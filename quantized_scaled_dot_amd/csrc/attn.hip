@@ -48,10 +48,11 @@ struct AttnK {
 };
 
 // LDS row of key kappa (0..63) of a KV tile: 32*h + m with m the MFMA row
-// m = 8*(v/4) + 4*g + v%4 for kappa = 32*g + 16*h + v.
-__device__ __forceinline__ int k_lds_row(int kap) {
-  const int g = kap >> 5, h = (kap >> 4) & 1, v = kap & 15;
-  return 32 * h + 8 * (v >> 2) + 4 * g + (v & 3);
+// m = 8*(v/4) + 4*g + v%4 for kappa = 32*g + 16*h + v.  k_lds_key inverts it.
+__device__ __forceinline__ int k_lds_key(int rho) {
+  const int h = rho >> 5, m = rho & 31;
+  const int g = (m >> 2) & 1, v = 4 * (m >> 3) + (m & 3);
+  return 32 * g + 16 * h + v;
 }
 // LDS rows are padded by 16 bytes (K: d+16, V: 64+16).  The matrix-core
 // operand reads (ds_read_b128) touch the same 16-byte chunk of 8 or 16
@@ -87,6 +88,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l writes
+// lds + 16 l (the LDS address must be the same for the whole wave).
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 template <int D, bool CAUSAL, int OUT, bool DUMP>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p) {
   constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
@@ -97,7 +104,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
   __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int li = lane & 31, lg = lane >> 5;
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
   // on XCD b % 8).  When the heads divide evenly, XCD x owns heads x, x+8, ...
@@ -134,43 +142,53 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   }
   const float dq = p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
 
-  // ---- staging: every thread moves CPT 16-byte chunks of each tile ----
-  // K and V tiles are contiguous TILE-byte blocks in HBM (K: 64 rows of d
-  // codes; V: d rows of 64 codes).  Chunk c of the K tile is key c/(d/16),
-  // chunk c%(d/16); chunk c of the V tile is channel c/4, chunk c%4.  The
-  // global offsets and LDS destinations are fixed per thread; only the tile
-  // offset (a scalar) changes from tile to tile.  K tile t lives in sK[t%2],
-  // V tile t in sV[t%3]; K is staged one tile ahead of V (see the loop).
+  // ---- staging: direct global -> LDS copies (buffer loads with the LDS
+  // destination, 16 bytes per lane, 1 KiB per wave instruction) ----
+  // Instruction i of a tile fills LDS bytes [1024 i, 1024 i + 1024) of its
+  // slot: lane l writes bytes 1024 i + 16 l onward, and its global source is
+  // chosen so that the padded LDS layout comes out directly (K rows in MFMA
+  // order, d + 16 bytes; V channel rows, 80 bytes).  Padding chunks re-read
+  // the last data chunk of their row.  Wave w issues instructions w, w+4, ...
+  // K tile t lives in sK[t%2], V tile t in sV[t%3]; K is staged one tile
+  // ahead of V (see the loop).  The K and V tiles are contiguous TILE-byte
+  // blocks in HBM (K: 64 rows of d codes; V: d rows of 64 codes).
+  constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
+  static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
+  constexpr int JK = (NKI + 3) / 4, JV = (NVI + 3) / 4;
   const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bh * N * D, (uint32_t)(N * D));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bh * N * D, (uint32_t)(N * D));
-  int k_dst[CPT], v_dst[CPT];
+  uint32_t koff[JK], voff[JV];
 #pragma unroll
-  for (int i = 0; i < CPT; i++) {
-    const int c = tid + 256 * i;
-    const int kap = c / (D / 16), c16 = c % (D / 16);
-    k_dst[i] = k_lds_row(kap) * RK + 16 * c16;
-    const int r = c >> 2, v16 = c & 3;
-    v_dst[i] = r * kRowV + 16 * v16;
+  for (int j = 0; j < JK; j++) {
+    const int o = 1024 * (wave + 4 * j) + 16 * lane;
+    const int rho = o / RK, c = min((o % RK) / 16, D / 16 - 1);
+    koff[j] = (uint32_t)(k_lds_key(rho) * D + 16 * c);
   }
-  v4i stK[CPT], stV[CPT];
-  auto fetchK = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < CPT; i++)
-      stK[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rK, (tid + 256 * i) * 16, t * TILE, 0));
-  };
-  auto fetchV = [&](int t) {
+  for (int j = 0; j < JV; j++) {
+    const int o = 1024 * (wave + 4 * j) + 16 * lane;
+    const int r = o / kRowV, c = min((o % kRowV) / 16, kKTile / 16 - 1);
+    voff[j] = (uint32_t)(r * kKTile + 16 * c);
+  }
+  auto stageK = [&](int t, int slot) {
 #pragma unroll
-    for (int i = 0; i < CPT; i++)
-      stV[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rV, (tid + 256 * i) * 16, t * TILE, 0));
+    for (int j = 0; j < JK; j++) {
+      const int i = wave + 4 * j;
+      if (i < NKI)
+        lds_copy16(rK, &sK[slot][1024 * i], koff[j], t * TILE);
+    }
   };
-  auto depositK = [&](int slot) {
+  auto stageV = [&](int t, int slot) {
 #pragma unroll
-    for (int i = 0; i < CPT; i++) *(v4i*)(&sK[slot][k_dst[i]]) = stK[i];
+    for (int j = 0; j < JV; j++) {
+      const int i = wave + 4 * j;
+      if (i < NVI)
+        lds_copy16(rV, &sV[slot][1024 * i], voff[j], t * TILE);
+    }
   };
-  auto depositV = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < CPT; i++) *(v4i*)(&sV[slot][v_dst[i]]) = stV[i];
-  };
+  // this wave's copies have landed in LDS (the barrier that follows makes
+  // them visible to the other waves)
+  auto staged = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
   v16f oacc[CT];
 #pragma unroll
@@ -249,10 +267,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     // copies, so waiting for it never waits for them.
     const float ks = ks_next;
     ks_next = kscale[min(t + 1, ntiles - 1)];
-    // In flight while tile t is computed.  Past the last tile the index is
-    // clamped: the extra copy lands in a slot that is never read again.
-    fetchK(min(t + 2, ntiles - 1));
-    fetchV(min(t + 1, ntiles - 1));
+    // In flight while tile t is computed: K_{t+2} replaces K_t (read by the
+    // previous step's score MFMAs), V_{t+1} replaces V_{t-2} (read by the
+    // previous step's P~V).  Past the last tile the index is clamped: the
+    // extra copy lands in a slot that is never read again.
+    stageK(min(t + 2, ntiles - 1), t & 1);
+    stageV(min(t + 1, ntiles - 1), (t + 1) % 3);
     __builtin_amdgcn_sched_barrier(0);   // issue the copies first
     const int kv0 = t * kKTile;
     const int keyb = kv0 + 32 * lg;   // sc0[v] is key keyb + v, sc1[v] is key keyb + 16 + v
@@ -330,18 +350,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       if (next) qk(t + 1, nx0, nx1);
       pend = false;
     }
-    // K_{t+2} replaces K_t (read by the previous step's score MFMAs); V_{t+1}
-    // replaces V_{t-2} (read by the previous step's P~V)
-    depositK(t & 1);
-    depositV((t + 1) % 3);
+    staged();
   };
 
   // prologue: K_0, V_0, K_1 staged, scores of tile 0 issued
-  fetchK(0);
-  fetchV(0);
-  depositK(0);
-  depositV(0);
-  if (ntiles > 1) { fetchK(1); depositK(1); }
+  stageK(0, 0);
+  stageV(0, 0);
+  stageK(1, 1);   // ntiles >= 2
+  staged();
   __syncthreads();
   v16i sa0, sa1, sb0, sb1;
   qk(0, sa0, sa1);
