@@ -7,7 +7,9 @@ fused attention kernel.  Inputs are resident in HBM before timing starts.
 Metric: attention TOPS = 4*B*H*N^2*d / t (halved for causal) with t the
 wall-clock time of one step.  The JSON line also carries the attention
 kernel's own rate against the dense INT8/FP8 matrix-core peak (roofline) and
-the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload, and the
+quantize passes' achieved HBM bandwidth (algorithmic bytes: 2 read + 1 written
+per element of Q, K and V; the statistics passes read K and V a second time).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -27,6 +29,7 @@ sys.path.insert(0, ROOT)
 from quantized_scaled_dot_amd import synth  # noqa: E402
 
 MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 = dense FP8 = 5.0 P op/s
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "video-dit-32k"
 METRIC = "attention TOPS (4·B·H·N²·d/t) at 1 MI355X; % of INT8/FP8 MFMA peak"
 KERNEL_SOURCES = ("quantized_scaled_dot_amd/csrc/attn.hip", "quantized_scaled_dot_amd/csrc/common.h")
@@ -129,6 +132,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        if ev is not None:
+            ev[2].record(stream)
         q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
         v = sage.quantize_v(Vd, workspace=ws_v)
         if ev is not None:
@@ -140,14 +145,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    quant_ms = [e[2].elapsed_time(e[0]) for e in evs]
     ms_step = t * 1e3 / args.steps
     attn_avg = float(np.mean(attn_ms))
     value = w.ops / (ms_step * 1e-3) / 1e12
@@ -155,6 +161,15 @@ def main():
     log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel avg {attn_avg:.3f} ms "
         f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
         f"{100 * attn_tops / MFMA_PEAK_TOPS:.1f}% of peak)")
+
+    n_el = B * H * N * d
+    in_bytes = 2 * n_el                    # f16 / bf16 inputs
+    quant_alg = 3 * (in_bytes + n_el)      # Q, K, V: read the input, write 1-byte codes
+    quant_act = quant_alg + 2 * in_bytes   # the K-sum and V-max passes read K and V once more
+    quant_avg = float(np.mean(quant_ms))
+    quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
+    log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "
+        f"({100 * quant_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {quant_act / (quant_avg * 1e-3) / 1e9:.0f} GB/s moved")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -175,6 +190,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 3),
                      "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / MFMA_PEAK_TOPS, 4),
                      "traffic": measured_traffic(w.name)},
+        "quantize": {"ms": round(quant_avg, 4), "bound": "hbm", "algorithmic_bytes": quant_alg,
+                     "bytes_moved": quant_act, "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(quant_gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
