@@ -185,13 +185,18 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
   const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
   const int n0 = chunk * kStatChunk;
   const int nrows = min(kStatChunk, N - n0);
-  float s[8];
+  // |x| of a finite f16 / bf16 value orders exactly like its sign-cleared
+  // bit pattern read as an unsigned integer, so the maxima are taken on the
+  // bit patterns, two channels per 32-bit lane, and decoded once at the end.
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mx[4];
 #pragma unroll
-  for (int e = 0; e < 8; e++) s[e] = 0.0f;
+  for (int j = 0; j < 4; j++) mx[j] = u16x2{0, 0};
   const uint16_t* base = V + ((size_t)bh * N + n0) * D + cg * 8;
   auto max_row = [&](const v4i& raw) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) s[e] = fmaxf(s[e], fabsf(half_of(raw, e, is_bf16)));
+    for (int j = 0; j < 4; j++)
+      mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, (unsigned)raw[j] & 0x7FFF7FFFu));
   };
   if (nrows == kStatChunk) {   // full chunk: issue every row load of this thread first
     constexpr int RPT = kStatChunk / RPP;
@@ -203,6 +208,9 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
   } else {
     for (int r = r0; r < nrows; r += RPP) max_row(*(const v4i*)(base + (size_t)r * D));
   }
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) s[e] = load_h(mx[e >> 1][e & 1], is_bf16);
   __shared__ float red[RPP][D];
 #pragma unroll
   for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = s[e];
