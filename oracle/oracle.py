@@ -6,8 +6,11 @@ leg may import this module.  It loads ``liboracle.so`` (plain C, see
 used for the accuracy check.  It imports nothing from the GPU package.
 
 Arrays are numpy.  Inputs Q, K, V are passed as the raw 16-bit patterns of
-float16 / bfloat16 tensors of shape [B, H, N, d] (``uint16``), with
-``dtype`` 0 for float16 and 1 for bfloat16.
+float16 / bfloat16 tensors (``uint16``), with ``dtype`` 0 for float16 and 1
+for bfloat16: Q of shape [B, Hq, Nq, d], K and V of shape [B, Hkv, Nkv, d].
+Query head h reads key/value head h // (Hq // Hkv) (grouped-query attention
+when Hkv < Hq); with causal masking, key j is visible to query i iff
+j <= i + (Nkv - Nq).
 """
 import ctypes
 import os
@@ -46,12 +49,17 @@ def lib():
         L.oracle_kmean.argtypes = [P, i32, i32, i32, i32, P, P]
         L.oracle_quantize_qk.restype = i32
         L.oracle_quantize_qk.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_quantize_q.restype = i32
+        L.oracle_quantize_q.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        L.oracle_quantize_k.restype = i32
+        L.oracle_quantize_k.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
         L.oracle_quantize_v.restype = i32
         L.oracle_quantize_v.argtypes = [P, i32, i32, i32, i32, P, P]
         L.oracle_qk_int32.restype = None
-        L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, P, i32, P]
+        L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P]
         L.oracle_attn_rows.restype = i32
-        L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, P, i32, P, P]
+        L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                       P, i32, P, P]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -104,19 +112,22 @@ def kmean(K_bits, dtype):
 
 
 def quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k):
+    """INT8 blocks of Q [B,Hq,Nq,d]; K mean and INT8 blocks of the smoothed K [B,Hkv,Nkv,d]."""
     Q_bits = _c(Q_bits, np.uint16)
     K_bits = _c(K_bits, np.uint16)
-    B, H, N, d = Q_bits.shape
-    assert K_bits.shape == Q_bits.shape
-    qc = np.empty((B, H, N, d), np.int8)
-    kc = np.empty((B, H, N, d), np.int8)
-    qs = np.empty((B, H, N // blk_q), np.float32)
-    ks = np.empty((B, H, N // blk_k), np.float32)
-    mu = np.empty((B, H, d), np.float32)
-    rc = lib().oracle_quantize_qk(_p(Q_bits), _p(K_bits), dtype, B * H, N, d, blk_q, blk_k,
-                                  _p(qc), _p(qs), _p(kc), _p(ks), _p(mu))
+    B, Hq, Nq, d = Q_bits.shape
+    Bk, Hkv, Nkv, dk = K_bits.shape
+    if Bk != B or dk != d:
+        raise ValueError("Q and K must share B and d")
+    qc = np.empty((B, Hq, Nq, d), np.int8)
+    kc = np.empty((B, Hkv, Nkv, d), np.int8)
+    qs = np.empty((B, Hq, Nq // blk_q), np.float32)
+    ks = np.empty((B, Hkv, Nkv // blk_k), np.float32)
+    mu = np.empty((B, Hkv, d), np.float32)
+    rc = lib().oracle_quantize_q(_p(Q_bits), dtype, B * Hq, Nq, d, blk_q, _p(qc), _p(qs))
+    rc |= lib().oracle_quantize_k(_p(K_bits), dtype, B * Hkv, Nkv, d, blk_k, _p(kc), _p(ks), _p(mu))
     if rc != 0:
-        raise ValueError("oracle_quantize_qk: unsupported shape")
+        raise ValueError("oracle quantize: unsupported shape")
     return dict(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks, k_mean=mu)
 
 
@@ -132,22 +143,24 @@ def quantize_v(V_bits, dtype):
 
 
 def qk_int32(q_codes, k_codes, rows):
+    """Exact int32 scores of flat query rows ``bh*Nq + i`` against every key of their K head: [nrows, Nkv]."""
     q_codes = _c(q_codes, np.int8)
     k_codes = _c(k_codes, np.int8)
-    B, H, N, d = q_codes.shape
+    B, Hq, Nq, d = q_codes.shape
+    _, Hkv, Nkv, _ = k_codes.shape
     rows = _c(rows, np.int64)
-    out = np.empty((rows.size, N), np.int32)
-    lib().oracle_qk_int32(_p(q_codes), _p(k_codes), B * H, N, d, _p(rows), rows.size, _p(out))
+    out = np.empty((rows.size, Nkv), np.int32)
+    lib().oracle_qk_int32(_p(q_codes), _p(k_codes), B, Hq, Hkv, Nq, Nkv, d, _p(rows), rows.size, _p(out))
     return out
 
 
 def attn_rows(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, rows=None, kv_tile=KV_TILE,
               want_p=False):
-    """Oracle attention for flat query rows ``bh*N + i`` (all rows when None).
+    """Oracle attention for flat query rows ``bh*Nq + i`` (all rows when None).
 
     ``qk`` is the dict returned by :func:`quantize_qk`; ``v_codes`` is in the
-    natural [B,H,N,d] layout.  Returns O [nrows, d] fp32 (and the FP8 codes of
-    P~ [nrows, N] when ``want_p``).
+    natural [B,Hkv,Nkv,d] layout.  Returns O [nrows, d] fp32 (and the FP8 codes
+    of P~ [nrows, Nkv] when ``want_p``).
     """
     qc = _c(qk["q_codes"], np.int8)
     kc = _c(qk["k_codes"], np.int8)
@@ -155,14 +168,16 @@ def attn_rows(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, rows=None, k
     ks = _c(qk["k_scale"], np.float32)
     vc = _c(v_codes, np.uint8)
     vs = _c(v_scale, np.float32)
-    B, H, N, d = qc.shape
+    B, Hq, Nq, d = qc.shape
+    _, Hkv, Nkv, _ = kc.shape
     if rows is None:
-        rows = np.arange(B * H * N, dtype=np.int64)
+        rows = np.arange(B * Hq * Nq, dtype=np.int64)
     rows = _c(rows, np.int64)
     out = np.empty((rows.size, d), np.float32)
-    p = np.empty((rows.size, N), np.uint8) if want_p else None
-    rc = lib().oracle_attn_rows(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B * H, N, d, blk_q, blk_k,
-                                kv_tile, int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
+    p = np.empty((rows.size, Nkv), np.uint8) if want_p else None
+    rc = lib().oracle_attn_rows(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B, Hq, Hkv, Nq, Nkv, d, blk_q,
+                                blk_k, kv_tile, int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out),
+                                _p(p))
     if rc != 0:
         raise ValueError("oracle_attn_rows: unsupported arguments")
     return (out, p) if want_p else out
@@ -179,31 +194,36 @@ def run(Q_bits, K_bits, V_bits, dtype, blk_q, blk_k, causal, sm_scale, rows=None
 
 # ---------------------------------------------------------------- exact reference
 def exact_attention(Q, K, V, causal, sm_scale, rows=None, chunk=256):
-    """softmax(Q K^T * sm_scale [+ causal mask]) V in fp64 from float inputs [B,H,N,d].
+    """softmax(Q K^T * sm_scale [+ causal mask]) V in fp64 from float inputs.
 
-    Plain definition, evaluated in row chunks so that long sequences fit in memory.
-    Returns [nrows, d] for flat rows ``bh*N + i`` (all rows when None).
+    Plain definition, evaluated in row chunks so that long sequences fit in
+    memory.  Q [B,Hq,Nq,d]; K, V [B,Hkv,Nkv,d]; query head h reads K/V head
+    h // (Hq // Hkv); causal: key j visible to query i iff j <= i + Nkv - Nq.
+    Returns [nrows, d] for flat rows ``bh*Nq + i`` (all rows when None).
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
-    B, H, N, d = Q.shape
-    Qf, Kf, Vf = Q.reshape(B * H, N, d), K.reshape(B * H, N, d), V.reshape(B * H, N, d)
+    B, Hq, Nq, d = Q.shape
+    _, Hkv, Nkv, _ = K.shape
+    group = Hq // Hkv
+    Qf, Kf, Vf = Q.reshape(B * Hq, Nq, d), K.reshape(B * Hkv, Nkv, d), V.reshape(B * Hkv, Nkv, d)
     if rows is None:
-        rows = np.arange(B * H * N, dtype=np.int64)
+        rows = np.arange(B * Hq * Nq, dtype=np.int64)
     rows = np.asarray(rows, np.int64)
     out = np.empty((rows.size, d), np.float64)
     for s in range(0, rows.size, chunk):
         r = rows[s:s + chunk]
-        bh, i = r // N, r % N
+        bh, i = r // Nq, r % Nq
         for h in np.unique(bh):
             sel = np.nonzero(bh == h)[0]
             qi = i[sel]
-            logits = (Qf[h][qi] @ Kf[h].T) * sm_scale
+            hk = (h // Hq) * Hkv + (h % Hq) // group
+            logits = (Qf[h][qi] @ Kf[hk].T) * sm_scale
             if causal:
-                logits = np.where(np.arange(N)[None, :] <= qi[:, None], logits, -np.inf)
+                logits = np.where(np.arange(Nkv)[None, :] <= qi[:, None] + (Nkv - Nq), logits, -np.inf)
             logits -= logits.max(axis=1, keepdims=True)
             w = np.exp(logits)
             w /= w.sum(axis=1, keepdims=True)
-            out[s + sel] = w @ Vf[h]
+            out[s + sel] = w @ Vf[hk]
     return out

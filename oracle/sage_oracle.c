@@ -166,23 +166,37 @@ static void quant_block_i8(const float* x, size_t n, int8_t* codes, float* delta
 /* Q, K: [BH, N, d] (float16/bfloat16 raw bits).  Outputs: q_codes, k_codes
  * [BH, N, d] int8; q_scale [BH, N/blk_q]; k_scale [BH, N/blk_k]; k_mean [BH, d].
  * Returns 0, or -1 for a shape the method does not define. */
-int oracle_quantize_qk(const uint16_t* Q, const uint16_t* K, int dtype, int BH, int N, int d,
-                       int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
-                       float* k_scale, float* k_mean) {
-  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1 || N % blk_q || N % blk_k) return -1;
-  int nbq = N / blk_q, nbk = N / blk_k;
+/* Q: blocks of blk_q tokens of one head, all d channels.  Q tensor [BH, N, d]. */
+int oracle_quantize_q(const uint16_t* Q, int dtype, int BH, int N, int d, int blk_q, int8_t* q_codes,
+                      float* q_scale) {
+  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || N % blk_q) return -1;
+  int nbq = N / blk_q;
 #pragma omp parallel for schedule(dynamic)
   for (int bh = 0; bh < BH; bh++) {
     const uint16_t* Qh = Q + (size_t)bh * N * d;
-    const uint16_t* Kh = K + (size_t)bh * N * d;
-    float* mu = k_mean + (size_t)bh * d;
-    kmean_head(Kh, dtype, N, d, mu, NULL);
-    float* buf = (float*)malloc(sizeof(float) * (size_t)(blk_q > blk_k ? blk_q : blk_k) * d);
+    float* buf = (float*)malloc(sizeof(float) * (size_t)blk_q * d);
     for (int b = 0; b < nbq; b++) {
       for (size_t k = 0; k < (size_t)blk_q * d; k++) buf[k] = load_in(Qh, (size_t)b * blk_q * d + k, dtype);
       quant_block_i8(buf, (size_t)blk_q * d, q_codes + (size_t)bh * N * d + (size_t)b * blk_q * d,
                      q_scale + (size_t)bh * nbq + b);
     }
+    free(buf);
+  }
+  return 0;
+}
+
+/* K: per-head channel mean over all N tokens (step 1), then blocks of blk_k
+ * tokens of the smoothed K.  K tensor [BH, N, d]. */
+int oracle_quantize_k(const uint16_t* K, int dtype, int BH, int N, int d, int blk_k, int8_t* k_codes,
+                      float* k_scale, float* k_mean) {
+  if (BH < 1 || N < 1 || d < 1 || blk_k < 1 || N % blk_k) return -1;
+  int nbk = N / blk_k;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    const uint16_t* Kh = K + (size_t)bh * N * d;
+    float* mu = k_mean + (size_t)bh * d;
+    kmean_head(Kh, dtype, N, d, mu, NULL);
+    float* buf = (float*)malloc(sizeof(float) * (size_t)blk_k * d);
     for (int b = 0; b < nbk; b++) {
       for (int t = 0; t < blk_k; t++)
         for (int c = 0; c < d; c++) {
@@ -195,6 +209,14 @@ int oracle_quantize_qk(const uint16_t* Q, const uint16_t* K, int dtype, int BH, 
     free(buf);
   }
   return 0;
+}
+
+/* Q and K of the same shape [BH, N, d] */
+int oracle_quantize_qk(const uint16_t* Q, const uint16_t* K, int dtype, int BH, int N, int d,
+                       int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                       float* k_scale, float* k_mean) {
+  if (oracle_quantize_q(Q, dtype, BH, N, d, blk_q, q_codes, q_scale)) return -1;
+  return oracle_quantize_k(K, dtype, BH, N, d, blk_k, k_codes, k_scale, k_mean);
 }
 
 /* exported for tests: the int64 fixed-point channel sums and the mean */
@@ -233,22 +255,32 @@ int oracle_quantize_v(const uint16_t* V, int dtype, int BH, int N, int d, uint8_
 }
 
 /* ------------------------------------------------------------------------ */
-/* Step 4 (diagnostic): exact int32 S = q_codes . k_codes over d for chosen   */
-/* query rows against every key of the same head.  rows[] are flat indices   */
-/* bh*N + i.  out: [nrows, N].                                               */
+/* Head sharing: query head h of batch b reads key/value head h / (Hq/Hkv)   */
+/* of the same batch (one head each when Hq = Hkv; grouped-query attention   */
+/* otherwise).  The flat index of that head among the B*Hkv K/V heads:       */
 /* ------------------------------------------------------------------------ */
-void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int BH, int N, int d,
-                     const int64_t* rows, int nrows, int32_t* out) {
-  (void)BH;
+static int64_t kv_head(int64_t bh, int Hq, int Hkv) {
+  return (bh / Hq) * Hkv + (bh % Hq) / (Hq / Hkv);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 4 (diagnostic): exact int32 S = q_codes . k_codes over d for chosen   */
+/* query rows against every key of the K/V head they read.  Q codes          */
+/* [B*Hq, Nq, d], K codes [B*Hkv, Nkv, d]; rows[] are flat indices bh*Nq + i */
+/* out: [nrows, Nkv].                                                        */
+/* ------------------------------------------------------------------------ */
+void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int B, int Hq, int Hkv, int Nq, int Nkv,
+                     int d, const int64_t* rows, int nrows, int32_t* out) {
+  (void)B;
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < nrows; r++) {
-    int64_t bh = rows[r] / N, i = rows[r] % N;
-    const int8_t* q = q_codes + ((size_t)bh * N + i) * d;
-    for (int j = 0; j < N; j++) {
-      const int8_t* k = k_codes + ((size_t)bh * N + j) * d;
+    int64_t bh = rows[r] / Nq, i = rows[r] % Nq, bk = kv_head(bh, Hq, Hkv);
+    const int8_t* q = q_codes + ((size_t)bh * Nq + i) * d;
+    for (int j = 0; j < Nkv; j++) {
+      const int8_t* k = k_codes + ((size_t)bk * Nkv + j) * d;
       int32_t s = 0;
       for (int c = 0; c < d; c++) s += (int32_t)q[c] * (int32_t)k[c];
-      out[(size_t)r * N + j] = s;
+      out[(size_t)r * Nkv + j] = s;
     }
   }
 }
@@ -258,7 +290,9 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int BH, int N
 /* tiles of kv_tile keys are visited in ascending order, one pass, as in the */
 /* tiled online softmax ([BLOG] "How FlashAttention reduces memory            */
 /* traffic"); tiles with no visible key (causal) are skipped ([BLOG] causal   */
-/* masking changes which blocks are skipped).  Per tile:                     */
+/* masking changes which blocks are skipped).  Causal visibility is aligned */
+/* at the end of the sequences: key j is visible to query i iff             */
+/* j <= i + (Nkv - Nq) (the usual top-left rule when Nq = Nkv).  Per tile:  */
 /*   S_j   = sum_c q_c k_c                       (int32, exact)              */
 /*   c2_j  = RN(RN(dQ * dK_j) * s2),  s2 = RN(sm_scale * log2 e)             */
 /*   u_j   = RN(float(S_j) * c2_j);  m' = max(m, max_j u_j)                  */
@@ -272,28 +306,33 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int BH, int N
 /*   Oacc_c = fma(alpha, Oacc_c, Oblk_c)             (outer fp32 level)      */
 /*   m = m'                                                                  */
 /* O_c = Oacc_c * deltaV_c / l.  ([SA2] abstract: two-level accumulation of  */
-/* FP8 P~V.)  rows[] are flat indices bh*N + i; out: [nrows, d] fp32;        */
-/* p_codes (optional): [nrows, N], 0 where a key is not visible.             */
+/* FP8 P~V.)  Q codes/scales of B*Hq heads of Nq tokens, K and V codes and  */
+/* scales of B*Hkv heads of Nkv tokens (kv_head above); rows[] are flat     */
+/* indices bh*Nq + i; out: [nrows, d] fp32; p_codes (optional):             */
+/* [nrows, Nkv], 0 where a key is not visible.                               */
 /* ------------------------------------------------------------------------ */
 static const float LOG2E_F = 0x1.715476p+0f;   /* RN(log2 e) */
 
 int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
-                     const float* k_scale, const uint8_t* v_codes, const float* v_scale, int BH, int N,
-                     int d, int blk_q, int blk_k, int kv_tile, int causal, float sm_scale,
-                     const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
-  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1 || kv_tile < 1) return -1;
-  if (N % blk_q || N % blk_k || N % kv_tile) return -1;
+                     const float* k_scale, const uint8_t* v_codes, const float* v_scale, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int kv_tile, int causal,
+                     float sm_scale, const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nkv < 1 || d < 1) return -1;
+  if (blk_q < 1 || blk_k < 1 || kv_tile < 1) return -1;
+  if (Nq % blk_q || Nkv % blk_k || Nkv % kv_tile) return -1;
+  if (causal && Nkv < Nq) return -1;   /* the first queries would see no key */
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return -1;
   const float s2 = sm_scale * LOG2E_F;
-  const int nbq = N / blk_q, nbk = N / blk_k;
+  const int nbq = Nq / blk_q, nbk = Nkv / blk_k;
+  const int64_t off = (int64_t)Nkv - Nq;
   double vdec[256];
   for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
   for (int r = 0; r < nrows; r++)
-    if (rows[r] < 0 || rows[r] >= (int64_t)BH * N) return -1;
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * Hq * Nq) return -1;
 #pragma omp parallel for schedule(dynamic)
   for (int r = 0; r < nrows; r++) {
-    int64_t bh = rows[r] / N, i = rows[r] % N;
-    const int8_t* q = q_codes + ((size_t)bh * N + i) * d;
+    int64_t bh = rows[r] / Nq, i = rows[r] % Nq, bk = kv_head(bh, Hq, Hkv);
+    const int8_t* q = q_codes + ((size_t)bh * Nq + i) * d;
     const float dq = q_scale[(size_t)bh * nbq + i / blk_q];
     int32_t* S = (int32_t*)malloc(sizeof(int32_t) * kv_tile);
     float* c2 = (float*)malloc(sizeof(float) * kv_tile);
@@ -303,19 +342,23 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
     double* oblk = (double*)malloc(sizeof(double) * d);
     float m = 0.0f, l = 0.0f;
     int first = 1;
-    if (p_codes) memset(p_codes + (size_t)r * N, 0, N);
-    for (int j0 = 0; j0 < N; j0 += kv_tile) {
+    if (p_codes) memset(p_codes + (size_t)r * Nkv, 0, Nkv);
+    for (int j0 = 0; j0 < Nkv; j0 += kv_tile) {
       int nvis = kv_tile;
-      if (causal) { if (j0 > i) break; if (i - j0 + 1 < nvis) nvis = (int)(i - j0 + 1); }
+      if (causal) {
+        const int64_t last = i + off;   /* last visible key */
+        if (j0 > last) break;
+        if (last - j0 + 1 < nvis) nvis = (int)(last - j0 + 1);
+      }
       /* scores of the visible keys j0 .. j0+nvis-1 */
       float mt = -INFINITY;
       for (int jj = 0; jj < nvis; jj++) {
         int j = j0 + jj;
-        const int8_t* k = k_codes + ((size_t)bh * N + j) * d;
+        const int8_t* k = k_codes + ((size_t)bk * Nkv + j) * d;
         int32_t s = 0;
         for (int c = 0; c < d; c++) s += (int32_t)q[c] * (int32_t)k[c];
         S[jj] = s;
-        c2[jj] = (dq * k_scale[(size_t)bh * nbk + j / blk_k]) * s2;
+        c2[jj] = (dq * k_scale[(size_t)bk * nbk + j / blk_k]) * s2;
         float u = (float)s * c2[jj];
         if (u > mt) mt = u;
       }
@@ -327,12 +370,12 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
         pt[jj] = oracle_exp2f(fmaf((float)S[jj], c2[jj], -mm));
         rowsum += pt[jj];
         ph[jj] = oracle_e4m3_encode(pt[jj]);
-        if (p_codes) p_codes[(size_t)r * N + j0 + jj] = ph[jj];
+        if (p_codes) p_codes[(size_t)r * Nkv + j0 + jj] = ph[jj];
       }
       for (int c = 0; c < d; c++) {
         double acc = 0.0;
         for (int jj = 0; jj < nvis; jj++)
-          acc += vdec[ph[jj]] * vdec[v_codes[((size_t)bh * N + j0 + jj) * d + c]];
+          acc += vdec[ph[jj]] * vdec[v_codes[((size_t)bk * Nkv + j0 + jj) * d + c]];
         oblk[c] = acc;
       }
       for (int c = 0; c < d; c++) oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);
@@ -341,7 +384,7 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
       first = 0;
     }
     for (int c = 0; c < d; c++)
-      out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bh * d + c]) / (double)l);
+      out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
     free(S); free(c2); free(pt); free(ph); free(oacc); free(oblk);
   }
   return 0;

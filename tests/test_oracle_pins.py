@@ -372,3 +372,80 @@ def test_online_softmax_matches_single_tile_reference_in_the_exact_limit():
     qk, (vc, vs), O64 = _run(w, Q, K, V, kv_tile=64)
     O256 = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, False, w.sm_scale, kv_tile=256)
     assert np.abs(O64 - O256).max() < 0.05
+
+
+# ------------------------------------------------------------------ head sharing and unequal lengths
+def _gqa_inputs(B=1, Hq=4, Hkv=2, Nq=256, Nkv=256, d=64, seed=11):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, Hq, Nq, d)).astype(np.float32)
+    K = (rng.standard_normal((B, Hkv, Nkv, d)) + 2 * rng.standard_normal((B, Hkv, 1, d))).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, Nkv, d)).astype(np.float32)
+    return Q, K, V
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_equal_repeated_kv_heads(causal):
+    """Query head h reading K/V head h // (Hq/Hkv) is the same computation as
+    every query head owning a copy of that K/V head: bit for bit."""
+    Q, K, V = _gqa_inputs()
+    g = Q.shape[1] // K.shape[1]
+    Kr, Vr = np.repeat(K, g, axis=1), np.repeat(V, g, axis=1)
+    qb, kb, vb, krb, vrb = (_f16_bits(a) for a in (Q, K, V, Kr, Vr))
+    qk, (vc, vs), (O, P) = orc.run(qb, kb, vb, 0, 64, 64, causal, 0.125, want_p=True)
+    qk_r, (vc_r, vs_r), (O_r, P_r) = orc.run(qb, krb, vrb, 0, 64, 64, causal, 0.125, want_p=True)
+    assert qk["k_codes"].shape[1] == 2 and qk_r["k_codes"].shape[1] == 4
+    assert np.array_equal(np.repeat(qk["k_codes"], g, axis=1), qk_r["k_codes"])
+    assert np.array_equal(O, O_r) and np.array_equal(P, P_r)
+    # and the head mapping is h // g, not h % Hkv: swapping the two K/V heads changes the result
+    qk_s, (vc_s, vs_s), O_s = orc.run(qb, kb[:, ::-1].copy(), vb[:, ::-1].copy(), 0, 64, 64, causal, 0.125)
+    assert not np.array_equal(O, O_s)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fewer_queries_equal_the_last_rows_of_the_square_problem(causal):
+    """Nq < Nkv with causal visibility aligned at the end (key j visible to query
+    i iff j <= i + Nkv - Nq): the Nq queries are the last Nq rows of the square
+    problem whose queries extend over all Nkv positions (the Q blocks line up
+    because Nkv - Nq is a multiple of the block)."""
+    Q, K, V = _gqa_inputs(Hq=2, Hkv=2, Nq=384, Nkv=384, seed=12)
+    Qs = Q[:, :, 128:]
+    qb, qsb, kb, vb = (_f16_bits(a) for a in (Q, Qs, K, V))
+    _, _, (O, P) = orc.run(qb, kb, vb, 0, 128, 64, causal, 0.125, want_p=True)
+    _, _, (Os, Ps) = orc.run(qsb, kb, vb, 0, 128, 64, causal, 0.125, want_p=True)
+    rows = (np.arange(2)[:, None] * 384 + 128 + np.arange(256)[None, :]).ravel()
+    assert np.array_equal(Os, O[rows]) and np.array_equal(Ps, P[rows])
+
+
+def test_unequal_lengths_and_groups_against_fp64_and_loops():
+    Q, K, V = _gqa_inputs(B=2, Hq=4, Hkv=1, Nq=128, Nkv=320, seed=13)
+    qb, kb, vb = (_f16_bits(a) for a in (Q, K, V))
+    Qv, Kv, Vv = (_f16_vals(a) for a in (Q, K, V))
+    for causal in (False, True):
+        _, _, O = orc.run(qb, kb, vb, 0, 64, 64, causal, 0.125)
+        ref = orc.exact_attention(Qv, Kv, Vv, causal, 0.125)
+        a, b = O.astype(np.float64).ravel(), ref.ravel()
+        assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.995
+    # the fp64 reference itself, one row by loops: query 5 of head 3 of batch 1
+    # reads K/V head 0 and, causally, keys 0 .. 5 + 320 - 128
+    got = orc.exact_attention(Qv, Kv, Vv, True, 0.125, rows=np.array([(1 * 4 + 3) * 128 + 5]))
+    last = 5 + 320 - 128
+    q64, k64 = Qv[1, 3, 5].astype(np.float64), Kv[1, 0].astype(np.float64)
+    logits = [float(q64 @ k64[j]) * 0.125 for j in range(last + 1)]
+    mx = max(logits)
+    wts = [math.exp(x - mx) for x in logits]
+    want = sum(wts[j] * Vv[1, 0, j].astype(np.float64) for j in range(last + 1)) / sum(wts)
+    assert np.abs(got[0] - want).max() < 1e-12
+
+
+def test_unequal_shapes_rejected():
+    Q, K, V = _gqa_inputs(Hq=3, Hkv=2)
+    qk = orc.quantize_qk(_f16_bits(Q), _f16_bits(K), 0, 64, 64)
+    vc, vs = orc.quantize_v(_f16_bits(V), 0)
+    with pytest.raises(ValueError):   # 3 query heads cannot share 2 K/V heads evenly
+        orc.attn_rows(qk, vc, vs, 64, 64, False, 0.125)
+    Q, K, V = _gqa_inputs(Nq=256, Nkv=128)
+    qk = orc.quantize_qk(_f16_bits(Q), _f16_bits(K), 0, 64, 64)
+    vc, vs = orc.quantize_v(_f16_bits(V), 0)
+    with pytest.raises(ValueError):   # causal with more queries than keys: the first queries see nothing
+        orc.attn_rows(qk, vc, vs, 64, 64, True, 0.125)
+    orc.attn_rows(qk, vc, vs, 64, 64, False, 0.125, rows=np.array([0, 255]))   # non-causal is fine
