@@ -115,7 +115,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} Hkv={w.Hkv} Nkv={w.Nkv} d={w.d} {w.dtype} "
+        f"causal={w.causal}")
     Q, K, V = synth.make_inputs(w)
     Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
     if args.pmc_calibration:
@@ -125,9 +126,9 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
 
-    B, H, N, d = w.B, w.H, w.N, w.d
-    ws_qk = torch.empty(max(sage.sage_quantize_qk_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(max(sage.sage_quantize_v_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=dev)
+    B, H, N, d, Hkv, Nkv = w.B, w.H, w.N, w.d, w.Hkv, w.Nkv
+    ws_qk = torch.empty(max(sage.sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(max(sage.sage_quantize_v_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, N, d), dtype=w.torch_dtype, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -162,10 +163,9 @@ def main():
         f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
         f"{100 * attn_tops / MFMA_PEAK_TOPS:.1f}% of peak)")
 
-    n_el = B * H * N * d
-    in_bytes = 2 * n_el                    # f16 / bf16 inputs
-    quant_alg = 3 * (in_bytes + n_el)      # Q, K, V: read the input, write 1-byte codes
-    quant_act = quant_alg + 2 * in_bytes   # the K-sum and V-max passes read K and V once more
+    q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
+    quant_alg = 3 * (q_el + 2 * kv_el)      # Q, K, V: read 2-byte inputs, write 1-byte codes
+    quant_act = quant_alg + 2 * 2 * kv_el   # the K-sum and V-max passes read K and V once more
     quant_avg = float(np.mean(quant_ms))
     quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
     log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "
@@ -181,7 +181,8 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8+fp8 (fp32 softmax)", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "in_dtype": w.dtype,
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "Hkv": Hkv, "Nkv": Nkv, "d": d, "causal": w.causal,
+                   "in_dtype": w.dtype,
                    "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_tile": sage.sage_kv_tile(), "parallelism": "none (1 GPU)"},
         "attn_kernel_ms": round(attn_avg, 4),
         "attn_kernel_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),

@@ -28,10 +28,16 @@
  *    is enqueued; then no output is touched.  A failed kernel launch returns
  *    SAGE_ERR_HIP.  Faults during execution surface at the caller's next
  *    synchronisation, as for any HIP work.
- *  - Tensors are contiguous, row-major, self-attention shaped [B, H, N, d]
- *    (the layout of PyTorch's scaled_dot_product_attention).
- *  - Supported: d in {64, 128}; N a multiple of 128 with 128 <= N <= 524288;
- *    blk_q in {64, 128}; blk_k = 64; B*H >= 1; sm_scale finite and > 0;
+ *  - Tensors are contiguous and row-major.  The plain entry points take
+ *    self-attention shaped [B, H, N, d] tensors (the layout of PyTorch's
+ *    scaled_dot_product_attention).  The _ex entry points also take
+ *    [B, N, H, d] inputs and outputs (layout SAGE_LAYOUT_BNHD), Hq query heads
+ *    sharing Hkv K/V heads (grouped heads: query head h reads K/V head
+ *    h / (Hq/Hkv)), and Nq queries against Nkv keys.  The quantized codes and
+ *    scales are always head-major, as documented below for H, N.
+ *  - Supported: d in {64, 128}; N (Nq and Nkv) a multiple of 128 with
+ *    128 <= N <= 524288; blk_q in {64, 128}; blk_k = 64; B*H >= 1; Hq a
+ *    multiple of Hkv; causal only with Nkv >= Nq; sm_scale finite and > 0;
  *    inputs finite.
  */
 #ifndef SAGE_H
@@ -55,6 +61,9 @@ enum {
 
 enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 };
 
+/* Memory layout of the fp16/bf16 inputs and of O in the _ex entry points. */
+enum { SAGE_LAYOUT_BHND = 0, SAGE_LAYOUT_BNHD = 1 };
+
 /* Human-readable text of a status code (static storage). */
 const char* sage_status_string(int status);
 
@@ -63,7 +72,8 @@ const char* sage_status_string(int status);
 int sage_kv_tile(void);
 
 /* Bytes of scratch memory sage_quantize_qk needs (int64 per-channel partial
- * sums of K, one row of d per 256 tokens of every head). */
+ * sums of K, one row of d per 256 tokens of every head).  It depends on K
+ * only: for sage_quantize_qk_ex pass H = Hkv and N = Nkv. */
 size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d);
 
 /*
@@ -89,6 +99,19 @@ int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, i
                      int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
                      float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sage_quantize_qk_ex -- sage_quantize_qk for Q of Hq heads and Nq tokens, K of
+ * Hkv heads and Nkv tokens (the mean of K runs over its own Nkv tokens), both
+ * in `layout` (same quantization as above).
+ * In:  Q [B,Hq,Nq,d] or [B,Nq,Hq,d]; K [B,Hkv,Nkv,d] or [B,Nkv,Hkv,d].
+ * Out: q_codes [B,Hq,Nq,d], q_scale [B,Hq,Nq/blk_q], k_codes [B,Hkv,Nkv,d],
+ *      k_scale [B,Hkv,Nkv/blk_k], k_mean [B,Hkv,d] (head-major whatever the
+ *      layout).  workspace: sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
+ */
+int sage_quantize_qk_ex(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
+                        int Nkv, int d, int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                        float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of scratch memory sage_quantize_v needs (fp32 per-channel partial
  * maxima, one row of d per 256 tokens of every head, plus one row per head). */
 size_t sage_quantize_v_workspace_bytes(int B, int H, int N, int d);
@@ -110,6 +133,13 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sage_quantize_v_ex -- sage_quantize_v with V in `layout`: [B,H,N,d] or
+ * [B,N,H,d] (H = Hkv, N = Nkv of the attention).  v_codes and v_scale as above.
+ */
+int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, int N, int d, uint8_t* v_codes,
+                       float* v_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sage_attn_fwd -- attention forward on the quantized operands.
  * (Tiled online softmax: blog section "How FlashAttention reduces memory
  * traffic"; FP8 P~ and two-level P~V accumulation: SageAttention2 abstract;
@@ -119,14 +149,15 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
  *   S_j    = sum_c q_codes[i,c] k_codes[j,c]               (int32, exact)
  *   c2     = (q_scale * k_scale_j) * (sm_scale * log2 e)   (fp32, in this order)
  *   m'     = max(m, max_j fp32(S_j) * c2)
- *   alpha  = X2(m - m')   (0 on the first tile)
- *   P~_j   = X2(fma(fp32(S_j), c2, -(m' - 8)))             (P~ scaled by 2^8)
+ *   alpha  = exp2(m - m')   (0 on the first tile)
+ *   P~_j   = exp2(fma(fp32(S_j), c2, -(m' - 8)))           (P~ scaled by 2^8)
  *   l      = fma(alpha, l, sum_j P~_j)
  *   O_blk  = sum_j e4m3(P~_j) * v_code_j                   (FP8 matrix cores)
- *   O_acc  = fma(alpha, O_acc, O_blk);  m = m'
+ *   O_acc  = alpha * O_acc + O_blk;  m = m'
  *   O[i,c] = O_acc[c] * v_scale[c] / l
- * X2(t) = p(f) * 2^n with n = floor(t), f = min(t - n, 1 - 2^-24) (fp32),
- *   p(f) = fma(fma(0x1.5beb9ep-2, f, 0x1.520a3p-1), f, 1).
+ * exp2 is the matrix core's companion fp32 exp2 (v_exp_f32, about 1 ulp), so
+ *   an FP8 code of P~ may differ by one step from one computed with exp2
+ *   rounded once from the exact value.
  * In:  the outputs of sage_quantize_qk (q_codes, q_scale, k_codes, k_scale)
  *      and sage_quantize_v (v_codes, v_scale), same B, H, N, d, blk_q, blk_k.
  * Out: O [B,H,N,d] of out_dtype (SAGE_F32, SAGE_F16 or SAGE_BF16; rounded to
@@ -135,6 +166,20 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
 int sage_attn_fwd(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                   const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
                   int blk_q, int blk_k, int causal, float sm_scale, void* stream);
+
+/*
+ * sage_attn_fwd_ex -- sage_attn_fwd with Hq query heads on Hkv K/V heads
+ * (query head h reads K/V head h / (Hq/Hkv)), Nq queries on Nkv keys, and O
+ * in `layout`.  Query row i is aligned with key i + (Nkv - Nq) (the queries
+ * are the last Nq positions of the sequence): under the causal mask key j is
+ * visible iff j <= i + Nkv - Nq, which needs Nkv >= Nq.
+ * In:  the outputs of sage_quantize_qk_ex and sage_quantize_v_ex for the same
+ *      B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k.
+ * Out: O [B,Hq,Nq,d] (SAGE_LAYOUT_BHND) or [B,Nq,Hq,d] (SAGE_LAYOUT_BNHD).
+ */
+int sage_attn_fwd_ex(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale, void* stream);
 
 /*
  * sage_attn_fwd_dump -- sage_attn_fwd through the same kernel code, which in
@@ -151,6 +196,16 @@ int sage_attn_fwd_dump(const int8_t* q_codes, const float* q_scale, const int8_t
                        const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N,
                        int d, int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel,
                        int32_t* s_dump, uint8_t* p_dump, void* stream);
+
+/*
+ * sage_attn_fwd_ex_dump -- sage_attn_fwd_ex with the dumps of
+ * sage_attn_fwd_dump: sel ids are (b*Hq + h) * (Nq/128) + qt; s_dump and
+ * p_dump are [n_sel, 128, Nkv].
+ */
+int sage_attn_fwd_ex_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                          const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B,
+                          int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                          const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, void* stream);
 
 #ifdef __cplusplus
 }

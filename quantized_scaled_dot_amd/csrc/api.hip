@@ -8,6 +8,12 @@
 
 namespace {
 
+#define SAGE_TRY(x)          \
+  do {                       \
+    int _s = (x);            \
+    if (_s != SAGE_OK) return _s; \
+  } while (0)
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_shape(int B, int H, int N, int d) {
@@ -20,18 +26,21 @@ int check_shape(int B, int H, int N, int d) {
   return SAGE_OK;
 }
 
+// Query heads Hq of Nq tokens, K/V heads Hkv of Nkv tokens, one memory layout.
+int check_shapes(int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d) {
+  if (layout != SAGE_LAYOUT_BHND && layout != SAGE_LAYOUT_BNHD) return SAGE_ERR_INVALID_ARG;
+  SAGE_TRY(check_shape(B, Hq, Nq, d));
+  SAGE_TRY(check_shape(B, Hkv, Nkv, d));
+  if (Hq % Hkv != 0) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
 int check_in_dtype(int dt) { return (dt == SAGE_F16 || dt == SAGE_BF16) ? SAGE_OK : SAGE_ERR_INVALID_ARG; }
 
 int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
-
-#define SAGE_TRY(x)          \
-  do {                       \
-    int _s = (x);            \
-    if (_s != SAGE_OK) return _s; \
-  } while (0)
 
 #define SAGE_PTR(p)                                    \
   do {                                                 \
@@ -40,14 +49,15 @@ int launch_status() {
   } while (0)
 
 int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
-                const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
-                int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump,
-                uint8_t* p_dump, bool dump, void* stream) {
-  SAGE_TRY(check_shape(B, H, N, d));
+                const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, bool dump, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
   if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (causal && Nkv < Nq) return SAGE_ERR_INVALID_ARG;   // the first rows would see no key
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
   SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
   SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O);
@@ -57,8 +67,8 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   }
   sage::AttnArgs a;
   a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
-  a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype;
-  a.BH = B * H; a.N = N; a.d = d; a.blk_q = blk_q; a.causal = causal;
+  a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.causal = causal;
   a.s2 = sm_scale * sage::kLog2e;
   a.sel = dump ? sel : nullptr; a.n_sel = dump ? n_sel : 0; a.s_dump = s_dump; a.p_dump = p_dump;
   (void)hipGetLastError();
@@ -73,8 +83,12 @@ extern "C" {
 const char* sage_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "SAGE_OK";
-    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG: null pointer, bad size, dtype or sm_scale";
-    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N % 128 == 0, N <= 2^19, blk_q in {64,128}, blk_k == 64";
+    case SAGE_ERR_INVALID_ARG:
+      return "SAGE_ERR_INVALID_ARG: null pointer, bad size, dtype, layout or sm_scale, Hq not a multiple of Hkv, "
+             "or causal with Nq > Nkv";
+    case SAGE_ERR_UNSUPPORTED:
+      return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N % 128 == 0, N <= 2^19 (Nq and Nkv), "
+             "blk_q in {64,128}, blk_k == 64";
     case SAGE_ERR_MISALIGNED: return "SAGE_ERR_MISALIGNED: pointer not 16-byte aligned";
     case SAGE_ERR_HIP: return "SAGE_ERR_HIP: kernel launch failed";
     case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
@@ -94,18 +108,19 @@ size_t sage_quantize_v_workspace_bytes(int B, int H, int N, int d) {
   return sage::quantize_v_workspace(B * H, N, d);
 }
 
-int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, int N, int d, int blk_q, int blk_k,
-                     int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale, float* k_mean, void* workspace,
-                     size_t workspace_bytes, void* stream) {
-  SAGE_TRY(check_shape(B, H, N, d));
+int sage_quantize_qk_ex(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
+                        int Nkv, int d, int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                        float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_in_dtype(in_dtype));
   if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
   if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
   SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
   SAGE_PTR(k_mean); SAGE_PTR(workspace);
-  if (workspace_bytes < sage::quantize_qk_workspace(B * H, N, d)) return SAGE_ERR_WORKSPACE;
+  if (workspace_bytes < sage::quantize_qk_workspace(B * Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
   sage::QuantQKArgs a;
-  a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.BH = B * H; a.N = N; a.d = d; a.blk_q = blk_q;
+  a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q;
   a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale; a.k_mean = k_mean;
   a.workspace = workspace;
   (void)hipGetLastError();
@@ -113,33 +128,62 @@ int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, i
   return launch_status();
 }
 
-int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  SAGE_TRY(check_shape(B, H, N, d));
+int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, int N, int d, int blk_q, int blk_k,
+                     int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale, float* k_mean, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return sage_quantize_qk_ex(Q, K, in_dtype, SAGE_LAYOUT_BHND, B, H, H, N, N, d, blk_q, blk_k, q_codes, q_scale,
+                             k_codes, k_scale, k_mean, workspace, workspace_bytes, stream);
+}
+
+int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, int N, int d, uint8_t* v_codes,
+                       float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, H, H, N, N, d));
   SAGE_TRY(check_in_dtype(in_dtype));
   SAGE_PTR(V); SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(workspace);
   if (workspace_bytes < sage::quantize_v_workspace(B * H, N, d)) return SAGE_ERR_WORKSPACE;
   sage::QuantVArgs a;
-  a.V = V; a.is_bf16 = in_dtype == SAGE_BF16; a.BH = B * H; a.N = N; a.d = d;
+  a.V = V; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.H = H; a.N = N; a.d = d;
   a.v_codes = v_codes; a.v_scale = v_scale; a.workspace = workspace;
   (void)hipGetLastError();
   sage::launch_quantize_v(a, (hipStream_t)stream);
   return launch_status();
 }
 
+int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return sage_quantize_v_ex(V, in_dtype, SAGE_LAYOUT_BHND, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes,
+                            stream);
+}
+
+int sage_attn_fwd_ex(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale, void* stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, blk_q, blk_k, causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream);
+}
+
+int sage_attn_fwd_ex_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                          const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B,
+                          int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                          const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, void* stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream);
+}
+
 int sage_attn_fwd(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                   const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
                   int blk_q, int blk_k, int causal, float sm_scale, void* stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
-                     causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream);
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, SAGE_LAYOUT_BHND, B, H, H, N,
+                     N, d, blk_q, blk_k, causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream);
 }
 
 int sage_attn_fwd_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                        const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int B, int H, int N, int d,
                        int blk_q, int blk_k, int causal, float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump,
                        uint8_t* p_dump, void* stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
-                     causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream);
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, SAGE_LAYOUT_BHND, B, H, H, N,
+                     N, d, blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream);
 }
 
 }  // extern "C"

@@ -1,7 +1,10 @@
 // Fused quantized attention forward for gfx950 (CDNA4).
 //
-// One workgroup = 128 query rows of one head (4 waves x 32 rows); KV tiles of
-// 64 keys are staged in LDS and visited in ascending order.
+// One workgroup = 128 query rows of one query head (4 waves x 32 rows); KV
+// tiles of 64 keys of its K/V head (query head h of Hq reads K/V head
+// h / (Hq/Hkv)) are staged in LDS and visited in ascending order.  With fewer
+// queries than keys, query row i is aligned with key i + (Nkv - Nq): under
+// the causal mask it sees keys 0 .. i + Nkv - Nq.
 //
 // LDS: two buffers of {K tile in MFMA order, rows padded to d+16 bytes;
 // V tile channel-major, rows padded to 80 bytes}.
@@ -11,7 +14,8 @@
 //   (transposed so that each lane holds one query row: lane l owns query l%32
 //    and 32 of the 64 keys; lanes l and l^32 share a row)
 //   row max on the int32 scores, dequantisation c2 = dQ*dK*sm_scale*log2e,
-//   P~ = X2(S*c2 - (m' - 8)) on the VALU, packed to FP8 e4m3 in registers
+//   P~ = exp2(S*c2 - (m' - 8)) (fp32 v_exp_f32) on the VALU, packed to FP8
+//   e4m3 in registers
 //   O_acc^T[32 ch x 32 q] += V^T_tile . P^T             d/32 v_mfma_scale_f32_32x32x64_f8f6f4
 //   (inner level: the instruction's 64-product block sum; outer level: the
 //    exact fp32 accumulate into its C operand; O_acc is rescaled by alpha
@@ -39,7 +43,7 @@ struct AttnK {
   const uint8_t* v_codes;
   const float* v_scale;
   void* O;
-  int N, nqt, nbq, blk_q;
+  int Hq, g, Nq, Nkv, off, nqt, nbq, blk_q, nhd;   // g = Hq/Hkv; off = Nkv - Nq
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -108,25 +112,36 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int li = lane & 31, lg = lane >> 5;
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
-  // on XCD b % 8).  When the heads divide evenly, XCD x owns heads x, x+8, ...
-  // so each head's K/V stays in one L2.  Non-causal: an XCD walks its heads
-  // one after another.  Causal (work grows with the query tile): an XCD walks
-  // its query tiles heaviest first across all of its heads, so the long
-  // tiles never start last.
+  // on XCD b % 8).  Flat query head bh = b*Hq + h reads flat K/V head
+  // bh / g (the g query heads of a K/V head are consecutive).  When the K/V
+  // heads divide evenly, XCD x owns K/V heads x, x+8, ... with all of their
+  // query heads, so each K/V head stays in one L2.  Non-causal: an XCD walks
+  // its K/V heads one after another.  Causal (work grows with the query
+  // tile): an XCD walks its query tiles heaviest first across all of its
+  // heads, so the long tiles never start last.
   const int G = gridDim.x, b = blockIdx.x;
-  const int BH = G / p.nqt;
+  const int BHq = G / p.nqt, BHkv = BHq / p.g;
   int bh, qt;
-  if (BH % 8 == 0) {
-    const int x = b % 8, j = b / 8, hpx = BH / 8;   // XCD, its j-th item, heads per XCD
-    if (CAUSAL) { bh = (j % hpx) * 8 + x; qt = p.nqt - 1 - j / hpx; }
-    else { bh = (j / p.nqt) * 8 + x; qt = j % p.nqt; }
+  if (BHkv % 8 == 0) {
+    const int x = b % 8, j = b / 8, hpx = BHkv / 8;   // XCD, its j-th item, K/V heads per XCD
+    if (CAUSAL) {
+      const int r = j % (hpx * p.g);
+      bh = ((r % hpx) * 8 + x) * p.g + r / hpx;
+      qt = p.nqt - 1 - j / (hpx * p.g);
+    } else {
+      const int u = p.g * p.nqt, r = j % u;           // units of one K/V head
+      bh = ((j / u) * 8 + x) * p.g + r / p.nqt;
+      qt = r % p.nqt;
+    }
   } else if (CAUSAL) {
-    bh = b % BH; qt = p.nqt - 1 - b / BH;           // heaviest first overall
+    bh = b % BHq; qt = p.nqt - 1 - b / BHq;          // heaviest first overall
   } else {
     bh = b / p.nqt; qt = b % p.nqt;
   }
-  const int N = p.N;
+  const int bhkv = bh / p.g;
+  const int Nq = p.Nq, Nkv = p.Nkv, off = p.off;
   const int q0 = qt * kQTile, qrow0 = q0 + wave * 32, row = qrow0 + li;
+  const int lastk = row + off;   // causal: the last key this row sees
 
   int dump_idx = -1;
   if (DUMP) {
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
 
   v4i qreg[KS];
   {
-    const int8_t* qp = p.q_codes + ((size_t)bh * N + row) * D + 16 * lg;
+    const int8_t* qp = p.q_codes + ((size_t)bh * Nq + row) * D + 16 * lg;
 #pragma unroll
     for (int s = 0; s < KS; s++) qreg[s] = *(const v4i*)(qp + 32 * s);
   }
@@ -155,8 +170,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
   constexpr int JK = (NKI + 3) / 4, JV = (NVI + 3) / 4;
-  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bh * N * D, (uint32_t)(N * D));
-  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bh * N * D, (uint32_t)(N * D));
+  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bhkv * Nkv * D, (uint32_t)(Nkv * D));
+  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * Nkv * D, (uint32_t)(Nkv * D));
   uint32_t koff[JK], voff[JV];
 #pragma unroll
   for (int j = 0; j < JK; j++) {
@@ -197,8 +212,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
 
-  const int ntiles = CAUSAL ? (q0 + kQTile) / kKTile : N / kKTile;
-  const float* kscale = p.k_scale + (size_t)bh * (N / kKTile);
+  const int ntiles = CAUSAL ? (q0 + kQTile + off) / kKTile : Nkv / kKTile;
+  const float* kscale = p.k_scale + (size_t)bhkv * (Nkv / kKTile);
 
   // S^T = K_t . Q^T (int32) for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v).
   auto qk = [&](int t, v16i& a0, v16i& a1) {
@@ -228,7 +243,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     }
   };
   // whole tile t after every row of this wave (causal): nothing to compute
-  auto future = [&](int t) { return CAUSAL && t * kKTile > qrow0 + 31; };
+  auto future = [&](int t) { return CAUSAL && t * kKTile > qrow0 + 31 + off; };
 
   // P~ codes of the last visited tile whose P~V is still to be issued, and
   // that tile's rescale of the running state (alpha_prev, applied before
@@ -280,17 +295,17 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
 
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
-        int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+        int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
 #pragma unroll
         for (int v = 0; v < 16; v++) { sd[v] = sc0[v]; sd[16 + v] = sc1[v]; }
       }
-      const bool diag = DIAG && (kv0 + kKTile - 1 > qrow0);
+      const bool diag = DIAG && (kv0 + kKTile - 1 > qrow0 + off);
       // ---- online softmax state (the max runs over visible keys only) ----
       int smax = INT32_MIN;
       if (diag) {
 #pragma unroll
         for (int v = 0; v < 16; v++)
-          smax = max(max(smax, keyb + v > row ? INT32_MIN : sc0[v]), keyb + 16 + v > row ? INT32_MIN : sc1[v]);
+          smax = max(max(smax, keyb + v > lastk ? INT32_MIN : sc0[v]), keyb + 16 + v > lastk ? INT32_MIN : sc1[v]);
       } else {
 #pragma unroll
         for (int v = 0; v < 16; v++) smax = max(max(smax, sc0[v]), sc1[v]);   // v_max3_i32 chain
@@ -317,7 +332,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
           for (int e = 0; e < 4; e++) {
             const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
             float arg = __builtin_fmaf((float)sv, c2, -mm);
-            if (diag && keyb + 16 * h + 4 * q + e > row) arg = -__builtin_inff();
+            if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
             pv4[e] = x;
             rs += x;
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       // overlap (an empty statement that reads the packed codes and the sum)
       asm volatile("" : "+v"(pb), "+v"(rs));
       if (DUMP && dump_idx >= 0) {
-        uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * N + keyb;
+        uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
 #pragma unroll
         for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
       }
@@ -363,13 +378,13 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   qk(0, sa0, sa1);
 
   // Tiles before the causal diagonal region are fully visible to every row;
-  // their count is even (N is a multiple of 128).  The pipelined step always
+  // their count is even (Nq and Nkv are multiples of 128).  The pipelined step always
   // computes the next tile's scores there: after the last tile of a
   // non-causal pass that reads a stale (but in-bounds) K slot and is unused.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  const int nint = CAUSAL ? 2 * qt : ntiles;
+  const int nint = CAUSAL ? (q0 + off) / kKTile : ntiles;
   int t = 0;
   if (nint > 0) {
     tile_step(0, sa0, sa1, sb0, sb1, std::false_type{}, I0{}, true);
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     tile_step(t, sb0, sb1, sa0, sa1, std::false_type{}, I1{}, true);   // t = nint - 1
     t = nint;
   }
-  if (CAUSAL) {   // the two diagonal tiles 2*qt and 2*qt + 1 (scores of tile t are in sa)
+  if (CAUSAL) {   // the two diagonal tiles (q0 + off)/64 and the next (scores of tile t are in sa)
     tile_step(t, sa0, sa1, sb0, sb1, std::integral_constant<bool, CAUSAL>{}, I2{}, !future(t + 1));
     tile_step(t + 1, sb0, sb1, sa0, sa1, std::integral_constant<bool, CAUSAL>{}, I2{}, false);
     t += 2;
@@ -393,7 +408,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   // ---- epilogue: O = O_acc * v_scale / l ----
   const float lt = pair_sum_f32(lpart);
   const float inv = 1.0f / lt;
-  const float* vs = p.v_scale + (size_t)bh * D;
+  const float* vs = p.v_scale + (size_t)bhkv * D;
+  const size_t orow = p.nhd ? ((size_t)(bh / p.Hq) * Nq + row) * p.Hq + bh % p.Hq : (size_t)bh * Nq + row;
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) {
 #pragma unroll
@@ -403,7 +419,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       v4f o;
 #pragma unroll
       for (int e = 0; e < 4; e++) o[e] = oacc[ct][4 * q + e] * (sc[e] * inv);
-      store4<OUT>(p.O, ((size_t)bh * N + row) * D + c0, o);
+      store4<OUT>(p.O, orow * D + c0, o);
     }
   }
 }
@@ -424,9 +440,10 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   AttnK k;
   k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
   k.v_codes = a.v_codes; k.v_scale = a.v_scale; k.O = a.O;
-  k.N = a.N; k.nqt = a.N / kQTile; k.nbq = a.N / a.blk_q; k.blk_q = a.blk_q; k.s2 = a.s2;
+  k.Hq = a.Hq; k.g = a.Hq / a.Hkv; k.Nq = a.Nq; k.Nkv = a.Nkv; k.off = a.Nkv - a.Nq;
+  k.nqt = a.Nq / kQTile; k.nbq = a.Nq / a.blk_q; k.blk_q = a.blk_q; k.nhd = a.nhd; k.s2 = a.s2;
   k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
-  const int grid = a.BH * k.nqt;
+  const int grid = a.B * a.Hq * k.nqt;
   if (a.d == 128) {
     if (a.causal) launch2<128, true>(k, grid, a.out_dtype, dump, st);
     else launch2<128, false>(k, grid, a.out_dtype, dump, st);

@@ -6,11 +6,14 @@
 
 namespace sage {
 
+// Input tensors are [B,H,N,d] (nhd = 0) or [B,N,H,d] (nhd = 1); Q has Hq
+// heads of Nq tokens, K and V have Hkv heads of Nkv tokens.  Codes and scales
+// are always head-major.
 struct QuantQKArgs {
   const void* Q;
   const void* K;
-  int is_bf16;
-  int BH, N, d, blk_q;
+  int is_bf16, nhd;
+  int B, Hq, Hkv, Nq, Nkv, d, blk_q;
   int8_t* q_codes;
   float* q_scale;
   int8_t* k_codes;
@@ -21,8 +24,8 @@ struct QuantQKArgs {
 
 struct QuantVArgs {
   const void* V;
-  int is_bf16;
-  int BH, N, d;
+  int is_bf16, nhd;
+  int B, H, N, d;
   uint8_t* v_codes;
   float* v_scale;
   void* workspace;
@@ -36,8 +39,8 @@ struct AttnArgs {
   const uint8_t* v_codes;
   const float* v_scale;
   void* O;
-  int out_dtype;
-  int BH, N, d, blk_q, causal;
+  int out_dtype, nhd;   // O layout: [B,Hq,Nq,d] (0) or [B,Nq,Hq,d] (1)
+  int B, Hq, Hkv, Nq, Nkv, d, blk_q, causal;
   float s2;   // fp32(sm_scale * log2 e)
   // dump (test) mode
   const int32_t* sel;
@@ -49,7 +52,7 @@ struct AttnArgs {
 void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st);
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st);
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st);
-size_t quantize_qk_workspace(int BH, int N, int d);
+size_t quantize_qk_workspace(int BHkv, int Nkv, int d);
 size_t quantize_v_workspace(int BH, int N, int d);
 
 }  // namespace sage

@@ -26,6 +26,16 @@ __device__ __forceinline__ float half_of(const v4i& raw, int e, int is_bf16) {
   return load_h((uint16_t)((unsigned)raw[e >> 1] >> (16 * (e & 1))), is_bf16);
 }
 
+// Rows of d elements of an input tensor: [B,H,N,d] (head-major) or [B,N,H,d]
+// (token-major).  Row n of flat head bh starts at head(bh) + n * stride.
+struct InRows {
+  int H, N, nhd;
+  __device__ __forceinline__ size_t head(int bh, int D) const {
+    return nhd ? ((size_t)(bh / H) * N * H + (size_t)(bh % H)) * D : (size_t)bh * N * D;
+  }
+  __device__ __forceinline__ size_t stride(int D) const { return nhd ? (size_t)H * D : (size_t)D; }
+};
+
 // ---------------------------------------------------------------------------
 // Symmetric INT8 quantization of one block of BLK tokens x D channels:
 // a = max|x| (x = K - mean when SMOOTH), scale = a/127, r = 127/a,
@@ -33,22 +43,23 @@ __device__ __forceinline__ float half_of(const v4i& raw, int e, int is_bf16) {
 // 256 threads hold BLK*D/256 values each.
 // ---------------------------------------------------------------------------
 template <int D, int BLK, bool SMOOTH>
-__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int is_bf16, int N,
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int is_bf16, InRows in,
                                             const float* __restrict__ mean, int8_t* __restrict__ codes,
                                             float* __restrict__ scale, int lin, float* red4) {
   constexpr int EPT = BLK * D / 256;   // values per thread
   constexpr int LPT = EPT / 8;         // 16-byte loads per thread
+  const int N = in.N;
   const int nblk = N / BLK;
   const int blk = lin % nblk, bh = lin / nblk;
   const int t = threadIdx.x;
-  const size_t off = ((size_t)bh * N + (size_t)blk * BLK) * D;
-  const uint16_t* src = X + off;
+  const size_t off = ((size_t)bh * N + (size_t)blk * BLK) * D;   // codes: [BH, N, D]
+  const uint16_t* src = X + in.head(bh, D) + (size_t)blk * BLK * in.stride(D);
   float x[EPT];
   float a = 0.0f;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
     const int ch = l * 256 + t;   // 16-byte chunk index within the block
-    v4i raw = *(const v4i*)(src + (size_t)ch * 8);
+    v4i raw = *(const v4i*)(src + (size_t)(ch / (D / 8)) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
     const int c0 = (ch * 8) % D;
     float mu[8];
     if (SMOOTH) {
@@ -93,8 +104,10 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
 // once to int64, and the threads' int64 sums are combined through LDS.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_bf16, int N, int nchunk, int lin,
+__device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_bf16, InRows in, int nchunk, int lin,
                                          long long* __restrict__ partial, long long (*red)[D]) {
+  const int N = in.N;
+  const size_t rs = in.stride(D);
   constexpr int TPR = D / 8;        // threads per token row
   constexpr int RPP = 256 / TPR;    // token rows per pass
   const int chunk = lin % nchunk, bh = lin / nchunk;
@@ -104,7 +117,7 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
   double s[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) s[e] = 0.0;
-  const uint16_t* base = K + ((size_t)bh * N + n0) * D + cg * 8;
+  const uint16_t* base = K + in.head(bh, D) + (size_t)n0 * rs + cg * 8;
   auto add_row = [&](const v4i& raw) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -116,11 +129,11 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * D);
+    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) add_row(raw[i]);
   } else {
-    for (int r = r0; r < nrows; r += RPP) add_row(*(const v4i*)(base + (size_t)r * D));
+    for (int r = r0; r < nrows; r += RPP) add_row(*(const v4i*)(base + (size_t)r * rs));
   }
 #pragma unroll
   for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = (long long)s[e];
@@ -132,17 +145,17 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
   }
 }
 
-// Pass 1 of quantize_qk.  Grid: BH*N/BLKQ Q blocks followed by BH*nchunk K chunks.
+// Pass 1 of quantize_qk.  Grid: B*Hq*Nq/BLKQ Q blocks followed by B*Hkv*nchunk K chunks.
 template <int D, int BLKQ>
 __global__ __launch_bounds__(256) void qk_pass1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                        int is_bf16, int N, int nq, int nchunk,
+                                                        int is_bf16, InRows qin, InRows kin, int nq, int nchunk,
                                                         int8_t* __restrict__ q_codes, float* __restrict__ q_scale,
                                                         long long* __restrict__ partial) {
   __shared__ long long red[256 / (D / 8)][D];
   __shared__ float red4[4];
   const int b = blockIdx.x;
-  if (b < nq) quant_block<D, BLKQ, false>(Q, is_bf16, N, nullptr, q_codes, q_scale, b, red4);
-  else k_colsum<D>(K, is_bf16, N, nchunk, b - nq, partial, red);
+  if (b < nq) quant_block<D, BLKQ, false>(Q, is_bf16, qin, nullptr, q_codes, q_scale, b, red4);
+  else k_colsum<D>(K, is_bf16, kin, nchunk, b - nq, partial, red);
 }
 
 // mean_c = fp32(fp64(sum_chunks s_c) * 2^-24 / N).  Grid: BH * D/16; a block
@@ -164,21 +177,23 @@ __global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict
   }
 }
 
-// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: BH*N/64.
+// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: B*Hkv*Nkv/64.
 template <int D>
-__global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, int N,
+__global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, InRows kin,
                                                        const float* __restrict__ k_mean, int8_t* __restrict__ k_codes,
                                                        float* __restrict__ k_scale) {
   __shared__ float red4[4];
-  quant_block<D, 64, true>(K, is_bf16, N, k_mean, k_codes, k_scale, blockIdx.x, red4);
+  quant_block<D, 64, true>(K, is_bf16, kin, k_mean, k_codes, k_scale, blockIdx.x, red4);
 }
 
 // ---------------------------------------------------------------------------
 // Per-channel maxima of |V| over one chunk of tokens.  Grid: nchunk * BH.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ V, int is_bf16, int N, int nchunk,
-                                                        float* __restrict__ partial) {
+__global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
+                                                        int nchunk, float* __restrict__ partial) {
+  const int N = in.N;
+  const size_t rs = in.stride(D);
   constexpr int TPR = D / 8;
   constexpr int RPP = 256 / TPR;
   const int chunk = blockIdx.x % nchunk, bh = blockIdx.x / nchunk;
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
   u16x2 mx[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) mx[j] = u16x2{0, 0};
-  const uint16_t* base = V + ((size_t)bh * N + n0) * D + cg * 8;
+  const uint16_t* base = V + in.head(bh, D) + (size_t)n0 * rs + cg * 8;
   auto max_row = [&](const v4i& raw) {
 #pragma unroll
     for (int j = 0; j < 4; j++)
@@ -202,11 +217,11 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * D);
+    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) max_row(raw[i]);
   } else {
-    for (int r = r0; r < nrows; r += RPP) max_row(*(const v4i*)(base + (size_t)r * D));
+    for (int r = r0; r < nrows; r += RPP) max_row(*(const v4i*)(base + (size_t)r * rs));
   }
   float s[8];
 #pragma unroll
@@ -254,13 +269,14 @@ __global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ 
 // Grid: BH * N/64.  Block: 16 * D/8 threads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, int N,
+__global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
                                                               const float* __restrict__ v_recip,
                                                               uint8_t* __restrict__ v_codes) {
-  const int ntile = N / kKTile;
+  const int ntile = in.N / kKTile;
+  const size_t rs = in.stride(D);
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
   const int t = threadIdx.x, cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
-  const uint16_t* src = V + ((size_t)bh * N + (size_t)tile * kKTile + 4 * tg) * D + 8 * cg;
+  const uint16_t* src = V + in.head(bh, D) + ((size_t)tile * kKTile + 4 * tg) * rs + 8 * cg;
   const v4f r0 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg);
   const v4f r1 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg + 4);
   float r[8];
@@ -269,7 +285,7 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
   float y[4][8];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const v4i raw = *(const v4i*)(src + (size_t)i * D);
+    const v4i raw = *(const v4i*)(src + (size_t)i * rs);
 #pragma unroll
     for (int e = 0; e < 8; e++) y[i][e] = fminf(fmaxf(half_of(raw, e, is_bf16) * r[e], -448.0f), 448.0f);
   }
@@ -289,20 +305,22 @@ static inline int stat_chunks(int N) { return (N + kStatChunk - 1) / kStatChunk;
 
 template <int D>
 static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
-  const int nchunk = stat_chunks(a.N);
+  const int BHq = a.B * a.Hq, BHkv = a.B * a.Hkv;
+  const int nchunk = stat_chunks(a.Nkv);
   long long* partial = (long long*)a.workspace;
-  const int nq = a.BH * (a.N / a.blk_q);
-  const int grid1 = nq + a.BH * nchunk;
+  const InRows qin{a.Hq, a.Nq, a.nhd}, kin{a.Hkv, a.Nkv, a.nhd};
+  const int nq = BHq * (a.Nq / a.blk_q);
+  const int grid1 = nq + BHkv * nchunk;
   if (a.blk_q == 128)
     hipLaunchKernelGGL((qk_pass1_kernel<D, 128>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
-                       (const uint16_t*)a.K, a.is_bf16, a.N, nq, nchunk, a.q_codes, a.q_scale, partial);
+                       (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
   else
     hipLaunchKernelGGL((qk_pass1_kernel<D, 64>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
-                       (const uint16_t*)a.K, a.is_bf16, a.N, nq, nchunk, a.q_codes, a.q_scale, partial);
-  hipLaunchKernelGGL(k_mean_kernel, dim3(a.BH * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.N,
+                       (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
+  hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
                      D, a.k_mean);
-  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(a.BH * (a.N / 64)), dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16,
-                     a.N, (const float*)a.k_mean, a.k_codes, a.k_scale);
+  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(BHkv * (a.Nkv / 64)), dim3(256), 0, st, (const uint16_t*)a.K,
+                     a.is_bf16, kin, (const float*)a.k_mean, a.k_codes, a.k_scale);
 }
 
 void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {
@@ -312,15 +330,17 @@ void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {
 
 template <int D>
 static void launch_v_d(const QuantVArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
   const int nchunk = stat_chunks(a.N);
   float* partial = (float*)a.workspace;
-  float* recip = partial + (size_t)a.BH * nchunk * D;
-  hipLaunchKernelGGL(v_colmax_kernel<D>, dim3(nchunk * a.BH), dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, a.N,
+  float* recip = partial + (size_t)BH * nchunk * D;
+  const InRows in{a.H, a.N, a.nhd};
+  hipLaunchKernelGGL(v_colmax_kernel<D>, dim3(nchunk * BH), dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, in,
                      nchunk, partial);
-  hipLaunchKernelGGL(v_scale_kernel, dim3(a.BH * (D / 16)), dim3(256), 0, st, (const float*)partial, nchunk, D,
+  hipLaunchKernelGGL(v_scale_kernel, dim3(BH * (D / 16)), dim3(256), 0, st, (const float*)partial, nchunk, D,
                      a.v_scale, recip);
-  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(a.N / kKTile * a.BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
-                     a.is_bf16, a.N, (const float*)recip, a.v_codes);
+  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(a.N / kKTile * BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
+                     a.is_bf16, in, (const float*)recip, a.v_codes);
 }
 
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {
@@ -328,8 +348,8 @@ void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {
   else launch_v_d<64>(a, st);
 }
 
-size_t quantize_qk_workspace(int BH, int N, int d) {
-  return (size_t)BH * stat_chunks(N) * d * sizeof(long long);
+size_t quantize_qk_workspace(int BHkv, int Nkv, int d) {
+  return (size_t)BHkv * stat_chunks(Nkv) * d * sizeof(long long);
 }
 size_t quantize_v_workspace(int BH, int N, int d) {
   return ((size_t)BH * stat_chunks(N) * d + (size_t)BH * d) * sizeof(float);

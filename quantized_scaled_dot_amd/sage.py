@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libsage.so")
 
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_MISALIGNED, SAGE_ERR_HIP, SAGE_ERR_WORKSPACE = range(6)
 SAGE_F16, SAGE_BF16, SAGE_F32 = 0, 1, 2
+SAGE_LAYOUT_BHND, SAGE_LAYOUT_BNHD = 0, 1
 #: exported symbols, in header order
 SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_bytes", "sage_quantize_qk",
-           "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_dump")
+           "sage_quantize_qk_ex", "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_quantize_v_ex",
+           "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -39,12 +41,20 @@ _lib.sage_quantize_v_workspace_bytes.restype = _SZ
 _lib.sage_quantize_v_workspace_bytes.argtypes = [_I, _I, _I, _I]
 _lib.sage_quantize_qk.restype = _I
 _lib.sage_quantize_qk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.sage_quantize_qk_ex.restype = _I
+_lib.sage_quantize_qk_ex.argtypes = [_P, _P, _I, _I] + [_I] * 8 + [_P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.sage_quantize_v.restype = _I
 _lib.sage_quantize_v.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]
+_lib.sage_quantize_v_ex.restype = _I
+_lib.sage_quantize_v_ex.argtypes = [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]
 _lib.sage_attn_fwd.restype = _I
 _lib.sage_attn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.sage_attn_fwd_ex.restype = _I
+_lib.sage_attn_fwd_ex.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P]
 _lib.sage_attn_fwd_dump.restype = _I
 _lib.sage_attn_fwd_dump.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _P]
+_lib.sage_attn_fwd_ex_dump.restype = _I
+_lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
 
 
 class SageError(RuntimeError):
@@ -81,8 +91,19 @@ def sage_quantize_qk(Q, K, in_dtype, B, H, N, d, blk_q, blk_k, q_codes, q_scale,
                                  workspace, workspace_bytes, stream)
 
 
+def sage_quantize_qk_ex(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, q_codes, q_scale, k_codes,
+                        k_scale, k_mean, workspace, workspace_bytes, stream):
+    return _lib.sage_quantize_qk_ex(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, q_codes, q_scale,
+                                    k_codes, k_scale, k_mean, workspace, workspace_bytes, stream)
+
+
 def sage_quantize_v(V, in_dtype, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes, stream):
     return _lib.sage_quantize_v(V, in_dtype, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes, stream)
+
+
+def sage_quantize_v_ex(V, in_dtype, layout, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes, stream):
+    return _lib.sage_quantize_v_ex(V, in_dtype, layout, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes,
+                                   stream)
 
 
 def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
@@ -91,10 +112,23 @@ def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_d
                               blk_k, causal, sm_scale, stream)
 
 
+def sage_attn_fwd_ex(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, blk_q, blk_k, causal, sm_scale, stream):
+    return _lib.sage_attn_fwd_ex(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq,
+                                 Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, stream)
+
+
 def sage_attn_fwd_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d, blk_q, blk_k,
                        causal, sm_scale, sel, n_sel, s_dump, p_dump, stream):
     return _lib.sage_attn_fwd_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, B, H, N, d,
                                    blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
+
+
+def sage_attn_fwd_ex_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq,
+                          Nkv, d, blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream):
+    return _lib.sage_attn_fwd_ex_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B,
+                                      Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump,
+                                      stream)
 
 
 # ---------------------------------------------------------------- tensor helpers
@@ -110,46 +144,73 @@ def _ptr(t):
     return t.data_ptr() if t is not None else None
 
 
-def _shape4(x):
+_LAYOUTS = {"bhnd": SAGE_LAYOUT_BHND, "bnhd": SAGE_LAYOUT_BNHD}
+
+
+def _layout(layout):
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}")
+    return _LAYOUTS[layout]
+
+
+def _bhnd(x, layout):
+    """(B, H, N, d) of a contiguous CUDA tensor in ``layout``."""
     if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
-        raise ValueError("expected a contiguous CUDA tensor [B, H, N, d]")
-    return x.shape
+        raise ValueError("expected a contiguous CUDA tensor [B, H, N, d] or [B, N, H, d]")
+    B, a, b, d = x.shape
+    return (B, a, b, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, b, a, d)
 
 
-def quantize_qk(Q, K, blk_q=128, blk_k=64, workspace=None, stream=None):
-    """INT8 per-block Q and smoothed K.  Returns a dict of device tensors."""
-    B, H, N, d = _shape4(Q)
-    if K.shape != Q.shape or K.dtype != Q.dtype:
-        raise ValueError("Q and K must have the same shape and dtype")
-    _shape4(K)
+def _plain(B, Hq, Hkv, Nq, Nkv, layout):
+    return _layout(layout) == SAGE_LAYOUT_BHND and Hq == Hkv and Nq == Nkv
+
+
+def quantize_qk(Q, K, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream=None):
+    """INT8 per-block Q and smoothed K.  Q: [B,Hq,Nq,d], K: [B,Hkv,Nkv,d] (or
+    [B,N,H,d] with layout="bnhd").  Returns a dict of device tensors; the codes
+    and scales are head-major whatever the layout."""
+    B, Hq, Nq, d = _bhnd(Q, layout)
+    Bk, Hkv, Nkv, dk = _bhnd(K, layout)
+    if (Bk, dk) != (B, d) or K.dtype != Q.dtype:
+        raise ValueError("Q and K must have the same batch, head dim and dtype")
     dev = Q.device
-    out = dict(q_codes=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
-               q_scale=torch.empty((B, H, N // blk_q), dtype=torch.float32, device=dev),
-               k_codes=torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
-               k_scale=torch.empty((B, H, N // blk_k), dtype=torch.float32, device=dev),
-               k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev))
-    wsb = sage_quantize_qk_workspace_bytes(B, H, N, d)
+    out = dict(q_codes=torch.empty((B, Hq, Nq, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, Hq, Nq // blk_q), dtype=torch.float32, device=dev),
+               k_codes=torch.empty((B, Hkv, Nkv, d), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, Hkv, Nkv // blk_k), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
+    wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    _check(sage_quantize_qk(_ptr(Q), _ptr(K), _DT.get(Q.dtype, -1), B, H, N, d, blk_q, blk_k, _ptr(out["q_codes"]),
-                            _ptr(out["q_scale"]), _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]),
-                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    ptrs = (_ptr(out["q_codes"]), _ptr(out["q_scale"]), _ptr(out["k_codes"]), _ptr(out["k_scale"]),
+            _ptr(out["k_mean"]), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    dt = _DT.get(Q.dtype, -1)
+    if _plain(B, Hq, Hkv, Nq, Nkv, layout):
+        _check(sage_quantize_qk(_ptr(Q), _ptr(K), dt, B, Hq, Nq, d, blk_q, blk_k, *ptrs))
+    else:
+        _check(sage_quantize_qk_ex(_ptr(Q), _ptr(K), dt, _layout(layout), B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k,
+                                   *ptrs))
     out.update(blk_q=blk_q, blk_k=blk_k)
     return out
 
 
-def quantize_v(V, workspace=None, stream=None):
+def quantize_v(V, layout="bhnd", workspace=None, stream=None):
     """FP8 e4m3 V with per-channel scales.  Returns (v_codes, v_scale); v_codes
     is in KV-tile channel-major order (see ``v_codes_to_natural``)."""
-    B, H, N, d = _shape4(V)
+    B, H, N, d = _bhnd(V, layout)
     dev = V.device
     v_codes = torch.empty((B, H, N // sage_kv_tile(), d, sage_kv_tile()), dtype=torch.uint8, device=dev)
     v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     wsb = sage_quantize_v_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    _check(sage_quantize_v(_ptr(V), _DT.get(V.dtype, -1), B, H, N, d, _ptr(v_codes), _ptr(v_scale), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    rest = (_ptr(v_codes), _ptr(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    dt = _DT.get(V.dtype, -1)
+    if _layout(layout) == SAGE_LAYOUT_BHND:
+        _check(sage_quantize_v(_ptr(V), dt, B, H, N, d, *rest))
+    else:
+        _check(sage_quantize_v_ex(_ptr(V), dt, _layout(layout), B, H, N, d, *rest))
     return v_codes, v_scale
 
 
@@ -163,31 +224,44 @@ def default_sm_scale(d):
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
 
 
-def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=None, stream=None, dump=None):
+def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=None, layout="bhnd", stream=None,
+             dump=None):
     """Attention on quantized operands.  ``qk`` from quantize_qk, ``v`` = (v_codes, v_scale).
-    ``dump`` = (sel int32 tensor, s_dump, p_dump) routes through sage_attn_fwd_dump."""
-    B, H, N, d = qk["q_codes"].shape
+    O is [B,Hq,Nq,d] (or [B,Nq,Hq,d] with layout="bnhd").  ``dump`` = (sel int32
+    tensor, s_dump, p_dump) routes through the dump entry points."""
+    B, Hq, Nq, d = qk["q_codes"].shape
+    Hkv, Nkv = qk["k_codes"].shape[1:3]
     v_codes, v_scale = v
     if sm_scale is None:
         sm_scale = default_sm_scale(d)
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=out_dtype, device=qk["q_codes"].device)
-    args = (_ptr(qk["q_codes"]), _ptr(qk["q_scale"]), _ptr(qk["k_codes"]), _ptr(qk["k_scale"]), _ptr(v_codes),
-            _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), B, H, N, d, qk["blk_q"], qk["blk_k"], int(bool(causal)),
-            float(sm_scale))
+        shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
+        out = torch.empty(shape, dtype=out_dtype, device=qk["q_codes"].device)
+    ops = (_ptr(qk["q_codes"]), _ptr(qk["q_scale"]), _ptr(qk["k_codes"]), _ptr(qk["k_scale"]), _ptr(v_codes),
+           _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1))
+    tail = (d, qk["blk_q"], qk["blk_k"], int(bool(causal)), float(sm_scale))
+    plain = _plain(B, Hq, Hkv, Nq, Nkv, layout)
+    shape = (B, Hq, Nq) if plain else (_layout(layout), B, Hq, Hkv, Nq, Nkv)
     if dump is None:
-        _check(sage_attn_fwd(*args, _stream(stream)))
+        fn = sage_attn_fwd if plain else sage_attn_fwd_ex
+        _check(fn(*ops, *shape, *tail, _stream(stream)))
     else:
         sel, s_dump, p_dump = dump
-        _check(sage_attn_fwd_dump(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
+        fn = sage_attn_fwd_dump if plain else sage_attn_fwd_ex_dump
+        _check(fn(*ops, *shape, *tail, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
     return out
 
 
-def attention(q, k, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, out_dtype=None, stream=None):
-    """Drop-in quantized attention forward for [B, H, N, d] float16/bfloat16 inputs."""
-    qk = quantize_qk(q, k, blk_q, blk_k, stream=stream)
-    vq = quantize_v(v, stream=stream)
-    return attn_fwd(qk, vq, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or q.dtype, stream=stream)
+def attention(q, k, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, out_dtype=None, layout="bhnd",
+              stream=None):
+    """Drop-in quantized attention forward for float16/bfloat16 inputs: q
+    [B,Hq,Nq,d], k and v [B,Hkv,Nkv,d] (layout="bhnd", the layout of PyTorch's
+    scaled_dot_product_attention) or [B,N,H,d] (layout="bnhd").  Hq must be a
+    multiple of Hkv; causal needs Nkv >= Nq (queries are the last Nq positions)."""
+    qk = quantize_qk(q, k, blk_q, blk_k, layout=layout, stream=stream)
+    vq = quantize_v(v, layout=layout, stream=stream)
+    return attn_fwd(qk, vq, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or q.dtype, layout=layout,
+                    stream=stream)
 
 
 def loaded_hip_runtimes():

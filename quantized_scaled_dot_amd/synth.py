@@ -9,8 +9,12 @@ then the V outlier channels; K gets a bias drawn per (b, h, channel) with the
 stated variance and added to every token (channel outliers that smoothing
 removes); optionally a fixed number of V channels per (b, h), chosen without
 replacement, are multiplied by a factor; finally the tensors are rounded to
-float16 / bfloat16 with round-to-nearest-even.  Shapes follow the workloads
-the method is aimed at: LLM prefill, ViT, video DiT and long-context prefill.
+float16 / bfloat16 with round-to-nearest-even.  Q is [B, H, N, d]; K and V
+are [B, Hkv, Nkv, d], which is Q's shape unless the workload sets grouped K/V
+heads (Hkv < H) or a different key count (then the queries are the last N
+positions of the Nkv-long sequence).  Shapes follow the workloads the method
+is aimed at: LLM prefill (also with grouped K/V heads and with a query chunk
+against a longer prefix), ViT, video DiT and long-context prefill.
 """
 from dataclasses import dataclass, field
 import math
@@ -35,6 +39,16 @@ class Workload:
     v_outlier_channels: int = 0
     v_outlier_scale: float = 1.0
     seed: int = 0
+    Hkv_: int = 0         # K/V heads (0: H)
+    Nkv_: int = 0         # keys (0: N)
+
+    @property
+    def Hkv(self):
+        return self.Hkv_ or self.H
+
+    @property
+    def Nkv(self):
+        return self.Nkv_ or self.N
 
     @property
     def torch_dtype(self):
@@ -46,9 +60,10 @@ class Workload:
 
     @property
     def ops(self):
-        """Attention operation count 4*B*H*N^2*d, halved for causal masking."""
-        o = 4.0 * self.B * self.H * self.N * self.N * self.d
-        return o / 2 if self.causal else o
+        """Attention operation count 4*B*H*N*Nkv*d; causal: 4*B*H*d*(N*Nkv - N^2/2)
+        (half of it when N = Nkv)."""
+        pairs = self.N * self.Nkv - (self.N * self.N / 2 if self.causal else 0)
+        return 4.0 * self.B * self.H * pairs * self.d
 
     def with_(self, **kw):
         d = dict(self.__dict__)
@@ -68,21 +83,29 @@ WORKLOADS = {
     "video-dit-32k": Workload("video-dit-32k", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0, _rsqrt32(128)),
     "long-prefill-128k-causal": Workload("long-prefill-128k-causal", 1, 8, 131072, 128, "bfloat16", True, 128, 64,
                                          4.0, _rsqrt32(128), v_outlier_channels=13, v_outlier_scale=8.0),
+    # grouped K/V heads: 32 query heads on 8 K/V heads (4 queries per K/V head)
+    "llm-prefill-8k-gqa-causal": Workload("llm-prefill-8k-gqa-causal", 1, 32, 8192, 128, "bfloat16", True, 128, 64,
+                                          4.0, _rsqrt32(128), Hkv_=8),
+    # a 4096-token query chunk at the end of a 32768-token prefix, grouped heads
+    "chunked-prefill-4k-of-32k-gqa-causal": Workload("chunked-prefill-4k-of-32k-gqa-causal", 1, 32, 4096, 128,
+                                                     "bfloat16", True, 128, 64, 4.0, _rsqrt32(128), Hkv_=8,
+                                                     Nkv_=32768),
 }
 
 
 def make_inputs(w: Workload, seed=None, device="cpu"):
-    """Return Q, K, V as torch tensors [B, H, N, d] of ``w.dtype`` on ``device``."""
+    """Return Q [B, H, N, d] and K, V [B, Hkv, Nkv, d] as torch tensors of
+    ``w.dtype`` on ``device``."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
-    shape = (w.B, w.H, w.N, w.d)
-    q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    bias = rng.standard_normal((w.B, w.H, 1, w.d), dtype=np.float32) * np.float32(math.sqrt(w.bias_var))
+    kv_shape = (w.B, w.Hkv, w.Nkv, w.d)
+    q = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
+    bias = rng.standard_normal((w.B, w.Hkv, 1, w.d), dtype=np.float32) * np.float32(math.sqrt(w.bias_var))
     k += bias
-    v = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(kv_shape, dtype=np.float32)
     if w.v_outlier_channels:
         for b in range(w.B):
-            for h in range(w.H):
+            for h in range(w.Hkv):
                 ch = rng.choice(w.d, size=w.v_outlier_channels, replace=False)
                 v[b, h][:, ch] *= np.float32(w.v_outlier_scale)
     out = []

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 8 and set(names) == set(sage.SYMBOLS)
+    assert len(names) == 12 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -104,7 +104,76 @@ def test_attn_fwd_dump_rejects_bad_selection():
     assert r == sage.SAGE_ERR_INVALID_ARG
 
 
+def _qk_ex(**kw):
+    args = dict(Q=A, K=A, in_dtype=1, layout=1, B=1, Hq=4, Hkv=2, Nq=128, Nkv=384, d=128, blk_q=128, blk_k=64,
+                q_codes=A, q_scale=A, k_codes=A, k_scale=A, k_mean=A, workspace=A, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return sage.sage_quantize_qk_ex(**args)
+
+
+def _v_ex(**kw):
+    args = dict(V=A, in_dtype=0, layout=1, B=1, H=2, N=384, d=64, v_codes=A, v_scale=A, workspace=A,
+                workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return sage.sage_quantize_v_ex(**args)
+
+
+def _attn_ex(**kw):
+    args = dict(q_codes=A, q_scale=A, k_codes=A, k_scale=A, v_codes=A, v_scale=A, O=A, out_dtype=2, layout=0, B=1,
+                Hq=4, Hkv=2, Nq=128, Nkv=384, d=128, blk_q=128, blk_k=64, causal=1, sm_scale=0.125, stream=None)
+    args.update(kw)
+    return sage.sage_attn_fwd_ex(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), sage.SAGE_ERR_INVALID_ARG), (dict(layout=-1), sage.SAGE_ERR_INVALID_ARG),
+    (dict(Hq=3), sage.SAGE_ERR_INVALID_ARG), (dict(Hkv=0), sage.SAGE_ERR_INVALID_ARG),
+    (dict(Hkv=8), sage.SAGE_ERR_INVALID_ARG), (dict(Nq=192), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(Nkv=100), sage.SAGE_ERR_UNSUPPORTED), (dict(Nkv=1 << 20), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(Nq=0), sage.SAGE_ERR_INVALID_ARG), (dict(d=32), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG), (dict(K=None), sage.SAGE_ERR_INVALID_ARG),
+    (dict(workspace_bytes=16), sage.SAGE_ERR_WORKSPACE),
+])
+def test_quantize_qk_ex_rejects(kw, status):
+    assert _qk_ex(**kw) == status
+
+
+def test_quantize_qk_ex_workspace_follows_k():
+    need = sage.sage_quantize_qk_workspace_bytes(1, 2, 384, 128)
+    assert need == 2 * 2 * 128 * 8
+    # the workspace covers K only (B*Hkv heads of Nkv tokens), however long Q is
+    assert _qk_ex(workspace_bytes=need - 1, Q=None) == sage.SAGE_ERR_INVALID_ARG
+    assert _qk_ex(workspace_bytes=need - 1, Nq=4096) == sage.SAGE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=5), sage.SAGE_ERR_INVALID_ARG), (dict(N=200), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(V=A + 8), sage.SAGE_ERR_MISALIGNED), (dict(workspace_bytes=0), sage.SAGE_ERR_WORKSPACE),
+])
+def test_quantize_v_ex_rejects(kw, status):
+    assert _v_ex(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=3), sage.SAGE_ERR_INVALID_ARG), (dict(Hq=6, Hkv=4), sage.SAGE_ERR_INVALID_ARG),
+    (dict(Nq=512), sage.SAGE_ERR_INVALID_ARG),              # causal with Nq > Nkv: first rows see no key
+    (dict(Nq=128, Nkv=320), sage.SAGE_ERR_UNSUPPORTED), (dict(Hkv=-2), sage.SAGE_ERR_INVALID_ARG),
+    (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
+    (dict(O=A + 4), sage.SAGE_ERR_MISALIGNED), (dict(k_scale=None), sage.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_ex_rejects(kw, status):
+    assert _attn_ex(**kw) == status
+
+
+def test_attn_fwd_ex_dump_rejects_bad_selection():
+    shape = (0, 1, 4, 2, 128, 384, 128, 128, 64, 0, 0.125)
+    assert sage.sage_attn_fwd_ex_dump(A, A, A, A, A, A, A, 2, *shape, None, 1, A, A, None) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_attn_fwd_ex_dump(A, A, A, A, A, A, A, 2, *shape, A, -1, A, A, None) == sage.SAGE_ERR_INVALID_ARG
+
+
 def test_python_helpers_validate_shapes():
     import torch
     with pytest.raises(ValueError):
         sage.quantize_qk(torch.zeros(2, 2), torch.zeros(2, 2))
+    with pytest.raises(ValueError):
+        sage.quantize_v(torch.zeros(1, 2, 128, 64), layout="nhd")

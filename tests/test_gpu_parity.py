@@ -28,27 +28,32 @@ def _sage():
     return sage
 
 
-def run_gpu(w, Q, K, V, out_dtype=torch.float32, dump_tiles=(), check_runtime=True):
+def run_gpu(w, Q, K, V, out_dtype=torch.float32, dump_tiles=(), check_runtime=True, layout="bhnd"):
+    """Q [B,H,N,d], K/V [B,Hkv,Nkv,d] through the C ABI; with layout="bnhd" the
+    device inputs are [B,N,H,d] copies and O comes back [B,N,H,d].  res["O"]
+    is always [B,H,N,d]."""
     sage = _sage()
     if check_runtime:
         assert len(sage.loaded_hip_runtimes()) == 1, sage.loaded_hip_runtimes()
     dev = torch.device("cuda:0")
-    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
-    qk = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k)
-    vq = sage.quantize_v(Vd)
+    tok = layout == "bnhd"
+    Qd, Kd, Vd = ((t.transpose(1, 2) if tok else t).contiguous().to(dev) for t in (Q, K, V))
+    qk = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, layout=layout)
+    vq = sage.quantize_v(Vd, layout=layout)
     dump = None
     if dump_tiles:
         sel = torch.tensor(list(dump_tiles), dtype=torch.int32, device=dev)
-        s_d = torch.full((len(dump_tiles), 128, w.N), S_SENTINEL, dtype=torch.int32, device=dev)
-        p_d = torch.full((len(dump_tiles), 128, w.N), P_SENTINEL, dtype=torch.uint8, device=dev)
+        s_d = torch.full((len(dump_tiles), 128, w.Nkv), S_SENTINEL, dtype=torch.int32, device=dev)
+        p_d = torch.full((len(dump_tiles), 128, w.Nkv), P_SENTINEL, dtype=torch.uint8, device=dev)
         dump = (sel, s_d, p_d)
-    O = sage.attn_fwd(qk, vq, causal=w.causal, sm_scale=w.sm_scale, out_dtype=out_dtype, dump=dump)
+    O = sage.attn_fwd(qk, vq, causal=w.causal, sm_scale=w.sm_scale, out_dtype=out_dtype, layout=layout, dump=dump)
     torch.cuda.synchronize()
+    assert O.shape == ((w.B, w.N, w.H, w.d) if tok else (w.B, w.H, w.N, w.d))
     res = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in qk.items()}
     res["v_codes"] = sage.v_codes_to_natural(vq[0]).cpu().numpy()
     res["v_codes_tiled"] = vq[0]
     res["v_scale"] = vq[1].cpu().numpy()
-    res["O"] = O.float().cpu().numpy()
+    res["O"] = (O.transpose(1, 2) if tok else O).float().cpu().numpy()
     res["O_dev"] = O
     res["qk_dev"], res["vq_dev"] = qk, vq
     if dump:
@@ -84,8 +89,8 @@ def check_dump(w, g, qk, tiles):
         s_got = g["s_dump"][k]
         written = s_got != S_SENTINEL
         i = qt * 128 + np.arange(128)[:, None]
-        j = np.arange(w.N)[None, :]
-        visible = (j <= i) if w.causal else np.ones_like(written)
+        j = np.arange(w.Nkv)[None, :]
+        visible = (j <= i + (w.Nkv - w.N)) if w.causal else np.ones_like(written)
         assert written[visible].all(), "a visible score was not computed"
         assert np.array_equal(s_got[written], s_ref[written]), "int32 QK^T mismatch"
         yield rows, g["p_dump"][k], visible
@@ -144,6 +149,94 @@ def test_small_full_parity(name):
     assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {np.unravel_index(err.argmax(), err.shape)}"
     ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
     assert cosine(O, ex) >= 0.995
+
+
+# grouped K/V heads (Hkv < H), fewer queries than keys (the queries are the
+# last N of Nkv positions; causal visibility j <= i + Nkv - N), and the
+# token-major [B, N, H, d] layout.  B*Hkv = 8 and 16 take the kernel's
+# per-XCD K/V-head order, the others the plain order.
+SMALL_EX = {
+    "gqa4-causal-bf16-d128": dict(base="llm-prefill-4k-causal", B=2, H=8, Hkv_=2, N=512),
+    "gqa2-xcd-f16-d64": dict(base="vit-2k-f16", B=1, H=16, Hkv_=8, N=256),
+    "gqa4-xcd-causal-d128": dict(base="llm-prefill-4k-causal", B=2, H=16, Hkv_=4, N=384),
+    "chunk256-of-1024-causal-blkq64": dict(base="llm-prefill-4k-causal", B=1, H=2, N=256, Nkv_=1024, blk_q=64),
+    "q384-of-k128-noncausal-f16": dict(base="tiny-f16-256", B=1, H=2, N=384, Nkv_=128),
+    "mqa-chunk128-of-640-causal-d64": dict(base="vit-2k-f16", B=2, H=4, Hkv_=1, N=128, Nkv_=640, causal=True),
+    "gqa8-xcd-chunk-noncausal-d128": dict(base="video-dit-32k", B=2, H=64, Hkv_=8, N=128, Nkv_=512),
+}
+
+
+def small_ex_workload(name):
+    kw = dict(SMALL_EX[name])
+    base = kw.pop("base")
+    return synth.WORKLOADS[base].with_(name=name, **kw)
+
+
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+@pytest.mark.parametrize("name", list(SMALL_EX))
+def test_small_grouped_and_unequal_parity(name, layout):
+    w = small_ex_workload(name)
+    Q, K, V = synth.make_inputs(w)
+    assert Q.shape == (w.B, w.H, w.N, w.d) and K.shape == (w.B, w.Hkv, w.Nkv, w.d)
+    nqt = w.N // 128
+    tiles = sorted({0, nqt - 1, (w.B * w.H - 1) * nqt + nqt // 2, (w.B * w.H // 2) * nqt})
+    g = run_gpu(w, Q, K, V, dump_tiles=tiles, layout=layout)
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, want_p=True)
+    for rows, p_got, visible in check_dump(w, g, qk, tiles):
+        check_p_codes(p_got, P_ref[rows], visible)
+    O = g["O"].reshape(-1, w.d)
+    err = np.abs(O - O_ref)
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {np.unravel_index(err.argmax(), err.shape)}"
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
+    assert cosine(O, ex) >= 0.995
+
+
+@pytest.mark.parametrize("name", ["gqa4-xcd-causal-d128", "chunk256-of-1024-causal-blkq64"])
+def test_token_major_layout_is_bit_identical(name):
+    """The layout only changes addressing: codes, scales and O bits agree."""
+    w = small_ex_workload(name)
+    Q, K, V = synth.make_inputs(w)
+    a = run_gpu(w, Q, K, V, out_dtype=torch.bfloat16)
+    b = run_gpu(w, Q, K, V, out_dtype=torch.bfloat16, layout="bnhd")
+    for key in ("q_codes", "k_codes", "v_codes", "k_mean", "q_scale", "k_scale", "v_scale", "O"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_square_problem_through_the_extended_entry_points():
+    """H = Hkv, N = Nkv, [B,H,N,d]: the _ex entry points give the plain ones' bits."""
+    sage = _sage()
+    w = small_workload("causal-bf16-d128-N1024")
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu(w, Q, K, V)
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    B, H, N, d = Q.shape
+    st = torch.cuda.current_stream().cuda_stream
+    codes = dict(q=torch.empty_like(Qd, dtype=torch.int8), k=torch.empty_like(Kd, dtype=torch.int8),
+                 qs=torch.empty((B, H, N // w.blk_q), dtype=torch.float32, device=dev),
+                 ks=torch.empty((B, H, N // 64), dtype=torch.float32, device=dev),
+                 km=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+                 v=torch.empty((B, H, N // 64, d, 64), dtype=torch.uint8, device=dev),
+                 vs=torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=dev)
+    p = {k: t.data_ptr() for k, t in codes.items()}
+    assert sage.sage_quantize_qk_ex(Qd.data_ptr(), Kd.data_ptr(), w.dtype_code, sage.SAGE_LAYOUT_BHND, B, H, H, N, N,
+                                    d, w.blk_q, 64, p["q"], p["qs"], p["k"], p["ks"], p["km"], ws.data_ptr(),
+                                    ws.numel(), st) == 0
+    assert sage.sage_quantize_v_ex(Vd.data_ptr(), w.dtype_code, sage.SAGE_LAYOUT_BHND, B, H, N, d, p["v"], p["vs"],
+                                   ws.data_ptr(), ws.numel(), st) == 0
+    O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    assert sage.sage_attn_fwd_ex(p["q"], p["qs"], p["k"], p["ks"], p["v"], p["vs"], O.data_ptr(), sage.SAGE_F32,
+                                 sage.SAGE_LAYOUT_BHND, B, H, H, N, N, d, w.blk_q, 64, int(w.causal), w.sm_scale,
+                                 st) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(codes["q"].cpu().numpy(), g["q_codes"])
+    assert np.array_equal(codes["k"].cpu().numpy(), g["k_codes"])
+    assert np.array_equal(codes["km"].cpu().numpy(), g["k_mean"])
+    assert torch.equal(codes["v"].cpu(), g["v_codes_tiled"].cpu())
+    assert np.array_equal(O.cpu().numpy(), g["O"])
 
 
 def test_output_dtypes_round_the_fp32_result():
