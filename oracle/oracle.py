@@ -112,7 +112,8 @@ def kmean(K_bits, dtype):
 
 
 def quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k):
-    """INT8 blocks of Q [B,Hq,Nq,d]; K mean and INT8 blocks of the smoothed K [B,Hkv,Nkv,d]."""
+    """INT8 blocks of Q [B,Hq,Nq,d]; K mean and INT8 blocks of the smoothed K [B,Hkv,Nkv,d].
+    Scales: [B,Hq,ceil(Nq/blk_q)] and [B,Hkv,ceil(Nkv/blk_k)] (a shorter last block)."""
     Q_bits = _c(Q_bits, np.uint16)
     K_bits = _c(K_bits, np.uint16)
     B, Hq, Nq, d = Q_bits.shape
@@ -121,8 +122,8 @@ def quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k):
         raise ValueError("Q and K must share B and d")
     qc = np.empty((B, Hq, Nq, d), np.int8)
     kc = np.empty((B, Hkv, Nkv, d), np.int8)
-    qs = np.empty((B, Hq, Nq // blk_q), np.float32)
-    ks = np.empty((B, Hkv, Nkv // blk_k), np.float32)
+    qs = np.empty((B, Hq, -(-Nq // blk_q)), np.float32)
+    ks = np.empty((B, Hkv, -(-Nkv // blk_k)), np.float32)
     mu = np.empty((B, Hkv, d), np.float32)
     rc = lib().oracle_quantize_q(_p(Q_bits), dtype, B * Hq, Nq, d, blk_q, _p(qc), _p(qs))
     rc |= lib().oracle_quantize_k(_p(K_bits), dtype, B * Hkv, Nkv, d, blk_k, _p(kc), _p(ks), _p(mu))

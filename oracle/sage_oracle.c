@@ -164,21 +164,26 @@ static void quant_block_i8(const float* x, size_t n, int8_t* codes, float* delta
 }
 
 /* Q, K: [BH, N, d] (float16/bfloat16 raw bits).  Outputs: q_codes, k_codes
- * [BH, N, d] int8; q_scale [BH, N/blk_q]; k_scale [BH, N/blk_k]; k_mean [BH, d].
- * Returns 0, or -1 for a shape the method does not define. */
+ * [BH, N, d] int8; q_scale [BH, ceil(N/blk_q)]; k_scale [BH, ceil(N/blk_k)];
+ * k_mean [BH, d].  Blocks are consecutive runs of blk tokens from token 0;
+ * when blk does not divide N the last block holds the N mod blk remaining
+ * tokens.  Returns 0, or -1 for a shape the method does not define. */
+static int nblocks(int N, int blk) { return (N + blk - 1) / blk; }
+static int block_len(int N, int blk, int b) { return (b + 1) * blk <= N ? blk : N - b * blk; }
+
 /* Q: blocks of blk_q tokens of one head, all d channels.  Q tensor [BH, N, d]. */
 int oracle_quantize_q(const uint16_t* Q, int dtype, int BH, int N, int d, int blk_q, int8_t* q_codes,
                       float* q_scale) {
-  if (BH < 1 || N < 1 || d < 1 || blk_q < 1 || N % blk_q) return -1;
-  int nbq = N / blk_q;
+  if (BH < 1 || N < 1 || d < 1 || blk_q < 1) return -1;
+  int nbq = nblocks(N, blk_q);
 #pragma omp parallel for schedule(dynamic)
   for (int bh = 0; bh < BH; bh++) {
     const uint16_t* Qh = Q + (size_t)bh * N * d;
     float* buf = (float*)malloc(sizeof(float) * (size_t)blk_q * d);
     for (int b = 0; b < nbq; b++) {
-      for (size_t k = 0; k < (size_t)blk_q * d; k++) buf[k] = load_in(Qh, (size_t)b * blk_q * d + k, dtype);
-      quant_block_i8(buf, (size_t)blk_q * d, q_codes + (size_t)bh * N * d + (size_t)b * blk_q * d,
-                     q_scale + (size_t)bh * nbq + b);
+      const size_t n = (size_t)block_len(N, blk_q, b) * d;
+      for (size_t k = 0; k < n; k++) buf[k] = load_in(Qh, (size_t)b * blk_q * d + k, dtype);
+      quant_block_i8(buf, n, q_codes + (size_t)bh * N * d + (size_t)b * blk_q * d, q_scale + (size_t)bh * nbq + b);
     }
     free(buf);
   }
@@ -189,8 +194,8 @@ int oracle_quantize_q(const uint16_t* Q, int dtype, int BH, int N, int d, int bl
  * tokens of the smoothed K.  K tensor [BH, N, d]. */
 int oracle_quantize_k(const uint16_t* K, int dtype, int BH, int N, int d, int blk_k, int8_t* k_codes,
                       float* k_scale, float* k_mean) {
-  if (BH < 1 || N < 1 || d < 1 || blk_k < 1 || N % blk_k) return -1;
-  int nbk = N / blk_k;
+  if (BH < 1 || N < 1 || d < 1 || blk_k < 1) return -1;
+  int nbk = nblocks(N, blk_k);
 #pragma omp parallel for schedule(dynamic)
   for (int bh = 0; bh < BH; bh++) {
     const uint16_t* Kh = K + (size_t)bh * N * d;
@@ -198,12 +203,13 @@ int oracle_quantize_k(const uint16_t* K, int dtype, int BH, int N, int d, int bl
     kmean_head(Kh, dtype, N, d, mu, NULL);
     float* buf = (float*)malloc(sizeof(float) * (size_t)blk_k * d);
     for (int b = 0; b < nbk; b++) {
-      for (int t = 0; t < blk_k; t++)
+      const int len = block_len(N, blk_k, b);
+      for (int t = 0; t < len; t++)
         for (int c = 0; c < d; c++) {
           size_t idx = (size_t)(b * blk_k + t) * d + c;
           buf[(size_t)t * d + c] = load_in(Kh, idx, dtype) - mu[c];   /* smoothed K, fp32 */
         }
-      quant_block_i8(buf, (size_t)blk_k * d, k_codes + (size_t)bh * N * d + (size_t)b * blk_k * d,
+      quant_block_i8(buf, (size_t)len * d, k_codes + (size_t)bh * N * d + (size_t)b * blk_k * d,
                      k_scale + (size_t)bh * nbk + b);
     }
     free(buf);
@@ -287,7 +293,8 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int B, int Hq
 
 /* ------------------------------------------------------------------------ */
 /* Steps 4-8: attention for chosen query rows.  For row i of head bh, KV      */
-/* tiles of kv_tile keys are visited in ascending order, one pass, as in the */
+/* tiles of kv_tile keys (the last one shorter when kv_tile does not divide */
+/* Nkv) are visited in ascending order, one pass, as in the                  */
 /* tiled online softmax ([BLOG] "How FlashAttention reduces memory            */
 /* traffic"); tiles with no visible key (causal) are skipped ([BLOG] causal   */
 /* masking changes which blocks are skipped).  Causal visibility is aligned */
@@ -319,11 +326,10 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
                      float sm_scale, const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nkv < 1 || d < 1) return -1;
   if (blk_q < 1 || blk_k < 1 || kv_tile < 1) return -1;
-  if (Nq % blk_q || Nkv % blk_k || Nkv % kv_tile) return -1;
   if (causal && Nkv < Nq) return -1;   /* the first queries would see no key */
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return -1;
   const float s2 = sm_scale * LOG2E_F;
-  const int nbq = Nq / blk_q, nbk = Nkv / blk_k;
+  const int nbq = nblocks(Nq, blk_q), nbk = nblocks(Nkv, blk_k);
   const int64_t off = (int64_t)Nkv - Nq;
   double vdec[256];
   for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
@@ -344,7 +350,7 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
     int first = 1;
     if (p_codes) memset(p_codes + (size_t)r * Nkv, 0, Nkv);
     for (int j0 = 0; j0 < Nkv; j0 += kv_tile) {
-      int nvis = kv_tile;
+      int nvis = j0 + kv_tile <= Nkv ? kv_tile : Nkv - j0;
       if (causal) {
         const int64_t last = i + off;   /* last visible key */
         if (j0 > last) break;

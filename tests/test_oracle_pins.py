@@ -449,3 +449,92 @@ def test_unequal_shapes_rejected():
     with pytest.raises(ValueError):   # causal with more queries than keys: the first queries see nothing
         orc.attn_rows(qk, vc, vs, 64, 64, True, 0.125)
     orc.attn_rows(qk, vc, vs, 64, 64, False, 0.125, rows=np.array([0, 255]))   # non-causal is fine
+
+
+# ------------------------------------------------------------------ lengths that are not block multiples
+def test_ragged_q_blocks_equal_the_zero_padded_tensor():
+    """A last Q block of N mod blk tokens: appending zero tokens up to a block
+    multiple changes no code of the real tokens and no scale (|0| never raises
+    a block's max), and the block count is ceil(N / blk)."""
+    rng = np.random.default_rng(21)
+    for N, blk in ((200, 64), (130, 128), (1, 64), (127, 128)):
+        Q = rng.standard_normal((1, 2, N, 64)).astype(np.float32) * 3
+        Np = -(-N // blk) * blk
+        Qp = np.zeros((1, 2, Np, 64), np.float32)
+        Qp[:, :, :N] = Q
+        K = rng.standard_normal((1, 2, 64, 64)).astype(np.float32)
+        a = orc.quantize_qk(_f16_bits(Q), _f16_bits(K), 0, blk, 64)
+        b = orc.quantize_qk(_f16_bits(Qp), _f16_bits(K), 0, blk, 64)
+        assert a["q_scale"].shape == (1, 2, Np // blk)
+        assert np.array_equal(a["q_scale"], b["q_scale"])
+        assert np.array_equal(a["q_codes"], b["q_codes"][:, :, :N])
+        assert not b["q_codes"][:, :, N:].any()
+
+
+def test_ragged_k_last_block_holds_exactly_the_tail_tokens():
+    """K of N = 64 m + r tokens: the last scale times 127 is the largest
+    |k - mean| over the r tail tokens alone (not over 64 tokens), and that
+    element's code is +-127; the mean runs over all N tokens."""
+    rng = np.random.default_rng(22)
+    N, r = 64 * 3 + 5, 5
+    K = rng.standard_normal((1, 1, N, 64)).astype(np.float32)
+    K[0, 0, N - r:] *= 0.25        # a quiet tail: any token of the previous block would raise its max
+    Kv = _f16_vals(K)
+    qk = orc.quantize_qk(_f16_bits(K[:, :, :64]), _f16_bits(K), 0, 64, 64)
+    mu = qk["k_mean"][0, 0]
+    assert np.abs(mu.astype(np.float64) - Kv[0, 0].astype(np.float64).mean(0)).max() < 1e-6
+    assert qk["k_scale"].shape == (1, 1, 4)
+    tail = Kv[0, 0, N - r:] - mu                       # fp32, as the method smooths
+    a = np.abs(tail).max()
+    assert qk["k_scale"][0, 0, 3] == np.float32(a / np.float32(127))
+    i = np.unravel_index(np.abs(tail).argmax(), tail.shape)
+    assert abs(int(qk["k_codes"][0, 0, N - r + i[0], i[1]])) == 127
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_fewer_queries_equal_the_last_rows(causal):
+    """Ragged Nq and Nkv: dropping the first 64 queries (one Q block) leaves the
+    remaining rows bit-identical, the causal offset Nkv - Nq growing by 64."""
+    Q, K, V = _gqa_inputs(Hq=2, Hkv=1, Nq=200, Nkv=261, seed=23)
+    qb, qsb, kb, vb = (_f16_bits(a) for a in (Q, Q[:, :, 64:], K, V))
+    _, _, (O, P) = orc.run(qb, kb, vb, 0, 64, 64, causal, 0.125, want_p=True)
+    _, _, (Os, Ps) = orc.run(qsb, kb, vb, 0, 64, 64, causal, 0.125, want_p=True)
+    rows = (np.arange(2)[:, None] * 200 + 64 + np.arange(136)[None, :]).ravel()
+    assert np.array_equal(Os, O[rows]) and np.array_equal(Ps, P[rows])
+
+
+def test_ragged_tail_key_is_attended():
+    """Nkv = 65: the one key of the short last tile dominates every score it
+    enters (weight above 0.999), so O is its V row; a dropped or misplaced tail
+    tile would give O near the mean of the other V rows (about 0) instead.
+    Causal, Nq = Nkv = 65: only query 64 sees that key.  Against fp64 exact
+    attention."""
+    rng = np.random.default_rng(24)
+    d = 64
+    K = rng.standard_normal((1, 1, 65, d)).astype(np.float32) * 0.5
+    K[0, 0, 64] = 0.0
+    K[0, 0, 64, 0] = 12.0            # score 8 * 12 * 0.125 = 12 above the others' ~0
+    V = rng.standard_normal((1, 1, 65, d)).astype(np.float32)
+    V[0, 0, 64] = 5.0
+    kb, vb = _f16_bits(K), _f16_bits(V)
+    for causal, nq in ((False, 128), (True, 65)):
+        Q = rng.standard_normal((1, 1, nq, d)).astype(np.float32)
+        Q[..., 0] = 8.0
+        _, _, O = orc.run(_f16_bits(Q), kb, vb, 0, 64, 64, causal, 0.125)
+        ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125).reshape(O.shape)
+        assert np.abs(O - ex).max() < 2.0 ** -4 * 5.0   # FP8 V: relative error below 2^-4 of max|v| = 5
+        seen = O if not causal else O[64:]
+        assert np.abs(seen - 5.0).max() < 0.02
+        if causal:
+            assert np.abs(O[:64]).max() < 4.0 and np.abs(O[:64] - 5.0).min() > 0.5
+
+
+def test_ragged_shapes_against_fp64():
+    for (B, Hq, Hkv, Nq, Nkv, causal, seed) in ((1, 2, 2, 77, 77, True, 25), (2, 4, 2, 130, 300, False, 26),
+                                                (1, 3, 1, 50, 190, True, 27), (1, 2, 1, 300, 70, False, 28)):
+        Q, K, V = _gqa_inputs(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, seed=seed)
+        qb, kb, vb = (_f16_bits(a) for a in (Q, K, V))
+        _, _, O = orc.run(qb, kb, vb, 0, 64, 64, causal, 0.125)
+        ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125)
+        a, b = O.astype(np.float64).ravel(), ex.ravel()
+        assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.995, (Nq, Nkv, causal)
