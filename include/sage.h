@@ -35,10 +35,14 @@
  *    sharing Hkv K/V heads (grouped heads: query head h reads K/V head
  *    h / (Hq/Hkv)), and Nq queries against Nkv keys.  The quantized codes and
  *    scales are always head-major, as documented below for H, N.
- *  - Supported: d in {64, 128}; N (Nq and Nkv) a multiple of 128 with
- *    128 <= N <= 524288; blk_q in {64, 128}; blk_k = 64; B*H >= 1; Hq a
- *    multiple of Hkv; causal only with Nkv >= Nq; sm_scale finite and > 0;
- *    inputs finite.
+ *  - Lengths need not be block multiples.  Quantization blocks are runs of
+ *    blk tokens from token 0 and the last one holds the N mod blk remaining
+ *    tokens.  The code buffers are padded with zero codes: Q codes to
+ *    Np = N rounded up to 128 rows, K and V codes to Nt = N rounded up to 64
+ *    (one KV tile); a padding block gets scale 0.
+ *  - Supported: d in {64, 128}; 1 <= N (Nq and Nkv) <= 524288; blk_q in
+ *    {64, 128}; blk_k = 64; B*H >= 1; Hq a multiple of Hkv; causal only with
+ *    Nkv >= Nq; sm_scale finite and > 0; inputs finite.
  */
 #ifndef SAGE_H
 #define SAGE_H
@@ -89,9 +93,11 @@ size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d);
  *     (ties to even) in [-127, 127]; a block with a < 2^-120 gets scale 0 and
  *     all-zero codes.
  * In:  Q, K        [B,H,N,d] float16 (in_dtype SAGE_F16) or bfloat16 (SAGE_BF16).
- * Out: q_codes     [B,H,N,d] int8;  q_scale [B,H,N/blk_q] fp32;
- *      k_codes     [B,H,N,d] int8;  k_scale [B,H,N/blk_k] fp32;
- *      k_mean      [B,H,d] fp32.
+ * Out: q_codes     [B,H,Np,d] int8;  q_scale [B,H,Np/blk_q] fp32;
+ *      k_codes     [B,H,Nt,d] int8;  k_scale [B,H,Nt/64] fp32;
+ *      k_mean      [B,H,d] fp32 (mean over the N tokens).
+ *      (Np = N rounded up to 128, Nt = N rounded up to 64; padding rows hold
+ *      zero codes.)
  * workspace: device scratch of at least sage_quantize_qk_workspace_bytes(...);
  *      contents on entry are ignored.
  */
@@ -104,9 +110,10 @@ int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, i
  * Hkv heads and Nkv tokens (the mean of K runs over its own Nkv tokens), both
  * in `layout` (same quantization as above).
  * In:  Q [B,Hq,Nq,d] or [B,Nq,Hq,d]; K [B,Hkv,Nkv,d] or [B,Nkv,Hkv,d].
- * Out: q_codes [B,Hq,Nq,d], q_scale [B,Hq,Nq/blk_q], k_codes [B,Hkv,Nkv,d],
- *      k_scale [B,Hkv,Nkv/blk_k], k_mean [B,Hkv,d] (head-major whatever the
- *      layout).  workspace: sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
+ * Out: q_codes [B,Hq,Nqp,d], q_scale [B,Hq,Nqp/blk_q], k_codes [B,Hkv,Nkt,d],
+ *      k_scale [B,Hkv,Nkt/64], k_mean [B,Hkv,d] (head-major whatever the
+ *      layout; Nqp = Nq rounded up to 128, Nkt = Nkv rounded up to 64).
+ *      workspace: sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
  */
 int sage_quantize_qk_ex(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
                         int Nkv, int d, int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
@@ -126,7 +133,8 @@ size_t sage_quantize_v_workspace_bytes(int B, int H, int N, int d);
  * Out: v_codes e4m3 bytes in KV-tile channel-major order: for head (b,h),
  *              tile t of 64 consecutive tokens and channel c, the 64 codes of
  *              tokens 64t..64t+63 are contiguous at byte offset
- *              (((b*H + h)*(N/64) + t)*d + c)*64.
+ *              (((b*H + h)*Nt/64 + t)*d + c)*64 (Nt = N rounded up to 64;
+ *              tokens at or past N get code 0).
  *      v_scale [B,H,d] fp32.
  */
 int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
@@ -145,7 +153,8 @@ int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, in
  * traffic"; FP8 P~ and two-level P~V accumulation: SageAttention2 abstract;
  * causal block skipping: blog, variables under "Attention kernel benchmarks".)
  * For query row i, KV tiles of sage_kv_tile() keys are visited in ascending
- * order (causal: only tiles holding a key j <= i; key j is visible iff j <= i):
+ * order (the last one may be partial; causal: only tiles holding a key
+ * j <= i; key j is visible iff j <= i):
  *   S_j    = sum_c q_codes[i,c] k_codes[j,c]               (int32, exact)
  *   c2     = (q_scale * k_scale_j) * (sm_scale * log2 e)   (fp32, in this order)
  *   m'     = max(m, max_j fp32(S_j) * c2)
@@ -185,7 +194,7 @@ int sage_attn_fwd_ex(const int8_t* q_codes, const float* q_scale, const int8_t* 
  * sage_attn_fwd_dump -- sage_attn_fwd through the same kernel code, which in
  * addition writes the int32 scores and the FP8 codes of P~ of selected
  * 128-query tiles (test and diagnostic use).
- * sel:    n_sel device int32 ids (b*H + h) * (N/128) + qt of query tiles.
+ * sel:    n_sel device int32 ids (b*H + h) * ceil(N/128) + qt of query tiles.
  * s_dump: [n_sel, 128, N] int32; entry (k, r, j) = S for query qt*128 + r and
  *         key j, for every key of every KV tile the kernel computed for that
  *         query's 32-row group (other entries are left untouched).
@@ -199,7 +208,7 @@ int sage_attn_fwd_dump(const int8_t* q_codes, const float* q_scale, const int8_t
 
 /*
  * sage_attn_fwd_ex_dump -- sage_attn_fwd_ex with the dumps of
- * sage_attn_fwd_dump: sel ids are (b*Hq + h) * (Nq/128) + qt; s_dump and
+ * sage_attn_fwd_dump: sel ids are (b*Hq + h) * ceil(Nq/128) + qt; s_dump and
  * p_dump are [n_sel, 128, Nkv].
  */
 int sage_attn_fwd_ex_dump(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,

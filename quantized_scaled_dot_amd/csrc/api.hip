@@ -19,10 +19,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
-  if (N % sage::kQTile != 0 || N > (1 << 19)) return SAGE_ERR_UNSUPPORTED;
+  if (N > (1 << 19)) return SAGE_ERR_UNSUPPORTED;
   const long long bh = (long long)B * H;
-  // flattened 1-D grids: (N/64) * B*H workgroups must fit in a grid dimension
-  if (bh * (N / sage::kKTile) > 0x7fffffffLL) return SAGE_ERR_UNSUPPORTED;
+  // flattened 1-D grids: ceil(N/64) * B*H workgroups must fit in a grid dimension
+  if (bh * ((N + sage::kKTile - 1) / sage::kKTile) > 0x7fffffffLL) return SAGE_ERR_UNSUPPORTED;
   return SAGE_OK;
 }
 
@@ -87,8 +87,8 @@ const char* sage_status_string(int status) {
       return "SAGE_ERR_INVALID_ARG: null pointer, bad size, dtype, layout or sm_scale, Hq not a multiple of Hkv, "
              "or causal with Nq > Nkv";
     case SAGE_ERR_UNSUPPORTED:
-      return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N % 128 == 0, N <= 2^19 (Nq and Nkv), "
-             "blk_q in {64,128}, blk_k == 64";
+      return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N <= 2^19 (Nq and Nkv), blk_q in {64,128}, "
+             "blk_k == 64";
     case SAGE_ERR_MISALIGNED: return "SAGE_ERR_MISALIGNED: pointer not 16-byte aligned";
     case SAGE_ERR_HIP: return "SAGE_ERR_HIP: kernel launch failed";
     case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";

@@ -4,7 +4,9 @@
 // tiles of 64 keys of its K/V head (query head h of Hq reads K/V head
 // h / (Hq/Hkv)) are staged in LDS and visited in ascending order.  With fewer
 // queries than keys, query row i is aligned with key i + (Nkv - Nq): under
-// the causal mask it sees keys 0 .. i + Nkv - Nq.
+// the causal mask it sees keys 0 .. i + Nkv - Nq.  Lengths need not be tile
+// multiples: the codes are zero-padded to whole tiles, keys at or past Nkv
+// are masked like causal ones, and rows at or past Nq are not stored.
 //
 // LDS: two buffers of {K tile in MFMA order, rows padded to d+16 bytes;
 // V tile channel-major, rows padded to 80 bytes}.
@@ -44,6 +46,7 @@ struct AttnK {
   const float* v_scale;
   void* O;
   int Hq, g, Nq, Nkv, off, nqt, nbq, blk_q, nhd;   // g = Hq/Hkv; off = Nkv - Nq
+  int nqp, nkt;   // Q code rows per head (Nq rounded up to 128); KV tiles per head
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -98,8 +101,13 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int D, bool CAUSAL, int OUT, bool DUMP>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p) {
+// RAGGED: Nq or Nkv is not a multiple of 128 (masked partial last KV tile,
+// unstored padding rows, 1 to 4 masked steps at the end; at d = 64 it runs 2
+// workgroups per CU, where the 3 of the other d = 64 kernels would spill).
+// Otherwise the masked steps are exactly the two causal diagonal tiles and
+// none at all without the mask.
+template <int D, bool CAUSAL, bool RAGGED, int OUT, bool DUMP>
+__global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
   constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
   constexpr int TILE = kKTile * D;             // bytes of one K tile = one V tile in HBM
@@ -141,7 +149,10 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   const int bhkv = bh / p.g;
   const int Nq = p.Nq, Nkv = p.Nkv, off = p.off;
   const int q0 = qt * kQTile, qrow0 = q0 + wave * 32, row = qrow0 + li;
-  const int lastk = row + off;   // causal: the last key this row sees
+  // the last key this row sees, and the smallest such key over the wave
+  // (only read in masked steps)
+  const int lastk = !RAGGED ? row + off : CAUSAL ? min(row + off, Nkv - 1) : Nkv - 1;
+  const int lastk0 = !RAGGED ? qrow0 + off : CAUSAL ? min(qrow0 + off, Nkv - 1) : Nkv - 1;
 
   int dump_idx = -1;
   if (DUMP) {
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
 
   v4i qreg[KS];
   {
-    const int8_t* qp = p.q_codes + ((size_t)bh * Nq + row) * D + 16 * lg;
+    const int8_t* qp = p.q_codes + ((size_t)bh * p.nqp + row) * D + 16 * lg;
 #pragma unroll
     for (int s = 0; s < KS; s++) qreg[s] = *(const v4i*)(qp + 32 * s);
   }
@@ -170,8 +181,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
   constexpr int JK = (NKI + 3) / 4, JV = (NVI + 3) / 4;
-  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bhkv * Nkv * D, (uint32_t)(Nkv * D));
-  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * Nkv * D, (uint32_t)(Nkv * D));
+  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
+  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
   uint32_t koff[JK], voff[JV];
 #pragma unroll
   for (int j = 0; j < JK; j++) {
@@ -212,8 +223,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     for (int e = 0; e < 16; e++) oacc[ct][e] = 0.0f;
   float m = -1e30f, lpart = 0.0f;
 
-  const int ntiles = CAUSAL ? (q0 + kQTile + off) / kKTile : Nkv / kKTile;
-  const float* kscale = p.k_scale + (size_t)bhkv * (Nkv / kKTile);
+  // tiles up to the one holding the workgroup's last visible key
+  const int ntiles = CAUSAL ? min((q0 + kQTile - 1 + off) / kKTile + 1, p.nkt) : p.nkt;
+  const float* kscale = p.k_scale + (size_t)bhkv * p.nkt;
 
   // S^T = K_t . Q^T (int32) for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v).
   auto qk = [&](int t, v16i& a0, v16i& a1) {
@@ -297,9 +309,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       if (DUMP && dump_idx >= 0) {
         int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
 #pragma unroll
-        for (int v = 0; v < 16; v++) { sd[v] = sc0[v]; sd[16 + v] = sc1[v]; }
+        for (int v = 0; v < 16; v++) {
+          if (!RAGGED || keyb + v < Nkv) sd[v] = sc0[v];
+          if (!RAGGED || keyb + 16 + v < Nkv) sd[16 + v] = sc1[v];
+        }
       }
-      const bool diag = DIAG && (kv0 + kKTile - 1 > qrow0 + off);
+      const bool diag = DIAG && (kv0 + kKTile - 1 > lastk0);
       // ---- online softmax state (the max runs over visible keys only) ----
       int smax = INT32_MIN;
       if (diag) {
@@ -350,7 +365,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
 #pragma unroll
-        for (int k = 0; k < 32; k++) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
+        for (int k = 0; k < 32; k++)
+          if (!RAGGED || keyb + k < Nkv) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
       }
       // alpha = exp2(m - m'): 1 exactly where the max did not grow, 0 on the
       // first visited tile (m = -1e30, the state is still zero)
@@ -371,20 +387,22 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   // prologue: K_0, V_0, K_1 staged, scores of tile 0 issued
   stageK(0, 0);
   stageV(0, 0);
-  stageK(1, 1);   // ntiles >= 2
+  stageK(min(1, ntiles - 1), 1);
   staged();
   __syncthreads();
   v16i sa0, sa1, sb0, sb1;
   qk(0, sa0, sa1);
 
-  // Tiles before the causal diagonal region are fully visible to every row;
-  // their count is even (Nq and Nkv are multiples of 128).  The pipelined step always
-  // computes the next tile's scores there: after the last tile of a
-  // non-causal pass that reads a stale (but in-bounds) K slot and is unused.
+  // Tiles fully visible to every row of the workgroup (before the causal
+  // diagonal and before a partial last tile), rounded down to an even count,
+  // take the unmasked steps in pairs.  The pipelined step always computes the
+  // next tile's scores there: after the last tile of a non-causal pass that
+  // reads a stale (but in-bounds) K slot and is unused.  The remaining 0 to 4
+  // tiles take the masked steps.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  const int nint = CAUSAL ? (q0 + off) / kKTile : ntiles;
+  const int nint = (CAUSAL ? (q0 + off + 1) / kKTile : Nkv / kKTile) & ~1;
   int t = 0;
   if (nint > 0) {
     tile_step(0, sa0, sa1, sb0, sb1, std::false_type{}, I0{}, true);
@@ -395,9 +413,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
     tile_step(t, sb0, sb1, sa0, sa1, std::false_type{}, I1{}, true);   // t = nint - 1
     t = nint;
   }
-  if (CAUSAL) {   // the two diagonal tiles (q0 + off)/64 and the next (scores of tile t are in sa)
-    tile_step(t, sa0, sa1, sb0, sb1, std::integral_constant<bool, CAUSAL>{}, I2{}, !future(t + 1));
-    tile_step(t + 1, sb0, sb1, sa0, sa1, std::integral_constant<bool, CAUSAL>{}, I2{}, false);
+  if (RAGGED) {
+    for (; t < ntiles; t += 2) {   // masked steps (scores of tile t are in sa)
+      tile_step(t, sa0, sa1, sb0, sb1, std::true_type{}, I2{}, t + 1 < ntiles && !future(t + 1));
+      if (t + 1 == ntiles) { t = ntiles; break; }
+      tile_step(t + 1, sb0, sb1, sa0, sa1, std::true_type{}, I2{}, t + 2 < ntiles && !future(t + 2));
+    }
+  } else if (CAUSAL) {   // the two diagonal tiles (q0 + off)/64 and the next (scores of tile t are in sa)
+    tile_step(t, sa0, sa1, sb0, sb1, std::true_type{}, I2{}, !future(t + 1));
+    tile_step(t + 1, sb0, sb1, sa0, sa1, std::true_type{}, I2{}, false);
     t += 2;
   }
   if (pend) {   // the last visited tile is t-1
@@ -410,6 +434,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
   const float inv = 1.0f / lt;
   const float* vs = p.v_scale + (size_t)bhkv * D;
   const size_t orow = p.nhd ? ((size_t)(bh / p.Hq) * Nq + row) * p.Hq + bh % p.Hq : (size_t)bh * Nq + row;
+  const bool store = !RAGGED || row < Nq;
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) {
 #pragma unroll
@@ -419,21 +444,31 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_kernel(AttnK p)
       v4f o;
 #pragma unroll
       for (int e = 0; e < 4; e++) o[e] = oacc[ct][4 * q + e] * (sc[e] * inv);
-      store4<OUT>(p.O, orow * D + c0, o);
+      if (store) store4<OUT>(p.O, orow * D + c0, o);
     }
   }
 }
 
-template <int D, bool CAUSAL, int OUT>
-static void launch3(const AttnK& k, int grid, bool dump, hipStream_t st) {
-  if (dump) hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, OUT, true>), dim3(grid), dim3(256), 0, st, k);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, OUT, false>), dim3(grid), dim3(256), 0, st, k);
+template <int D, bool CAUSAL, bool RAGGED, int OUT>
+static void launch4(const AttnK& k, int grid, bool dump, hipStream_t st) {
+  if (dump) hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, OUT, true>), dim3(grid), dim3(256), 0, st, k);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, OUT, false>), dim3(grid), dim3(256), 0, st, k);
 }
-template <int D, bool CAUSAL>
-static void launch2(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
-  if (out == 2) launch3<D, CAUSAL, 2>(k, grid, dump, st);
-  else if (out == 1) launch3<D, CAUSAL, 1>(k, grid, dump, st);
-  else launch3<D, CAUSAL, 0>(k, grid, dump, st);
+template <int D, bool CAUSAL, bool RAGGED>
+static void launch3(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
+  if (out == 2) launch4<D, CAUSAL, RAGGED, 2>(k, grid, dump, st);
+  else if (out == 1) launch4<D, CAUSAL, RAGGED, 1>(k, grid, dump, st);
+  else launch4<D, CAUSAL, RAGGED, 0>(k, grid, dump, st);
+}
+template <int D>
+static void launch2(const AttnK& k, int grid, bool causal, bool ragged, int out, bool dump, hipStream_t st) {
+  if (causal) {
+    if (ragged) launch3<D, true, true>(k, grid, out, dump, st);
+    else launch3<D, true, false>(k, grid, out, dump, st);
+  } else {
+    if (ragged) launch3<D, false, true>(k, grid, out, dump, st);
+    else launch3<D, false, false>(k, grid, out, dump, st);
+  }
 }
 
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
@@ -441,16 +476,13 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
   k.v_codes = a.v_codes; k.v_scale = a.v_scale; k.O = a.O;
   k.Hq = a.Hq; k.g = a.Hq / a.Hkv; k.Nq = a.Nq; k.Nkv = a.Nkv; k.off = a.Nkv - a.Nq;
-  k.nqt = a.Nq / kQTile; k.nbq = a.Nq / a.blk_q; k.blk_q = a.blk_q; k.nhd = a.nhd; k.s2 = a.s2;
+  k.nqt = (a.Nq + kQTile - 1) / kQTile; k.nqp = k.nqt * kQTile; k.nbq = k.nqp / a.blk_q;
+  k.nkt = (a.Nkv + kKTile - 1) / kKTile; k.blk_q = a.blk_q; k.nhd = a.nhd; k.s2 = a.s2;
   k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
   const int grid = a.B * a.Hq * k.nqt;
-  if (a.d == 128) {
-    if (a.causal) launch2<128, true>(k, grid, a.out_dtype, dump, st);
-    else launch2<128, false>(k, grid, a.out_dtype, dump, st);
-  } else {
-    if (a.causal) launch2<64, true>(k, grid, a.out_dtype, dump, st);
-    else launch2<64, false>(k, grid, a.out_dtype, dump, st);
-  }
+  const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
+  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, a.out_dtype, dump, st);
+  else launch2<64>(k, grid, a.causal, ragged, a.out_dtype, dump, st);
 }
 
 }  // namespace sage

@@ -27,9 +27,11 @@ __device__ __forceinline__ float half_of(const v4i& raw, int e, int is_bf16) {
 }
 
 // Rows of d elements of an input tensor: [B,H,N,d] (head-major) or [B,N,H,d]
-// (token-major).  Row n of flat head bh starts at head(bh) + n * stride.
+// (token-major).  Row n of flat head bh starts at head(bh) + n * stride.  The
+// codes of a head hold P >= N rows (N rounded up to the block / tile); rows
+// N..P-1 are zero codes.
 struct InRows {
-  int H, N, nhd;
+  int H, N, P, nhd;
   __device__ __forceinline__ size_t head(int bh, int D) const {
     return nhd ? ((size_t)(bh / H) * N * H + (size_t)(bh % H)) * D : (size_t)bh * N * D;
   }
@@ -40,6 +42,7 @@ struct InRows {
 // Symmetric INT8 quantization of one block of BLK tokens x D channels:
 // a = max|x| (x = K - mean when SMOOTH), scale = a/127, r = 127/a,
 // code = rint(x * r) in [-127, 127]; a < 2^-120 gives scale 0 and zero codes.
+// Tokens at or past N (the shorter last block) are not read and count as 0.
 // 256 threads hold BLK*D/256 values each.
 // ---------------------------------------------------------------------------
 template <int D, int BLK, bool SMOOTH>
@@ -48,18 +51,20 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
                                             float* __restrict__ scale, int lin, float* red4) {
   constexpr int EPT = BLK * D / 256;   // values per thread
   constexpr int LPT = EPT / 8;         // 16-byte loads per thread
-  const int N = in.N;
-  const int nblk = N / BLK;
+  const int nblk = in.P / BLK;
   const int blk = lin % nblk, bh = lin / nblk;
   const int t = threadIdx.x;
-  const size_t off = ((size_t)bh * N + (size_t)blk * BLK) * D;   // codes: [BH, N, D]
+  const size_t off = ((size_t)bh * in.P + (size_t)blk * BLK) * D;   // codes: [BH, P, D]
   const uint16_t* src = X + in.head(bh, D) + (size_t)blk * BLK * in.stride(D);
+  const int nvalid = min(BLK, in.N - blk * BLK);   // tokens of this block present in X (may be <= 0)
   float x[EPT];
   float a = 0.0f;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
     const int ch = l * 256 + t;   // 16-byte chunk index within the block
-    v4i raw = *(const v4i*)(src + (size_t)(ch / (D / 8)) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
+    const bool valid = nvalid == BLK || ch / (D / 8) < nvalid;
+    v4i raw = {0, 0, 0, 0};
+    if (valid) raw = *(const v4i*)(src + (size_t)(ch / (D / 8)) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
     const int c0 = (ch * 8) % D;
     float mu[8];
     if (SMOOTH) {
@@ -71,7 +76,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       float v = half_of(raw, e, is_bf16);
-      if (SMOOTH) v = v - mu[e];
+      if (SMOOTH) v = valid ? v - mu[e] : 0.0f;
       x[l * 8 + e] = v;
       a = fmaxf(a, fabsf(v));
     }
@@ -145,7 +150,7 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
   }
 }
 
-// Pass 1 of quantize_qk.  Grid: B*Hq*Nq/BLKQ Q blocks followed by B*Hkv*nchunk K chunks.
+// Pass 1 of quantize_qk.  Grid: B*Hq*P/BLKQ Q blocks followed by B*Hkv*nchunk K chunks.
 template <int D, int BLKQ>
 __global__ __launch_bounds__(256) void qk_pass1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                         int is_bf16, InRows qin, InRows kin, int nq, int nchunk,
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict
   }
 }
 
-// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: B*Hkv*Nkv/64.
+// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: B*Hkv*P/64.
 template <int D>
 __global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, InRows kin,
                                                        const float* __restrict__ k_mean, int8_t* __restrict__ k_codes,
@@ -263,16 +268,16 @@ __global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ 
 // FP8 codes of one KV tile of 64 tokens, written channel-major: the 64 codes of
 // channel c are contiguous (the layout the attention kernel stages into LDS).
 // code = e4m3(clamp(rn(v * r_c), +-448)), round to nearest even; zero channels
-// give code 0.  A thread converts 4 consecutive tokens x 8 channels and packs
+// and tokens at or past N (padding of the last tile) give code 0.  A thread converts 4 consecutive tokens x 8 channels and packs
 // each channel's 4 codes into one dword, so the transpose happens in registers
 // and every channel row is written as 16 consecutive dwords.
-// Grid: BH * N/64.  Block: 16 * D/8 threads.
+// Grid: BH * P/64.  Block: 16 * D/8 threads.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
                                                               const float* __restrict__ v_recip,
                                                               uint8_t* __restrict__ v_codes) {
-  const int ntile = in.N / kKTile;
+  const int ntile = in.P / kKTile;
   const size_t rs = in.stride(D);
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
   const int t = threadIdx.x, cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
@@ -283,9 +288,11 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
 #pragma unroll
   for (int e = 0; e < 4; e++) { r[e] = r0[e]; r[e + 4] = r1[e]; }
   float y[4][8];
+  const int nvalid = in.N - (tile * kKTile + 4 * tg);   // this thread's tokens present in V
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const v4i raw = *(const v4i*)(src + (size_t)i * rs);
+    v4i raw = {0, 0, 0, 0};
+    if (i < nvalid) raw = *(const v4i*)(src + (size_t)i * rs);
 #pragma unroll
     for (int e = 0; e < 8; e++) y[i][e] = fminf(fmaxf(half_of(raw, e, is_bf16) * r[e], -448.0f), 448.0f);
   }
@@ -302,14 +309,15 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
 // Host launchers.
 // ---------------------------------------------------------------------------
 static inline int stat_chunks(int N) { return (N + kStatChunk - 1) / kStatChunk; }
+static inline int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
 template <int D>
 static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
   const int BHq = a.B * a.Hq, BHkv = a.B * a.Hkv;
   const int nchunk = stat_chunks(a.Nkv);
   long long* partial = (long long*)a.workspace;
-  const InRows qin{a.Hq, a.Nq, a.nhd}, kin{a.Hkv, a.Nkv, a.nhd};
-  const int nq = BHq * (a.Nq / a.blk_q);
+  const InRows qin{a.Hq, a.Nq, round_up(a.Nq, kQTile), a.nhd}, kin{a.Hkv, a.Nkv, round_up(a.Nkv, kKTile), a.nhd};
+  const int nq = BHq * (qin.P / a.blk_q);
   const int grid1 = nq + BHkv * nchunk;
   if (a.blk_q == 128)
     hipLaunchKernelGGL((qk_pass1_kernel<D, 128>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
@@ -319,7 +327,7 @@ static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
                        (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
   hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
                      D, a.k_mean);
-  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(BHkv * (a.Nkv / 64)), dim3(256), 0, st, (const uint16_t*)a.K,
+  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(BHkv * (kin.P / kKTile)), dim3(256), 0, st, (const uint16_t*)a.K,
                      a.is_bf16, kin, (const float*)a.k_mean, a.k_codes, a.k_scale);
 }
 
@@ -334,12 +342,12 @@ static void launch_v_d(const QuantVArgs& a, hipStream_t st) {
   const int nchunk = stat_chunks(a.N);
   float* partial = (float*)a.workspace;
   float* recip = partial + (size_t)BH * nchunk * D;
-  const InRows in{a.H, a.N, a.nhd};
+  const InRows in{a.H, a.N, round_up(a.N, kKTile), a.nhd};
   hipLaunchKernelGGL(v_colmax_kernel<D>, dim3(nchunk * BH), dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, in,
                      nchunk, partial);
   hipLaunchKernelGGL(v_scale_kernel, dim3(BH * (D / 16)), dim3(256), 0, st, (const float*)partial, nchunk, D,
                      a.v_scale, recip);
-  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(a.N / kKTile * BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
+  hipLaunchKernelGGL(v_quant_kernel<D>, dim3(in.P / kKTile * BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
                      a.is_bf16, in, (const float*)recip, a.v_codes);
 }
 

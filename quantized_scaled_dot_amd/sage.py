@@ -161,6 +161,10 @@ def _bhnd(x, layout):
     return (B, a, b, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, b, a, d)
 
 
+def _round_up(n, m):
+    return -(-n // m) * m
+
+
 def _plain(B, Hq, Hkv, Nq, Nkv, layout):
     return _layout(layout) == SAGE_LAYOUT_BHND and Hq == Hkv and Nq == Nkv
 
@@ -168,16 +172,19 @@ def _plain(B, Hq, Hkv, Nq, Nkv, layout):
 def quantize_qk(Q, K, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream=None):
     """INT8 per-block Q and smoothed K.  Q: [B,Hq,Nq,d], K: [B,Hkv,Nkv,d] (or
     [B,N,H,d] with layout="bnhd").  Returns a dict of device tensors; the codes
-    and scales are head-major whatever the layout."""
+    and scales are head-major whatever the layout, with Q codes padded to a
+    multiple of 128 rows and K codes to a multiple of 64 (zero codes), plus
+    the true lengths "Nq" and "Nkv"."""
     B, Hq, Nq, d = _bhnd(Q, layout)
     Bk, Hkv, Nkv, dk = _bhnd(K, layout)
     if (Bk, dk) != (B, d) or K.dtype != Q.dtype:
         raise ValueError("Q and K must have the same batch, head dim and dtype")
     dev = Q.device
-    out = dict(q_codes=torch.empty((B, Hq, Nq, d), dtype=torch.int8, device=dev),
-               q_scale=torch.empty((B, Hq, Nq // blk_q), dtype=torch.float32, device=dev),
-               k_codes=torch.empty((B, Hkv, Nkv, d), dtype=torch.int8, device=dev),
-               k_scale=torch.empty((B, Hkv, Nkv // blk_k), dtype=torch.float32, device=dev),
+    Nqp, Nkt = _round_up(Nq, 128), _round_up(Nkv, sage_kv_tile())
+    out = dict(q_codes=torch.empty((B, Hq, Nqp, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, Hq, Nqp // blk_q), dtype=torch.float32, device=dev),
+               k_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, Hkv, Nkt // blk_k), dtype=torch.float32, device=dev),
                k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
     wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
     if workspace is None:
@@ -190,16 +197,18 @@ def quantize_qk(Q, K, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream
     else:
         _check(sage_quantize_qk_ex(_ptr(Q), _ptr(K), dt, _layout(layout), B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k,
                                    *ptrs))
-    out.update(blk_q=blk_q, blk_k=blk_k)
+    out.update(blk_q=blk_q, blk_k=blk_k, Nq=Nq, Nkv=Nkv)
     return out
 
 
 def quantize_v(V, layout="bhnd", workspace=None, stream=None):
     """FP8 e4m3 V with per-channel scales.  Returns (v_codes, v_scale); v_codes
-    is in KV-tile channel-major order (see ``v_codes_to_natural``)."""
+    is in KV-tile channel-major order (see ``v_codes_to_natural``), padded with
+    zero codes to whole tiles of 64 tokens."""
     B, H, N, d = _bhnd(V, layout)
     dev = V.device
-    v_codes = torch.empty((B, H, N // sage_kv_tile(), d, sage_kv_tile()), dtype=torch.uint8, device=dev)
+    kt = sage_kv_tile()
+    v_codes = torch.empty((B, H, -(-N // kt), d, kt), dtype=torch.uint8, device=dev)
     v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     wsb = sage_quantize_v_workspace_bytes(B, H, N, d)
     if workspace is None:
@@ -215,7 +224,7 @@ def quantize_v(V, layout="bhnd", workspace=None, stream=None):
 
 
 def v_codes_to_natural(v_codes):
-    """[B, H, N/64, d, 64] tile layout -> [B, H, N, d] token-major (a view permutation)."""
+    """[B, H, Nt/64, d, 64] tile layout -> [B, H, Nt, d] token-major (Nt: tokens rounded up to 64)."""
     B, H, T, d, kt = v_codes.shape
     return v_codes.permute(0, 1, 2, 4, 3).reshape(B, H, T * kt, d)
 
@@ -229,8 +238,9 @@ def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=No
     """Attention on quantized operands.  ``qk`` from quantize_qk, ``v`` = (v_codes, v_scale).
     O is [B,Hq,Nq,d] (or [B,Nq,Hq,d] with layout="bnhd").  ``dump`` = (sel int32
     tensor, s_dump, p_dump) routes through the dump entry points."""
-    B, Hq, Nq, d = qk["q_codes"].shape
-    Hkv, Nkv = qk["k_codes"].shape[1:3]
+    B, Hq, _, d = qk["q_codes"].shape
+    Hkv = qk["k_codes"].shape[1]
+    Nq, Nkv = qk["Nq"], qk["Nkv"]
     v_codes, v_scale = v
     if sm_scale is None:
         sm_scale = default_sm_scale(d)

@@ -90,6 +90,10 @@ WORKLOADS = {
     "chunked-prefill-4k-of-32k-gqa-causal": Workload("chunked-prefill-4k-of-32k-gqa-causal", 1, 32, 4096, 128,
                                                      "bfloat16", True, 128, 64, 4.0, _rsqrt32(128), Hkv_=8,
                                                      Nkv_=32768),
+    # lengths that are not tile multiples: 3000 queries at the end of 3500 keys
+    "llm-prefill-ragged-3000-of-3500-gqa-causal": Workload("llm-prefill-ragged-3000-of-3500-gqa-causal", 2, 32,
+                                                           3000, 128, "bfloat16", True, 128, 64, 4.0,
+                                                           _rsqrt32(128), Hkv_=8, Nkv_=3500),
 }
 
 

@@ -35,7 +35,9 @@ def test_status_strings_and_constants():
 def test_workspace_sizes():
     assert sage.sage_quantize_qk_workspace_bytes(1, 24, 32768, 128) == 24 * 128 * 128 * 8   # 256-token chunks
     assert sage.sage_quantize_v_workspace_bytes(1, 2, 256, 64) == (2 * 1 * 64 + 2 * 64) * 4
-    assert sage.sage_quantize_qk_workspace_bytes(1, 1, 100, 64) == 0   # unsupported N
+    assert sage.sage_quantize_qk_workspace_bytes(1, 1, 0, 64) == 0     # invalid N
+    assert sage.sage_quantize_qk_workspace_bytes(1, 1, 100, 64) == 64 * 8   # one partial 256-token chunk
+    assert sage.sage_quantize_v_workspace_bytes(1, 1, 257, 64) == (2 * 64 + 64) * 4
 
 
 A = 4096  # a fake 16-byte aligned address; never dereferenced because validation fails first
@@ -63,7 +65,7 @@ def _attn(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=96), sage.SAGE_ERR_UNSUPPORTED), (dict(N=200), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(d=96), sage.SAGE_ERR_UNSUPPORTED), (dict(N=(1 << 19) + 1), sage.SAGE_ERR_UNSUPPORTED),
     (dict(N=1 << 20), sage.SAGE_ERR_UNSUPPORTED), (dict(B=0), sage.SAGE_ERR_INVALID_ARG),
     (dict(H=-1), sage.SAGE_ERR_INVALID_ARG), (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG),
     (dict(in_dtype=7), sage.SAGE_ERR_INVALID_ARG), (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED),
@@ -76,7 +78,7 @@ def test_quantize_qk_rejects(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=32), sage.SAGE_ERR_UNSUPPORTED), (dict(N=64), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(d=32), sage.SAGE_ERR_UNSUPPORTED), (dict(N=0), sage.SAGE_ERR_INVALID_ARG),
     (dict(V=None), sage.SAGE_ERR_INVALID_ARG), (dict(v_codes=A + 4), sage.SAGE_ERR_MISALIGNED),
     (dict(in_dtype=-1), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=0), sage.SAGE_ERR_WORKSPACE),
 ])
@@ -85,7 +87,7 @@ def test_quantize_v_rejects(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=256), sage.SAGE_ERR_UNSUPPORTED), (dict(N=192), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(d=256), sage.SAGE_ERR_UNSUPPORTED), (dict(N=-128), sage.SAGE_ERR_INVALID_ARG),
     (dict(blk_q=256), sage.SAGE_ERR_UNSUPPORTED), (dict(blk_k=32), sage.SAGE_ERR_UNSUPPORTED),
     (dict(out_dtype=3), sage.SAGE_ERR_INVALID_ARG), (dict(causal=2), sage.SAGE_ERR_INVALID_ARG),
     (dict(sm_scale=0.0), sage.SAGE_ERR_INVALID_ARG), (dict(sm_scale=-1.0), sage.SAGE_ERR_INVALID_ARG),
@@ -128,8 +130,8 @@ def _attn_ex(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(layout=2), sage.SAGE_ERR_INVALID_ARG), (dict(layout=-1), sage.SAGE_ERR_INVALID_ARG),
     (dict(Hq=3), sage.SAGE_ERR_INVALID_ARG), (dict(Hkv=0), sage.SAGE_ERR_INVALID_ARG),
-    (dict(Hkv=8), sage.SAGE_ERR_INVALID_ARG), (dict(Nq=192), sage.SAGE_ERR_UNSUPPORTED),
-    (dict(Nkv=100), sage.SAGE_ERR_UNSUPPORTED), (dict(Nkv=1 << 20), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(Hkv=8), sage.SAGE_ERR_INVALID_ARG), (dict(Nq=(1 << 19) + 64), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(Nkv=-100), sage.SAGE_ERR_INVALID_ARG), (dict(Nkv=1 << 20), sage.SAGE_ERR_UNSUPPORTED),
     (dict(Nq=0), sage.SAGE_ERR_INVALID_ARG), (dict(d=32), sage.SAGE_ERR_UNSUPPORTED),
     (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG), (dict(K=None), sage.SAGE_ERR_INVALID_ARG),
     (dict(workspace_bytes=16), sage.SAGE_ERR_WORKSPACE),
@@ -147,7 +149,7 @@ def test_quantize_qk_ex_workspace_follows_k():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(layout=5), sage.SAGE_ERR_INVALID_ARG), (dict(N=200), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(layout=5), sage.SAGE_ERR_INVALID_ARG), (dict(N=(1 << 19) + 2), sage.SAGE_ERR_UNSUPPORTED),
     (dict(V=A + 8), sage.SAGE_ERR_MISALIGNED), (dict(workspace_bytes=0), sage.SAGE_ERR_WORKSPACE),
 ])
 def test_quantize_v_ex_rejects(kw, status):
@@ -157,7 +159,7 @@ def test_quantize_v_ex_rejects(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(layout=3), sage.SAGE_ERR_INVALID_ARG), (dict(Hq=6, Hkv=4), sage.SAGE_ERR_INVALID_ARG),
     (dict(Nq=512), sage.SAGE_ERR_INVALID_ARG),              # causal with Nq > Nkv: first rows see no key
-    (dict(Nq=128, Nkv=320), sage.SAGE_ERR_UNSUPPORTED), (dict(Hkv=-2), sage.SAGE_ERR_INVALID_ARG),
+    (dict(Nq=385, Nkv=384), sage.SAGE_ERR_INVALID_ARG), (dict(Hkv=-2), sage.SAGE_ERR_INVALID_ARG),
     (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
     (dict(O=A + 4), sage.SAGE_ERR_MISALIGNED), (dict(k_scale=None), sage.SAGE_ERR_INVALID_ARG),
 ])

@@ -68,32 +68,43 @@ def run_oracle_quant(w, Q, K, V):
 
 
 def check_quant_bit_exact(g, qk, vc, vs):
-    for key in ("k_mean", "q_scale", "k_scale"):
-        assert np.array_equal(g[key].view(np.uint32), qk[key].view(np.uint32)), key
-    for key in ("q_codes", "k_codes"):
-        if not np.array_equal(g[key], qk[key]):
-            bad = np.argwhere(g[key] != qk[key])
+    """Codes and scales bit-exact on the real tokens and blocks; the padding
+    of the device buffers (Q rows to a multiple of 128, K/V rows to a multiple
+    of 64, their extra blocks) is all zero."""
+    def split(got, n, axis=2):
+        return np.split(got, [n], axis=axis)
+
+    assert np.array_equal(g["k_mean"].view(np.uint32), qk["k_mean"].view(np.uint32)), "k_mean"
+    for key in ("q_scale", "k_scale"):
+        real, pad = split(g[key], qk[key].shape[2])
+        assert np.array_equal(real.view(np.uint32), qk[key].view(np.uint32)), key
+        assert not pad.any(), f"{key} padding"
+    for key, ref in (("q_codes", qk["q_codes"]), ("k_codes", qk["k_codes"]), ("v_codes", vc)):
+        real, pad = split(g[key], ref.shape[2])
+        if not np.array_equal(real, ref):
+            bad = np.argwhere(real != ref)
             raise AssertionError(f"{key}: {len(bad)} mismatches, first at {bad[0]}")
+        assert not pad.any(), f"{key} padding"
     assert np.array_equal(g["v_scale"].view(np.uint32), vs.view(np.uint32))
-    if not np.array_equal(g["v_codes"], vc):
-        bad = np.argwhere(g["v_codes"] != vc)
-        raise AssertionError(f"v_codes: {len(bad)} mismatches, first at {bad[0]}")
 
 
 def check_dump(w, g, qk, tiles):
-    nqt = w.N // 128
+    """Yields (flat query rows, their P~ dump rows, visibility) of each dumped
+    tile; rows past N (padding of the last query tile) are left out."""
+    nqt = -(-w.N // 128)
     for k, tid in enumerate(tiles):
         bh, qt = divmod(tid, nqt)
-        rows = bh * w.N + qt * 128 + np.arange(128)
+        nr = min(128, w.N - qt * 128)
+        rows = bh * w.N + qt * 128 + np.arange(nr)
         s_ref = orc.qk_int32(qk["q_codes"], qk["k_codes"], rows)
-        s_got = g["s_dump"][k]
+        s_got = g["s_dump"][k][:nr]
         written = s_got != S_SENTINEL
-        i = qt * 128 + np.arange(128)[:, None]
+        i = qt * 128 + np.arange(nr)[:, None]
         j = np.arange(w.Nkv)[None, :]
         visible = (j <= i + (w.Nkv - w.N)) if w.causal else np.ones_like(written)
         assert written[visible].all(), "a visible score was not computed"
         assert np.array_equal(s_got[written], s_ref[written]), "int32 QK^T mismatch"
-        yield rows, g["p_dump"][k], visible
+        yield rows, g["p_dump"][k][:nr], visible
 
 
 def check_p_codes(p_got, p_ref, visible):
@@ -136,7 +147,7 @@ def small_workload(name):
 def test_small_full_parity(name):
     w = small_workload(name)
     Q, K, V = synth.make_inputs(w)
-    nqt = w.N // 128
+    nqt = -(-w.N // 128)
     tiles = sorted({0, nqt - 1, (w.B * w.H - 1) * nqt + nqt // 2})
     g = run_gpu(w, Q, K, V, dump_tiles=tiles)
     qk, vc, vs = run_oracle_quant(w, Q, K, V)
@@ -163,6 +174,18 @@ SMALL_EX = {
     "q384-of-k128-noncausal-f16": dict(base="tiny-f16-256", B=1, H=2, N=384, Nkv_=128),
     "mqa-chunk128-of-640-causal-d64": dict(base="vit-2k-f16", B=2, H=4, Hkv_=1, N=128, Nkv_=640, causal=True),
     "gqa8-xcd-chunk-noncausal-d128": dict(base="video-dit-32k", B=2, H=64, Hkv_=8, N=128, Nkv_=512),
+    # lengths that are not multiples of 128: partial last Q block / query tile,
+    # partial last KV tile, causal offsets that are not tile multiples
+    "ragged-causal-N200-d128": dict(base="llm-prefill-4k-causal", B=1, H=2, N=200),
+    "ragged-f16-d64-N77-blkq64": dict(base="vit-2k-f16", B=2, H=2, N=77, blk_q=64),
+    "ragged-gqa-causal-130-of-1000": dict(base="llm-prefill-4k-causal", B=1, H=8, Hkv_=2, N=130, Nkv_=1000,
+                                          blk_q=64),
+    "ragged-one-key-tail-d64": dict(base="vit-2k-f16", B=1, H=2, N=256, Nkv_=65),
+    "ragged-single-token-causal": dict(base="llm-prefill-4k-causal", B=1, H=1, N=1),
+    "ragged-causal-300-of-384": dict(base="llm-prefill-4k-causal", B=1, H=2, N=300, Nkv_=384),
+    "ragged-mqa-256-of-333": dict(base="video-dit-32k", B=1, H=4, Hkv_=1, N=256, Nkv_=333),
+    "ragged-xcd-causal-d64-N190": dict(base="vit-2k-f16", B=1, H=16, Hkv_=8, N=190, causal=True,
+                                       dtype="bfloat16"),
 }
 
 
@@ -178,7 +201,7 @@ def test_small_grouped_and_unequal_parity(name, layout):
     w = small_ex_workload(name)
     Q, K, V = synth.make_inputs(w)
     assert Q.shape == (w.B, w.H, w.N, w.d) and K.shape == (w.B, w.Hkv, w.Nkv, w.d)
-    nqt = w.N // 128
+    nqt = -(-w.N // 128)
     tiles = sorted({0, nqt - 1, (w.B * w.H - 1) * nqt + nqt // 2, (w.B * w.H // 2) * nqt})
     g = run_gpu(w, Q, K, V, dump_tiles=tiles, layout=layout)
     qk, vc, vs = run_oracle_quant(w, Q, K, V)
@@ -325,17 +348,20 @@ def _sample_rows(w, rng, n_rand=24):
 def test_full_size_workload(name):
     w = synth.WORKLOADS[name]
     Q, K, V = synth.make_inputs(w)
-    nqt = w.N // 128
+    nqt = -(-w.N // 128)
     tiles = (0, w.B * w.H * nqt - 1)
     g = run_gpu(w, Q, K, V, dump_tiles=tiles)
     qk, vc, vs = run_oracle_quant(w, Q, K, V)
     check_quant_bit_exact(g, qk, vc, vs)
     rows = _sample_rows(w, np.random.default_rng(123))
-    dump_rows = np.concatenate([np.arange(128), (w.B * w.H - 1) * w.N + (nqt - 1) * 128 + np.arange(128)])
+    dumps = list(check_dump(w, g, qk, tiles))
+    dump_rows = np.concatenate([r for r, _, _ in dumps])
     O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale,
                                  rows=np.concatenate([rows, dump_rows]), want_p=True)
-    for k, (r, p_got, visible) in enumerate(check_dump(w, g, qk, tiles)):
-        check_p_codes(p_got, P_ref[len(rows) + 128 * k: len(rows) + 128 * (k + 1)], visible)
+    at = len(rows)
+    for r, p_got, visible in dumps:
+        check_p_codes(p_got, P_ref[at: at + len(r)], visible)
+        at += len(r)
     O = g["O"].reshape(-1, w.d)
     err = np.abs(O[rows] - O_ref[:len(rows)])
     assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"
