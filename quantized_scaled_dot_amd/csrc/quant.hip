@@ -55,16 +55,18 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
   const int blk = lin % nblk, bh = lin / nblk;
   const int t = threadIdx.x;
   const size_t off = ((size_t)bh * in.P + (size_t)blk * BLK) * D;   // codes: [BH, P, D]
-  const uint16_t* src = X + in.head(bh, D) + (size_t)blk * BLK * in.stride(D);
-  const int nvalid = min(BLK, in.N - blk * BLK);   // tokens of this block present in X (may be <= 0)
+  const uint16_t* src = X + in.head(bh, D);
   float x[EPT];
   float a = 0.0f;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
     const int ch = l * 256 + t;   // 16-byte chunk index within the block
-    const bool valid = nvalid == BLK || ch / (D / 8) < nvalid;
-    v4i raw = {0, 0, 0, 0};
-    if (valid) raw = *(const v4i*)(src + (size_t)(ch / (D / 8)) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
+    // a token past N reads the last real token (every load stays in bounds
+    // and none is predicated) and then counts as zero
+    const int tok = blk * BLK + ch / (D / 8);
+    const bool valid = tok < in.N;
+    v4i raw = *(const v4i*)(src + (size_t)min(tok, in.N - 1) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
+    if (!valid) raw = v4i{0, 0, 0, 0};
     const int c0 = (ch * 8) % D;
     float mu[8];
     if (SMOOTH) {
@@ -281,18 +283,19 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
   const size_t rs = in.stride(D);
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
   const int t = threadIdx.x, cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
-  const uint16_t* src = V + in.head(bh, D) + ((size_t)tile * kKTile + 4 * tg) * rs + 8 * cg;
+  const uint16_t* src = V + in.head(bh, D) + 8 * cg;   // channel group of this head; rows added below
   const v4f r0 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg);
   const v4f r1 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg + 4);
   float r[8];
 #pragma unroll
   for (int e = 0; e < 4; e++) { r[e] = r0[e]; r[e + 4] = r1[e]; }
   float y[4][8];
-  const int nvalid = in.N - (tile * kKTile + 4 * tg);   // this thread's tokens present in V
+  const int tok0 = tile * kKTile + 4 * tg;   // this thread's first token
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    v4i raw = {0, 0, 0, 0};
-    if (i < nvalid) raw = *(const v4i*)(src + (size_t)i * rs);
+    // a token past N reads the last real token and then counts as zero
+    v4i raw = *(const v4i*)(src + (size_t)min(tok0 + i, in.N - 1) * rs);
+    if (tok0 + i >= in.N) raw = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; e++) y[i][e] = fminf(fmaxf(half_of(raw, e, is_bf16) * r[e], -448.0f), 448.0f);
   }
