@@ -41,7 +41,7 @@
  *    Np = N rounded up to 128 rows, K and V codes to Nt = N rounded up to 64
  *    (one KV tile); a padding block gets scale 0.
  *  - Supported: d in {64, 128}; 1 <= N (Nq and Nkv) <= 524288; blk_q in
- *    {64, 128}; blk_k = 64; B*H >= 1; Hq a multiple of Hkv; causal only with
+ *    {32, 64, 128}; blk_k in {16, 32, 64}; B*H >= 1; Hq a multiple of Hkv; causal only with
  *    Nkv >= Nq; sm_scale finite and > 0; inputs finite.
  */
 #ifndef SAGE_H
@@ -94,7 +94,7 @@ size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d);
  *     all-zero codes.
  * In:  Q, K        [B,H,N,d] float16 (in_dtype SAGE_F16) or bfloat16 (SAGE_BF16).
  * Out: q_codes     [B,H,Np,d] int8;  q_scale [B,H,Np/blk_q] fp32;
- *      k_codes     [B,H,Nt,d] int8;  k_scale [B,H,Nt/64] fp32;
+ *      k_codes     [B,H,Nt,d] int8;  k_scale [B,H,Nt/blk_k] fp32;
  *      k_mean      [B,H,d] fp32 (mean over the N tokens).
  *      (Np = N rounded up to 128, Nt = N rounded up to 64; padding rows hold
  *      zero codes.)
@@ -111,7 +111,7 @@ int sage_quantize_qk(const void* Q, const void* K, int in_dtype, int B, int H, i
  * in `layout` (same quantization as above).
  * In:  Q [B,Hq,Nq,d] or [B,Nq,Hq,d]; K [B,Hkv,Nkv,d] or [B,Nkv,Hkv,d].
  * Out: q_codes [B,Hq,Nqp,d], q_scale [B,Hq,Nqp/blk_q], k_codes [B,Hkv,Nkt,d],
- *      k_scale [B,Hkv,Nkt/64], k_mean [B,Hkv,d] (head-major whatever the
+ *      k_scale [B,Hkv,Nkt/blk_k], k_mean [B,Hkv,d] (head-major whatever the
  *      layout; Nqp = Nq rounded up to 128, Nkt = Nkv rounded up to 64).
  *      workspace: sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
  */

@@ -35,6 +35,14 @@ int check_shapes(int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d) {
   return SAGE_OK;
 }
 
+// Quantization block sizes: Q blocks of 32 (one wave's rows), 64 or 128
+// tokens; K blocks of 16, 32 or 64 keys (a quarter, half or whole KV tile).
+int check_blocks(int blk_q, int blk_k) {
+  if (blk_q != 32 && blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
+  if (blk_k != 16 && blk_k != 32 && blk_k != 64) return SAGE_ERR_UNSUPPORTED;
+  return SAGE_OK;
+}
+
 int check_in_dtype(int dt) { return (dt == SAGE_F16 || dt == SAGE_BF16) ? SAGE_OK : SAGE_ERR_INVALID_ARG; }
 
 int launch_status() {
@@ -53,8 +61,7 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
                 int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
                 const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, bool dump, void* stream) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
-  if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
-  if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
+  SAGE_TRY(check_blocks(blk_q, blk_k));
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
   if (causal && Nkv < Nq) return SAGE_ERR_INVALID_ARG;   // the first rows would see no key
@@ -68,7 +75,8 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   sage::AttnArgs a;
   a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
   a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype; a.nhd = layout == SAGE_LAYOUT_BNHD;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.causal = causal;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.blk_k = blk_k;
+  a.causal = causal;
   a.s2 = sm_scale * sage::kLog2e;
   a.sel = dump ? sel : nullptr; a.n_sel = dump ? n_sel : 0; a.s_dump = s_dump; a.p_dump = p_dump;
   (void)hipGetLastError();
@@ -87,8 +95,8 @@ const char* sage_status_string(int status) {
       return "SAGE_ERR_INVALID_ARG: null pointer, bad size, dtype, layout or sm_scale, Hq not a multiple of Hkv, "
              "or causal with Nq > Nkv";
     case SAGE_ERR_UNSUPPORTED:
-      return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N <= 2^19 (Nq and Nkv), blk_q in {64,128}, "
-             "blk_k == 64";
+      return "SAGE_ERR_UNSUPPORTED: shape outside d in {64,128}, N <= 2^19 (Nq and Nkv), blk_q in {32,64,128}, "
+             "blk_k in {16,32,64}";
     case SAGE_ERR_MISALIGNED: return "SAGE_ERR_MISALIGNED: pointer not 16-byte aligned";
     case SAGE_ERR_HIP: return "SAGE_ERR_HIP: kernel launch failed";
     case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
@@ -113,14 +121,13 @@ int sage_quantize_qk_ex(const void* Q, const void* K, int in_dtype, int layout, 
                         float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_in_dtype(in_dtype));
-  if (blk_q != 64 && blk_q != 128) return SAGE_ERR_UNSUPPORTED;
-  if (blk_k != 64) return SAGE_ERR_UNSUPPORTED;
+  SAGE_TRY(check_blocks(blk_q, blk_k));
   SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
   SAGE_PTR(k_mean); SAGE_PTR(workspace);
   if (workspace_bytes < sage::quantize_qk_workspace(B * Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
   sage::QuantQKArgs a;
   a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.blk_k = blk_k;
   a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale; a.k_mean = k_mean;
   a.workspace = workspace;
   (void)hipGetLastError();

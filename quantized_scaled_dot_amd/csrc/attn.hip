@@ -47,6 +47,7 @@ struct AttnK {
   void* O;
   int Hq, g, Nq, Nkv, off, nqt, nbq, blk_q, nhd;   // g = Hq/Hkv; off = Nkv - Nq
   int nqp, nkt;   // Q code rows per head (Nq rounded up to 128); KV tiles per head
+  int nbk, lgk;   // K scales per head; log2 of the K block size
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -106,7 +107,11 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, 
 // workgroups per CU, where the 3 of the other d = 64 kernels would spill).
 // Otherwise the masked steps are exactly the two causal diagonal tiles and
 // none at all without the mask.
-template <int D, bool CAUSAL, bool RAGGED, int OUT, bool DUMP>
+// FINEK: K blocks of 16 or 32 keys.  A lane's 32 keys of a tile are two runs
+// of 16 (keys 32g + v and 32g + 16 + v), each inside one K block, so a lane
+// dequantizes each run with its own factor and the row max combines the two
+// scaled run maxima.  Otherwise one K block is one KV tile.
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int OUT, bool DUMP>
 __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
   constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
@@ -225,7 +230,9 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
 
   // tiles up to the one holding the workgroup's last visible key
   const int ntiles = CAUSAL ? min((q0 + kQTile - 1 + off) / kKTile + 1, p.nkt) : p.nkt;
-  const float* kscale = p.k_scale + (size_t)bhkv * p.nkt;
+  const float* kscale = p.k_scale + (size_t)bhkv * p.nbk;
+  // K scale index of the run of 16 keys of half h of this lane in tile t
+  auto kidx = [&](int t, int h) { return FINEK ? (t * kKTile + 32 * lg + 16 * h) >> p.lgk : t; };
 
   // S^T = K_t . Q^T (int32) for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v).
   auto qk = [&](int t, v16i& a0, v16i& a1) {
@@ -263,7 +270,8 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   v8i pprev;
   bool pend = false, grew = false;
   float alpha_prev = 1.0f;
-  float ks_next = kscale[0];   // K scale of the tile whose softmax comes next
+  // K scales (of this lane's two runs) of the tile whose softmax comes next
+  float ks_next[2] = {kscale[kidx(0, 0)], FINEK ? kscale[kidx(0, 1)] : 0.0f};
   auto rescale = [&]() {
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
@@ -292,8 +300,9 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     if (had && grew) rescale();   // rare
     // The K scale of tile t+1 is read one step ahead, before the tile
     // copies, so waiting for it never waits for them.
-    const float ks = ks_next;
-    ks_next = kscale[min(t + 1, ntiles - 1)];
+    const float ks0 = ks_next[0], ks1 = ks_next[1];
+    ks_next[0] = kscale[kidx(min(t + 1, ntiles - 1), 0)];
+    if (FINEK) ks_next[1] = kscale[kidx(min(t + 1, ntiles - 1), 1)];
     // In flight while tile t is computed: K_{t+2} replaces K_t (read by the
     // previous step's score MFMAs), V_{t+1} replaces V_{t-2} (read by the
     // previous step's P~V).  Past the last tile the index is clamped: the
@@ -316,19 +325,35 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
       }
       const bool diag = DIAG && (kv0 + kKTile - 1 > lastk0);
       // ---- online softmax state (the max runs over visible keys only) ----
-      int smax = INT32_MIN;
-      if (diag) {
+      float ustar, c2a, c2b;   // c2a, c2b: dequantization factors of the two runs
+      if (!FINEK) {
+        int smax = INT32_MIN;
+        if (diag) {
 #pragma unroll
-        for (int v = 0; v < 16; v++)
-          smax = max(max(smax, keyb + v > lastk ? INT32_MIN : sc0[v]), keyb + 16 + v > lastk ? INT32_MIN : sc1[v]);
+          for (int v = 0; v < 16; v++)
+            smax = max(max(smax, keyb + v > lastk ? INT32_MIN : sc0[v]), keyb + 16 + v > lastk ? INT32_MIN : sc1[v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; v++) smax = max(max(smax, sc0[v]), sc1[v]);   // v_max3_i32 chain
+        }
+        smax = pair_max_i32(smax);
+        c2a = c2b = (dq * ks0) * p.s2;
+        ustar = (float)smax * c2a;
+        if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
       } else {
+        int sa = INT32_MIN, sb = INT32_MIN;
 #pragma unroll
-        for (int v = 0; v < 16; v++) smax = max(max(smax, sc0[v]), sc1[v]);   // v_max3_i32 chain
+        for (int v = 0; v < 16; v++) {
+          sa = max(sa, diag && keyb + v > lastk ? INT32_MIN : sc0[v]);
+          sb = max(sb, diag && keyb + 16 + v > lastk ? INT32_MIN : sc1[v]);
+        }
+        c2a = (dq * ks0) * p.s2;
+        c2b = (dq * ks1) * p.s2;
+        float ua = (float)sa * c2a, ub = (float)sb * c2b;
+        if (DIAG && sa == INT32_MIN) ua = -1e30f;
+        if (DIAG && sb == INT32_MIN) ub = -1e30f;
+        ustar = pair_max_f32(fmaxf(ua, ub));
       }
-      smax = pair_max_i32(smax);
-      const float c2 = (dq * ks) * p.s2;
-      float ustar = (float)smax * c2;
-      if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
       const float mnew = fmaxf(m, ustar);
       const float mm = mnew - 8.0f;
       if (next) qk(t + 1, nx0, nx1);
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
-            float arg = __builtin_fmaf((float)sv, c2, -mm);
+            float arg = __builtin_fmaf((float)sv, h == 0 ? c2a : c2b, -mm);
             if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
             pv4[e] = x;
@@ -449,25 +474,33 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 }
 
-template <int D, bool CAUSAL, bool RAGGED, int OUT>
-static void launch4(const AttnK& k, int grid, bool dump, hipStream_t st) {
-  if (dump) hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, OUT, true>), dim3(grid), dim3(256), 0, st, k);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, OUT, false>), dim3(grid), dim3(256), 0, st, k);
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int OUT>
+static void launch5(const AttnK& k, int grid, bool dump, hipStream_t st) {
+  if (dump)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, OUT, true>), dim3(grid), dim3(256), 0, st, k);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, OUT, false>), dim3(grid), dim3(256), 0, st, k);
+}
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK>
+static void launch4(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
+  if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, 2>(k, grid, dump, st);
+  else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, 1>(k, grid, dump, st);
+  else launch5<D, CAUSAL, RAGGED, FINEK, 0>(k, grid, dump, st);
 }
 template <int D, bool CAUSAL, bool RAGGED>
-static void launch3(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
-  if (out == 2) launch4<D, CAUSAL, RAGGED, 2>(k, grid, dump, st);
-  else if (out == 1) launch4<D, CAUSAL, RAGGED, 1>(k, grid, dump, st);
-  else launch4<D, CAUSAL, RAGGED, 0>(k, grid, dump, st);
+static void launch3(const AttnK& k, int grid, bool finek, int out, bool dump, hipStream_t st) {
+  if (finek) launch4<D, CAUSAL, RAGGED, true>(k, grid, out, dump, st);
+  else launch4<D, CAUSAL, RAGGED, false>(k, grid, out, dump, st);
 }
 template <int D>
-static void launch2(const AttnK& k, int grid, bool causal, bool ragged, int out, bool dump, hipStream_t st) {
+static void launch2(const AttnK& k, int grid, bool causal, bool ragged, bool finek, int out, bool dump,
+                    hipStream_t st) {
   if (causal) {
-    if (ragged) launch3<D, true, true>(k, grid, out, dump, st);
-    else launch3<D, true, false>(k, grid, out, dump, st);
+    if (ragged) launch3<D, true, true>(k, grid, finek, out, dump, st);
+    else launch3<D, true, false>(k, grid, finek, out, dump, st);
   } else {
-    if (ragged) launch3<D, false, true>(k, grid, out, dump, st);
-    else launch3<D, false, false>(k, grid, out, dump, st);
+    if (ragged) launch3<D, false, true>(k, grid, finek, out, dump, st);
+    else launch3<D, false, false>(k, grid, finek, out, dump, st);
   }
 }
 
@@ -478,11 +511,13 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.Hq = a.Hq; k.g = a.Hq / a.Hkv; k.Nq = a.Nq; k.Nkv = a.Nkv; k.off = a.Nkv - a.Nq;
   k.nqt = (a.Nq + kQTile - 1) / kQTile; k.nqp = k.nqt * kQTile; k.nbq = k.nqp / a.blk_q;
   k.nkt = (a.Nkv + kKTile - 1) / kKTile; k.blk_q = a.blk_q; k.nhd = a.nhd; k.s2 = a.s2;
+  k.nbk = k.nkt * kKTile / a.blk_k; k.lgk = a.blk_k == 16 ? 4 : a.blk_k == 32 ? 5 : 6;
   k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
   const int grid = a.B * a.Hq * k.nqt;
   const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
-  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, a.out_dtype, dump, st);
-  else launch2<64>(k, grid, a.causal, ragged, a.out_dtype, dump, st);
+  const bool finek = a.blk_k < kKTile;
+  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, finek, a.out_dtype, dump, st);
+  else launch2<64>(k, grid, a.causal, ragged, finek, a.out_dtype, dump, st);
 }
 
 }  // namespace sage

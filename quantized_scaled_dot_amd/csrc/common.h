@@ -47,24 +47,6 @@ __device__ __forceinline__ uint32_t f16_bits_rne(float x) {
   return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 16777216.0f);
 }
 
-// Exponential of the fp32 online softmax: X2(t) = p(f) * 2^n with n = floor(t),
-// f = min(t - n, 1 - 2^-24) (v_fract_f32 computes exactly this fp32 value),
-// p(f) = fma(fma(C2, f, C1), f, 1), C1 = 0x1.520a3p-1, C2 = 0x1.5beb9ep-2
-// (relative minimax of 2^f on [0, 1) with p(0) = 1, p(1) = 2; max relative
-// error 2.68e-3).  Scaling by 2^n is v_ldexp_f32 (exact unless the result is
-// subnormal; 0 once n is far below the fp32 range).  Five VALU instructions
-// (fract, floor-convert, 2 fma, ldexp) when NaNs are not honoured, so that
-// floor and conversion fuse; no transcendental unit; reproducible bit for bit.
-// Requires |t| < 2^31 (the conversion); exp2_softmax_clamped accepts any
-// finite t and returns the same values (X2(t) = 0 for t < -200).
-__device__ __forceinline__ float exp2_softmax(float t) {
-  const float f = __builtin_amdgcn_fractf(t);
-  const float n = __builtin_floorf(t);
-  const float p = __builtin_fmaf(__builtin_fmaf(0x1.5beb9ep-2f, f, 0x1.520a3p-1f), f, 1.0f);
-  return __builtin_amdgcn_ldexpf(p, (int)n);
-}
-__device__ __forceinline__ float exp2_softmax_clamped(float t) { return exp2_softmax(fmaxf(t, -256.0f)); }
-
 // Exchange with the lane 32 apart (same query row, other half of the keys /
 // channels): v_permlane32_swap returns {x[l], x[l^32]} in some order for every
 // lane, so a symmetric combination of the two results is the pair's combination.
@@ -72,6 +54,10 @@ __device__ __forceinline__ int pair_max_i32(int x) {
   auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
   int a = (int)r[0], b = (int)r[1];
   return a > b ? a : b;
+}
+__device__ __forceinline__ float pair_max_f32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum_f32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

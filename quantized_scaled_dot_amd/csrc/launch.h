@@ -13,7 +13,7 @@ struct QuantQKArgs {
   const void* Q;
   const void* K;
   int is_bf16, nhd;
-  int B, Hq, Hkv, Nq, Nkv, d, blk_q;
+  int B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k;
   int8_t* q_codes;
   float* q_scale;
   int8_t* k_codes;
@@ -40,7 +40,7 @@ struct AttnArgs {
   const float* v_scale;
   void* O;
   int out_dtype, nhd;   // O layout: [B,Hq,Nq,d] (0) or [B,Nq,Hq,d] (1)
-  int B, Hq, Hkv, Nq, Nkv, d, blk_q, causal;
+  int B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal;
   float s2;   // fp32(sm_scale * log2 e)
   // dump (test) mode
   const int32_t* sel;

@@ -14,12 +14,17 @@
 
 namespace sage {
 
-__device__ __forceinline__ float block_max_256(float a, float* red4) {
+// Max over each group of TPB consecutive threads (TPB = 128 or 256) of a
+// 256-thread workgroup.
+template <int TPB>
+__device__ __forceinline__ float group_max(float a, float* red4) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
   if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = a;
   __syncthreads();
-  return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+  if (TPB == 256) return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+  const int g = (threadIdx.x >> 7) * 2;
+  return fmaxf(red4[g], red4[g + 1]);
 }
 
 __device__ __forceinline__ float half_of(const v4i& raw, int e, int is_bf16) {
@@ -43,24 +48,32 @@ struct InRows {
 // a = max|x| (x = K - mean when SMOOTH), scale = a/127, r = 127/a,
 // code = rint(x * r) in [-127, 127]; a < 2^-120 gives scale 0 and zero codes.
 // Tokens at or past N (the shorter last block) are not read and count as 0.
-// 256 threads hold BLK*D/256 values each.
+// A block is held by TPB = min(256, BLK*D/8) threads, 8 values per 16-byte
+// load; a 256-thread workgroup quantizes 256/TPB consecutive blocks.
 // ---------------------------------------------------------------------------
+template <int D, int BLK>
+constexpr int blocks_per_wg() { return BLK * D / 8 >= 256 ? 1 : 256 / (BLK * D / 8); }
+
 template <int D, int BLK, bool SMOOTH>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int is_bf16, InRows in,
                                             const float* __restrict__ mean, int8_t* __restrict__ codes,
                                             float* __restrict__ scale, int lin, float* red4) {
-  constexpr int EPT = BLK * D / 256;   // values per thread
-  constexpr int LPT = EPT / 8;         // 16-byte loads per thread
+  constexpr int NB = blocks_per_wg<D, BLK>();
+  constexpr int TPB = 256 / NB;                // threads per block
+  constexpr int LPT = BLK * D / 8 / TPB;       // 16-byte loads per thread
+  constexpr int EPT = 8 * LPT;                 // values per thread
+  static_assert(TPB == 128 || TPB == 256, "block sizes of 16 to 128 tokens at d = 64 or 128");
   const int nblk = in.P / BLK;
-  const int blk = lin % nblk, bh = lin / nblk;
-  const int t = threadIdx.x;
+  const int gblk = lin * NB + (int)threadIdx.x / TPB;
+  const int blk = gblk % nblk, bh = gblk / nblk;
+  const int t = threadIdx.x % TPB;
   const size_t off = ((size_t)bh * in.P + (size_t)blk * BLK) * D;   // codes: [BH, P, D]
   const uint16_t* src = X + in.head(bh, D);
   float x[EPT];
   float a = 0.0f;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
-    const int ch = l * 256 + t;   // 16-byte chunk index within the block
+    const int ch = l * TPB + t;   // 16-byte chunk index within the block
     // a token past N reads the last real token (every load stays in bounds
     // and none is predicated) and then counts as zero
     const int tok = blk * BLK + ch / (D / 8);
@@ -83,14 +96,14 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
       a = fmaxf(a, fabsf(v));
     }
   }
-  a = block_max_256(a, red4);
+  a = group_max<TPB>(a, red4);
   const bool zero = !(a >= 0x1p-120f);
   const float dl = zero ? 0.0f : a / 127.0f;
   const float r = zero ? 0.0f : 127.0f / a;
   int8_t* dst = codes + off;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
-    const int ch = l * 256 + t;
+    const int ch = l * TPB + t;
     unsigned w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -152,7 +165,8 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
   }
 }
 
-// Pass 1 of quantize_qk.  Grid: B*Hq*P/BLKQ Q blocks followed by B*Hkv*nchunk K chunks.
+// Pass 1 of quantize_qk.  Grid: the workgroups of the B*Hq*P/BLKQ Q blocks,
+// followed by B*Hkv*nchunk K chunks.
 template <int D, int BLKQ>
 __global__ __launch_bounds__(256) void qk_pass1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                         int is_bf16, InRows qin, InRows kin, int nq, int nchunk,
@@ -184,13 +198,14 @@ __global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict
   }
 }
 
-// Pass 2 of quantize_qk: INT8 blocks of the smoothed K.  Grid: B*Hkv*P/64.
-template <int D>
+// Pass 2 of quantize_qk: INT8 blocks of BLKK tokens of the smoothed K.
+// Grid: (B*Hkv*P/BLKK) / blocks_per_wg.
+template <int D, int BLKK>
 __global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, InRows kin,
                                                        const float* __restrict__ k_mean, int8_t* __restrict__ k_codes,
                                                        float* __restrict__ k_scale) {
   __shared__ float red4[4];
-  quant_block<D, 64, true>(K, is_bf16, kin, k_mean, k_codes, k_scale, blockIdx.x, red4);
+  quant_block<D, BLKK, true>(K, is_bf16, kin, k_mean, k_codes, k_scale, blockIdx.x, red4);
 }
 
 // ---------------------------------------------------------------------------
@@ -314,24 +329,37 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
 static inline int stat_chunks(int N) { return (N + kStatChunk - 1) / kStatChunk; }
 static inline int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
+template <int D, int BLKQ>
+static int launch_qk_pass1(const QuantQKArgs& a, InRows qin, InRows kin, int nchunk, long long* partial,
+                           hipStream_t st) {
+  const int nq = a.B * a.Hq * (qin.P / BLKQ) / blocks_per_wg<D, BLKQ>();
+  const int grid1 = nq + a.B * a.Hkv * nchunk;
+  hipLaunchKernelGGL((qk_pass1_kernel<D, BLKQ>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
+                     (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
+  return nq;
+}
+
+template <int D, int BLKK>
+static void launch_k_quant(const QuantQKArgs& a, InRows kin, hipStream_t st) {
+  const int grid = a.B * a.Hkv * (kin.P / BLKK) / blocks_per_wg<D, BLKK>();
+  hipLaunchKernelGGL((k_quant_kernel<D, BLKK>), dim3(grid), dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin,
+                     (const float*)a.k_mean, a.k_codes, a.k_scale);
+}
+
 template <int D>
 static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
-  const int BHq = a.B * a.Hq, BHkv = a.B * a.Hkv;
+  const int BHkv = a.B * a.Hkv;
   const int nchunk = stat_chunks(a.Nkv);
   long long* partial = (long long*)a.workspace;
   const InRows qin{a.Hq, a.Nq, round_up(a.Nq, kQTile), a.nhd}, kin{a.Hkv, a.Nkv, round_up(a.Nkv, kKTile), a.nhd};
-  const int nq = BHq * (qin.P / a.blk_q);
-  const int grid1 = nq + BHkv * nchunk;
-  if (a.blk_q == 128)
-    hipLaunchKernelGGL((qk_pass1_kernel<D, 128>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
-                       (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
-  else
-    hipLaunchKernelGGL((qk_pass1_kernel<D, 64>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
-                       (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
+  if (a.blk_q == 128) launch_qk_pass1<D, 128>(a, qin, kin, nchunk, partial, st);
+  else if (a.blk_q == 64) launch_qk_pass1<D, 64>(a, qin, kin, nchunk, partial, st);
+  else launch_qk_pass1<D, 32>(a, qin, kin, nchunk, partial, st);
   hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
                      D, a.k_mean);
-  hipLaunchKernelGGL(k_quant_kernel<D>, dim3(BHkv * (kin.P / kKTile)), dim3(256), 0, st, (const uint16_t*)a.K,
-                     a.is_bf16, kin, (const float*)a.k_mean, a.k_codes, a.k_scale);
+  if (a.blk_k == 64) launch_k_quant<D, 64>(a, kin, st);
+  else if (a.blk_k == 32) launch_k_quant<D, 32>(a, kin, st);
+  else launch_k_quant<D, 16>(a, kin, st);
 }
 
 void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {

@@ -90,6 +90,9 @@ WORKLOADS = {
     "chunked-prefill-4k-of-32k-gqa-causal": Workload("chunked-prefill-4k-of-32k-gqa-causal", 1, 32, 4096, 128,
                                                      "bfloat16", True, 128, 64, 4.0, _rsqrt32(128), Hkv_=8,
                                                      Nkv_=32768),
+    # finer quantization granularity: a Q scale per 32 rows, a K scale per 16 keys
+    "llm-prefill-4k-causal-fine": Workload("llm-prefill-4k-causal-fine", 4, 32, 4096, 128, "bfloat16", True, 32, 16,
+                                           4.0, _rsqrt32(128)),
     # lengths that are not tile multiples: 3000 queries at the end of 3500 keys
     "llm-prefill-ragged-3000-of-3500-gqa-causal": Workload("llm-prefill-ragged-3000-of-3500-gqa-causal", 2, 32,
                                                            3000, 128, "bfloat16", True, 128, 64, 4.0,

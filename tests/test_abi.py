@@ -68,7 +68,7 @@ def _attn(**kw):
     (dict(d=96), sage.SAGE_ERR_UNSUPPORTED), (dict(N=(1 << 19) + 1), sage.SAGE_ERR_UNSUPPORTED),
     (dict(N=1 << 20), sage.SAGE_ERR_UNSUPPORTED), (dict(B=0), sage.SAGE_ERR_INVALID_ARG),
     (dict(H=-1), sage.SAGE_ERR_INVALID_ARG), (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG),
-    (dict(in_dtype=7), sage.SAGE_ERR_INVALID_ARG), (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), sage.SAGE_ERR_INVALID_ARG), (dict(blk_q=16), sage.SAGE_ERR_UNSUPPORTED),
     (dict(blk_k=128), sage.SAGE_ERR_UNSUPPORTED), (dict(Q=None), sage.SAGE_ERR_INVALID_ARG),
     (dict(k_mean=None), sage.SAGE_ERR_INVALID_ARG), (dict(K=A + 8), sage.SAGE_ERR_MISALIGNED),
     (dict(workspace=None), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=16), sage.SAGE_ERR_WORKSPACE),
@@ -88,7 +88,7 @@ def test_quantize_v_rejects(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d=256), sage.SAGE_ERR_UNSUPPORTED), (dict(N=-128), sage.SAGE_ERR_INVALID_ARG),
-    (dict(blk_q=256), sage.SAGE_ERR_UNSUPPORTED), (dict(blk_k=32), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(blk_q=256), sage.SAGE_ERR_UNSUPPORTED), (dict(blk_k=8), sage.SAGE_ERR_UNSUPPORTED),
     (dict(out_dtype=3), sage.SAGE_ERR_INVALID_ARG), (dict(causal=2), sage.SAGE_ERR_INVALID_ARG),
     (dict(sm_scale=0.0), sage.SAGE_ERR_INVALID_ARG), (dict(sm_scale=-1.0), sage.SAGE_ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), sage.SAGE_ERR_INVALID_ARG), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
@@ -160,7 +160,7 @@ def test_quantize_v_ex_rejects(kw, status):
     (dict(layout=3), sage.SAGE_ERR_INVALID_ARG), (dict(Hq=6, Hkv=4), sage.SAGE_ERR_INVALID_ARG),
     (dict(Nq=512), sage.SAGE_ERR_INVALID_ARG),              # causal with Nq > Nkv: first rows see no key
     (dict(Nq=385, Nkv=384), sage.SAGE_ERR_INVALID_ARG), (dict(Hkv=-2), sage.SAGE_ERR_INVALID_ARG),
-    (dict(blk_q=32), sage.SAGE_ERR_UNSUPPORTED), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
+    (dict(blk_q=96), sage.SAGE_ERR_UNSUPPORTED), (dict(sm_scale=float("nan")), sage.SAGE_ERR_INVALID_ARG),
     (dict(O=A + 4), sage.SAGE_ERR_MISALIGNED), (dict(k_scale=None), sage.SAGE_ERR_INVALID_ARG),
 ])
 def test_attn_fwd_ex_rejects(kw, status):

@@ -186,6 +186,13 @@ SMALL_EX = {
     "ragged-mqa-256-of-333": dict(base="video-dit-32k", B=1, H=4, Hkv_=1, N=256, Nkv_=333),
     "ragged-xcd-causal-d64-N190": dict(base="vit-2k-f16", B=1, H=16, Hkv_=8, N=190, causal=True,
                                        dtype="bfloat16"),
+    # finer quantization granularity: one Q scale per wave (32 rows), K scales
+    # per 16 or 32 keys (two runs of 16 keys per lane and tile)
+    "fine-q32-k16-causal-d128": dict(base="llm-prefill-4k-causal", B=1, H=2, N=512, blk_q=32, blk_k=16),
+    "fine-k32-noncausal-d64": dict(base="vit-2k-f16", B=1, H=2, N=384, blk_k=32),
+    "fine-q32-k16-ragged-gqa-d64": dict(base="vit-2k-f16", B=1, H=4, Hkv_=2, N=200, Nkv_=333, causal=True,
+                                        blk_q=32, blk_k=16),
+    "fine-k32-outliers-causal": dict(base="long-prefill-128k-causal", H=2, N=1024, blk_k=32),
 }
 
 
