@@ -57,6 +57,8 @@ def lib():
         L.oracle_quantize_v.argtypes = [P, i32, i32, i32, i32, P, P]
         L.oracle_qk_int32.restype = None
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P]
+        L.oracle_attn_rows_split.restype = i32
+        L.oracle_attn_rows_split.argtypes = [P, P, P, P, P, P] + [i32] * 11 + [f32, P, i32, P]
         L.oracle_attn_rows.restype = i32
         L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                        P, i32, P, P]
@@ -182,6 +184,30 @@ def attn_rows(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, rows=None, k
     if rc != 0:
         raise ValueError("oracle_attn_rows: unsupported arguments")
     return (out, p) if want_p else out
+
+
+def attn_rows_split(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, kv_chunk, rows=None, kv_tile=KV_TILE):
+    """Split-KV oracle attention: chunks of ``kv_chunk`` keys, each with its own
+    online softmax, merged by the log-sum-exp rule.  Same arguments and result
+    as :func:`attn_rows` (no P~ codes)."""
+    qc = _c(qk["q_codes"], np.int8)
+    kc = _c(qk["k_codes"], np.int8)
+    qs = _c(qk["q_scale"], np.float32)
+    ks = _c(qk["k_scale"], np.float32)
+    vc = _c(v_codes, np.uint8)
+    vs = _c(v_scale, np.float32)
+    B, Hq, Nq, d = qc.shape
+    _, Hkv, Nkv, _ = kc.shape
+    if rows is None:
+        rows = np.arange(B * Hq * Nq, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, d), np.float32)
+    rc = lib().oracle_attn_rows_split(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B, Hq, Hkv, Nq, Nkv, d, blk_q,
+                                      blk_k, kv_tile, kv_chunk, int(bool(causal)), float(sm_scale), _p(rows),
+                                      rows.size, _p(out))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows_split: unsupported arguments")
+    return out
 
 
 def run(Q_bits, K_bits, V_bits, dtype, blk_q, blk_k, causal, sm_scale, rows=None, kv_tile=KV_TILE,

@@ -320,78 +320,183 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int B, int Hq
 /* ------------------------------------------------------------------------ */
 static const float LOG2E_F = 0x1.715476p+0f;   /* RN(log2 e) */
 
+/* One query row against the keys of one K/V head (shared by the two entry  */
+/* points below).                                                            */
+typedef struct {
+  const int8_t* q;        /* the row's d codes */
+  float dq;               /* the row's Q scale */
+  const int8_t* k;        /* the head's K codes [Nkv, d] */
+  const float* ks;        /* the head's K scales [ceil(Nkv/blk_k)] */
+  const uint8_t* v;       /* the head's V codes [Nkv, d] */
+  int Nkv, d, blk_k, kv_tile;
+  int64_t last;           /* last visible key (Nkv - 1 without the mask) */
+  float s2;
+  const double* vdec;     /* e4m3 decode table */
+} row_ctx;
+
+/* The online softmax over the tiles j0 = j_begin, j_begin + kv_tile, ...    */
+/* below j_end (j_begin a multiple of kv_tile), from a fresh state: returns  */
+/* the number of visited tiles and leaves m, l and Oacc[d] (Oacc without the */
+/* V scale).  prow (optional): FP8 codes of P~ of the visited keys, indexed  */
+/* by key.                                                                   */
+static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, float* l_out, float* oacc,
+                        uint8_t* prow) {
+  const int kv_tile = x->kv_tile, d = x->d;
+  int32_t* S = (int32_t*)malloc(sizeof(int32_t) * kv_tile);
+  float* c2 = (float*)malloc(sizeof(float) * kv_tile);
+  float* pt = (float*)malloc(sizeof(float) * kv_tile);
+  uint8_t* ph = (uint8_t*)malloc(kv_tile);
+  double* oblk = (double*)malloc(sizeof(double) * d);
+  for (int c = 0; c < d; c++) oacc[c] = 0.0f;
+  float m = 0.0f, l = 0.0f;
+  int visited = 0;
+  for (int j0 = j_begin; j0 < j_end; j0 += kv_tile) {
+    if (j0 > x->last) break;   /* no visible key from here on */
+    int nvis = j0 + kv_tile <= j_end ? kv_tile : j_end - j0;
+    if (x->last - j0 + 1 < nvis) nvis = (int)(x->last - j0 + 1);
+    /* scores of the visible keys j0 .. j0+nvis-1 */
+    float mt = -INFINITY;
+    for (int jj = 0; jj < nvis; jj++) {
+      int j = j0 + jj;
+      const int8_t* k = x->k + (size_t)j * d;
+      int32_t s = 0;
+      for (int c = 0; c < d; c++) s += (int32_t)x->q[c] * (int32_t)k[c];
+      S[jj] = s;
+      c2[jj] = (x->dq * x->ks[j / x->blk_k]) * x->s2;
+      float u = (float)s * c2[jj];
+      if (u > mt) mt = u;
+    }
+    const int first = visited == 0;
+    float mnew = first ? mt : (mt > m ? mt : m);
+    float alpha = first ? 0.0f : oracle_exp2f(m - mnew);
+    float mm = mnew - 8.0f;
+    float rowsum = 0.0f;
+    for (int jj = 0; jj < nvis; jj++) {
+      pt[jj] = oracle_exp2f(fmaf((float)S[jj], c2[jj], -mm));
+      rowsum += pt[jj];
+      ph[jj] = oracle_e4m3_encode(pt[jj]);
+      if (prow) prow[j0 + jj] = ph[jj];
+    }
+    for (int c = 0; c < d; c++) {
+      double acc = 0.0;
+      for (int jj = 0; jj < nvis; jj++) acc += x->vdec[ph[jj]] * x->vdec[x->v[(size_t)(j0 + jj) * d + c]];
+      oblk[c] = acc;
+    }
+    for (int c = 0; c < d; c++) oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);
+    l = fmaf(alpha, l, rowsum);
+    m = mnew;
+    visited++;
+  }
+  free(S); free(c2); free(pt); free(ph); free(oblk);
+  *m_out = m;
+  *l_out = l;
+  return visited;
+}
+
+static int attn_args_ok(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int kv_tile,
+                        int causal, float sm_scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nkv < 1 || d < 1) return 0;
+  if (blk_q < 1 || blk_k < 1 || kv_tile < 1) return 0;
+  if (causal && Nkv < Nq) return 0;   /* the first queries would see no key */
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return 0;
+  return 1;
+}
+
+static void row_setup(row_ctx* x, const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                      const float* k_scale, const uint8_t* v_codes, int Hq, int Hkv, int Nq, int Nkv, int d,
+                      int blk_q, int blk_k, int kv_tile, int causal, float sm_scale, int64_t row,
+                      const double* vdec, int64_t* bk_out) {
+  const int nbq = nblocks(Nq, blk_q), nbk = nblocks(Nkv, blk_k);
+  int64_t bh = row / Nq, i = row % Nq, bk = kv_head(bh, Hq, Hkv);
+  x->q = q_codes + ((size_t)bh * Nq + i) * d;
+  x->dq = q_scale[(size_t)bh * nbq + i / blk_q];
+  x->k = k_codes + (size_t)bk * Nkv * d;
+  x->ks = k_scale + (size_t)bk * nbk;
+  x->v = v_codes + (size_t)bk * Nkv * d;
+  x->Nkv = Nkv; x->d = d; x->blk_k = blk_k; x->kv_tile = kv_tile;
+  x->last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
+  x->s2 = sm_scale * LOG2E_F;
+  x->vdec = vdec;
+  *bk_out = bk;
+}
+
 int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
                      const float* k_scale, const uint8_t* v_codes, const float* v_scale, int B, int Hq,
                      int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int kv_tile, int causal,
                      float sm_scale, const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nkv < 1 || d < 1) return -1;
-  if (blk_q < 1 || blk_k < 1 || kv_tile < 1) return -1;
-  if (causal && Nkv < Nq) return -1;   /* the first queries would see no key */
-  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return -1;
-  const float s2 = sm_scale * LOG2E_F;
-  const int nbq = nblocks(Nq, blk_q), nbk = nblocks(Nkv, blk_k);
-  const int64_t off = (int64_t)Nkv - Nq;
+  if (!attn_args_ok(B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, kv_tile, causal, sm_scale)) return -1;
   double vdec[256];
   for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
   for (int r = 0; r < nrows; r++)
     if (rows[r] < 0 || rows[r] >= (int64_t)B * Hq * Nq) return -1;
 #pragma omp parallel for schedule(dynamic)
   for (int r = 0; r < nrows; r++) {
-    int64_t bh = rows[r] / Nq, i = rows[r] % Nq, bk = kv_head(bh, Hq, Hkv);
-    const int8_t* q = q_codes + ((size_t)bh * Nq + i) * d;
-    const float dq = q_scale[(size_t)bh * nbq + i / blk_q];
-    int32_t* S = (int32_t*)malloc(sizeof(int32_t) * kv_tile);
-    float* c2 = (float*)malloc(sizeof(float) * kv_tile);
-    float* pt = (float*)malloc(sizeof(float) * kv_tile);
-    uint8_t* ph = (uint8_t*)malloc(kv_tile);
-    float* oacc = (float*)calloc(d, sizeof(float));
-    double* oblk = (double*)malloc(sizeof(double) * d);
-    float m = 0.0f, l = 0.0f;
-    int first = 1;
-    if (p_codes) memset(p_codes + (size_t)r * Nkv, 0, Nkv);
-    for (int j0 = 0; j0 < Nkv; j0 += kv_tile) {
-      int nvis = j0 + kv_tile <= Nkv ? kv_tile : Nkv - j0;
-      if (causal) {
-        const int64_t last = i + off;   /* last visible key */
-        if (j0 > last) break;
-        if (last - j0 + 1 < nvis) nvis = (int)(last - j0 + 1);
-      }
-      /* scores of the visible keys j0 .. j0+nvis-1 */
-      float mt = -INFINITY;
-      for (int jj = 0; jj < nvis; jj++) {
-        int j = j0 + jj;
-        const int8_t* k = k_codes + ((size_t)bk * Nkv + j) * d;
-        int32_t s = 0;
-        for (int c = 0; c < d; c++) s += (int32_t)q[c] * (int32_t)k[c];
-        S[jj] = s;
-        c2[jj] = (dq * k_scale[(size_t)bk * nbk + j / blk_k]) * s2;
-        float u = (float)s * c2[jj];
-        if (u > mt) mt = u;
-      }
-      float mnew = first ? mt : (mt > m ? mt : m);
-      float alpha = first ? 0.0f : oracle_exp2f(m - mnew);
-      float mm = mnew - 8.0f;
-      float rowsum = 0.0f;
-      for (int jj = 0; jj < nvis; jj++) {
-        pt[jj] = oracle_exp2f(fmaf((float)S[jj], c2[jj], -mm));
-        rowsum += pt[jj];
-        ph[jj] = oracle_e4m3_encode(pt[jj]);
-        if (p_codes) p_codes[(size_t)r * Nkv + j0 + jj] = ph[jj];
-      }
-      for (int c = 0; c < d; c++) {
-        double acc = 0.0;
-        for (int jj = 0; jj < nvis; jj++)
-          acc += vdec[ph[jj]] * vdec[v_codes[((size_t)bk * Nkv + j0 + jj) * d + c]];
-        oblk[c] = acc;
-      }
-      for (int c = 0; c < d; c++) oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);
-      l = fmaf(alpha, l, rowsum);
-      m = mnew;
-      first = 0;
-    }
+    row_ctx x;
+    int64_t bk;
+    row_setup(&x, q_codes, q_scale, k_codes, k_scale, v_codes, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, kv_tile, causal,
+              sm_scale, rows[r], vdec, &bk);
+    float* oacc = (float*)malloc(sizeof(float) * d);
+    float m, l;
+    uint8_t* prow = p_codes ? p_codes + (size_t)r * Nkv : NULL;
+    if (prow) memset(prow, 0, Nkv);
+    attend_range(&x, 0, Nkv, &m, &l, oacc, prow);
     for (int c = 0; c < d; c++)
       out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
-    free(S); free(c2); free(pt); free(ph); free(oacc); free(oblk);
+    free(oacc);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Split-KV form of the same attention (decode: few queries, a long KV      */
+/* cache; the pages note that decode is bound by reading the KV cache).     */
+/* The keys are cut into chunks of kv_chunk keys (a multiple of kv_tile);   */
+/* each chunk runs the online softmax above from a fresh state, giving      */
+/* (m_c, l_c, Oacc_c) (a chunk with no visible key is left out), and the    */
+/* chunks are merged in ascending order with the log-sum-exp rule:          */
+/*   m* = max_c m_c,  w_c = exp2f(RN(m_c - m*)),                            */
+/*   L = fma(w_c, l_c, L),  O'_c = fma(w_c, Oacc_c, O'_c)   (fp32, from 0)  */
+/*   O = O' * deltaV / L   (as above).                                      */
+/* With kv_chunk >= Nkv this is oracle_attn_rows exactly.                   */
+/* ------------------------------------------------------------------------ */
+int oracle_attn_rows_split(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                           const float* k_scale, const uint8_t* v_codes, const float* v_scale, int B, int Hq,
+                           int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int kv_tile, int kv_chunk,
+                           int causal, float sm_scale, const int64_t* rows, int nrows, float* out) {
+  if (!attn_args_ok(B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, kv_tile, causal, sm_scale)) return -1;
+  if (kv_chunk < kv_tile || kv_chunk % kv_tile) return -1;
+  double vdec[256];
+  for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
+  for (int r = 0; r < nrows; r++)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * Hq * Nq) return -1;
+  const int nc = (Nkv + kv_chunk - 1) / kv_chunk;
+#pragma omp parallel for schedule(dynamic)
+  for (int r = 0; r < nrows; r++) {
+    row_ctx x;
+    int64_t bk;
+    row_setup(&x, q_codes, q_scale, k_codes, k_scale, v_codes, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, kv_tile, causal,
+              sm_scale, rows[r], vdec, &bk);
+    float* mc = (float*)malloc(sizeof(float) * nc);
+    float* lc = (float*)malloc(sizeof(float) * nc);
+    int* vis = (int*)malloc(sizeof(int) * nc);
+    float* oc = (float*)malloc(sizeof(float) * (size_t)nc * d);
+    float* o = (float*)calloc(d, sizeof(float));
+    float mstar = -INFINITY;
+    for (int c = 0; c < nc; c++) {
+      const int j1 = (c + 1) * kv_chunk < Nkv ? (c + 1) * kv_chunk : Nkv;
+      vis[c] = attend_range(&x, c * kv_chunk, j1, &mc[c], &lc[c], oc + (size_t)c * d, NULL) > 0;
+      if (vis[c] && mc[c] > mstar) mstar = mc[c];
+    }
+    float L = 0.0f;
+    for (int c = 0; c < nc; c++) {
+      if (!vis[c]) continue;
+      const float w = oracle_exp2f(mc[c] - mstar);
+      L = fmaf(w, lc[c], L);
+      for (int ch = 0; ch < d; ch++) o[ch] = fmaf(w, oc[(size_t)c * d + ch], o[ch]);
+    }
+    for (int ch = 0; ch < d; ch++)
+      out[(size_t)r * d + ch] = (float)(((double)o[ch] * (double)v_scale[(size_t)bk * d + ch]) / (double)L);
+    free(mc); free(lc); free(vis); free(oc); free(o);
   }
   return 0;
 }

@@ -538,3 +538,91 @@ def test_ragged_shapes_against_fp64():
         ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125)
         a, b = O.astype(np.float64).ravel(), ex.ravel()
         assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.995, (Nq, Nkv, causal)
+
+
+# ------------------------------------------------------------------ split-KV form (decode)
+def _split_case(Hq=4, Hkv=2, Nq=3, Nkv=700, seed=31, causal=True):
+    Q, K, V = _gqa_inputs(Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, seed=seed)
+    qb, kb, vb = (_f16_bits(a) for a in (Q, K, V))
+    qk = orc.quantize_qk(qb, kb, 0, 64, 64)
+    vc, vs = orc.quantize_v(vb, 0)
+    return Q, K, V, qk, vc, vs
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_with_one_chunk_is_the_single_pass(causal):
+    """kv_chunk covering every key: the merge weight is exp2(0) = 1 and the
+    fma merge of one chunk is exact, so the split form is bit-identical."""
+    Q, K, V, qk, vc, vs = _split_case(causal=causal)
+    one = orc.attn_rows(qk, vc, vs, 64, 64, causal, 0.125)
+    for chunk in (704, 768, 4096):
+        split = orc.attn_rows_split(qk, vc, vs, 64, 64, causal, 0.125, kv_chunk=chunk)
+        assert np.array_equal(split.view(np.uint32), one.view(np.uint32)), chunk
+
+
+def test_split_zero_q_gives_mean_of_dequantized_v():
+    """Q = 0: every chunk has m = 0 and P~ = 2^8 per key, so the merged O is the
+    mean of the dequantized V rows the query sees, whatever the chunk size."""
+    Q, K, V, qk, vc, vs = _split_case(Hq=2, Hkv=1, Nq=2, Nkv=300, causal=True)
+    qk = dict(qk, q_codes=np.zeros_like(qk["q_codes"]), q_scale=np.zeros_like(qk["q_scale"]))
+    deq = orc.e4m3_decode(vc) * vs[:, :, None, :].astype(np.float64)   # [1,1,300,d]
+    for chunk in (64, 128, 192):
+        O = orc.attn_rows_split(qk, vc, vs, 64, 64, True, 0.125, kv_chunk=chunk)
+        for r in range(4):   # rows: head h = r // 2, query i = r % 2 sees keys 0 .. i + 298
+            last = r % 2 + 298
+            assert np.allclose(O[r], deq[0, 0, :last + 1].mean(0), rtol=2e-6, atol=1e-6), (chunk, r)
+
+
+def test_split_merge_weights_follow_the_dominant_chunk():
+    """One key in the last chunk dominates every score: the merge must carry
+    its chunk's O (weight ~1) and scale the others by exp2(m_c - m*) ~ 0."""
+    rng = np.random.default_rng(32)
+    d = 64
+    K = rng.standard_normal((1, 1, 640, d)).astype(np.float32) * 0.5
+    K[0, 0, 600] = 0.0
+    K[0, 0, 600, 0] = 12.0
+    V = rng.standard_normal((1, 1, 640, d)).astype(np.float32)
+    V[0, 0, 600] = 5.0
+    Q = rng.standard_normal((1, 1, 4, d)).astype(np.float32)
+    Q[..., 0] = 8.0
+    qk = orc.quantize_qk(_f16_bits(Q), _f16_bits(K), 0, 64, 64)
+    vc, vs = orc.quantize_v(_f16_bits(V), 0)
+    ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), False, 0.125).reshape(4, d)
+    for chunk in (64, 192, 320):
+        O = orc.attn_rows_split(qk, vc, vs, 64, 64, False, 0.125, kv_chunk=chunk)
+        # exact: about 4.972 (the other 639 keys keep ~0.5% of the weight); a
+        # merge that dropped or misweighted the dominant chunk lands near 0
+        assert np.abs(O - 5.0).max() < 0.05 and np.abs(O - ex).max() < 0.03, chunk
+
+
+def test_split_chunks_without_visible_keys_are_left_out():
+    """Causal, Nq = 40 queries at the end of Nkv = 130 keys, chunks of 64: the
+    last chunk (keys 128, 129) is invisible to queries 0 .. 37 and must not
+    enter their merge; the result stays on fp64 exact attention."""
+    Q, K, V, qk, vc, vs = _split_case(Hq=1, Hkv=1, Nq=40, Nkv=130, seed=33)
+    O = orc.attn_rows_split(qk, vc, vs, 64, 64, True, 0.125, kv_chunk=64)
+    assert np.isfinite(O).all()
+    ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), True, 0.125).reshape(O.shape)
+    assert np.abs(O - ex).max() < 0.05
+    a, b = O.astype(np.float64).ravel(), ex.ravel()
+    assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.999
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 320])
+def test_split_against_fp64(chunk):
+    Q, K, V, qk, vc, vs = _split_case(Hq=8, Hkv=2, Nq=4, Nkv=1000, seed=34)
+    for causal in (False, True):
+        O = orc.attn_rows_split(qk, vc, vs, 64, 64, causal, 0.125, kv_chunk=chunk)
+        ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125).reshape(O.shape)
+        a, b = O.astype(np.float64).ravel(), ex.ravel()
+        assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.999
+        one = orc.attn_rows(qk, vc, vs, 64, 64, causal, 0.125)
+        # the split changes where P~ is rounded to FP8, not the size of the error
+        assert np.abs(O - ex).max() < 1.5 * np.abs(one - ex).max() + 1e-3
+
+
+def test_split_rejects_chunks_that_are_not_tile_multiples():
+    Q, K, V, qk, vc, vs = _split_case()
+    for chunk in (0, 32, 100):
+        with pytest.raises(ValueError):
+            orc.attn_rows_split(qk, vc, vs, 64, 64, True, 0.125, kv_chunk=chunk)
