@@ -11,6 +11,12 @@ the CPU oracle timed on a bounded sample of the same workload, and the
 quantize passes' achieved HBM bandwidth (algorithmic bytes: 2 read + 1 written
 per element of Q, K and V; the statistics passes read K and V a second time).
 
+Decode workloads (few new queries against a long cache): the cache is
+quantized once before timing (it is built at prefill); a step is quantize_q
+plus the split-KV decode (chunk kernel + merge).  Its roofline is HBM: the
+algorithmic bytes are the K/V codes and scales read once per query row group,
+the Q codes and scales and O.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
@@ -33,24 +39,25 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "video-dit-32k"
 METRIC = "attention TOPS (4·B·H·N²·d/t) at 1 MI355X; % of INT8/FP8 MFMA peak"
 KERNEL_SOURCES = ("quantized_scaled_dot_amd/csrc/attn.hip", "quantized_scaled_dot_amd/csrc/common.h")
+DECODE_SOURCES = ("quantized_scaled_dot_amd/csrc/decode.hip", "quantized_scaled_dot_amd/csrc/common.h")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_kernel.{workload}.pmc.txt")
+def measured_traffic(workload, kernel="attn_fwd_kernel", sources=KERNEL_SOURCES):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -58,7 +65,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_sha():
+    if vals.get("kernel_source_sha256_16") != kernel_source_sha(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -95,6 +102,105 @@ def cpu_baseline(w, Q, K, V, budget_s=20.0):
                       f"({t_step:.0f} s)"}
 
 
+def decode_rows(w):
+    return w.B * w.H * w.N
+
+
+def cpu_baseline_decode(w, Q, K, V, kv_chunk, budget_s=20.0):
+    """The oracle on the host cores for a decode step: quantize the new queries,
+    then the split-KV attention of a bounded sample of query rows against the
+    quantized cache (quantized once beforehand, as on the GPU)."""
+    from oracle import oracle as orc
+
+    qk = orc.quantize_qk(synth.bits(Q), synth.bits(K), w.dtype_code, w.blk_q, w.blk_k)
+    vc, vs = orc.quantize_v(synth.bits(V), w.dtype_code)
+    t0 = time.perf_counter()
+    orc.quantize_q(synth.bits(Q), w.dtype_code, w.blk_q)
+    t_quant = time.perf_counter() - t0
+    total_rows = decode_rows(w)
+    rng = np.random.default_rng(0)
+    rows = rng.choice(total_rows, min(16, total_rows), replace=False).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk, rows=rows)
+    per_row = (time.perf_counter() - t0) / len(rows)
+    n = int(max(16, min(total_rows, budget_s / max(per_row, 1e-9))))
+    rows = rng.choice(total_rows, n, replace=False).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk, rows=rows)
+    t_rows = time.perf_counter() - t0
+    t_step = t_quant + t_rows * total_rows / n
+    return {"value": round(w.ops / t_step / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"oracle quantization of the {w.B * w.H * w.N} new queries ({t_quant:.3f} s) plus split-KV "
+                      f"attention (chunks of {kv_chunk} keys) for {n} random query rows of {total_rows} "
+                      f"({t_rows:.1f} s), extrapolated linearly to the full step ({t_step:.2f} s); the cache is "
+                      f"quantized beforehand and not timed"}
+
+
+def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
+    B, H, N, d, Hkv, Nkv = w.B, w.H, w.N, w.d, w.Hkv, w.Nkv
+    kc = sage.quantize_k(Kd, w.blk_k)
+    vq = sage.quantize_v(Vd)
+    chunk = sage.sage_decode_kv_chunk(B, H, Hkv, N, Nkv, d)
+    ws = torch.empty(max(sage.sage_attn_decode_workspace_bytes(B, H, Hkv, N, Nkv, d, chunk), 16), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, H, N, d), dtype=w.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        q = sage.quantize_q(Qd, w.blk_q)
+        if ev is not None:
+            ev[0].record(stream)
+        sage.attn_decode(q, kc, vq, causal=w.causal, sm_scale=w.sm_scale, out=out, kv_chunk=chunk, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_step = t * 1e3 / args.steps
+    dec_avg = float(np.mean(dec_ms))
+    value = w.ops / (ms_step * 1e-3) / 1e12
+    # algorithmic bytes of one decode call: every K/V code and scale once per group of 32 query rows
+    # of a K/V head, the Q codes and scales, O
+    groups = -(-(H // Hkv) * N // 32)
+    nkt = -(-Nkv // 64)
+    kv_bytes = B * Hkv * groups * (2 * nkt * 64 * d + nkt * 64 // w.blk_k * 4 + d * 4)
+    q_bytes = B * H * N * d + B * H * -(-N // w.blk_q) * 4
+    o_bytes = B * H * N * d * torch.tensor([], dtype=w.torch_dtype).element_size()
+    alg = kv_bytes + q_bytes + o_bytes
+    gbs = alg / (dec_avg * 1e-3) / 1e9
+    log(f"[bench] decode step {ms_step:.3f} ms; decode call avg {dec_avg:.4f} ms p50 {np.median(dec_ms):.4f} "
+        f"p95 {np.percentile(dec_ms, 95):.4f}: {gbs:.0f} GB/s of {alg / 1e6:.1f} MB algorithmic "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); split {chunk} keys")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)...")
+        cpu = cpu_baseline_decode(w, Q, K, V, chunk, budget_s=args.cpu_budget)
+        log(f"[bench] CPU oracle: {cpu}")
+    line = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+fp8 (fp32 softmax)", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "Hkv": Hkv, "Nkv": Nkv, "d": d, "causal": w.causal,
+                   "in_dtype": w.dtype, "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_chunk": chunk,
+                   "parallelism": "none (1 GPU)"},
+        "decode_ms": round(dec_avg, 5),
+        "roofline": {"bound": "hbm", "kernel": "decode_chunk_kernel + decode_merge_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, "decode_chunk_kernel", DECODE_SOURCES)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +232,9 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
 
+    if w.decode:
+        bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev)
+        return
     B, H, N, d, Hkv, Nkv = w.B, w.H, w.N, w.d, w.Hkv, w.Nkv
     ws_qk = torch.empty(max(sage.sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(max(sage.sage_quantize_v_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)

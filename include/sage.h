@@ -216,6 +216,57 @@ int sage_attn_fwd_ex_dump(const int8_t* q_codes, const float* q_scale, const int
                           int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
                           const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, void* stream);
 
+/*
+ * sage_quantize_q -- the Q part of sage_quantize_qk_ex alone: INT8 blocks of
+ * blk_q tokens of Q [B,Hq,Nq,d] or [B,Nq,Hq,d].  Out: q_codes [B,Hq,Nqp,d],
+ * q_scale [B,Hq,Nqp/blk_q] as there.  No workspace.  (For decode: the new
+ * queries are quantized on their own, the K/V cache once.)
+ */
+int sage_quantize_q(const void* Q, int in_dtype, int layout, int B, int Hq, int Nq, int d, int blk_q,
+                    int8_t* q_codes, float* q_scale, void* stream);
+
+/*
+ * sage_quantize_k -- the K part of sage_quantize_qk_ex alone (mean over the
+ * Nkv tokens, smoothed INT8 blocks of blk_k keys).  Out: k_codes
+ * [B,Hkv,Nkt,d], k_scale [B,Hkv,Nkt/blk_k], k_mean [B,Hkv,d].  workspace:
+ * sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
+ */
+int sage_quantize_k(const void* K, int in_dtype, int layout, int B, int Hkv, int Nkv, int d, int blk_k,
+                    int8_t* k_codes, float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Default keys per split of sage_attn_decode for this shape: a multiple of
+ * sage_kv_tile(), giving as many splits as fit one round of waves (one wave
+ * per SIMD, 1024 on MI355X), at least one tile each; 0 for a bad shape. */
+int sage_decode_kv_chunk(int B, int Hq, int Hkv, int Nq, int Nkv, int d);
+
+/* Bytes of scratch memory sage_attn_decode needs (fp32 partial states, one
+ * [32][d + 2] block per wave of work); kv_chunk 0 = the default.  0 for a bad
+ * shape or chunk. */
+size_t sage_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int kv_chunk);
+
+/*
+ * sage_attn_decode -- sage_attn_fwd_ex for few queries against a long
+ * quantized K/V cache, split over the keys (the pages note that decode is
+ * bound by reading the KV cache).  The Nkv keys are cut into splits of
+ * kv_chunk keys (a multiple of sage_kv_tile(); 0 = sage_decode_kv_chunk).
+ * For every query row each split runs the tiled online softmax of
+ * sage_attn_fwd from a fresh state, giving (m_c, l_c, O_acc,c); the splits
+ * with a visible key are then merged in ascending order:
+ *   m* = max m_c,  w_c = exp2(m_c - m*),  L = sum w_c l_c,
+ *   O' = sum w_c O_acc,c  (fp32 fma),  O = O' * v_scale / L.
+ * The FP8 codes of P~ therefore depend on kv_chunk (each split has its own
+ * running max); with one split the result is that of sage_attn_fwd_ex.
+ * Work: one wave per (batch, K/V head, group of 32 query rows, split); the
+ * Hq/Hkv query heads of a K/V head and their Nq queries share the group, so
+ * each K/V byte is read once per group.  Arguments as sage_attn_fwd_ex, plus
+ * workspace: sage_attn_decode_workspace_bytes(...) bytes, contents ignored.
+ */
+int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                     int kv_chunk, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

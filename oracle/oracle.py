@@ -134,6 +134,17 @@ def quantize_qk(Q_bits, K_bits, dtype, blk_q, blk_k):
     return dict(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks, k_mean=mu)
 
 
+def quantize_q(Q_bits, dtype, blk_q):
+    """INT8 blocks of Q [B,Hq,Nq,d] alone: (q_codes, q_scale [B,Hq,ceil(Nq/blk_q)])."""
+    Q_bits = _c(Q_bits, np.uint16)
+    B, Hq, Nq, d = Q_bits.shape
+    qc = np.empty((B, Hq, Nq, d), np.int8)
+    qs = np.empty((B, Hq, -(-Nq // blk_q)), np.float32)
+    if lib().oracle_quantize_q(_p(Q_bits), dtype, B * Hq, Nq, d, blk_q, _p(qc), _p(qs)) != 0:
+        raise ValueError("oracle quantize_q: unsupported shape")
+    return qc, qs
+
+
 def quantize_v(V_bits, dtype):
     """Returns (v_codes [B,H,N,d] e4m3 in natural token-major layout, v_scale [B,H,d])."""
     V_bits = _c(V_bits, np.uint16)

@@ -163,6 +163,80 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
                             stream);
 }
 
+int sage_quantize_q(const void* Q, int in_dtype, int layout, int B, int Hq, int Nq, int d, int blk_q,
+                    int8_t* q_codes, float* q_scale, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hq, Nq, Nq, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_TRY(check_blocks(blk_q, 64));
+  SAGE_PTR(Q); SAGE_PTR(q_codes); SAGE_PTR(q_scale);
+  sage::QuantQKArgs a{};
+  a.Q = Q; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hq; a.Nq = Nq; a.Nkv = Nq; a.d = d; a.blk_q = blk_q; a.blk_k = 64;
+  a.q_codes = q_codes; a.q_scale = q_scale;
+  (void)hipGetLastError();
+  sage::launch_quantize_qk(a, (hipStream_t)stream, true, false);
+  return launch_status();
+}
+
+int sage_quantize_k(const void* K, int in_dtype, int layout, int B, int Hkv, int Nkv, int d, int blk_k,
+                    int8_t* k_codes, float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hkv, Hkv, Nkv, Nkv, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_TRY(check_blocks(64, blk_k));
+  SAGE_PTR(K); SAGE_PTR(k_codes); SAGE_PTR(k_scale); SAGE_PTR(k_mean); SAGE_PTR(workspace);
+  if (workspace_bytes < sage::quantize_qk_workspace(B * Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
+  sage::QuantQKArgs a{};
+  a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hkv; a.Hkv = Hkv; a.Nq = Nkv; a.Nkv = Nkv; a.d = d; a.blk_q = 64; a.blk_k = blk_k;
+  a.k_codes = k_codes; a.k_scale = k_scale; a.k_mean = k_mean; a.workspace = workspace;
+  (void)hipGetLastError();
+  sage::launch_quantize_qk(a, (hipStream_t)stream, false, true);
+  return launch_status();
+}
+
+int sage_decode_kv_chunk(int B, int Hq, int Hkv, int Nq, int Nkv, int d) {
+  if (check_shapes(SAGE_LAYOUT_BHND, B, Hq, Hkv, Nq, Nkv, d) != SAGE_OK) return 0;
+  return sage::decode_default_chunk(B, Hq, Hkv, Nq, Nkv);
+}
+
+size_t sage_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int kv_chunk) {
+  if (check_shapes(SAGE_LAYOUT_BHND, B, Hq, Hkv, Nq, Nkv, d) != SAGE_OK) return 0;
+  if (kv_chunk == 0) kv_chunk = sage::decode_default_chunk(B, Hq, Hkv, Nq, Nkv);
+  if (kv_chunk < sage::kKTile || kv_chunk % sage::kKTile) return 0;
+  return sage::decode_workspace(B, Hq, Hkv, Nq, Nkv, d, kv_chunk);
+}
+
+int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                     int kv_chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
+  SAGE_TRY(check_blocks(blk_q, blk_k));
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (causal && Nkv < Nq) return SAGE_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  if (kv_chunk == 0) kv_chunk = sage::decode_default_chunk(B, Hq, Hkv, Nq, Nkv);
+  if (kv_chunk < sage::kKTile || kv_chunk % sage::kKTile) return SAGE_ERR_INVALID_ARG;
+  // waves of work: B*Hkv * ceil(g*Nq/32) * chunks, four per workgroup of a 1-D grid
+  const long long units = (long long)B * Hkv * (((long long)(Hq / Hkv) * Nq + 31) / 32) *
+                          (((Nkv + sage::kKTile - 1) / sage::kKTile + kv_chunk / sage::kKTile - 1) /
+                           (kv_chunk / sage::kKTile));
+  if (units / 4 + 1 > 0x7fffffffLL) return SAGE_ERR_UNSUPPORTED;
+  SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O); SAGE_PTR(workspace);
+  if (workspace_bytes < sage::decode_workspace(B, Hq, Hkv, Nq, Nkv, d, kv_chunk)) return SAGE_ERR_WORKSPACE;
+  sage::DecodeArgs a;
+  a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
+  a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.blk_k = blk_k;
+  a.causal = causal; a.kv_chunk = kv_chunk; a.s2 = sm_scale * sage::kLog2e; a.workspace = workspace;
+  (void)hipGetLastError();
+  sage::launch_attn_decode(a, (hipStream_t)stream);
+  return launch_status();
+}
+
 int sage_attn_fwd_ex(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                      const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
                      int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale, void* stream) {

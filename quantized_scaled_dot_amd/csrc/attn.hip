@@ -55,53 +55,6 @@ struct AttnK {
   uint8_t* p_dump;
 };
 
-// LDS row of key kappa (0..63) of a KV tile: 32*h + m with m the MFMA row
-// m = 8*(v/4) + 4*g + v%4 for kappa = 32*g + 16*h + v.  k_lds_key inverts it.
-__device__ __forceinline__ int k_lds_key(int rho) {
-  const int h = rho >> 5, m = rho & 31;
-  const int g = (m >> 2) & 1, v = 4 * (m >> 3) + (m & 3);
-  return 32 * g + 16 * h + v;
-}
-// LDS rows are padded by 16 bytes (K: d+16, V: 64+16).  The matrix-core
-// operand reads (ds_read_b128) touch the same 16-byte chunk of 8 or 16
-// consecutive rows; with these strides those rows fall on distinct banks
-// whether the LDS serves 8 lanes (128 bytes) or 16 lanes (256 bytes) per
-// cycle, and every read of a wave shares one base address plus an immediate
-// offset.
-template <int D> constexpr int kRowK = D + 16;
-constexpr int kRowV = kKTile + 16;
-
-template <int OUT>
-__device__ __forceinline__ void store4(void* O, size_t idx, v4f v) {
-  if (OUT == 2) {
-    *(v4f*)((float*)O + idx) = v;
-  } else if (OUT == 1) {
-    unsigned u[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) u[e] = bf16_bits_rne(v[e]);
-    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
-    *(v2i*)((uint16_t*)O + idx) = w;
-  } else {
-    unsigned u[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) u[e] = f16_bits_rne(v[e]);
-    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
-    *(v2i*)((uint16_t*)O + idx) = w;
-  }
-}
-
-// Buffer resource for raw 16-byte loads of one head's codes (out-of-range
-// offsets read zero; every offset used here is in range).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l writes
-// lds + 16 l (the LDS address must be the same for the whole wave).
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
-
 // RAGGED: Nq or Nkv is not a multiple of 128 (masked partial last KV tile,
 // unstored padding rows, 1 to 4 masked steps at the end; at d = 64 it runs 2
 // workgroups per CU, where the 3 of the other d = 64 kernels would spill).

@@ -49,10 +49,29 @@ struct AttnArgs {
   uint8_t* p_dump;
 };
 
-void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st);
+// Decode over a quantized KV cache: split-KV chunks of kv_chunk keys, merged.
+struct DecodeArgs {
+  const int8_t* q_codes;
+  const float* q_scale;
+  const int8_t* k_codes;
+  const float* k_scale;
+  const uint8_t* v_codes;
+  const float* v_scale;
+  void* O;
+  int out_dtype, nhd;
+  int B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal, kv_chunk;
+  float s2;
+  void* workspace;   // decode_workspace(...) bytes of partial chunk states
+};
+
+// with_q / with_k: quantize Q (blocks), K (mean, smoothed blocks), or both
+void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st, bool with_q = true, bool with_k = true);
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st);
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st);
 size_t quantize_qk_workspace(int BHkv, int Nkv, int d);
 size_t quantize_v_workspace(int BH, int N, int d);
+void launch_attn_decode(const DecodeArgs& a, hipStream_t st);
+int decode_default_chunk(int B, int Hq, int Hkv, int Nq, int Nkv);
+size_t decode_workspace(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int kv_chunk);
 
 }  // namespace sage

@@ -331,9 +331,9 @@ static inline int round_up(int n, int m) { return (n + m - 1) / m * m; }
 
 template <int D, int BLKQ>
 static int launch_qk_pass1(const QuantQKArgs& a, InRows qin, InRows kin, int nchunk, long long* partial,
-                           hipStream_t st) {
-  const int nq = a.B * a.Hq * (qin.P / BLKQ) / blocks_per_wg<D, BLKQ>();
-  const int grid1 = nq + a.B * a.Hkv * nchunk;
+                           bool with_q, bool with_k, hipStream_t st) {
+  const int nq = with_q ? a.B * a.Hq * (qin.P / BLKQ) / blocks_per_wg<D, BLKQ>() : 0;
+  const int grid1 = nq + (with_k ? a.B * a.Hkv * nchunk : 0);
   hipLaunchKernelGGL((qk_pass1_kernel<D, BLKQ>), dim3(grid1), dim3(256), 0, st, (const uint16_t*)a.Q,
                      (const uint16_t*)a.K, a.is_bf16, qin, kin, nq, nchunk, a.q_codes, a.q_scale, partial);
   return nq;
@@ -347,14 +347,15 @@ static void launch_k_quant(const QuantQKArgs& a, InRows kin, hipStream_t st) {
 }
 
 template <int D>
-static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
+static void launch_qk_d(const QuantQKArgs& a, hipStream_t st, bool with_q, bool with_k) {
   const int BHkv = a.B * a.Hkv;
   const int nchunk = stat_chunks(a.Nkv);
   long long* partial = (long long*)a.workspace;
   const InRows qin{a.Hq, a.Nq, round_up(a.Nq, kQTile), a.nhd}, kin{a.Hkv, a.Nkv, round_up(a.Nkv, kKTile), a.nhd};
-  if (a.blk_q == 128) launch_qk_pass1<D, 128>(a, qin, kin, nchunk, partial, st);
-  else if (a.blk_q == 64) launch_qk_pass1<D, 64>(a, qin, kin, nchunk, partial, st);
-  else launch_qk_pass1<D, 32>(a, qin, kin, nchunk, partial, st);
+  if (a.blk_q == 128) launch_qk_pass1<D, 128>(a, qin, kin, nchunk, partial, with_q, with_k, st);
+  else if (a.blk_q == 64) launch_qk_pass1<D, 64>(a, qin, kin, nchunk, partial, with_q, with_k, st);
+  else launch_qk_pass1<D, 32>(a, qin, kin, nchunk, partial, with_q, with_k, st);
+  if (!with_k) return;
   hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
                      D, a.k_mean);
   if (a.blk_k == 64) launch_k_quant<D, 64>(a, kin, st);
@@ -362,9 +363,9 @@ static void launch_qk_d(const QuantQKArgs& a, hipStream_t st) {
   else launch_k_quant<D, 16>(a, kin, st);
 }
 
-void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st) {
-  if (a.d == 128) launch_qk_d<128>(a, st);
-  else launch_qk_d<64>(a, st);
+void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st, bool with_q, bool with_k) {
+  if (a.d == 128) launch_qk_d<128>(a, st, with_q, with_k);
+  else launch_qk_d<64>(a, st, with_q, with_k);
 }
 
 template <int D>

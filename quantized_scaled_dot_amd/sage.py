@@ -23,7 +23,8 @@ SAGE_LAYOUT_BHND, SAGE_LAYOUT_BNHD = 0, 1
 #: exported symbols, in header order
 SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_bytes", "sage_quantize_qk",
            "sage_quantize_qk_ex", "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_quantize_v_ex",
-           "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump")
+           "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
+           "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -53,6 +54,16 @@ _lib.sage_attn_fwd_ex.restype = _I
 _lib.sage_attn_fwd_ex.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P]
 _lib.sage_attn_fwd_dump.restype = _I
 _lib.sage_attn_fwd_dump.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _P]
+_lib.sage_quantize_q.restype = _I
+_lib.sage_quantize_q.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]
+_lib.sage_quantize_k.restype = _I
+_lib.sage_quantize_k.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.sage_decode_kv_chunk.restype = _I
+_lib.sage_decode_kv_chunk.argtypes = [_I] * 6
+_lib.sage_attn_decode_workspace_bytes.restype = _SZ
+_lib.sage_attn_decode_workspace_bytes.argtypes = [_I] * 7
+_lib.sage_attn_decode.restype = _I
+_lib.sage_attn_decode.argtypes = [_P] * 7 + [_I] * 11 + [_F, _I, _P, _SZ, _P]
 _lib.sage_attn_fwd_ex_dump.restype = _I
 _lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
 
@@ -129,6 +140,31 @@ def sage_attn_fwd_ex_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, 
     return _lib.sage_attn_fwd_ex_dump(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B,
                                       Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, sel, n_sel, s_dump, p_dump,
                                       stream)
+
+
+def sage_quantize_q(Q, in_dtype, layout, B, Hq, Nq, d, blk_q, q_codes, q_scale, stream):
+    return _lib.sage_quantize_q(Q, in_dtype, layout, B, Hq, Nq, d, blk_q, q_codes, q_scale, stream)
+
+
+def sage_quantize_k(K, in_dtype, layout, B, Hkv, Nkv, d, blk_k, k_codes, k_scale, k_mean, workspace, workspace_bytes,
+                    stream):
+    return _lib.sage_quantize_k(K, in_dtype, layout, B, Hkv, Nkv, d, blk_k, k_codes, k_scale, k_mean, workspace,
+                                workspace_bytes, stream)
+
+
+def sage_decode_kv_chunk(B, Hq, Hkv, Nq, Nkv, d):
+    return _lib.sage_decode_kv_chunk(B, Hq, Hkv, Nq, Nkv, d)
+
+
+def sage_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, kv_chunk):
+    return _lib.sage_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, kv_chunk)
+
+
+def sage_attn_decode(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, blk_q, blk_k, causal, sm_scale, kv_chunk, workspace, workspace_bytes, stream):
+    return _lib.sage_attn_decode(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq,
+                                 Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, workspace,
+                                 workspace_bytes, stream)
 
 
 # ---------------------------------------------------------------- tensor helpers
@@ -259,6 +295,66 @@ def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=No
         sel, s_dump, p_dump = dump
         fn = sage_attn_fwd_dump if plain else sage_attn_fwd_ex_dump
         _check(fn(*ops, *shape, *tail, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
+    return out
+
+
+def quantize_q(Q, blk_q=128, layout="bhnd", stream=None):
+    """INT8 blocks of Q alone (the queries of a decode step).  Returns a dict
+    with q_codes (padded to a multiple of 128 rows), q_scale, blk_q and Nq."""
+    B, Hq, Nq, d = _bhnd(Q, layout)
+    dev = Q.device
+    Nqp = _round_up(Nq, 128)
+    out = dict(q_codes=torch.empty((B, Hq, Nqp, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, Hq, Nqp // blk_q), dtype=torch.float32, device=dev))
+    _check(sage_quantize_q(_ptr(Q), _DT.get(Q.dtype, -1), _layout(layout), B, Hq, Nq, d, blk_q, _ptr(out["q_codes"]),
+                           _ptr(out["q_scale"]), _stream(stream)))
+    out.update(blk_q=blk_q, Nq=Nq)
+    return out
+
+
+def quantize_k(K, blk_k=64, layout="bhnd", workspace=None, stream=None):
+    """K mean and smoothed INT8 blocks of K alone (a K cache).  Returns a dict
+    with k_codes (padded to a multiple of 64 rows), k_scale, k_mean, blk_k and Nkv."""
+    B, Hkv, Nkv, d = _bhnd(K, layout)
+    dev = K.device
+    Nkt = _round_up(Nkv, sage_kv_tile())
+    out = dict(k_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, Hkv, Nkt // blk_k), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
+    wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(sage_quantize_k(_ptr(K), _DT.get(K.dtype, -1), _layout(layout), B, Hkv, Nkv, d, blk_k,
+                           _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    out.update(blk_k=blk_k, Nkv=Nkv)
+    return out
+
+
+def attn_decode(q, kc, v, causal=True, sm_scale=None, out_dtype=torch.float32, out=None, layout="bhnd",
+                kv_chunk=0, workspace=None, stream=None):
+    """Split-KV attention of quantized queries ``q`` (from quantize_q) against a
+    quantized cache: ``kc`` from quantize_k (or quantize_qk), ``v`` = (v_codes,
+    v_scale) from quantize_v.  kv_chunk 0 = the library's default split."""
+    B, Hq, _, d = q["q_codes"].shape
+    Hkv = kc["k_codes"].shape[1]
+    Nq, Nkv = q["Nq"], kc["Nkv"]
+    v_codes, v_scale = v
+    if sm_scale is None:
+        sm_scale = default_sm_scale(d)
+    if kv_chunk == 0:
+        kv_chunk = sage_decode_kv_chunk(B, Hq, Hkv, Nq, Nkv, d)
+    dev = q["q_codes"].device
+    if out is None:
+        shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    wsb = sage_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, kv_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(sage_attn_decode(_ptr(q["q_codes"]), _ptr(q["q_scale"]), _ptr(kc["k_codes"]), _ptr(kc["k_scale"]),
+                            _ptr(v_codes), _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), _layout(layout), B, Hq,
+                            Hkv, Nq, Nkv, d, q["blk_q"], kc["blk_k"], int(bool(causal)), float(sm_scale), kv_chunk,
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -14,7 +14,8 @@ are [B, Hkv, Nkv, d], which is Q's shape unless the workload sets grouped K/V
 heads (Hkv < H) or a different key count (then the queries are the last N
 positions of the Nkv-long sequence).  Shapes follow the workloads the method
 is aimed at: LLM prefill (also with grouped K/V heads and with a query chunk
-against a longer prefix), ViT, video DiT and long-context prefill.
+against a longer prefix), ViT, video DiT, long-context prefill, and decode
+(one or four new queries per sequence against a long quantized cache).
 """
 from dataclasses import dataclass, field
 import math
@@ -41,6 +42,7 @@ class Workload:
     seed: int = 0
     Hkv_: int = 0         # K/V heads (0: H)
     Nkv_: int = 0         # keys (0: N)
+    decode: bool = False  # N new queries against a quantized cache of Nkv keys (split over the keys)
 
     @property
     def Hkv(self):
@@ -93,6 +95,12 @@ WORKLOADS = {
     # finer quantization granularity: a Q scale per 32 rows, a K scale per 16 keys
     "llm-prefill-4k-causal-fine": Workload("llm-prefill-4k-causal-fine", 4, 32, 4096, 128, "bfloat16", True, 32, 16,
                                            4.0, _rsqrt32(128)),
+    # decode: one new query per sequence (32 query heads on 8 K/V heads) against a
+    # 32768-token quantized cache, batch 16; and 4 speculative queries against 131072
+    "decode-32k-gqa": Workload("decode-32k-gqa", 16, 32, 1, 128, "bfloat16", True, 128, 64, 4.0, _rsqrt32(128),
+                               Hkv_=8, Nkv_=32768, decode=True),
+    "decode-128k-gqa-4q": Workload("decode-128k-gqa-4q", 4, 32, 4, 128, "bfloat16", True, 128, 64, 4.0,
+                                   _rsqrt32(128), Hkv_=8, Nkv_=131072, decode=True),
     # lengths that are not tile multiples: 3000 queries at the end of 3500 keys
     "llm-prefill-ragged-3000-of-3500-gqa-causal": Workload("llm-prefill-ragged-3000-of-3500-gqa-causal", 2, 32,
                                                            3000, 128, "bfloat16", True, 128, 64, 4.0,

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 12 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 17 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -179,3 +179,44 @@ def test_python_helpers_validate_shapes():
         sage.quantize_qk(torch.zeros(2, 2), torch.zeros(2, 2))
     with pytest.raises(ValueError):
         sage.quantize_v(torch.zeros(1, 2, 128, 64), layout="nhd")
+
+
+def _dec(**kw):
+    args = dict(q_codes=A, q_scale=A, k_codes=A, k_scale=A, v_codes=A, v_scale=A, O=A, out_dtype=2, layout=0, B=2,
+                Hq=8, Hkv=2, Nq=1, Nkv=1000, d=128, blk_q=128, blk_k=64, causal=1, sm_scale=0.125, kv_chunk=128,
+                workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return sage.sage_attn_decode(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_chunk=96), sage.SAGE_ERR_INVALID_ARG), (dict(kv_chunk=-64), sage.SAGE_ERR_INVALID_ARG),
+    (dict(kv_chunk=32), sage.SAGE_ERR_INVALID_ARG), (dict(Hq=7), sage.SAGE_ERR_INVALID_ARG),
+    (dict(Nq=1001), sage.SAGE_ERR_INVALID_ARG), (dict(blk_k=128), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(workspace=None), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=1024), sage.SAGE_ERR_WORKSPACE),
+    (dict(O=A + 4), sage.SAGE_ERR_MISALIGNED), (dict(out_dtype=5), sage.SAGE_ERR_INVALID_ARG),
+    (dict(sm_scale=0.0), sage.SAGE_ERR_INVALID_ARG), (dict(d=96), sage.SAGE_ERR_UNSUPPORTED),
+])
+def test_attn_decode_rejects(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_decode_split_and_workspace_sizes():
+    # 2 batches x 2 K/V heads x 1 row group (4 query heads x 1 query) = 4 row groups:
+    # 256 splits would fit, the 16 tiles of 1000 keys allow 16, one tile each
+    assert sage.sage_decode_kv_chunk(2, 8, 2, 1, 1000, 128) == 64
+    # 16 x 8 x 1 = 128 row groups, 8 splits of the 512 tiles of 32768 keys (1024 waves)
+    assert sage.sage_decode_kv_chunk(16, 32, 8, 1, 32768, 128) == 64 * 64
+    units = 2 * 2 * 1 * 8   # 8 splits of 128 keys over ceil(1000/64) = 16 tiles
+    assert sage.sage_attn_decode_workspace_bytes(2, 8, 2, 1, 1000, 128, 128) == units * (32 * 128 + 64) * 4
+    assert sage.sage_attn_decode_workspace_bytes(2, 8, 2, 1, 1000, 128, 100) == 0
+    assert sage.sage_decode_kv_chunk(2, 6, 4, 1, 100, 128) == 0   # Hq not a multiple of Hkv
+
+
+def test_quantize_q_and_k_reject():
+    assert sage.sage_quantize_q(A, 1, 0, 1, 2, 5, 128, 48, A, A, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert sage.sage_quantize_q(None, 1, 0, 1, 2, 5, 128, 64, A, A, None) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_quantize_q(A, 1, 2, 1, 2, 5, 128, 64, A, A, None) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 16, A, A, A, A, 8, None) == sage.SAGE_ERR_WORKSPACE
+    assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 24, A, A, A, A, 1 << 20, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 16, A, A, None, A, 1 << 20, None) == sage.SAGE_ERR_INVALID_ARG

@@ -355,6 +355,21 @@ def _sample_rows(w, rng, n_rand=24):
 def test_full_size_workload(name):
     w = synth.WORKLOADS[name]
     Q, K, V = synth.make_inputs(w)
+    if w.decode:
+        # the split the library picks for this shape, on both sides
+        g = run_gpu_decode(w, Q, K, V, 0)
+        qk, vc, vs = run_oracle_quant(w, Q, K, V)
+        check_quant_bit_exact(g, qk, vc, vs)
+        rows = np.unique(np.concatenate([np.arange(8), w.B * w.H * w.N - 1 - np.arange(8),
+                                         np.random.default_rng(7).integers(0, w.B * w.H * w.N, 48)]))
+        O_ref = orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk=g["kv_chunk"],
+                                    rows=rows)
+        O = g["O"].reshape(-1, w.d)
+        assert np.abs(O[rows] - O_ref).max() <= O_TOL
+        ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale,
+                                 rows=rows)
+        assert cosine(O[rows], ex) >= 0.995
+        return
     nqt = -(-w.N // 128)
     tiles = (0, w.B * w.H * nqt - 1)
     g = run_gpu(w, Q, K, V, dump_tiles=tiles)
@@ -374,3 +389,106 @@ def test_full_size_workload(name):
     assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"
     ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
     assert cosine(O[rows], ex) >= 0.995
+
+
+# ------------------------------------------------------------------ decode (split-KV) over a quantized cache
+DECODE = {
+    # name: (workload overrides, kv_chunk, layout)
+    "gqa4-one-query-ragged-1000": (dict(base="llm-prefill-4k-causal", B=2, H=8, Hkv_=2, N=1, Nkv_=1000), 128, "bhnd"),
+    "gqa8-four-queries-noncausal": (dict(base="video-dit-32k", B=1, H=16, Hkv_=2, N=4, Nkv_=4096), 256, "bhnd"),
+    "gqa2-two-row-groups-fine-d64": (dict(base="vit-2k-f16", B=1, H=4, Hkv_=2, N=20, Nkv_=333, causal=True, blk_q=32,
+                                          blk_k=16), 64, "bnhd"),
+    "mha-tiny-cache-default-split": (dict(base="vit-2k-f16", B=3, H=4, N=1, Nkv_=70, causal=True), 0, "bhnd"),
+    "late-chunk-invisible-to-early-rows": (dict(base="llm-prefill-4k-causal", B=1, H=1, N=40, Nkv_=130), 64, "bhnd"),
+    "outliers-gqa-k32": (dict(base="long-prefill-128k-causal", H=8, Hkv_=2, N=2, Nkv_=3000, blk_k=32), 512, "bnhd"),
+}
+
+
+def decode_workload(name):
+    kw, chunk, layout = DECODE[name]
+    kw = dict(kw)
+    return synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw), chunk, layout
+
+
+def run_gpu_decode(w, Q, K, V, kv_chunk, layout="bhnd", out_dtype=torch.float32):
+    """Queries and cache quantized separately (quantize_q, quantize_k,
+    quantize_v), then the split-KV decode; res["O"] is [B,H,N,d]."""
+    sage = _sage()
+    dev = torch.device("cuda:0")
+    tok = layout == "bnhd"
+    Qd, Kd, Vd = ((t.transpose(1, 2) if tok else t).contiguous().to(dev) for t in (Q, K, V))
+    q = sage.quantize_q(Qd, w.blk_q, layout=layout)
+    kc = sage.quantize_k(Kd, w.blk_k, layout=layout)
+    vq = sage.quantize_v(Vd, layout=layout)
+    if kv_chunk == 0:
+        kv_chunk = sage.sage_decode_kv_chunk(w.B, w.H, w.Hkv, w.N, w.Nkv, w.d)
+    O = sage.attn_decode(q, kc, vq, causal=w.causal, sm_scale=w.sm_scale, out_dtype=out_dtype, layout=layout,
+                         kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in list(q.items()) + list(kc.items()) if torch.is_tensor(v)}
+    res["v_codes"] = sage.v_codes_to_natural(vq[0]).cpu().numpy()
+    res["v_scale"] = vq[1].cpu().numpy()
+    res["O"] = (O.transpose(1, 2) if tok else O).float().cpu().numpy()
+    res["kv_chunk"] = kv_chunk
+    res["dev"] = (q, kc, vq)
+    return res
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_against_the_split_oracle(name):
+    w, chunk, layout = decode_workload(name)
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu_decode(w, Q, K, V, chunk, layout)
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    O_ref = orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk=g["kv_chunk"])
+    O = g["O"].reshape(-1, w.d)
+    err = np.abs(O - O_ref)
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {np.unravel_index(err.argmax(), err.shape)}"
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
+    assert cosine(O, ex) >= 0.995
+
+
+@pytest.mark.parametrize("name", ["gqa4-one-query-ragged-1000", "gqa2-two-row-groups-fine-d64"])
+def test_decode_with_one_split_is_the_attention_kernel(name):
+    """kv_chunk covering the whole cache: per row the decode wave computes what
+    the attention kernel computes (same tiles, same order), and the merge of one
+    split is exact, so O agrees bit for bit."""
+    sage = _sage()
+    w, _, layout = decode_workload(name)
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu_decode(w, Q, K, V, -(-w.Nkv // 64) * 64, layout)
+    q, kc, vq = g["dev"]
+    qk = dict(q_codes=q["q_codes"], q_scale=q["q_scale"], k_codes=kc["k_codes"], k_scale=kc["k_scale"],
+              blk_q=w.blk_q, blk_k=w.blk_k, Nq=w.N, Nkv=w.Nkv)
+    O = sage.attn_fwd(qk, vq, causal=w.causal, sm_scale=w.sm_scale, layout=layout)
+    torch.cuda.synchronize()
+    O = (O.transpose(1, 2) if layout == "bnhd" else O).cpu().numpy()
+    assert np.array_equal(O.view(np.uint32), g["O"].view(np.uint32))
+
+
+def test_separate_quantize_calls_equal_the_fused_one():
+    sage = _sage()
+    w = small_ex_workload("chunk256-of-1024-causal-blkq64")
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd = Q.cuda(), K.cuda()
+    both = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k)
+    q = sage.quantize_q(Qd, w.blk_q)
+    kc = sage.quantize_k(Kd, w.blk_k)
+    torch.cuda.synchronize()
+    for key in ("q_codes", "q_scale"):
+        assert torch.equal(both[key], q[key]), key
+    for key in ("k_codes", "k_scale", "k_mean"):
+        assert torch.equal(both[key], kc[key]), key
+
+
+def test_decode_output_dtypes_round_the_fp32_result():
+    w, chunk, layout = decode_workload("gqa8-four-queries-noncausal")
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu_decode(w, Q, K, V, chunk, layout)
+    sage = _sage()
+    q, kc, vq = g["dev"]
+    for dt in (torch.bfloat16, torch.float16):
+        o = sage.attn_decode(q, kc, vq, causal=w.causal, sm_scale=w.sm_scale, out_dtype=dt, kv_chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o.cpu().view(torch.int16), torch.from_numpy(g["O"]).to(dt).view(torch.int16))
