@@ -57,6 +57,17 @@ def lib():
         L.oracle_quantize_v.argtypes = [P, i32, i32, i32, i32, P, P]
         L.oracle_qk_int32.restype = None
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i32, P]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_encode_n.argtypes = [P, P, i64]
+        L.oracle_quantize_q4.restype = i32
+        L.oracle_quantize_q4.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.oracle_quantize_k4.restype = i32
+        L.oracle_quantize_k4.argtypes = [P, i32, i32, i32, i32, P, P, P]
+        L.oracle_attn_rows_qk4.restype = i32
+        L.oracle_attn_rows_qk4.argtypes = [P, P, P, P, P, P] + [i32] * 8 + [f32, P, i32, P, P]
+        L.oracle_qk4_scores.restype = i32
+        L.oracle_qk4_scores.argtypes = [P, P, P, P] + [i32] * 6 + [P, i32, P]
         L.oracle_attn_rows_split.restype = i32
         L.oracle_attn_rows_split.argtypes = [P, P, P, P, P, P] + [i32] * 11 + [f32, P, i32, P]
         L.oracle_attn_rows.restype = i32
@@ -219,6 +230,70 @@ def attn_rows_split(qk, v_codes, v_scale, blk_q, blk_k, causal, sm_scale, kv_chu
     if rc != 0:
         raise ValueError("oracle_attn_rows_split: unsupported arguments")
     return out
+
+
+# ---------------------------------------------------------------- 4-bit QK^T variant
+def e2m1_decode(codes):
+    codes = np.asarray(codes, np.uint8)
+    tab = np.array([lib().oracle_e2m1_decode(c) for c in range(16)])
+    return tab[codes]
+
+
+def e2m1_encode(x):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e2m1_encode_n(_p(x), _p(out), x.size)
+    return out
+
+
+def quantize_qk4(Q_bits, K_bits, dtype):
+    """E2M1 blocks of 32 channels of Q [B,Hq,Nq,d] and of the smoothed K
+    [B,Hkv,Nkv,d]: codes (one per value, 0..15) and E8M0 scale bytes per block."""
+    Q_bits = _c(Q_bits, np.uint16)
+    K_bits = _c(K_bits, np.uint16)
+    B, Hq, Nq, d = Q_bits.shape
+    _, Hkv, Nkv, _ = K_bits.shape
+    qc = np.empty((B, Hq, Nq, d), np.uint8)
+    qs = np.empty((B, Hq, Nq, d // 32), np.uint8)
+    kc = np.empty((B, Hkv, Nkv, d), np.uint8)
+    ks = np.empty((B, Hkv, Nkv, d // 32), np.uint8)
+    mu = np.empty((B, Hkv, d), np.float32)
+    rc = lib().oracle_quantize_q4(_p(Q_bits), dtype, B * Hq, Nq, d, _p(qc), _p(qs))
+    rc |= lib().oracle_quantize_k4(_p(K_bits), dtype, B * Hkv, Nkv, d, _p(kc), _p(ks), _p(mu))
+    if rc != 0:
+        raise ValueError("oracle quantize_qk4: unsupported shape")
+    return dict(q4_codes=qc, q4_scale=qs, k4_codes=kc, k4_scale=ks, k_mean=mu)
+
+
+def qk4_scores(qk4, rows):
+    qc, qs, kc, ks = (_c(qk4[k], np.uint8) for k in ("q4_codes", "q4_scale", "k4_codes", "k4_scale"))
+    B, Hq, Nq, d = qc.shape
+    _, Hkv, Nkv, _ = kc.shape
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, Nkv), np.float32)
+    if lib().oracle_qk4_scores(_p(qc), _p(qs), _p(kc), _p(ks), B, Hq, Hkv, Nq, Nkv, d, _p(rows), rows.size,
+                               _p(out)) != 0:
+        raise ValueError("oracle qk4_scores: unsupported arguments")
+    return out
+
+
+def attn_rows_qk4(qk4, v_codes, v_scale, causal, sm_scale, rows=None, kv_tile=KV_TILE, want_p=False):
+    """Oracle attention with 4-bit QK^T for flat query rows bh*Nq + i."""
+    qc, qs, kc, ks = (_c(qk4[k], np.uint8) for k in ("q4_codes", "q4_scale", "k4_codes", "k4_scale"))
+    vc = _c(v_codes, np.uint8)
+    vs = _c(v_scale, np.float32)
+    B, Hq, Nq, d = qc.shape
+    _, Hkv, Nkv, _ = kc.shape
+    if rows is None:
+        rows = np.arange(B * Hq * Nq, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, d), np.float32)
+    p = np.empty((rows.size, Nkv), np.uint8) if want_p else None
+    rc = lib().oracle_attn_rows_qk4(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B, Hq, Hkv, Nq, Nkv, d, kv_tile,
+                                    int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows_qk4: unsupported arguments")
+    return (out, p) if want_p else out
 
 
 def run(Q_bits, K_bits, V_bits, dtype, blk_q, blk_k, causal, sm_scale, rows=None, kv_tile=KV_TILE,

@@ -122,6 +122,55 @@ void oracle_exp2f_n(const float* t, float* out, int64_t n) {
 /* shift vector leaves softmax(QK^T) unchanged; the fixed-point sum makes     */
 /* the vector independent of summation order.                                */
 /* ------------------------------------------------------------------------ */
+/* FP4 (E2M1) and its microscaled blocks, for the 4-bit QK^T variant (the   */
+/* SageAttention3 abstract: attention on FP4 tensor cores; here the FP4     */
+/* matrix instruction of the target takes E2M1 values with one power-of-two */
+/* scale per 32 values along the contraction).                              */
+/* E2M1 magnitudes by code 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the    */
+/* sign.  Encoding rounds to the nearest magnitude, ties to the code with    */
+/* an even last bit, and saturates at 6.                                     */
+/* ------------------------------------------------------------------------ */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_decode(uint8_t c) {
+  const double m = E2M1_MAG[c & 7];
+  return (c & 8) ? -m : m;
+}
+
+uint8_t oracle_e2m1_encode(float x) {
+  const double a = fabs((double)x);
+  int best = 0;
+  for (int k = 1; k < 8; k++) {
+    const double dk = fabs(a - E2M1_MAG[k]), db = fabs(a - E2M1_MAG[best]);
+    if (dk < db || (dk == db && (k & 1) == 0)) best = k;
+  }
+  return (uint8_t)(best | (signbit(x) ? 8 : 0));
+}
+
+/* One block of n values (n <= 32): shared exponent E = floor(log2(max|x|)) - 2
+ * (2 = the largest E2M1 exponent), clamped to [-127, 127]; codes =
+ * E2M1(x / 2^E); stored scale = E + 127 (an E8M0 byte).  An all-zero block
+ * gets scale byte 0 and zero codes. */
+static void quant_block_mx4(const float* x, int n, uint8_t* codes, uint8_t* scale) {
+  float a = 0.0f;
+  for (int k = 0; k < n; k++) a = fmaxf(a, fabsf(x[k]));
+  if (a == 0.0f) {
+    *scale = 0;
+    for (int k = 0; k < n; k++) codes[k] = 0;
+    return;
+  }
+  int e = (int)floor(log2((double)a)) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  *scale = (uint8_t)(e + 127);
+  for (int k = 0; k < n; k++) codes[k] = oracle_e2m1_encode((float)ldexp((double)x[k], -e));
+}
+
+void oracle_e2m1_encode_n(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_e2m1_encode(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 static const double KMEAN_CLAMP = 1048576.0;  /* 2^20 */
 
 static void kmean_head(const uint16_t* K, int dtype, int N, int d, float* mu, int64_t* sums_out) {
@@ -239,6 +288,43 @@ int oracle_kmean(const uint16_t* K, int dtype, int BH, int N, int d, float* mu, 
 /*   a_c = max_t |v[t,c]| (a_c < 2^-120: channel is zero),                   */
 /*   delta_c = RN(a_c / 448), r_c = RN(448 / a_c), code = E(RN(v * r_c)).    */
 /* Output codes in natural layout [BH, N, d].                                */
+/* 4-bit Q and K: every token row of d channels in blocks of 32 channels,    */
+/* each block its own shared exponent (quant_block_mx4).  K is smoothed     */
+/* first, exactly as for the INT8 path (same mean, fp32 subtraction).        */
+/* Codes: one E2M1 code per value [BH, N, d]; scales [BH, N, d/32] (E8M0).   */
+int oracle_quantize_q4(const uint16_t* Q, int dtype, int BH, int N, int d, uint8_t* q4_codes, uint8_t* q4_scale) {
+  if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    float buf[32];
+    for (int n = 0; n < N; n++)
+      for (int b = 0; b < d / 32; b++) {
+        const size_t r = ((size_t)bh * N + n);
+        for (int k = 0; k < 32; k++) buf[k] = load_in(Q, r * d + 32 * b + k, dtype);
+        quant_block_mx4(buf, 32, q4_codes + r * d + 32 * b, q4_scale + r * (d / 32) + b);
+      }
+  }
+  return 0;
+}
+
+int oracle_quantize_k4(const uint16_t* K, int dtype, int BH, int N, int d, uint8_t* k4_codes, uint8_t* k4_scale,
+                       float* k_mean) {
+  if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    float* mu = k_mean + (size_t)bh * d;
+    kmean_head(K + (size_t)bh * N * d, dtype, N, d, mu, NULL);
+    float buf[32];
+    for (int n = 0; n < N; n++)
+      for (int b = 0; b < d / 32; b++) {
+        const size_t r = ((size_t)bh * N + n);
+        for (int k = 0; k < 32; k++) buf[k] = load_in(K, r * d + 32 * b + k, dtype) - mu[32 * b + k];
+        quant_block_mx4(buf, 32, k4_codes + r * d + 32 * b, k4_scale + r * (d / 32) + b);
+      }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 int oracle_quantize_v(const uint16_t* V, int dtype, int BH, int N, int d, uint8_t* v_codes, float* v_scale) {
   if (BH < 1 || N < 1 || d < 1) return -1;
@@ -325,6 +411,12 @@ static const float LOG2E_F = 0x1.715476p+0f;   /* RN(log2 e) */
 typedef struct {
   const int8_t* q;        /* the row's d codes */
   float dq;               /* the row's Q scale */
+  /* 4-bit QK^T instead (q4 != NULL): the row's E2M1 codes and block scales,
+   * the head's K codes [Nkv, d] and scales [Nkv, d/32] */
+  const uint8_t* q4;
+  const uint8_t* q4s;
+  const uint8_t* k4;
+  const uint8_t* k4s;
   const int8_t* k;        /* the head's K codes [Nkv, d] */
   const float* ks;        /* the head's K scales [ceil(Nkv/blk_k)] */
   const uint8_t* v;       /* the head's V codes [Nkv, d] */
@@ -334,6 +426,22 @@ typedef struct {
   const double* vdec;     /* e4m3 decode table */
 } row_ctx;
 
+/* 4-bit score of the row against key j: the exact sum over the 32-channel   */
+/* blocks of 2^(Eq + Ek) times the block's E2M1 dot product (fp64, exact for */
+/* the exponent spreads that occur), rounded once to fp32.                  */
+static float score4(const row_ctx* x, int j) {
+  const int d = x->d;
+  const uint8_t* k = x->k4 + (size_t)j * d;
+  const uint8_t* ks = x->k4s + (size_t)j * (d / 32);
+  double s = 0.0;
+  for (int b = 0; b < d / 32; b++) {
+    double blk = 0.0;
+    for (int c = 32 * b; c < 32 * b + 32; c++) blk += oracle_e2m1_decode(x->q4[c]) * oracle_e2m1_decode(k[c]);
+    s += ldexp(blk, (int)x->q4s[b] + (int)ks[b] - 254);
+  }
+  return (float)s;
+}
+
 /* The online softmax over the tiles j0 = j_begin, j_begin + kv_tile, ...    */
 /* below j_end (j_begin a multiple of kv_tile), from a fresh state: returns  */
 /* the number of visited tiles and leaves m, l and Oacc[d] (Oacc without the */
@@ -342,7 +450,7 @@ typedef struct {
 static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, float* l_out, float* oacc,
                         uint8_t* prow) {
   const int kv_tile = x->kv_tile, d = x->d;
-  int32_t* S = (int32_t*)malloc(sizeof(int32_t) * kv_tile);
+  float* S = (float*)malloc(sizeof(float) * kv_tile);
   float* c2 = (float*)malloc(sizeof(float) * kv_tile);
   float* pt = (float*)malloc(sizeof(float) * kv_tile);
   uint8_t* ph = (uint8_t*)malloc(kv_tile);
@@ -354,16 +462,21 @@ static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, 
     if (j0 > x->last) break;   /* no visible key from here on */
     int nvis = j0 + kv_tile <= j_end ? kv_tile : j_end - j0;
     if (x->last - j0 + 1 < nvis) nvis = (int)(x->last - j0 + 1);
-    /* scores of the visible keys j0 .. j0+nvis-1 */
+    /* scores of the visible keys j0 .. j0+nvis-1, as fp32 S and its factor c2 */
     float mt = -INFINITY;
     for (int jj = 0; jj < nvis; jj++) {
       int j = j0 + jj;
-      const int8_t* k = x->k + (size_t)j * d;
-      int32_t s = 0;
-      for (int c = 0; c < d; c++) s += (int32_t)x->q[c] * (int32_t)k[c];
-      S[jj] = s;
-      c2[jj] = (x->dq * x->ks[j / x->blk_k]) * x->s2;
-      float u = (float)s * c2[jj];
+      if (x->q4) {
+        S[jj] = score4(x, j);
+        c2[jj] = x->s2;
+      } else {
+        const int8_t* k = x->k + (size_t)j * d;
+        int32_t s = 0;
+        for (int c = 0; c < d; c++) s += (int32_t)x->q[c] * (int32_t)k[c];
+        S[jj] = (float)s;   /* exact: |s| < 2^24 */
+        c2[jj] = (x->dq * x->ks[j / x->blk_k]) * x->s2;
+      }
+      float u = S[jj] * c2[jj];
       if (u > mt) mt = u;
     }
     const int first = visited == 0;
@@ -372,7 +485,7 @@ static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, 
     float mm = mnew - 8.0f;
     float rowsum = 0.0f;
     for (int jj = 0; jj < nvis; jj++) {
-      pt[jj] = oracle_exp2f(fmaf((float)S[jj], c2[jj], -mm));
+      pt[jj] = oracle_exp2f(fmaf(S[jj], c2[jj], -mm));
       rowsum += pt[jj];
       ph[jj] = oracle_e4m3_encode(pt[jj]);
       if (prow) prow[j0 + jj] = ph[jj];
@@ -417,6 +530,7 @@ static void row_setup(row_ctx* x, const int8_t* q_codes, const float* q_scale, c
   x->last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
   x->s2 = sm_scale * LOG2E_F;
   x->vdec = vdec;
+  x->q4 = x->q4s = x->k4 = x->k4s = NULL;
   *bk_out = bk;
 }
 
@@ -443,6 +557,68 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
     for (int c = 0; c < d; c++)
       out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
     free(oacc);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The same attention with 4-bit QK^T: scores from the E2M1 codes and block  */
+/* scales of oracle_quantize_q4 / _k4 (score4), dequantization factor        */
+/* c2 = s2 for every key (the block scales are inside the score); softmax,   */
+/* FP8 P~ and the two-level P~V exactly as above.  Codes [B*H, N, d], scales */
+/* [B*H, N, d/32]; out [nrows, d]; p_codes (optional) as above.              */
+/* ------------------------------------------------------------------------ */
+int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                         const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, int B, int Hq,
+                         int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
+                         const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+  if (!attn_args_ok(B, Hq, Hkv, Nq, Nkv, d, 1, 1, kv_tile, causal, sm_scale) || d % 32) return -1;
+  double vdec[256];
+  for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
+  for (int r = 0; r < nrows; r++)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * Hq * Nq) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int r = 0; r < nrows; r++) {
+    const int64_t bh = rows[r] / Nq, i = rows[r] % Nq, bk = kv_head(bh, Hq, Hkv);
+    row_ctx x;
+    memset(&x, 0, sizeof x);
+    x.q4 = q4_codes + ((size_t)bh * Nq + i) * d;
+    x.q4s = q4_scale + ((size_t)bh * Nq + i) * (d / 32);
+    x.k4 = k4_codes + (size_t)bk * Nkv * d;
+    x.k4s = k4_scale + (size_t)bk * Nkv * (d / 32);
+    x.v = v_codes + (size_t)bk * Nkv * d;
+    x.Nkv = Nkv; x.d = d; x.blk_k = 1; x.kv_tile = kv_tile;
+    x.last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
+    x.s2 = sm_scale * LOG2E_F;
+    x.vdec = vdec;
+    float* oacc = (float*)malloc(sizeof(float) * d);
+    float m, l;
+    uint8_t* prow = p_codes ? p_codes + (size_t)r * Nkv : NULL;
+    if (prow) memset(prow, 0, Nkv);
+    attend_range(&x, 0, Nkv, &m, &l, oacc, prow);
+    for (int c = 0; c < d; c++)
+      out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
+    free(oacc);
+  }
+  return 0;
+}
+
+/* fp32 4-bit scores (score4) of flat query rows bh*Nq + i against every key: [nrows, Nkv] */
+int oracle_qk4_scores(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                      const uint8_t* k4_scale, int B, int Hq, int Hkv, int Nq, int Nkv, int d, const int64_t* rows,
+                      int nrows, float* out) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d % 32) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int r = 0; r < nrows; r++) {
+    const int64_t bh = rows[r] / Nq, i = rows[r] % Nq, bk = kv_head(bh, Hq, Hkv);
+    row_ctx x;
+    memset(&x, 0, sizeof x);
+    x.q4 = q4_codes + ((size_t)bh * Nq + i) * d;
+    x.q4s = q4_scale + ((size_t)bh * Nq + i) * (d / 32);
+    x.k4 = k4_codes + (size_t)bk * Nkv * d;
+    x.k4s = k4_scale + (size_t)bk * Nkv * (d / 32);
+    x.d = d;
+    for (int j = 0; j < Nkv; j++) out[(size_t)r * Nkv + j] = score4(&x, j);
   }
   return 0;
 }

@@ -626,3 +626,118 @@ def test_split_rejects_chunks_that_are_not_tile_multiples():
     for chunk in (0, 32, 100):
         with pytest.raises(ValueError):
             orc.attn_rows_split(qk, vc, vs, 64, 64, True, 0.125, kv_chunk=chunk)
+
+
+# ------------------------------------------------------------------ 4-bit QK^T (E2M1 with 32-value power-of-two blocks)
+def _e2m1_from_bits(c):
+    """E2M1 from its bit fields: sign s, exponent e (2 bits, bias 1), mantissa m (1 bit)."""
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+    return -mag if s else mag
+
+
+def test_e2m1_decode_is_the_bit_field_definition():
+    got = orc.e2m1_decode(np.arange(16))
+    assert [float(g) for g in got] == [_e2m1_from_bits(c) for c in range(16)]
+
+
+def test_e2m1_encode_is_nearest_with_ties_to_even():
+    rng = np.random.default_rng(41)
+    mags = np.array([_e2m1_from_bits(c) for c in range(8)])
+    mids = (mags[1:] + mags[:-1]) / 2
+    x = np.concatenate([rng.uniform(-7, 7, 200000), mids, -mids, [0.0, -0.0, 6.0, 6.5, 100.0, -100.0]]).astype(np.float32)
+    got = orc.e2m1_encode(x)
+    for xi, ci in zip(x[-2000:].tolist() + mids.tolist(), list(got[-2000:]) + list(orc.e2m1_encode(mids))):
+        a = abs(xi)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]   # ties: even code
+        assert (ci & 7) == want, (xi, ci)
+    # all values: decoded code is a nearest magnitude, sign kept
+    dec = orc.e2m1_decode(got)
+    err = np.abs(np.abs(dec) - np.minimum(np.abs(x), 6.0))
+    nearest = np.min(np.abs(mags[None, :] - np.minimum(np.abs(x), 6.0)[:, None]), axis=1)
+    assert np.array_equal(err, nearest)
+    assert ((got >> 3) == np.signbit(x)).all()
+
+
+def _q4_case(seed=42, N=64, d=128, scale=1.0):
+    rng = np.random.default_rng(seed)
+    Q = (rng.standard_normal((1, 2, N, d)) * scale).astype(np.float32)
+    K = (rng.standard_normal((1, 2, N, d)) * scale + rng.standard_normal((1, 2, 1, d))).astype(np.float32)
+    return Q, K
+
+
+def test_mx4_blocks_properties():
+    Q, K = _q4_case()
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+    x = _f16_vals(Q).reshape(1, 2, 64, 4, 32).astype(np.float64)
+    c = r["q4_codes"].reshape(1, 2, 64, 4, 32)
+    sc = 2.0 ** (r["q4_scale"].astype(np.float64)[..., None] - 127)
+    amax = np.abs(x).max(-1, keepdims=True)
+    # the shared exponent puts the block max in [4, 8): its code is 4 or 6
+    assert ((amax / sc >= 4) & (amax / sc < 8)).all()
+    top = np.take_along_axis(c, np.abs(x).argmax(-1)[..., None], -1) & 7
+    assert np.isin(top, [6, 7]).all()
+    # round trip: within half the E2M1 spacing at each value's magnitude (1 above 4, 0.5 in [2,4), 0.25 below)
+    y = orc.e2m1_decode(c) * sc
+    t = np.minimum(np.abs(x) / sc, 6.0)
+    half = np.where(t >= 4, 1.0, np.where(t >= 2, 0.5, 0.25))
+    assert (np.abs(np.abs(y) / sc - t) <= half + 1e-12).all()
+    # scaling the input by 2^5 moves every scale byte by 5 and keeps the codes
+    r2 = orc.quantize_qk4(_f16_bits(Q * 32), _f16_bits(K), 0)
+    assert np.array_equal(r2["q4_codes"], r["q4_codes"]) and np.array_equal(r2["q4_scale"], r["q4_scale"] + 5)
+    # an all-zero block: scale byte 0, zero codes
+    Qz = Q.copy(); Qz[0, 0, 3, 32:64] = 0
+    r3 = orc.quantize_qk4(_f16_bits(Qz), _f16_bits(K), 0)
+    assert r3["q4_scale"][0, 0, 3, 1] == 0 and (r3["q4_codes"][0, 0, 3, 32:64] == 0).all()
+
+
+def test_k4_uses_the_same_smoothing_as_int8():
+    Q, K = _q4_case(seed=43)
+    r4 = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+    r8 = orc.quantize_qk(_f16_bits(Q), _f16_bits(K), 0, 64, 64)
+    assert np.array_equal(r4["k_mean"].view(np.uint32), r8["k_mean"].view(np.uint32))
+
+
+def test_qk4_scores_against_exact_python_arithmetic():
+    from fractions import Fraction
+    Q, K = _q4_case(seed=44, N=8, d=64)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+    rows = np.array([0, 5, 8 + 7], dtype=np.int64)   # (head 0, rows 0 and 5), (head 1, row 7)
+    got = orc.qk4_scores(r, rows)
+    dec = [Fraction(float(v)) for v in orc.e2m1_decode(np.arange(16))]
+    for k, row in enumerate(rows):
+        h, i = divmod(int(row), 8)
+        for j in range(8):
+            s = Fraction(0)
+            for b in range(2):
+                blk = sum(dec[r["q4_codes"][0, h, i, c]] * dec[r["k4_codes"][0, h, j, c]] for c in range(32 * b, 32 * b + 32))
+                s += blk * Fraction(2) ** (int(r["q4_scale"][0, h, i, b]) + int(r["k4_scale"][0, h, j, b]) - 254)
+            assert got[k, j] == np.float32(float(s)), (row, j)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_qk4_zero_q_gives_mean_of_dequantized_v(causal):
+    Q, K, V = _gqa_inputs(Hq=2, Hkv=1, Nq=128, Nkv=192, seed=45)
+    r = orc.quantize_qk4(_f16_bits(np.zeros_like(Q)), _f16_bits(K), 0)
+    vc, vs = orc.quantize_v(_f16_bits(V), 0)
+    O = orc.attn_rows_qk4(r, vc, vs, causal, 0.125)
+    deq = orc.e4m3_decode(vc) * vs[:, :, None, :].astype(np.float64)
+    for row in (0, 77, 128 + 5):
+        i = row % 128
+        last = i + 64 if causal else 191
+        assert np.allclose(O[row], deq[0, 0, :last + 1].mean(0), rtol=2e-6, atol=1e-6)
+
+
+def test_qk4_attention_against_fp64():
+    """4-bit scores lose about three bits against INT8: the bar is the accuracy
+    of E2M1 blocks (cosine >= 0.98 on these inputs), not that of the 8-bit path."""
+    for causal in (False, True):
+        Q, K, V = _gqa_inputs(B=1, Hq=4, Hkv=2, Nq=128, Nkv=320, seed=46)
+        r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+        vc, vs = orc.quantize_v(_f16_bits(V), 0)
+        O = orc.attn_rows_qk4(r, vc, vs, causal, 0.125)
+        ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125).reshape(O.shape)
+        a, b = O.astype(np.float64).ravel(), ex.ravel()
+        assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.98
