@@ -35,6 +35,9 @@ sys.path.insert(0, ROOT)
 from quantized_scaled_dot_amd import synth  # noqa: E402
 
 MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 = dense FP8 = 5.0 P op/s
+FP4_PEAK_TOPS = 10100.0          # MI355X dense FP4 (MXFP4) 10.1 P op/s
+# 4-bit QK^T: half the counted ops on FP4, half (P~V) on FP8 -> 1 / (0.5/10.1 + 0.5/5.0) P op/s
+QK4_PEAK_TOPS = 1.0 / (0.5 / FP4_PEAK_TOPS + 0.5 / MFMA_PEAK_TOPS)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "video-dit-32k"
 METRIC = "attention TOPS (4·B·H·N²·d/t) at 1 MI355X; % of INT8/FP8 MFMA peak"
@@ -80,20 +83,29 @@ def cpu_baseline(w, Q, K, V, budget_s=20.0):
 
     qb, kb, vb = synth.bits(Q), synth.bits(K), synth.bits(V)
     t0 = time.perf_counter()
-    qk = orc.quantize_qk(qb, kb, w.dtype_code, w.blk_q, w.blk_k)
+    if w.qk4:
+        qk = orc.quantize_qk4(qb, kb, w.dtype_code)
+    else:
+        qk = orc.quantize_qk(qb, kb, w.dtype_code, w.blk_q, w.blk_k)
     vc, vs = orc.quantize_v(vb, w.dtype_code)
     t_quant = time.perf_counter() - t0
+
+    def attend(rows):
+        if w.qk4:
+            return orc.attn_rows_qk4(qk, vc, vs, w.causal, w.sm_scale, rows=rows)
+        return orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
+
     rng = np.random.default_rng(0)
     total_rows = w.B * w.H * w.N
     # calibrate with a small batch, then size the sample to the budget
     rows = rng.choice(total_rows, 64, replace=False).astype(np.int64)
     t0 = time.perf_counter()
-    orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
+    attend(rows)
     per_row = (time.perf_counter() - t0) / len(rows)
     n = int(max(64, min(total_rows, (budget_s - t_quant) / max(per_row, 1e-9))))
     rows = rng.choice(total_rows, n, replace=False).astype(np.int64)
     t0 = time.perf_counter()
-    orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
+    attend(rows)
     t_rows = time.perf_counter() - t0
     t_step = t_quant + t_rows * total_rows / n
     return {"value": round(w.ops / t_step / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(), "kind": "oracle",
@@ -244,11 +256,17 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[2].record(stream)
-        q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
+        if w.qk4:
+            q = sage.quantize_qk4(Qd, Kd, workspace=ws_qk)
+        else:
+            q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
         v = sage.quantize_v(Vd, workspace=ws_v)
         if ev is not None:
             ev[0].record(stream)
-        sage.attn_fwd(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
+        if w.qk4:
+            sage.attn_fwd_qk4(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
+        else:
+            sage.attn_fwd(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
         if ev is not None:
             ev[1].record(stream)
 
@@ -268,12 +286,16 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     value = w.ops / (ms_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_avg * 1e-3) / 1e12
+    peak = QK4_PEAK_TOPS if w.qk4 else MFMA_PEAK_TOPS
     log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel avg {attn_avg:.3f} ms "
         f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
-        f"{100 * attn_tops / MFMA_PEAK_TOPS:.1f}% of peak)")
+        f"{100 * attn_tops / peak:.1f}% of peak {peak:.0f})")
 
     q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
-    quant_alg = 3 * (q_el + 2 * kv_el)      # Q, K, V: read 2-byte inputs, write 1-byte codes
+    if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below
+        quant_alg = (q_el + kv_el) * (2 + 0.5 + 1 / 32) + 3 * kv_el
+    else:
+        quant_alg = 3 * (q_el + 2 * kv_el)  # Q, K, V: read 2-byte inputs, write 1-byte codes
     quant_act = quant_alg + 2 * 2 * kv_el   # the K-sum and V-max passes read K and V once more
     quant_avg = float(np.mean(quant_ms))
     quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
@@ -289,16 +311,17 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8+fp8 (fp32 softmax)", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp4+fp8 (fp32 softmax)" if w.qk4 else "int8+fp8 (fp32 softmax)",
+        "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "Hkv": Hkv, "Nkv": Nkv, "d": d, "causal": w.causal,
                    "in_dtype": w.dtype,
                    "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_tile": sage.sage_kv_tile(), "parallelism": "none (1 GPU)"},
         "attn_kernel_ms": round(attn_avg, 4),
         "attn_kernel_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),
         "attn_tops": round(attn_tops, 3),
-        "frac_of_mfma_peak_step": round(value / MFMA_PEAK_TOPS, 4),
+        "frac_of_mfma_peak_step": round(value / peak, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 3),
-                     "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(attn_tops / MFMA_PEAK_TOPS, 4),
+                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(attn_tops / peak, 4),
                      "traffic": measured_traffic(w.name)},
         "quantize": {"ms": round(quant_avg, 4), "bound": "hbm", "algorithmic_bytes": quant_alg,
                      "bytes_moved": quant_act, "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

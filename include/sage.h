@@ -267,6 +267,46 @@ int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* 
                      int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
                      int kv_chunk, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sage_quantize_qk4 -- Q and smoothed K to 4-bit E2M1 for sage_attn_fwd_qk4
+ * (SageAttention3 abstract: attention on FP4 matrix cores; here the FP4
+ * matrix instruction multiplies E2M1 values with one power-of-two scale per
+ * 32 values along d).  The K mean is that of sage_quantize_qk.  Every token
+ * row is cut into blocks of 32 channels: E = floor(log2(max|x|)) - 2 clamped
+ * to [-127, 127], stored as the scale byte E + 127 (E8M0); codes =
+ * E2M1(x / 2^E), round to nearest with ties to the even code, saturating at 6
+ * (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 by code 0..7, bit 3 the sign); an
+ * all-zero block gets scale byte 0.
+ * Out: q4_codes [B,Hq,Nqp,d/2] bytes (two codes per byte, the even channel in
+ *      the low nibble), q4_scale [B,Hq,Nqp,d/32] bytes, k4_codes [B,Hkv,Nkt,d/2],
+ *      k4_scale [B,Hkv,Nkt,d/32], k_mean [B,Hkv,d] fp32; padding rows zero.
+ * workspace: sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d).
+ */
+int sage_quantize_qk4(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
+                      int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes, uint8_t* k4_scale,
+                      float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_attn_fwd_qk4 -- sage_attn_fwd_ex with the scores from the 4-bit codes:
+ *   S_j = sum over blocks b of 2^(Eq_b + Ek_b) * sum_{c in b} q_c k_c
+ * on the FP4 matrix cores (fp32; exact products, fp32 accumulation), and the
+ * dequantization factor c2 = sm_scale * log2 e for every key; softmax, FP8 P~
+ * (V from sage_quantize_v_ex) and the two-level P~V as in sage_attn_fwd.
+ * The 4-bit scores are coarser than INT8 (about three bits fewer).
+ */
+int sage_attn_fwd_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                      const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype,
+                      int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, float sm_scale,
+                      void* stream);
+
+/* sage_attn_fwd_qk4_dump -- sage_attn_fwd_qk4 with the dumps of
+ * sage_attn_fwd_ex_dump; s_dump holds the fp32 scores' bit patterns. */
+int sage_attn_fwd_qk4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                           const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, void* O,
+                           int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                           float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

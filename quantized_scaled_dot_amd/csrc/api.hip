@@ -56,17 +56,30 @@ int launch_status() {
     if (!aligned16(p)) return SAGE_ERR_MISALIGNED;     \
   } while (0)
 
+// q4 (4-bit QK^T): q_codes/k_codes/q_scale/k_scale are unused and the four q4 pointers are the operands
+struct Q4Ptrs {
+  const uint8_t* q4_codes;
+  const uint8_t* q4_scale;
+  const uint8_t* k4_codes;
+  const uint8_t* k4_scale;
+};
+
 int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                 const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
                 int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
-                const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, bool dump, void* stream) {
+                const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump, bool dump, void* stream,
+                const Q4Ptrs* q4 = nullptr) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_blocks(blk_q, blk_k));
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
   if (causal && Nkv < Nq) return SAGE_ERR_INVALID_ARG;   // the first rows would see no key
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  if (q4) {
+    SAGE_PTR(q4->q4_codes); SAGE_PTR(q4->q4_scale); SAGE_PTR(q4->k4_codes); SAGE_PTR(q4->k4_scale);
+  } else {
+    SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  }
   SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O);
   if (dump) {
     if (n_sel < 0) return SAGE_ERR_INVALID_ARG;
@@ -79,6 +92,7 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   a.causal = causal;
   a.s2 = sm_scale * sage::kLog2e;
   a.sel = dump ? sel : nullptr; a.n_sel = dump ? n_sel : 0; a.s_dump = s_dump; a.p_dump = p_dump;
+  if (q4) { a.q4_codes = q4->q4_codes; a.q4_scale = q4->q4_scale; a.k4_codes = q4->k4_codes; a.k4_scale = q4->k4_scale; }
   (void)hipGetLastError();
   sage::launch_attn_fwd(a, dump, (hipStream_t)stream);
   return launch_status();
@@ -161,6 +175,43 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
                     void* workspace, size_t workspace_bytes, void* stream) {
   return sage_quantize_v_ex(V, in_dtype, SAGE_LAYOUT_BHND, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes,
                             stream);
+}
+
+int sage_quantize_qk4(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
+                      int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes, uint8_t* k4_scale,
+                      float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(q4_codes); SAGE_PTR(q4_scale); SAGE_PTR(k4_codes); SAGE_PTR(k4_scale);
+  SAGE_PTR(k_mean); SAGE_PTR(workspace);
+  if (workspace_bytes < sage::quantize_qk_workspace(B * Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
+  sage::Quant4Args a{};
+  a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d;
+  a.q4_codes = q4_codes; a.q4_scale = q4_scale; a.k4_codes = k4_codes; a.k4_scale = k4_scale; a.k_mean = k_mean;
+  a.workspace = workspace;
+  (void)hipGetLastError();
+  sage::launch_quantize_qk4(a, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sage_attn_fwd_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                      const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype,
+                      int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, float sm_scale,
+                      void* stream) {
+  const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale};
+  return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream, &q4);
+}
+
+int sage_attn_fwd_qk4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                           const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, void* O,
+                           int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                           float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump,
+                           void* stream) {
+  const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale};
+  return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream, &q4);
 }
 
 int sage_quantize_q(const void* Q, int in_dtype, int layout, int B, int Hq, int Nq, int d, int blk_q,

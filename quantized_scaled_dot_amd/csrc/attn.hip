@@ -48,6 +48,12 @@ struct AttnK {
   int Hq, g, Nq, Nkv, off, nqt, nbq, blk_q, nhd;   // g = Hq/Hkv; off = Nkv - Nq
   int nqp, nkt;   // Q code rows per head (Nq rounded up to 128); KV tiles per head
   int nbk, lgk;   // K scales per head; log2 of the K block size
+  // 4-bit QK^T: E2M1 codes (two per byte, rows of d/2 bytes) and one E8M0
+  // scale byte per 32 channels of a row
+  const uint8_t* q4_codes;
+  const uint8_t* q4_scale;
+  const uint8_t* k4_codes;
+  const uint8_t* k4_scale;
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -64,13 +70,21 @@ struct AttnK {
 // of 16 (keys 32g + v and 32g + 16 + v), each inside one K block, so a lane
 // dequantizes each run with its own factor and the row max combines the two
 // scaled run maxima.  Otherwise one K block is one KV tile.
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int OUT, bool DUMP>
+// QK4: 4-bit QK^T.  Q and K are E2M1 with a power-of-two scale per 32
+// channels; the scores come from the scaled FP4 matrix instruction as fp32
+// (the block scales applied inside it), so the dequantization factor is
+// sm_scale * log2(e) alone and the row max runs on fp32.  K tiles are d/2
+// bytes per key; each lane loads the scale bytes of its two MFMA rows' keys
+// one step ahead.
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4, int OUT, bool DUMP>
 __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
-  constexpr int KS = D / 32;                   // k-steps of the int8 MFMA over d
+  constexpr int KB = QK4 ? D / 2 : D;          // K code bytes per key
+  constexpr int KS = KB / 32;                  // k-steps of the score MFMA over d (32 code bytes a lane pair)
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
-  constexpr int TILE = kKTile * D;             // bytes of one K tile = one V tile in HBM
-  constexpr int CPT = TILE / 16 / 256;         // 16-byte chunks per thread per tile (2 or 1)
-  constexpr int RK = kRowK<D>;
+  constexpr int TILE = kKTile * D;             // bytes of one V tile (and of one INT8 K tile) in HBM
+  constexpr int KTILE = kKTile * KB;           // bytes of one K tile in HBM
+  constexpr int RK = QK4 ? KB + 16 : kRowK<D>;
+  using SV = typename std::conditional<QK4, v16f, v16i>::type;   // score registers
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
   __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
 
@@ -119,12 +133,17 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 
   v4i qreg[KS];
+  int qsc[KS];   // QK4: the E8M0 scale byte of each of this lane's Q blocks
   {
-    const int8_t* qp = p.q_codes + ((size_t)bh * p.nqp + row) * D + 16 * lg;
+    const int8_t* qp = (QK4 ? (const int8_t*)p.q4_codes : p.q_codes) + ((size_t)bh * p.nqp + row) * KB + 16 * lg;
 #pragma unroll
     for (int s = 0; s < KS; s++) qreg[s] = *(const v4i*)(qp + 32 * s);
+    if (QK4) {
+#pragma unroll
+      for (int s = 0; s < KS; s++) qsc[s] = p.q4_scale[((size_t)bh * p.nqp + row) * (D / 32) + 2 * s + lg];
+    }
   }
-  const float dq = p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
+  const float dq = QK4 ? 0.0f : p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
 
   // ---- staging: direct global -> LDS copies (buffer loads with the LDS
   // destination, 16 bytes per lane, 1 KiB per wave instruction) ----
@@ -139,14 +158,15 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
   constexpr int JK = (NKI + 3) / 4, JV = (NVI + 3) / 4;
-  const __amdgpu_buffer_rsrc_t rK = head_rsrc(p.k_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
+  const __amdgpu_buffer_rsrc_t rK =
+      head_rsrc((QK4 ? (const int8_t*)p.k4_codes : p.k_codes) + (size_t)bhkv * p.nkt * KTILE, (uint32_t)(p.nkt * KTILE));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
   uint32_t koff[JK], voff[JV];
 #pragma unroll
   for (int j = 0; j < JK; j++) {
     const int o = 1024 * (wave + 4 * j) + 16 * lane;
-    const int rho = o / RK, c = min((o % RK) / 16, D / 16 - 1);
-    koff[j] = (uint32_t)(k_lds_key(rho) * D + 16 * c);
+    const int rho = o / RK, c = min((o % RK) / 16, KB / 16 - 1);
+    koff[j] = (uint32_t)(k_lds_key(rho) * KB + 16 * c);
   }
 #pragma unroll
   for (int j = 0; j < JV; j++) {
@@ -159,7 +179,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     for (int j = 0; j < JK; j++) {
       const int i = wave + 4 * j;
       if (i < NKI)
-        lds_copy16(rK, &sK[slot][1024 * i], koff[j], t * TILE);
+        lds_copy16(rK, &sK[slot][1024 * i], koff[j], t * KTILE);
     }
   };
   auto stageV = [&](int t, int slot) {
@@ -187,16 +207,36 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // K scale index of the run of 16 keys of half h of this lane in tile t
   auto kidx = [&](int t, int h) { return FINEK ? (t * kKTile + 32 * lg + 16 * h) >> p.lgk : t; };
 
-  // S^T = K_t . Q^T (int32) for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v).
-  auto qk = [&](int t, v16i& a0, v16i& a1) {
+  // QK4: K scale words of this lane's two MFMA rows (keys k_lds_key(li) and
+  // k_lds_key(32 + li) of a tile): byte b is the scale of channels 32b..32b+31
+  auto kscale4 = [&](int t, int h) -> unsigned {
+    const uint8_t* ksp =
+        p.k4_scale + ((size_t)bhkv * p.nkt * kKTile + (size_t)t * kKTile + k_lds_key(32 * h + li)) * (D / 32);
+    return D == 128 ? *(const unsigned*)ksp : (unsigned)*(const uint16_t*)ksp;
+  };
+  unsigned ksw_next[2] = {QK4 ? kscale4(0, 0) : 0u, QK4 ? kscale4(0, 1) : 0u};
+  unsigned ksw[2] = {0u, 0u};
+  // S^T = K_t . Q^T for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v):
+  // int32 (INT8 codes) or fp32 (QK4, scales applied in the instruction)
+  auto qk = [&](int t, SV& a0, SV& a1) {
     const int8_t* kb0 = sK[t & 1] + li * RK + 16 * lg;   // MFMA rows li and 32 + li
-    a0 = v16i{}; a1 = v16i{};
+    a0 = SV{}; a1 = SV{};
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       const v4i k0 = *(const v4i*)(kb0 + 32 * s);
       const v4i k1 = *(const v4i*)(kb0 + 32 * RK + 32 * s);
-      a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
+      if constexpr (QK4) {
+        // this lane's 32 channels of the instruction are block 2s + lg
+        const int s0 = (int)((ksw[0] >> (8 * (2 * s + lg))) & 0xFFu), s1 = (int)((ksw[1] >> (8 * (2 * s + lg))) & 0xFFu);
+        const v8i q8 = {qreg[s][0], qreg[s][1], qreg[s][2], qreg[s][3], 0, 0, 0, 0};
+        const v8i a8 = {k0[0], k0[1], k0[2], k0[3], 0, 0, 0, 0};
+        const v8i b8 = {k1[0], k1[1], k1[2], k1[3], 0, 0, 0, 0};
+        a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8, a0, 4, 4, 0, s0, 0, qsc[s]);
+        a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, q8, a1, 4, 4, 0, s1, 0, qsc[s]);
+      } else {
+        a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
+      }
     }
   };
   // ---- two-level P~V for the tile whose V codes are in slot vslot: the
@@ -224,7 +264,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   bool pend = false, grew = false;
   float alpha_prev = 1.0f;
   // K scales (of this lane's two runs) of the tile whose softmax comes next
-  float ks_next[2] = {kscale[kidx(0, 0)], FINEK ? kscale[kidx(0, 1)] : 0.0f};
+  float ks_next[2] = {QK4 ? 0.0f : kscale[kidx(0, 0)], FINEK ? kscale[kidx(0, 1)] : 0.0f};
   auto rescale = [&]() {
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
@@ -242,7 +282,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // DIAG: the tile may hold keys after some row (causal diagonal region).
   // HAD: 1 = a P~V is pending (every step after the first in the interior),
   // 0 = none (first step), 2 = decided at run time (causal diagonal steps).
-  auto tile_step = [&](const int t, v16i& sc0, v16i& sc1, v16i& nx0, v16i& nx1, auto diag_tag, auto had_tag,
+  auto tile_step = [&](const int t, SV& sc0, SV& sc1, SV& nx0, SV& nx1, auto diag_tag, auto had_tag,
                        bool next) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     constexpr int HAD = decltype(had_tag)::value;
@@ -254,8 +294,15 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     // The K scale of tile t+1 is read one step ahead, before the tile
     // copies, so waiting for it never waits for them.
     const float ks0 = ks_next[0], ks1 = ks_next[1];
-    ks_next[0] = kscale[kidx(min(t + 1, ntiles - 1), 0)];
-    if (FINEK) ks_next[1] = kscale[kidx(min(t + 1, ntiles - 1), 1)];
+    if (QK4) {
+      // scale words of tile t+1 (its scores are computed in this step)
+      ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
+      ksw_next[0] = kscale4(min(t + 2, ntiles - 1), 0);
+      ksw_next[1] = kscale4(min(t + 2, ntiles - 1), 1);
+    } else {
+      ks_next[0] = kscale[kidx(min(t + 1, ntiles - 1), 0)];
+      if (FINEK) ks_next[1] = kscale[kidx(min(t + 1, ntiles - 1), 1)];
+    }
     // In flight while tile t is computed: K_{t+2} replaces K_t (read by the
     // previous step's score MFMAs), V_{t+1} replaces V_{t-2} (read by the
     // previous step's P~V).  Past the last tile the index is clamped: the
@@ -270,16 +317,32 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
         int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
+        const v16i si0 = __builtin_bit_cast(v16i, sc0), si1 = __builtin_bit_cast(v16i, sc1);   // QK4: fp32 bits
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-          if (!RAGGED || keyb + v < Nkv) sd[v] = sc0[v];
-          if (!RAGGED || keyb + 16 + v < Nkv) sd[16 + v] = sc1[v];
+          if (!RAGGED || keyb + v < Nkv) sd[v] = si0[v];
+          if (!RAGGED || keyb + 16 + v < Nkv) sd[16 + v] = si1[v];
         }
       }
       const bool diag = DIAG && (kv0 + kKTile - 1 > lastk0);
       // ---- online softmax state (the max runs over visible keys only) ----
       float ustar, c2a, c2b;   // c2a, c2b: dequantization factors of the two runs
-      if (!FINEK) {
+      if constexpr (QK4) {
+        float smx = -__builtin_inff();
+        if (diag) {
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            smx = fmaxf(fmaxf(smx, keyb + v > lastk ? -__builtin_inff() : sc0[v]),
+                        keyb + 16 + v > lastk ? -__builtin_inff() : sc1[v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; v++) smx = fmaxf(fmaxf(smx, sc0[v]), sc1[v]);   // v_max3_f32 chain
+        }
+        smx = pair_max_f32(smx);
+        c2a = c2b = p.s2;
+        ustar = smx * c2a;
+        if (DIAG && smx == -__builtin_inff()) ustar = -1e30f;   // no visible key in this tile for this row
+      } else if (!FINEK) {
         int smax = INT32_MIN;
         if (diag) {
 #pragma unroll
@@ -323,7 +386,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
           float pv4[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
+            const auto sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];   // int32 or fp32 score
             float arg = __builtin_fmaf((float)sv, h == 0 ? c2a : c2b, -mm);
             if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
@@ -368,7 +431,12 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   stageK(min(1, ntiles - 1), 1);
   staged();
   __syncthreads();
-  v16i sa0, sa1, sb0, sb1;
+  SV sa0, sa1, sb0, sb1;
+  if (QK4) {   // scale words of tiles 0 and 1
+    ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
+    ksw_next[0] = kscale4(min(1, ntiles - 1), 0);
+    ksw_next[1] = kscale4(min(1, ntiles - 1), 1);
+  }
   qk(0, sa0, sa1);
 
   // Tiles fully visible to every row of the workgroup (before the causal
@@ -427,33 +495,35 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 }
 
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int OUT>
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4, int OUT>
 static void launch5(const AttnK& k, int grid, bool dump, hipStream_t st) {
   if (dump)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, OUT, true>), dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, true>), dim3(grid), dim3(256), 0, st, k);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, OUT, false>), dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, false>), dim3(grid), dim3(256), 0, st, k);
 }
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK>
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4>
 static void launch4(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
-  if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, 2>(k, grid, dump, st);
-  else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, 1>(k, grid, dump, st);
-  else launch5<D, CAUSAL, RAGGED, FINEK, 0>(k, grid, dump, st);
+  if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 2>(k, grid, dump, st);
+  else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 1>(k, grid, dump, st);
+  else launch5<D, CAUSAL, RAGGED, FINEK, QK4, 0>(k, grid, dump, st);
 }
+// the score variant: INT8 with K blocks of a tile, INT8 with finer K blocks, or 4-bit
 template <int D, bool CAUSAL, bool RAGGED>
-static void launch3(const AttnK& k, int grid, bool finek, int out, bool dump, hipStream_t st) {
-  if (finek) launch4<D, CAUSAL, RAGGED, true>(k, grid, out, dump, st);
-  else launch4<D, CAUSAL, RAGGED, false>(k, grid, out, dump, st);
+static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, hipStream_t st) {
+  if (variant == 2) launch4<D, CAUSAL, RAGGED, false, true>(k, grid, out, dump, st);
+  else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, false>(k, grid, out, dump, st);
+  else launch4<D, CAUSAL, RAGGED, false, false>(k, grid, out, dump, st);
 }
 template <int D>
-static void launch2(const AttnK& k, int grid, bool causal, bool ragged, bool finek, int out, bool dump,
+static void launch2(const AttnK& k, int grid, bool causal, bool ragged, int variant, int out, bool dump,
                     hipStream_t st) {
   if (causal) {
-    if (ragged) launch3<D, true, true>(k, grid, finek, out, dump, st);
-    else launch3<D, true, false>(k, grid, finek, out, dump, st);
+    if (ragged) launch3<D, true, true>(k, grid, variant, out, dump, st);
+    else launch3<D, true, false>(k, grid, variant, out, dump, st);
   } else {
-    if (ragged) launch3<D, false, true>(k, grid, finek, out, dump, st);
-    else launch3<D, false, false>(k, grid, finek, out, dump, st);
+    if (ragged) launch3<D, false, true>(k, grid, variant, out, dump, st);
+    else launch3<D, false, false>(k, grid, variant, out, dump, st);
   }
 }
 
@@ -468,9 +538,10 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
   const int grid = a.B * a.Hq * k.nqt;
   const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
-  const bool finek = a.blk_k < kKTile;
-  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, finek, a.out_dtype, dump, st);
-  else launch2<64>(k, grid, a.causal, ragged, finek, a.out_dtype, dump, st);
+  k.q4_codes = a.q4_codes; k.q4_scale = a.q4_scale; k.k4_codes = a.k4_codes; k.k4_scale = a.k4_scale;
+  const int variant = a.q4_codes ? 2 : a.blk_k < kKTile ? 1 : 0;
+  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
+  else launch2<64>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
 }
 
 }  // namespace sage

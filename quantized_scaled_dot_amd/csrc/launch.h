@@ -42,12 +42,32 @@ struct AttnArgs {
   int out_dtype, nhd;   // O layout: [B,Hq,Nq,d] (0) or [B,Nq,Hq,d] (1)
   int B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal;
   float s2;   // fp32(sm_scale * log2 e)
+  // 4-bit QK^T instead of INT8 (q4_codes != nullptr): codes and scales as in Quant4Args
+  const uint8_t* q4_codes = nullptr;
+  const uint8_t* q4_scale = nullptr;
+  const uint8_t* k4_codes = nullptr;
+  const uint8_t* k4_scale = nullptr;
   // dump (test) mode
   const int32_t* sel;
   int n_sel;
   int32_t* s_dump;
   uint8_t* p_dump;
 };
+
+// 4-bit Q and smoothed K (E2M1, one power-of-two scale per 32 channels).
+struct Quant4Args {
+  const void* Q;
+  const void* K;
+  int is_bf16, nhd;
+  int B, Hq, Hkv, Nq, Nkv, d;
+  uint8_t* q4_codes;   // [B,Hq,Nqp,d/2] packed nibbles
+  uint8_t* q4_scale;   // [B,Hq,Nqp,d/32]
+  uint8_t* k4_codes;   // [B,Hkv,Nkt,d/2]
+  uint8_t* k4_scale;   // [B,Hkv,Nkt,d/32]
+  float* k_mean;
+  void* workspace;     // quantize_qk_workspace(B*Hkv, Nkv, d) bytes
+};
+void launch_quantize_qk4(const Quant4Args& a, hipStream_t st);
 
 // Decode over a quantized KV cache: split-KV chunks of kv_chunk keys, merged.
 struct DecodeArgs {

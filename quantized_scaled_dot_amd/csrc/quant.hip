@@ -324,6 +324,71 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit Q / K: E2M1 values in blocks of 32 channels of a token row, one
+// power-of-two scale per block: E = floor(log2(max|x|)) - 2 clamped to
+// [-127, 127] (stored as the byte E + 127), values E2M1(x / 2^E) rounded to
+// nearest with ties to the even code, saturating at 6; an all-zero block gets
+// scale byte 0.  Codes are packed two per byte (even channel in the low
+// nibble), rows of d/2 bytes, padded with zero rows like the INT8 codes.
+// One thread per (row, block).  SMOOTH: x = K - mean (fp32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned e2m1_code(float x) {
+  const float y = fabsf(x);
+  // thresholds between consecutive magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; at a
+  // midpoint the code with the even last bit wins (strict or non-strict test)
+  const unsigned m = (unsigned)(y > 0.25f) + (unsigned)(y >= 0.75f) + (unsigned)(y > 1.25f) +
+                     (unsigned)(y >= 1.75f) + (unsigned)(y > 2.5f) + (unsigned)(y >= 3.5f) + (unsigned)(y > 5.0f);
+  return m | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <int D, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict__ X, int is_bf16, InRows in, int BH,
+                                                     const float* __restrict__ mean, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scale) {
+  constexpr int NB = D / 32;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)BH * in.P * NB) return;
+  const int b = (int)(gid % NB);
+  const long long rowid = gid / NB;
+  const int n = (int)(rowid % in.P), bh = (int)(rowid / in.P);
+  float x[32];
+  if (n < in.N) {
+    const uint16_t* src = X + in.head(bh, D) + (size_t)n * in.stride(D) + 32 * b;
+#pragma unroll
+    for (int l = 0; l < 4; l++) {
+      const v4i raw = *(const v4i*)(src + 8 * l);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float v = half_of(raw, e, is_bf16);
+        if (SMOOTH) v = v - mean[(size_t)bh * D + 32 * b + 8 * l + e];
+        x[8 * l + e] = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; k++) x[k] = 0.0f;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; k++) a = fmaxf(a, fabsf(x[k]));
+  unsigned sbyte = 0;
+  v4i packed = {0, 0, 0, 0};
+  if (a != 0.0f) {
+    const int e = min(max(ilogbf(a) - 2, -127), 127);
+    sbyte = (unsigned)(e + 127);
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      unsigned word = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) word |= e2m1_code(ldexpf(x[8 * w + k], -e)) << (4 * k);
+      packed[w] = (int)word;
+    }
+  }
+  *(v4i*)(codes + (size_t)rowid * (D / 2) + 16 * b) = packed;
+  scale[(size_t)rowid * NB + b] = (uint8_t)sbyte;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
 static inline int stat_chunks(int N) { return (N + kStatChunk - 1) / kStatChunk; }
@@ -386,6 +451,29 @@ static void launch_v_d(const QuantVArgs& a, hipStream_t st) {
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {
   if (a.d == 128) launch_v_d<128>(a, st);
   else launch_v_d<64>(a, st);
+}
+
+template <int D>
+static void launch_qk4_d(const Quant4Args& a, hipStream_t st) {
+  const int BHq = a.B * a.Hq, BHkv = a.B * a.Hkv;
+  const int nchunk = stat_chunks(a.Nkv);
+  long long* partial = (long long*)a.workspace;
+  const InRows qin{a.Hq, a.Nq, round_up(a.Nq, kQTile), a.nhd}, kin{a.Hkv, a.Nkv, round_up(a.Nkv, kKTile), a.nhd};
+  // K column sums (the Q part of pass 1 is not launched), then the K mean
+  hipLaunchKernelGGL((qk_pass1_kernel<D, 128>), dim3(BHkv * nchunk), dim3(256), 0, st, (const uint16_t*)nullptr,
+                     (const uint16_t*)a.K, a.is_bf16, qin, kin, 0, nchunk, (int8_t*)nullptr, (float*)nullptr, partial);
+  hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
+                     D, a.k_mean);
+  const long long tq = (long long)BHq * qin.P * (D / 32), tk = (long long)BHkv * kin.P * (D / 32);
+  hipLaunchKernelGGL((quant4_kernel<D, false>), dim3((unsigned)((tq + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)a.Q, a.is_bf16, qin, BHq, (const float*)nullptr, a.q4_codes, a.q4_scale);
+  hipLaunchKernelGGL((quant4_kernel<D, true>), dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)a.K, a.is_bf16, kin, BHkv, (const float*)a.k_mean, a.k4_codes, a.k4_scale);
+}
+
+void launch_quantize_qk4(const Quant4Args& a, hipStream_t st) {
+  if (a.d == 128) launch_qk4_d<128>(a, st);
+  else launch_qk4_d<64>(a, st);
 }
 
 size_t quantize_qk_workspace(int BHkv, int Nkv, int d) {

@@ -43,6 +43,7 @@ class Workload:
     Hkv_: int = 0         # K/V heads (0: H)
     Nkv_: int = 0         # keys (0: N)
     decode: bool = False  # N new queries against a quantized cache of Nkv keys (split over the keys)
+    qk4: bool = False     # 4-bit QK^T (E2M1, a power-of-two scale per 32 channels) instead of INT8
 
     @property
     def Hkv(self):
@@ -92,6 +93,9 @@ WORKLOADS = {
     "chunked-prefill-4k-of-32k-gqa-causal": Workload("chunked-prefill-4k-of-32k-gqa-causal", 1, 32, 4096, 128,
                                                      "bfloat16", True, 128, 64, 4.0, _rsqrt32(128), Hkv_=8,
                                                      Nkv_=32768),
+    # the video DiT shape with 4-bit QK^T
+    "video-dit-32k-qk4": Workload("video-dit-32k-qk4", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0,
+                                  _rsqrt32(128), qk4=True),
     # finer quantization granularity: a Q scale per 32 rows, a K scale per 16 keys
     "llm-prefill-4k-causal-fine": Workload("llm-prefill-4k-causal-fine", 4, 32, 4096, 128, "bfloat16", True, 32, 16,
                                            4.0, _rsqrt32(128)),

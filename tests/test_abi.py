@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 17 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 20 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -220,3 +220,36 @@ def test_quantize_q_and_k_reject():
     assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 16, A, A, A, A, 8, None) == sage.SAGE_ERR_WORKSPACE
     assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 24, A, A, A, A, 1 << 20, None) == sage.SAGE_ERR_UNSUPPORTED
     assert sage.sage_quantize_k(A, 0, 0, 1, 2, 300, 64, 16, A, A, None, A, 1 << 20, None) == sage.SAGE_ERR_INVALID_ARG
+
+
+def _qk4(**kw):
+    args = dict(Q=A, K=A, in_dtype=1, layout=0, B=1, Hq=4, Hkv=2, Nq=256, Nkv=300, d=128, q4_codes=A, q4_scale=A,
+                k4_codes=A, k4_scale=A, k_mean=A, workspace=A, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return sage.sage_quantize_qk4(**args)
+
+
+def _attn4(**kw):
+    args = dict(q4_codes=A, q4_scale=A, k4_codes=A, k4_scale=A, v_codes=A, v_scale=A, O=A, out_dtype=2, layout=1, B=1,
+                Hq=4, Hkv=2, Nq=256, Nkv=300, d=64, causal=1, sm_scale=0.125, stream=None)
+    args.update(kw)
+    return sage.sage_attn_fwd_qk4(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), sage.SAGE_ERR_UNSUPPORTED), (dict(Hq=3), sage.SAGE_ERR_INVALID_ARG),
+    (dict(in_dtype=2), sage.SAGE_ERR_INVALID_ARG), (dict(layout=4), sage.SAGE_ERR_INVALID_ARG),
+    (dict(k4_scale=None), sage.SAGE_ERR_INVALID_ARG), (dict(q4_codes=A + 1), sage.SAGE_ERR_MISALIGNED),
+    (dict(workspace_bytes=8), sage.SAGE_ERR_WORKSPACE), (dict(Nkv=0), sage.SAGE_ERR_INVALID_ARG),
+])
+def test_quantize_qk4_rejects(kw, status):
+    assert _qk4(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=400), sage.SAGE_ERR_INVALID_ARG), (dict(q4_scale=None), sage.SAGE_ERR_INVALID_ARG),
+    (dict(k4_codes=A + 8), sage.SAGE_ERR_MISALIGNED), (dict(out_dtype=9), sage.SAGE_ERR_INVALID_ARG),
+    (dict(sm_scale=-1.0), sage.SAGE_ERR_INVALID_ARG), (dict(d=32), sage.SAGE_ERR_UNSUPPORTED),
+])
+def test_attn_fwd_qk4_rejects(kw, status):
+    assert _attn4(**kw) == status
