@@ -151,44 +151,54 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // slot: lane l writes bytes 1024 i + 16 l onward, and its global source is
   // chosen so that the padded LDS layout comes out directly (K rows in MFMA
   // order, d + 16 bytes; V channel rows, 80 bytes).  Padding chunks re-read
-  // the last data chunk of their row.  Wave w issues instructions w, w+4, ...
+  // the last data chunk of their row.  A step copies one K and one V tile:
+  // wave w issues K and V instructions w, w+4, ... of the whole rounds of
+  // four, then one of the leftover instructions (K first, then V; none when
+  // w is past them), so that no copy depends on a branch per instruction.
   // K tile t lives in sK[t%2], V tile t in sV[t%3]; K is staged one tile
-  // ahead of V (see the loop).  The K and V tiles are contiguous TILE-byte
-  // blocks in HBM (K: 64 rows of d codes; V: d rows of 64 codes).
+  // ahead of V (see the loop).  The K and V tiles are contiguous blocks in
+  // HBM (K: 64 rows of KB code bytes; V: d rows of 64 codes).
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
-  constexpr int JK = (NKI + 3) / 4, JV = (NVI + 3) / 4;
+  constexpr int FK = NKI / 4, FV = NVI / 4;              // whole rounds
+  constexpr int XK = NKI % 4, XR = NKI % 4 + NVI % 4;    // leftovers: K ones, all
+  static_assert(XR <= 4, "one leftover instruction per wave");
+  __builtin_assume(wave >= 0 && wave < 4);
   const __amdgpu_buffer_rsrc_t rK =
       head_rsrc((QK4 ? (const int8_t*)p.k4_codes : p.k_codes) + (size_t)bhkv * p.nkt * KTILE, (uint32_t)(p.nkt * KTILE));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
-  uint32_t koff[JK], voff[JV];
-#pragma unroll
-  for (int j = 0; j < JK; j++) {
-    const int o = 1024 * (wave + 4 * j) + 16 * lane;
+  auto k_src = [&](int i) {
+    const int o = 1024 * i + 16 * lane;
     const int rho = o / RK, c = min((o % RK) / 16, KB / 16 - 1);
-    koff[j] = (uint32_t)(k_lds_key(rho) * KB + 16 * c);
-  }
-#pragma unroll
-  for (int j = 0; j < JV; j++) {
-    const int o = 1024 * (wave + 4 * j) + 16 * lane;
-    const int r = o / kRowV, c = min((o % kRowV) / 16, kKTile / 16 - 1);
-    voff[j] = (uint32_t)(r * kKTile + 16 * c);
-  }
-  auto stageK = [&](int t, int slot) {
-#pragma unroll
-    for (int j = 0; j < JK; j++) {
-      const int i = wave + 4 * j;
-      if (i < NKI)
-        lds_copy16(rK, &sK[slot][1024 * i], koff[j], t * KTILE);
-    }
+    return (uint32_t)(k_lds_key(rho) * KB + 16 * c);
   };
-  auto stageV = [&](int t, int slot) {
+  auto v_src = [&](int i) {
+    const int o = 1024 * i + 16 * lane;
+    const int r = o / kRowV, c = min((o % kRowV) / 16, kKTile / 16 - 1);
+    return (uint32_t)(r * kKTile + 16 * c);
+  };
+  uint32_t koff[FK > 0 ? FK : 1], voff[FV > 0 ? FV : 1];
 #pragma unroll
-    for (int j = 0; j < JV; j++) {
-      const int i = wave + 4 * j;
-      if (i < NVI)
-        lds_copy16(rV, &sV[slot][1024 * i], voff[j], t * TILE);
-    }
+  for (int j = 0; j < FK; j++) koff[j] = k_src(wave + 4 * j);
+#pragma unroll
+  for (int j = 0; j < FV; j++) voff[j] = v_src(wave + 4 * j);
+  const bool xk = wave < XK, xv = !xk && wave < XR;   // this wave's leftover: K, V or none
+  const int xi = xk ? 4 * FK + wave : 4 * FV + wave - XK;
+  const uint32_t xoff = xk ? k_src(xi) : v_src(min(xi, NVI - 1));
+  // The copies take their LDS destination as a plain address: the compiler
+  // then does not relate them to the operand reads of the other slots (it
+  // would wait for every copy before a step's first read), and the kernel
+  // orders them itself (wait for this wave's copies, then the barrier,
+  // before any read of a slot).
+  const uint32_t kbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sK[0][0]);
+  const uint32_t vbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sV[0][0]);
+  auto stageKV = [&](int tk, int kslot, int tv, int vslot) {
+    const uint32_t kd = kbase + (uint32_t)(kslot * (kKTile * RK)), vd = vbase + (uint32_t)(vslot * (D * kRowV));
+#pragma unroll
+    for (int j = 0; j < FK; j++) lds_copy16_at(rK, kd + 1024 * (wave + 4 * j), koff[j], tk * KTILE);
+#pragma unroll
+    for (int j = 0; j < FV; j++) lds_copy16_at(rV, vd + 1024 * (wave + 4 * j), voff[j], tv * TILE);
+    if (xk || xv) lds_copy16_at(xk ? rK : rV, (xk ? kd : vd) + 1024 * xi, xoff, xk ? tk * KTILE : tv * TILE);
   };
   // this wave's copies have landed in LDS (the barrier that follows makes
   // them visible to the other waves)
@@ -307,8 +317,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     // previous step's score MFMAs), V_{t+1} replaces V_{t-2} (read by the
     // previous step's P~V).  Past the last tile the index is clamped: the
     // extra copy lands in a slot that is never read again.
-    stageK(min(t + 2, ntiles - 1), t & 1);
-    stageV(min(t + 1, ntiles - 1), (t + 1) % 3);
+    stageKV(min(t + 2, ntiles - 1), t & 1, min(t + 1, ntiles - 1), (t + 1) % 3);
     __builtin_amdgcn_sched_barrier(0);   // issue the copies first
     const int kv0 = t * kKTile;
     const int keyb = kv0 + 32 * lg;   // sc0[v] is key keyb + v, sc1[v] is key keyb + 16 + v
@@ -425,10 +434,9 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     staged();
   };
 
-  // prologue: K_0, V_0, K_1 staged, scores of tile 0 issued
-  stageK(0, 0);
-  stageV(0, 0);
-  stageK(min(1, ntiles - 1), 1);
+  // prologue: K_0, V_0, K_1 (and V_1) staged, scores of tile 0 issued
+  stageKV(0, 0, 0, 0);
+  stageKV(min(1, ntiles - 1), 1, min(1, ntiles - 1), 1);   // V_1 early: step 0 copies it to the same slot again
   staged();
   __syncthreads();
   SV sa0, sa1, sb0, sb1;

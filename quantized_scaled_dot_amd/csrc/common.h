@@ -112,5 +112,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
 __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
+// The same copy to the LDS byte address lds_addr (an integer, so that the
+// compiler does not tie the copy to an LDS object).
+__device__ __forceinline__ void lds_copy16_at(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr, 16, voff, soff, 0, 0);
+}
 
 }  // namespace sage
