@@ -65,9 +65,13 @@ def lib():
         L.oracle_quantize_k4.restype = i32
         L.oracle_quantize_k4.argtypes = [P, i32, i32, i32, i32, P, P, P]
         L.oracle_attn_rows_qk4.restype = i32
-        L.oracle_attn_rows_qk4.argtypes = [P, P, P, P, P, P] + [i32] * 8 + [f32, P, i32, P, P]
+        L.oracle_attn_rows_qk4.argtypes = [P] * 10 + [i32] * 8 + [f32, P, i32, P, P]
         L.oracle_qk4_scores.restype = i32
-        L.oracle_qk4_scores.argtypes = [P, P, P, P] + [i32] * 6 + [P, i32, P]
+        L.oracle_qk4_scores.argtypes = [P] * 8 + [i32] * 6 + [P, i32, P]
+        L.oracle_quantize_k8.restype = i32
+        L.oracle_quantize_k8.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.oracle_quantize_q4_smooth.restype = i32
+        L.oracle_quantize_q4_smooth.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_attn_rows_split.restype = i32
         L.oracle_attn_rows_split.argtypes = [P, P, P, P, P, P] + [i32] * 11 + [f32, P, i32, P]
         L.oracle_attn_rows.restype = i32
@@ -246,9 +250,12 @@ def e2m1_encode(x):
     return out
 
 
-def quantize_qk4(Q_bits, K_bits, dtype):
+def quantize_qk4(Q_bits, K_bits, dtype, smooth_q=False):
     """E2M1 blocks of 32 channels of Q [B,Hq,Nq,d] and of the smoothed K
-    [B,Hkv,Nkv,d]: codes (one per value, 0..15) and E8M0 scale bytes per block."""
+    [B,Hkv,Nkv,d]: codes (one per value, 0..15) and E8M0 scale bytes per block.
+    smooth_q: Q minus the mean of its 32-query block, which is returned as
+    q_mean [B,Hq,ceil(Nq/32),d] and its e4m3 codes / E8M0 scales, with the
+    smoothed K also in e4m3 blocks (k8_codes, k8_scale) for the mean's term."""
     Q_bits = _c(Q_bits, np.uint16)
     K_bits = _c(K_bits, np.uint16)
     B, Hq, Nq, d = Q_bits.shape
@@ -258,11 +265,31 @@ def quantize_qk4(Q_bits, K_bits, dtype):
     kc = np.empty((B, Hkv, Nkv, d), np.uint8)
     ks = np.empty((B, Hkv, Nkv, d // 32), np.uint8)
     mu = np.empty((B, Hkv, d), np.float32)
-    rc = lib().oracle_quantize_q4(_p(Q_bits), dtype, B * Hq, Nq, d, _p(qc), _p(qs))
+    extra = {}
+    if smooth_q:
+        nb = -(-Nq // 32)
+        qmean = np.empty((B, Hq, nb, d), np.float32)
+        qmc = np.empty((B, Hq, nb, d), np.uint8)
+        qms = np.empty((B, Hq, nb, d // 32), np.uint8)
+        rc = lib().oracle_quantize_q4_smooth(_p(Q_bits), dtype, B * Hq, Nq, d, _p(qc), _p(qs), _p(qmean), _p(qmc),
+                                             _p(qms))
+        k8c = np.empty((B, Hkv, Nkv, d), np.uint8)
+        k8s = np.empty((B, Hkv, Nkv, d // 32), np.uint8)
+        rc |= lib().oracle_quantize_k8(_p(K_bits), dtype, B * Hkv, Nkv, d, _p(k8c), _p(k8s))
+        extra = dict(q_mean=qmean, qm_codes=qmc, qm_scale=qms, k8_codes=k8c, k8_scale=k8s)
+    else:
+        rc = lib().oracle_quantize_q4(_p(Q_bits), dtype, B * Hq, Nq, d, _p(qc), _p(qs))
     rc |= lib().oracle_quantize_k4(_p(K_bits), dtype, B * Hkv, Nkv, d, _p(kc), _p(ks), _p(mu))
     if rc != 0:
         raise ValueError("oracle quantize_qk4: unsupported shape")
-    return dict(q4_codes=qc, q4_scale=qs, k4_codes=kc, k4_scale=ks, k_mean=mu)
+    return dict(q4_codes=qc, q4_scale=qs, k4_codes=kc, k4_scale=ks, k_mean=mu, **extra)
+
+
+def _qm(qk4):
+    """The Q-mean and FP8 K codes and scales of a smoothed quantization, else NULLs."""
+    if "qm_codes" not in qk4:
+        return None, None, None, None
+    return tuple(_c(qk4[k], np.uint8) for k in ("qm_codes", "qm_scale", "k8_codes", "k8_scale"))
 
 
 def qk4_scores(qk4, rows):
@@ -271,8 +298,10 @@ def qk4_scores(qk4, rows):
     _, Hkv, Nkv, _ = kc.shape
     rows = _c(rows, np.int64)
     out = np.empty((rows.size, Nkv), np.float32)
-    if lib().oracle_qk4_scores(_p(qc), _p(qs), _p(kc), _p(ks), B, Hq, Hkv, Nq, Nkv, d, _p(rows), rows.size,
-                               _p(out)) != 0:
+    mc, ms, k8c, k8s = _qm(qk4)
+    if lib().oracle_qk4_scores(_p(qc), _p(qs), _p(kc), _p(ks), _p(mc), _p(ms), _p(k8c), _p(k8s), B, Hq, Hkv, Nq, Nkv,
+                               d, _p(rows),
+                               rows.size, _p(out)) != 0:
         raise ValueError("oracle qk4_scores: unsupported arguments")
     return out
 
@@ -289,7 +318,10 @@ def attn_rows_qk4(qk4, v_codes, v_scale, causal, sm_scale, rows=None, kv_tile=KV
     rows = _c(rows, np.int64)
     out = np.empty((rows.size, d), np.float32)
     p = np.empty((rows.size, Nkv), np.uint8) if want_p else None
-    rc = lib().oracle_attn_rows_qk4(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B, Hq, Hkv, Nq, Nkv, d, kv_tile,
+    mc, ms, k8c, k8s = _qm(qk4)
+    rc = lib().oracle_attn_rows_qk4(_p(qc), _p(qs), _p(kc), _p(ks), _p(mc), _p(ms), _p(k8c), _p(k8s), _p(vc), _p(vs),
+                                    B, Hq, Hkv, Nq,
+                                    Nkv, d, kv_tile,
                                     int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
     if rc != 0:
         raise ValueError("oracle_attn_rows_qk4: unsupported arguments")

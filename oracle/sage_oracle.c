@@ -307,6 +307,88 @@ int oracle_quantize_q4(const uint16_t* Q, int dtype, int BH, int N, int d, uint8
   return 0;
 }
 
+/* Q smoothing for the 4-bit scores (SageAttention2 abstract: Q is smoothed */
+/* to make the low-bit QK^T accurate; no block or precision given).         */
+/* Reading: the queries of a head are cut into blocks of 32 consecutive     */
+/* rows (the last block holds the N mod 32 remaining rows); the block mean   */
+/* qm[c] = fp32(S / n), S the fp64 sum of the block's rows in ascending row  */
+/* order; each row is quantized as RN(q - qm) in the E2M1 blocks above.  The */
+/* removed part returns in the scores as qm . k (see score4), with qm and  */
+/* the smoothed K both in FP8 (e4m3) blocks of 32 channels with one power-  */
+/* of-two scale each (quant_block_mx8; K in oracle_quantize_k8): an 8-bit    */
+/* product, since qm can be large and 4-bit K codes would carry their error */
+/* into it.                                                                  */
+/* Outputs: q4 codes/scales as oracle_quantize_q4; q_mean [BH, nb, d] fp32, */
+/* qm_codes [BH, nb, d] e4m3, qm_scale [BH, nb, d/32] E8M0; nb = ceil(N/32). */
+
+/* n values (n <= 32) with one shared exponent E = floor(log2(max|x|)) - 7,  */
+/* clamped to [-127, 127] (the block max lands in [128, 256), below the     */
+/* e4m3 saturation at 448); codes = E(x / 2^E); scale byte E + 127; an      */
+/* all-zero block gets scale byte 0 and zero codes.                         */
+static void quant_block_mx8(const float* x, int n, uint8_t* codes, uint8_t* scale) {
+  float a = 0.0f;
+  for (int k = 0; k < n; k++) a = fmaxf(a, fabsf(x[k]));
+  if (a == 0.0f) {
+    *scale = 0;
+    for (int k = 0; k < n; k++) codes[k] = 0;
+    return;
+  }
+  int e = (int)floor(log2((double)a)) - 7;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  *scale = (uint8_t)(e + 127);
+  for (int k = 0; k < n; k++) codes[k] = oracle_e4m3_encode((float)ldexp((double)x[k], -e));
+}
+
+int oracle_quantize_q4_smooth(const uint16_t* Q, int dtype, int BH, int N, int d, uint8_t* q4_codes,
+                              uint8_t* q4_scale, float* q_mean, uint8_t* qm_codes, uint8_t* qm_scale) {
+  if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
+  const int nb = (N + 31) / 32;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    float buf[32];
+    for (int blk = 0; blk < nb; blk++) {
+      const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;
+      float* qm = q_mean + ((size_t)bh * nb + blk) * d;
+      for (int c = 0; c < d; c++) {
+        double sum = 0.0;
+        for (int i = 0; i < n; i++) sum += (double)load_in(Q, ((size_t)bh * N + n0 + i) * d + c, dtype);
+        qm[c] = (float)(sum / n);
+      }
+      for (int b = 0; b < d / 32; b++)
+        quant_block_mx8(qm + 32 * b, 32, qm_codes + ((size_t)bh * nb + blk) * d + 32 * b,
+                        qm_scale + ((size_t)bh * nb + blk) * (d / 32) + b);
+      for (int i = 0; i < n; i++)
+        for (int b = 0; b < d / 32; b++) {
+          const size_t r = (size_t)bh * N + n0 + i;
+          for (int k = 0; k < 32; k++) buf[k] = load_in(Q, r * d + 32 * b + k, dtype) - qm[32 * b + k];
+          quant_block_mx4(buf, 32, q4_codes + r * d + 32 * b, q4_scale + r * (d / 32) + b);
+        }
+    }
+  }
+  return 0;
+}
+
+/* The smoothed K (the same mean and fp32 subtraction as oracle_quantize_k4) */
+/* in e4m3 blocks of 32 channels: k8_codes [BH, N, d], k8_scale [BH, N, d/32]. */
+int oracle_quantize_k8(const uint16_t* K, int dtype, int BH, int N, int d, uint8_t* k8_codes, uint8_t* k8_scale) {
+  if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    float* mu = (float*)malloc(sizeof(float) * d);
+    kmean_head(K + (size_t)bh * N * d, dtype, N, d, mu, NULL);
+    float buf[32];
+    for (int n = 0; n < N; n++)
+      for (int b = 0; b < d / 32; b++) {
+        const size_t r = ((size_t)bh * N + n);
+        for (int k = 0; k < 32; k++) buf[k] = load_in(K, r * d + 32 * b + k, dtype) - mu[32 * b + k];
+        quant_block_mx8(buf, 32, k8_codes + r * d + 32 * b, k8_scale + r * (d / 32) + b);
+      }
+    free(mu);
+  }
+  return 0;
+}
+
 int oracle_quantize_k4(const uint16_t* K, int dtype, int BH, int N, int d, uint8_t* k4_codes, uint8_t* k4_scale,
                        float* k_mean) {
   if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
@@ -417,6 +499,13 @@ typedef struct {
   const uint8_t* q4s;
   const uint8_t* k4;
   const uint8_t* k4s;
+  /* with Q smoothing (qm != NULL): the FP8 codes and scales of the mean of
+   * the row's 32-query block, and the head's FP8 K codes [Nkv, d] and
+   * scales [Nkv, d/32] */
+  const uint8_t* qm;
+  const uint8_t* qms;
+  const uint8_t* k8;
+  const uint8_t* k8s;
   const int8_t* k;        /* the head's K codes [Nkv, d] */
   const float* ks;        /* the head's K scales [ceil(Nkv/blk_k)] */
   const uint8_t* v;       /* the head's V codes [Nkv, d] */
@@ -427,8 +516,10 @@ typedef struct {
 } row_ctx;
 
 /* 4-bit score of the row against key j: the exact sum over the 32-channel   */
-/* blocks of 2^(Eq + Ek) times the block's E2M1 dot product (fp64, exact for */
-/* the exponent spreads that occur), rounded once to fp32.                  */
+/* blocks of 2^(Eq + Ek) times the block's E2M1 dot product, plus with Q     */
+/* smoothing the same sum for the block mean against the FP8 K (2^(Em + Ek8) */
+/* times the e4m3 dot product); fp64, exact for the exponent spreads that occur, */
+/* rounded once to fp32.                                                     */
 static float score4(const row_ctx* x, int j) {
   const int d = x->d;
   const uint8_t* k = x->k4 + (size_t)j * d;
@@ -438,6 +529,13 @@ static float score4(const row_ctx* x, int j) {
     double blk = 0.0;
     for (int c = 32 * b; c < 32 * b + 32; c++) blk += oracle_e2m1_decode(x->q4[c]) * oracle_e2m1_decode(k[c]);
     s += ldexp(blk, (int)x->q4s[b] + (int)ks[b] - 254);
+    if (x->qm) {
+      const uint8_t* k8 = x->k8 + (size_t)j * d;
+      const int ek8 = x->k8s[(size_t)j * (d / 32) + b];
+      double bm = 0.0;
+      for (int c = 32 * b; c < 32 * b + 32; c++) bm += oracle_e4m3_decode(x->qm[c]) * oracle_e4m3_decode(k8[c]);
+      s += ldexp(bm, (int)x->qms[b] + ek8 - 254);
+    }
   }
   return (float)s;
 }
@@ -569,7 +667,9 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
 /* [B*H, N, d/32]; out [nrows, d]; p_codes (optional) as above.              */
 /* ------------------------------------------------------------------------ */
 int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                         const uint8_t* k4_scale, const uint8_t* v_codes, const float* v_scale, int B, int Hq,
+                         const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
+                         const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                         const float* v_scale, int B, int Hq,
                          int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
                          const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
   if (!attn_args_ok(B, Hq, Hkv, Nq, Nkv, d, 1, 1, kv_tile, causal, sm_scale) || d % 32) return -1;
@@ -586,6 +686,13 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
     x.q4s = q4_scale + ((size_t)bh * Nq + i) * (d / 32);
     x.k4 = k4_codes + (size_t)bk * Nkv * d;
     x.k4s = k4_scale + (size_t)bk * Nkv * (d / 32);
+    if (qm_codes) {
+      const int64_t blk = (bh * ((Nq + 31) / 32) + i / 32);
+      x.qm = qm_codes + (size_t)blk * d;
+      x.qms = qm_scale + (size_t)blk * (d / 32);
+      x.k8 = k8_codes + (size_t)bk * Nkv * d;
+      x.k8s = k8_scale + (size_t)bk * Nkv * (d / 32);
+    }
     x.v = v_codes + (size_t)bk * Nkv * d;
     x.Nkv = Nkv; x.d = d; x.blk_k = 1; x.kv_tile = kv_tile;
     x.last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
@@ -605,7 +712,9 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
 
 /* fp32 4-bit scores (score4) of flat query rows bh*Nq + i against every key: [nrows, Nkv] */
 int oracle_qk4_scores(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                      const uint8_t* k4_scale, int B, int Hq, int Hkv, int Nq, int Nkv, int d, const int64_t* rows,
+                      const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
+                      const uint8_t* k8_codes, const uint8_t* k8_scale, int B, int Hq,
+                      int Hkv, int Nq, int Nkv, int d, const int64_t* rows,
                       int nrows, float* out) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d % 32) return -1;
 #pragma omp parallel for schedule(dynamic)
@@ -617,6 +726,13 @@ int oracle_qk4_scores(const uint8_t* q4_codes, const uint8_t* q4_scale, const ui
     x.q4s = q4_scale + ((size_t)bh * Nq + i) * (d / 32);
     x.k4 = k4_codes + (size_t)bk * Nkv * d;
     x.k4s = k4_scale + (size_t)bk * Nkv * (d / 32);
+    if (qm_codes) {
+      const int64_t blk = (bh * ((Nq + 31) / 32) + i / 32);
+      x.qm = qm_codes + (size_t)blk * d;
+      x.qms = qm_scale + (size_t)blk * (d / 32);
+      x.k8 = k8_codes + (size_t)bk * Nkv * d;
+      x.k8s = k8_scale + (size_t)bk * Nkv * (d / 32);
+    }
     x.d = d;
     for (int j = 0; j < Nkv; j++) out[(size_t)r * Nkv + j] = score4(&x, j);
   }

@@ -741,3 +741,122 @@ def test_qk4_attention_against_fp64():
         ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), causal, 0.125).reshape(O.shape)
         a, b = O.astype(np.float64).ravel(), ex.ravel()
         assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.98
+
+
+# ------------------------------------------------------------ Q smoothing (4-bit)
+def test_q_block_mean_is_the_exact_mean_of_32_query_rows():
+    """q_mean of each block of 32 consecutive queries (the last block ragged) is
+    the exact rational mean of the block's f16 rows, rounded once to fp32."""
+    from fractions import Fraction
+    rng = np.random.default_rng(50)
+    Q = (rng.standard_normal((1, 2, 75, 64)) * 3 + rng.standard_normal((1, 2, 1, 64)) * 8).astype(np.float32)
+    K = rng.standard_normal((1, 1, 40, 64)).astype(np.float32)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    q = _f16_vals(Q)
+    assert r["q_mean"].shape == (1, 2, 3, 64)
+    for h in range(2):
+        for blk, (a, b) in enumerate(((0, 32), (32, 64), (64, 75))):
+            for c in (0, 17, 63):
+                exact = sum(Fraction(float(v)) for v in q[0, h, a:b, c]) / (b - a)
+                assert r["q_mean"][0, h, blk, c] == np.float32(float(exact)), (h, blk, c)
+
+
+def test_q_smoothing_removes_a_per_channel_bias_exactly():
+    """Dyadic inputs: adding a per-channel bias to every query leaves the
+    smoothed 4-bit codes and scales unchanged and moves the mean by the bias."""
+    rng = np.random.default_rng(51)
+    Q0 = (np.clip(np.round(rng.standard_normal((1, 2, 64, 64)) * 64), -255, 255) / 64).astype(np.float32)
+    beta = (np.clip(np.round(rng.standard_normal((1, 2, 1, 64)) * 4 * 64), -960, 960) / 64).astype(np.float32)
+    K = rng.standard_normal((1, 1, 64, 64)).astype(np.float32)
+    r0 = orc.quantize_qk4(_f16_bits(Q0), _f16_bits(K), 0, smooth_q=True)
+    r1 = orc.quantize_qk4(_f16_bits(Q0 + beta), _f16_bits(K), 0, smooth_q=True)
+    assert np.array_equal(_f16_vals(Q0 + beta), Q0 + beta)   # the biased inputs are exact in f16
+    # equal values (a -0 input minus a +0 mean gives -0, whose code keeps the sign bit)
+    assert np.array_equal(orc.e2m1_decode(r0["q4_codes"]), orc.e2m1_decode(r1["q4_codes"]))
+    assert np.array_equal(r0["q4_scale"], r1["q4_scale"])
+    assert np.array_equal(r1["q_mean"], r0["q_mean"] + beta)
+    # without smoothing the bias changes the codes
+    p1 = orc.quantize_qk4(_f16_bits(Q0 + beta), _f16_bits(K), 0)
+    assert not np.array_equal(p1["q4_codes"], r1["q4_codes"])
+
+
+def test_q_mean_fp8_blocks_properties():
+    rng = np.random.default_rng(52)
+    Q = (rng.standard_normal((1, 1, 256, 128)) + rng.standard_normal((1, 1, 1, 128)) * 5).astype(np.float32)
+    K = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    x = r["q_mean"].reshape(-1, 4, 32).astype(np.float64)
+    c = r["qm_codes"].reshape(-1, 4, 32)
+    sc = 2.0 ** (r["qm_scale"].reshape(-1, 4, 1).astype(np.float64) - 127)
+    amax = np.abs(x).max(-1, keepdims=True)
+    assert ((amax / sc >= 128) & (amax / sc < 256)).all()   # below the e4m3 saturation at 448
+    y = orc.e4m3_decode(c) * sc
+    # within half an e4m3 step (3 mantissa bits) of each value, relative to the value's binade
+    t = np.abs(x) / sc
+    step = 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3)
+    assert (np.abs(np.abs(y) / sc - t) <= step / 2 + 1e-12).all()
+    assert (np.signbit(y) == np.signbit(x))[x != 0].all()
+    # a block whose mean is all zero: scale byte 0 and zero codes
+    Qz = Q.copy(); Qz[0, 0, 32:64, 64:96] = 0
+    rz = orc.quantize_qk4(_f16_bits(Qz), _f16_bits(K), 0, smooth_q=True)
+    assert rz["qm_scale"][0, 0, 1, 2] == 0 and (rz["qm_codes"][0, 0, 1, 64:96] == 0).all()
+
+
+def test_smoothed_qk4_scores_against_exact_python_arithmetic():
+    """Score = the E2M1 blocks of the smoothed row against K's E2M1 blocks plus
+    the FP8 mean of the row's block against K's FP8 blocks, each block scaled
+    by its power-of-two scales."""
+    from fractions import Fraction
+    rng = np.random.default_rng(53)
+    Q = (rng.standard_normal((1, 2, 40, 64)) + rng.standard_normal((1, 2, 1, 64)) * 6).astype(np.float32)
+    K = (rng.standard_normal((1, 2, 8, 64)) + rng.standard_normal((1, 2, 1, 64))).astype(np.float32)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    rows = np.array([0, 33, 40 + 39], dtype=np.int64)   # head 0 rows 0 and 33 (second block), head 1 row 39
+    got = orc.qk4_scores(r, rows)
+    d4 = [Fraction(float(v)) for v in orc.e2m1_decode(np.arange(16))]
+    d8 = {c: Fraction(float(v)) for c, v in enumerate(orc.e4m3_decode(np.arange(256, dtype=np.uint8))) if np.isfinite(v)}
+    for k, row in enumerate(rows):
+        h, i = divmod(int(row), 40)
+        for j in range(8):
+            s = Fraction(0)
+            for b in range(2):
+                ek = int(r["k4_scale"][0, h, j, b])
+                blk = sum(d4[r["q4_codes"][0, h, i, c]] * d4[r["k4_codes"][0, h, j, c]] for c in range(32 * b, 32 * b + 32))
+                s += blk * Fraction(2) ** (int(r["q4_scale"][0, h, i, b]) + ek - 254)
+                bm = sum(d8[r["qm_codes"][0, h, i // 32, c]] * d8[r["k8_codes"][0, h, j, c]] for c in range(32 * b, 32 * b + 32))
+                s += bm * Fraction(2) ** (int(r["qm_scale"][0, h, i // 32, b]) + int(r["k8_scale"][0, h, j, b]) - 254)
+            assert got[k, j] == np.float32(float(s)), (row, j)
+
+
+def test_q_smoothing_helps_4bit_scores_when_q_has_a_channel_bias():
+    """With a per-channel bias in Q, the smoothed 4-bit path is closer to fp64
+    attention than the plain one; dropping the mean term would wreck it."""
+    rng = np.random.default_rng(54)
+    Q, K, V = _gqa_inputs(B=1, Hq=2, Hkv=1, Nq=128, Nkv=256, seed=55)
+    Q = (Q + 3 * rng.standard_normal((1, 2, 1, Q.shape[-1]))).astype(np.float32)
+    vc, vs = orc.quantize_v(_f16_bits(V), 0)
+    ex = orc.exact_attention(_f16_vals(Q), _f16_vals(K), _f16_vals(V), False, 0.125).reshape(-1, Q.shape[-1])
+    cos = lambda a, b: float(a.ravel() @ b.ravel() / np.sqrt((a.ravel() @ a.ravel()) * (b.ravel() @ b.ravel())))
+    rp = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+    rs = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    cp = cos(orc.attn_rows_qk4(rp, vc, vs, False, 0.125).astype(np.float64), ex)
+    cs = cos(orc.attn_rows_qk4(rs, vc, vs, False, 0.125).astype(np.float64), ex)
+    dropped = {k: v for k, v in rs.items() if k not in ("qm_codes", "qm_scale", "k8_codes", "k8_scale")}
+    cd = cos(orc.attn_rows_qk4(dropped, vc, vs, False, 0.125).astype(np.float64), ex)
+    # on these inputs: about 0.915 plain, 0.99 smoothed (the smoothed path stays near the unbiased 0.985)
+    assert cs > cp + 0.05 and cs >= 0.98 and cd < cs - 0.05, (cp, cs, cd)
+
+
+def test_k8_blocks_are_the_smoothed_k_in_fp8():
+    """FP8 K blocks: the same K mean as the 4-bit and INT8 paths, the block max
+    in [128, 256) after scaling, values within half an e4m3 step."""
+    Q, K = _q4_case(seed=56)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    ks = (_f16_vals(K) - r["k_mean"][:, :, None, :]).astype(np.float32).reshape(1, 2, 64, 4, 32).astype(np.float64)
+    sc = 2.0 ** (r["k8_scale"].astype(np.float64)[..., None] - 127)
+    amax = np.abs(ks).max(-1, keepdims=True)
+    assert ((amax / sc >= 128) & (amax / sc < 256)).all()
+    y = orc.e4m3_decode(r["k8_codes"].reshape(ks.shape)) * sc
+    t = np.abs(ks) / sc
+    step = 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3)
+    assert (np.abs(np.abs(y) / sc - t) <= step / 2 + 1e-12).all()
