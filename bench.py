@@ -38,6 +38,9 @@ MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 = dense FP8 = 5.0 P op/s
 FP4_PEAK_TOPS = 10100.0          # MI355X dense FP4 (MXFP4) 10.1 P op/s
 # 4-bit QK^T: half the counted ops on FP4, half (P~V) on FP8 -> 1 / (0.5/10.1 + 0.5/5.0) P op/s
 QK4_PEAK_TOPS = 1.0 / (0.5 / FP4_PEAK_TOPS + 0.5 / MFMA_PEAK_TOPS)
+# with Q smoothing the block mean against the FP8 K adds 2d FP8 ops per (query, key) pair beyond
+# the 4d counted: 4d counted ops need 2d FP4 + 4d FP8 matrix work -> 4 / (2/10.1 + 4/5.0) P op/s
+QK4S_PEAK_TOPS = 4.0 / (2.0 / FP4_PEAK_TOPS + 4.0 / MFMA_PEAK_TOPS)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "video-dit-32k"
 METRIC = "attention TOPS (4·B·H·N²·d/t) at 1 MI355X; % of INT8/FP8 MFMA peak"
@@ -84,7 +87,7 @@ def cpu_baseline(w, Q, K, V, budget_s=20.0):
     qb, kb, vb = synth.bits(Q), synth.bits(K), synth.bits(V)
     t0 = time.perf_counter()
     if w.qk4:
-        qk = orc.quantize_qk4(qb, kb, w.dtype_code)
+        qk = orc.quantize_qk4(qb, kb, w.dtype_code, smooth_q=w.smooth_q)
     else:
         qk = orc.quantize_qk(qb, kb, w.dtype_code, w.blk_q, w.blk_k)
     vc, vs = orc.quantize_v(vb, w.dtype_code)
@@ -257,7 +260,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         if w.qk4:
-            q = sage.quantize_qk4(Qd, Kd, workspace=ws_qk)
+            q = sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q)
         else:
             q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
         v = sage.quantize_v(Vd, workspace=ws_v)
@@ -286,7 +289,7 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     value = w.ops / (ms_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_avg * 1e-3) / 1e12
-    peak = QK4_PEAK_TOPS if w.qk4 else MFMA_PEAK_TOPS
+    peak = (QK4S_PEAK_TOPS if w.smooth_q else QK4_PEAK_TOPS) if w.qk4 else MFMA_PEAK_TOPS
     log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel avg {attn_avg:.3f} ms "
         f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
         f"{100 * attn_tops / peak:.1f}% of peak {peak:.0f})")
@@ -294,9 +297,13 @@ def main():
     q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
     if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below
         quant_alg = (q_el + kv_el) * (2 + 0.5 + 1 / 32) + 3 * kv_el
+        if w.smooth_q:   # K also as FP8 blocks (a byte per value and per 32)
+            quant_alg += kv_el * (1 + 1 / 32)
     else:
         quant_alg = 3 * (q_el + 2 * kv_el)  # Q, K, V: read 2-byte inputs, write 1-byte codes
     quant_act = quant_alg + 2 * 2 * kv_el   # the K-sum and V-max passes read K and V once more
+    if w.smooth_q:
+        quant_act += 2 * q_el               # the block-mean pass reads Q once more
     quant_avg = float(np.mean(quant_ms))
     quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
     log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "

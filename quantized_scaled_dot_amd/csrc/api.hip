@@ -62,6 +62,11 @@ struct Q4Ptrs {
   const uint8_t* q4_scale;
   const uint8_t* k4_codes;
   const uint8_t* k4_scale;
+  // Q smoothing (all four or none)
+  const uint8_t* qm_codes = nullptr;
+  const uint8_t* qm_scale = nullptr;
+  const uint8_t* k8_codes = nullptr;
+  const uint8_t* k8_scale = nullptr;
 };
 
 int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
@@ -77,6 +82,9 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   if (!(sm_scale > 0.0f) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (q4) {
     SAGE_PTR(q4->q4_codes); SAGE_PTR(q4->q4_scale); SAGE_PTR(q4->k4_codes); SAGE_PTR(q4->k4_scale);
+    if (q4->qm_codes || q4->qm_scale || q4->k8_codes || q4->k8_scale) {
+      SAGE_PTR(q4->qm_codes); SAGE_PTR(q4->qm_scale); SAGE_PTR(q4->k8_codes); SAGE_PTR(q4->k8_scale);
+    }
   } else {
     SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
   }
@@ -92,7 +100,10 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   a.causal = causal;
   a.s2 = sm_scale * sage::kLog2e;
   a.sel = dump ? sel : nullptr; a.n_sel = dump ? n_sel : 0; a.s_dump = s_dump; a.p_dump = p_dump;
-  if (q4) { a.q4_codes = q4->q4_codes; a.q4_scale = q4->q4_scale; a.k4_codes = q4->k4_codes; a.k4_scale = q4->k4_scale; }
+  if (q4) {
+    a.q4_codes = q4->q4_codes; a.q4_scale = q4->q4_scale; a.k4_codes = q4->k4_codes; a.k4_scale = q4->k4_scale;
+    a.qm_codes = q4->qm_codes; a.qm_scale = q4->qm_scale; a.k8_codes = q4->k8_codes; a.k8_scale = q4->k8_scale;
+  }
   (void)hipGetLastError();
   sage::launch_attn_fwd(a, dump, (hipStream_t)stream);
   return launch_status();
@@ -180,15 +191,28 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
 int sage_quantize_qk4(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv, int Nq,
                       int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes, uint8_t* k4_scale,
                       float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  return sage_quantize_qk4_smooth_q(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, q4_codes, q4_scale, k4_codes,
+                                    k4_scale, k_mean, nullptr, nullptr, nullptr, nullptr, nullptr, workspace,
+                                    workspace_bytes, stream);
+}
+
+int sage_quantize_qk4_smooth_q(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv,
+                               int Nq, int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes,
+                               uint8_t* k4_scale, float* k_mean, float* q_mean, uint8_t* qm_codes,
+                               uint8_t* qm_scale, uint8_t* k8_codes, uint8_t* k8_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_in_dtype(in_dtype));
   SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(q4_codes); SAGE_PTR(q4_scale); SAGE_PTR(k4_codes); SAGE_PTR(k4_scale);
   SAGE_PTR(k_mean); SAGE_PTR(workspace);
+  const bool smooth = q_mean || qm_codes || qm_scale || k8_codes || k8_scale;
+  if (smooth) { SAGE_PTR(q_mean); SAGE_PTR(qm_codes); SAGE_PTR(qm_scale); SAGE_PTR(k8_codes); SAGE_PTR(k8_scale); }
   if (workspace_bytes < sage::quantize_qk_workspace(B * Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
   sage::Quant4Args a{};
   a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d;
   a.q4_codes = q4_codes; a.q4_scale = q4_scale; a.k4_codes = k4_codes; a.k4_scale = k4_scale; a.k_mean = k_mean;
+  if (smooth) { a.q_mean = q_mean; a.qm_codes = qm_codes; a.qm_scale = qm_scale; a.k8_codes = k8_codes; a.k8_scale = k8_scale; }
   a.workspace = workspace;
   (void)hipGetLastError();
   sage::launch_quantize_qk4(a, (hipStream_t)stream);
@@ -210,6 +234,29 @@ int sage_attn_fwd_qk4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, con
                            float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump,
                            void* stream) {
   const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale};
+  return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream, &q4);
+}
+
+int sage_attn_fwd_qk4_smooth_q(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                               const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
+                               const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                               const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
+                               int Nq, int Nkv, int d, int causal, float sm_scale, void* stream) {
+  if (!qm_codes || !qm_scale || !k8_codes || !k8_scale) return SAGE_ERR_INVALID_ARG;
+  const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale};
+  return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream, &q4);
+}
+
+int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                                    const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
+                                    const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                                    const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
+                                    int Nq, int Nkv, int d, int causal, float sm_scale, const int32_t* sel, int n_sel,
+                                    int32_t* s_dump, uint8_t* p_dump, void* stream) {
+  if (!qm_codes || !qm_scale || !k8_codes || !k8_scale) return SAGE_ERR_INVALID_ARG;
+  const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale};
   return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
                      d, 128, 64, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream, &q4);
 }

@@ -54,6 +54,13 @@ struct AttnK {
   const uint8_t* q4_scale;
   const uint8_t* k4_codes;
   const uint8_t* k4_scale;
+  // Q smoothing of the 4-bit scores: FP8 block means of 32 queries (nqp/32
+  // blocks per head, rows of d codes) with E8M0 scales per 32 channels, and
+  // the smoothed K in FP8 blocks (rows of d codes, scales per 32 channels)
+  const uint8_t* qm_codes;
+  const uint8_t* qm_scale;
+  const uint8_t* k8_codes;
+  const uint8_t* k8_scale;
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -75,18 +82,24 @@ struct AttnK {
 // (the block scales applied inside it), so the dequantization factor is
 // sm_scale * log2(e) alone and the row max runs on fp32.  K tiles are d/2
 // bytes per key; each lane loads the scale bytes of its two MFMA rows' keys
-// one step ahead.
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4, int OUT, bool DUMP>
+// one step ahead.  QK4 = 2 adds Q smoothing: the scores also take the mean
+// of the wave's 32 queries (one block) against the FP8 K, on the FP8 matrix
+// instruction into the same fp32 accumulators (the FP8 K tile is staged next
+// to the 4-bit one, rows of d + 16 bytes in the same MFMA order).
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP>
 __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
+  constexpr bool QSM = QK4 == 2;
   constexpr int KB = QK4 ? D / 2 : D;          // K code bytes per key
   constexpr int KS = KB / 32;                  // k-steps of the score MFMA over d (32 code bytes a lane pair)
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
   constexpr int TILE = kKTile * D;             // bytes of one V tile (and of one INT8 K tile) in HBM
   constexpr int KTILE = kKTile * KB;           // bytes of one K tile in HBM
   constexpr int RK = QK4 ? KB + 16 : kRowK<D>;
-  using SV = typename std::conditional<QK4, v16f, v16i>::type;   // score registers
+  using SV = typename std::conditional<(QK4 != 0), v16f, v16i>::type;   // score registers
+  constexpr int RK8 = kRowK<D>;                 // FP8 K rows (Q smoothing), padded like INT8 K
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
   __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
+  __shared__ __attribute__((aligned(16))) uint8_t sK8[2][QSM ? kKTile * RK8 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -144,6 +157,23 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     }
   }
   const float dq = QK4 ? 0.0f : p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
+  // Q smoothing: the FP8 mean of this wave's 32 queries as the B operand of
+  // every column, and its scales.  An FP8 operand of the scaled 64-deep
+  // instruction holds, in lane group g, elements 16g .. 16g+15 of the first
+  // 32-element scale block in bytes 0-15 and the same of the second block in
+  // bytes 16-31; the scale given by lane group g covers block g.
+  v8i qm8[QSM ? KS : 1];
+  int qmsc[QSM ? KS : 1];
+  if (QSM) {
+    const size_t r = (size_t)bh * (p.nqp / 32) + qrow0 / 32;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      const uint8_t* mp = p.qm_codes + r * D + 64 * s + 16 * lg;
+      const v4i m0 = *(const v4i*)mp, m1 = *(const v4i*)(mp + 32);
+      qm8[s] = v8i{m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+      qmsc[s] = p.qm_scale[r * (D / 32) + 2 * s + lg];
+    }
+  }
 
   // ---- staging: direct global -> LDS copies (buffer loads with the LDS
   // destination, 16 bytes per lane, 1 KiB per wave instruction) ----
@@ -159,32 +189,48 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // ahead of V (see the loop).  The K and V tiles are contiguous blocks in
   // HBM (K: 64 rows of KB code bytes; V: d rows of 64 codes).
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
-  static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0, "whole DMA instructions per tile");
-  constexpr int FK = NKI / 4, FV = NVI / 4;              // whole rounds
-  constexpr int XK = NKI % 4, XR = NKI % 4 + NVI % 4;    // leftovers: K ones, all
-  static_assert(XR <= 4, "one leftover instruction per wave");
+  constexpr int N8I = QSM ? kKTile * RK8 / 1024 : 0;                 // FP8 K tile (Q smoothing)
+  constexpr int KTILE8 = kKTile * D;                                 // bytes of one FP8 K tile in HBM
+  static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0 && kKTile * RK8 % 1024 == 0,
+                "whole DMA instructions per tile");
+  constexpr int FK = NKI / 4, F8 = N8I / 4, FV = NVI / 4;            // whole rounds
+  constexpr int XK = NKI % 4, X8 = N8I % 4, XR = NKI % 4 + N8I % 4 + NVI % 4;   // leftovers: K, FP8 K, all
+  constexpr int NXR = (XR + 3) / 4;                                  // leftover rounds
+  static_assert(NXR <= 2, "at most two leftover rounds");
   __builtin_assume(wave >= 0 && wave < 4);
   const __amdgpu_buffer_rsrc_t rK =
       head_rsrc((QK4 ? (const int8_t*)p.k4_codes : p.k_codes) + (size_t)bhkv * p.nkt * KTILE, (uint32_t)(p.nkt * KTILE));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
-  auto k_src = [&](int i) {
+  const __amdgpu_buffer_rsrc_t rK8 =
+      QSM ? head_rsrc(p.k8_codes + (size_t)bhkv * p.nkt * KTILE8, (uint32_t)(p.nkt * KTILE8)) : rK;
+  auto k_src = [&](int i, int rk, int kb) {
     const int o = 1024 * i + 16 * lane;
-    const int rho = o / RK, c = min((o % RK) / 16, KB / 16 - 1);
-    return (uint32_t)(k_lds_key(rho) * KB + 16 * c);
+    const int rho = o / rk, c = min((o % rk) / 16, kb / 16 - 1);
+    return (uint32_t)(k_lds_key(rho) * kb + 16 * c);
   };
   auto v_src = [&](int i) {
     const int o = 1024 * i + 16 * lane;
     const int r = o / kRowV, c = min((o % kRowV) / 16, kKTile / 16 - 1);
     return (uint32_t)(r * kKTile + 16 * c);
   };
-  uint32_t koff[FK > 0 ? FK : 1], voff[FV > 0 ? FV : 1];
+  uint32_t koff[FK > 0 ? FK : 1], k8off[F8 > 0 ? F8 : 1], voff[FV > 0 ? FV : 1];
 #pragma unroll
-  for (int j = 0; j < FK; j++) koff[j] = k_src(wave + 4 * j);
+  for (int j = 0; j < FK; j++) koff[j] = k_src(wave + 4 * j, RK, KB);
+#pragma unroll
+  for (int j = 0; j < F8; j++) k8off[j] = k_src(wave + 4 * j, RK8, D);
 #pragma unroll
   for (int j = 0; j < FV; j++) voff[j] = v_src(wave + 4 * j);
-  const bool xk = wave < XK, xv = !xk && wave < XR;   // this wave's leftover: K, V or none
-  const int xi = xk ? 4 * FK + wave : 4 * FV + wave - XK;
-  const uint32_t xoff = xk ? k_src(xi) : v_src(min(xi, NVI - 1));
+  // this wave's leftover of round r: entry e = 4 r + wave of the list (K ones,
+  // then FP8 K, then V); xt = 0 K, 1 FP8 K, 2 V, -1 none
+  int xt[NXR > 0 ? NXR : 1], xi[NXR > 0 ? NXR : 1];
+  uint32_t xoff[NXR > 0 ? NXR : 1];
+#pragma unroll
+  for (int r = 0; r < NXR; r++) {
+    const int e = 4 * r + wave;
+    xt[r] = e < XK ? 0 : e < XK + X8 ? 1 : e < XR ? 2 : -1;
+    xi[r] = xt[r] == 0 ? 4 * FK + e : xt[r] == 1 ? 4 * F8 + e - XK : 4 * FV + e - XK - X8;
+    xoff[r] = xt[r] == 0 ? k_src(xi[r], RK, KB) : xt[r] == 1 ? k_src(min(xi[r], N8I - 1), RK8, D) : v_src(min(xi[r], NVI - 1));
+  }
   // The copies take their LDS destination as a plain address: the compiler
   // then does not relate them to the operand reads of the other slots (it
   // would wait for every copy before a step's first read), and the kernel
@@ -192,13 +238,22 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // before any read of a slot).
   const uint32_t kbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sK[0][0]);
   const uint32_t vbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sV[0][0]);
+  const uint32_t k8base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sK8[0][0]);
+  // K tile tk (and its FP8 form) into K slot kslot, V tile tv into V slot vslot
   auto stageKV = [&](int tk, int kslot, int tv, int vslot) {
     const uint32_t kd = kbase + (uint32_t)(kslot * (kKTile * RK)), vd = vbase + (uint32_t)(vslot * (D * kRowV));
+    const uint32_t k8d = k8base + (uint32_t)(kslot * (kKTile * RK8));
 #pragma unroll
     for (int j = 0; j < FK; j++) lds_copy16_at(rK, kd + 1024 * (wave + 4 * j), koff[j], tk * KTILE);
 #pragma unroll
+    for (int j = 0; j < F8; j++) lds_copy16_at(rK8, k8d + 1024 * (wave + 4 * j), k8off[j], tk * KTILE8);
+#pragma unroll
     for (int j = 0; j < FV; j++) lds_copy16_at(rV, vd + 1024 * (wave + 4 * j), voff[j], tv * TILE);
-    if (xk || xv) lds_copy16_at(xk ? rK : rV, (xk ? kd : vd) + 1024 * xi, xoff, xk ? tk * KTILE : tv * TILE);
+#pragma unroll
+    for (int r = 0; r < NXR; r++)
+      if (4 * (r + 1) <= XR || xt[r] >= 0)
+        lds_copy16_at(xt[r] == 0 ? rK : xt[r] == 1 ? rK8 : rV, (xt[r] == 0 ? kd : xt[r] == 1 ? k8d : vd) + 1024 * xi[r],
+                      xoff[r], xt[r] == 0 ? tk * KTILE : xt[r] == 1 ? tk * KTILE8 : tv * TILE);
   };
   // this wave's copies have landed in LDS (the barrier that follows makes
   // them visible to the other waves)
@@ -226,6 +281,25 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   };
   unsigned ksw_next[2] = {QK4 ? kscale4(0, 0) : 0u, QK4 ? kscale4(0, 1) : 0u};
   unsigned ksw[2] = {0u, 0u};
+  // the same for the FP8 K blocks (Q smoothing)
+  auto kscale8 = [&](int t, int h) -> unsigned {
+    const uint8_t* ksp =
+        p.k8_scale + ((size_t)bhkv * p.nkt * kKTile + (size_t)t * kKTile + k_lds_key(32 * h + li)) * (D / 32);
+    return D == 128 ? *(const unsigned*)ksp : (unsigned)*(const uint16_t*)ksp;
+  };
+  unsigned ksw8_next[2] = {QSM ? kscale8(0, 0) : 0u, QSM ? kscale8(0, 1) : 0u};
+  unsigned ksw8[2] = {0u, 0u};
+  // the scale words of tile t+1 become current; those of tile t+2 are loaded
+  auto next_kscales = [&](int tn) {
+    ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
+    ksw_next[0] = kscale4(tn, 0);
+    ksw_next[1] = kscale4(tn, 1);
+    if (QSM) {
+      ksw8[0] = ksw8_next[0]; ksw8[1] = ksw8_next[1];
+      ksw8_next[0] = kscale8(tn, 0);
+      ksw8_next[1] = kscale8(tn, 1);
+    }
+  };
   // S^T = K_t . Q^T for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v):
   // int32 (INT8 codes) or fp32 (QK4, scales applied in the instruction)
   auto qk = [&](int t, SV& a0, SV& a1) {
@@ -243,6 +317,18 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
         const v8i b8 = {k1[0], k1[1], k1[2], k1[3], 0, 0, 0, 0};
         a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8, a0, 4, 4, 0, s0, 0, qsc[s]);
         a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, q8, a1, 4, 4, 0, s1, 0, qsc[s]);
+        if constexpr (QSM) {
+          // + the block mean of Q against the FP8 K: same rows, channels 64s + 16lg .. + 16
+          // and 64s + 32 + 16lg .. + 16 (the FP8 operand layout above)
+          const uint8_t* k8b = sK8[t & 1] + li * RK8 + 64 * s + 16 * lg;
+          const v4i x0 = *(const v4i*)k8b, x1 = *(const v4i*)(k8b + 32);
+          const v4i y0 = *(const v4i*)(k8b + 32 * RK8), y1 = *(const v4i*)(k8b + 32 * RK8 + 32);
+          const int e0 = (int)((ksw8[0] >> (8 * (2 * s + lg))) & 0xFFu), e1 = (int)((ksw8[1] >> (8 * (2 * s + lg))) & 0xFFu);
+          const v8i ka = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          const v8i kb = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+          a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qm8[s], a0, 0, 0, 0, e0, 0, qmsc[s]);
+          a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb, qm8[s], a1, 0, 0, 0, e1, 0, qmsc[s]);
+        }
       } else {
         a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
@@ -305,10 +391,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     // copies, so waiting for it never waits for them.
     const float ks0 = ks_next[0], ks1 = ks_next[1];
     if (QK4) {
-      // scale words of tile t+1 (its scores are computed in this step)
-      ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
-      ksw_next[0] = kscale4(min(t + 2, ntiles - 1), 0);
-      ksw_next[1] = kscale4(min(t + 2, ntiles - 1), 1);
+      next_kscales(min(t + 2, ntiles - 1));   // tile t+1's scores are computed in this step
     } else {
       ks_next[0] = kscale[kidx(min(t + 1, ntiles - 1), 0)];
       if (FINEK) ks_next[1] = kscale[kidx(min(t + 1, ntiles - 1), 1)];
@@ -440,11 +523,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   staged();
   __syncthreads();
   SV sa0, sa1, sb0, sb1;
-  if (QK4) {   // scale words of tiles 0 and 1
-    ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
-    ksw_next[0] = kscale4(min(1, ntiles - 1), 0);
-    ksw_next[1] = kscale4(min(1, ntiles - 1), 1);
-  }
+  if (QK4) next_kscales(min(1, ntiles - 1));   // scale words of tiles 0 and 1
   qk(0, sa0, sa1);
 
   // Tiles fully visible to every row of the workgroup (before the causal
@@ -503,25 +582,27 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 }
 
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4, int OUT>
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT>
 static void launch5(const AttnK& k, int grid, bool dump, hipStream_t st) {
   if (dump)
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, true>), dim3(grid), dim3(256), 0, st, k);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, false>), dim3(grid), dim3(256), 0, st, k);
 }
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, bool QK4>
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4>
 static void launch4(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
   if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 2>(k, grid, dump, st);
   else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 1>(k, grid, dump, st);
   else launch5<D, CAUSAL, RAGGED, FINEK, QK4, 0>(k, grid, dump, st);
 }
-// the score variant: INT8 with K blocks of a tile, INT8 with finer K blocks, or 4-bit
+// the score variant: INT8 with K blocks of a tile, INT8 with finer K blocks,
+// 4-bit, or 4-bit with Q smoothing
 template <int D, bool CAUSAL, bool RAGGED>
 static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, hipStream_t st) {
-  if (variant == 2) launch4<D, CAUSAL, RAGGED, false, true>(k, grid, out, dump, st);
-  else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, false>(k, grid, out, dump, st);
-  else launch4<D, CAUSAL, RAGGED, false, false>(k, grid, out, dump, st);
+  if (variant == 3) launch4<D, CAUSAL, RAGGED, false, 2>(k, grid, out, dump, st);
+  else if (variant == 2) launch4<D, CAUSAL, RAGGED, false, 1>(k, grid, out, dump, st);
+  else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, 0>(k, grid, out, dump, st);
+  else launch4<D, CAUSAL, RAGGED, false, 0>(k, grid, out, dump, st);
 }
 template <int D>
 static void launch2(const AttnK& k, int grid, bool causal, bool ragged, int variant, int out, bool dump,
@@ -547,7 +628,8 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   const int grid = a.B * a.Hq * k.nqt;
   const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
   k.q4_codes = a.q4_codes; k.q4_scale = a.q4_scale; k.k4_codes = a.k4_codes; k.k4_scale = a.k4_scale;
-  const int variant = a.q4_codes ? 2 : a.blk_k < kKTile ? 1 : 0;
+  k.qm_codes = a.qm_codes; k.qm_scale = a.qm_scale; k.k8_codes = a.k8_codes; k.k8_scale = a.k8_scale;
+  const int variant = a.q4_codes ? (a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
   if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
   else launch2<64>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
 }

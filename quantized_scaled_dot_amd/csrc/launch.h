@@ -47,6 +47,13 @@ struct AttnArgs {
   const uint8_t* q4_scale = nullptr;
   const uint8_t* k4_codes = nullptr;
   const uint8_t* k4_scale = nullptr;
+  // with Q smoothing of the 4-bit scores (qm_codes != nullptr): the FP8 block
+  // means of Q [B,Hq,Nqp/32,d] with scales [..,d/32], and the smoothed K in
+  // FP8 blocks [B,Hkv,Nkt,d] with scales [..,d/32]
+  const uint8_t* qm_codes = nullptr;
+  const uint8_t* qm_scale = nullptr;
+  const uint8_t* k8_codes = nullptr;
+  const uint8_t* k8_scale = nullptr;
   // dump (test) mode
   const int32_t* sel;
   int n_sel;
@@ -65,6 +72,14 @@ struct Quant4Args {
   uint8_t* k4_codes;   // [B,Hkv,Nkt,d/2]
   uint8_t* k4_scale;   // [B,Hkv,Nkt,d/32]
   float* k_mean;
+  // Q smoothing (all null: none): block means of 32 queries [B,Hq,Nqp/32,d]
+  // fp32, their FP8 codes [B,Hq,Nqp/32,d] and scales [..,d/32], and the
+  // smoothed K in FP8 blocks [B,Hkv,Nkt,d] with scales [B,Hkv,Nkt,d/32]
+  float* q_mean = nullptr;
+  uint8_t* qm_codes = nullptr;
+  uint8_t* qm_scale = nullptr;
+  uint8_t* k8_codes = nullptr;
+  uint8_t* k8_scale = nullptr;
   void* workspace;     // quantize_qk_workspace(B*Hkv, Nkv, d) bytes
 };
 void launch_quantize_qk4(const Quant4Args& a, hipStream_t st);

@@ -341,10 +341,22 @@ __device__ __forceinline__ unsigned e2m1_code(float x) {
   return m | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-template <int D, bool SMOOTH>
+// FP8 (e4m3) code of x, x already scaled into the format's range (|x| < 256):
+// the hardware conversion rounds to nearest even.
+__device__ __forceinline__ unsigned e4m3_code(float x) {
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
+}
+
+// One token row of d channels in blocks of 32, each with one power-of-two
+// scale: E2M1 codes (E = ilogb(max) - 2) and, with FP8OUT, also e4m3 codes
+// (E = ilogb(max) - 7, the block max in [128, 256)).  MEAN: 0 none, 1 one
+// mean per head (K), 2 one per block of 32 rows (Q smoothing; mean
+// [BH, P/32, d]).
+template <int D, int MEAN, bool FP8OUT>
 __global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict__ X, int is_bf16, InRows in, int BH,
                                                      const float* __restrict__ mean, uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scale) {
+                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ codes8,
+                                                     uint8_t* __restrict__ scale8) {
   constexpr int NB = D / 32;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (long long)BH * in.P * NB) return;
@@ -360,7 +372,8 @@ __global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         float v = half_of(raw, e, is_bf16);
-        if (SMOOTH) v = v - mean[(size_t)bh * D + 32 * b + 8 * l + e];
+        if (MEAN == 1) v = v - mean[(size_t)bh * D + 32 * b + 8 * l + e];
+        if (MEAN == 2) v = v - mean[((size_t)bh * (in.P / 32) + n / 32) * D + 32 * b + 8 * l + e];
         x[8 * l + e] = v;
       }
     }
@@ -386,6 +399,62 @@ __global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict_
   }
   *(v4i*)(codes + (size_t)rowid * (D / 2) + 16 * b) = packed;
   scale[(size_t)rowid * NB + b] = (uint8_t)sbyte;
+  if (FP8OUT) {
+    unsigned s8 = 0;
+    v4i c8[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (a != 0.0f) {
+      const int e = min(max(ilogbf(a) - 7, -127), 127);
+      s8 = (unsigned)(e + 127);
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        unsigned word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) word |= e4m3_code(ldexpf(x[4 * w + k], -e)) << (8 * k);
+        c8[w / 4][w % 4] = (int)word;
+      }
+    }
+    *(v4i*)(codes8 + (size_t)rowid * D + 32 * b) = c8[0];
+    *(v4i*)(codes8 + (size_t)rowid * D + 32 * b + 16) = c8[1];
+    scale8[(size_t)rowid * NB + b] = (uint8_t)s8;
+  }
+}
+
+// Block means of Q for smoothing: one workgroup per (head, block of 32 query
+// rows), one thread per channel.  The mean is the fp64 sum of the block's
+// rows in ascending order over the number of rows (the last block may be
+// short), rounded to fp32; padding blocks (past Nq) get 0.  It is written as
+// fp32 and as e4m3 codes with one power-of-two scale per 32 channels (the
+// block max in [128, 256)); an all-zero group gets scale byte 0.
+template <int D>
+__global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ X, int is_bf16, InRows in,
+                                                   float* __restrict__ q_mean, uint8_t* __restrict__ qm_codes,
+                                                   uint8_t* __restrict__ qm_scale) {
+  const int nb = in.P / 32;
+  const int blk = blockIdx.x % nb, bh = blockIdx.x / nb, c = threadIdx.x;
+  const int n0 = 32 * blk, n = min(32, in.N - n0);
+  float qm = 0.0f;
+  if (n > 0) {
+    const uint16_t* src = X + in.head(bh, D) + (size_t)n0 * in.stride(D) + c;
+    double sum = 0.0;
+    for (int i = 0; i < n; i++) {
+      const uint16_t h = src[(size_t)i * in.stride(D)];
+      sum += (double)load_h(h, is_bf16);
+    }
+    qm = (float)(sum / n);
+  }
+  float a = fabsf(qm);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));   // max over the 32-channel group
+  unsigned code = 0, sbyte = 0;
+  if (a != 0.0f) {
+    const int e = min(max(ilogbf(a) - 7, -127), 127);
+    sbyte = (unsigned)(e + 127);
+    code = e4m3_code(ldexpf(qm, -e));
+  }
+  const size_t r = (size_t)bh * nb + blk;
+  q_mean[r * D + c] = qm;
+  qm_codes[r * D + c] = (uint8_t)code;
+  if ((c & 31) == 0) qm_scale[r * (D / 32) + c / 32] = (uint8_t)sbyte;
 }
 
 // ---------------------------------------------------------------------------
@@ -465,10 +534,20 @@ static void launch_qk4_d(const Quant4Args& a, hipStream_t st) {
   hipLaunchKernelGGL(k_mean_kernel, dim3(BHkv * (D / 16)), dim3(256), 0, st, (const long long*)partial, nchunk, a.Nkv,
                      D, a.k_mean);
   const long long tq = (long long)BHq * qin.P * (D / 32), tk = (long long)BHkv * kin.P * (D / 32);
-  hipLaunchKernelGGL((quant4_kernel<D, false>), dim3((unsigned)((tq + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)a.Q, a.is_bf16, qin, BHq, (const float*)nullptr, a.q4_codes, a.q4_scale);
-  hipLaunchKernelGGL((quant4_kernel<D, true>), dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)a.K, a.is_bf16, kin, BHkv, (const float*)a.k_mean, a.k4_codes, a.k4_scale);
+  const dim3 gq((unsigned)((tq + 255) / 256)), gk((unsigned)((tk + 255) / 256));
+  if (a.q_mean) {   // Q smoothing: block means, smoothed Q, and K also in FP8 blocks
+    hipLaunchKernelGGL(q_mean_kernel<D>, dim3(BHq * (qin.P / 32)), dim3(D), 0, st, (const uint16_t*)a.Q, a.is_bf16,
+                       qin, a.q_mean, a.qm_codes, a.qm_scale);
+    hipLaunchKernelGGL((quant4_kernel<D, 2, false>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
+                       (const float*)a.q_mean, a.q4_codes, a.q4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
+    hipLaunchKernelGGL((quant4_kernel<D, 1, true>), gk, dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin, BHkv,
+                       (const float*)a.k_mean, a.k4_codes, a.k4_scale, a.k8_codes, a.k8_scale);
+    return;
+  }
+  hipLaunchKernelGGL((quant4_kernel<D, 0, false>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
+                     (const float*)nullptr, a.q4_codes, a.q4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
+  hipLaunchKernelGGL((quant4_kernel<D, 1, false>), gk, dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin, BHkv,
+                     (const float*)a.k_mean, a.k4_codes, a.k4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
 }
 
 void launch_quantize_qk4(const Quant4Args& a, hipStream_t st) {

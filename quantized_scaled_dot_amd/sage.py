@@ -25,7 +25,8 @@ SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_byt
            "sage_quantize_qk_ex", "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_quantize_v_ex",
            "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
            "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode",
-           "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump")
+           "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
+           "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -71,6 +72,12 @@ _lib.sage_attn_fwd_qk4.restype = _I
 _lib.sage_attn_fwd_qk4.argtypes = [_P] * 7 + [_I] * 9 + [_F, _P]
 _lib.sage_attn_fwd_qk4_dump.restype = _I
 _lib.sage_attn_fwd_qk4_dump.argtypes = [_P] * 7 + [_I] * 9 + [_F, _P, _I, _P, _P, _P]
+_lib.sage_quantize_qk4_smooth_q.restype = _I
+_lib.sage_quantize_qk4_smooth_q.argtypes = [_P, _P] + [_I] * 8 + [_P] * 11 + [_SZ, _P]
+_lib.sage_attn_fwd_qk4_smooth_q.restype = _I
+_lib.sage_attn_fwd_qk4_smooth_q.argtypes = [_P] * 11 + [_I] * 9 + [_F, _P]
+_lib.sage_attn_fwd_qk4_smooth_q_dump.restype = _I
+_lib.sage_attn_fwd_qk4_smooth_q_dump.argtypes = [_P] * 11 + [_I] * 9 + [_F, _P, _I, _P, _P, _P]
 _lib.sage_attn_fwd_ex_dump.restype = _I
 _lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
 
@@ -190,6 +197,29 @@ def sage_attn_fwd_qk4_dump(q4_codes, q4_scale, k4_codes, k4_scale, v_codes, v_sc
                            Hkv, Nq, Nkv, d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream):
     return _lib.sage_attn_fwd_qk4_dump(q4_codes, q4_scale, k4_codes, k4_scale, v_codes, v_scale, O, out_dtype, layout,
                                        B, Hq, Hkv, Nq, Nkv, d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
+
+
+def sage_quantize_qk4_smooth_q(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, q4_codes, q4_scale, k4_codes, k4_scale,
+                               k_mean, q_mean, qm_codes, qm_scale, k8_codes, k8_scale, workspace, workspace_bytes,
+                               stream):
+    return _lib.sage_quantize_qk4_smooth_q(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, q4_codes, q4_scale,
+                                           k4_codes, k4_scale, k_mean, q_mean, qm_codes, qm_scale, k8_codes, k8_scale,
+                                           workspace, workspace_bytes, stream)
+
+
+def sage_attn_fwd_qk4_smooth_q(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale, v_codes,
+                               v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, causal, sm_scale, stream):
+    return _lib.sage_attn_fwd_qk4_smooth_q(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes,
+                                           k8_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv, d,
+                                           causal, sm_scale, stream)
+
+
+def sage_attn_fwd_qk4_smooth_q_dump(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale,
+                                    v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, causal, sm_scale,
+                                    sel, n_sel, s_dump, p_dump, stream):
+    return _lib.sage_attn_fwd_qk4_smooth_q_dump(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes,
+                                                k8_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                                                d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
 
 
 # ---------------------------------------------------------------- tensor helpers
@@ -383,10 +413,11 @@ def attn_decode(q, kc, v, causal=True, sm_scale=None, out_dtype=torch.float32, o
     return out
 
 
-def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None):
+def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None, smooth_q=False):
     """4-bit Q and smoothed K (E2M1, a power-of-two scale per 32 channels).
     Returns a dict with q4_codes [B,Hq,Nqp,d/2], q4_scale [B,Hq,Nqp,d/32],
-    k4_codes, k4_scale, k_mean, Nq and Nkv."""
+    k4_codes, k4_scale, k_mean, Nq and Nkv; with ``smooth_q`` also q_mean
+    [B,Hq,Nqp/32,d], qm_codes, qm_scale, k8_codes [B,Hkv,Nkt,d] and k8_scale."""
     B, Hq, Nq, d = _bhnd(Q, layout)
     _, Hkv, Nkv, _ = _bhnd(K, layout)
     dev = Q.device
@@ -399,17 +430,28 @@ def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None):
     wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    _check(sage_quantize_qk4(_ptr(Q), _ptr(K), _DT.get(Q.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv, d,
-                             _ptr(out["q4_codes"]), _ptr(out["q4_scale"]), _ptr(out["k4_codes"]),
-                             _ptr(out["k4_scale"]), _ptr(out["k_mean"]), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    head = (_ptr(Q), _ptr(K), _DT.get(Q.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv, d, _ptr(out["q4_codes"]),
+            _ptr(out["q4_scale"]), _ptr(out["k4_codes"]), _ptr(out["k4_scale"]), _ptr(out["k_mean"]))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if smooth_q:
+        nb = Nqp // 32
+        out.update(q_mean=torch.empty((B, Hq, nb, d), dtype=torch.float32, device=dev),
+                   qm_codes=torch.empty((B, Hq, nb, d), dtype=torch.uint8, device=dev),
+                   qm_scale=torch.empty((B, Hq, nb, d // 32), dtype=torch.uint8, device=dev),
+                   k8_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.uint8, device=dev),
+                   k8_scale=torch.empty((B, Hkv, Nkt, d // 32), dtype=torch.uint8, device=dev))
+        _check(sage_quantize_qk4_smooth_q(*head, _ptr(out["q_mean"]), _ptr(out["qm_codes"]), _ptr(out["qm_scale"]),
+                                          _ptr(out["k8_codes"]), _ptr(out["k8_scale"]), *tail))
+    else:
+        _check(sage_quantize_qk4(*head, *tail))
     out.update(Nq=Nq, Nkv=Nkv)
     return out
 
 
 def attn_fwd_qk4(qk4, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=None, layout="bhnd", stream=None,
                  dump=None):
-    """Attention with 4-bit QK^T: ``qk4`` from quantize_qk4, ``v`` from quantize_v."""
+    """Attention with 4-bit QK^T: ``qk4`` from quantize_qk4 (with or without
+    Q smoothing), ``v`` from quantize_v."""
     B, Hq, _, h2 = qk4["q4_codes"].shape
     d = 2 * h2
     Hkv = qk4["k4_codes"].shape[1]
@@ -420,14 +462,18 @@ def attn_fwd_qk4(qk4, v, causal=False, sm_scale=None, out_dtype=torch.float32, o
     if out is None:
         shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
         out = torch.empty(shape, dtype=out_dtype, device=qk4["q4_codes"].device)
-    args = (_ptr(qk4["q4_codes"]), _ptr(qk4["q4_scale"]), _ptr(qk4["k4_codes"]), _ptr(qk4["k4_scale"]),
-            _ptr(v_codes), _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv, d,
-            int(bool(causal)), float(sm_scale))
+    smooth = "qm_codes" in qk4
+    ops = (_ptr(qk4["q4_codes"]), _ptr(qk4["q4_scale"]), _ptr(qk4["k4_codes"]), _ptr(qk4["k4_scale"]))
+    if smooth:
+        ops += (_ptr(qk4["qm_codes"]), _ptr(qk4["qm_scale"]), _ptr(qk4["k8_codes"]), _ptr(qk4["k8_scale"]))
+    args = ops + (_ptr(v_codes), _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), _layout(layout), B, Hq, Hkv, Nq,
+                  Nkv, d, int(bool(causal)), float(sm_scale))
     if dump is None:
-        _check(sage_attn_fwd_qk4(*args, _stream(stream)))
+        _check((sage_attn_fwd_qk4_smooth_q if smooth else sage_attn_fwd_qk4)(*args, _stream(stream)))
     else:
         sel, s_dump, p_dump = dump
-        _check(sage_attn_fwd_qk4_dump(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
+        fn = sage_attn_fwd_qk4_smooth_q_dump if smooth else sage_attn_fwd_qk4_dump
+        _check(fn(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
     return out
 
 

@@ -44,6 +44,8 @@ class Workload:
     Nkv_: int = 0         # keys (0: N)
     decode: bool = False  # N new queries against a quantized cache of Nkv keys (split over the keys)
     qk4: bool = False     # 4-bit QK^T (E2M1, a power-of-two scale per 32 channels) instead of INT8
+    smooth_q: bool = False  # with qk4: Q smoothing (mean of each 32-query block, restored in FP8)
+    q_bias_var: float = 0.0   # variance of a per-(b, h, channel) bias added to every query
 
     @property
     def Hkv(self):
@@ -96,6 +98,9 @@ WORKLOADS = {
     # the video DiT shape with 4-bit QK^T
     "video-dit-32k-qk4": Workload("video-dit-32k-qk4", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0,
                                   _rsqrt32(128), qk4=True),
+    # the same with a channel bias in Q too (variance 4, like K's), 4-bit QK^T with Q smoothing
+    "video-dit-32k-qk4-qsmooth": Workload("video-dit-32k-qk4-qsmooth", 1, 24, 32768, 128, "bfloat16", False, 128,
+                                          64, 4.0, _rsqrt32(128), qk4=True, smooth_q=True, q_bias_var=4.0),
     # finer quantization granularity: a Q scale per 32 rows, a K scale per 16 keys
     "llm-prefill-4k-causal-fine": Workload("llm-prefill-4k-causal-fine", 4, 32, 4096, 128, "bfloat16", True, 32, 16,
                                            4.0, _rsqrt32(128)),
@@ -127,6 +132,8 @@ def make_inputs(w: Workload, seed=None, device="cpu"):
             for h in range(w.Hkv):
                 ch = rng.choice(w.d, size=w.v_outlier_channels, replace=False)
                 v[b, h][:, ch] *= np.float32(w.v_outlier_scale)
+    if w.q_bias_var:   # drawn last, so the other tensors keep their draws
+        q += rng.standard_normal((w.B, w.H, 1, w.d), dtype=np.float32) * np.float32(math.sqrt(w.q_bias_var))
     out = []
     for a in (q, k, v):
         t = torch.from_numpy(a).to(w.torch_dtype)

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 20 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 23 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -253,3 +253,39 @@ def test_quantize_qk4_rejects(kw, status):
 ])
 def test_attn_fwd_qk4_rejects(kw, status):
     assert _attn4(**kw) == status
+
+
+def _qk4s(**kw):
+    args = dict(Q=A, K=A, in_dtype=1, layout=0, B=1, Hq=4, Hkv=2, Nq=256, Nkv=300, d=128, q4_codes=A, q4_scale=A,
+                k4_codes=A, k4_scale=A, k_mean=A, q_mean=A, qm_codes=A, qm_scale=A, k8_codes=A, k8_scale=A,
+                workspace=A, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return sage.sage_quantize_qk4_smooth_q(**args)
+
+
+def _attn4s(**kw):
+    args = dict(q4_codes=A, q4_scale=A, k4_codes=A, k4_scale=A, qm_codes=A, qm_scale=A, k8_codes=A, k8_scale=A,
+                v_codes=A, v_scale=A, O=A, out_dtype=2, layout=1, B=1, Hq=4, Hkv=2, Nq=256, Nkv=300, d=64, causal=1,
+                sm_scale=0.125, stream=None)
+    args.update(kw)
+    return sage.sage_attn_fwd_qk4_smooth_q(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_mean=None), sage.SAGE_ERR_INVALID_ARG), (dict(k8_scale=None), sage.SAGE_ERR_INVALID_ARG),
+    (dict(qm_codes=A + 4), sage.SAGE_ERR_MISALIGNED), (dict(d=96), sage.SAGE_ERR_UNSUPPORTED),
+    (dict(Hq=3), sage.SAGE_ERR_INVALID_ARG), (dict(workspace_bytes=8), sage.SAGE_ERR_WORKSPACE),
+])
+def test_quantize_qk4_smooth_q_rejects(kw, status):
+    """The five smoothing outputs go together: a null among them is an error
+    (all five null is the plain call, which the GPU tests run)."""
+    assert _qk4s(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qm_codes=None), sage.SAGE_ERR_INVALID_ARG), (dict(k8_codes=None), sage.SAGE_ERR_INVALID_ARG),
+    (dict(qm_scale=A + 8), sage.SAGE_ERR_MISALIGNED), (dict(Nq=400), sage.SAGE_ERR_INVALID_ARG),
+    (dict(out_dtype=7), sage.SAGE_ERR_INVALID_ARG),
+])
+def test_attn_fwd_qk4_smooth_q_rejects(kw, status):
+    assert _attn4s(**kw) == status
