@@ -18,6 +18,17 @@
  *    under "Attention kernel benchmarks" (causal masking changes which blocks are
  *    skipped).
  *
+ * Entry points, by group
+ *  - the path: sage_quantize_qk, sage_quantize_v, sage_attn_fwd (and their
+ *    workspace queries); sage_attn_fwd_dump for tests;
+ *  - the extended shapes (_ex: layouts, grouped heads, Nq != Nkv);
+ *  - decode over a quantized KV cache: sage_quantize_q, sage_quantize_k,
+ *    sage_decode_kv_chunk, sage_attn_decode_workspace_bytes, sage_attn_decode;
+ *  - 4-bit QK^T (the SageAttention3 abstract: attention on FP4 matrix cores):
+ *    sage_quantize_qk4, sage_attn_fwd_qk4(_dump), and with Q smoothing (the
+ *    SageAttention2 abstract) sage_quantize_qk4_smooth_q,
+ *    sage_attn_fwd_qk4_smooth_q(_dump).
+ *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
  *    nothing and keeps no state between calls.  Every pointer must be 16-byte
