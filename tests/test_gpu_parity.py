@@ -672,3 +672,31 @@ def test_qk4_against_the_oracle(name):
         plain = run_gpu_qk4(w, Q, K, V, layout, smooth_q=False)["O"].reshape(-1, w.d)
         print(f"{name}: cosine vs fp64 {cosine(O, ex):.5f} smoothed, {cosine(plain, ex):.5f} plain")
         assert cosine(O, ex) > cosine(plain, ex)
+
+
+@pytest.mark.gpu
+def test_qk4_smoothing_degenerate_cases():
+    """One query per head: its block mean is the row itself, the smoothed
+    codes are all zero and the scores are the mean's term alone (against the
+    oracle).  Q = 0: mean, codes and scores all zero, so O is the plain mean
+    of the dequantized V rows (a closed form)."""
+    base = synth.WORKLOADS["vit-2k-f16"].with_(B=1, H=4, Hkv_=2, N=1, Nkv_=200, smooth_q=True, q_bias_var=4.0)
+    Q, K, V = synth.make_inputs(base)
+    g = run_gpu_qk4(base, Q, K, V)
+    r = orc.quantize_qk4(synth.bits(Q), synth.bits(K), base.dtype_code, smooth_q=True)
+    check_qk4_quant(base, g, r)
+    assert not unpack4(g["q4_codes"])[:, :, 0].any()   # q - mean(q) = +0 for a one-row block
+    vc, vs = orc.quantize_v(synth.bits(V), base.dtype_code)
+    O_ref = orc.attn_rows_qk4(r, vc, vs, False, base.sm_scale)
+    check_smoothed_o(g["O"].reshape(-1, base.d), O_ref, vc, vs, "one-query")
+
+    zq = base.with_(N=64, q_bias_var=0.0)
+    Q, K, V = synth.make_inputs(zq)
+    Q = torch.zeros_like(Q)
+    g = run_gpu_qk4(zq, Q, K, V)
+    assert not g["q_mean"].any() and not g["qm_codes"].any() and not unpack4(g["q4_codes"]).any()
+    vc, vs = orc.quantize_v(synth.bits(V), zq.dtype_code)
+    deq = orc.e4m3_decode(vc) * vs[:, :, None, :].astype(np.float64)        # [B, Hkv, Nkv, d]
+    want = np.repeat(deq.mean(axis=2), zq.H // zq.Hkv, axis=1)              # per query head
+    O = g["O"].reshape(zq.B, zq.H, zq.N, zq.d)
+    assert np.abs(O - want[:, :, None, :]).max() <= 1e-5 * max(1.0, np.abs(want).max())
