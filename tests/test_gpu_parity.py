@@ -700,3 +700,49 @@ def test_qk4_smoothing_degenerate_cases():
     want = np.repeat(deq.mean(axis=2), zq.H // zq.Hkv, axis=1)              # per query head
     O = g["O"].reshape(zq.B, zq.H, zq.N, zq.d)
     assert np.abs(O - want[:, :, None, :]).max() <= 1e-5 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.gpu
+def test_graph_capture_replays_match_eager():
+    """The calls allocate nothing, set no memory and never synchronize, so a
+    prefill step (quantize Q/K, quantize V, attention) and a decode step
+    (quantize the new queries, split-KV attention against a quantized cache)
+    can be captured in a HIP graph.  Every replay, with eager work and
+    synchronizations in between, equals the eager result bit for bit."""
+    sage = _sage()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["llm-prefill-4k-causal"].with_(B=1, H=4, Hkv_=2, N=512)
+    Q, K, V = (t.to(dev) for t in synth.make_inputs(w))
+
+    def prefill():
+        qk = sage.quantize_qk(Q, K, w.blk_q, w.blk_k)
+        vq = sage.quantize_v(V)
+        return sage.attn_fwd(qk, vq, causal=True, sm_scale=w.sm_scale, out_dtype=torch.float32)
+
+    kc = sage.quantize_k(K)
+    vq = sage.quantize_v(V)
+    Qn = Q[:, :, -3:].contiguous()
+
+    def decode():
+        q = sage.quantize_q(Qn)
+        return sage.attn_decode(q, kc, vq, causal=True, sm_scale=w.sm_scale, kv_chunk=128)
+
+    for step in (prefill, decode):
+        ref = step().clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()   # warm up on the side stream before capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = step()
+        for _ in range(3):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), step.__name__
+            eager = step()      # the program's own eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(eager, ref)
