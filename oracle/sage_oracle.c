@@ -20,7 +20,12 @@
  *         "How SageAttention uses quantization for more throughput" (Q, K to
  *         8-bit before the matmul, then precision-aware scaling); "A handful of
  *         variables swing rankings hard" (causal masking changes which blocks are
- *         skipped).
+ *         skipped); "FlashAttention for training and inference: where
+ *         SageAttention fits" (decode against a KV cache is bound by reading
+ *         the cache: the split-KV form).
+ *  [SA3]  The SageAttention3 abstract on the dblp listing: attention on FP4
+ *         matrix cores (the 4-bit QK^T variant).
+ *  [SA2] also: Q smoothing for the low-bit QK^T (the smoothed 4-bit variant).
  * The concrete arithmetic (K smoothing by the per-channel mean, INT8 per-block
  * Q/K, int32 QK^T, fp32 online softmax, FP8 V with per-channel scales, two-level
  * accumulation) is the method statement this build implements; every rounding
