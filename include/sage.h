@@ -22,7 +22,9 @@
  *  - the path: sage_quantize_qk, sage_quantize_v, sage_attn_fwd (and their
  *    workspace queries); sage_attn_fwd_dump for tests;
  *  - the extended shapes (_ex: layouts, grouped heads, Nq != Nkv);
- *  - decode over a quantized KV cache: sage_quantize_q, sage_quantize_k,
+ *  - decode over a quantized KV cache (blog section "FlashAttention for
+ *    training and inference: where SageAttention fits": decode is bound by
+ *    reading the cache): sage_quantize_q, sage_quantize_k,
  *    sage_decode_kv_chunk, sage_attn_decode_workspace_bytes, sage_attn_decode;
  *  - 4-bit QK^T (the SageAttention3 abstract: attention on FP4 matrix cores):
  *    sage_quantize_qk4, sage_attn_fwd_qk4(_dump), and with Q smoothing (the
