@@ -746,3 +746,32 @@ def test_graph_capture_replays_match_eager():
             eager = step()      # the program's own eager work between replays
             torch.cuda.synchronize()
             assert torch.equal(eager, ref)
+
+
+@pytest.mark.gpu
+def test_fp8_conversion_at_every_midpoint():
+    """The V path's FP8 conversion (the hardware convert) on exact e4m3 values,
+    every midpoint between neighbours (ties to even), subnormals and both signs:
+    with 448 in every channel the channel scale is exactly 1, so each code is
+    the conversion of the input itself.  Checked against the oracle's encoder
+    and against torch's CPU float8_e4m3fn conversion."""
+    sage = _sage()
+    mags = np.unique(np.abs(orc.e4m3_decode(np.arange(256, dtype=np.uint8))))
+    mags = mags[np.isfinite(mags) & (mags <= 448)]
+    mids = (mags[1:] + mags[:-1]) / 2
+    vals = np.concatenate([mags, mids, -mags, -mids])
+    assert np.array_equal(vals.astype(np.float16).astype(np.float64), vals)   # all exact in f16
+    d, N = 64, 64 * -(-(len(vals) + 1) // 64)
+    V = np.zeros((1, 1, N, d), np.float32)
+    V[0, 0, 0, :] = 448.0
+    for c in range(d):
+        V[0, 0, 1:1 + len(vals), c] = np.roll(vals, 7 * c)
+    Vt = torch.from_numpy(V).to(torch.float16)
+    vq = sage.quantize_v(Vt.to("cuda:0"))
+    torch.cuda.synchronize()
+    codes = sage.v_codes_to_natural(vq[0]).cpu().numpy()[0, 0]
+    assert np.array_equal(vq[1].cpu().numpy(), np.ones((1, 1, d), np.float32))
+    want_oracle = orc.e4m3_encode(V[0, 0].ravel()).reshape(N, d)
+    want_torch = Vt[0, 0].float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want_oracle)
+    assert np.array_equal(codes, want_torch)
