@@ -8,8 +8,11 @@
 // multiples: the codes are zero-padded to whole tiles, keys at or past Nkv
 // are masked like causal ones, and rows at or past Nq are not stored.
 //
-// LDS: two buffers of {K tile in MFMA order, rows padded to d+16 bytes;
-// V tile channel-major, rows padded to 80 bytes}.
+// LDS: two K tile slots (MFMA order, rows padded to d+16 bytes) and three V
+// tile slots (channel-major, rows padded to 80 bytes), filled by direct
+// global -> LDS copies: K two tiles ahead of use, V one (with Q smoothing also
+// two slots of the FP8 K tile).  Step t computes the scores of tile t+1, the
+// softmax of tile t and the P~V of tile t-1, one barrier per step.
 //
 // Per wave and KV tile:
 //   S^T[64 keys x 32 queries] = K_tile . Q^T          2 x (d/32) v_mfma_i32_32x32x32_i8

@@ -9,6 +9,10 @@
 // quantize_v:  pass 1 = per-chunk V channel maxima; finalize = per-channel
 //              scales and reciprocals; pass 2 = FP8 codes, transposed in
 //              registers into the KV-tile channel-major layout.
+// quantize_qk4: the K mean as above, then 4-bit E2M1 blocks of Q and of the
+//              smoothed K (one thread per token and 32 channels); with Q
+//              smoothing first the block means of 32 queries, and K also in
+//              FP8 blocks.
 #include "common.h"
 #include "launch.h"
 
