@@ -775,3 +775,18 @@ def test_fp8_conversion_at_every_midpoint():
     want_torch = Vt[0, 0].float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(codes, want_oracle)
     assert np.array_equal(codes, want_torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("smooth", [False, True])
+def test_qk4_output_dtypes_round_the_fp32_result(smooth):
+    """The 4-bit variants (plain and Q-smoothed) share the epilogue: f16 and
+    bf16 outputs are the round-to-nearest-even of the fp32 output."""
+    w = synth.WORKLOADS["llm-prefill-4k-causal"].with_(B=1, H=4, Hkv_=2, N=384, smooth_q=smooth,
+                                                       q_bias_var=4.0 if smooth else 0.0)
+    Q, K, V = synth.make_inputs(w)
+    ref = torch.from_numpy(run_gpu_qk4(w, Q, K, V, "bnhd")["O"])
+    for dt in (torch.bfloat16, torch.float16):
+        got = torch.from_numpy(run_gpu_qk4(w, Q, K, V, "bnhd", out_dtype=dt)["O"])
+        exp = ref.to(dt).float()
+        assert torch.equal(got, exp), f"{dt}: {(got != exp).sum().item()} mismatches"
