@@ -256,6 +256,47 @@ def _round_up(n, m):
     return -(-n // m) * m
 
 
+def _expect(t, shape, dtypes, dev, name):
+    """A tensor handed to the library: contiguous, on ``dev``, of ``shape`` and
+    one of ``dtypes`` (the C ABI cannot see buffer sizes, so they are checked
+    here before any pointer is passed)."""
+    if not torch.is_tensor(t) or t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor on {dev}")
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes:
+        raise ValueError(f"{name}: expected shape {tuple(shape)} and dtype in {dtypes}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+
+
+def _workspace(workspace, nbytes, dev):
+    """The caller's workspace (any contiguous tensor on ``dev``), or a new one."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if not torch.is_tensor(workspace) or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace: expected a contiguous tensor on {dev}")
+    return workspace
+
+
+_OUT_DTYPES = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _out(out, B, H, N, d, out_dtype, layout, dev):
+    """O as given (checked) or new: [B,H,N,d] or [B,N,H,d]."""
+    shape = (B, H, N, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, N, H, d)
+    if out is None:
+        return torch.empty(shape, dtype=out_dtype, device=dev)
+    _expect(out, shape, _OUT_DTYPES, dev, "out")
+    return out
+
+
+def _check_v(v, B, Hkv, Nkt, d, dev):
+    """(v_codes, v_scale) from quantize_v for B x Hkv heads of Nkt (tile-padded) keys."""
+    v_codes, v_scale = v
+    kt = sage_kv_tile()
+    _expect(v_codes, (B, Hkv, Nkt // kt, d, kt), (torch.uint8,), dev, "v_codes")
+    _expect(v_scale, (B, Hkv, d), (torch.float32,), dev, "v_scale")
+    return v_codes, v_scale
+
+
 def _plain(B, Hq, Hkv, Nq, Nkv, layout):
     return _layout(layout) == SAGE_LAYOUT_BHND and Hq == Hkv and Nq == Nkv
 
@@ -268,8 +309,8 @@ def quantize_qk(Q, K, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream
     the true lengths "Nq" and "Nkv"."""
     B, Hq, Nq, d = _bhnd(Q, layout)
     Bk, Hkv, Nkv, dk = _bhnd(K, layout)
-    if (Bk, dk) != (B, d) or K.dtype != Q.dtype:
-        raise ValueError("Q and K must have the same batch, head dim and dtype")
+    if (Bk, dk) != (B, d) or K.dtype != Q.dtype or K.device != Q.device:
+        raise ValueError("Q and K must have the same batch, head dim, dtype and device")
     dev = Q.device
     Nqp, Nkt = _round_up(Nq, 128), _round_up(Nkv, sage_kv_tile())
     out = dict(q_codes=torch.empty((B, Hq, Nqp, d), dtype=torch.int8, device=dev),
@@ -277,9 +318,7 @@ def quantize_qk(Q, K, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream
                k_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
                k_scale=torch.empty((B, Hkv, Nkt // blk_k), dtype=torch.float32, device=dev),
                k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
-    wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), dev)
     ptrs = (_ptr(out["q_codes"]), _ptr(out["q_scale"]), _ptr(out["k_codes"]), _ptr(out["k_scale"]),
             _ptr(out["k_mean"]), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     dt = _DT.get(Q.dtype, -1)
@@ -301,9 +340,7 @@ def quantize_v(V, layout="bhnd", workspace=None, stream=None):
     kt = sage_kv_tile()
     v_codes = torch.empty((B, H, -(-N // kt), d, kt), dtype=torch.uint8, device=dev)
     v_scale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    wsb = sage_quantize_v_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, sage_quantize_v_workspace_bytes(B, H, N, d), dev)
     rest = (_ptr(v_codes), _ptr(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
     dt = _DT.get(V.dtype, -1)
@@ -330,14 +367,13 @@ def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=No
     O is [B,Hq,Nq,d] (or [B,Nq,Hq,d] with layout="bnhd").  ``dump`` = (sel int32
     tensor, s_dump, p_dump) routes through the dump entry points."""
     B, Hq, _, d = qk["q_codes"].shape
-    Hkv = qk["k_codes"].shape[1]
+    Hkv, Nkt = qk["k_codes"].shape[1], qk["k_codes"].shape[2]
     Nq, Nkv = qk["Nq"], qk["Nkv"]
-    v_codes, v_scale = v
+    dev = qk["q_codes"].device
+    v_codes, v_scale = _check_v(v, B, Hkv, Nkt, d, dev)
     if sm_scale is None:
         sm_scale = default_sm_scale(d)
-    if out is None:
-        shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
-        out = torch.empty(shape, dtype=out_dtype, device=qk["q_codes"].device)
+    out = _out(out, B, Hq, Nq, d, out_dtype, layout, dev)
     ops = (_ptr(qk["q_codes"]), _ptr(qk["q_scale"]), _ptr(qk["k_codes"]), _ptr(qk["k_scale"]), _ptr(v_codes),
            _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1))
     tail = (d, qk["blk_q"], qk["blk_k"], int(bool(causal)), float(sm_scale))
@@ -376,9 +412,7 @@ def quantize_k(K, blk_k=64, layout="bhnd", workspace=None, stream=None):
     out = dict(k_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
                k_scale=torch.empty((B, Hkv, Nkt // blk_k), dtype=torch.float32, device=dev),
                k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
-    wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), dev)
     _check(sage_quantize_k(_ptr(K), _DT.get(K.dtype, -1), _layout(layout), B, Hkv, Nkv, d, blk_k,
                            _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -392,20 +426,19 @@ def attn_decode(q, kc, v, causal=True, sm_scale=None, out_dtype=torch.float32, o
     quantized cache: ``kc`` from quantize_k (or quantize_qk), ``v`` = (v_codes,
     v_scale) from quantize_v.  kv_chunk 0 = the library's default split."""
     B, Hq, _, d = q["q_codes"].shape
-    Hkv = kc["k_codes"].shape[1]
+    Bk, Hkv, Nkt, dk = kc["k_codes"].shape
+    if (Bk, dk) != (B, d) or kc["k_codes"].device != q["q_codes"].device:
+        raise ValueError("queries and cache must have the same batch, head dim and device")
     Nq, Nkv = q["Nq"], kc["Nkv"]
-    v_codes, v_scale = v
+    dev = q["q_codes"].device
+    v_codes, v_scale = _check_v(v, B, Hkv, Nkt, d, dev)
     if sm_scale is None:
         sm_scale = default_sm_scale(d)
     if kv_chunk == 0:
         kv_chunk = sage_decode_kv_chunk(B, Hq, Hkv, Nq, Nkv, d)
-    dev = q["q_codes"].device
-    if out is None:
-        shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
-        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    out = _out(out, B, Hq, Nq, d, out_dtype, layout, dev)
     wsb = sage_attn_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, kv_chunk)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, wsb, dev)
     _check(sage_attn_decode(_ptr(q["q_codes"]), _ptr(q["q_scale"]), _ptr(kc["k_codes"]), _ptr(kc["k_scale"]),
                             _ptr(v_codes), _ptr(v_scale), _ptr(out), _DT.get(out.dtype, -1), _layout(layout), B, Hq,
                             Hkv, Nq, Nkv, d, q["blk_q"], kc["blk_k"], int(bool(causal)), float(sm_scale), kv_chunk,
@@ -419,7 +452,9 @@ def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None, smooth_q=Fals
     k4_codes, k4_scale, k_mean, Nq and Nkv; with ``smooth_q`` also q_mean
     [B,Hq,Nqp/32,d], qm_codes, qm_scale, k8_codes [B,Hkv,Nkt,d] and k8_scale."""
     B, Hq, Nq, d = _bhnd(Q, layout)
-    _, Hkv, Nkv, _ = _bhnd(K, layout)
+    Bk, Hkv, Nkv, dk = _bhnd(K, layout)
+    if (Bk, dk) != (B, d) or K.dtype != Q.dtype or K.device != Q.device:
+        raise ValueError("Q and K must have the same batch, head dim, dtype and device")
     dev = Q.device
     Nqp, Nkt = _round_up(Nq, 128), _round_up(Nkv, sage_kv_tile())
     out = dict(q4_codes=torch.empty((B, Hq, Nqp, d // 2), dtype=torch.uint8, device=dev),
@@ -427,9 +462,7 @@ def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None, smooth_q=Fals
                k4_codes=torch.empty((B, Hkv, Nkt, d // 2), dtype=torch.uint8, device=dev),
                k4_scale=torch.empty((B, Hkv, Nkt, d // 32), dtype=torch.uint8, device=dev),
                k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
-    wsb = sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), dev)
     head = (_ptr(Q), _ptr(K), _DT.get(Q.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv, d, _ptr(out["q4_codes"]),
             _ptr(out["q4_scale"]), _ptr(out["k4_codes"]), _ptr(out["k4_scale"]), _ptr(out["k_mean"]))
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -454,14 +487,13 @@ def attn_fwd_qk4(qk4, v, causal=False, sm_scale=None, out_dtype=torch.float32, o
     Q smoothing), ``v`` from quantize_v."""
     B, Hq, _, h2 = qk4["q4_codes"].shape
     d = 2 * h2
-    Hkv = qk4["k4_codes"].shape[1]
+    Hkv, Nkt = qk4["k4_codes"].shape[1], qk4["k4_codes"].shape[2]
     Nq, Nkv = qk4["Nq"], qk4["Nkv"]
-    v_codes, v_scale = v
+    dev = qk4["q4_codes"].device
+    v_codes, v_scale = _check_v(v, B, Hkv, Nkt, d, dev)
     if sm_scale is None:
         sm_scale = default_sm_scale(d)
-    if out is None:
-        shape = (B, Hq, Nq, d) if _layout(layout) == SAGE_LAYOUT_BHND else (B, Nq, Hq, d)
-        out = torch.empty(shape, dtype=out_dtype, device=qk4["q4_codes"].device)
+    out = _out(out, B, Hq, Nq, d, out_dtype, layout, dev)
     smooth = "qm_codes" in qk4
     ops = (_ptr(qk4["q4_codes"]), _ptr(qk4["q4_scale"]), _ptr(qk4["k4_codes"]), _ptr(qk4["k4_scale"]))
     if smooth:

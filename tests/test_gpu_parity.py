@@ -790,3 +790,37 @@ def test_qk4_output_dtypes_round_the_fp32_result(smooth):
         got = torch.from_numpy(run_gpu_qk4(w, Q, K, V, "bnhd", out_dtype=dt)["O"])
         exp = ref.to(dt).float()
         assert torch.equal(got, exp), f"{dt}: {(got != exp).sum().item()} mismatches"
+
+
+@pytest.mark.gpu
+def test_binding_rejects_mismatched_tensors_before_launching():
+    """The C ABI cannot see buffer sizes, so the tensor helpers check every
+    tensor they pass: V codes of another length, an output of the wrong shape
+    or layout, a workspace on the host, Q/K of different dtypes, queries and a
+    cache of different batches.  Each raises before any kernel is launched;
+    the matching call still runs."""
+    sage = _sage()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["llm-prefill-4k-causal"].with_(B=2, H=2, N=256)
+    Q, K, V = (t.to(dev) for t in synth.make_inputs(w))
+    qk = sage.quantize_qk(Q, K)
+    vq = sage.quantize_v(V)
+    with pytest.raises(ValueError):
+        sage.attn_fwd(qk, sage.quantize_v(V[:, :, :64].contiguous()))           # fewer keys than K
+    with pytest.raises(ValueError):
+        sage.attn_fwd(qk, vq, out=torch.empty(16, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):                                              # [B,N,H,d] view, not contiguous
+        sage.attn_fwd(qk, vq, out=torch.empty(2, 256, 2, 128, device=dev).transpose(1, 2))
+    with pytest.raises(ValueError):
+        sage.quantize_qk(Q, K, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        sage.quantize_qk4(Q, K.to(torch.float16))
+    with pytest.raises(ValueError):
+        sage.attn_fwd_qk4(sage.quantize_qk4(Q, K), sage.quantize_v(V[:1].contiguous()))
+    kc = sage.quantize_k(K)
+    with pytest.raises(ValueError):
+        sage.attn_decode(sage.quantize_q(Q[:1, :, -2:].contiguous()), kc, vq)
+    out = torch.empty((2, 2, 256, 128), dtype=torch.bfloat16, device=dev)
+    assert sage.attn_fwd(qk, vq, causal=True, out=out) is out
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
