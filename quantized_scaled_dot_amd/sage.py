@@ -288,6 +288,16 @@ def _out(out, B, H, N, d, out_dtype, layout, dev):
     return out
 
 
+def _check_dump(dump, Nkv, dev):
+    """(sel int32 [n], s_dump int32 [n,128,Nkv], p_dump uint8 [n,128,Nkv]) of the dump calls."""
+    sel, s_dump, p_dump = dump
+    n = sel.numel()
+    _expect(sel, (n,), (torch.int32,), dev, "sel")
+    _expect(s_dump, (n, 128, Nkv), (torch.int32,), dev, "s_dump")
+    _expect(p_dump, (n, 128, Nkv), (torch.uint8,), dev, "p_dump")
+    return sel, s_dump, p_dump
+
+
 def _check_v(v, B, Hkv, Nkt, d, dev):
     """(v_codes, v_scale) from quantize_v for B x Hkv heads of Nkt (tile-padded) keys."""
     v_codes, v_scale = v
@@ -383,7 +393,7 @@ def attn_fwd(qk, v, causal=False, sm_scale=None, out_dtype=torch.float32, out=No
         fn = sage_attn_fwd if plain else sage_attn_fwd_ex
         _check(fn(*ops, *shape, *tail, _stream(stream)))
     else:
-        sel, s_dump, p_dump = dump
+        sel, s_dump, p_dump = _check_dump(dump, Nkv, dev)
         fn = sage_attn_fwd_dump if plain else sage_attn_fwd_ex_dump
         _check(fn(*ops, *shape, *tail, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
     return out
@@ -503,7 +513,7 @@ def attn_fwd_qk4(qk4, v, causal=False, sm_scale=None, out_dtype=torch.float32, o
     if dump is None:
         _check((sage_attn_fwd_qk4_smooth_q if smooth else sage_attn_fwd_qk4)(*args, _stream(stream)))
     else:
-        sel, s_dump, p_dump = dump
+        sel, s_dump, p_dump = _check_dump(dump, Nkv, dev)
         fn = sage_attn_fwd_qk4_smooth_q_dump if smooth else sage_attn_fwd_qk4_dump
         _check(fn(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
     return out
