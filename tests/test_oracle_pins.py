@@ -60,6 +60,10 @@ def test_e4m3_encode_midpoints_ties_to_even_and_saturation():
         xs += [v, np.nextafter(v, np.float32(1e30)), np.nextafter(v, np.float32(-1e30)),
                mid, np.nextafter(mid, np.float32(1e30)), np.nextafter(mid, np.float32(-1e30))]
     xs += [np.float32(v) for v in (448, 449, 463.99, 464, 1e6, 3e38, 0, 2 ** -10, 3 * 2 ** -11, 2 ** -11, 1e-30)]
+    # the whole saturating range: past the largest finite value every input
+    # maps to 448, including the band where the next binade's codes would be NaN
+    big = np.concatenate([np.arange(448.0, 512.0, 0.125), 2.0 ** np.arange(9, 128)]).astype(np.float32)
+    xs += list(big) + list(np.nextafter(big, np.float32(1e30))) + list(np.nextafter(big, np.float32(0)))
     xs = np.array(xs, np.float32)
     xs = np.concatenate([xs, -xs])
     got = orc.e4m3_encode(xs)
@@ -326,6 +330,36 @@ def test_v_power_of_two_scales_output_exactly():
     _, (vc1, vs1), O1 = _run(w, Q, K, V * 4)
     assert np.array_equal(vc0, vc1) and np.array_equal(vs1, vs0 * 4)
     assert np.array_equal(O1, O0 * 4)
+
+
+def test_identity_v_exposes_p_tilde_on_the_fp8_grid():
+    """With V the identity (one key per channel, one 64-key tile) row i of O is
+    P~_i . diag(1) scaled by one common factor, so O shows the values that enter
+    the P~V product: the row's largest is 2^8 (the running-max offset) and every
+    other value must be an e4m3 value, the FP8 rounding of
+    2^(8 + s_ij - max_j s_ij) for the exact dequantized scores s."""
+    rng = np.random.default_rng(11)
+    N = d = 64
+    q = rng.standard_normal((1, 1, N, d)) * 0.8
+    k = rng.standard_normal((1, 1, N, d)) * 0.8
+    v = np.eye(N, d)[None, None]
+    args = dict(dtype=0, blk_q=64, blk_k=64, causal=False, sm_scale=0.125)
+    qk, (vc, vs), (O, P) = orc.run(_f16_bits(q), _f16_bits(k), _f16_bits(v), want_p=True, **args)
+    O = O.reshape(N, d).astype(np.float64)
+    ratio = 256.0 * O / O.max(axis=1, keepdims=True)
+    grid = orc.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    nearest = grid[np.abs(ratio[..., None] - grid).argmin(axis=-1)]
+    assert np.all(np.abs(ratio - nearest) <= 1e-6 * nearest)
+    # the dump's FP8 codes are exactly what entered the product
+    assert np.array_equal(orc.e4m3_decode(P.reshape(N, N)), nearest)
+    # and they round the exact exponentials of the dequantized INT8 scores
+    qc = qk["q_codes"].reshape(N, d).astype(np.int64)
+    kc = qk["k_codes"].reshape(N, d).astype(np.int64)
+    s = (qc @ kc.T) * float(qk["q_scale"].ravel()[0]) * float(qk["k_scale"].ravel()[0]) * 0.125 * math.log2(math.e)
+    p = 2.0 ** (8.0 + s - s.max(axis=1, keepdims=True))
+    assert np.all(np.abs(nearest - p) <= p / 8 + 2.0 ** -9)
+    # random scores put most values off the grid: the check above has teeth
+    assert np.mean(np.abs(p - nearest) > 1e-3 * p) > 0.5
 
 
 def test_head_permutation_equivariance():
