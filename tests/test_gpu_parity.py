@@ -143,6 +143,40 @@ def cosine(a, b):
     return float(a @ b / np.sqrt((a @ a) * (b @ b)))
 
 
+# The FP8 matrix instruction sums each group of 8 products of its 64-key block inside a window
+# of about 13 bits below the group's largest product (measured; the oracle sums the block
+# exactly).  An element of O can then differ from the oracle by up to 7 * 2^-13 of
+# A = sum_j P^_j |V^_jc| delta_c / sum_j P^_j, the P^-weighted mean of |V| in that channel
+# (observed: 2^-12.9 of A on an outlier channel with |O| = 24).  The bar is the larger of the
+# absolute 2e-3 and 2^-11 * A, so only elements whose weighted |V| exceeds 4 (outlier
+# channels) are allowed more than 2e-3.
+INNER_REL = 2.0 ** -11
+
+
+def weighted_abs_v(P_rows, rows, vc, vs, w):
+    """A[i, c] of the flat query rows `rows` (over B*Hq*Nq) from their FP8 P~ codes
+    P_rows [len(rows), Nkv] and the V codes / scales of their K/V heads."""
+    vcf, vsf = vc.reshape(-1, w.Nkv, w.d), vs.reshape(-1, w.d)
+    g = w.H // w.Hkv
+    bks = np.array([(r // w.N // w.H) * w.Hkv + (r // w.N % w.H) // g for r in rows])
+    out = np.empty((len(rows), w.d))
+    for bk in np.unique(bks):
+        sel = np.flatnonzero(bks == bk)
+        p = orc.e4m3_decode(P_rows[sel])
+        out[sel] = (p @ np.abs(orc.e4m3_decode(vcf[bk]))) * vsf[bk] / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def check_o_inner(O_rows, O_ref, A, name=""):
+    """Element-wise bar max(O_TOL, INNER_REL * A) (see INNER_REL)."""
+    err = np.abs(O_rows.astype(np.float64) - O_ref)
+    bar = np.maximum(O_TOL, INNER_REL * A)
+    worst = np.unravel_index(int(np.argmax(err / bar)), err.shape)
+    print(f"{name}: max |O - oracle| {err.max():.3g}; worst element {worst}: error {err[worst]:.3g}, "
+          f"bar {bar[worst]:.3g}, A {A[worst]:.3g}")
+    assert (err <= bar).all(), f"|O - oracle| {err[worst]:.3g} above the bar {bar[worst]:.3g}"
+
+
 # ------------------------------------------------------------------ small cases: every row
 SMALL = {
     "tiny-f16-256": dict(),
@@ -419,8 +453,33 @@ def test_full_size_workload(name):
         check_p_codes(p_got, P_ref[at: at + len(r)], visible)
         at += len(r)
     O = g["O"].reshape(-1, w.d)
-    err = np.abs(O[rows] - O_ref[:len(rows)])
-    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"
+    check_o_inner(O[rows], O_ref[:len(rows)], weighted_abs_v(P_ref[:len(rows)], rows, vc, vs, w), name)
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
+    assert cosine(O[rows], ex) >= 0.995
+
+
+# ------------------------------------------------------------------ the longest supported sequence
+MAX_LEN = {
+    # one head at the length limit of the C ABI (2^19 tokens): causal d = 128 with V outliers, and a
+    # ragged non-causal d = 64 length just below it
+    "max-len-causal-d128": dict(base="long-prefill-128k-causal", H=1, N=1 << 19),
+    "max-len-ragged-d64": dict(base="vit-2k-f16", B=1, H=1, N=(1 << 19) - 37),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(MAX_LEN))
+def test_maximum_length(name):
+    kw = dict(MAX_LEN[name])
+    w = synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw)
+    Q, K, V = synth.make_inputs(w)
+    g = run_gpu(w, Q, K, V)
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    check_quant_bit_exact(g, qk, vc, vs)
+    rows = _sample_rows(w, np.random.default_rng(5), n_rand=16)
+    O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows, want_p=True)
+    O = g["O"].reshape(-1, w.d)
+    check_o_inner(O[rows], O_ref, weighted_abs_v(P_ref, rows, vc, vs, w), name)
     ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
     assert cosine(O[rows], ex) >= 0.995
 
