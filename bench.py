@@ -117,6 +117,32 @@ def cpu_baseline(w, Q, K, V, budget_s=20.0):
                       f"({t_step:.0f} s)"}
 
 
+MFMA_PROBE_WG, MFMA_PROBE_ITERS = 512, 20000   # about 10 ms: 2 workgroups per CU, 2^20 ops a wave per iteration
+
+
+def mfma_sustained(sage, stream, attn_tops, reps=3):
+    """Sustained dense INT8/FP8 matrix rate from the library's probe (the attention kernel's
+    matrix instructions per KV tile at its occupancy, and nothing else), timed with HIP events on
+    the stream it runs on; the attention kernel's fraction of it; and the clock that rate implies
+    at the published 5.0 P op/s for 2.4 GHz."""
+    ops = 4.0 * 2 ** 20 * MFMA_PROBE_WG * MFMA_PROBE_ITERS
+    ms = []
+    for i in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        st = sage.sage_probe_mfma_peak(MFMA_PROBE_WG, MFMA_PROBE_ITERS, None, stream.cuda_stream)
+        b.record(stream)
+        if st != sage.SAGE_OK:
+            raise RuntimeError(sage.sage_status_string(st))
+        torch.cuda.synchronize()
+        if i:   # the first launch warms up
+            ms.append(a.elapsed_time(b))
+    t = float(np.median(ms))
+    tops = ops / (t * 1e-3) / 1e12
+    return {"tops": round(tops, 1), "attn_frac": round(attn_tops / tops, 4),
+            "implied_clock_ghz": round(2.4 * tops / MFMA_PEAK_TOPS, 3), "probe_ms": round(t, 3)}
+
+
 def decode_rows(w):
     return w.B * w.H * w.N
 
@@ -309,6 +335,12 @@ def main():
     log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "
         f"({100 * quant_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {quant_act / (quant_avg * 1e-3) / 1e9:.0f} GB/s moved")
 
+    sustained = None
+    if not w.qk4:
+        sustained = mfma_sustained(sage, stream, attn_tops)
+        log(f"[bench] matrix-core probe: {sustained['tops']:.1f} TOPS sustained (implied clock "
+            f"{sustained['implied_clock_ghz']:.2f} GHz); attention kernel at {100 * sustained['attn_frac']:.1f}% of it")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)...")
@@ -333,6 +365,7 @@ def main():
         "quantize": {"ms": round(quant_avg, 4), "bound": "hbm", "algorithmic_bytes": quant_alg,
                      "bytes_moved": quant_act, "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(quant_gbs / HBM_PEAK_GBS, 4)},
+        "mfma_sustained": sustained,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

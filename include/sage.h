@@ -369,6 +369,21 @@ int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_s
                                     int Nq, int Nkv, int d, int causal, float sm_scale, const int32_t* sel, int n_sel,
                                     int32_t* s_dump, uint8_t* p_dump, void* stream);
 
+/*
+ * sage_probe_mfma_peak -- a measurement aid, not a step of the method: each of
+ * `workgroups` workgroups of 256 threads (2 per CU, the attention kernel's
+ * occupancy at d = 128) runs `iters` iterations of the matrix instructions
+ * one d = 128 KV tile costs a wave of the attention kernel (8 INT8
+ * 32x32x32 and 4 FP8 32x32x64 instructions, 2^20 operations a wave) and
+ * nothing else.  Operation count 4 * 2^20 * workgroups * iters; divided by
+ * the launch's time it gives the sustained dense INT8/FP8 matrix rate of the
+ * chip.  sink: null, or device memory for workgroups * 256 ints (4-byte
+ * aligned) that receives a checksum per thread.  Enqueued on `stream`;
+ * errors: SAGE_ERR_INVALID_ARG (workgroups outside 1..65536, iters outside
+ * 1..2^24), SAGE_ERR_MISALIGNED, SAGE_ERR_HIP.
+ */
+int sage_probe_mfma_peak(int workgroups, int iters, int* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

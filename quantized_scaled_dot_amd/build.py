@@ -26,7 +26,8 @@ COMMON = [
 # The attention kernel never produces or tests NaNs (inputs are finite by
 # contract); not honouring them lets floor+convert fuse into v_cvt_flr_i32_f32.
 # The host-side argument checks in api.hip do rely on NaN semantics.
-SOURCES = {"quant.hip": [], "attn.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"], "api.hip": []}
+SOURCES = {"quant.hip": [], "attn.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"], "api.hip": [],
+           "peak.hip": []}
 NOISE = "is not a recognized feature for this target"
 
 

@@ -1,0 +1,58 @@
+// Matrix-core throughput probe for gfx950 (a measurement aid next to the
+// attention kernels, not a step of the method).  Every wave issues, per loop
+// iteration, the matrix instructions one d = 128 KV tile costs a wave of the
+// attention kernel: 8 v_mfma_i32_32x32x32_i8 (the scores) and 4
+// v_mfma_scale_f32_32x32x64_f8f6f4 in FP8 form (P~V), on six independent
+// accumulators and with no other work.  The measured rate is the sustained
+// dense INT8/FP8 rate of the chip at the clock it holds under that load; the
+// attention kernel's rate can be read against it as well as against the
+// published peak.
+#include <hip/hip_runtime.h>
+
+#include "../../include/sage.h"
+#include "common.h"
+
+namespace sage {
+
+// 2 workgroups of 4 waves per CU: the attention kernel's occupancy at d = 128.
+__global__ __launch_bounds__(256, 2) void mfma_peak_kernel(int iters, int* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  // operands that depend on the lane (nothing to fold); FP8 bytes 0x38 = 1.0
+  const v4i a = {lane, lane * 3 + 1, lane * 5 + 2, lane * 7 + 3};
+  const v4i b = {lane ^ 21, lane ^ 42, lane + 9, lane + 17};
+  const v8i a8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x30383830, 0x38303038, 0x38383838, 0x38303830};
+  const v8i b8 = {0x38383838, 0x30303030, 0x38383838, 0x30303030, 0x38383838, 0x30303030, 0x38383838, 0x30303030};
+  v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  v16f f0 = {}, f1 = {};
+  for (int i = 0; i < iters; i++) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+    f0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, f0, 0, 0, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+    f1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, f1, 0, 0, 0, 127, 0, 127);
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+    f0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, f0, 0, 0, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+    f1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, f1, 0, 0, 0, 127, 0, 127);
+  }
+  // the accumulators are live: a checksum per thread when a sink is given
+  if (sink) {
+    int s = 0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) s += c0[e] + c1[e] + c2[e] + c3[e] + (int)f0[e] + (int)f1[e];
+    sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+  }
+}
+
+}  // namespace sage
+
+extern "C" int sage_probe_mfma_peak(int workgroups, int iters, int* sink, void* stream) {
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24)) return SAGE_ERR_INVALID_ARG;
+  if (((uintptr_t)sink & 3u) != 0) return SAGE_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(sage::mfma_peak_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}

@@ -26,7 +26,7 @@ SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_byt
            "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
            "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode",
            "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
-           "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump")
+           "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump", "sage_probe_mfma_peak")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -80,6 +80,8 @@ _lib.sage_attn_fwd_qk4_smooth_q_dump.restype = _I
 _lib.sage_attn_fwd_qk4_smooth_q_dump.argtypes = [_P] * 11 + [_I] * 9 + [_F, _P, _I, _P, _P, _P]
 _lib.sage_attn_fwd_ex_dump.restype = _I
 _lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
+_lib.sage_probe_mfma_peak.restype = _I
+_lib.sage_probe_mfma_peak.argtypes = [_I, _I, _P, _P]
 
 
 class SageError(RuntimeError):
@@ -100,6 +102,10 @@ def sage_status_string(status):
 
 def sage_kv_tile():
     return _lib.sage_kv_tile()
+
+
+def sage_probe_mfma_peak(workgroups, iters, sink=None, stream=None):
+    return _lib.sage_probe_mfma_peak(workgroups, iters, sink, stream)
 
 
 def sage_quantize_qk_workspace_bytes(B, H, N, d):

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 23 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 24 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -30,6 +30,14 @@ def test_status_strings_and_constants():
     for s in range(1, 6):
         assert sage.sage_status_string(s).startswith("SAGE_ERR_")
     assert sage.sage_kv_tile() == 64
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    assert sage.sage_probe_mfma_peak(0, 10) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_probe_mfma_peak(65537, 10) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_probe_mfma_peak(512, 0) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_probe_mfma_peak(512, (1 << 24) + 1) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_probe_mfma_peak(512, 10, 4097) == sage.SAGE_ERR_MISALIGNED
 
 
 def test_workspace_sizes():
