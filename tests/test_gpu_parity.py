@@ -461,9 +461,12 @@ def test_full_size_workload(name):
 # ------------------------------------------------------------------ the longest supported sequence
 MAX_LEN = {
     # one head at the length limit of the C ABI (2^19 tokens): causal d = 128 with V outliers, and a
-    # ragged non-causal d = 64 length just below it
+    # ragged non-causal d = 64 length just below it; the 4-bit scores at the limit; and decode of four
+    # queries of two grouped heads against a cache at the limit
     "max-len-causal-d128": dict(base="long-prefill-128k-causal", H=1, N=1 << 19),
     "max-len-ragged-d64": dict(base="vit-2k-f16", B=1, H=1, N=(1 << 19) - 37),
+    "max-len-qk4": dict(base="video-dit-32k-qk4", H=1, N=1 << 19),
+    "max-len-decode": dict(base="decode-128k-gqa-4q", B=1, H=2, Hkv_=1, Nkv_=1 << 19),
 }
 
 
@@ -473,6 +476,31 @@ def test_maximum_length(name):
     kw = dict(MAX_LEN[name])
     w = synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw)
     Q, K, V = synth.make_inputs(w)
+    if w.qk4:
+        g = run_gpu_qk4(w, Q, K, V)
+        r = orc.quantize_qk4(synth.bits(Q), synth.bits(K), w.dtype_code, smooth_q=w.smooth_q)
+        vc, vs = orc.quantize_v(synth.bits(V), w.dtype_code)
+        check_qk4_quant(w, g, r)
+        rows = _sample_rows(w, np.random.default_rng(5), n_rand=16)
+        O_ref = orc.attn_rows_qk4(r, vc, vs, w.causal, w.sm_scale, rows=rows)
+        O = g["O"].reshape(-1, w.d)
+        assert np.abs(O[rows] - O_ref).max() <= O_TOL
+        ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale,
+                                 rows=rows)
+        assert cosine(O[rows], ex) >= QK4_COS
+        return
+    if w.decode:
+        g = run_gpu_decode(w, Q, K, V, 0)
+        qk, vc, vs = run_oracle_quant(w, Q, K, V)
+        check_quant_bit_exact(g, qk, vc, vs)
+        rows = np.arange(w.B * w.H * w.N)
+        O_ref = orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk=g["kv_chunk"],
+                                    rows=rows)
+        assert np.abs(g["O"].reshape(-1, w.d) - O_ref).max() <= O_TOL
+        ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale,
+                                 rows=rows)
+        assert cosine(g["O"].reshape(-1, w.d), ex) >= 0.995
+        return
     g = run_gpu(w, Q, K, V)
     qk, vc, vs = run_oracle_quant(w, Q, K, V)
     check_quant_bit_exact(g, qk, vc, vs)
