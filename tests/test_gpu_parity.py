@@ -512,6 +512,29 @@ def test_maximum_length(name):
     assert cosine(O[rows], ex) >= 0.995
 
 
+@pytest.mark.timeout(600)
+def test_offsets_beyond_2gib():
+    """33 copies of one 2^19-token head: each input tensor spans 2.2 GB, so the last heads sit past
+    every 32-bit byte offset.  Every head's codes, scales and O must equal head 0's bit for bit,
+    and head 0 matches the oracle."""
+    H = 33
+    w1 = synth.WORKLOADS["vit-2k-f16"].with_(name="one-head", B=1, H=1, N=1 << 19, causal=True)
+    w = w1.with_(name="offsets-beyond-2gib", H=H)
+    Q1, K1, V1 = synth.make_inputs(w1)
+    Q, K, V = (t.repeat(1, H, 1, 1) for t in (Q1, K1, V1))
+    assert Q.numel() * Q.element_size() > (1 << 31)
+    g = run_gpu(w, Q, K, V)
+    for key in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean", "v_codes", "v_scale", "O"):
+        a = g[key]
+        assert all(np.array_equal(a[:, h], a[:, 0]) for h in range(1, H)), key
+    one = {k: (v[:, :1] if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    qk, vc, vs = run_oracle_quant(w1, Q1, K1, V1)
+    check_quant_bit_exact(one, qk, vc, vs)
+    rows = _sample_rows(w1, np.random.default_rng(9), n_rand=8)
+    O_ref = orc.attn_rows(qk, vc, vs, w1.blk_q, w1.blk_k, w1.causal, w1.sm_scale, rows=rows)
+    assert np.abs(one["O"].reshape(-1, w1.d)[rows] - O_ref).max() <= O_TOL
+
+
 # ------------------------------------------------------------------ decode (split-KV) over a quantized cache
 DECODE = {
     # name: (workload overrides, kv_chunk, layout)
