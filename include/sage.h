@@ -177,7 +177,7 @@ int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, in
  *   O_blk  = sum_j e4m3(P~_j) * v_code_j                   (FP8 matrix cores)
  *   O_acc  = alpha * O_acc + O_blk;  m = m'
  *   O[i,c] = O_acc[c] * v_scale[c] / l
- * exp2 is the matrix core's companion fp32 exp2 (v_exp_f32, about 1 ulp), so
+ * exp2 is the hardware's fp32 exp2 instruction (v_exp_f32, about 1 ulp), so
  *   an FP8 code of P~ may differ by one step from one computed with exp2
  *   rounded once from the exact value.
  * In:  the outputs of sage_quantize_qk (q_codes, q_scale, k_codes, k_scale)
@@ -377,8 +377,8 @@ int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_s
  * 32x32x32 and 4 FP8 32x32x64 instructions, 2^20 operations a wave) and
  * nothing else.  Operation count 4 * 2^20 * workgroups * iters; divided by
  * the launch's time it gives the sustained dense INT8/FP8 matrix rate of the
- * chip.  sink: null, or device memory for workgroups * 256 ints (4-byte
- * aligned) that receives a checksum per thread.  Enqueued on `stream`;
+ * chip.  sink: null, or device memory for workgroups * 256 ints that
+ * receives a checksum per thread.  Enqueued on `stream`;
  * errors: SAGE_ERR_INVALID_ARG (workgroups outside 1..65536, iters outside
  * 1..2^24), SAGE_ERR_MISALIGNED, SAGE_ERR_HIP.
  */

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256, 2) void mfma_peak_kernel(int iters, int* __res
 
 extern "C" int sage_probe_mfma_peak(int workgroups, int iters, int* sink, void* stream) {
   if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24)) return SAGE_ERR_INVALID_ARG;
-  if (((uintptr_t)sink & 3u) != 0) return SAGE_ERR_MISALIGNED;
+  if (((uintptr_t)sink & 15u) != 0) return SAGE_ERR_MISALIGNED;
   (void)hipGetLastError();
   hipLaunchKernelGGL(sage::mfma_peak_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, iters, sink);
   return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
