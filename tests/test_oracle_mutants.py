@@ -112,6 +112,12 @@ MUTANTS = [
     ("e2m1 without the magnitude 6", "for (int k = 1; k < 8; k++) {", "for (int k = 1; k < 7; k++) {", 1),
     ("P~ not quantized to FP8", "acc += x->vdec[ph[jj]] * x->vdec[",
      "acc += (double)pt[jj] * x->vdec[", 1),
+    # third batch: split merge, block edge cases, Q-smoothing blocks
+    ("split merge: row sums not weighted", "L = fmaf(w, lc[c], L);", "L = L + lc[c];", 1),
+    ("split merge: chunks without a visible key kept", "      if (!vis[c]) continue;\n", "", 1),
+    ("all-zero MX blocks get scale byte 127", "    *scale = 0;\n", "    *scale = 127;\n", 2),
+    ("Q-smoothing blocks of 16 rows", "const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;",
+     "const int n0 = 16 * blk, n = (N - n0 < 16) ? N - n0 : 16;", 1),
 ]
 
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")

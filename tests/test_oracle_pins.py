@@ -642,6 +642,30 @@ def test_split_chunks_without_visible_keys_are_left_out():
     assert a @ b / np.sqrt((a @ a) * (b @ b)) >= 0.999
 
 
+def test_split_row_with_one_visible_key_and_a_very_negative_score():
+    """Causal and square: query 0 sees key 0 alone, so its output is key 0's dequantized V row
+    whatever the score.  The score is made thousands below zero (in log2 units), so the row's
+    running max is too: the chunks without a visible key must still stay out of the merge, whose
+    weight exp2(m_c - m*) would overflow for them."""
+    rng = np.random.default_rng(41)
+    N, d, sm = 256, 64, 50.0
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    ks0 = k[0, 0, 0] - k[0, 0].mean(axis=0)               # key 0 after smoothing
+    q[0, 0, 0] = -4.0 * ks0 / np.abs(ks0).max()           # query 0 points against it
+    qk = orc.quantize_qk(_f16_bits(q), _f16_bits(k), 0, 64, 64)
+    vc, vs = orc.quantize_v(_f16_bits(v), 0)
+    s0 = int(qk["q_codes"][0, 0, 0].astype(np.int64) @ qk["k_codes"][0, 0, 0].astype(np.int64))
+    u0 = s0 * float(qk["q_scale"][0, 0, 0]) * float(qk["k_scale"][0, 0, 0]) * sm * math.log2(math.e)
+    assert u0 < -1000
+    O = orc.attn_rows_split(qk, vc, vs, 64, 64, True, sm, kv_chunk=64, rows=np.array([0], np.int64))
+    expect = orc.e4m3_decode(vc[0, 0, 0]) * vs[0, 0].astype(np.float64)
+    assert np.isfinite(O).all()
+    # P~ = exp2(fma(S, c2, -(m' - 8))) with m' the fp32-rounded score: 2^(8 + e) with |e| at most
+    # half an fp32 ulp of |u0|; P^ still rounds to 256 but l = P~, so O = expect * 2^-e
+    e = 2.0 ** (math.floor(math.log2(-u0)) - 24)
+    assert np.all(np.abs(O[0] - expect) <= (e * math.log(2) * 1.01 + 2e-7) * np.abs(expect) + 1e-12)
+
+
 @pytest.mark.parametrize("chunk", [64, 128, 320])
 def test_split_against_fp64(chunk):
     Q, K, V, qk, vc, vs = _split_case(Hq=8, Hkv=2, Nq=4, Nkv=1000, seed=34)
