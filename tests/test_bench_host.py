@@ -22,6 +22,8 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 @pytest.mark.parametrize("workload,kernel,sources", [
     ("video-dit-32k", "attn_fwd_kernel", bench.KERNEL_SOURCES),
+    ("video-dit-32k-qk4", "attn_fwd_kernel", bench.KERNEL_SOURCES),
+    ("video-dit-32k-qk4-qsmooth", "attn_fwd_kernel", bench.KERNEL_SOURCES),
     ("decode-32k-gqa", "decode_chunk_kernel", bench.DECODE_SOURCES),
 ])
 def test_counter_summaries_match_the_current_kernel_source(workload, kernel, sources):
