@@ -1,11 +1,13 @@
 """Build libsage.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
 
-Each source is compiled to an object with the common flags plus its own, then
-the objects are linked into one shared library.
+Each source is compiled to an object with the common flags plus its own (the
+attention source once per part of its kernel instances), in parallel, then the
+objects are linked into one shared library.
 """
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -28,6 +30,8 @@ COMMON = [
 # The host-side argument checks in api.hip do rely on NaN semantics.
 SOURCES = {"quant.hip": [], "attn.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"], "api.hip": [],
            "peak.hip": []}
+# the attention kernel instances are split into this many compile units (SAGE_ATTN_PART in attn.hip)
+ATTN_PARTS = 8
 NOISE = "is not a recognized feature for this target"
 
 
@@ -42,13 +46,27 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = []
+def _jobs():
+    jobs = []
     for src, flags in SOURCES.items():
-        obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        _run([HIPCC, *COMMON, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        if src == "attn.hip":
+            for p in range(ATTN_PARTS):
+                jobs.append((src, [*flags, f"-DSAGE_ATTN_PART={p}"], f"attn_p{p}.o"))
+        else:
+            jobs.append((src, flags, src.replace(".hip", ".o")))
+    return jobs
+
+
+def build(verbose: bool = False, extra=(), workers: int = 0) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = _jobs()
+    cmds = [[HIPCC, *COMMON, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(OBJ, obj)]
+            for src, flags, obj in jobs]
+    workers = workers or min(len(cmds), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    objs = [os.path.join(OBJ, obj) for _, _, obj in jobs]
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB

@@ -623,18 +623,52 @@ static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, h
   else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, 0>(k, grid, out, dump, st);
   else launch4<D, CAUSAL, RAGGED, false, 0>(k, grid, out, dump, st);
 }
-template <int D>
-static void launch2(const AttnK& k, int grid, bool causal, bool ragged, int variant, int out, bool dump,
-                    hipStream_t st) {
-  if (causal) {
-    if (ragged) launch3<D, true, true>(k, grid, variant, out, dump, st);
-    else launch3<D, true, false>(k, grid, variant, out, dump, st);
-  } else {
-    if (ragged) launch3<D, false, true>(k, grid, variant, out, dump, st);
-    else launch3<D, false, false>(k, grid, variant, out, dump, st);
-  }
-}
+// The kernel instances are compiled in eight parts, one per (head size,
+// causal, ragged) combination, so that the build can run them in parallel:
+// SAGE_ATTN_PART = 0..7 compiles part p only (D = 128 for p < 4, causal for
+// p % 4 < 2, ragged for odd p); part 0 also holds the dispatcher.  Without
+// the macro everything is compiled in one unit.
+#ifndef SAGE_ATTN_PART
+#define SAGE_ATTN_PART -1
+#endif
+#define SAGE_PART_DEF(P, D, C, R)                                                                         \
+  void launch_attn_part##P(const AttnK& k, int grid, int variant, int out, bool dump, hipStream_t st)
+SAGE_PART_DEF(0, 128, true, false);
+SAGE_PART_DEF(1, 128, true, true);
+SAGE_PART_DEF(2, 128, false, false);
+SAGE_PART_DEF(3, 128, false, true);
+SAGE_PART_DEF(4, 64, true, false);
+SAGE_PART_DEF(5, 64, true, true);
+SAGE_PART_DEF(6, 64, false, false);
+SAGE_PART_DEF(7, 64, false, true);
+#define SAGE_PART_BODY(P, D, C, R)                                                                        \
+  SAGE_PART_DEF(P, D, C, R) { launch3<D, C, R>(k, grid, variant, out, dump, st); }
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 0
+SAGE_PART_BODY(0, 128, true, false)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 1
+SAGE_PART_BODY(1, 128, true, true)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 2
+SAGE_PART_BODY(2, 128, false, false)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 3
+SAGE_PART_BODY(3, 128, false, true)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 4
+SAGE_PART_BODY(4, 64, true, false)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 5
+SAGE_PART_BODY(5, 64, true, true)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 6
+SAGE_PART_BODY(6, 64, false, false)
+#endif
+#if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 7
+SAGE_PART_BODY(7, 64, false, true)
+#endif
 
+#if SAGE_ATTN_PART <= 0
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   AttnK k;
   k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
@@ -649,8 +683,12 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.q4_codes = a.q4_codes; k.q4_scale = a.q4_scale; k.k4_codes = a.k4_codes; k.k4_scale = a.k4_scale;
   k.qm_codes = a.qm_codes; k.qm_scale = a.qm_scale; k.k8_codes = a.k8_codes; k.k8_scale = a.k8_scale;
   const int variant = a.q4_codes ? (a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
-  if (a.d == 128) launch2<128>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
-  else launch2<64>(k, grid, a.causal, ragged, variant, a.out_dtype, dump, st);
+  const int part = (a.d == 128 ? 0 : 4) + (a.causal ? 0 : 2) + (ragged ? 1 : 0);
+  void (*const parts[8])(const AttnK&, int, int, int, bool, hipStream_t) = {
+      launch_attn_part0, launch_attn_part1, launch_attn_part2, launch_attn_part3,
+      launch_attn_part4, launch_attn_part5, launch_attn_part6, launch_attn_part7};
+  parts[part](k, grid, variant, a.out_dtype, dump, st);
 }
+#endif
 
 }  // namespace sage
