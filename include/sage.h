@@ -98,8 +98,8 @@ size_t sage_quantize_qk_workspace_bytes(int B, int H, int N, int d);
  * (SageAttention abstract; blog section "How SageAttention uses quantization
  * for more throughput".)
  *   k_mean[b,h,c] = mean over all N tokens of K[b,h,:,c], computed from the
- *     exact int64 sum of trunc(clamp(k, +-2^20) * 2^24) (order-free), divided in
- *     fp64 and rounded to fp32.
+ *     exact int64 sum of trunc(clamp(k, +-2^19) * 2^24) (order-free; at most
+ *     2^62 in magnitude for N <= 2^19), divided in fp64 and rounded to fp32.
  *   Smoothed K: ks = fp32(k) - k_mean (fp32).
  *   Blocks of blk_q tokens of Q / blk_k tokens of ks, all d channels: a = max|x|;
  *     scale = a/127, r = 127/a (fp32, correctly rounded), code = rint(x*r)

@@ -12,10 +12,11 @@ SRC = os.path.join(HERE, "sage_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
-    """Compile ``src`` into the shared library ``out`` (atomically replaced)."""
+def build(verbose: bool = False, src: str = SRC, out: str = LIB, extra=()) -> str:
+    """Compile ``src`` into the shared library ``out`` (atomically replaced); ``extra``
+    flags are appended (the sanitizer build of the tests uses them)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", out + ".tmp", src, "-lm"]
+           "-Wall", "-Wextra", *extra, "-o", out + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

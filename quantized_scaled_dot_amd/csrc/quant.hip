@@ -123,9 +123,10 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
 
 // ---------------------------------------------------------------------------
 // Per-channel fixed-point sums of K over one chunk of kStatChunk tokens:
-// s_c = sum_t trunc(clamp(k, +-2^20) * 2^24).  Each term is an integer below
-// 2^44; a thread adds at most 32 of them in fp64 (exact below 2^53), converts
-// once to int64, and the threads' int64 sums are combined through LDS.
+// s_c = sum_t trunc(clamp(k, +-2^19) * 2^24).  Each term is an integer of at
+// most 2^43; a thread adds at most 32 of them in fp64 (exact below 2^53),
+// converts once to int64, and the threads' int64 sums are combined through
+// LDS.  With at most 2^19 tokens a head's sum stays within 2^62.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_bf16, InRows in, int nchunk, int lin,
@@ -145,7 +146,7 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
   auto add_row = [&](const v4i& raw) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const float x = fminf(fmaxf(half_of(raw, e, is_bf16), -1048576.0f), 1048576.0f);
+      const float x = fminf(fmaxf(half_of(raw, e, is_bf16), -524288.0f), 524288.0f);
       s[e] += (double)__builtin_truncf(x * 16777216.0f);   // exact product, exact sum
     }
   };

@@ -50,6 +50,8 @@ MUTANTS = [
     ("mx8 block exponent off by one", "int e = (int)floor(log2((double)a)) - 7;",
      "int e = (int)floor(log2((double)a)) - 8;", 1),
     # K smoothing
+    ("k mean clamp 2^20 overflows int64 at the length limit", "KMEAN_CLAMP = 524288.0;",
+     "KMEAN_CLAMP = 1048576.0;", 1),
     ("k mean divides by N+1", "mu[c] = (float)(((double)s * 0x1p-24) / (double)N);",
      "mu[c] = (float)(((double)s * 0x1p-24) / (double)(N + 1));", 1),
     ("k mean added, not subtracted", "buf[(size_t)t * d + c] = load_in(Kh, idx, dtype) - mu[c];",

@@ -172,6 +172,21 @@ def test_kmean_constant_channels_and_bf16_tiny_values():
         assert np.array_equal(mu[0, 0], expect)
 
 
+def test_kmean_at_the_length_limit_with_saturated_channels():
+    """N = 2^19 tokens (the C ABI's limit) with channels far beyond the fixed-point clamp of
+    2^19 on every token: each term is 2^43, so the int64 sum is exactly +-2^62 (no overflow)
+    and the mean is the clamp value itself; ordinary channels keep their exact mean."""
+    N, d = 1 << 19, 4
+    k = np.zeros((1, 1, N, d), np.float32)
+    k[..., 0] = 2.0 ** 100          # bfloat16 keeps it; far past the clamp
+    k[..., 1] = -3.0e38             # near the bfloat16 maximum
+    k[..., 2] = 2.0 ** 19           # exactly at the clamp
+    k[..., 3] = np.where(np.arange(N) % 2 == 0, 1.5, -0.5)
+    mu, sums = orc.kmean(_bf16_bits(k), 1)
+    assert sums[0, 0].tolist() == [2 ** 62, -(2 ** 62), 2 ** 62, (N // 2) * 2 ** 24]
+    assert mu[0, 0].tolist() == [2.0 ** 19, -(2.0 ** 19), 2.0 ** 19, 0.5]
+
+
 # ------------------------------------------------------------------ Q/K block quantizer
 def _quantize(B=2, H=2, N=256, d=64, blk_q=64, blk_k=64, seed=4, dtype=0, scale=1.0):
     rng = np.random.default_rng(seed)
