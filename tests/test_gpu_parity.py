@@ -2,9 +2,10 @@
 same seeded inputs.
 
 Bar: bit-exact K means, INT8 Q/K codes and scales, FP8 V codes and scales
-and int32 QK^T tiles; fp32 O within max-abs 2e-3 of the oracle (on the large
-shapes max(2e-3, INNER_REL * A) per element, for the FP8 instruction's inner
-sum window; see INNER_REL); cosine similarity to fp64 exact attention >= 0.995.  FP8 codes of P~: the kernel's
+and int32 QK^T tiles; fp32 O within max-abs 2e-3 of the oracle (only the
+single heads at the 2^19-token length limit take max(2e-3, INNER_REL * A) per
+element, for the FP8 instruction's inner sum window; see INNER_REL); cosine
+similarity to fp64 exact attention >= 0.995.  FP8 codes of P~: the kernel's
 exp2 is the hardware fp32 exp2 (within one ulp; the oracle rounds the exact
 value once), so a code may differ by one e4m3 step where P~ lies within an ulp
 of a rounding tie: at most P_FLIP_FRAC of the visible codes, all others equal.
@@ -152,7 +153,10 @@ def cosine(a, b):
 # A = sum_j P^_j |V^_jc| delta_c / sum_j P^_j, the P^-weighted mean of |V| in that channel
 # (observed: 2^-12.9 of A on an outlier channel with |O| = 24).  The bar is the larger of the
 # absolute 2e-3 and 2^-11 * A, so only elements whose weighted |V| exceeds 4 (outlier
-# channels) are allowed more than 2e-3.
+# channels) are allowed more than 2e-3.  It is used only for the single heads at the 2^19-token
+# length limit (outside the five stated workloads, which are held to the plain 2e-3): there a
+# 2^19-key row with x8 V outlier channels differed from the oracle by 3.06e-3 at |O| = 23.6 with
+# every P~ code equal, a known exceedance of 2e-3 that this bar records.
 INNER_REL = 2.0 ** -11
 
 
@@ -446,17 +450,39 @@ def test_full_size_workload(name):
     g = run_gpu(w, Q, K, V, dump_tiles=tiles)
     qk, vc, vs = run_oracle_quant(w, Q, K, V)
     check_quant_bit_exact(g, qk, vc, vs)
+    # The kernel instance that serves users (and that bench.py times) has no dump stores: run it on
+    # the same device codes, in fp32 and in the input dtype, and check it against the oracle.
+    sage = _sage()
+    O_prod = sage.attn_fwd(g["qk_dev"], g["vq_dev"], causal=w.causal, sm_scale=w.sm_scale, out_dtype=torch.float32)
+    O_user = sage.attn_fwd(g["qk_dev"], g["vq_dev"], causal=w.causal, sm_scale=w.sm_scale, out_dtype=w.torch_dtype)
+    torch.cuda.synchronize()
+    O = O_prod.cpu().numpy().reshape(-1, w.d)
+    assert np.array_equal(O.view(np.uint32), g["O"].reshape(-1, w.d).view(np.uint32)), \
+        "the instance without dump stores gives other O bits than the dump instance"
+    assert torch.equal(O_user.cpu().view(torch.int16), O_prod.cpu().to(w.torch_dtype).view(torch.int16)), \
+        f"{w.dtype} output is not the round-to-nearest-even cast of the fp32 O"
+    del O_prod, O_user
     rows = _sample_rows(w, np.random.default_rng(123))
     dumps = list(check_dump(w, g, qk, tiles))
     dump_rows = np.concatenate([r for r, _, _ in dumps])
+    # one whole head where the oracle finishes it in seconds (N * Nkv * d <= 2^31: the tiny, 4k
+    # causal, ViT, ragged and finer-block workloads)
+    head_rows = np.arange(0)
+    if w.N * w.Nkv * w.d <= 2 ** 31:
+        bh = (w.B * w.H) // 2
+        head_rows = bh * w.N + np.arange(w.N)
     O_ref, P_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale,
-                                 rows=np.concatenate([rows, dump_rows]), want_p=True)
+                                 rows=np.concatenate([rows, dump_rows, head_rows]), want_p=True)
     at = len(rows)
     for r, p_got, visible in dumps:
         check_p_codes(p_got, P_ref[at: at + len(r)], visible)
         at += len(r)
-    O = g["O"].reshape(-1, w.d)
-    check_o_inner(O[rows], O_ref[:len(rows)], weighted_abs_v(P_ref[:len(rows)], rows, vc, vs, w), name)
+    all_rows = np.concatenate([rows, dump_rows, head_rows])
+    err = np.abs(O[all_rows].astype(np.float64) - O_ref)
+    worst = np.unravel_index(int(err.argmax()), err.shape)
+    print(f"{name}: {len(all_rows)} rows ({len(dump_rows)} of the dumped tiles, {len(head_rows)} of one whole "
+          f"head): max |O - oracle| {err.max():.3g} at row {all_rows[worst[0]]}, channel {worst[1]}")
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g} at row {all_rows[worst[0]]}"
     ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
     assert cosine(O[rows], ex) >= 0.995
 
@@ -513,6 +539,30 @@ def test_maximum_length(name):
     check_o_inner(O[rows], O_ref, weighted_abs_v(P_ref, rows, vc, vs, w), name)
     ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale, rows=rows)
     assert cosine(O[rows], ex) >= 0.995
+
+
+@pytest.mark.timeout(300)
+def test_k_mean_at_the_length_limit_with_saturated_channels():
+    """2^19 tokens with channels far past the fixed-point clamp on every token: the int64 channel
+    sums reach +-2^62 without overflowing; K mean, codes and scales equal the oracle's bit for bit."""
+    w = synth.WORKLOADS["vit-2k-f16"].with_(name="kmean-saturated", B=1, H=1, N=1 << 19, dtype="bfloat16")
+    Q, K, V = synth.make_inputs(w)
+    K = K.clone()
+    K[..., 0] = 2.0 ** 100
+    K[..., 1] = -3.0e38
+    K[..., 2] = 2.0 ** 19
+    sage = _sage()
+    qk = sage.quantize_qk(Q.cuda(), K.cuda(), w.blk_q, w.blk_k)
+    torch.cuda.synchronize()
+    ref = orc.quantize_qk(synth.bits(Q), synth.bits(K), w.dtype_code, w.blk_q, w.blk_k)
+    km = qk["k_mean"].cpu().numpy()
+    assert km[0, 0, :3].tolist() == [2.0 ** 19, -(2.0 ** 19), 2.0 ** 19]
+    assert np.array_equal(km.view(np.uint32), ref["k_mean"].view(np.uint32))
+    for key in ("k_codes", "q_codes"):
+        assert np.array_equal(qk[key].cpu().numpy()[:, :, :w.N], ref[key]), key
+    for key in ("k_scale", "q_scale"):
+        got = qk[key].cpu().numpy()[:, :, :ref[key].shape[2]]
+        assert np.array_equal(got.view(np.uint32), ref[key].view(np.uint32)), key
 
 
 @pytest.mark.timeout(600)
