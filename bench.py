@@ -6,7 +6,11 @@ fused attention kernel.  Inputs are resident in HBM before timing starts.
 
 Metric: attention TOPS = 4*B*H*N^2*d / t (halved for causal) with t the
 wall-clock time of one step.  The JSON line also carries the attention
-kernel's own rate against the dense INT8/FP8 matrix-core peak (roofline) and
+kernel's own rate against the dense INT8/FP8 matrix-core peak (roofline, on
+the mean of the per-step HIP-event timings; attn_kernel_ms is their median,
+with the mean and p95 beside it), the peak allocated device memory, the shader
+clock read with
+amd-smi while the attention kernel runs back to back, and
 the CPU oracle timed on a bounded sample of the same workload, and the
 quantize passes' achieved HBM bandwidth (algorithmic bytes: 2 read + 1 written
 per element of Q, K and V; the statistics passes read K and V a second time).
@@ -50,6 +54,70 @@ DECODE_SOURCES = ("quantized_scaled_dot_amd/csrc/decode.hip", "quantized_scaled_
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def _mhz_values(obj, path=""):
+    """Every (key path, MHz) pair of an amd-smi / rocm-smi JSON document whose path names the
+    graphics (shader) clock."""
+    out = []
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            out += _mhz_values(v, f"{path}/{k}".lower())
+    elif isinstance(obj, list):
+        for i, v in enumerate(obj):
+            out += _mhz_values(v, f"{path}/{i}")
+    else:
+        comps = path.split("/")
+        skip = any(x in c for c in comps for x in ("min", "max", "locked", "level", "sleep"))
+        named = any("sclk" in c for c in comps) or (any("gfx" in c for c in comps) and any("clk" in c for c in comps))
+        digits = "".join(ch if (ch.isdigit() or ch == ".") else " " for ch in str(obj)).split()
+        if digits and named and not skip:
+            try:
+                out.append((path, float(digits[0])))
+            except ValueError:
+                pass
+    return out
+
+
+def read_sclk_mhz():
+    """Current shader clock of GPU 0 in MHz (amd-smi, else rocm-smi), or None."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "--json"], ["rocm-smi", "-d", "0", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            vals = [v for p, v in _mhz_values(json.loads(r.stdout)) if 100 <= v <= 5000]
+        except Exception:   # tool missing, not JSON, no such field: try the next one
+            continue
+        if vals:
+            return max(vals)   # several XCD entries: the graphics clock is the same for all
+    return None
+
+
+def sample_sclk(run, seconds=1.5):
+    """Keep the GPU busy with run() (enqueue-only, on the bench stream) for about `seconds` while
+    another thread reads the shader clock; returns {"samples", "median", "min", "max"} in MHz or None."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is None:
+                return
+            samples.append(v)
+
+    th = threading.Thread(target=reader, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    return {"samples": len(samples), "median_mhz": float(np.median(samples)), "min_mhz": min(samples),
+            "max_mhz": max(samples)}
 
 
 def kernel_source_sha(sources=KERNEL_SOURCES):
@@ -207,7 +275,9 @@ def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
     t = time.perf_counter() - t0
     dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
     ms_step = t * 1e3 / args.steps
-    dec_avg = float(np.mean(dec_ms))
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    dec_mean = float(np.mean(dec_ms))
+    dec_avg = float(np.median(dec_ms))   # the p50 is the headline decode time
     value = w.ops / (ms_step * 1e-3) / 1e12
     # algorithmic bytes of one decode call: every K/V code and scale once per group of 32 query rows
     # of a K/V head, the Q codes and scales, O
@@ -217,10 +287,15 @@ def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
     q_bytes = B * H * N * d + B * H * -(-N // w.blk_q) * 4
     o_bytes = B * H * N * d * torch.tensor([], dtype=w.torch_dtype).element_size()
     alg = kv_bytes + q_bytes + o_bytes
-    gbs = alg / (dec_avg * 1e-3) / 1e9
-    log(f"[bench] decode step {ms_step:.3f} ms; decode call avg {dec_avg:.4f} ms p50 {np.median(dec_ms):.4f} "
+    gbs = alg / (dec_mean * 1e-3) / 1e9   # roofline: the average launch duration
+    log(f"[bench] decode step {ms_step:.3f} ms; decode call p50 {dec_avg:.4f} ms mean {dec_mean:.4f} "
         f"p95 {np.percentile(dec_ms, 95):.4f}: {gbs:.0f} GB/s of {alg / 1e6:.1f} MB algorithmic "
-        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); split {chunk} keys")
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s); split {chunk} keys; peak allocated "
+        f"{peak_mem / 2 ** 20:.0f} MiB")
+    q_keep = sage.quantize_q(Qd, w.blk_q)
+    sclk = sample_sclk(lambda: sage.attn_decode(q_keep, kc, vq, causal=w.causal, sm_scale=w.sm_scale, out=out,
+                                                kv_chunk=chunk, workspace=ws))
+    log(f"[bench] shader clock while the decode kernels run: {sclk}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)...")
@@ -234,6 +309,11 @@ def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
                    "in_dtype": w.dtype, "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_chunk": chunk,
                    "parallelism": "none (1 GPU)"},
         "decode_ms": round(dec_avg, 5),
+        "decode_ms_p50": round(dec_avg, 5),
+        "decode_ms_mean": round(dec_mean, 5),
+        "decode_ms_p95": round(float(np.percentile(dec_ms, 95)), 5),
+        "peak_allocated_bytes": int(peak_mem),
+        "sclk_during_decode": sclk,
         "roofline": {"bound": "hbm", "kernel": "decode_chunk_kernel + decode_merge_kernel", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, "decode_chunk_kernel", DECODE_SOURCES)},
@@ -255,7 +335,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path shards over (batch, head) with no "
-              "communication, and this build runs and reports the single-GPU share.", file=sys.stderr)
+              "communication, and this benchmark runs and reports the single-GPU share.", file=sys.stderr)
         sys.exit(2)
 
     from quantized_scaled_dot_amd import sage
@@ -312,13 +392,17 @@ def main():
     attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     quant_ms = [e[2].elapsed_time(e[0]) for e in evs]
     ms_step = t * 1e3 / args.steps
+    peak_mem = torch.cuda.max_memory_allocated(dev)
     attn_avg = float(np.mean(attn_ms))
+    attn_p50 = float(np.median(attn_ms))
+    attn_p95 = float(np.percentile(attn_ms, 95))
     value = w.ops / (ms_step * 1e-3) / 1e12
-    attn_tops = w.ops / (attn_avg * 1e-3) / 1e12
+    attn_tops = w.ops / (attn_avg * 1e-3) / 1e12       # roofline: the average launch duration
+    attn_tops_p50 = w.ops / (attn_p50 * 1e-3) / 1e12
     peak = (QK4S_PEAK_TOPS if w.smooth_q else QK4_PEAK_TOPS) if w.qk4 else MFMA_PEAK_TOPS
-    log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel avg {attn_avg:.3f} ms "
-        f"p50 {np.median(attn_ms):.3f} p95 {np.percentile(attn_ms, 95):.3f} ({attn_tops:.1f} TOPS, "
-        f"{100 * attn_tops / peak:.1f}% of peak {peak:.0f})")
+    log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel p50 {attn_p50:.3f} ms "
+        f"mean {attn_avg:.3f} p95 {attn_p95:.3f} ({attn_tops_p50:.1f} TOPS at p50, {attn_tops:.1f} at the mean: "
+        f"{100 * attn_tops / peak:.1f}% of peak {peak:.0f}); peak allocated {peak_mem / 2 ** 20:.0f} MiB")
 
     q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
     if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below
@@ -334,6 +418,17 @@ def main():
     quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
     log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "
         f"({100 * quant_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {quant_act / (quant_avg * 1e-3) / 1e9:.0f} GB/s moved")
+
+    def attn_only():
+        if w.qk4:
+            sage.attn_fwd_qk4(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
+        else:
+            sage.attn_fwd(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
+
+    q_keep = ((sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q) if w.qk4
+               else sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)), sage.quantize_v(Vd, workspace=ws_v))
+    sclk = sample_sclk(attn_only)
+    log(f"[bench] shader clock while the attention kernel runs: {sclk}")
 
     sustained = None
     if not w.qk4:
@@ -355,9 +450,14 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "Hkv": Hkv, "Nkv": Nkv, "d": d, "causal": w.causal,
                    "in_dtype": w.dtype,
                    "blk_q": w.blk_q, "blk_k": w.blk_k, "kv_tile": sage.sage_kv_tile(), "parallelism": "none (1 GPU)"},
-        "attn_kernel_ms": round(attn_avg, 4),
-        "attn_kernel_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),
-        "attn_tops": round(attn_tops, 3),
+        "attn_kernel_ms": round(attn_p50, 4),
+        "attn_kernel_ms_p50": round(attn_p50, 4),
+        "attn_kernel_ms_mean": round(attn_avg, 4),
+        "attn_kernel_ms_p95": round(attn_p95, 4),
+        "attn_tops": round(attn_tops_p50, 3),
+        "attn_tops_mean": round(attn_tops, 3),
+        "peak_allocated_bytes": int(peak_mem),
+        "sclk_during_attention": sclk,
         "frac_of_mfma_peak_step": round(value / peak, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tops, 3),
                      "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(attn_tops / peak, 4),
