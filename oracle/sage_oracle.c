@@ -480,9 +480,17 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int B, int Hq
 /*   c2_j  = RN(RN(dQ * dK_j) * s2),  s2 = RN(sm_scale * log2 e)             */
 /*   u_j   = RN(float(S_j) * c2_j);  m' = max(m, max_j u_j)                  */
 /*   alpha = exp2f(RN(m - m'))   (0 on the first visited tile)               */
-/*   P~_j  = exp2f(fma(float(S_j), c2_j, -RN(m' - 8)))  (P~ scaled by 2^8)  */
-/*   l     = fma(alpha, l, sum_j P~_j)               (fp32 state)            */
-/*   P^_j  = E(P~_j)                                 (FP8 e4m3)              */
+/*   INT8 scores, with B = 1.5 * 2^23 (B + S_j is exact in fp32):           */
+/*     K_j   = RN(B * c2_j + RN(m' - 8))        (one fused multiply-add)     */
+/*     P~_j  = exp2f(RN((B + S_j) * c2_j - K_j)) (one fused multiply-add)    */
+/*     i.e. exp2 of RN(S_j c2_j - (m' - 8)) with the offset m' - 8 rounded   */
+/*     to fp32 at the magnitude of B c2_j (a shift of the whole tile's       */
+/*     exponents by at most one unit of S_j times c2_j)                      */
+/*     rowsum = RN(sum_j dec(P^_j))              (the FP8 codes, exact sum)  */
+/*   4-bit scores: P~_j = exp2f(fma(S_j, c2_j, -RN(m' - 8)));                */
+/*     rowsum = sum_j P~_j                      (fp32, ascending keys)       */
+/*   l     = fma(alpha, l, rowsum)               (fp32 state)                */
+/*   P^_j  = E(P~_j)                             (FP8 e4m3; P~ scaled by 2^8) */
 /*   Oblk_c = sum_j dec(P^_j) dec(v^_jc)             (inner level; exact     */
 /*                                                    products, summed in    */
 /*                                                    fp64, rounded to fp32) */
@@ -495,6 +503,9 @@ void oracle_qk_int32(const int8_t* q_codes, const int8_t* k_codes, int B, int Hq
 /* [nrows, Nkv], 0 where a key is not visible.                               */
 /* ------------------------------------------------------------------------ */
 static const float LOG2E_F = 0x1.715476p+0f;   /* RN(log2 e) */
+/* Offset of the INT8 scores in the exponent argument: 1.5 * 2^23, so that   */
+/* B + S is an integer in [2^23, 2^24) for every |S| < 2^21, exact in fp32.  */
+static const float SCORE_BIAS = 12582912.0f;
 
 /* One query row against the keys of one K/V head (shared by the two entry  */
 /* points below).                                                            */
@@ -590,12 +601,20 @@ static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, 
     float alpha = first ? 0.0f : oracle_exp2f(m - mnew);
     float mm = mnew - 8.0f;
     float rowsum = 0.0f;
+    double code_sum = 0.0;
     for (int jj = 0; jj < nvis; jj++) {
-      pt[jj] = oracle_exp2f(fmaf(S[jj], c2[jj], -mm));
-      rowsum += pt[jj];
+      if (x->q4) {
+        pt[jj] = oracle_exp2f(fmaf(S[jj], c2[jj], -mm));
+        rowsum += pt[jj];
+      } else {
+        const float K = fmaf(SCORE_BIAS, c2[jj], mm);
+        pt[jj] = oracle_exp2f(fmaf(SCORE_BIAS + S[jj], c2[jj], -K));
+      }
       ph[jj] = oracle_e4m3_encode(pt[jj]);
+      code_sum += x->vdec[ph[jj]];
       if (prow) prow[j0 + jj] = ph[jj];
     }
+    if (!x->q4) rowsum = (float)code_sum;   /* exact: at most 2^10 codes per tile */
     for (int c = 0; c < d; c++) {
       double acc = 0.0;
       for (int jj = 0; jj < nvis; jj++) acc += x->vdec[ph[jj]] * x->vdec[x->v[(size_t)(j0 + jj) * d + c]];

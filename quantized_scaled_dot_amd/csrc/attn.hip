@@ -18,9 +18,12 @@
 //   S^T[64 keys x 32 queries] = K_tile . Q^T          2 x (d/32) v_mfma_i32_32x32x32_i8
 //   (transposed so that each lane holds one query row: lane l owns query l%32
 //    and 32 of the 64 keys; lanes l and l^32 share a row)
+//   (the accumulators start at the bit pattern of B = 1.5 * 2^23, so each
+//    int32 result read as fp32 is exactly B + S: no conversion per score)
 //   row max on the int32 scores, dequantisation c2 = dQ*dK*sm_scale*log2e,
-//   P~ = exp2(S*c2 - (m' - 8)) (fp32 v_exp_f32) on the VALU, packed to FP8
-//   e4m3 in registers
+//   P~ = exp2((B + S)*c2 - K), K = RN(B*c2 + m' - 8) (one fma, fp32
+//   v_exp_f32) on the VALU, packed to FP8 e4m3 in registers
+//   l += sum of the FP8 codes of the row             1 v_mfma_scale_f32_16x16x128_f8f6f4
 //   O_acc^T[32 ch x 32 q] += V^T_tile . P^T             d/32 v_mfma_scale_f32_32x32x64_f8f6f4
 //   (inner level: the instruction's 64-product block sum; outer level: the
 //    exact fp32 accumulate into its C operand; O_acc is rescaled by alpha
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int li = lane & 31, lg = lane >> 5;
+  const v8i ones16 = rowsum_ones_operand(lane);   // INT8 row sums (see rowsum_fp8)
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
   // on XCD b % 8).  Flat query head bh = b*Hq + h reads flat K/V head
   // bh / g (the g query heads of a K/V head are consecutive).  When the K/V
@@ -307,7 +311,11 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // int32 (INT8 codes) or fp32 (QK4, scales applied in the instruction)
   auto qk = [&](int t, SV& a0, SV& a1) {
     const int8_t* kb0 = sK[t & 1] + li * RK + 16 * lg;   // MFMA rows li and 32 + li
-    a0 = SV{}; a1 = SV{};
+    if constexpr (QK4) {
+      a0 = SV{}; a1 = SV{};
+    } else {
+      a0 = kScoreBias16; a1 = kScoreBias16;   // int32 results read as fp32 give B + S exactly
+    }
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       const v4i k0 = *(const v4i*)(kb0 + 32 * s);
@@ -412,7 +420,9 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
         int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
-        const v16i si0 = __builtin_bit_cast(v16i, sc0), si1 = __builtin_bit_cast(v16i, sc1);   // QK4: fp32 bits
+        // INT8: the exact int32 scores (the accumulator started at the bias); QK4: fp32 bits
+        const v16i si0 = __builtin_bit_cast(v16i, sc0) - (QK4 ? 0 : kScoreBiasBits);   // no wrap: B + S > 0
+        const v16i si1 = __builtin_bit_cast(v16i, sc1) - (QK4 ? 0 : kScoreBiasBits);
 #pragma unroll
         for (int v = 0; v < 16; v++) {
           if (!RAGGED || keyb + v < Nkv) sd[v] = si0[v];
@@ -449,8 +459,8 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
         }
         smax = pair_max_i32(smax);
         c2a = c2b = (dq * ks0) * p.s2;
-        ustar = (float)smax * c2a;
-        if (DIAG && smax == INT32_MIN) ustar = -1e30f;   // no visible key in this tile for this row
+        ustar = DIAG && smax == INT32_MIN ? -1e30f   // no visible key in this tile for this row
+                                          : (float)unbias_score(smax) * c2a;
       } else {
         int sa = INT32_MIN, sb = INT32_MIN;
 #pragma unroll
@@ -460,20 +470,23 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
         }
         c2a = (dq * ks0) * p.s2;
         c2b = (dq * ks1) * p.s2;
-        float ua = (float)sa * c2a, ub = (float)sb * c2b;
-        if (DIAG && sa == INT32_MIN) ua = -1e30f;
-        if (DIAG && sb == INT32_MIN) ub = -1e30f;
+        const float ua = DIAG && sa == INT32_MIN ? -1e30f : (float)unbias_score(sa) * c2a;
+        const float ub = DIAG && sb == INT32_MIN ? -1e30f : (float)unbias_score(sb) * c2b;
         ustar = pair_max_f32(fmaxf(ua, ub));
       }
       const float mnew = fmaxf(m, ustar);
       const float mm = mnew - 8.0f;
+      // INT8: the argument is one fma of the biased score, (B + S) c2 - K with
+      // K = RN(B c2 + mm): the offset mm taken at the precision of B c2
+      const float ka = QK4 ? mm : __builtin_fmaf(kScoreBiasF, c2a, mm);
+      const float kb = QK4 ? mm : (FINEK ? __builtin_fmaf(kScoreBiasF, c2b, mm) : ka);
       if (next) qk(t + 1, nx0, nx1);
 
       // ---- P~ (fp32) -> FP8 B operand, packed in place ----
       // exp2 is the hardware's fp32 exp2 (v_exp_f32): any argument is valid,
       // and masked (future) keys get -inf, whose exp2 is exactly 0.
       v8i pb;
-      float rs = 0.0f;
+      float rs = 0.0f;   // 4-bit scores: the fp32 row sum of P~ on the VALU
 #pragma unroll
       for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -481,12 +494,15 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
           float pv4[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            const auto sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];   // int32 or fp32 score
-            float arg = __builtin_fmaf((float)sv, h == 0 ? c2a : c2b, -mm);
+            const auto sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];   // biased int32 or fp32 score
+            float sf;
+            if constexpr (QK4) sf = sv;
+            else sf = __builtin_bit_cast(float, sv);
+            float arg = __builtin_fmaf(sf, h == 0 ? c2a : c2b, h == 0 ? -ka : -kb);
             if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
             pv4[e] = x;
-            rs += x;
+            if constexpr (QK4 != 0) rs += x;
           }
           // the low-half convert's "old" operand is a register that dies here
           // (its high half is overwritten by the second convert)
@@ -498,6 +514,9 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
       // moves it below the rescale branch, away from the MFMAs it should
       // overlap (an empty statement that reads the packed codes and the sum)
       asm volatile("" : "+v"(pb), "+v"(rs));
+      // INT8 scores: the row sum of the FP8 codes P^ on the matrix core (each
+      // lane gets its row's whole 64-key sum)
+      if constexpr (QK4 == 0) rs = rowsum_fp8(ones16, pb);
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
 #pragma unroll
@@ -582,7 +601,8 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 
   // ---- epilogue: O = O_acc * v_scale / l ----
-  const float lt = pair_sum_f32(lpart);
+  // INT8: every lane holds its row's whole sum; 4-bit: each lane summed half the keys
+  const float lt = QK4 ? pair_sum_f32(lpart) : lpart;
   const float inv = 1.0f / lt;
   const float* vs = p.v_scale + (size_t)bhkv * D;
   const size_t orow = p.nhd ? ((size_t)(bh / p.Hq) * Nq + row) * p.Hq + bh % p.Hq : (size_t)bh * Nq + row;

@@ -21,6 +21,39 @@ constexpr int kStatChunk = 256;
 // log2(e) rounded to fp32.
 constexpr float kLog2e = 0x1.715476p+0f;
 
+// Bias of the INT8 score accumulators: the integer matrix instruction starts
+// from the bit pattern of B = 1.5 * 2^23, so each int32 result B_bits + S,
+// read as fp32, is exactly B + S (|S| <= 127^2 * 128 < 2^21 keeps it inside
+// [2^23, 2^24), where fp32 spacing is 1): the softmax needs no int-to-float
+// conversion per score.
+constexpr float kScoreBiasF = 12582912.0f;
+constexpr int kScoreBiasBits = 0x4B400000;
+constexpr v16i kScoreBias16 = {kScoreBiasBits, kScoreBiasBits, kScoreBiasBits, kScoreBiasBits,
+                               kScoreBiasBits, kScoreBiasBits, kScoreBiasBits, kScoreBiasBits,
+                               kScoreBiasBits, kScoreBiasBits, kScoreBiasBits, kScoreBiasBits,
+                               kScoreBiasBits, kScoreBiasBits, kScoreBiasBits, kScoreBiasBits};
+// The exact score S of a biased accumulator value (wrapping unsigned arithmetic:
+// masked sentinels are compared before this is used, never converted).
+__device__ __forceinline__ int unbias_score(int x) { return (int)((unsigned)x - (unsigned)kScoreBiasBits); }
+
+// Row sum of a wave's FP8 P~ codes on the matrix core.  pb is the B operand
+// of the 32x32x64 P~V instruction (lane l: query l%32, keys 32(l/32) ..
+// +31).  Read as the B operand of the 16x16x128 FP8 instruction, lane l is
+// column l%16 of lane group l/16; with an A operand that is all ones (e4m3
+// 1.0) exactly where row (l%16)/4 and lane group l/16 have the same parity,
+// and zero elsewhere, row r of column n sums lane groups of r's parity: the
+// 64 keys of query n (even) or n + 16 (odd).  Lane l holds rows 4(l/16) ..
+// +3 of column l%16, i.e. the sum for its own query l%32 in every register.
+__device__ __forceinline__ v8i rowsum_ones_operand(int lane) {
+  const int w = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
+  return v8i{w, w, w, w, w, w, w, w};
+}
+__device__ __forceinline__ float rowsum_fp8(const v8i& ones, const v8i& pb) {
+  const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
+                                                                 127, 0, 127);
+  return r[0];
+}
+
 // fp16 / bf16 -> fp32 (both exact).
 __device__ __forceinline__ float load_h(uint16_t h, bool is_bf16) {
   if (is_bf16) return __uint_as_float((uint32_t)h << 16);

@@ -9,7 +9,9 @@
 //
 // Per wave and KV tile (64 keys), with the tile's K and V operands in registers:
 //   S^T = K_tile . Q^T    2 x (d/32) v_mfma_i32_32x32x32_i8
-//   softmax on the VALU (one lane per query row, as in the attention kernel)
+//   softmax on the VALU (one lane per query row, the attention kernel's
+//   arithmetic: exponent argument (B + S) c2 - K, row sum of the FP8 codes on
+//   the matrix core)
 //   O^T += V^T . P~^T     d/32 v_mfma_scale_f32_32x32x64_f8f6f4
 // Waves share nothing and never synchronise with each other.
 #include "common.h"
@@ -55,6 +57,7 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lg = lane >> 5;
+  const v8i ones16 = rowsum_ones_operand(lane);
   const int unit = blockIdx.x * 4 + wave;
   if (unit >= p.units) return;   // whole wave; no barrier in this kernel
   const int chunk = unit % p.nchunk, rest = unit / p.nchunk;
@@ -140,8 +143,8 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
     }
     const float mnew = fmaxf(m, ustar);
     const float mm = mnew - 8.0f;
+    const float ka = __builtin_fmaf(kScoreBiasF, c2a, mm), kb = FINEK ? __builtin_fmaf(kScoreBiasF, c2b, mm) : ka;
     v8i pb;
-    float rs = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -150,16 +153,17 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int sv = h == 0 ? sc0[4 * q + e] : sc1[4 * q + e];
-          float arg = __builtin_fmaf((float)sv, h == 0 ? c2a : c2b, -mm);
+          // B + S as fp32 (an exact add): the attention kernel's argument bit for bit
+          float arg = __builtin_fmaf((float)sv + kScoreBiasF, h == 0 ? c2a : c2b, h == 0 ? -ka : -kb);
           if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
           const float x = __builtin_amdgcn_exp2f(arg);
           pv4[e] = x;
-          rs += x;
         }
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[0], pv4[1], __float_as_int(pv4[0]), false);
         pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[2], pv4[3], w, true);
       }
     }
+    const float rs = rowsum_fp8(ones16, pb);   // the row's whole 64-key sum of the FP8 codes
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     if (__builtin_amdgcn_ballot_w64(mnew > m) != 0) {
 #pragma unroll
@@ -167,7 +171,6 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
 #pragma unroll
         for (int e = 0; e < 16; e++) oacc[ct][e] *= alpha;
     }
-    lpart = __builtin_fmaf(alpha, lpart, rs);
     m = mnew;
 #pragma unroll
     for (int ct = 0; ct < CT; ct++) {
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
                       o.vb[ct][0], o.vb[ct][1], o.vb[ct][2], o.vb[ct][3]};
       oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
     }
+    lpart = __builtin_fmaf(alpha, lpart, rs);
   };
 
   const int t0 = chunk * p.ctiles, t1 = min(t0 + p.ctiles, p.nkt);
@@ -193,7 +197,9 @@ __global__ __launch_bounds__(256, 1) void decode_chunk_kernel(DecodeK p) {
   }
 
   float* up = p.part + (size_t)unit * unit_floats<D>();
-  const float lt = pair_sum_f32(lpart);
+  // lanes l and l^32 hold the same whole sum (the max of the pair is that sum; this
+  // form also keeps the register allocation of this kernel free of spills)
+  const float lt = pair_max_f32(lpart);
 #pragma unroll
   for (int ct = 0; ct < CT; ct++)
 #pragma unroll

@@ -99,6 +99,15 @@ MUTANTS = [
     ("accumulator not rescaled", "oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);",
      "oacc[c] = oacc[c] + (float)oblk[c];", 1),
     ("P~ without the 2^8 headroom", "float mm = mnew - 8.0f;", "float mm = mnew;", 1),
+    ("INT8 row sum over the fp32 P~, not the FP8 codes", "if (!x->q4) rowsum = (float)code_sum;",
+     "if (!x->q4) { rowsum = 0.0f; for (int jj = 0; jj < nvis; jj++) rowsum += pt[jj]; }", 1),
+    ("INT8 row sum of the first half of the keys", "if (!x->q4) rowsum = (float)code_sum;",
+     "if (!x->q4) { double h = 0; for (int jj = 0; jj < nvis / 2; jj++) h += x->vdec[ph[jj]]; rowsum = (float)h; }",
+     1),
+    ("INT8 exponent offset without the score bias", "const float K = fmaf(SCORE_BIAS, c2[jj], mm);",
+     "const float K = mm;", 1),
+    ("INT8 exponent argument without the score bias", "fmaf(SCORE_BIAS + S[jj], c2[jj], -K)",
+     "fmaf(S[jj], c2[jj], -K)", 1),
     # split-KV merge
     ("split merge weight inverted", "const float w = oracle_exp2f(mc[c] - mstar);",
      "const float w = oracle_exp2f(mstar - mc[c]);", 1),

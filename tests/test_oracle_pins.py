@@ -347,6 +347,40 @@ def test_v_power_of_two_scales_output_exactly():
     assert np.array_equal(O1, O0 * 4)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_channels_give_that_constant(causal):
+    """V constant over the tokens of each channel: every V code is +-448 and O is a weighted
+    average whose weights are the FP8 codes P^ divided by their own sum l (INT8 path: l sums
+    the codes, not the fp32 P~), so O equals the channel's dequantized value to fp32 rounding
+    for any Q and K, through several tiles, rescales and the causal mask.  With l summed over
+    the fp32 P~ the weights would miss one by the FP8 rounding of P~ (about 1e-2)."""
+    w, Q, K, _ = _small(dict(causal=causal, N=512, d=128, blk_q=128, dtype="bfloat16"))
+    rng = np.random.default_rng(5)
+    a = (rng.standard_normal((w.B, w.H, 1, w.d)) * 3).astype(np.float32)
+    V = torch.from_numpy(np.broadcast_to(a, (w.B, w.H, w.N, w.d)).copy()).to(torch.bfloat16)
+    qk, (vc, vs), O = _run(w, Q * 3, K, V)
+    assert (np.abs(orc.e4m3_decode(vc)) == 448).all()
+    expect = orc.e4m3_decode(vc[:, :, :1, :]) * vs[:, :, None, :].astype(np.float64)   # the dequantized constant
+    O = O.reshape(w.B, w.H, w.N, w.d).astype(np.float64)
+    assert np.abs(O - expect).max() <= 4e-6 * np.abs(expect).max()
+
+
+def test_split_chunks_with_constant_v_give_that_constant():
+    """The split-KV form merges chunk states with the same weights for O and l, so constant V
+    channels come out exactly (to fp32 rounding) whatever the chunking."""
+    w, Q, K, _ = _small(dict(causal=True, N=512, d=128, blk_q=128, dtype="bfloat16"))
+    a = np.linspace(-5, 5, w.d, dtype=np.float32)[None, None, None, :]
+    V = torch.from_numpy(np.broadcast_to(a, (w.B, w.H, w.N, w.d)).copy()).to(torch.bfloat16)
+    qk = orc.quantize_qk(synth.bits(Q), synth.bits(K), w.dtype_code, w.blk_q, w.blk_k)
+    vc, vs = orc.quantize_v(synth.bits(V), w.dtype_code)
+    expect = orc.e4m3_decode(vc[:, :, :1, :]) * vs[:, :, None, :].astype(np.float64)
+    rows = np.arange(w.B * w.H * w.N)
+    for chunk in (64, 128, 256):
+        O = orc.attn_rows_split(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, kv_chunk=chunk, rows=rows)
+        O = O.reshape(w.B, w.H, w.N, w.d)
+        assert np.abs(O - expect).max() <= 4e-6 * np.abs(expect).max(), chunk
+
+
 def test_identity_v_exposes_p_tilde_on_the_fp8_grid():
     """With V the identity (one key per channel, one 64-key tile) row i of O is
     P~_i . diag(1) scaled by one common factor, so O shows the values that enter
