@@ -25,7 +25,8 @@
  *  - decode over a quantized KV cache (blog section "FlashAttention for
  *    training and inference: where SageAttention fits": decode is bound by
  *    reading the cache): sage_quantize_q, sage_quantize_k,
- *    sage_decode_kv_chunk, sage_attn_decode_workspace_bytes, sage_attn_decode;
+ *    sage_decode_kv_chunk, sage_attn_decode_workspace_bytes, sage_attn_decode,
+ *    sage_attn_decode_noalloc;
  *  - 4-bit QK^T (the SageAttention3 abstract: attention on FP4 matrix cores):
  *    sage_quantize_qk4, sage_attn_fwd_qk4(_dump), and with Q smoothing (the
  *    SageAttention2 abstract) sage_quantize_qk4_smooth_q,
@@ -33,7 +34,8 @@
  *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
- *    nothing and keeps no state between calls.  Every pointer must be 16-byte
+ *    nothing and keeps no state between calls (sage_attn_decode_noalloc
+ *    alone uses a device array of the library's own, see there).  Every pointer must be 16-byte
  *    aligned; outputs must not alias inputs.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work on it and return; no host synchronisation happens inside.
@@ -287,6 +289,32 @@ int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* 
                      const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
                      int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
                      int kv_chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array of sage_attn_decode_noalloc (one per
+ * device): the chunk states of 2016 waves of work at d = 128, 3968 at d = 64. */
+#define SAGE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * sage_attn_decode_noalloc -- sage_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and result as
+ * sage_attn_decode without the workspace: the chunk states go to a device
+ * array inside the library, SAGE_NOALLOC_SCRATCH_BYTES on each device, which
+ * that device holds until the process ends.  Its address is looked up on the
+ * first call on each device; nothing is allocated, set or synchronised.
+ * Errors: SAGE_ERR_WORKSPACE (before anything is enqueued) when
+ * sage_attn_decode_workspace_bytes(...) of the shape and kv_chunk exceeds
+ * SAGE_NOALLOC_SCRATCH_BYTES; SAGE_ERR_INVALID_ARG when `stream` is not a
+ * stream of the current device; the argument errors of sage_attn_decode.
+ * The array keeps the last call's contents and needs no clearing (a call
+ * writes every state before reading it).  All calls on one GPU share it:
+ * calls that overlap on one GPU (on different streams or host threads) race
+ * and give wrong results, so issue them in order on one stream.
+ */
+int sage_attn_decode_noalloc(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                             const float* k_scale, const uint8_t* v_codes, const float* v_scale, void* O,
+                             int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q,
+                             int blk_k, int causal, float sm_scale, int kv_chunk, void* stream);
 
 /*
  * sage_quantize_qk4 -- Q and smoothed K to 4-bit E2M1 for sage_attn_fwd_qk4

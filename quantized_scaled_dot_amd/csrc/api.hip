@@ -1,6 +1,10 @@
 // C ABI of libsage.so: argument validation, then kernel launches on the
-// caller's stream.  No allocation, no host synchronisation, no global state.
+// caller's stream.  No allocation and no host synchronisation; the only
+// global state is the per-device address of the allocation-free decode's
+// scratch array.
 #include <math.h>
+
+#include <mutex>
 
 #include "../../include/sage.h"
 #include "common.h"
@@ -305,10 +309,56 @@ size_t sage_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv,
   return sage::decode_workspace(B, Hq, Hkv, Nq, Nkv, d, kv_chunk);
 }
 
-int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
-                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
-                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
-                     int kv_chunk, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Chunk states of sage_attn_decode_noalloc: one copy of this array per device,
+// held until the process ends.  In host code its name is only a handle for
+// hipGetSymbolAddress: the device address of each device's copy is looked up
+// once, with that device current, and only that pointer reaches the kernels.
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the current device's scratch array (looked up on the
+// first call on that device).  The stream must belong to the current device.
+int noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SAGE_ERR_HIP;
+  }
+  if (dev >= kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return SAGE_ERR_HIP;
+    }
+    if (sdev != dev) return SAGE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SAGE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
+// sage_attn_decode with the workspace given (noalloc = false) or the
+// library's scratch array (noalloc = true; workspace and workspace_bytes unused).
+int decode_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                  const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                  int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale, int kv_chunk,
+                  void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_blocks(blk_q, blk_k));
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARG;
@@ -323,8 +373,15 @@ int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* 
                            (kv_chunk / sage::kKTile));
   if (units / 4 + 1 > 0x7fffffffLL) return SAGE_ERR_UNSUPPORTED;
   SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
-  SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O); SAGE_PTR(workspace);
-  if (workspace_bytes < sage::decode_workspace(B, Hq, Hkv, Nq, Nkv, d, kv_chunk)) return SAGE_ERR_WORKSPACE;
+  SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O);
+  const size_t need = sage::decode_workspace(B, Hq, Hkv, Nq, Nkv, d, kv_chunk);
+  if (noalloc) {
+    if (need > SAGE_NOALLOC_SCRATCH_BYTES) return SAGE_ERR_WORKSPACE;
+    SAGE_TRY(noalloc_scratch(stream, &workspace));
+  } else {
+    SAGE_PTR(workspace);
+    if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  }
   sage::DecodeArgs a;
   a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale;
   a.v_codes = v_codes; a.v_scale = v_scale; a.O = O; a.out_dtype = out_dtype; a.nhd = layout == SAGE_LAYOUT_BNHD;
@@ -333,6 +390,26 @@ int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* 
   (void)hipGetLastError();
   sage::launch_attn_decode(a, (hipStream_t)stream);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_attn_decode(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                     const uint8_t* v_codes, const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq,
+                     int Hkv, int Nq, int Nkv, int d, int blk_q, int blk_k, int causal, float sm_scale,
+                     int kv_chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq,
+                       Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, workspace, workspace_bytes, false, stream);
+}
+
+int sage_attn_decode_noalloc(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
+                             const float* k_scale, const uint8_t* v_codes, const float* v_scale, void* O,
+                             int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int blk_q,
+                             int blk_k, int causal, float sm_scale, int kv_chunk, void* stream) {
+  return decode_common(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq,
+                       Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, nullptr, 0, true, stream);
 }
 
 int sage_attn_fwd_ex(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,

@@ -25,7 +25,7 @@ SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_byt
            "sage_quantize_qk_ex", "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_quantize_v_ex",
            "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
            "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode",
-           "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
+           "sage_attn_decode_noalloc", "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
            "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump", "sage_probe_mfma_peak")
 
 if not os.path.exists(LIB_PATH):
@@ -66,6 +66,10 @@ _lib.sage_attn_decode_workspace_bytes.restype = _SZ
 _lib.sage_attn_decode_workspace_bytes.argtypes = [_I] * 7
 _lib.sage_attn_decode.restype = _I
 _lib.sage_attn_decode.argtypes = [_P] * 7 + [_I] * 11 + [_F, _I, _P, _SZ, _P]
+_lib.sage_attn_decode_noalloc.restype = _I
+_lib.sage_attn_decode_noalloc.argtypes = [_P] * 7 + [_I] * 11 + [_F, _I, _P]
+#: bytes of the library's per-device scratch array for sage_attn_decode_noalloc
+SAGE_NOALLOC_SCRATCH_BYTES = 32 << 20
 _lib.sage_quantize_qk4.restype = _I
 _lib.sage_quantize_qk4.argtypes = [_P, _P] + [_I] * 8 + [_P] * 6 + [_SZ, _P]
 _lib.sage_attn_fwd_qk4.restype = _I
@@ -185,6 +189,12 @@ def sage_attn_decode(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, ou
     return _lib.sage_attn_decode(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq,
                                  Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, workspace,
                                  workspace_bytes, stream)
+
+
+def sage_attn_decode_noalloc(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv,
+                             Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, stream):
+    return _lib.sage_attn_decode_noalloc(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, O, out_dtype, layout,
+                                         B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, causal, sm_scale, kv_chunk, stream)
 
 
 def sage_quantize_qk4(Q, K, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, q4_codes, q4_scale, k4_codes, k4_scale, k_mean,

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 24 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 25 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -297,3 +297,22 @@ def test_quantize_qk4_smooth_q_rejects(kw, status):
 ])
 def test_attn_fwd_qk4_smooth_q_rejects(kw, status):
     assert _attn4s(**kw) == status
+
+
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call():
+    """The allocation-free decode checks its size limit (the header constant, mirrored by the
+    binding) before it looks up its device array or enqueues anything."""
+    src = open(os.path.join(ROOT, "include", "sage.h")).read()
+    m = re.search(r"#define SAGE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == sage.SAGE_NOALLOC_SCRATCH_BYTES
+    # 16 batches x 8 K/V heads x 512 one-tile splits of 32768 keys: 65536 waves of chunk states
+    need = sage.sage_attn_decode_workspace_bytes(16, 32, 8, 1, 32768, 128, 64)
+    assert need > sage.SAGE_NOALLOC_SCRATCH_BYTES
+    st = sage.sage_attn_decode_noalloc(A, A, A, A, A, A, A, sage.SAGE_F32, 0, 16, 32, 8, 1, 32768, 128, 128, 64, 1,
+                                       0.088, 64, None)
+    assert st == sage.SAGE_ERR_WORKSPACE
+    # the argument checks of sage_attn_decode come first
+    assert sage.sage_attn_decode_noalloc(A, A, A, A, A, A, None, sage.SAGE_F32, 0, 16, 32, 8, 1, 32768, 128, 128, 64,
+                                         1, 0.088, 64, None) == sage.SAGE_ERR_INVALID_ARG
+    assert sage.sage_attn_decode_noalloc(A, A, A, A, A, A, A, sage.SAGE_F32, 0, 16, 32, 8, 1, 32768, 128, 128, 64, 1,
+                                         0.088, 96, None) == sage.SAGE_ERR_INVALID_ARG
