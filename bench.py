@@ -93,9 +93,18 @@ def read_sclk_mhz():
     return None
 
 
+def under_profiler():
+    """True when a profiler's library is preloaded into this process (its children inherit it, so
+    the clock reader, itself a script, would start with the profiler attached)."""
+    return any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def sample_sclk(run, seconds=1.5):
     """Keep the GPU busy with run() (enqueue-only, on the bench stream) for about `seconds` while
-    another thread reads the shader clock; returns {"samples", "median", "min", "max"} in MHz or None."""
+    another thread reads the shader clock; returns {"samples", "median", "min", "max"} in MHz or None
+    (also None under a profiler, where the reader is not started)."""
+    if under_profiler():
+        return None
     import threading
     samples, stop = [], threading.Event()
 

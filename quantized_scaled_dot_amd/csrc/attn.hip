@@ -92,8 +92,13 @@ struct AttnK {
 // of the wave's 32 queries (one block) against the FP8 K, on the FP8 matrix
 // instruction into the same fp32 accumulators (the FP8 K tile is staged next
 // to the 4-bit one, rows of d + 16 bytes in the same MFMA order).
-template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP>
-__global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
+// NW: waves per workgroup (query rows 32 NW).  4 everywhere; 8 for the
+// non-causal INT8 d = 128 kernel on whole 256-row query tiles, where one
+// workgroup then fills a CU and each K/V tile copy serves twice the rows.
+template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP, int NW = 4>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
+  static_assert(NW == 4 || (NW == 8 && D == 128 && !CAUSAL && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
+  constexpr int QT = 32 * NW;   // query rows per workgroup
   constexpr bool QSM = QK4 == 2;
   constexpr int KB = QK4 ? D / 2 : D;          // K code bytes per key
   constexpr int KS = KB / 32;                  // k-steps of the score MFMA over d (32 code bytes a lane pair)
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
   const int bhkv = bh / p.g;
   const int Nq = p.Nq, Nkv = p.Nkv, off = p.off;
-  const int q0 = qt * kQTile, qrow0 = q0 + wave * 32, row = qrow0 + li;
+  const int q0 = qt * QT, qrow0 = q0 + wave * 32, row = qrow0 + li;
   // the last key this row sees, and the smallest such key over the wave
   // (only read in masked steps)
   const int lastk = !RAGGED ? row + off : CAUSAL ? min(row + off, Nkv - 1) : Nkv - 1;
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   // chosen so that the padded LDS layout comes out directly (K rows in MFMA
   // order, d + 16 bytes; V channel rows, 80 bytes).  Padding chunks re-read
   // the last data chunk of their row.  A step copies one K and one V tile:
-  // wave w issues K and V instructions w, w+4, ... of the whole rounds of
+  // wave w issues K and V instructions w, w+NW, ... of the whole rounds of
   // four, then one of the leftover instructions (K first, then V; none when
   // w is past them), so that no copy depends on a branch per instruction.
   // K tile t lives in sK[t%2], V tile t in sV[t%3]; K is staged one tile
@@ -200,11 +205,11 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   constexpr int KTILE8 = kKTile * D;                                 // bytes of one FP8 K tile in HBM
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0 && kKTile * RK8 % 1024 == 0,
                 "whole DMA instructions per tile");
-  constexpr int FK = NKI / 4, F8 = N8I / 4, FV = NVI / 4;            // whole rounds
-  constexpr int XK = NKI % 4, X8 = N8I % 4, XR = NKI % 4 + N8I % 4 + NVI % 4;   // leftovers: K, FP8 K, all
-  constexpr int NXR = (XR + 3) / 4;                                  // leftover rounds
+  constexpr int FK = NKI / NW, F8 = N8I / NW, FV = NVI / NW;         // whole rounds
+  constexpr int XK = NKI % NW, X8 = N8I % NW, XR = NKI % NW + N8I % NW + NVI % NW;   // leftovers: K, FP8 K, all
+  constexpr int NXR = (XR + NW - 1) / NW;                             // leftover rounds
   static_assert(NXR <= 2, "at most two leftover rounds");
-  __builtin_assume(wave >= 0 && wave < 4);
+  __builtin_assume(wave >= 0 && wave < NW);
   const __amdgpu_buffer_rsrc_t rK =
       head_rsrc((QK4 ? (const int8_t*)p.k4_codes : p.k_codes) + (size_t)bhkv * p.nkt * KTILE, (uint32_t)(p.nkt * KTILE));
   const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
@@ -222,20 +227,20 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   };
   uint32_t koff[FK > 0 ? FK : 1], k8off[F8 > 0 ? F8 : 1], voff[FV > 0 ? FV : 1];
 #pragma unroll
-  for (int j = 0; j < FK; j++) koff[j] = k_src(wave + 4 * j, RK, KB);
+  for (int j = 0; j < FK; j++) koff[j] = k_src(wave + NW * j, RK, KB);
 #pragma unroll
-  for (int j = 0; j < F8; j++) k8off[j] = k_src(wave + 4 * j, RK8, D);
+  for (int j = 0; j < F8; j++) k8off[j] = k_src(wave + NW * j, RK8, D);
 #pragma unroll
-  for (int j = 0; j < FV; j++) voff[j] = v_src(wave + 4 * j);
+  for (int j = 0; j < FV; j++) voff[j] = v_src(wave + NW * j);
   // this wave's leftover of round r: entry e = 4 r + wave of the list (K ones,
   // then FP8 K, then V); xt = 0 K, 1 FP8 K, 2 V, -1 none
   int xt[NXR > 0 ? NXR : 1], xi[NXR > 0 ? NXR : 1];
   uint32_t xoff[NXR > 0 ? NXR : 1];
 #pragma unroll
   for (int r = 0; r < NXR; r++) {
-    const int e = 4 * r + wave;
+    const int e = NW * r + wave;
     xt[r] = e < XK ? 0 : e < XK + X8 ? 1 : e < XR ? 2 : -1;
-    xi[r] = xt[r] == 0 ? 4 * FK + e : xt[r] == 1 ? 4 * F8 + e - XK : 4 * FV + e - XK - X8;
+    xi[r] = xt[r] == 0 ? NW * FK + e : xt[r] == 1 ? NW * F8 + e - XK : NW * FV + e - XK - X8;
     xoff[r] = xt[r] == 0 ? k_src(xi[r], RK, KB) : xt[r] == 1 ? k_src(min(xi[r], N8I - 1), RK8, D) : v_src(min(xi[r], NVI - 1));
   }
   // The copies take their LDS destination as a plain address: the compiler
@@ -251,14 +256,14 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
     const uint32_t kd = kbase + (uint32_t)(kslot * (kKTile * RK)), vd = vbase + (uint32_t)(vslot * (D * kRowV));
     const uint32_t k8d = k8base + (uint32_t)(kslot * (kKTile * RK8));
 #pragma unroll
-    for (int j = 0; j < FK; j++) lds_copy16_at(rK, kd + 1024 * (wave + 4 * j), koff[j], tk * KTILE);
+    for (int j = 0; j < FK; j++) lds_copy16_at(rK, kd + 1024 * (wave + NW * j), koff[j], tk * KTILE);
 #pragma unroll
-    for (int j = 0; j < F8; j++) lds_copy16_at(rK8, k8d + 1024 * (wave + 4 * j), k8off[j], tk * KTILE8);
+    for (int j = 0; j < F8; j++) lds_copy16_at(rK8, k8d + 1024 * (wave + NW * j), k8off[j], tk * KTILE8);
 #pragma unroll
-    for (int j = 0; j < FV; j++) lds_copy16_at(rV, vd + 1024 * (wave + 4 * j), voff[j], tv * TILE);
+    for (int j = 0; j < FV; j++) lds_copy16_at(rV, vd + 1024 * (wave + NW * j), voff[j], tv * TILE);
 #pragma unroll
     for (int r = 0; r < NXR; r++)
-      if (4 * (r + 1) <= XR || xt[r] >= 0)
+      if (NW * (r + 1) <= XR || xt[r] >= 0)
         lds_copy16_at(xt[r] == 0 ? rK : xt[r] == 1 ? rK8 : rV, (xt[r] == 0 ? kd : xt[r] == 1 ? k8d : vd) + 1024 * xi[r],
                       xoff[r], xt[r] == 0 ? tk * KTILE : xt[r] == 1 ? tk * KTILE8 : tv * TILE);
   };
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   float m = -1e30f, lpart = 0.0f;
 
   // tiles up to the one holding the workgroup's last visible key
-  const int ntiles = CAUSAL ? min((q0 + kQTile - 1 + off) / kKTile + 1, p.nkt) : p.nkt;
+  const int ntiles = CAUSAL ? min((q0 + QT - 1 + off) / kKTile + 1, p.nkt) : p.nkt;
   const float* kscale = p.k_scale + (size_t)bhkv * p.nbk;
   // K scale index of the run of 16 keys of half h of this lane in tile t
   auto kidx = [&](int t, int h) { return FINEK ? (t * kKTile + 32 * lg + 16 * h) >> p.lgk : t; };
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
 
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
-        int32_t* sd = p.s_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
+        int32_t* sd = p.s_dump + ((size_t)dump_idx * QT + (row - q0)) * Nkv + keyb;
         // INT8: the exact int32 scores (the accumulator started at the bias); QK4: fp32 bits
         const v16i si0 = __builtin_bit_cast(v16i, sc0) - (QK4 ? 0 : kScoreBiasBits);   // no wrap: B + S > 0
         const v16i si1 = __builtin_bit_cast(v16i, sc1) - (QK4 ? 0 : kScoreBiasBits);
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
       // lane gets its row's whole 64-key sum)
       if constexpr (QK4 == 0) rs = rowsum_fp8(ones16, pb);
       if (DUMP && dump_idx >= 0) {
-        uint8_t* pd = p.p_dump + ((size_t)dump_idx * kQTile + (row - q0)) * Nkv + keyb;
+        uint8_t* pd = p.p_dump + ((size_t)dump_idx * QT + (row - q0)) * Nkv + keyb;
 #pragma unroll
         for (int k = 0; k < 32; k++)
           if (!RAGGED || keyb + k < Nkv) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
@@ -621,27 +626,36 @@ __global__ __launch_bounds__(256, D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kern
   }
 }
 
+// wide: the 8-wave workgroups of 256 query rows (see attn_fwd_kernel); the
+// launcher only asks for them where that instance exists
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT>
-static void launch5(const AttnK& k, int grid, bool dump, hipStream_t st) {
+static void launch5(const AttnK& k, int grid, bool dump, bool wide, hipStream_t st) {
+  if constexpr (D == 128 && !CAUSAL && !RAGGED && QK4 == 0) {
+    if (wide) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, false, 8>), dim3(grid), dim3(512), 0,
+                         st, k);
+      return;
+    }
+  }
   if (dump)
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, true>), dim3(grid), dim3(256), 0, st, k);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, false>), dim3(grid), dim3(256), 0, st, k);
 }
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4>
-static void launch4(const AttnK& k, int grid, int out, bool dump, hipStream_t st) {
-  if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 2>(k, grid, dump, st);
-  else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 1>(k, grid, dump, st);
-  else launch5<D, CAUSAL, RAGGED, FINEK, QK4, 0>(k, grid, dump, st);
+static void launch4(const AttnK& k, int grid, int out, bool dump, bool wide, hipStream_t st) {
+  if (out == 2) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 2>(k, grid, dump, wide, st);
+  else if (out == 1) launch5<D, CAUSAL, RAGGED, FINEK, QK4, 1>(k, grid, dump, wide, st);
+  else launch5<D, CAUSAL, RAGGED, FINEK, QK4, 0>(k, grid, dump, wide, st);
 }
 // the score variant: INT8 with K blocks of a tile, INT8 with finer K blocks,
 // 4-bit, or 4-bit with Q smoothing
 template <int D, bool CAUSAL, bool RAGGED>
-static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, hipStream_t st) {
-  if (variant == 3) launch4<D, CAUSAL, RAGGED, false, 2>(k, grid, out, dump, st);
-  else if (variant == 2) launch4<D, CAUSAL, RAGGED, false, 1>(k, grid, out, dump, st);
-  else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, 0>(k, grid, out, dump, st);
-  else launch4<D, CAUSAL, RAGGED, false, 0>(k, grid, out, dump, st);
+static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, bool wide, hipStream_t st) {
+  if (variant == 3) launch4<D, CAUSAL, RAGGED, false, 2>(k, grid, out, dump, wide, st);
+  else if (variant == 2) launch4<D, CAUSAL, RAGGED, false, 1>(k, grid, out, dump, wide, st);
+  else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, 0>(k, grid, out, dump, wide, st);
+  else launch4<D, CAUSAL, RAGGED, false, 0>(k, grid, out, dump, wide, st);
 }
 // The kernel instances are compiled in eight parts, one per (head size,
 // causal, ragged) combination, so that the build can run them in parallel:
@@ -652,7 +666,7 @@ static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, h
 #define SAGE_ATTN_PART -1
 #endif
 #define SAGE_PART_DEF(P, D, C, R)                                                                         \
-  void launch_attn_part##P(const AttnK& k, int grid, int variant, int out, bool dump, hipStream_t st)
+  void launch_attn_part##P(const AttnK& k, int grid, int variant, int out, bool dump, bool wide, hipStream_t st)
 SAGE_PART_DEF(0, 128, true, false);
 SAGE_PART_DEF(1, 128, true, true);
 SAGE_PART_DEF(2, 128, false, false);
@@ -662,7 +676,7 @@ SAGE_PART_DEF(5, 64, true, true);
 SAGE_PART_DEF(6, 64, false, false);
 SAGE_PART_DEF(7, 64, false, true);
 #define SAGE_PART_BODY(P, D, C, R)                                                                        \
-  SAGE_PART_DEF(P, D, C, R) { launch3<D, C, R>(k, grid, variant, out, dump, st); }
+  SAGE_PART_DEF(P, D, C, R) { launch3<D, C, R>(k, grid, variant, out, dump, wide, st); }
 #if SAGE_ATTN_PART < 0 || SAGE_ATTN_PART == 0
 SAGE_PART_BODY(0, 128, true, false)
 #endif
@@ -694,20 +708,26 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
   k.v_codes = a.v_codes; k.v_scale = a.v_scale; k.O = a.O;
   k.Hq = a.Hq; k.g = a.Hq / a.Hkv; k.Nq = a.Nq; k.Nkv = a.Nkv; k.off = a.Nkv - a.Nq;
-  k.nqt = (a.Nq + kQTile - 1) / kQTile; k.nqp = k.nqt * kQTile; k.nbq = k.nqp / a.blk_q;
+  // Q code rows per head: Nq rounded up to 128 (the layout of the quantized Q)
+  k.nqp = (a.Nq + kQTile - 1) / kQTile * kQTile; k.nbq = k.nqp / a.blk_q;
   k.nkt = (a.Nkv + kKTile - 1) / kKTile; k.blk_q = a.blk_q; k.nhd = a.nhd; k.s2 = a.s2;
   k.nbk = k.nkt * kKTile / a.blk_k; k.lgk = a.blk_k == 16 ? 4 : a.blk_k == 32 ? 5 : 6;
   k.sel = a.sel; k.n_sel = a.n_sel; k.s_dump = a.s_dump; k.p_dump = a.p_dump;
-  const int grid = a.B * a.Hq * k.nqt;
   const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
   k.q4_codes = a.q4_codes; k.q4_scale = a.q4_scale; k.k4_codes = a.k4_codes; k.k4_scale = a.k4_scale;
   k.qm_codes = a.qm_codes; k.qm_scale = a.qm_scale; k.k8_codes = a.k8_codes; k.k8_scale = a.k8_scale;
   const int variant = a.q4_codes ? (a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
+  // 256-row workgroups: non-causal INT8 at d = 128 on whole 256-row query tiles
+  // (not for the test dumps, which address 128-row tiles)
+  const bool wide = !dump && a.d == 128 && !a.causal && !ragged && variant <= 1 && a.Nq % 256 == 0;
+  const int qtile = wide ? 256 : kQTile;
+  k.nqt = (a.Nq + qtile - 1) / qtile;   // query tiles (workgroups) per head
+  const int grid = a.B * a.Hq * k.nqt;
   const int part = (a.d == 128 ? 0 : 4) + (a.causal ? 0 : 2) + (ragged ? 1 : 0);
-  void (*const parts[8])(const AttnK&, int, int, int, bool, hipStream_t) = {
+  void (*const parts[8])(const AttnK&, int, int, int, bool, bool, hipStream_t) = {
       launch_attn_part0, launch_attn_part1, launch_attn_part2, launch_attn_part3,
       launch_attn_part4, launch_attn_part5, launch_attn_part6, launch_attn_part7};
-  parts[part](k, grid, variant, a.out_dtype, dump, st);
+  parts[part](k, grid, variant, a.out_dtype, dump, wide, st);
 }
 #endif
 

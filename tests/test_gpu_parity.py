@@ -282,6 +282,41 @@ def test_small_grouped_and_unequal_parity(name, layout):
     assert cosine(O, ex) >= 0.995
 
 
+# Non-causal INT8 at d = 128 on whole 256-row query tiles runs in 8-wave workgroups of 256 rows
+# (the dump instance always runs 128-row workgroups): the per-row arithmetic is the same, so O
+# must be bit-identical to the 128-row kernel's, and within 2e-3 of the oracle.
+WIDE = {
+    "wide-noncausal-N768-blkq64": dict(base="video-dit-32k", B=1, H=2, N=768, blk_q=64),
+    "wide-gqa-chunk-512-of-1024": dict(base="video-dit-32k", B=2, H=8, Hkv_=2, N=512, Nkv_=1024),
+    "wide-fine-k16-N512": dict(base="video-dit-32k", B=1, H=3, N=512, blk_q=32, blk_k=16),
+    "wide-mqa-N256-xcd": dict(base="video-dit-32k", B=1, H=64, Hkv_=8, N=256),
+}
+
+
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_workgroups_equal_the_128_row_kernel(name, layout):
+    kw = dict(WIDE[name])
+    w = synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw)
+    Q, K, V = synth.make_inputs(w)
+    assert w.d == 128 and not w.causal and w.N % 256 == 0 and w.Nkv % 128 == 0
+    nqt = -(-w.N // 128)
+    g = run_gpu(w, Q, K, V, dump_tiles=(0,), layout=layout)     # the 128-row instance
+    sage = _sage()
+    tok = layout == "bnhd"
+    for dt in (torch.float32, w.torch_dtype):
+        o = sage.attn_fwd(g["qk_dev"], g["vq_dev"], causal=w.causal, sm_scale=w.sm_scale, out_dtype=dt, layout=layout)
+        torch.cuda.synchronize()
+        o = (o.transpose(1, 2) if tok else o).cpu()
+        ref = torch.from_numpy(g["O"]).to(dt)
+        assert torch.equal(o.view(torch.int16 if dt != torch.float32 else torch.int32),
+                           ref.view(torch.int16 if dt != torch.float32 else torch.int32)), f"{dt}: differs"
+    qk, vc, vs = run_oracle_quant(w, Q, K, V)
+    O_ref = orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale)
+    assert np.abs(g["O"].reshape(-1, w.d) - O_ref).max() <= O_TOL
+    assert nqt >= 2
+
+
 @pytest.mark.parametrize("name", ["gqa4-xcd-causal-d128", "chunk256-of-1024-causal-blkq64"])
 def test_token_major_layout_is_bit_identical(name):
     """The layout only changes addressing: codes, scales and O bits agree."""
