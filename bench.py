@@ -220,6 +220,31 @@ def mfma_sustained(sage, stream, attn_tops, reps=3):
             "implied_clock_ghz": round(2.4 * tops / MFMA_PEAK_TOPS, 3), "probe_ms": round(t, 3)}
 
 
+HBM_PROBE_BYTES = 1 << 30   # 1 GiB, four times the last-level cache
+
+
+def hbm_sustained(sage, stream, dev, reps=3):
+    """Sustained HBM read bandwidth from the library's streaming-read probe (1 GiB read once per
+    launch, HIP events on the probe's stream), the measured ceiling of the HBM-bound passes."""
+    buf = torch.empty(HBM_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    ms = []
+    for i in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        st = sage.sage_probe_hbm_read(buf.data_ptr(), HBM_PROBE_BYTES, sink.data_ptr(), stream.cuda_stream)
+        b.record(stream)
+        if st != sage.SAGE_OK:
+            raise RuntimeError(sage.sage_status_string(st))
+        torch.cuda.synchronize()
+        if i:   # the first launch warms up
+            ms.append(a.elapsed_time(b))
+    t = float(np.median(ms))
+    del buf, sink
+    return {"gbs": round(HBM_PROBE_BYTES / (t * 1e-3) / 1e9, 1), "probe_ms": round(t, 4), "bytes": HBM_PROBE_BYTES}
+
+
 def decode_rows(w):
     return w.B * w.H * w.N
 
@@ -305,6 +330,8 @@ def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
     sclk = sample_sclk(lambda: sage.attn_decode(q_keep, kc, vq, causal=w.causal, sm_scale=w.sm_scale, out=out,
                                                 kv_chunk=chunk, workspace=ws))
     log(f"[bench] shader clock while the decode kernels run: {sclk}")
+    hbm = hbm_sustained(sage, stream, dev)
+    log(f"[bench] HBM read probe: {hbm['gbs']:.0f} GB/s sustained; decode at {100 * gbs / hbm['gbs']:.1f}% of it")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)...")
@@ -325,7 +352,9 @@ def bench_decode(args, w, Q, K, V, Qd, Kd, Vd, sage, dev):
         "sclk_during_decode": sclk,
         "roofline": {"bound": "hbm", "kernel": "decode_chunk_kernel + decode_merge_kernel", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name, "decode_chunk_kernel", DECODE_SOURCES)},
+                     "traffic": measured_traffic(w.name, "decode_chunk_kernel", DECODE_SOURCES),
+                     "frac_of_hbm_read_probe": round(gbs / hbm["gbs"], 4)},
+        "hbm_read_sustained": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -439,6 +468,10 @@ def main():
     sclk = sample_sclk(attn_only)
     log(f"[bench] shader clock while the attention kernel runs: {sclk}")
 
+    hbm = hbm_sustained(sage, stream, dev)
+    log(f"[bench] HBM read probe: {hbm['gbs']:.0f} GB/s sustained; quantize passes at "
+        f"{100 * quant_gbs / hbm['gbs']:.1f}% of it (algorithmic bytes)")
+
     sustained = None
     if not w.qk4:
         sustained = mfma_sustained(sage, stream, attn_tops)
@@ -473,8 +506,9 @@ def main():
                      "traffic": measured_traffic(w.name)},
         "quantize": {"ms": round(quant_avg, 4), "bound": "hbm", "algorithmic_bytes": quant_alg,
                      "bytes_moved": quant_act, "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(quant_gbs / HBM_PEAK_GBS, 4)},
+                     "frac": round(quant_gbs / HBM_PEAK_GBS, 4), "frac_of_hbm_read_probe": round(quant_gbs / hbm["gbs"], 4)},
         "mfma_sustained": sustained,
+        "hbm_read_sustained": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

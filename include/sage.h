@@ -422,6 +422,20 @@ int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_s
  */
 int sage_probe_mfma_peak(int workgroups, int iters, int* sink, void* stream);
 
+/*
+ * sage_probe_hbm_read -- a measurement aid, not a step of the method: reads
+ * `bytes` of device memory at `buf` once with 16-byte streaming loads (1024
+ * workgroups of 256 threads, each over one contiguous span, eight loads in
+ * flight per thread) and writes one checksum per thread to sink (device
+ * memory for 1024 * 256 ints).  bytes / the
+ * launch's time is the sustained HBM read bandwidth when bytes is well above
+ * the caches (1 GiB and more): the measured ceiling for the HBM-bound passes
+ * (quantization, decode).  Enqueued on `stream`; errors: SAGE_ERR_INVALID_ARG
+ * (null pointer, bytes not a positive multiple of 16), SAGE_ERR_MISALIGNED,
+ * SAGE_ERR_HIP.
+ */
+int sage_probe_hbm_read(const void* buf, size_t bytes, int* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

