@@ -1,8 +1,9 @@
 """Benchmark of the quantized attention forward on one MI355X.
 
 One step = the whole hot path on one batch of synthetic input: quantize Q and K
-(K smoothing, INT8 per block), quantize V (FP8, per-channel scales), then the
-fused attention kernel.  Inputs are resident in HBM before timing starts.
+(K smoothing, INT8 per block) and V (FP8, per-channel scales) in one library
+call (sage_quantize_qkv, three launches), then the fused attention kernel.
+Inputs are resident in HBM before timing starts.
 
 Metric: attention TOPS = 4*B*H*N^2*d / t (halved for causal) with t the
 wall-clock time of one step.  The JSON line also carries the attention
@@ -397,6 +398,7 @@ def main():
     B, H, N, d, Hkv, Nkv = w.B, w.H, w.N, w.d, w.Hkv, w.Nkv
     ws_qk = torch.empty(max(sage.sage_quantize_qk_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(max(sage.sage_quantize_v_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
+    ws_qkv = torch.empty(max(sage.sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv, d), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, N, d), dtype=w.torch_dtype, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -405,9 +407,9 @@ def main():
             ev[2].record(stream)
         if w.qk4:
             q = sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q)
-        else:
-            q = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)
-        v = sage.quantize_v(Vd, workspace=ws_v)
+            v = sage.quantize_v(Vd, workspace=ws_v)
+        else:   # quantize_qk + quantize_v in one call (three launches)
+            q, v = sage.quantize_qkv(Qd, Kd, Vd, w.blk_q, w.blk_k, workspace=ws_qkv)
         if ev is not None:
             ev[0].record(stream)
         if w.qk4:
@@ -463,8 +465,8 @@ def main():
         else:
             sage.attn_fwd(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
 
-    q_keep = ((sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q) if w.qk4
-               else sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, workspace=ws_qk)), sage.quantize_v(Vd, workspace=ws_v))
+    q_keep = ((sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q), sage.quantize_v(Vd, workspace=ws_v))
+              if w.qk4 else sage.quantize_qkv(Qd, Kd, Vd, w.blk_q, w.blk_k, workspace=ws_qkv))
     sclk = sample_sclk(attn_only)
     log(f"[bench] shader clock while the attention kernel runs: {sclk}")
 

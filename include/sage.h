@@ -20,7 +20,8 @@
  *
  * Entry points, by group
  *  - the path: sage_quantize_qk, sage_quantize_v, sage_attn_fwd (and their
- *    workspace queries); sage_attn_fwd_dump for tests;
+ *    workspace queries); sage_attn_fwd_dump for tests; sage_quantize_qkv,
+ *    the two quantize calls in one;
  *  - the extended shapes (_ex: layouts, grouped heads, Nq != Nkv);
  *  - decode over a quantized KV cache (blog section "FlashAttention for
  *    training and inference: where SageAttention fits": decode is bound by
@@ -161,6 +162,27 @@ int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uin
  */
 int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, int N, int d, uint8_t* v_codes,
                        float* v_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch memory sage_quantize_qkv needs: the K channel sums of
+ * sage_quantize_qk and the V channel maxima of sage_quantize_v (0 for a bad
+ * shape). */
+size_t sage_quantize_qkv_workspace_bytes(int B, int Hkv, int Nkv, int d);
+
+/*
+ * sage_quantize_qkv -- sage_quantize_qk_ex and sage_quantize_v_ex of the same
+ * K/V heads in one call: the same outputs bit for bit (the same kernels'
+ * arithmetic) in three launches instead of six.  Pass 1 quantizes the Q
+ * blocks and takes the per-chunk K channel sums and V channel maxima, the
+ * finalize step the K means and V scales, pass 2 the smoothed K blocks and
+ * the V tiles; fewer, larger launches keep the HBM-bound passes busy on short
+ * sequences.  Arguments as the two calls (V in `layout` with Hkv heads of Nkv
+ * tokens, like K); workspace: sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv,
+ * d) bytes, contents ignored.
+ */
+int sage_quantize_qkv(const void* Q, const void* K, const void* V, int in_dtype, int layout, int B, int Hq, int Hkv,
+                      int Nq, int Nkv, int d, int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                      float* k_scale, float* k_mean, uint8_t* v_codes, float* v_scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * sage_attn_fwd -- attention forward on the quantized operands.

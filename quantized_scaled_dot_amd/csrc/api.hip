@@ -186,6 +186,35 @@ int sage_quantize_v_ex(const void* V, int in_dtype, int layout, int B, int H, in
   return launch_status();
 }
 
+size_t sage_quantize_qkv_workspace_bytes(int B, int Hkv, int Nkv, int d) {
+  if (B < 1 || Hkv < 1 || Nkv < 1 || d < 1) return 0;
+  return (sage::quantize_qk_workspace(B * Hkv, Nkv, d) + 255) / 256 * 256 + sage::quantize_v_workspace(B * Hkv, Nkv, d);
+}
+
+int sage_quantize_qkv(const void* Q, const void* K, const void* V, int in_dtype, int layout, int B, int Hq, int Hkv,
+                      int Nq, int Nkv, int d, int blk_q, int blk_k, int8_t* q_codes, float* q_scale, int8_t* k_codes,
+                      float* k_scale, float* k_mean, uint8_t* v_codes, float* v_scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_TRY(check_blocks(blk_q, blk_k));
+  SAGE_PTR(Q); SAGE_PTR(K); SAGE_PTR(V); SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
+  SAGE_PTR(k_mean); SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(workspace);
+  if (workspace_bytes < sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv, d)) return SAGE_ERR_WORKSPACE;
+  sage::QuantQKArgs a;
+  a.Q = Q; a.K = K; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.d = d; a.blk_q = blk_q; a.blk_k = blk_k;
+  a.q_codes = q_codes; a.q_scale = q_scale; a.k_codes = k_codes; a.k_scale = k_scale; a.k_mean = k_mean;
+  a.workspace = workspace;
+  sage::QuantVArgs v;
+  v.V = V; v.is_bf16 = a.is_bf16; v.nhd = a.nhd; v.B = B; v.H = Hkv; v.N = Nkv; v.d = d;
+  v.v_codes = v_codes; v.v_scale = v_scale;
+  v.workspace = (char*)workspace + (sage::quantize_qk_workspace(B * Hkv, Nkv, d) + 255) / 256 * 256;
+  (void)hipGetLastError();
+  sage::launch_quantize_qkv(a, v, (hipStream_t)stream);
+  return launch_status();
+}
+
 int sage_quantize_v(const void* V, int in_dtype, int B, int H, int N, int d, uint8_t* v_codes, float* v_scale,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return sage_quantize_v_ex(V, in_dtype, SAGE_LAYOUT_BHND, B, H, N, d, v_codes, v_scale, workspace, workspace_bytes,

@@ -102,6 +102,9 @@ struct DecodeArgs {
 // with_q / with_k: quantize Q (blocks), K (mean, smoothed blocks), or both
 void launch_quantize_qk(const QuantQKArgs& a, hipStream_t st, bool with_q = true, bool with_k = true);
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st);
+// quantize_qk and quantize_v of one K/V (v.H = a.Hkv, v.N = a.Nkv, same layout and
+// dtype) in three launches; a.workspace and v.workspace as for the two calls
+void launch_quantize_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t st);
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st);
 size_t quantize_qk_workspace(int BHkv, int Nkv, int d);
 size_t quantize_v_workspace(int BH, int N, int d);

@@ -140,7 +140,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
 // converts once to int64, and the threads' int64 sums are combined through
 // LDS.  With at most 2^19 tokens a head's sum stays within 2^62.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool STREAM = true>
 __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_bf16, InRows in, int nchunk, int lin,
                                          long long* __restrict__ partial, long long (*red)[D]) {
   const int N = in.N;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void k_colsum(const uint16_t* __restrict__ K, int is_
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = load16_in<true>(base + (size_t)(r0 + i * RPP) * rs);
+    for (int i = 0; i < RPT; i++) raw[i] = load16_in<STREAM>(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) add_row(raw[i]);
   } else {
@@ -198,14 +198,13 @@ __global__ __launch_bounds__(256) void qk_pass1_kernel(const uint16_t* __restric
 
 // mean_c = fp32(fp64(sum_chunks s_c) * 2^-24 / N).  Grid: BH * D/16; a block
 // of 256 = 16 channels x 16 chunk lanes.
-__global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict__ partial, int nchunk, int N, int D,
-                                                      float* __restrict__ k_mean) {
-  const int ng = D / 16, g = blockIdx.x % ng, bh = blockIdx.x / ng;
+__device__ __forceinline__ void k_mean_group(const long long* __restrict__ partial, int nchunk, int N, int D,
+                                             float* __restrict__ k_mean, int lin, long long (*red)[16]) {
+  const int ng = D / 16, g = lin % ng, bh = lin / ng;
   const int cl = threadIdx.x & 15, j = threadIdx.x >> 4;
   const int c = g * 16 + cl;
   long long s = 0;
   for (int ch = j; ch < nchunk; ch += 16) s += partial[((size_t)bh * nchunk + ch) * D + c];
-  __shared__ long long red[16][16];
   red[j][cl] = s;
   __syncthreads();
   if (threadIdx.x < 16) {
@@ -213,6 +212,11 @@ __global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict
     for (int k = 0; k < 16; k++) tot += red[k][threadIdx.x];
     k_mean[(size_t)bh * D + g * 16 + threadIdx.x] = (float)(((double)tot * 0x1p-24) / (double)N);
   }
+}
+__global__ __launch_bounds__(256) void k_mean_kernel(const long long* __restrict__ partial, int nchunk, int N, int D,
+                                                      float* __restrict__ k_mean) {
+  __shared__ long long red[16][16];
+  k_mean_group(partial, nchunk, N, D, k_mean, blockIdx.x, red);
 }
 
 // Pass 2 of quantize_qk: INT8 blocks of BLKK tokens of the smoothed K.
@@ -228,14 +232,14 @@ __global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // Per-channel maxima of |V| over one chunk of tokens.  Grid: nchunk * BH.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
-                                                        int nchunk, float* __restrict__ partial) {
+template <int D, bool STREAM = true>
+__device__ __forceinline__ void v_colmax_chunk(const uint16_t* __restrict__ V, int is_bf16, InRows in, int nchunk,
+                                               float* __restrict__ partial, int lin, float (*red)[D]) {
   const int N = in.N;
   const size_t rs = in.stride(D);
   constexpr int TPR = D / 8;
   constexpr int RPP = 256 / TPR;
-  const int chunk = blockIdx.x % nchunk, bh = blockIdx.x / nchunk;
+  const int chunk = lin % nchunk, bh = lin / nchunk;
   const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
   const int n0 = chunk * kStatChunk;
   const int nrows = min(kStatChunk, N - n0);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
     constexpr int RPT = kStatChunk / RPP;
     v4i raw[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; i++) raw[i] = load16_in<true>(base + (size_t)(r0 + i * RPP) * rs);
+    for (int i = 0; i < RPT; i++) raw[i] = load16_in<STREAM>(base + (size_t)(r0 + i * RPP) * rs);
 #pragma unroll
     for (int i = 0; i < RPT; i++) max_row(raw[i]);
   } else {
@@ -265,7 +269,6 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) s[e] = load_h(mx[e >> 1][e & 1], is_bf16);
-  __shared__ float red[RPP][D];
 #pragma unroll
   for (int e = 0; e < 8; e++) red[r0][cg * 8 + e] = s[e];
   __syncthreads();
@@ -275,17 +278,23 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
     partial[((size_t)bh * nchunk + chunk) * D + c] = m;
   }
 }
+template <int D>
+__global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
+                                                        int nchunk, float* __restrict__ partial) {
+  __shared__ float red[256 / (D / 8)][D];
+  v_colmax_chunk<D>(V, is_bf16, in, nchunk, partial, blockIdx.x, red);
+}
 
 // scale_c = a_c / 448, r_c = 448 / a_c (0 and 0 when a_c < 2^-120).
 // Grid: BH * D/16; a block of 256 = 16 channels x 16 chunk lanes.
-__global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ partial, int nchunk, int D,
-                                                       float* __restrict__ v_scale, float* __restrict__ v_recip) {
-  const int ng = D / 16, g = blockIdx.x % ng, bh = blockIdx.x / ng;
+__device__ __forceinline__ void v_scale_group(const float* __restrict__ partial, int nchunk, int D,
+                                              float* __restrict__ v_scale, float* __restrict__ v_recip, int lin,
+                                              float (*red)[16]) {
+  const int ng = D / 16, g = lin % ng, bh = lin / ng;
   const int cl = threadIdx.x & 15, j = threadIdx.x >> 4;
   const int c = g * 16 + cl;
   float a = 0.0f;
   for (int ch = j; ch < nchunk; ch += 16) a = fmaxf(a, partial[((size_t)bh * nchunk + ch) * D + c]);
-  __shared__ float red[16][16];
   red[j][cl] = a;
   __syncthreads();
   if (threadIdx.x < 16) {
@@ -296,6 +305,11 @@ __global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ 
     v_scale[o] = zero ? 0.0f : m / 448.0f;
     v_recip[o] = zero ? 0.0f : 448.0f / m;
   }
+}
+__global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ partial, int nchunk, int D,
+                                                       float* __restrict__ v_scale, float* __restrict__ v_recip) {
+  __shared__ float red[16][16];
+  v_scale_group(partial, nchunk, D, v_scale, v_recip, blockIdx.x, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -308,13 +322,13 @@ __global__ __launch_bounds__(256) void v_scale_kernel(const float* __restrict__ 
 // Grid: BH * P/64.  Block: 16 * D/8 threads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
-                                                              const float* __restrict__ v_recip,
-                                                              uint8_t* __restrict__ v_codes) {
+__device__ __forceinline__ void v_quant_tile(const uint16_t* __restrict__ V, int is_bf16, InRows in,
+                                             const float* __restrict__ v_recip, uint8_t* __restrict__ v_codes,
+                                             int lin, int t) {
   const int ntile = in.P / kKTile;
   const size_t rs = in.stride(D);
-  const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
-  const int t = threadIdx.x, cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
+  const int tile = lin % ntile, bh = lin / ntile;
+  const int cg = t >> 4, tg = t & 15;   // channels 8cg.., tokens 4tg..4tg+3
   const uint16_t* src = V + in.head(bh, D) + 8 * cg;   // channel group of this head; rows added below
   const v4f r0 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg);
   const v4f r1 = *(const v4f*)(v_recip + (size_t)bh * D + 8 * cg + 4);
@@ -337,6 +351,68 @@ __global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __r
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][e], y[1][e], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][e], y[3][e], w, true);
     __builtin_nontemporal_store(r[e] == 0.0f ? 0 : w, (int*)(dst + (size_t)e * kKTile));
+  }
+}
+template <int D>
+__global__ __launch_bounds__(16 * D / 8) void v_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in,
+                                                              const float* __restrict__ v_recip,
+                                                              uint8_t* __restrict__ v_codes) {
+  v_quant_tile<D>(V, is_bf16, in, v_recip, v_codes, blockIdx.x, threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// quantize_qkv: the two calls above in three launches instead of six (the
+// same device functions and arithmetic, so the same bits): pass 1 = Q blocks,
+// K channel sums and V channel maxima; finalize = K means and V scales;
+// pass 2 = V tiles, then smoothed K blocks (V was read last).  Each workgroup
+// takes one item of one of the parts by its index range.  When K and V
+// together are not much larger than the last-level cache (CACHED), pass 1
+// reads them with ordinary loads so that pass 2 finds part of them there;
+// otherwise with streaming loads (measured: 4-6% faster at 268 MB and 134 MB
+// of K and V, 1% slower at 402 MB).
+// ---------------------------------------------------------------------------
+template <int D, int BLKQ, bool CACHED>
+__global__ __launch_bounds__(256) void qkv_pass1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                         const uint16_t* __restrict__ V, int is_bf16, InRows qin,
+                                                         InRows kin, int nq, int nk, int nchunk,
+                                                         int8_t* __restrict__ q_codes, float* __restrict__ q_scale,
+                                                         long long* __restrict__ ksum, float* __restrict__ vmax) {
+  __shared__ long long red[256 / (D / 8)][D];   // K sums; V maxima use the first half as floats
+  __shared__ float red4[4];
+  const int b = blockIdx.x;
+  if (b < nq) quant_block<D, BLKQ, false>(Q, is_bf16, qin, nullptr, q_codes, q_scale, b, red4);
+  else if (b < nq + nk) k_colsum<D, !CACHED>(K, is_bf16, kin, nchunk, b - nq, ksum, red);
+  else v_colmax_chunk<D, !CACHED>(V, is_bf16, kin, nchunk, vmax, b - nq - nk, (float (*)[D])&red[0][0]);
+}
+
+__global__ __launch_bounds__(256) void qkv_finalize_kernel(const long long* __restrict__ ksum,
+                                                            const float* __restrict__ vmax, int nchunk, int N, int D,
+                                                            int ng, float* __restrict__ k_mean,
+                                                            float* __restrict__ v_scale, float* __restrict__ v_recip) {
+  __shared__ long long red[16][16];   // V scales use it as floats
+  const int b = blockIdx.x;
+  if (b < ng) k_mean_group(ksum, nchunk, N, D, k_mean, b, red);
+  else v_scale_group(vmax, nchunk, D, v_scale, v_recip, b - ng, (float (*)[16])&red[0][0]);
+}
+
+// pass 2: V tiles (one per workgroup at d = 128; two per workgroup of 256
+// threads at d = 64, whose tiles take 128 threads), then nkq workgroups of
+// smoothed K blocks
+template <int D, int BLKK>
+__global__ __launch_bounds__(256) void qkv_pass2_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                         int is_bf16, InRows kin, int nkq, int ntiles,
+                                                         const float* __restrict__ k_mean, int8_t* __restrict__ k_codes,
+                                                         float* __restrict__ k_scale, const float* __restrict__ v_recip,
+                                                         uint8_t* __restrict__ v_codes) {
+  __shared__ float red4[4];
+  constexpr int TPT = 16 * D / 8;   // threads per V tile
+  const int nvw = (ntiles + 256 / TPT - 1) / (256 / TPT);
+  const int b = blockIdx.x;
+  if (b >= nvw) {
+    quant_block<D, BLKK, true>(K, is_bf16, kin, k_mean, k_codes, k_scale, b - nvw, red4);
+  } else {
+    const int tile = b * (256 / TPT) + (int)threadIdx.x / TPT;
+    if (tile < ntiles) v_quant_tile<D>(V, is_bf16, kin, v_recip, v_codes, tile, (int)threadIdx.x % TPT);
   }
 }
 
@@ -532,6 +608,56 @@ static void launch_v_d(const QuantVArgs& a, hipStream_t st) {
                      a.v_scale, recip);
   hipLaunchKernelGGL(v_quant_kernel<D>, dim3(in.P / kKTile * BH), dim3(16 * D / 8), 0, st, (const uint16_t*)a.V,
                      a.is_bf16, in, (const float*)recip, a.v_codes);
+}
+
+template <int D, int BLKQ, int BLKK>
+static void launch_qkv_d(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t st) {
+  const int BHkv = a.B * a.Hkv;
+  const int nchunk = stat_chunks(a.Nkv);
+  long long* ksum = (long long*)a.workspace;
+  float* vmax = (float*)v.workspace;
+  float* recip = vmax + (size_t)BHkv * nchunk * D;
+  const InRows qin{a.Hq, a.Nq, round_up(a.Nq, kQTile), a.nhd}, kin{a.Hkv, a.Nkv, round_up(a.Nkv, kKTile), a.nhd};
+  const int nq = a.B * a.Hq * (qin.P / BLKQ) / blocks_per_wg<D, BLKQ>();
+  const int nk = BHkv * nchunk;
+  // K and V of at most 320 MB together: ordinary loads in pass 1 (the last-level cache is 256 MB;
+  // measured faster at 268 MB, slower at 402 MB)
+  const bool cached = 2.0 * 2.0 * BHkv * a.Nkv * D <= 320.0 * (1 << 20);
+  if (cached)
+    hipLaunchKernelGGL((qkv_pass1_kernel<D, BLKQ, true>), dim3(nq + 2 * nk), dim3(256), 0, st, (const uint16_t*)a.Q,
+                       (const uint16_t*)a.K, (const uint16_t*)v.V, a.is_bf16, qin, kin, nq, nk, nchunk, a.q_codes,
+                       a.q_scale, ksum, vmax);
+  else
+    hipLaunchKernelGGL((qkv_pass1_kernel<D, BLKQ, false>), dim3(nq + 2 * nk), dim3(256), 0, st, (const uint16_t*)a.Q,
+                       (const uint16_t*)a.K, (const uint16_t*)v.V, a.is_bf16, qin, kin, nq, nk, nchunk, a.q_codes,
+                       a.q_scale, ksum, vmax);
+  const int ng = BHkv * (D / 16);
+  hipLaunchKernelGGL(qkv_finalize_kernel, dim3(2 * ng), dim3(256), 0, st, (const long long*)ksum, (const float*)vmax,
+                     nchunk, a.Nkv, D, ng, a.k_mean, v.v_scale, recip);
+  const int nkq = BHkv * (kin.P / BLKK) / blocks_per_wg<D, BLKK>();
+  const int ntiles = BHkv * (kin.P / kKTile);
+  constexpr int TPW = 256 / (16 * D / 8);   // V tiles per workgroup
+  hipLaunchKernelGGL((qkv_pass2_kernel<D, BLKK>), dim3(nkq + (ntiles + TPW - 1) / TPW), dim3(256), 0, st,
+                     (const uint16_t*)a.K, (const uint16_t*)v.V, a.is_bf16, kin, nkq, ntiles, (const float*)a.k_mean,
+                     a.k_codes, a.k_scale, (const float*)recip, v.v_codes);
+}
+
+template <int D, int BLKQ>
+static void launch_qkv_q(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t st) {
+  if (a.blk_k == 64) launch_qkv_d<D, BLKQ, 64>(a, v, st);
+  else if (a.blk_k == 32) launch_qkv_d<D, BLKQ, 32>(a, v, st);
+  else launch_qkv_d<D, BLKQ, 16>(a, v, st);
+}
+template <int D>
+static void launch_qkv_dd(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t st) {
+  if (a.blk_q == 128) launch_qkv_q<D, 128>(a, v, st);
+  else if (a.blk_q == 64) launch_qkv_q<D, 64>(a, v, st);
+  else launch_qkv_q<D, 32>(a, v, st);
+}
+
+void launch_quantize_qkv(const QuantQKArgs& a, const QuantVArgs& v, hipStream_t st) {
+  if (a.d == 128) launch_qkv_dd<128>(a, v, st);
+  else launch_qkv_dd<64>(a, v, st);
 }
 
 void launch_quantize_v(const QuantVArgs& a, hipStream_t st) {

@@ -23,6 +23,7 @@ SAGE_LAYOUT_BHND, SAGE_LAYOUT_BNHD = 0, 1
 #: exported symbols, in header order
 SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_bytes", "sage_quantize_qk",
            "sage_quantize_qk_ex", "sage_quantize_v_workspace_bytes", "sage_quantize_v", "sage_quantize_v_ex",
+           "sage_quantize_qkv_workspace_bytes", "sage_quantize_qkv",
            "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
            "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode",
            "sage_attn_decode_noalloc", "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
@@ -87,6 +88,10 @@ _lib.sage_attn_fwd_ex_dump.restype = _I
 _lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
 _lib.sage_probe_mfma_peak.restype = _I
 _lib.sage_probe_mfma_peak.argtypes = [_I, _I, _P, _P]
+_lib.sage_quantize_qkv_workspace_bytes.restype = _SZ
+_lib.sage_quantize_qkv_workspace_bytes.argtypes = [_I] * 4
+_lib.sage_quantize_qkv.restype = _I
+_lib.sage_quantize_qkv.argtypes = [_P] * 3 + [_I] * 10 + [_P] * 8 + [_SZ, _P]
 _lib.sage_probe_hbm_read.restype = _I
 _lib.sage_probe_hbm_read.argtypes = [_P, _SZ, _P, _P]
 
@@ -113,6 +118,16 @@ def sage_kv_tile():
 
 def sage_probe_mfma_peak(workgroups, iters, sink=None, stream=None):
     return _lib.sage_probe_mfma_peak(workgroups, iters, sink, stream)
+
+
+def sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv, d):
+    return _lib.sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv, d)
+
+
+def sage_quantize_qkv(Q, K, V, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, q_codes, q_scale, k_codes,
+                      k_scale, k_mean, v_codes, v_scale, workspace, workspace_bytes, stream):
+    return _lib.sage_quantize_qkv(Q, K, V, in_dtype, layout, B, Hq, Hkv, Nq, Nkv, d, blk_q, blk_k, q_codes, q_scale,
+                                  k_codes, k_scale, k_mean, v_codes, v_scale, workspace, workspace_bytes, stream)
 
 
 def sage_probe_hbm_read(buf, nbytes, sink, stream=None):
@@ -382,6 +397,33 @@ def quantize_v(V, layout="bhnd", workspace=None, stream=None):
     else:
         _check(sage_quantize_v_ex(_ptr(V), dt, _layout(layout), B, H, N, d, *rest))
     return v_codes, v_scale
+
+
+def quantize_qkv(Q, K, V, blk_q=128, blk_k=64, layout="bhnd", workspace=None, stream=None):
+    """quantize_qk(Q, K) and quantize_v(V) in one library call (the same outputs bit for bit,
+    fewer launches).  Returns (qk dict, (v_codes, v_scale)) as those two helpers do."""
+    B, Hq, Nq, d = _bhnd(Q, layout)
+    Bk, Hkv, Nkv, dk = _bhnd(K, layout)
+    if (Bk, dk) != (B, d) or K.dtype != Q.dtype or K.device != Q.device:
+        raise ValueError("Q and K must have the same batch, head dim, dtype and device")
+    if tuple(V.shape) != tuple(K.shape) or V.dtype != K.dtype or V.device != K.device:
+        raise ValueError("V must have the shape, dtype and device of K")
+    dev = Q.device
+    Nqp, Nkt = _round_up(Nq, 128), _round_up(Nkv, sage_kv_tile())
+    out = dict(q_codes=torch.empty((B, Hq, Nqp, d), dtype=torch.int8, device=dev),
+               q_scale=torch.empty((B, Hq, Nqp // blk_q), dtype=torch.float32, device=dev),
+               k_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
+               k_scale=torch.empty((B, Hkv, Nkt // blk_k), dtype=torch.float32, device=dev),
+               k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=dev))
+    v_codes = torch.empty((B, Hkv, Nkt // sage_kv_tile(), d, sage_kv_tile()), dtype=torch.uint8, device=dev)
+    v_scale = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+    workspace = _workspace(workspace, sage_quantize_qkv_workspace_bytes(B, Hkv, Nkv, d), dev)
+    _check(sage_quantize_qkv(_ptr(Q), _ptr(K), _ptr(V), _DT.get(Q.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv, d,
+                             blk_q, blk_k, _ptr(out["q_codes"]), _ptr(out["q_scale"]), _ptr(out["k_codes"]),
+                             _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(v_codes), _ptr(v_scale), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    out.update(blk_q=blk_q, blk_k=blk_k, Nq=Nq, Nkv=Nkv)
+    return out, (v_codes, v_scale)
 
 
 def v_codes_to_natural(v_codes):

@@ -317,6 +317,43 @@ def test_wide_workgroups_equal_the_128_row_kernel(name, layout):
     assert nqt >= 2
 
 
+QKV_CASES = ["gqa4-causal-bf16-d128", "gqa2-xcd-f16-d64", "ragged-gqa-causal-130-of-1000", "ragged-f16-d64-N77-blkq64",
+             "fine-q32-k16-ragged-gqa-d64", "fine-k32-outliers-causal", "ragged-single-token-causal"]
+
+
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+@pytest.mark.parametrize("name", QKV_CASES + ["llm-prefill-4k-causal", "video-dit-32k"])
+def test_fused_qkv_quantize_equals_the_two_calls(name, layout):
+    """sage_quantize_qkv gives the codes, scales and K means of sage_quantize_qk + sage_quantize_v
+    bit for bit (including the zero padding), on grouped, ragged and finer-block shapes and two
+    full-size workloads."""
+    if name in synth.WORKLOADS:
+        if layout == "bnhd":
+            pytest.skip("the full-size workloads run in the head-major layout")
+        w = synth.WORKLOADS[name]
+    else:
+        w = small_ex_workload(name)
+    sage = _sage()
+    Q, K, V = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    tok = layout == "bnhd"
+    Qd, Kd, Vd = ((t.transpose(1, 2) if tok else t).contiguous().to(dev) for t in (Q, K, V))
+    qk = sage.quantize_qk(Qd, Kd, w.blk_q, w.blk_k, layout=layout)
+    vq = sage.quantize_v(Vd, layout=layout)
+    qk2, vq2 = sage.quantize_qkv(Qd, Kd, Vd, w.blk_q, w.blk_k, layout=layout)
+    torch.cuda.synchronize()
+    for key in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean"):
+        a, b = qk[key].cpu(), qk2[key].cpu()
+        assert a.shape == b.shape and torch.equal(a.view(torch.uint8), b.view(torch.uint8)), key
+    for a, b in zip(vq, vq2):
+        assert torch.equal(a.cpu().view(torch.uint8), b.cpu().view(torch.uint8))
+    if name not in synth.WORKLOADS:   # and the oracle's, on the small shapes
+        g = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in qk2.items()}
+        g["v_codes"] = sage.v_codes_to_natural(vq2[0]).cpu().numpy()
+        g["v_scale"] = vq2[1].cpu().numpy()
+        check_quant_bit_exact(g, *run_oracle_quant(w, Q, K, V))
+
+
 @pytest.mark.parametrize("name", ["gqa4-xcd-causal-d128", "chunk256-of-1024-causal-blkq64"])
 def test_token_major_layout_is_bit_identical(name):
     """The layout only changes addressing: codes, scales and O bits agree."""
