@@ -258,8 +258,10 @@ def quantize_qk4(Q_bits, K_bits, dtype, smooth_q=False):
     """E2M1 blocks of 32 channels of Q [B,Hq,Nq,d] and of the smoothed K
     [B,Hkv,Nkv,d]: codes (one per value, 0..15) and E8M0 scale bytes per block.
     smooth_q: Q minus the mean of its 32-query block, which is returned as
-    q_mean [B,Hq,ceil(Nq/32),d] and its e4m3 codes / E8M0 scales, with the
-    smoothed K also in e4m3 blocks (k8_codes, k8_scale) for the mean's term."""
+    q_mean [B,Hq,ceil(Nq/32),d] with its INT8 codes qm_codes and one exponent
+    byte per block qm_scale [B,Hq,ceil(Nq/32)] (scale 2^(byte - 127)), and the
+    smoothed K also in INT8 blocks of 64 keys, k8_codes [B,Hkv,Nkv,d] and
+    k8_scale [B,Hkv,ceil(Nkv/64)], for the mean's term."""
     Q_bits = _c(Q_bits, np.uint16)
     K_bits = _c(K_bits, np.uint16)
     B, Hq, Nq, d = Q_bits.shape
@@ -273,12 +275,12 @@ def quantize_qk4(Q_bits, K_bits, dtype, smooth_q=False):
     if smooth_q:
         nb = -(-Nq // 32)
         qmean = np.empty((B, Hq, nb, d), np.float32)
-        qmc = np.empty((B, Hq, nb, d), np.uint8)
-        qms = np.empty((B, Hq, nb, d // 32), np.uint8)
+        qmc = np.empty((B, Hq, nb, d), np.int8)
+        qms = np.empty((B, Hq, nb), np.uint8)
         rc = lib().oracle_quantize_q4_smooth(_p(Q_bits), dtype, B * Hq, Nq, d, _p(qc), _p(qs), _p(qmean), _p(qmc),
                                              _p(qms))
-        k8c = np.empty((B, Hkv, Nkv, d), np.uint8)
-        k8s = np.empty((B, Hkv, Nkv, d // 32), np.uint8)
+        k8c = np.empty((B, Hkv, Nkv, d), np.int8)
+        k8s = np.empty((B, Hkv, -(-Nkv // 64)), np.uint8)
         rc |= lib().oracle_quantize_k8(_p(K_bits), dtype, B * Hkv, Nkv, d, _p(k8c), _p(k8s))
         extra = dict(q_mean=qmean, qm_codes=qmc, qm_scale=qms, k8_codes=k8c, k8_scale=k8s)
     else:
@@ -290,10 +292,11 @@ def quantize_qk4(Q_bits, K_bits, dtype, smooth_q=False):
 
 
 def _qm(qk4):
-    """The Q-mean and FP8 K codes and scales of a smoothed quantization, else NULLs."""
+    """The Q-mean and INT8 K codes and exponent bytes of a smoothed quantization, else NULLs."""
     if "qm_codes" not in qk4:
         return None, None, None, None
-    return tuple(_c(qk4[k], np.uint8) for k in ("qm_codes", "qm_scale", "k8_codes", "k8_scale"))
+    return (_c(qk4["qm_codes"], np.int8), _c(qk4["qm_scale"], np.uint8), _c(qk4["k8_codes"], np.int8),
+            _c(qk4["k8_scale"], np.uint8))
 
 
 def qk4_scores(qk4, rows):

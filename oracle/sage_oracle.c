@@ -322,34 +322,41 @@ int oracle_quantize_q4(const uint16_t* Q, int dtype, int BH, int N, int d, uint8
 /* qm[c] = fp32(S / n), S the fp64 sum of the block's rows in ascending row  */
 /* order; each row is quantized as RN(q - qm) in the E2M1 blocks above.  The */
 /* removed part returns in the scores as qm . k (see score4), with qm and  */
-/* the smoothed K both in FP8 (e4m3) blocks of 32 channels with one power-  */
-/* of-two scale each (quant_block_mx8; K in oracle_quantize_k8): an 8-bit    */
-/* product, since qm can be large and 4-bit K codes would carry their error */
-/* into it.                                                                  */
+/* the smoothed K both in INT8 with one power-of-two scale per block        */
+/* (quant_int8_pow2): qm per 32-query block over all d channels, K per      */
+/* block of 64 consecutive keys (the last block holds the rest) over all d  */
+/* channels (oracle_quantize_k8).  8-bit, since qm can be large and 4-bit K */
+/* codes would carry their error into the product; integer, so that the    */
+/* term is an exact integer sum times 2^(Em + Ek).                          */
 /* Outputs: q4 codes/scales as oracle_quantize_q4; q_mean [BH, nb, d] fp32, */
-/* qm_codes [BH, nb, d] e4m3, qm_scale [BH, nb, d/32] E8M0; nb = ceil(N/32). */
+/* qm_codes [BH, nb, d] int8, qm_scale [BH, nb] exponent bytes; nb =        */
+/* ceil(N/32).                                                               */
 
-/* n values (n <= 32) with one shared exponent E = floor(log2(max|x|)) - 7,  */
-/* clamped to [-127, 127] (the block max lands in [128, 256), below the     */
-/* e4m3 saturation at 448); codes = E(x / 2^E); scale byte E + 127; an      */
-/* all-zero block gets scale byte 0 and zero codes.                         */
-static void quant_block_mx8(const float* x, int n, uint8_t* codes, uint8_t* scale) {
+/* n values with one power-of-two scale 2^E for INT8 codes: E = the smallest */
+/* exponent in [-63, 52] with max|x| * 2^-E <= 127 (an all-zero block gets  */
+/* -63); codes = RN(x * 2^-E), ties to even, saturated at +-127 (reached    */
+/* only at the upper clamp); scale byte E + 127.                             */
+static void quant_int8_pow2(const float* x, size_t n, int8_t* codes, uint8_t* scale) {
   float a = 0.0f;
-  for (int k = 0; k < n; k++) a = fmaxf(a, fabsf(x[k]));
-  if (a == 0.0f) {
-    *scale = 0;
-    for (int k = 0; k < n; k++) codes[k] = 0;
-    return;
+  for (size_t k = 0; k < n; k++) a = fmaxf(a, fabsf(x[k]));
+  int e = -63;
+  if (a != 0.0f) {
+    e = ilogb((double)a) - 6;                       /* a * 2^-e in [64, 128) */
+    if (ldexp((double)a, -e) > 127.0) e += 1;       /* then in [32, 64) */
+    if (e < -63) e = -63;
+    if (e > 52) e = 52;
   }
-  int e = (int)floor(log2((double)a)) - 7;
-  if (e < -127) e = -127;
-  if (e > 127) e = 127;
   *scale = (uint8_t)(e + 127);
-  for (int k = 0; k < n; k++) codes[k] = oracle_e4m3_encode((float)ldexp((double)x[k], -e));
+  for (size_t k = 0; k < n; k++) {
+    double y = nearbyint(ldexp((double)x[k], -e));   /* exact scaling, ties to even */
+    if (y > 127.0) y = 127.0;
+    if (y < -127.0) y = -127.0;
+    codes[k] = (int8_t)y;
+  }
 }
 
 int oracle_quantize_q4_smooth(const uint16_t* Q, int dtype, int BH, int N, int d, uint8_t* q4_codes,
-                              uint8_t* q4_scale, float* q_mean, uint8_t* qm_codes, uint8_t* qm_scale) {
+                              uint8_t* q4_scale, float* q_mean, int8_t* qm_codes, uint8_t* qm_scale) {
   if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
   const int nb = (N + 31) / 32;
 #pragma omp parallel for schedule(dynamic)
@@ -363,9 +370,7 @@ int oracle_quantize_q4_smooth(const uint16_t* Q, int dtype, int BH, int N, int d
         for (int i = 0; i < n; i++) sum += (double)load_in(Q, ((size_t)bh * N + n0 + i) * d + c, dtype);
         qm[c] = (float)(sum / n);
       }
-      for (int b = 0; b < d / 32; b++)
-        quant_block_mx8(qm + 32 * b, 32, qm_codes + ((size_t)bh * nb + blk) * d + 32 * b,
-                        qm_scale + ((size_t)bh * nb + blk) * (d / 32) + b);
+      quant_int8_pow2(qm, (size_t)d, qm_codes + ((size_t)bh * nb + blk) * d, qm_scale + (size_t)bh * nb + blk);
       for (int i = 0; i < n; i++)
         for (int b = 0; b < d / 32; b++) {
           const size_t r = (size_t)bh * N + n0 + i;
@@ -378,20 +383,23 @@ int oracle_quantize_q4_smooth(const uint16_t* Q, int dtype, int BH, int N, int d
 }
 
 /* The smoothed K (the same mean and fp32 subtraction as oracle_quantize_k4) */
-/* in e4m3 blocks of 32 channels: k8_codes [BH, N, d], k8_scale [BH, N, d/32]. */
-int oracle_quantize_k8(const uint16_t* K, int dtype, int BH, int N, int d, uint8_t* k8_codes, uint8_t* k8_scale) {
+/* in INT8 blocks of 64 keys x d channels, one power-of-two scale each:      */
+/* k8_codes [BH, N, d] int8, k8_scale [BH, ceil(N/64)] exponent bytes.       */
+int oracle_quantize_k8(const uint16_t* K, int dtype, int BH, int N, int d, int8_t* k8_codes, uint8_t* k8_scale) {
   if (BH < 1 || N < 1 || d < 32 || d % 32) return -1;
+  const int nkb = (N + 63) / 64;
 #pragma omp parallel for schedule(dynamic)
   for (int bh = 0; bh < BH; bh++) {
     float* mu = (float*)malloc(sizeof(float) * d);
+    float* buf = (float*)malloc(sizeof(float) * 64 * d);
     kmean_head(K + (size_t)bh * N * d, dtype, N, d, mu, NULL);
-    float buf[32];
-    for (int n = 0; n < N; n++)
-      for (int b = 0; b < d / 32; b++) {
-        const size_t r = ((size_t)bh * N + n);
-        for (int k = 0; k < 32; k++) buf[k] = load_in(K, r * d + 32 * b + k, dtype) - mu[32 * b + k];
-        quant_block_mx8(buf, 32, k8_codes + r * d + 32 * b, k8_scale + r * (d / 32) + b);
-      }
+    for (int blk = 0; blk < nkb; blk++) {
+      const int n0 = 64 * blk, n = (N - n0 < 64) ? N - n0 : 64;
+      for (int i = 0; i < n; i++)
+        for (int c = 0; c < d; c++) buf[(size_t)i * d + c] = load_in(K, ((size_t)bh * N + n0 + i) * d + c, dtype) - mu[c];
+      quant_int8_pow2(buf, (size_t)n * d, k8_codes + ((size_t)bh * N + n0) * d, k8_scale + (size_t)bh * nkb + blk);
+    }
+    free(buf);
     free(mu);
   }
   return 0;
@@ -518,12 +526,12 @@ typedef struct {
   const uint8_t* q4s;
   const uint8_t* k4;
   const uint8_t* k4s;
-  /* with Q smoothing (qm != NULL): the FP8 codes and scales of the mean of
-   * the row's 32-query block, and the head's FP8 K codes [Nkv, d] and
-   * scales [Nkv, d/32] */
-  const uint8_t* qm;
-  const uint8_t* qms;
-  const uint8_t* k8;
+  /* with Q smoothing (qm != NULL): the INT8 codes and the exponent byte of
+   * the mean of the row's 32-query block, and the head's INT8 K codes
+   * [Nkv, d] and exponent bytes [ceil(Nkv/64)] */
+  const int8_t* qm;
+  int qms;
+  const int8_t* k8;
   const uint8_t* k8s;
   const int8_t* k;        /* the head's K codes [Nkv, d] */
   const float* ks;        /* the head's K scales [ceil(Nkv/blk_k)] */
@@ -536,9 +544,9 @@ typedef struct {
 
 /* 4-bit score of the row against key j: the exact sum over the 32-channel   */
 /* blocks of 2^(Eq + Ek) times the block's E2M1 dot product, plus with Q     */
-/* smoothing the same sum for the block mean against the FP8 K (2^(Em + Ek8) */
-/* times the e4m3 dot product); fp64, exact for the exponent spreads that occur, */
-/* rounded once to fp32.                                                     */
+/* smoothing the integer dot product of the block mean's INT8 codes with    */
+/* the key's INT8 codes times 2^(Em + Ek8) (Ek8 of the key's 64-key block);  */
+/* fp64, exact for the exponent spreads that occur, rounded once to fp32.   */
 static float score4(const row_ctx* x, int j) {
   const int d = x->d;
   const uint8_t* k = x->k4 + (size_t)j * d;
@@ -548,13 +556,12 @@ static float score4(const row_ctx* x, int j) {
     double blk = 0.0;
     for (int c = 32 * b; c < 32 * b + 32; c++) blk += oracle_e2m1_decode(x->q4[c]) * oracle_e2m1_decode(k[c]);
     s += ldexp(blk, (int)x->q4s[b] + (int)ks[b] - 254);
-    if (x->qm) {
-      const uint8_t* k8 = x->k8 + (size_t)j * d;
-      const int ek8 = x->k8s[(size_t)j * (d / 32) + b];
-      double bm = 0.0;
-      for (int c = 32 * b; c < 32 * b + 32; c++) bm += oracle_e4m3_decode(x->qm[c]) * oracle_e4m3_decode(k8[c]);
-      s += ldexp(bm, (int)x->qms[b] + ek8 - 254);
-    }
+  }
+  if (x->qm) {
+    const int8_t* k8 = x->k8 + (size_t)j * d;
+    int64_t dot = 0;
+    for (int c = 0; c < d; c++) dot += (int64_t)x->qm[c] * (int64_t)k8[c];
+    s += ldexp((double)dot, x->qms + (int)x->k8s[j / 64] - 254);
   }
   return (float)s;
 }
@@ -694,8 +701,8 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
 /* [B*H, N, d/32]; out [nrows, d]; p_codes (optional) as above.              */
 /* ------------------------------------------------------------------------ */
 int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                         const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                         const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                         const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                         const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
                          const float* v_scale, int B, int Hq,
                          int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
                          const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
@@ -716,9 +723,9 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
     if (qm_codes) {
       const int64_t blk = (bh * ((Nq + 31) / 32) + i / 32);
       x.qm = qm_codes + (size_t)blk * d;
-      x.qms = qm_scale + (size_t)blk * (d / 32);
+      x.qms = qm_scale[blk];
       x.k8 = k8_codes + (size_t)bk * Nkv * d;
-      x.k8s = k8_scale + (size_t)bk * Nkv * (d / 32);
+      x.k8s = k8_scale + (size_t)bk * ((Nkv + 63) / 64);
     }
     x.v = v_codes + (size_t)bk * Nkv * d;
     x.Nkv = Nkv; x.d = d; x.blk_k = 1; x.kv_tile = kv_tile;
@@ -739,8 +746,8 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
 
 /* fp32 4-bit scores (score4) of flat query rows bh*Nq + i against every key: [nrows, Nkv] */
 int oracle_qk4_scores(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                      const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                      const uint8_t* k8_codes, const uint8_t* k8_scale, int B, int Hq,
+                      const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                      const int8_t* k8_codes, const uint8_t* k8_scale, int B, int Hq,
                       int Hkv, int Nq, int Nkv, int d, const int64_t* rows,
                       int nrows, float* out) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d % 32) return -1;
@@ -756,9 +763,9 @@ int oracle_qk4_scores(const uint8_t* q4_codes, const uint8_t* q4_scale, const ui
     if (qm_codes) {
       const int64_t blk = (bh * ((Nq + 31) / 32) + i / 32);
       x.qm = qm_codes + (size_t)blk * d;
-      x.qms = qm_scale + (size_t)blk * (d / 32);
+      x.qms = qm_scale[blk];
       x.k8 = k8_codes + (size_t)bk * Nkv * d;
-      x.k8s = k8_scale + (size_t)bk * Nkv * (d / 32);
+      x.k8s = k8_scale + (size_t)bk * ((Nkv + 63) / 64);
     }
     x.d = d;
     for (int j = 0; j < Nkv; j++) out[(size_t)r * Nkv + j] = score4(&x, j);

@@ -47,8 +47,10 @@ MUTANTS = [
     ("e2m1 ties to the odd code", "(dk == db && (k & 1) == 0)", "(dk == db && (k & 1) == 1)", 1),
     ("mx4 block exponent off by one", "int e = (int)floor(log2((double)a)) - 2;",
      "int e = (int)floor(log2((double)a)) - 1;", 1),
-    ("mx8 block exponent off by one", "int e = (int)floor(log2((double)a)) - 7;",
-     "int e = (int)floor(log2((double)a)) - 8;", 1),
+    ("int8 power-of-two exponent one too large", "e = ilogb((double)a) - 6;", "e = ilogb((double)a) - 5;", 1),
+    ("int8 power-of-two exponent not raised past 127", "if (ldexp((double)a, -e) > 127.0) e += 1;", "", 1),
+    ("int8 power-of-two codes truncated", "double y = nearbyint(ldexp((double)x[k], -e));",
+     "double y = trunc(ldexp((double)x[k], -e));", 1),
     # K smoothing
     ("k mean clamp 2^20 overflows int64 at the length limit", "KMEAN_CLAMP = 524288.0;",
      "KMEAN_CLAMP = 1048576.0;", 1),
@@ -58,8 +60,8 @@ MUTANTS = [
      "buf[(size_t)t * d + c] = load_in(Kh, idx, dtype) + mu[c];", 1),
     ("4-bit K not smoothed", "- mu[32 * b + k];\n        quant_block_mx4(",
      ";\n        quant_block_mx4(", 1),
-    ("FP8 K not smoothed", "- mu[32 * b + k];\n        quant_block_mx8(",
-     ";\n        quant_block_mx8(", 1),
+    ("INT8 K of the mean term not smoothed", "load_in(K, ((size_t)bh * N + n0 + i) * d + c, dtype) - mu[c];",
+     "load_in(K, ((size_t)bh * N + n0 + i) * d + c, dtype);", 1),
     # INT8 block quantizer
     ("int8 scale over 128", "float dl = a / 127.0f;", "float dl = a / 128.0f;", 1),
     ("int8 codes truncated", "float y = rintf(x[k] * r);", "float y = truncf(x[k] * r);", 1),
@@ -76,10 +78,14 @@ MUTANTS = [
      "for (int c = 0; c < d - 1; c++) s += (int32_t)x->q[c] * (int32_t)k[c];", 1),
     ("4-bit block scale off by one", "s += ldexp(blk, (int)x->q4s[b] + (int)ks[b] - 254);",
      "s += ldexp(blk, (int)x->q4s[b] + (int)ks[b] - 253);", 1),
-    ("q-mean term scale off by one", "s += ldexp(bm, (int)x->qms[b] + ek8 - 254);",
-     "s += ldexp(bm, (int)x->qms[b] + ek8 - 255);", 1),
-    ("q-mean term dropped", "s += ldexp(bm, (int)x->qms[b] + ek8 - 254);",
-     "s += 0.0 * ldexp(bm, (int)x->qms[b] + ek8 - 254);", 1),
+    ("q-mean term scale off by one", "s += ldexp((double)dot, x->qms + (int)x->k8s[j / 64] - 254);",
+     "s += ldexp((double)dot, x->qms + (int)x->k8s[j / 64] - 255);", 1),
+    ("q-mean term dropped", "s += ldexp((double)dot, x->qms + (int)x->k8s[j / 64] - 254);",
+     "s += 0.0 * ldexp((double)dot, x->qms + (int)x->k8s[j / 64] - 254);", 1),
+    ("q-mean term with the K block of the previous key", "(int)x->k8s[j / 64]", "(int)x->k8s[j > 0 ? (j - 1) / 64 : 0]",
+     1),
+    ("q-mean term drops the last channel", "for (int c = 0; c < d; c++) dot += (int64_t)x->qm[c] * (int64_t)k8[c];",
+     "for (int c = 0; c < d - 1; c++) dot += (int64_t)x->qm[c] * (int64_t)k8[c];", 1),
     ("k block scale of the previous key", "c2[jj] = (x->dq * x->ks[j / x->blk_k]) * x->s2;",
      "c2[jj] = (x->dq * x->ks[(j > 0 ? j - 1 : 0) / x->blk_k]) * x->s2;", 1),
     ("q block scale of the previous row", "x->dq = q_scale[(size_t)bh * nbq + i / blk_q];",
@@ -126,7 +132,7 @@ MUTANTS = [
     # third batch: split merge, block edge cases, Q-smoothing blocks
     ("split merge: row sums not weighted", "L = fmaf(w, lc[c], L);", "L = L + lc[c];", 1),
     ("split merge: chunks without a visible key kept", "      if (!vis[c]) continue;\n", "", 1),
-    ("all-zero MX blocks get scale byte 127", "    *scale = 0;\n", "    *scale = 127;\n", 2),
+    ("all-zero MX blocks get scale byte 127", "    *scale = 0;\n", "    *scale = 127;\n", 1),
     ("Q-smoothing blocks of 16 rows", "const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;",
      "const int n0 = 16 * blk, n = (N - n0 < 16) ? N - n0 : 16;", 1),
 ]

@@ -887,52 +887,97 @@ def test_q_smoothing_removes_a_per_channel_bias_exactly():
     assert not np.array_equal(p1["q4_codes"], r1["q4_codes"])
 
 
-def test_q_mean_fp8_blocks_properties():
+def _check_int8_pow2_block(x, codes, byte):
+    """INT8 codes of one block with one power-of-two scale 2^e, e = byte - 127:
+    e is the smallest exponent in [-63, 52] with max|x| 2^-e <= 127, and each
+    code is the nearest integer to x 2^-e (ties to the even one)."""
+    x = np.asarray(x, np.float64).ravel()
+    codes = np.asarray(codes).astype(np.int64).ravel()
+    e = int(byte) - 127
+    a = float(np.abs(x).max())
+    assert -63 <= e <= 52
+    assert a * 2.0 ** -e <= 127
+    if e > -63:
+        assert a * 2.0 ** -(e - 1) > 127, "not the smallest exponent"
+    y = x * 2.0 ** -e                      # exact: a power-of-two scaling
+    lo = np.floor(y)
+    frac = y - lo
+    want = np.where(frac > 0.5, lo + 1, np.where(frac < 0.5, lo, np.where(lo % 2 == 0, lo, lo + 1)))
+    assert np.array_equal(codes, want.astype(np.int64))
+    assert np.abs(codes).max(initial=0) <= 127
+
+
+def test_q_mean_int8_blocks_properties():
+    """The block means of Q in INT8, one power-of-two scale per 32-query block
+    over all d channels; an all-zero mean gets the lowest exponent and zero
+    codes; a block max just below 128 steps after the scale goes to the next
+    exponent instead of saturating."""
     rng = np.random.default_rng(52)
     Q = (rng.standard_normal((1, 1, 256, 128)) + rng.standard_normal((1, 1, 1, 128)) * 5).astype(np.float32)
+    Q[0, 0, 64:96] = 0.0                                   # block 2: zero mean
+    Q[0, 0, 96:128] = np.clip(Q[0, 0, 96], -7, 7)          # block 3: 32 equal rows, mean = the row
+    Q[0, 0, 96:128, 7] = 511 / 64                          # 127.75 * 2^-4: exact in f16, just above 127 at e = -4
     K = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
     r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
-    x = r["q_mean"].reshape(-1, 4, 32).astype(np.float64)
-    c = r["qm_codes"].reshape(-1, 4, 32)
-    sc = 2.0 ** (r["qm_scale"].reshape(-1, 4, 1).astype(np.float64) - 127)
-    amax = np.abs(x).max(-1, keepdims=True)
-    assert ((amax / sc >= 128) & (amax / sc < 256)).all()   # below the e4m3 saturation at 448
-    y = orc.e4m3_decode(c) * sc
-    # within half an e4m3 step (3 mantissa bits) of each value, relative to the value's binade
-    t = np.abs(x) / sc
-    step = 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3)
-    assert (np.abs(np.abs(y) / sc - t) <= step / 2 + 1e-12).all()
-    assert (np.signbit(y) == np.signbit(x))[x != 0].all()
-    # a block whose mean is all zero: scale byte 0 and zero codes
-    Qz = Q.copy(); Qz[0, 0, 32:64, 64:96] = 0
-    rz = orc.quantize_qk4(_f16_bits(Qz), _f16_bits(K), 0, smooth_q=True)
-    assert rz["qm_scale"][0, 0, 1, 2] == 0 and (rz["qm_codes"][0, 0, 1, 64:96] == 0).all()
+    assert r["qm_codes"].shape == (1, 1, 8, 128) and r["qm_scale"].shape == (1, 1, 8)
+    assert r["qm_codes"].dtype == np.int8
+    for blk in range(8):
+        _check_int8_pow2_block(r["q_mean"][0, 0, blk], r["qm_codes"][0, 0, blk], r["qm_scale"][0, 0, blk])
+    assert r["qm_scale"][0, 0, 2] == 127 - 63 and not r["qm_codes"][0, 0, 2].any()
+    assert r["q_mean"][0, 0, 3, 7] == np.float32(511 / 64)
+    assert np.abs(r["q_mean"][0, 0, 3]).max() == np.float32(511 / 64)
+    assert r["qm_scale"][0, 0, 3] == 127 - 3 and r["qm_codes"][0, 0, 3, 7] == 64   # 63.875 -> 64 at e = -3
 
 
 def test_smoothed_qk4_scores_against_exact_python_arithmetic():
-    """Score = the E2M1 blocks of the smoothed row against K's E2M1 blocks plus
-    the FP8 mean of the row's block against K's FP8 blocks, each block scaled
-    by its power-of-two scales."""
+    """Score = the E2M1 blocks of the smoothed row against K's E2M1 blocks,
+    each scaled by its power-of-two scales, plus the integer dot product of
+    the row block's INT8 mean codes with the key's INT8 codes times the two
+    blocks' scales (the key's block of 64 keys; 100 keys = a ragged second
+    block), summed exactly and rounded once."""
     from fractions import Fraction
     rng = np.random.default_rng(53)
     Q = (rng.standard_normal((1, 2, 40, 64)) + rng.standard_normal((1, 2, 1, 64)) * 6).astype(np.float32)
-    K = (rng.standard_normal((1, 2, 8, 64)) + rng.standard_normal((1, 2, 1, 64))).astype(np.float32)
+    K = (rng.standard_normal((1, 2, 100, 64)) + rng.standard_normal((1, 2, 1, 64))).astype(np.float32)
+    K[0, 1, 64:] *= 5                                  # head 1: the second K block gets its own scale
     r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    assert r["k8_scale"].shape == (1, 2, 2) and r["k8_scale"][0, 1, 0] != r["k8_scale"][0, 1, 1]
     rows = np.array([0, 33, 40 + 39], dtype=np.int64)   # head 0 rows 0 and 33 (second block), head 1 row 39
     got = orc.qk4_scores(r, rows)
     d4 = [Fraction(float(v)) for v in orc.e2m1_decode(np.arange(16))]
-    d8 = {c: Fraction(float(v)) for c, v in enumerate(orc.e4m3_decode(np.arange(256, dtype=np.uint8))) if np.isfinite(v)}
     for k, row in enumerate(rows):
         h, i = divmod(int(row), 40)
-        for j in range(8):
+        for j in (0, 1, 63, 64, 65, 99):
             s = Fraction(0)
             for b in range(2):
                 ek = int(r["k4_scale"][0, h, j, b])
                 blk = sum(d4[r["q4_codes"][0, h, i, c]] * d4[r["k4_codes"][0, h, j, c]] for c in range(32 * b, 32 * b + 32))
                 s += blk * Fraction(2) ** (int(r["q4_scale"][0, h, i, b]) + ek - 254)
-                bm = sum(d8[r["qm_codes"][0, h, i // 32, c]] * d8[r["k8_codes"][0, h, j, c]] for c in range(32 * b, 32 * b + 32))
-                s += bm * Fraction(2) ** (int(r["qm_scale"][0, h, i // 32, b]) + int(r["k8_scale"][0, h, j, b]) - 254)
+            dot = sum(int(r["qm_codes"][0, h, i // 32, c]) * int(r["k8_codes"][0, h, j, c]) for c in range(64))
+            s += dot * Fraction(2) ** (int(r["qm_scale"][0, h, i // 32]) + int(r["k8_scale"][0, h, j // 64]) - 254)
             assert got[k, j] == np.float32(float(s)), (row, j)
+
+
+def test_q_mean_term_is_close_to_the_exact_mean_times_smoothed_k():
+    """The mean's term (INT8 codes times their scales) is the fp64 product of
+    the block mean and the smoothed key within the quantization bound: each
+    code is within half a step of its value, so |t - qm.k| <= sum_c
+    (|qm_c| dk / 2 + |k_c| dq / 2 + dq dk / 4)."""
+    rng = np.random.default_rng(57)
+    Q = (rng.standard_normal((1, 2, 96, 128)) + rng.standard_normal((1, 2, 1, 128)) * 4).astype(np.float32)
+    K = (rng.standard_normal((1, 2, 150, 128)) + rng.standard_normal((1, 2, 1, 128)) * 2).astype(np.float32)
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
+    ks = (_f16_vals(K) - r["k_mean"][:, :, None, :]).astype(np.float32).astype(np.float64)
+    for h in range(2):
+        for blk in range(3):
+            qm = r["q_mean"][0, h, blk].astype(np.float64)
+            dq = 2.0 ** (int(r["qm_scale"][0, h, blk]) - 127)
+            for j in range(150):
+                dk = 2.0 ** (int(r["k8_scale"][0, h, j // 64]) - 127)
+                t = float(r["qm_codes"][0, h, blk].astype(np.int64) @ r["k8_codes"][0, h, j].astype(np.int64)) * dq * dk
+                exact = float(qm @ ks[0, h, j])
+                bound = float((np.abs(qm) * dk / 2 + np.abs(ks[0, h, j]) * dq / 2 + dq * dk / 4).sum())
+                assert abs(t - exact) <= bound, (h, blk, j, t, exact, bound)
 
 
 def test_q_smoothing_helps_4bit_scores_when_q_has_a_channel_bias():
@@ -954,16 +999,20 @@ def test_q_smoothing_helps_4bit_scores_when_q_has_a_channel_bias():
     assert cs > cp + 0.05 and cs >= 0.98 and cd < cs - 0.05, (cp, cs, cd)
 
 
-def test_k8_blocks_are_the_smoothed_k_in_fp8():
-    """FP8 K blocks: the same K mean as the 4-bit and INT8 paths, the block max
-    in [128, 256) after scaling, values within half an e4m3 step."""
-    Q, K = _q4_case(seed=56)
+def test_k8_blocks_are_the_smoothed_k_in_int8():
+    """INT8 K blocks of the mean term: the same K mean as the 4-bit and INT8
+    paths, one power-of-two scale per 64 keys over all channels (the last
+    block ragged), codes the nearest integers."""
+    rng = np.random.default_rng(56)
+    K = (rng.standard_normal((1, 2, 150, 128)) + rng.standard_normal((1, 2, 1, 128))).astype(np.float32)
+    K[0, 0, 128:] *= 16
+    Q = rng.standard_normal((1, 2, 32, 128)).astype(np.float32)
     r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0, smooth_q=True)
-    ks = (_f16_vals(K) - r["k_mean"][:, :, None, :]).astype(np.float32).reshape(1, 2, 64, 4, 32).astype(np.float64)
-    sc = 2.0 ** (r["k8_scale"].astype(np.float64)[..., None] - 127)
-    amax = np.abs(ks).max(-1, keepdims=True)
-    assert ((amax / sc >= 128) & (amax / sc < 256)).all()
-    y = orc.e4m3_decode(r["k8_codes"].reshape(ks.shape)) * sc
-    t = np.abs(ks) / sc
-    step = 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3)
-    assert (np.abs(np.abs(y) / sc - t) <= step / 2 + 1e-12).all()
+    assert r["k8_codes"].shape == (1, 2, 150, 128) and r["k8_scale"].shape == (1, 2, 3)
+    assert r["k8_codes"].dtype == np.int8
+    ks = (_f16_vals(K) - r["k_mean"][:, :, None, :]).astype(np.float32)
+    for h in range(2):
+        for blk in range(3):
+            sl = slice(64 * blk, min(64 * blk + 64, 150))
+            _check_int8_pow2_block(ks[0, h, sl], r["k8_codes"][0, h, sl], r["k8_scale"][0, h, blk])
+    assert r["k8_scale"][0, 0, 2] >= r["k8_scale"][0, 0, 1] + 3   # the scaled tail block has its own exponent
