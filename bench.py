@@ -43,8 +43,9 @@ MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 = dense FP8 = 5.0 P op/s
 FP4_PEAK_TOPS = 10100.0          # MI355X dense FP4 (MXFP4) 10.1 P op/s
 # 4-bit QK^T: half the counted ops on FP4, half (P~V) on FP8 -> 1 / (0.5/10.1 + 0.5/5.0) P op/s
 QK4_PEAK_TOPS = 1.0 / (0.5 / FP4_PEAK_TOPS + 0.5 / MFMA_PEAK_TOPS)
-# with Q smoothing the block mean against the FP8 K adds 2d FP8 ops per (query, key) pair beyond
-# the 4d counted: 4d counted ops need 2d FP4 + 4d FP8 matrix work -> 4 / (2/10.1 + 4/5.0) P op/s
+# with Q smoothing the block mean against the INT8 K adds 2d INT8 ops (INT8 rate = FP8 rate) per
+# (query, key) pair beyond the 4d counted: 4d counted ops need 2d FP4 + 4d INT8/FP8 matrix work
+# -> 4 / (2/10.1 + 4/5.0) P op/s
 QK4S_PEAK_TOPS = 4.0 / (2.0 / FP4_PEAK_TOPS + 4.0 / MFMA_PEAK_TOPS)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "video-dit-32k"
@@ -447,13 +448,13 @@ def main():
     q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
     if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below
         quant_alg = (q_el + kv_el) * (2 + 0.5 + 1 / 32) + 3 * kv_el
-        if w.smooth_q:   # K also as FP8 blocks (a byte per value and per 32)
-            quant_alg += kv_el * (1 + 1 / 32)
+        if w.smooth_q:   # K also in INT8 (a byte per value; one exponent byte per 64 keys)
+            quant_alg += kv_el * (1 + 1 / (64 * d))
     else:
         quant_alg = 3 * (q_el + 2 * kv_el)  # Q, K, V: read 2-byte inputs, write 1-byte codes
     quant_act = quant_alg + 2 * 2 * kv_el   # the K-sum and V-max passes read K and V once more
     if w.smooth_q:
-        quant_act += 2 * q_el               # the block-mean pass reads Q once more
+        quant_act += 2 * q_el + 2 * kv_el   # the block-mean pass reads Q, the INT8 K pass K once more
     quant_avg = float(np.mean(quant_ms))
     quant_gbs = quant_alg / (quant_avg * 1e-3) / 1e9
     log(f"[bench] quantize passes avg {quant_avg:.3f} ms: {quant_gbs:.0f} GB/s algorithmic "

@@ -388,43 +388,47 @@ int sage_attn_fwd_qk4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, con
  *   q_mean[c] = fp32( (fp64 sum over the block's rows, ascending) / rows )
  * is subtracted in fp32 before the E2M1 blocks are formed, and returns in
  * the scores (sage_attn_fwd_qk4_smooth_q) as the mean against K, both in
- * FP8 (e4m3) with one power-of-two scale per 32 channels:
- *   E = floor(log2(max|x|)) - 7 clamped to [-127, 127] (the block max lands
- *   in [128, 256)), scale byte E + 127, codes = e4m3(x / 2^E) round to
- *   nearest even; an all-zero block gets scale byte 0.
+ * INT8 with one power-of-two scale 2^E per block: the mean per block of 32
+ * queries over all d channels, the smoothed K (the values of k4_codes) per
+ * block of 64 keys (one KV tile) over all d channels;
+ *   E = the smallest exponent in [-63, 52] with max|x| * 2^-E <= 127 (an
+ *   all-zero block: -63), exponent byte E + 127, codes = RN(x * 2^-E) ties
+ *   to even, saturated at +-127 (reached only at the upper clamp).
  * Out, besides those of sage_quantize_qk4:
  *   q_mean [B,Hq,Nqp/32,d] fp32 (Nqp = Nq rounded up to 128; padding blocks 0),
- *   qm_codes [B,Hq,Nqp/32,d] e4m3, qm_scale [B,Hq,Nqp/32,d/32] bytes,
- *   k8_codes [B,Hkv,Nkt,d] e4m3 (the smoothed K of k4_codes), k8_scale
- *   [B,Hkv,Nkt,d/32] bytes.
+ *   qm_codes [B,Hq,Nqp/32,d] int8, qm_scale [B,Hq,Nqp/32] exponent bytes,
+ *   k8_codes [B,Hkv,Nkt,d] int8 (padding keys 0), k8_scale [B,Hkv,Nkt/64]
+ *   exponent bytes.
  * The five smoothing pointers are all null (plain sage_quantize_qk4) or all
  * valid (SAGE_ERR_INVALID_ARG otherwise).
  */
 int sage_quantize_qk4_smooth_q(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv,
                                int Nq, int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes,
-                               uint8_t* k4_scale, float* k_mean, float* q_mean, uint8_t* qm_codes,
-                               uint8_t* qm_scale, uint8_t* k8_codes, uint8_t* k8_scale, void* workspace,
+                               uint8_t* k4_scale, float* k_mean, float* q_mean, int8_t* qm_codes,
+                               uint8_t* qm_scale, int8_t* k8_codes, uint8_t* k8_scale, void* workspace,
                                size_t workspace_bytes, void* stream);
 
 /*
  * sage_attn_fwd_qk4_smooth_q -- sage_attn_fwd_qk4 on smoothed codes: the
- * score of query row i (block m = i / 32) and key j is
+ * score of query row i (block m = i / 32) and key j (block t = j / 64) is
  *   S_ij = sum_b 2^(Eq_b + Ek_b) q4_i . k4_j over block b
- *        + sum_b 2^(Em_b + Ek8_b) qm_m . k8_j over block b
- * on the matrix cores (FP4 and FP8, fp32 accumulation); the rest as
- * sage_attn_fwd_qk4.  Null smoothing pointers: SAGE_ERR_INVALID_ARG.
+ *        + 2^(Em + Ek8_t) qm_m . k8_j
+ * where the second dot product is the exact int32 sum of the INT8 codes
+ * (INT8 matrix core), made fp32 exactly, and the first is added to it on the
+ * FP4 matrix core (fp32 accumulation); the rest as sage_attn_fwd_qk4.  Null
+ * smoothing pointers: SAGE_ERR_INVALID_ARG.
  */
 int sage_attn_fwd_qk4_smooth_q(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                               const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                               const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                               const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                               const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
                                const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
                                int Nq, int Nkv, int d, int causal, float sm_scale, void* stream);
 
 /* sage_attn_fwd_qk4_smooth_q_dump -- sage_attn_fwd_qk4_smooth_q with the
  * dumps of sage_attn_fwd_qk4_dump. */
 int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                                    const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                                    const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                                    const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                                    const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
                                     const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
                                     int Nq, int Nkv, int d, int causal, float sm_scale, const int32_t* sel, int n_sel,
                                     int32_t* s_dump, uint8_t* p_dump, void* stream);

@@ -67,9 +67,9 @@ struct Q4Ptrs {
   const uint8_t* k4_codes;
   const uint8_t* k4_scale;
   // Q smoothing (all four or none)
-  const uint8_t* qm_codes = nullptr;
+  const int8_t* qm_codes = nullptr;
   const uint8_t* qm_scale = nullptr;
-  const uint8_t* k8_codes = nullptr;
+  const int8_t* k8_codes = nullptr;
   const uint8_t* k8_scale = nullptr;
 };
 
@@ -231,8 +231,8 @@ int sage_quantize_qk4(const void* Q, const void* K, int in_dtype, int layout, in
 
 int sage_quantize_qk4_smooth_q(const void* Q, const void* K, int in_dtype, int layout, int B, int Hq, int Hkv,
                                int Nq, int Nkv, int d, uint8_t* q4_codes, uint8_t* q4_scale, uint8_t* k4_codes,
-                               uint8_t* k4_scale, float* k_mean, float* q_mean, uint8_t* qm_codes,
-                               uint8_t* qm_scale, uint8_t* k8_codes, uint8_t* k8_scale, void* workspace,
+                               uint8_t* k4_scale, float* k_mean, float* q_mean, int8_t* qm_codes,
+                               uint8_t* qm_scale, int8_t* k8_codes, uint8_t* k8_scale, void* workspace,
                                size_t workspace_bytes, void* stream) {
   SAGE_TRY(check_shapes(layout, B, Hq, Hkv, Nq, Nkv, d));
   SAGE_TRY(check_in_dtype(in_dtype));
@@ -272,8 +272,8 @@ int sage_attn_fwd_qk4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, con
 }
 
 int sage_attn_fwd_qk4_smooth_q(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                               const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                               const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                               const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                               const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
                                const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
                                int Nq, int Nkv, int d, int causal, float sm_scale, void* stream) {
   if (!qm_codes || !qm_scale || !k8_codes || !k8_scale) return SAGE_ERR_INVALID_ARG;
@@ -283,8 +283,8 @@ int sage_attn_fwd_qk4_smooth_q(const uint8_t* q4_codes, const uint8_t* q4_scale,
 }
 
 int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                                    const uint8_t* k4_scale, const uint8_t* qm_codes, const uint8_t* qm_scale,
-                                    const uint8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                                    const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                                    const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
                                     const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
                                     int Nq, int Nkv, int d, int causal, float sm_scale, const int32_t* sel, int n_sel,
                                     int32_t* s_dump, uint8_t* p_dump, void* stream) {

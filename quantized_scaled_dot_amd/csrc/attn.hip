@@ -11,7 +11,7 @@
 // LDS: two K tile slots (MFMA order, rows padded to d+16 bytes) and three V
 // tile slots (channel-major, rows padded to 80 bytes), filled by direct
 // global -> LDS copies: K two tiles ahead of use, V one (with Q smoothing also
-// two slots of the FP8 K tile).  Step t computes the scores of tile t+1, the
+// two slots of the INT8 K tile).  Step t computes the scores of tile t+1, the
 // softmax of tile t and the P~V of tile t-1, one barrier per step.
 //
 // Per wave and KV tile:
@@ -63,9 +63,9 @@ struct AttnK {
   // Q smoothing of the 4-bit scores: FP8 block means of 32 queries (nqp/32
   // blocks per head, rows of d codes) with E8M0 scales per 32 channels, and
   // the smoothed K in FP8 blocks (rows of d codes, scales per 32 channels)
-  const uint8_t* qm_codes;
+  const int8_t* qm_codes;
   const uint8_t* qm_scale;
-  const uint8_t* k8_codes;
+  const int8_t* k8_codes;
   const uint8_t* k8_scale;
   float s2;
   const int32_t* sel;
@@ -89,9 +89,11 @@ struct AttnK {
 // sm_scale * log2(e) alone and the row max runs on fp32.  K tiles are d/2
 // bytes per key; each lane loads the scale bytes of its two MFMA rows' keys
 // one step ahead.  QK4 = 2 adds Q smoothing: the scores also take the mean
-// of the wave's 32 queries (one block) against the FP8 K, on the FP8 matrix
-// instruction into the same fp32 accumulators (the FP8 K tile is staged next
-// to the 4-bit one, rows of d + 16 bytes in the same MFMA order).
+// of the wave's 32 queries (one block) against the smoothed K, both INT8
+// with power-of-two block scales: the INT8 matrix instruction sums the
+// integer products exactly, one fma per score turns that sum into the exact
+// fp32 term, and the FP4 products are added on top (the INT8 K tile is
+// staged next to the 4-bit one, rows of d + 16 bytes in the same MFMA order).
 // NW: waves per workgroup (query rows 32 NW).  4 everywhere; 8 for the
 // non-causal INT8 d = 128 kernel on whole 256-row query tiles, where one
 // workgroup then fills a CU and each K/V tile copy serves twice the rows.
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   constexpr int KTILE = kKTile * KB;           // bytes of one K tile in HBM
   constexpr int RK = QK4 ? KB + 16 : kRowK<D>;
   using SV = typename std::conditional<(QK4 != 0), v16f, v16i>::type;   // score registers
-  constexpr int RK8 = kRowK<D>;                 // FP8 K rows (Q smoothing), padded like INT8 K
+  constexpr int RK8 = kRowK<D>;                 // INT8 K rows of the mean term (Q smoothing), padded like INT8 K
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
   __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
   __shared__ __attribute__((aligned(16))) uint8_t sK8[2][QSM ? kKTile * RK8 : 16];
@@ -169,22 +171,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
     }
   }
   const float dq = QK4 ? 0.0f : p.q_scale[(size_t)bh * p.nbq + qrow0 / p.blk_q];
-  // Q smoothing: the FP8 mean of this wave's 32 queries as the B operand of
-  // every column, and its scales.  An FP8 operand of the scaled 64-deep
-  // instruction holds, in lane group g, elements 16g .. 16g+15 of the first
-  // 32-element scale block in bytes 0-15 and the same of the second block in
-  // bytes 16-31; the scale given by lane group g covers block g.
-  v8i qm8[QSM ? KS : 1];
-  int qmsc[QSM ? KS : 1];
+  // Q smoothing: the INT8 mean of this wave's 32 queries as the B operand of
+  // every column (lane group g holds channels 32s + 16g .. +15 of k-step s,
+  // as the INT8 Q codes), and its scale exponent
+  v4i qm8[QSM ? CT : 1];
+  int qme = 0;
   if (QSM) {
     const size_t r = (size_t)bh * (p.nqp / 32) + qrow0 / 32;
 #pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const uint8_t* mp = p.qm_codes + r * D + 64 * s + 16 * lg;
-      const v4i m0 = *(const v4i*)mp, m1 = *(const v4i*)(mp + 32);
-      qm8[s] = v8i{m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-      qmsc[s] = p.qm_scale[r * (D / 32) + 2 * s + lg];
-    }
+    for (int s = 0; s < CT; s++) qm8[s] = *(const v4i*)(p.qm_codes + r * D + 32 * s + 16 * lg);
+    qme = (int)p.qm_scale[r] - 127;
   }
 
   // ---- staging: direct global -> LDS copies (buffer loads with the LDS
@@ -201,12 +197,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   // ahead of V (see the loop).  The K and V tiles are contiguous blocks in
   // HBM (K: 64 rows of KB code bytes; V: d rows of 64 codes).
   constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
-  constexpr int N8I = QSM ? kKTile * RK8 / 1024 : 0;                 // FP8 K tile (Q smoothing)
-  constexpr int KTILE8 = kKTile * D;                                 // bytes of one FP8 K tile in HBM
+  constexpr int N8I = QSM ? kKTile * RK8 / 1024 : 0;                 // INT8 K tile (Q smoothing)
+  constexpr int KTILE8 = kKTile * D;                                 // bytes of one INT8 K tile in HBM
   static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0 && kKTile * RK8 % 1024 == 0,
                 "whole DMA instructions per tile");
   constexpr int FK = NKI / NW, F8 = N8I / NW, FV = NVI / NW;         // whole rounds
-  constexpr int XK = NKI % NW, X8 = N8I % NW, XR = NKI % NW + N8I % NW + NVI % NW;   // leftovers: K, FP8 K, all
+  constexpr int XK = NKI % NW, X8 = N8I % NW, XR = NKI % NW + N8I % NW + NVI % NW;   // leftovers: K, INT8 K, all
   constexpr int NXR = (XR + NW - 1) / NW;                             // leftover rounds
   static_assert(NXR <= 2, "at most two leftover rounds");
   __builtin_assume(wave >= 0 && wave < NW);
@@ -233,7 +229,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
 #pragma unroll
   for (int j = 0; j < FV; j++) voff[j] = v_src(wave + NW * j);
   // this wave's leftover of round r: entry e = 4 r + wave of the list (K ones,
-  // then FP8 K, then V); xt = 0 K, 1 FP8 K, 2 V, -1 none
+  // then INT8 K, then V); xt = 0 K, 1 INT8 K, 2 V, -1 none
   int xt[NXR > 0 ? NXR : 1], xi[NXR > 0 ? NXR : 1];
   uint32_t xoff[NXR > 0 ? NXR : 1];
 #pragma unroll
@@ -293,30 +289,47 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   };
   unsigned ksw_next[2] = {QK4 ? kscale4(0, 0) : 0u, QK4 ? kscale4(0, 1) : 0u};
   unsigned ksw[2] = {0u, 0u};
-  // the same for the FP8 K blocks (Q smoothing)
-  auto kscale8 = [&](int t, int h) -> unsigned {
-    const uint8_t* ksp =
-        p.k8_scale + ((size_t)bhkv * p.nkt * kKTile + (size_t)t * kKTile + k_lds_key(32 * h + li)) * (D / 32);
-    return D == 128 ? *(const unsigned*)ksp : (unsigned)*(const uint16_t*)ksp;
-  };
-  unsigned ksw8_next[2] = {QSM ? kscale8(0, 0) : 0u, QSM ? kscale8(0, 1) : 0u};
-  unsigned ksw8[2] = {0u, 0u};
+  // the scale exponent byte of the INT8 K tile (Q smoothing)
+  auto kscale8 = [&](int t) -> int { return (int)p.k8_scale[(size_t)bhkv * p.nkt + t]; };
+  int ke8_next = QSM ? kscale8(0) : 0, ke8 = 0;
   // the scale words of tile t+1 become current; those of tile t+2 are loaded
   auto next_kscales = [&](int tn) {
     ksw[0] = ksw_next[0]; ksw[1] = ksw_next[1];
     ksw_next[0] = kscale4(tn, 0);
     ksw_next[1] = kscale4(tn, 1);
     if (QSM) {
-      ksw8[0] = ksw8_next[0]; ksw8[1] = ksw8_next[1];
-      ksw8_next[0] = kscale8(tn, 0);
-      ksw8_next[1] = kscale8(tn, 1);
+      ke8 = ke8_next;
+      ke8_next = kscale8(tn);
     }
   };
   // S^T = K_t . Q^T for KV tile t, into (a0: keys 32*lg + v, a1: keys 32*lg + 16 + v):
   // int32 (INT8 codes) or fp32 (QK4, scales applied in the instruction)
   auto qk = [&](int t, SV& a0, SV& a1) {
     const int8_t* kb0 = sK[t & 1] + li * RK + 16 * lg;   // MFMA rows li and 32 + li
-    if constexpr (QK4) {
+    if constexpr (QSM) {
+      // the block mean of Q against the INT8 K: n = exact int32 sum, in the
+      // accumulator biased by B (its bits read as fp32 are B + n exactly,
+      // |n| <= d 127^2 < 2^21); then fma((B + n), 2^e, -B 2^e) = n 2^e exactly,
+      // e = Em + Ek8 in [-126, 104]
+      v16i i0 = kScoreBias16, i1 = kScoreBias16;
+      const int8_t* k8b = (const int8_t*)sK8[t & 1] + li * RK8 + 16 * lg;
+#pragma unroll
+      for (int s = 0; s < CT; s++) {
+        const v4i x0 = *(const v4i*)(k8b + 32 * s), x1 = *(const v4i*)(k8b + 32 * RK8 + 32 * s);
+        i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x0, qm8[s], i0, 0, 0, 0);
+        i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x1, qm8[s], i1, 0, 0, 0);
+      }
+      const int e = qme + ke8 - 127;
+      const float sc = __builtin_amdgcn_ldexpf(1.0f, e), bs = __builtin_amdgcn_ldexpf(kScoreBiasF, e);
+      // (each element is copied out before the bit cast: this compiler's
+      // __builtin_bit_cast of a vector element expression reads element 0)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int n0 = i0[v], n1 = i1[v];
+        a0[v] = __builtin_fmaf(__builtin_bit_cast(float, n0), sc, -bs);
+        a1[v] = __builtin_fmaf(__builtin_bit_cast(float, n1), sc, -bs);
+      }
+    } else if constexpr (QK4) {
       a0 = SV{}; a1 = SV{};
     } else {
       a0 = kScoreBias16; a1 = kScoreBias16;   // int32 results read as fp32 give B + S exactly
@@ -333,18 +346,6 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
         const v8i b8 = {k1[0], k1[1], k1[2], k1[3], 0, 0, 0, 0};
         a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8, a0, 4, 4, 0, s0, 0, qsc[s]);
         a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, q8, a1, 4, 4, 0, s1, 0, qsc[s]);
-        if constexpr (QSM) {
-          // + the block mean of Q against the FP8 K: same rows, channels 64s + 16lg .. + 16
-          // and 64s + 32 + 16lg .. + 16 (the FP8 operand layout above)
-          const uint8_t* k8b = sK8[t & 1] + li * RK8 + 64 * s + 16 * lg;
-          const v4i x0 = *(const v4i*)k8b, x1 = *(const v4i*)(k8b + 32);
-          const v4i y0 = *(const v4i*)(k8b + 32 * RK8), y1 = *(const v4i*)(k8b + 32 * RK8 + 32);
-          const int e0 = (int)((ksw8[0] >> (8 * (2 * s + lg))) & 0xFFu), e1 = (int)((ksw8[1] >> (8 * (2 * s + lg))) & 0xFFu);
-          const v8i ka = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          const v8i kb = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-          a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qm8[s], a0, 0, 0, 0, e0, 0, qmsc[s]);
-          a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb, qm8[s], a1, 0, 0, 0, e1, 0, qmsc[s]);
-        }
       } else {
         a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);

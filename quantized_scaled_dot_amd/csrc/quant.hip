@@ -59,10 +59,21 @@ struct InRows {
   __device__ __forceinline__ size_t stride(int D) const { return nhd ? (size_t)H * D : (size_t)D; }
 };
 
+// Exponent of the power-of-two scale of INT8 codes for a block with
+// max |x| = a: the smallest e in [-63, 52] with a * 2^-e <= 127 (a = 0: -63).
+__device__ __forceinline__ int int8_pow2_exponent(float a) {
+  if (a == 0.0f) return -63;
+  int e = ilogbf(a) - 6;                 // a * 2^-e in [64, 128)
+  if (ldexpf(a, -e) > 127.0f) e += 1;    // then in [32, 64)
+  return min(max(e, -63), 52);
+}
+
 // ---------------------------------------------------------------------------
 // Symmetric INT8 quantization of one block of BLK tokens x D channels:
 // a = max|x| (x = K - mean when SMOOTH), scale = a/127, r = 127/a,
 // code = rint(x * r) in [-127, 127]; a < 2^-120 gives scale 0 and zero codes.
+// POW2: the scale is 2^e instead (int8_pow2_exponent), r = 2^-e exactly, and
+// the byte e + 127 is written as the scale.
 // Tokens at or past N (the shorter last block) are not read and count as 0.
 // A block is held by TPB = min(256, BLK*D/8) threads, 8 values per 16-byte
 // load; a 256-thread workgroup quantizes 256/TPB consecutive blocks.
@@ -70,10 +81,10 @@ struct InRows {
 template <int D, int BLK>
 constexpr int blocks_per_wg() { return BLK * D / 8 >= 256 ? 1 : 256 / (BLK * D / 8); }
 
-template <int D, int BLK, bool SMOOTH>
+template <int D, int BLK, bool SMOOTH, bool POW2 = false, typename ST = float>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int is_bf16, InRows in,
                                             const float* __restrict__ mean, int8_t* __restrict__ codes,
-                                            float* __restrict__ scale, int lin, float* red4) {
+                                            ST* __restrict__ scale, int lin, float* red4) {
   constexpr int NB = blocks_per_wg<D, BLK>();
   constexpr int TPB = 256 / NB;                // threads per block
   constexpr int LPT = BLK * D / 8 / TPB;       // 16-byte loads per thread
@@ -115,7 +126,8 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
   a = group_max<TPB>(a, red4);
   const bool zero = !(a >= 0x1p-120f);
   const float dl = zero ? 0.0f : a / 127.0f;
-  const float r = zero ? 0.0f : 127.0f / a;
+  const int e2 = POW2 ? int8_pow2_exponent(a) : 0;
+  const float r = POW2 ? ldexpf(1.0f, -e2) : zero ? 0.0f : 127.0f / a;
   int8_t* dst = codes + off;
 #pragma unroll
   for (int l = 0; l < LPT; l++) {
@@ -130,7 +142,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, int 
     v2i pk = {(int)w[0], (int)w[1]};
     __builtin_nontemporal_store(pk, (v2i*)(dst + (size_t)ch * 8));
   }
-  if (t == 0) scale[(size_t)bh * nblk + blk] = dl;
+  if (t == 0) scale[(size_t)bh * nblk + blk] = POW2 ? (ST)(e2 + 127) : (ST)dl;
 }
 
 // ---------------------------------------------------------------------------
@@ -434,22 +446,13 @@ __device__ __forceinline__ unsigned e2m1_code(float x) {
   return m | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// FP8 (e4m3) code of x, x already scaled into the format's range (|x| < 256):
-// the hardware conversion rounds to nearest even.
-__device__ __forceinline__ unsigned e4m3_code(float x) {
-  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
-}
-
 // One token row of d channels in blocks of 32, each with one power-of-two
-// scale: E2M1 codes (E = ilogb(max) - 2) and, with FP8OUT, also e4m3 codes
-// (E = ilogb(max) - 7, the block max in [128, 256)).  MEAN: 0 none, 1 one
-// mean per head (K), 2 one per block of 32 rows (Q smoothing; mean
-// [BH, P/32, d]).
-template <int D, int MEAN, bool FP8OUT>
+// scale: E2M1 codes (E = ilogb(max) - 2).  MEAN: 0 none, 1 one mean per
+// head (K), 2 one per block of 32 rows (Q smoothing; mean [BH, P/32, d]).
+template <int D, int MEAN>
 __global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict__ X, int is_bf16, InRows in, int BH,
                                                      const float* __restrict__ mean, uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ codes8,
-                                                     uint8_t* __restrict__ scale8) {
+                                                     uint8_t* __restrict__ scale) {
   constexpr int NB = D / 32;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (long long)BH * in.P * NB) return;
@@ -492,35 +495,28 @@ __global__ __launch_bounds__(256) void quant4_kernel(const uint16_t* __restrict_
   }
   *(v4i*)(codes + (size_t)rowid * (D / 2) + 16 * b) = packed;
   scale[(size_t)rowid * NB + b] = (uint8_t)sbyte;
-  if (FP8OUT) {
-    unsigned s8 = 0;
-    v4i c8[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (a != 0.0f) {
-      const int e = min(max(ilogbf(a) - 7, -127), 127);
-      s8 = (unsigned)(e + 127);
-#pragma unroll
-      for (int w = 0; w < 8; w++) {
-        unsigned word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) word |= e4m3_code(ldexpf(x[4 * w + k], -e)) << (8 * k);
-        c8[w / 4][w % 4] = (int)word;
-      }
-    }
-    *(v4i*)(codes8 + (size_t)rowid * D + 32 * b) = c8[0];
-    *(v4i*)(codes8 + (size_t)rowid * D + 32 * b + 16) = c8[1];
-    scale8[(size_t)rowid * NB + b] = (uint8_t)s8;
-  }
+}
+
+// Q smoothing, the K of the mean's term: the smoothed K in INT8 blocks of
+// one KV tile (64 keys) x d channels, one power-of-two scale each (exponent
+// bytes [BH, P/64]).
+template <int D>
+__global__ __launch_bounds__(256) void k8_quant_kernel(const uint16_t* __restrict__ K, int is_bf16, InRows kin,
+                                                       const float* __restrict__ k_mean, int8_t* __restrict__ k8_codes,
+                                                       uint8_t* __restrict__ k8_scale) {
+  __shared__ float red4[4];
+  quant_block<D, kKTile, true, true>(K, is_bf16, kin, k_mean, k8_codes, k8_scale, blockIdx.x, red4);
 }
 
 // Block means of Q for smoothing: one workgroup per (head, block of 32 query
 // rows), one thread per channel.  The mean is the fp64 sum of the block's
 // rows in ascending order over the number of rows (the last block may be
 // short), rounded to fp32; padding blocks (past Nq) get 0.  It is written as
-// fp32 and as e4m3 codes with one power-of-two scale per 32 channels (the
-// block max in [128, 256)); an all-zero group gets scale byte 0.
+// fp32 and as INT8 codes with one power-of-two scale over the d channels
+// (int8_pow2_exponent; exponent byte e + 127).
 template <int D>
 __global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ X, int is_bf16, InRows in,
-                                                   float* __restrict__ q_mean, uint8_t* __restrict__ qm_codes,
+                                                   float* __restrict__ q_mean, int8_t* __restrict__ qm_codes,
                                                    uint8_t* __restrict__ qm_scale) {
   const int nb = in.P / 32;
   const int blk = blockIdx.x % nb, bh = blockIdx.x / nb, c = threadIdx.x;
@@ -537,17 +533,20 @@ __global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ 
   }
   float a = fabsf(qm);
 #pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));   // max over the 32-channel group
-  unsigned code = 0, sbyte = 0;
-  if (a != 0.0f) {
-    const int e = min(max(ilogbf(a) - 7, -127), 127);
-    sbyte = (unsigned)(e + 127);
-    code = e4m3_code(ldexpf(qm, -e));
+  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));   // max over the wave's 64 channels
+  if constexpr (D > 64) {
+    __shared__ float red[D / 64];
+    if ((c & 63) == 0) red[c >> 6] = a;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < D / 64; w++) a = fmaxf(a, red[w]);
   }
+  const int e = int8_pow2_exponent(a);
+  const float y = fminf(fmaxf(__builtin_rintf(ldexpf(qm, -e)), -127.0f), 127.0f);
   const size_t r = (size_t)bh * nb + blk;
   q_mean[r * D + c] = qm;
-  qm_codes[r * D + c] = (uint8_t)code;
-  if ((c & 31) == 0) qm_scale[r * (D / 32) + c / 32] = (uint8_t)sbyte;
+  qm_codes[r * D + c] = (int8_t)(int)y;
+  if (c == 0) qm_scale[r] = (uint8_t)(e + 127);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,19 +677,19 @@ static void launch_qk4_d(const Quant4Args& a, hipStream_t st) {
                      D, a.k_mean);
   const long long tq = (long long)BHq * qin.P * (D / 32), tk = (long long)BHkv * kin.P * (D / 32);
   const dim3 gq((unsigned)((tq + 255) / 256)), gk((unsigned)((tk + 255) / 256));
-  if (a.q_mean) {   // Q smoothing: block means, smoothed Q, and K also in FP8 blocks
+  if (a.q_mean) {   // Q smoothing: block means, smoothed Q, and K also in INT8 blocks for the mean's term
     hipLaunchKernelGGL(q_mean_kernel<D>, dim3(BHq * (qin.P / 32)), dim3(D), 0, st, (const uint16_t*)a.Q, a.is_bf16,
                        qin, a.q_mean, a.qm_codes, a.qm_scale);
-    hipLaunchKernelGGL((quant4_kernel<D, 2, false>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
-                       (const float*)a.q_mean, a.q4_codes, a.q4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
-    hipLaunchKernelGGL((quant4_kernel<D, 1, true>), gk, dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin, BHkv,
-                       (const float*)a.k_mean, a.k4_codes, a.k4_scale, a.k8_codes, a.k8_scale);
-    return;
+    hipLaunchKernelGGL((quant4_kernel<D, 2>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
+                       (const float*)a.q_mean, a.q4_codes, a.q4_scale);
+    hipLaunchKernelGGL(k8_quant_kernel<D>, dim3(BHkv * (kin.P / kKTile)), dim3(256), 0, st, (const uint16_t*)a.K,
+                       a.is_bf16, kin, (const float*)a.k_mean, a.k8_codes, a.k8_scale);
+  } else {
+    hipLaunchKernelGGL((quant4_kernel<D, 0>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
+                       (const float*)nullptr, a.q4_codes, a.q4_scale);
   }
-  hipLaunchKernelGGL((quant4_kernel<D, 0, false>), gq, dim3(256), 0, st, (const uint16_t*)a.Q, a.is_bf16, qin, BHq,
-                     (const float*)nullptr, a.q4_codes, a.q4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
-  hipLaunchKernelGGL((quant4_kernel<D, 1, false>), gk, dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin, BHkv,
-                     (const float*)a.k_mean, a.k4_codes, a.k4_scale, (uint8_t*)nullptr, (uint8_t*)nullptr);
+  hipLaunchKernelGGL((quant4_kernel<D, 1>), gk, dim3(256), 0, st, (const uint16_t*)a.K, a.is_bf16, kin, BHkv,
+                     (const float*)a.k_mean, a.k4_codes, a.k4_scale);
 }
 
 void launch_quantize_qk4(const Quant4Args& a, hipStream_t st) {

@@ -525,7 +525,9 @@ def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None, smooth_q=Fals
     """4-bit Q and smoothed K (E2M1, a power-of-two scale per 32 channels).
     Returns a dict with q4_codes [B,Hq,Nqp,d/2], q4_scale [B,Hq,Nqp,d/32],
     k4_codes, k4_scale, k_mean, Nq and Nkv; with ``smooth_q`` also q_mean
-    [B,Hq,Nqp/32,d], qm_codes, qm_scale, k8_codes [B,Hkv,Nkt,d] and k8_scale."""
+    [B,Hq,Nqp/32,d] with its INT8 codes qm_codes and exponent bytes qm_scale
+    [B,Hq,Nqp/32], and the smoothed K in INT8, k8_codes [B,Hkv,Nkt,d] with
+    one exponent byte per 64-key tile, k8_scale [B,Hkv,Nkt/64]."""
     B, Hq, Nq, d = _bhnd(Q, layout)
     Bk, Hkv, Nkv, dk = _bhnd(K, layout)
     if (Bk, dk) != (B, d) or K.dtype != Q.dtype or K.device != Q.device:
@@ -544,10 +546,10 @@ def quantize_qk4(Q, K, layout="bhnd", workspace=None, stream=None, smooth_q=Fals
     if smooth_q:
         nb = Nqp // 32
         out.update(q_mean=torch.empty((B, Hq, nb, d), dtype=torch.float32, device=dev),
-                   qm_codes=torch.empty((B, Hq, nb, d), dtype=torch.uint8, device=dev),
-                   qm_scale=torch.empty((B, Hq, nb, d // 32), dtype=torch.uint8, device=dev),
-                   k8_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.uint8, device=dev),
-                   k8_scale=torch.empty((B, Hkv, Nkt, d // 32), dtype=torch.uint8, device=dev))
+                   qm_codes=torch.empty((B, Hq, nb, d), dtype=torch.int8, device=dev),
+                   qm_scale=torch.empty((B, Hq, nb), dtype=torch.uint8, device=dev),
+                   k8_codes=torch.empty((B, Hkv, Nkt, d), dtype=torch.int8, device=dev),
+                   k8_scale=torch.empty((B, Hkv, Nkt // sage_kv_tile()), dtype=torch.uint8, device=dev))
         _check(sage_quantize_qk4_smooth_q(*head, _ptr(out["q_mean"]), _ptr(out["qm_codes"]), _ptr(out["qm_scale"]),
                                           _ptr(out["k8_codes"]), _ptr(out["k8_scale"]), *tail))
     else:
