@@ -70,6 +70,10 @@ def lib():
         L.oracle_quantize_k4.argtypes = [P, i32, i32, i32, i32, P, P, P]
         L.oracle_attn_rows_qk4.restype = i32
         L.oracle_attn_rows_qk4.argtypes = [P] * 10 + [i32] * 8 + [f32, P, i32, P, P]
+        L.oracle_quantize_v4.restype = i32
+        L.oracle_quantize_v4.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.oracle_attn_rows_fp4.restype = i32
+        L.oracle_attn_rows_fp4.argtypes = [P] * 6 + [i32] * 8 + [f32, P, i32, P, P]
         L.oracle_qk4_scores.restype = i32
         L.oracle_qk4_scores.argtypes = [P] * 8 + [i32] * 6 + [P, i32, P]
         L.oracle_quantize_k8.restype = i32
@@ -332,6 +336,37 @@ def attn_rows_qk4(qk4, v_codes, v_scale, causal, sm_scale, rows=None, kv_tile=KV
                                     int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
     if rc != 0:
         raise ValueError("oracle_attn_rows_qk4: unsupported arguments")
+    return (out, p) if want_p else out
+
+
+def quantize_v4(V_bits, dtype):
+    """V [B,H,N,d] in E2M1 blocks of 32 consecutive tokens per channel (MXFP4):
+    codes [B,H,N,d] (one per value, 0..15) and E8M0 scale bytes [B,H,ceil(N/32),d]."""
+    V_bits = _c(V_bits, np.uint16)
+    B, H, N, d = V_bits.shape
+    vc = np.empty((B, H, N, d), np.uint8)
+    vs = np.empty((B, H, -(-N // 32), d), np.uint8)
+    if lib().oracle_quantize_v4(_p(V_bits), dtype, B * H, N, d, _p(vc), _p(vs)) != 0:
+        raise ValueError("oracle quantize_v4: unsupported shape")
+    return vc, vs
+
+
+def attn_rows_fp4(qk4, v4_codes, v4_scale, causal, sm_scale, rows=None, kv_tile=KV_TILE, want_p=False):
+    """Oracle FP4 attention (4-bit QK^T, FP4 P~V) for flat query rows bh*Nq + i;
+    with want_p also the E2M1 code of P~ of every visited key."""
+    qc, qs, kc, ks = (_c(qk4[k], np.uint8) for k in ("q4_codes", "q4_scale", "k4_codes", "k4_scale"))
+    vc, vs = _c(v4_codes, np.uint8), _c(v4_scale, np.uint8)
+    B, Hq, Nq, d = qc.shape
+    _, Hkv, Nkv, _ = kc.shape
+    if rows is None:
+        rows = np.arange(B * Hq * Nq, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, d), np.float32)
+    p = np.empty((rows.size, Nkv), np.uint8) if want_p else None
+    rc = lib().oracle_attn_rows_fp4(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vs), B, Hq, Hkv, Nq, Nkv, d, kv_tile,
+                                    int(bool(causal)), float(sm_scale), _p(rows), rows.size, _p(out), _p(p))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows_fp4: unsupported arguments")
     return (out, p) if want_p else out
 
 

@@ -423,6 +423,31 @@ int oracle_quantize_k4(const uint16_t* K, int dtype, int BH, int N, int d, uint8
   return 0;
 }
 
+/* 4-bit V for the FP4 P~V variant (R23), following the OCP Microscaling     */
+/* (MX) formats' MXFP4 (E2M1 elements, one E8M0 scale per block of 32): each */
+/* channel of a head in blocks of 32 consecutive tokens (the last block holds */
+/* the N mod 32 remaining tokens), each block its own shared exponent        */
+/* (quant_block_mx4, the rule of the 4-bit Q and K).                          */
+/* Codes one per value [BH, N, d] (0..15); scales [BH, ceil(N/32), d].       */
+int oracle_quantize_v4(const uint16_t* V, int dtype, int BH, int N, int d, uint8_t* v4_codes, uint8_t* v4_scale) {
+  if (BH < 1 || N < 1 || d < 1) return -1;
+  const int nb = (N + 31) / 32;
+#pragma omp parallel for schedule(dynamic)
+  for (int bh = 0; bh < BH; bh++) {
+    float buf[32];
+    uint8_t cod[32];
+    for (int blk = 0; blk < nb; blk++) {
+      const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;
+      for (int c = 0; c < d; c++) {
+        for (int i = 0; i < n; i++) buf[i] = load_in(V, ((size_t)bh * N + n0 + i) * d + c, dtype);
+        quant_block_mx4(buf, n, cod, v4_scale + ((size_t)bh * nb + blk) * d + c);
+        for (int i = 0; i < n; i++) v4_codes[((size_t)bh * N + n0 + i) * d + c] = cod[i];
+      }
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 int oracle_quantize_v(const uint16_t* V, int dtype, int BH, int N, int d, uint8_t* v_codes, float* v_scale) {
   if (BH < 1 || N < 1 || d < 1) return -1;
@@ -533,6 +558,10 @@ typedef struct {
   int qms;
   const int8_t* k8;
   const uint8_t* k8s;
+  /* FP4 P~V instead of FP8 (v4 != NULL, R23): the head's V codes [Nkv, d]
+   * (0..15) and block scales [ceil(Nkv/32), d] */
+  const uint8_t* v4;
+  const uint8_t* v4s;
   const int8_t* k;        /* the head's K codes [Nkv, d] */
   const float* ks;        /* the head's K scales [ceil(Nkv/blk_k)] */
   const uint8_t* v;       /* the head's V codes [Nkv, d] */
@@ -578,6 +607,8 @@ static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, 
   float* c2 = (float*)malloc(sizeof(float) * kv_tile);
   float* pt = (float*)malloc(sizeof(float) * kv_tile);
   uint8_t* ph = (uint8_t*)malloc(kv_tile);
+  float* ag = (float*)malloc(sizeof(float) * kv_tile);
+  double* pd = (double*)malloc(sizeof(double) * kv_tile);
   double* oblk = (double*)malloc(sizeof(double) * d);
   for (int c = 0; c < d; c++) oacc[c] = 0.0f;
   float m = 0.0f, l = 0.0f;
@@ -609,30 +640,69 @@ static int attend_range(const row_ctx* x, int j_begin, int j_end, float* m_out, 
     float mm = mnew - 8.0f;
     float rowsum = 0.0f;
     double code_sum = 0.0;
-    for (int jj = 0; jj < nvis; jj++) {
-      if (x->q4) {
-        pt[jj] = oracle_exp2f(fmaf(S[jj], c2[jj], -mm));
-        rowsum += pt[jj];
-      } else {
-        const float K = fmaf(SCORE_BIAS, c2[jj], mm);
-        pt[jj] = oracle_exp2f(fmaf(SCORE_BIAS + S[jj], c2[jj], -K));
+    if (x->v4) {
+      /* FP4 P~ (R23): the tile's keys in blocks of 32 (keys j0 .. j0+31 and  */
+      /* j0+32 .. j0+63, visible ones only), each with the MX shared exponent */
+      /* of its largest value taken on the exponent argument, E = floor(max   */
+      /* arg) - 2 clamped to [-126, 127] (no visible key: -126); P^ = E2M1 of */
+      /* P~ / 2^E, P~ below 2^-126 counted as 0; l_tile = sum of the decoded   */
+      /* values P^ 2^E; the block product uses the same values.              */
+      for (int b0 = 0; b0 < nvis; b0 += 32) {
+        const int b1 = b0 + 32 < nvis ? b0 + 32 : nvis;
+        float amax = -INFINITY;
+        for (int jj = b0; jj < b1; jj++) {
+          ag[jj] = fmaf(S[jj], c2[jj], -mm);
+          if (ag[jj] > amax) amax = ag[jj];
+        }
+        float fe = floorf(amax) - 2.0f;
+        if (!(fe >= -126.0f)) fe = -126.0f;
+        if (fe > 127.0f) fe = 127.0f;
+        const int e = (int)fe;
+        for (int jj = b0; jj < b1; jj++) {
+          float p = oracle_exp2f(ag[jj]);
+          if (p < 0x1p-126f) p = 0.0f;
+          pt[jj] = p;
+          ph[jj] = oracle_e2m1_encode(ldexpf(p, -e));
+          pd[jj] = ldexp(oracle_e2m1_decode(ph[jj]), e);
+          code_sum += pd[jj];
+          if (prow) prow[j0 + jj] = ph[jj];
+        }
       }
-      ph[jj] = oracle_e4m3_encode(pt[jj]);
-      code_sum += x->vdec[ph[jj]];
-      if (prow) prow[j0 + jj] = ph[jj];
-    }
-    if (!x->q4) rowsum = (float)code_sum;   /* exact: at most 2^10 codes per tile */
-    for (int c = 0; c < d; c++) {
-      double acc = 0.0;
-      for (int jj = 0; jj < nvis; jj++) acc += x->vdec[ph[jj]] * x->vdec[x->v[(size_t)(j0 + jj) * d + c]];
-      oblk[c] = acc;
+      rowsum = (float)code_sum;   /* exact: 64 values of at most 4 significant bits */
+      for (int c = 0; c < d; c++) {
+        double acc = 0.0;
+        for (int jj = 0; jj < nvis; jj++) {
+          const int j = j0 + jj;
+          acc += pd[jj] * ldexp(oracle_e2m1_decode(x->v4[(size_t)j * d + c]), (int)x->v4s[(size_t)(j / 32) * d + c] - 127);
+        }
+        oblk[c] = acc;
+      }
+    } else {
+      for (int jj = 0; jj < nvis; jj++) {
+        if (x->q4) {
+          pt[jj] = oracle_exp2f(fmaf(S[jj], c2[jj], -mm));
+          rowsum += pt[jj];
+        } else {
+          const float K = fmaf(SCORE_BIAS, c2[jj], mm);
+          pt[jj] = oracle_exp2f(fmaf(SCORE_BIAS + S[jj], c2[jj], -K));
+        }
+        ph[jj] = oracle_e4m3_encode(pt[jj]);
+        code_sum += x->vdec[ph[jj]];
+        if (prow) prow[j0 + jj] = ph[jj];
+      }
+      if (!x->q4) rowsum = (float)code_sum;   /* exact: at most 2^10 codes per tile */
+      for (int c = 0; c < d; c++) {
+        double acc = 0.0;
+        for (int jj = 0; jj < nvis; jj++) acc += x->vdec[ph[jj]] * x->vdec[x->v[(size_t)(j0 + jj) * d + c]];
+        oblk[c] = acc;
+      }
     }
     for (int c = 0; c < d; c++) oacc[c] = fmaf(alpha, oacc[c], (float)oblk[c]);
     l = fmaf(alpha, l, rowsum);
     m = mnew;
     visited++;
   }
-  free(S); free(c2); free(pt); free(ph); free(oblk);
+  free(S); free(c2); free(pt); free(ph); free(ag); free(pd); free(oblk);
   *m_out = m;
   *l_out = l;
   return visited;
@@ -653,6 +723,7 @@ static void row_setup(row_ctx* x, const int8_t* q_codes, const float* q_scale, c
                       const double* vdec, int64_t* bk_out) {
   const int nbq = nblocks(Nq, blk_q), nbk = nblocks(Nkv, blk_k);
   int64_t bh = row / Nq, i = row % Nq, bk = kv_head(bh, Hq, Hkv);
+  memset(x, 0, sizeof *x);   /* every optional pointer (4-bit, smoothing, FP4 V) NULL */
   x->q = q_codes + ((size_t)bh * Nq + i) * d;
   x->dq = q_scale[(size_t)bh * nbq + i / blk_q];
   x->k = k_codes + (size_t)bk * Nkv * d;
@@ -662,7 +733,6 @@ static void row_setup(row_ctx* x, const int8_t* q_codes, const float* q_scale, c
   x->last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
   x->s2 = sm_scale * LOG2E_F;
   x->vdec = vdec;
-  x->q4 = x->q4s = x->k4 = x->k4s = NULL;
   *bk_out = bk;
 }
 
@@ -700,12 +770,12 @@ int oracle_attn_rows(const int8_t* q_codes, const float* q_scale, const int8_t* 
 /* FP8 P~ and the two-level P~V exactly as above.  Codes [B*H, N, d], scales */
 /* [B*H, N, d/32]; out [nrows, d]; p_codes (optional) as above.              */
 /* ------------------------------------------------------------------------ */
-int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
-                         const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
-                         const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
-                         const float* v_scale, int B, int Hq,
-                         int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
-                         const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+static int attn_rows_4bit(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                          const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                          const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                          const float* v_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, int B, int Hq,
+                          int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
+                          const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
   if (!attn_args_ok(B, Hq, Hkv, Nq, Nkv, d, 1, 1, kv_tile, causal, sm_scale) || d % 32) return -1;
   double vdec[256];
   for (int c = 0; c < 256; c++) vdec[c] = oracle_e4m3_decode((uint8_t)c);
@@ -727,7 +797,12 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
       x.k8 = k8_codes + (size_t)bk * Nkv * d;
       x.k8s = k8_scale + (size_t)bk * ((Nkv + 63) / 64);
     }
-    x.v = v_codes + (size_t)bk * Nkv * d;
+    if (v4_codes) {
+      x.v4 = v4_codes + (size_t)bk * Nkv * d;
+      x.v4s = v4_scale + (size_t)bk * ((Nkv + 31) / 32) * d;
+    } else {
+      x.v = v_codes + (size_t)bk * Nkv * d;
+    }
     x.Nkv = Nkv; x.d = d; x.blk_k = 1; x.kv_tile = kv_tile;
     x.last = causal ? i + ((int64_t)Nkv - Nq) : (int64_t)Nkv - 1;
     x.s2 = sm_scale * LOG2E_F;
@@ -738,10 +813,35 @@ int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const
     if (prow) memset(prow, 0, Nkv);
     attend_range(&x, 0, Nkv, &m, &l, oacc, prow);
     for (int c = 0; c < d; c++)
-      out[(size_t)r * d + c] = (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
+      out[(size_t)r * d + c] = v4_codes ? (float)((double)oacc[c] / (double)l)
+                                        : (float)(((double)oacc[c] * (double)v_scale[(size_t)bk * d + c]) / (double)l);
     free(oacc);
   }
   return 0;
+}
+
+int oracle_attn_rows_qk4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                         const uint8_t* k4_scale, const int8_t* qm_codes, const uint8_t* qm_scale,
+                         const int8_t* k8_codes, const uint8_t* k8_scale, const uint8_t* v_codes,
+                         const float* v_scale, int B, int Hq,
+                         int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
+                         const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+  return attn_rows_4bit(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale, v_codes,
+                        v_scale, NULL, NULL, B, Hq, Hkv, Nq, Nkv, d, kv_tile, causal, sm_scale, rows, nrows, out,
+                        p_codes);
+}
+
+/* FP4 attention (R21 scores, R23 P~V): the 4-bit scores of oracle_attn_rows_qk4, */
+/* P~ and V in E2M1 blocks of 32 with E8M0 scales (V from oracle_quantize_v4),   */
+/* O = O_acc / l (the V scales are inside the products).  p_codes (optional):   */
+/* the E2M1 code (0..15) of every visited key.                                   */
+int oracle_attn_rows_fp4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                         const uint8_t* k4_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, int B, int Hq,
+                         int Hkv, int Nq, int Nkv, int d, int kv_tile, int causal, float sm_scale,
+                         const int64_t* rows, int nrows, float* out, uint8_t* p_codes) {
+  if (!v4_codes || !v4_scale || kv_tile % 32) return -1;
+  return attn_rows_4bit(q4_codes, q4_scale, k4_codes, k4_scale, NULL, NULL, NULL, NULL, NULL, NULL, v4_codes,
+                        v4_scale, B, Hq, Hkv, Nq, Nkv, d, kv_tile, causal, sm_scale, rows, nrows, out, p_codes);
 }
 
 /* fp32 4-bit scores (score4) of flat query rows bh*Nq + i against every key: [nrows, Nkv] */

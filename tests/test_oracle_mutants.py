@@ -133,8 +133,17 @@ MUTANTS = [
     ("split merge: row sums not weighted", "L = fmaf(w, lc[c], L);", "L = L + lc[c];", 1),
     ("split merge: chunks without a visible key kept", "      if (!vis[c]) continue;\n", "", 1),
     ("all-zero MX blocks get scale byte 127", "    *scale = 0;\n", "    *scale = 127;\n", 1),
-    ("Q-smoothing blocks of 16 rows", "const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;",
-     "const int n0 = 16 * blk, n = (N - n0 < 16) ? N - n0 : 16;", 1),
+    # FP4 P~V
+    ("FP4 P~ block exponent one too large", "float fe = floorf(amax) - 2.0f;", "float fe = floorf(amax) - 1.0f;", 1),
+    ("FP4 P~ blocks of 64 keys", "for (int b0 = 0; b0 < nvis; b0 += 32) {\n        const int b1 = b0 + 32 < nvis ? b0 + 32 : nvis;",
+     "for (int b0 = 0; b0 < nvis; b0 += 64) {\n        const int b1 = b0 + 64 < nvis ? b0 + 64 : nvis;", 1),
+    ("FP4 P~ not quantized", "pd[jj] = ldexp(oracle_e2m1_decode(ph[jj]), e);", "pd[jj] = p;", 1),
+    ("FP4 row sum of the unquantized P~", "          code_sum += pd[jj];\n", "          code_sum += p;\n", 1),
+    ("FP4 V scale of the previous key's block", "(int)x->v4s[(size_t)(j / 32) * d + c] - 127",
+     "(int)x->v4s[(size_t)((j > 0 ? j - 1 : 0) / 32) * d + c] - 127", 1),
+    ("FP4 V scale off by one", "(int)x->v4s[(size_t)(j / 32) * d + c] - 127", "(int)x->v4s[(size_t)(j / 32) * d + c] - 126", 1),
+    ("Q-smoothing blocks of 16 rows", "const int n0 = 32 * blk, n = (N - n0 < 32) ? N - n0 : 32;\n      float* qm",
+     "const int n0 = 16 * blk, n = (N - n0 < 16) ? N - n0 : 16;\n      float* qm", 1),
 ]
 
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")

@@ -1016,3 +1016,131 @@ def test_k8_blocks_are_the_smoothed_k_in_int8():
             sl = slice(64 * blk, min(64 * blk + 64, 150))
             _check_int8_pow2_block(ks[0, h, sl], r["k8_codes"][0, h, sl], r["k8_scale"][0, h, blk])
     assert r["k8_scale"][0, 0, 2] >= r["k8_scale"][0, 0, 1] + 3   # the scaled tail block has its own exponent
+
+
+# ------------------------------------------------------------ FP4 P~V (MXFP4 P~ and V)
+def _v4_case(seed=60, B=1, H=2, N=100, d=64):
+    rng = np.random.default_rng(seed)
+    V = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    V[:, :, :, 5] *= 40                                     # an outlier channel gets its own scales
+    return V
+
+
+def test_v4_blocks_properties():
+    """V in E2M1 blocks of 32 consecutive tokens per channel (the last block
+    ragged): the shared exponent puts each block max in [4, 8), codes round to
+    within half the E2M1 spacing, a zero block gets scale byte 0."""
+    V = _v4_case()
+    V[0, 1, 64:96, 9] = 0.0
+    vc, vs = orc.quantize_v4(_f16_bits(V), 0)
+    assert vc.shape == V.shape and vs.shape == (1, 2, 4, 64)
+    x = _f16_vals(V).astype(np.float64)
+    for blk, (a, b) in enumerate(((0, 32), (32, 64), (64, 96), (96, 100))):
+        xb = x[:, :, a:b, :]
+        cb = vc[:, :, a:b, :]
+        sc = 2.0 ** (vs[:, :, blk, :].astype(np.float64) - 127)[:, :, None, :]
+        amax = np.abs(xb).max(2, keepdims=True)
+        live = amax > 0
+        r = amax / sc
+        assert ((r >= 4) & (r < 8))[live].all()
+        y = orc.e2m1_decode(cb) * sc
+        t = np.minimum(np.abs(xb) / sc, 6.0)
+        half = np.where(t >= 4, 1.0, np.where(t >= 2, 0.5, 0.25))
+        assert (np.abs(np.abs(y) / sc - t) <= half + 1e-12)[np.broadcast_to(live, t.shape)].all()
+    assert vs[0, 1, 2, 9] == 0 and not vc[0, 1, 64:96, 9].any()
+    assert vs[0, 0, 0, 5] >= vs[0, 0, 0, 4] + 4             # the outlier channel's own exponent
+
+
+def _fp4_attention(Q, K, V, causal, rows=None, want_p=False):
+    r = orc.quantize_qk4(_f16_bits(Q), _f16_bits(K), 0)
+    vc, vs = orc.quantize_v4(_f16_bits(V), 0)
+    return r, (vc, vs), orc.attn_rows_fp4(r, vc, vs, causal, 1.0 / math.sqrt(Q.shape[-1]), rows=rows, want_p=want_p)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp4_attention_of_a_power_of_two_constant_v_is_that_constant(causal):
+    """V constant per channel and a power of two (exact in every MX block):
+    the same P^ weights both O_acc and l, so O is that constant exactly."""
+    rng = np.random.default_rng(61)
+    Q = rng.standard_normal((1, 2, 70, 64)).astype(np.float32)
+    K = (rng.standard_normal((1, 1, 150, 64)) + 1).astype(np.float32)
+    c = 2.0 ** rng.integers(-6, 6, 64) * np.where(rng.random(64) < 0.5, -1, 1)
+    V = np.broadcast_to(c.astype(np.float32), (1, 1, 150, 64)).copy()
+    _, _, O = _fp4_attention(Q, K, V, causal)
+    assert np.array_equal(O, np.broadcast_to(c.astype(np.float32), O.shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp4_attention_with_q_zero_is_the_mean_of_the_fp4_v(causal):
+    """Q = 0: every score is 0, every P~ is 2^8 and lands on the E2M1 value 4
+    of its block's scale 2^6, so O is the plain mean of the dequantized FP4 V
+    over the visible keys (a closed form)."""
+    rng = np.random.default_rng(62)
+    Nq, Nkv = 40, 131
+    Q = np.zeros((1, 2, Nq, 64), np.float32)
+    K = rng.standard_normal((1, 1, Nkv, 64)).astype(np.float32)
+    V = _v4_case(seed=63, H=1, N=Nkv)
+    r, (vc, vs), (O, P) = _fp4_attention(Q, K, V, causal, want_p=True)
+    deq = orc.e2m1_decode(vc[0, 0]) * 2.0 ** (np.repeat(vs[0, 0], 32, axis=0)[:Nkv].astype(np.float64) - 127)
+    for h in range(2):
+        for i in range(Nq):
+            last = i + Nkv - Nq if causal else Nkv - 1
+            want = deq[:last + 1].mean(axis=0)
+            got = O[h * Nq + i]
+            assert np.abs(got - want).max() <= 2e-6 * max(1.0, np.abs(want).max()), (h, i)
+            assert (P[h * Nq + i, :last + 1] == 6).all()      # E2M1 4.0
+
+
+def test_fp4_p_blocks_take_the_mx_exponent_of_their_largest_value():
+    """Every visited 32-key block of P^ has its largest code at 4 or 6 (E2M1
+    codes 6, 7): the block max, divided by 2^(floor(log2 max) - 2), lies in
+    [4, 8).  Codes are non-negative (P~ >= 0) and masked keys get none."""
+    rng = np.random.default_rng(64)
+    Q = rng.standard_normal((1, 2, 96, 64)).astype(np.float32) * 2
+    K = rng.standard_normal((1, 2, 200, 64)).astype(np.float32)
+    V = _v4_case(seed=65, H=2, N=200)
+    for causal in (False, True):
+        _, _, (O, P) = _fp4_attention(Q, K, V, causal, want_p=True)
+        assert (P < 8).all()                                 # no sign bit
+        for row in range(P.shape[0]):
+            i = row % 96
+            last = i + 200 - 96 if causal else 199
+            for b0 in range(0, last + 1, 32):
+                blk = P[row, b0:min(b0 + 32, last + 1)]
+                assert blk.max() in (6, 7), (causal, row, b0, blk)
+            if causal:
+                assert not P[row, last + 1:].any()
+
+
+def test_fp4_attention_single_tile_against_exact_python_arithmetic():
+    """One KV tile (no rescale): O = RN(sum_k P^_k V^_kc) / RN(sum_k P^_k) with
+    P^ rebuilt here from the scores: fp32 argument (fma), exp2, the block
+    exponent floor(max arg) - 2, E2M1 nearest-even codes; V^ decoded from the
+    oracle's FP4 V.  Exact rationals for the sums."""
+    from fractions import Fraction
+    rng = np.random.default_rng(66)
+    Q = rng.standard_normal((1, 1, 5, 32)).astype(np.float32)
+    K = rng.standard_normal((1, 1, 50, 32)).astype(np.float32)
+    V = _v4_case(seed=67, H=1, N=50, d=32)
+    r, (vc, vs), O = _fp4_attention(Q, K, V, False)
+    S = orc.qk4_scores(r, np.arange(5)).astype(np.float64)
+    c2 = np.float32(np.float32(1.0 / math.sqrt(32)) * np.float32(1.4426950408889634))
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+    def e2m1_nearest_even(t):
+        best = min(range(8), key=lambda k: (abs(mags[k] - t), k & 1))
+        return mags[best]
+    vdec = orc.e2m1_decode(vc[0, 0]) * 2.0 ** (np.repeat(vs[0, 0], 32, axis=0)[:50].astype(np.float64) - 127)
+    for i in range(5):
+        u = (S[i] * np.float64(c2)).astype(np.float32)
+        mm = np.float32(u.max()) - np.float32(8)
+        arg = (S[i] * np.float64(c2) - np.float64(mm)).astype(np.float32)     # fma: exact product, one rounding
+        p = np.exp2(arg.astype(np.float64)).astype(np.float32)
+        ph = []
+        for b0 in (0, 32):
+            e = int(np.floor(arg[b0:b0 + 32].max())) - 2
+            ph += [Fraction(e2m1_nearest_even(float(x) * 2.0 ** -e)) * Fraction(2) ** e for x in p[b0:b0 + 32]]
+        l = np.float32(float(sum(ph)))
+        for c in range(32):
+            acc = np.float32(float(sum(ph[k] * Fraction(float(vdec[k, c])) for k in range(50))))
+            assert O[i, c] == np.float32(np.float64(acc) / np.float64(l)), (i, c)
