@@ -169,10 +169,12 @@ def cpu_baseline(w, Q, K, V, budget_s=20.0):
         qk = orc.quantize_qk4(qb, kb, w.dtype_code, smooth_q=w.smooth_q)
     else:
         qk = orc.quantize_qk(qb, kb, w.dtype_code, w.blk_q, w.blk_k)
-    vc, vs = orc.quantize_v(vb, w.dtype_code)
+    vc, vs = orc.quantize_v4(vb, w.dtype_code) if w.pv4 else orc.quantize_v(vb, w.dtype_code)
     t_quant = time.perf_counter() - t0
 
     def attend(rows):
+        if w.pv4:
+            return orc.attn_rows_fp4(qk, vc, vs, w.causal, w.sm_scale, rows=rows)
         if w.qk4:
             return orc.attn_rows_qk4(qk, vc, vs, w.causal, w.sm_scale, rows=rows)
         return orc.attn_rows(qk, vc, vs, w.blk_q, w.blk_k, w.causal, w.sm_scale, rows=rows)
@@ -408,12 +410,14 @@ def main():
             ev[2].record(stream)
         if w.qk4:
             q = sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q)
-            v = sage.quantize_v(Vd, workspace=ws_v)
+            v = sage.quantize_v4(Vd) if w.pv4 else sage.quantize_v(Vd, workspace=ws_v)
         else:   # quantize_qk + quantize_v in one call (three launches)
             q, v = sage.quantize_qkv(Qd, Kd, Vd, w.blk_q, w.blk_k, workspace=ws_qkv)
         if ev is not None:
             ev[0].record(stream)
-        if w.qk4:
+        if w.pv4:
+            sage.attn_fwd_fp4(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
+        elif w.qk4:
             sage.attn_fwd_qk4(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
         else:
             sage.attn_fwd(q, v, causal=w.causal, sm_scale=w.sm_scale, out=out)
@@ -440,19 +444,19 @@ def main():
     value = w.ops / (ms_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_avg * 1e-3) / 1e12       # roofline: the average launch duration
     attn_tops_p50 = w.ops / (attn_p50 * 1e-3) / 1e12
-    peak = (QK4S_PEAK_TOPS if w.smooth_q else QK4_PEAK_TOPS) if w.qk4 else MFMA_PEAK_TOPS
+    peak = (FP4_PEAK_TOPS if w.pv4 else QK4S_PEAK_TOPS if w.smooth_q else QK4_PEAK_TOPS) if w.qk4 else MFMA_PEAK_TOPS
     log(f"[bench] step {ms_step:.3f} ms ({value:.1f} TOPS); attention kernel p50 {attn_p50:.3f} ms "
         f"mean {attn_avg:.3f} p95 {attn_p95:.3f} ({attn_tops_p50:.1f} TOPS at p50, {attn_tops:.1f} at the mean: "
         f"{100 * attn_tops / peak:.1f}% of peak {peak:.0f}); peak allocated {peak_mem / 2 ** 20:.0f} MiB")
 
     q_el, kv_el = B * H * N * d, B * Hkv * Nkv * d
-    if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below
-        quant_alg = (q_el + kv_el) * (2 + 0.5 + 1 / 32) + 3 * kv_el
+    if w.qk4:   # Q and K: 2-byte inputs, half-byte codes plus a byte per 32; V as below (FP4 V: like Q and K)
+        quant_alg = (q_el + kv_el) * (2 + 0.5 + 1 / 32) + (kv_el * (2 + 0.5 + 1 / 32) if w.pv4 else 3 * kv_el)
         if w.smooth_q:   # K also in INT8 (a byte per value; one exponent byte per 64 keys)
             quant_alg += kv_el * (1 + 1 / (64 * d))
     else:
         quant_alg = 3 * (q_el + 2 * kv_el)  # Q, K, V: read 2-byte inputs, write 1-byte codes
-    quant_act = quant_alg + 2 * 2 * kv_el   # the K-sum and V-max passes read K and V once more
+    quant_act = quant_alg + (2 if w.pv4 else 2 * 2) * kv_el   # the K-sum (and V-max) passes read K (and V) once more
     if w.smooth_q:
         quant_act += 2 * q_el + 2 * kv_el   # the block-mean pass reads Q, the INT8 K pass K once more
     quant_avg = float(np.mean(quant_ms))
@@ -461,12 +465,15 @@ def main():
         f"({100 * quant_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {quant_act / (quant_avg * 1e-3) / 1e9:.0f} GB/s moved")
 
     def attn_only():
-        if w.qk4:
+        if w.pv4:
+            sage.attn_fwd_fp4(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
+        elif w.qk4:
             sage.attn_fwd_qk4(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
         else:
             sage.attn_fwd(q_keep[0], q_keep[1], causal=w.causal, sm_scale=w.sm_scale, out=out)
 
-    q_keep = ((sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q), sage.quantize_v(Vd, workspace=ws_v))
+    q_keep = ((sage.quantize_qk4(Qd, Kd, workspace=ws_qk, smooth_q=w.smooth_q),
+               sage.quantize_v4(Vd) if w.pv4 else sage.quantize_v(Vd, workspace=ws_v))
               if w.qk4 else sage.quantize_qkv(Qd, Kd, Vd, w.blk_q, w.blk_k, workspace=ws_qkv))
     sclk = sample_sclk(attn_only)
     log(f"[bench] shader clock while the attention kernel runs: {sclk}")
@@ -490,7 +497,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp4+fp8 (fp32 softmax)" if w.qk4 else "int8+fp8 (fp32 softmax)",
+        "vs_baseline": None, "dtype": ("fp4 (fp32 softmax)" if w.pv4 else "int8+fp4+fp8 (fp32 softmax)" if w.smooth_q
+                                           else "fp4+fp8 (fp32 softmax)") if w.qk4 else "int8+fp8 (fp32 softmax)",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "Hkv": Hkv, "Nkv": Nkv, "d": d, "causal": w.causal,
                    "in_dtype": w.dtype,

@@ -31,7 +31,8 @@
  *  - 4-bit QK^T (the SageAttention3 abstract: attention on FP4 matrix cores):
  *    sage_quantize_qk4, sage_attn_fwd_qk4(_dump), and with Q smoothing (the
  *    SageAttention2 abstract) sage_quantize_qk4_smooth_q,
- *    sage_attn_fwd_qk4_smooth_q(_dump).
+ *    sage_attn_fwd_qk4_smooth_q(_dump); FP4 P~V as well: sage_quantize_v4,
+ *    sage_attn_fwd_fp4(_dump).
  *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
@@ -432,6 +433,51 @@ int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_s
                                     const float* v_scale, void* O, int out_dtype, int layout, int B, int Hq, int Hkv,
                                     int Nq, int Nkv, int d, int causal, float sm_scale, const int32_t* sel, int n_sel,
                                     int32_t* s_dump, uint8_t* p_dump, void* stream);
+
+/*
+ * sage_quantize_v4 -- V to FP4 for FP4 P~V (SageAttention3 abstract:
+ * attention on FP4 matrix cores), in the OCP Microscaling formats' MXFP4:
+ * E2M1 elements with one E8M0 scale per channel and block of 32 consecutive
+ * tokens of a head (the last block holds the rest, padding tokens zero):
+ *   E = floor(log2(max|v|)) - 2 clamped to [-127, 127], scale byte E + 127,
+ *   codes = E2M1(v / 2^E) round to nearest even, saturating at 6 (sign
+ *   kept); an all-zero block gets scale byte 0 and zero codes.
+ * In:  V [B,H,N,d] or [B,N,H,d] (layout), fp16/bf16 (in_dtype).
+ * Out: v4_codes [B,H,Nkt,d,32] bytes (Nkt = N rounded up to the KV tile of
+ *      64 tokens: per tile, d channel rows of its 64 codes, two tokens per
+ *      byte, the lower token in the low nibble);
+ *      v4_scale [B,H,Nkt/64,2,32,d/32] bytes (per tile, byte (g, m, c) is
+ *      the scale of channel 32c + m over tokens 32g .. 32g+31).
+ * Allocates nothing; no workspace.  Errors as sage_quantize_v.
+ */
+int sage_quantize_v4(const void* V, int in_dtype, int layout, int B, int H, int N, int d, uint8_t* v4_codes,
+                     uint8_t* v4_scale, void* stream);
+
+/*
+ * sage_attn_fwd_fp4 -- FP4 attention: the 4-bit scores of sage_attn_fwd_qk4
+ * and P~V in FP4 as well (all matrix work on the FP4 instructions).  Per
+ * row and KV tile, each 32-key half is one MX block of P~ with exponent
+ *   E = floor(max over its visible keys of the exp2 argument) - 2
+ *   clamped to [-126, 127] (no visible key: -126),
+ * P^ = E2M1(P~ / 2^E) (round to nearest even, saturating; the hardware's
+ * fp32 exp2), the tile's row sum is that of the decoded P^ 2^E (as the
+ * weights of the product), P^V accumulates in fp32 with the block sum as
+ * the inner level, and O = O_acc / l.  V from sage_quantize_v4 (the K/V
+ * head of each query head as sage_attn_fwd_ex).  Other arguments and
+ * errors as sage_attn_fwd_qk4; null V pointers: SAGE_ERR_INVALID_ARG.
+ */
+int sage_attn_fwd_fp4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                      const uint8_t* k4_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, void* O,
+                      int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                      float sm_scale, void* stream);
+
+/* sage_attn_fwd_fp4_dump -- sage_attn_fwd_fp4 with the dumps of
+ * sage_attn_fwd_qk4_dump, the P~ codes as E2M1 codes (0..15). */
+int sage_attn_fwd_fp4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                           const uint8_t* k4_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, void* O,
+                           int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                           float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump,
+                           void* stream);
 
 /*
  * sage_probe_mfma_peak -- a measurement aid, not a step of the method: each of

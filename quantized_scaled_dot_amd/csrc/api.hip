@@ -71,6 +71,9 @@ struct Q4Ptrs {
   const uint8_t* qm_scale = nullptr;
   const int8_t* k8_codes = nullptr;
   const uint8_t* k8_scale = nullptr;
+  // FP4 P~V (both or none; v_codes / v_scale are then unused)
+  const uint8_t* v4_codes = nullptr;
+  const uint8_t* v4_scale = nullptr;
 };
 
 int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
@@ -92,7 +95,12 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   } else {
     SAGE_PTR(q_codes); SAGE_PTR(q_scale); SAGE_PTR(k_codes); SAGE_PTR(k_scale);
   }
-  SAGE_PTR(v_codes); SAGE_PTR(v_scale); SAGE_PTR(O);
+  if (q4 && q4->v4_codes) {
+    SAGE_PTR(q4->v4_codes); SAGE_PTR(q4->v4_scale);
+  } else {
+    SAGE_PTR(v_codes); SAGE_PTR(v_scale);
+  }
+  SAGE_PTR(O);
   if (dump) {
     if (n_sel < 0) return SAGE_ERR_INVALID_ARG;
     if (n_sel > 0) { SAGE_PTR(sel); SAGE_PTR(s_dump); SAGE_PTR(p_dump); }
@@ -107,6 +115,7 @@ int attn_common(const int8_t* q_codes, const float* q_scale, const int8_t* k_cod
   if (q4) {
     a.q4_codes = q4->q4_codes; a.q4_scale = q4->q4_scale; a.k4_codes = q4->k4_codes; a.k4_scale = q4->k4_scale;
     a.qm_codes = q4->qm_codes; a.qm_scale = q4->qm_scale; a.k8_codes = q4->k8_codes; a.k8_scale = q4->k8_scale;
+    a.v4_codes = q4->v4_codes; a.v4_scale = q4->v4_scale;
   }
   (void)hipGetLastError();
   sage::launch_attn_fwd(a, dump, (hipStream_t)stream);
@@ -291,6 +300,42 @@ int sage_attn_fwd_qk4_smooth_q_dump(const uint8_t* q4_codes, const uint8_t* q4_s
   if (!qm_codes || !qm_scale || !k8_codes || !k8_scale) return SAGE_ERR_INVALID_ARG;
   const Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes, k8_scale};
   return attn_common(nullptr, nullptr, nullptr, nullptr, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream, &q4);
+}
+
+int sage_quantize_v4(const void* V, int in_dtype, int layout, int B, int H, int N, int d, uint8_t* v4_codes,
+                     uint8_t* v4_scale, void* stream) {
+  SAGE_TRY(check_shapes(layout, B, H, H, N, N, d));
+  SAGE_TRY(check_in_dtype(in_dtype));
+  SAGE_PTR(V); SAGE_PTR(v4_codes); SAGE_PTR(v4_scale);
+  sage::QuantV4Args a{};
+  a.V = V; a.is_bf16 = in_dtype == SAGE_BF16; a.nhd = layout == SAGE_LAYOUT_BNHD;
+  a.B = B; a.H = H; a.N = N; a.d = d; a.v4_codes = v4_codes; a.v4_scale = v4_scale;
+  (void)hipGetLastError();
+  sage::launch_quantize_v4(a, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sage_attn_fwd_fp4(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                      const uint8_t* k4_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, void* O,
+                      int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                      float sm_scale, void* stream) {
+  if (!v4_codes || !v4_scale) return SAGE_ERR_INVALID_ARG;
+  Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale};
+  q4.v4_codes = v4_codes; q4.v4_scale = v4_scale;
+  return attn_common(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
+                     d, 128, 64, causal, sm_scale, nullptr, 0, nullptr, nullptr, false, stream, &q4);
+}
+
+int sage_attn_fwd_fp4_dump(const uint8_t* q4_codes, const uint8_t* q4_scale, const uint8_t* k4_codes,
+                           const uint8_t* k4_scale, const uint8_t* v4_codes, const uint8_t* v4_scale, void* O,
+                           int out_dtype, int layout, int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                           float sm_scale, const int32_t* sel, int n_sel, int32_t* s_dump, uint8_t* p_dump,
+                           void* stream) {
+  if (!v4_codes || !v4_scale) return SAGE_ERR_INVALID_ARG;
+  Q4Ptrs q4{q4_codes, q4_scale, k4_codes, k4_scale};
+  q4.v4_codes = v4_codes; q4.v4_scale = v4_scale;
+  return attn_common(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
                      d, 128, 64, causal, sm_scale, sel, n_sel, s_dump, p_dump, true, stream, &q4);
 }
 

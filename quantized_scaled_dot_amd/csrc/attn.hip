@@ -60,13 +60,18 @@ struct AttnK {
   const uint8_t* q4_scale;
   const uint8_t* k4_codes;
   const uint8_t* k4_scale;
-  // Q smoothing of the 4-bit scores: FP8 block means of 32 queries (nqp/32
-  // blocks per head, rows of d codes) with E8M0 scales per 32 channels, and
-  // the smoothed K in FP8 blocks (rows of d codes, scales per 32 channels)
+  // Q smoothing of the 4-bit scores: INT8 block means of 32 queries (nqp/32
+  // blocks per head, rows of d codes) with one exponent byte each, and the
+  // smoothed K in INT8 tiles (rows of d codes, one exponent byte per tile)
   const int8_t* qm_codes;
   const uint8_t* qm_scale;
   const int8_t* k8_codes;
   const uint8_t* k8_scale;
+  // FP4 P~V: V in E2M1 (tiles of d channel rows of 32 bytes, two keys per
+  // byte) with E8M0 scales per channel and 32 keys (per tile: 2 x 32 x d/32
+  // bytes, byte (g, m, c) for channel 32c + m and keys 32g .. 32g+31)
+  const uint8_t* v4_codes;
+  const uint8_t* v4_scale;
   float s2;
   const int32_t* sel;
   int n_sel;
@@ -88,7 +93,13 @@ struct AttnK {
 // (the block scales applied inside it), so the dequantization factor is
 // sm_scale * log2(e) alone and the row max runs on fp32.  K tiles are d/2
 // bytes per key; each lane loads the scale bytes of its two MFMA rows' keys
-// one step ahead.  QK4 = 2 adds Q smoothing: the scores also take the mean
+// one step ahead.  QK4 = 3: the same 4-bit scores with P~V in FP4 as well:
+// each lane's 32 keys of a row are one MX block, whose E8M0 exponent is
+// floor(max exponent argument) - 2; the hardware converts P~ / 2^E to E2M1
+// (round to nearest even, saturating), the row sum of the decoded P^ comes
+// from one 16x16x128 FP4 instruction, the P~V instructions take both
+// operands in FP4 with their block scales, and O = O_acc / l (the V scales
+// are inside the products).  QK4 = 2 adds Q smoothing: the scores also take the mean
 // of the wave's 32 queries (one block) against the smoothed K, both INT8
 // with power-of-two block scales: the INT8 matrix instruction sums the
 // integer products exactly, one fma per score turns that sum into the exact
@@ -102,22 +113,25 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   static_assert(NW == 4 || (NW == 8 && D == 128 && !CAUSAL && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
   constexpr int QT = 32 * NW;   // query rows per workgroup
   constexpr bool QSM = QK4 == 2;
+  constexpr bool PV4 = QK4 == 3;               // FP4 P~V
   constexpr int KB = QK4 ? D / 2 : D;          // K code bytes per key
   constexpr int KS = KB / 32;                  // k-steps of the score MFMA over d (32 code bytes a lane pair)
   constexpr int CT = D / 32;                   // 32-channel tiles of the FP8 MFMA
-  constexpr int TILE = kKTile * D;             // bytes of one V tile (and of one INT8 K tile) in HBM
+  constexpr int VB = PV4 ? kKTile / 2 : kKTile;  // V code bytes per channel row of a tile
+  constexpr int TILE = VB * D;                 // bytes of one V tile in HBM
+  constexpr int RV = VB + 16;                  // V rows in LDS, padded by 16 bytes
   constexpr int KTILE = kKTile * KB;           // bytes of one K tile in HBM
   constexpr int RK = QK4 ? KB + 16 : kRowK<D>;
   using SV = typename std::conditional<(QK4 != 0), v16f, v16i>::type;   // score registers
   constexpr int RK8 = kRowK<D>;                 // INT8 K rows of the mean term (Q smoothing), padded like INT8 K
   __shared__ __attribute__((aligned(16))) int8_t sK[2][kKTile * RK];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * kRowV];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * RV];
   __shared__ __attribute__((aligned(16))) uint8_t sK8[2][QSM ? kKTile * RK8 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int li = lane & 31, lg = lane >> 5;
-  const v8i ones16 = rowsum_ones_operand(lane);   // INT8 row sums (see rowsum_fp8)
+  const v8i ones16 = rowsum_ones_operand(lane, PV4);   // row sums of P^ (see rowsum_fp8)
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
   // on XCD b % 8).  Flat query head bh = b*Hq + h reads flat K/V head
   // bh / g (the g query heads of a K/V head are consecutive).  When the K/V
@@ -196,10 +210,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   // K tile t lives in sK[t%2], V tile t in sV[t%3]; K is staged one tile
   // ahead of V (see the loop).  The K and V tiles are contiguous blocks in
   // HBM (K: 64 rows of KB code bytes; V: d rows of 64 codes).
-  constexpr int NKI = kKTile * RK / 1024, NVI = D * kRowV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64)
+  constexpr int NKI = kKTile * RK / 1024, NVI = D * RV / 1024;   // 9, 10 (d = 128); 5, 5 (d = 64); FP4 V: 6, 3
   constexpr int N8I = QSM ? kKTile * RK8 / 1024 : 0;                 // INT8 K tile (Q smoothing)
   constexpr int KTILE8 = kKTile * D;                                 // bytes of one INT8 K tile in HBM
-  static_assert(kKTile * RK % 1024 == 0 && D * kRowV % 1024 == 0 && kKTile * RK8 % 1024 == 0,
+  static_assert(kKTile * RK % 1024 == 0 && D * RV % 1024 == 0 && kKTile * RK8 % 1024 == 0,
                 "whole DMA instructions per tile");
   constexpr int FK = NKI / NW, F8 = N8I / NW, FV = NVI / NW;         // whole rounds
   constexpr int XK = NKI % NW, X8 = N8I % NW, XR = NKI % NW + N8I % NW + NVI % NW;   // leftovers: K, INT8 K, all
@@ -208,7 +222,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   __builtin_assume(wave >= 0 && wave < NW);
   const __amdgpu_buffer_rsrc_t rK =
       head_rsrc((QK4 ? (const int8_t*)p.k4_codes : p.k_codes) + (size_t)bhkv * p.nkt * KTILE, (uint32_t)(p.nkt * KTILE));
-  const __amdgpu_buffer_rsrc_t rV = head_rsrc(p.v_codes + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
+  const __amdgpu_buffer_rsrc_t rV =
+      head_rsrc((PV4 ? p.v4_codes : p.v_codes) + (size_t)bhkv * p.nkt * TILE, (uint32_t)(p.nkt * TILE));
   const __amdgpu_buffer_rsrc_t rK8 =
       QSM ? head_rsrc(p.k8_codes + (size_t)bhkv * p.nkt * KTILE8, (uint32_t)(p.nkt * KTILE8)) : rK;
   auto k_src = [&](int i, int rk, int kb) {
@@ -218,8 +233,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   };
   auto v_src = [&](int i) {
     const int o = 1024 * i + 16 * lane;
-    const int r = o / kRowV, c = min((o % kRowV) / 16, kKTile / 16 - 1);
-    return (uint32_t)(r * kKTile + 16 * c);
+    const int r = o / RV, c = min((o % RV) / 16, VB / 16 - 1);
+    return (uint32_t)(r * VB + 16 * c);
   };
   uint32_t koff[FK > 0 ? FK : 1], k8off[F8 > 0 ? F8 : 1], voff[FV > 0 ? FV : 1];
 #pragma unroll
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   const uint32_t k8base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)&sK8[0][0]);
   // K tile tk (and its FP8 form) into K slot kslot, V tile tv into V slot vslot
   auto stageKV = [&](int tk, int kslot, int tv, int vslot) {
-    const uint32_t kd = kbase + (uint32_t)(kslot * (kKTile * RK)), vd = vbase + (uint32_t)(vslot * (D * kRowV));
+    const uint32_t kd = kbase + (uint32_t)(kslot * (kKTile * RK)), vd = vbase + (uint32_t)(vslot * (D * RV));
     const uint32_t k8d = k8base + (uint32_t)(kslot * (kKTile * RK8));
 #pragma unroll
     for (int j = 0; j < FK; j++) lds_copy16_at(rK, kd + 1024 * (wave + NW * j), koff[j], tk * KTILE);
@@ -357,15 +372,29 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   // that block sum into the fp32 accumulator O_acc passed as its C operand
   // (outer level; the C addition is an fp32 add outside the instruction's
   // product-alignment window) ----
-  auto pv = [&](const v8i& pb, int vslot) {
+  // FP4 P~V: pb holds 32 E2M1 codes in its low 16 bytes, pscale the lane's
+  // E8M0 byte of them, vsw the V scale bytes of the lane's rows (byte ct:
+  // channel 32ct + li, keys 32lg ..)
+  auto pv = [&](const v8i& pb, int vslot, int pscale, unsigned vsw) {
 #pragma unroll
     for (int ct = 0; ct < CT; ct++) {
-      const uint8_t* vb = sV[vslot] + (32 * ct + li) * kRowV + 32 * lg;   // channel row, keys 32*lg..
+      const uint8_t* vb = sV[vslot] + (32 * ct + li) * RV + (PV4 ? 16 : 32) * lg;   // channel row, keys 32*lg..
       const v4i v0 = *(const v4i*)(vb);
-      const v4i v1 = *(const v4i*)(vb + 16);
-      const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
+      if constexpr (PV4) {
+        const v8i av = {v0[0], v0[1], v0[2], v0[3], 0, 0, 0, 0};
+        oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 4, 4, 0,
+                                                                   (int)((vsw >> (8 * ct)) & 0xFFu), 0, pscale);
+      } else {
+        const v4i v1 = *(const v4i*)(vb + 16);
+        const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 0, 0, 0, 127, 0, 127);
+      }
     }
+  };
+  // FP4 P~V: the V scale bytes of this lane's rows in tile t
+  auto vscale4 = [&](int t) -> unsigned {
+    const uint8_t* vsp = p.v4_scale + ((size_t)(bhkv * p.nkt + t) * 64 + 32 * lg + li) * (D / 32);
+    return D == 128 ? *(const unsigned*)vsp : (unsigned)*(const uint16_t*)vsp;
   };
   // whole tile t after every row of this wave (causal): nothing to compute
   auto future = [&](int t) { return CAUSAL && t * kKTile > qrow0 + 31 + off; };
@@ -374,6 +403,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   // that tile's rescale of the running state (alpha_prev, applied before
   // the pending P~V when some row of the wave got a larger max).
   v8i pprev;
+  int pscale_prev = 127;        // FP4 P~V: E8M0 byte of pprev
+  unsigned vsw_prev = 0u;       // FP4 P~V: V scale bytes of the tile of pprev
   bool pend = false, grew = false;
   float alpha_prev = 1.0f;
   // K scales (of this lane's two runs) of the tile whose softmax comes next
@@ -421,7 +452,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
     __builtin_amdgcn_sched_barrier(0);   // issue the copies first
     const int kv0 = t * kKTile;
     const int keyb = kv0 + 32 * lg;   // sc0[v] is key keyb + v, sc1[v] is key keyb + 16 + v
-    if (had) pv(pprev, (t + 2) % 3);   // slot of tile t-1
+    if (had) pv(pprev, (t + 2) % 3, pscale_prev, vsw_prev);   // slot of tile t-1
+    if (PV4) vsw_prev = vscale4(min(t, ntiles - 1));   // for the P~V of tile t (next step)
 
     if (!(DIAG && future(t))) {
       if (DUMP && dump_idx >= 0) {
@@ -438,6 +470,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
       const bool diag = DIAG && (kv0 + kKTile - 1 > lastk0);
       // ---- online softmax state (the max runs over visible keys only) ----
       float ustar, c2a, c2b;   // c2a, c2b: dequantization factors of the two runs
+      float smx_lane = 0.0f;   // 4-bit: the max over this lane's visible keys
       if constexpr (QK4) {
         float smx = -__builtin_inff();
         if (diag) {
@@ -449,6 +482,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
 #pragma unroll
           for (int v = 0; v < 16; v++) smx = fmaxf(fmaxf(smx, sc0[v]), sc1[v]);   // v_max3_f32 chain
         }
+        smx_lane = smx;
         smx = pair_max_f32(smx);
         c2a = c2b = p.s2;
         ustar = smx * c2a;
@@ -492,7 +526,18 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
       // exp2 is the hardware's fp32 exp2 (v_exp_f32): any argument is valid,
       // and masked (future) keys get -inf, whose exp2 is exactly 0.
       v8i pb;
-      float rs = 0.0f;   // 4-bit scores: the fp32 row sum of P~ on the VALU
+      float rs = 0.0f;   // 4-bit scores with FP8 P~V: the fp32 row sum of P~ on the VALU
+      // FP4 P~V: this lane's block exponent E = floor(max arg) - 2 in
+      // [-126, 127] (no visible key: -126), the convert's divisor 2^E and
+      // the E8M0 byte E + 127
+      int pscale = 127;
+      float pdiv = 1.0f;
+      if constexpr (PV4) {
+        const float fe = fminf(fmaxf(__builtin_floorf(__builtin_fmaf(smx_lane, c2a, -ka)) - 2.0f, -126.0f), 127.0f);
+        const int e = (int)fe;
+        pscale = e + 127;
+        pdiv = __builtin_amdgcn_ldexpf(1.0f, e);
+      }
 #pragma unroll
       for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -508,26 +553,45 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
             if (diag && keyb + 16 * h + 4 * q + e > lastk) arg = -__builtin_inff();
             const float x = __builtin_amdgcn_exp2f(arg);
             pv4[e] = x;
-            if constexpr (QK4 != 0) rs += x;
+            if constexpr (QK4 == 1 || QK4 == 2) rs += x;
           }
-          // the low-half convert's "old" operand is a register that dies here
-          // (its high half is overwritten by the second convert)
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[0], pv4[1], __float_as_int(pv4[0]), false);
-          pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[2], pv4[3], w, true);
+          if constexpr (PV4) {
+            // keys 16h + 4q .. +3 are E2M1 elements 16h + 4q .. of the lane's
+            // block: bytes 2(q%2), 2(q%2)+1 of dword 2h + q/2, low nibble first
+            unsigned w;
+            if (q % 2 == 0) {
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv4[0], pv4[1], pdiv, 0);
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv4[2], pv4[3], pdiv, 1);
+            } else {
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((unsigned)pb[2 * h + q / 2], pv4[0], pv4[1], pdiv, 2);
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv4[2], pv4[3], pdiv, 3);
+            }
+            pb[2 * h + q / 2] = (int)w;
+          } else {
+            // the low-half convert's "old" operand is a register that dies here
+            // (its high half is overwritten by the second convert)
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[0], pv4[1], __float_as_int(pv4[0]), false);
+            pb[4 * h + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pv4[2], pv4[3], w, true);
+          }
         }
       }
+      if constexpr (PV4) { pb[4] = 0; pb[5] = 0; pb[6] = 0; pb[7] = 0; }
       // keep the softmax in this block: without a use here the compiler
       // moves it below the rescale branch, away from the MFMAs it should
       // overlap (an empty statement that reads the packed codes and the sum)
       asm volatile("" : "+v"(pb), "+v"(rs));
       // INT8 scores: the row sum of the FP8 codes P^ on the matrix core (each
-      // lane gets its row's whole 64-key sum)
+      // lane gets its row's whole 64-key sum); FP4 P~V: of the E2M1 codes
+      // with their block scales
       if constexpr (QK4 == 0) rs = rowsum_fp8(ones16, pb);
+      if constexpr (PV4) rs = rowsum_fp4(ones16, pb, pscale);
       if (DUMP && dump_idx >= 0) {
         uint8_t* pd = p.p_dump + ((size_t)dump_idx * QT + (row - q0)) * Nkv + keyb;
 #pragma unroll
         for (int k = 0; k < 32; k++)
-          if (!RAGGED || keyb + k < Nkv) pd[k] = (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
+          if (!RAGGED || keyb + k < Nkv)
+            pd[k] = PV4 ? (uint8_t)(((unsigned)pb[k >> 3] >> (4 * (k & 7))) & 0xF)
+                        : (uint8_t)(((unsigned)pb[k >> 2] >> (8 * (k & 3))) & 0xFF);
       }
       // alpha = exp2(m - m'): 1 exactly where the max did not grow, 0 on the
       // first visited tile (m = -1e30, the state is still zero)
@@ -537,6 +601,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
       alpha_prev = alpha;
       m = mnew;
       pprev = pb;
+      pscale_prev = pscale;
       pend = true;
     } else {
       if (next) qk(t + 1, nx0, nx1);
@@ -603,12 +668,13 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
   }
   if (pend) {   // the last visited tile is t-1
     if (grew) rescale();
-    pv(pprev, (t + 2) % 3);
+    pv(pprev, (t + 2) % 3, pscale_prev, vsw_prev);
   }
 
   // ---- epilogue: O = O_acc * v_scale / l ----
-  // INT8: every lane holds its row's whole sum; 4-bit: each lane summed half the keys
-  const float lt = QK4 ? pair_sum_f32(lpart) : lpart;
+  // INT8 and FP4 P~V: every lane holds its row's whole sum; 4-bit with FP8 P~V:
+  // each lane summed half the keys
+  const float lt = QK4 == 1 || QK4 == 2 ? pair_sum_f32(lpart) : lpart;
   const float inv = 1.0f / lt;
   const float* vs = p.v_scale + (size_t)bhkv * D;
   const size_t orow = p.nhd ? ((size_t)(bh / p.Hq) * Nq + row) * p.Hq + bh % p.Hq : (size_t)bh * Nq + row;
@@ -618,10 +684,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) 
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int c0 = 32 * ct + 8 * q + 4 * lg;   // O^T register 4q+e holds channel c0 + e
-      const v4f sc = *(const v4f*)(vs + c0);
+      const v4f sc = PV4 ? v4f{1.0f, 1.0f, 1.0f, 1.0f} : *(const v4f*)(vs + c0);
       v4f o;
 #pragma unroll
-      for (int e = 0; e < 4; e++) o[e] = oacc[ct][4 * q + e] * (sc[e] * inv);
+      for (int e = 0; e < 4; e++) o[e] = PV4 ? oacc[ct][4 * q + e] * inv : oacc[ct][4 * q + e] * (sc[e] * inv);
       if (store) store4<OUT>(p.O, orow * D + c0, o);
     }
   }
@@ -650,10 +716,11 @@ static void launch4(const AttnK& k, int grid, int out, bool dump, bool wide, hip
   else launch5<D, CAUSAL, RAGGED, FINEK, QK4, 0>(k, grid, dump, wide, st);
 }
 // the score variant: INT8 with K blocks of a tile, INT8 with finer K blocks,
-// 4-bit, or 4-bit with Q smoothing
+// 4-bit, 4-bit with Q smoothing, or 4-bit with FP4 P~V
 template <int D, bool CAUSAL, bool RAGGED>
 static void launch3(const AttnK& k, int grid, int variant, int out, bool dump, bool wide, hipStream_t st) {
-  if (variant == 3) launch4<D, CAUSAL, RAGGED, false, 2>(k, grid, out, dump, wide, st);
+  if (variant == 4) launch4<D, CAUSAL, RAGGED, false, 3>(k, grid, out, dump, wide, st);
+  else if (variant == 3) launch4<D, CAUSAL, RAGGED, false, 2>(k, grid, out, dump, wide, st);
   else if (variant == 2) launch4<D, CAUSAL, RAGGED, false, 1>(k, grid, out, dump, wide, st);
   else if (variant == 1) launch4<D, CAUSAL, RAGGED, true, 0>(k, grid, out, dump, wide, st);
   else launch4<D, CAUSAL, RAGGED, false, 0>(k, grid, out, dump, wide, st);
@@ -717,7 +784,8 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   const bool ragged = a.Nq % kQTile != 0 || a.Nkv % kQTile != 0;
   k.q4_codes = a.q4_codes; k.q4_scale = a.q4_scale; k.k4_codes = a.k4_codes; k.k4_scale = a.k4_scale;
   k.qm_codes = a.qm_codes; k.qm_scale = a.qm_scale; k.k8_codes = a.k8_codes; k.k8_scale = a.k8_scale;
-  const int variant = a.q4_codes ? (a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
+  k.v4_codes = a.v4_codes; k.v4_scale = a.v4_scale;
+  const int variant = a.q4_codes ? (a.v4_codes ? 4 : a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
   // 256-row workgroups: non-causal INT8 at d = 128 on whole 256-row query tiles
   // (not for the test dumps, which address 128-row tiles)
   const bool wide = !dump && a.d == 128 && !a.causal && !ragged && variant <= 1 && a.Nq % 256 == 0;

@@ -44,13 +44,22 @@ __device__ __forceinline__ int unbias_score(int x) { return (int)((unsigned)x - 
 // and zero elsewhere, row r of column n sums lane groups of r's parity: the
 // 64 keys of query n (even) or n + 16 (odd).  Lane l holds rows 4(l/16) ..
 // +3 of column l%16, i.e. the sum for its own query l%32 in every register.
-__device__ __forceinline__ v8i rowsum_ones_operand(int lane) {
-  const int w = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
-  return v8i{w, w, w, w, w, w, w, w};
+// The same with E2M1 operands (fp4): 32 codes per lane in the low 16 bytes,
+// E2M1 1.0 = code 2, and the B scale of each lane (its own block's E8M0
+// byte) applied inside the instruction.
+__device__ __forceinline__ v8i rowsum_ones_operand(int lane, bool fp4 = false) {
+  const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+  const int w = on ? (fp4 ? 0x22222222 : 0x38383838) : 0;
+  return fp4 ? v8i{w, w, w, w, 0, 0, 0, 0} : v8i{w, w, w, w, w, w, w, w};
 }
 __device__ __forceinline__ float rowsum_fp8(const v8i& ones, const v8i& pb) {
   const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
                                                                  127, 0, 127);
+  return r[0];
+}
+__device__ __forceinline__ float rowsum_fp4(const v8i& ones, const v8i& pb, int pscale) {
+  const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0,
+                                                                 127, 0, pscale);
   return r[0];
 }
 

@@ -55,6 +55,10 @@ struct AttnArgs {
   const uint8_t* qm_scale = nullptr;
   const int8_t* k8_codes = nullptr;
   const uint8_t* k8_scale = nullptr;
+  // FP4 P~V (v4_codes != nullptr, with the 4-bit scores): V in E2M1 tiles and
+  // their E8M0 scales as in QuantV4Args; v_codes / v_scale unused
+  const uint8_t* v4_codes = nullptr;
+  const uint8_t* v4_scale = nullptr;
   // dump (test) mode
   const int32_t* sel;
   int n_sel;
@@ -85,6 +89,20 @@ struct Quant4Args {
   void* workspace;     // quantize_qk_workspace(B*Hkv, Nkv, d) bytes
 };
 void launch_quantize_qk4(const Quant4Args& a, hipStream_t st);
+
+// V in E2M1 (MXFP4) for FP4 P~V: per channel and block of 32 tokens one E8M0
+// scale; codes as KV tiles of d channel rows of 32 bytes (two tokens per
+// byte, low nibble first) [B,H,Nkt,d,32]; scales per tile permuted for the
+// attention kernel, [B,H,Nkt/64,2,32,d/32] (byte (g, m, c) for channel
+// 32c + m and tokens 32g .. 32g+31 of the tile); padding tokens zero.
+struct QuantV4Args {
+  const void* V;
+  int is_bf16, nhd;
+  int B, H, N, d;
+  uint8_t* v4_codes;
+  uint8_t* v4_scale;
+};
+void launch_quantize_v4(const QuantV4Args& a, hipStream_t st);
 
 // Decode over a quantized KV cache: split-KV chunks of kv_chunk keys, merged.
 struct DecodeArgs {

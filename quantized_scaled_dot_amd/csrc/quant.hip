@@ -549,6 +549,56 @@ __global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ 
   if (c == 0) qm_scale[r] = (uint8_t)(e + 127);
 }
 
+// FP4 V (MXFP4): one thread per (head, KV tile, channel): the tile's 64
+// tokens of the channel in two blocks of 32, each with the shared exponent
+// E = ilogb(max) - 2 clamped to [-127, 127] (an all-zero block: byte 0) and
+// the E2M1 codes of v / 2^E; tokens past N count as zero.  Lanes are
+// consecutive channels, so each token's loads are one contiguous row piece.
+template <int D>
+__global__ __launch_bounds__(256) void v4_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in, int BH,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
+  const int nkt = in.P / kKTile;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)BH * nkt * D) return;
+  const int c = (int)(gid % D);
+  const long long rest = gid / D;
+  const int t = (int)(rest % nkt), bh = (int)(rest / nkt);
+  const uint16_t* src = V + in.head(bh, D) + c;
+  const size_t stride = in.stride(D);
+  v4i packed[2];
+  unsigned sbyte[2];
+#pragma unroll
+  for (int g = 0; g < 2; g++) {
+    float x[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      const int tok = t * kKTile + 32 * g + i;
+      x[i] = tok < in.N ? load_h(src[(size_t)tok * stride], is_bf16) : 0.0f;
+      a = fmaxf(a, fabsf(x[i]));
+    }
+    packed[g] = v4i{0, 0, 0, 0};
+    sbyte[g] = 0;
+    if (a != 0.0f) {
+      const int e = min(max(ilogbf(a) - 2, -127), 127);
+      sbyte[g] = (unsigned)(e + 127);
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        unsigned word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) word |= e2m1_code(ldexpf(x[8 * w + k], -e)) << (4 * k);
+        packed[g][w] = (int)word;
+      }
+    }
+  }
+  uint8_t* dst = codes + ((size_t)(bh * nkt + t) * D + c) * 32;
+  __builtin_nontemporal_store(packed[0], (v4i*)dst);
+  __builtin_nontemporal_store(packed[1], (v4i*)(dst + 16));
+  uint8_t* sp = scale + (size_t)(bh * nkt + t) * 64 * (D / 32);
+  sp[(c % 32) * (D / 32) + c / 32] = (uint8_t)sbyte[0];
+  sp[(32 + c % 32) * (D / 32) + c / 32] = (uint8_t)sbyte[1];
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
@@ -695,6 +745,19 @@ static void launch_qk4_d(const Quant4Args& a, hipStream_t st) {
 void launch_quantize_qk4(const Quant4Args& a, hipStream_t st) {
   if (a.d == 128) launch_qk4_d<128>(a, st);
   else launch_qk4_d<64>(a, st);
+}
+
+void launch_quantize_v4(const QuantV4Args& a, hipStream_t st) {
+  const InRows in{a.H, a.N, round_up(a.N, kKTile), a.nhd};
+  const int BH = a.B * a.H;
+  const long long n = (long long)BH * (in.P / kKTile) * a.d;
+  const dim3 g((unsigned)((n + 255) / 256));
+  if (a.d == 128)
+    hipLaunchKernelGGL(v4_quant_kernel<128>, g, dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, in, BH, a.v4_codes,
+                       a.v4_scale);
+  else
+    hipLaunchKernelGGL(v4_quant_kernel<64>, g, dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, in, BH, a.v4_codes,
+                       a.v4_scale);
 }
 
 size_t quantize_qk_workspace(int BHkv, int Nkv, int d) {

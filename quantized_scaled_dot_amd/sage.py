@@ -27,8 +27,8 @@ SYMBOLS = ("sage_status_string", "sage_kv_tile", "sage_quantize_qk_workspace_byt
            "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attn_fwd_dump", "sage_attn_fwd_ex_dump", "sage_quantize_q",
            "sage_quantize_k", "sage_decode_kv_chunk", "sage_attn_decode_workspace_bytes", "sage_attn_decode",
            "sage_attn_decode_noalloc", "sage_quantize_qk4", "sage_attn_fwd_qk4", "sage_attn_fwd_qk4_dump", "sage_quantize_qk4_smooth_q",
-           "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump", "sage_probe_mfma_peak",
-           "sage_probe_hbm_read")
+           "sage_attn_fwd_qk4_smooth_q", "sage_attn_fwd_qk4_smooth_q_dump", "sage_quantize_v4", "sage_attn_fwd_fp4",
+           "sage_attn_fwd_fp4_dump", "sage_probe_mfma_peak", "sage_probe_hbm_read")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -84,6 +84,12 @@ _lib.sage_attn_fwd_qk4_smooth_q.restype = _I
 _lib.sage_attn_fwd_qk4_smooth_q.argtypes = [_P] * 11 + [_I] * 9 + [_F, _P]
 _lib.sage_attn_fwd_qk4_smooth_q_dump.restype = _I
 _lib.sage_attn_fwd_qk4_smooth_q_dump.argtypes = [_P] * 11 + [_I] * 9 + [_F, _P, _I, _P, _P, _P]
+_lib.sage_quantize_v4.restype = _I
+_lib.sage_quantize_v4.argtypes = [_P] + [_I] * 6 + [_P, _P, _P]
+_lib.sage_attn_fwd_fp4.restype = _I
+_lib.sage_attn_fwd_fp4.argtypes = [_P] * 7 + [_I] * 9 + [_F, _P]
+_lib.sage_attn_fwd_fp4_dump.restype = _I
+_lib.sage_attn_fwd_fp4_dump.argtypes = [_P] * 7 + [_I] * 9 + [_F, _P, _I, _P, _P, _P]
 _lib.sage_attn_fwd_ex_dump.restype = _I
 _lib.sage_attn_fwd_ex_dump.argtypes = [_P] * 7 + [_I] * 11 + [_F, _P, _I, _P, _P, _P]
 _lib.sage_probe_mfma_peak.restype = _I
@@ -258,6 +264,22 @@ def sage_attn_fwd_qk4_smooth_q_dump(q4_codes, q4_scale, k4_codes, k4_scale, qm_c
     return _lib.sage_attn_fwd_qk4_smooth_q_dump(q4_codes, q4_scale, k4_codes, k4_scale, qm_codes, qm_scale, k8_codes,
                                                 k8_scale, v_codes, v_scale, O, out_dtype, layout, B, Hq, Hkv, Nq, Nkv,
                                                 d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
+
+
+def sage_quantize_v4(V, in_dtype, layout, B, H, N, d, v4_codes, v4_scale, stream):
+    return _lib.sage_quantize_v4(V, in_dtype, layout, B, H, N, d, v4_codes, v4_scale, stream)
+
+
+def sage_attn_fwd_fp4(q4_codes, q4_scale, k4_codes, k4_scale, v4_codes, v4_scale, O, out_dtype, layout, B, Hq, Hkv,
+                      Nq, Nkv, d, causal, sm_scale, stream):
+    return _lib.sage_attn_fwd_fp4(q4_codes, q4_scale, k4_codes, k4_scale, v4_codes, v4_scale, O, out_dtype, layout, B,
+                                  Hq, Hkv, Nq, Nkv, d, causal, sm_scale, stream)
+
+
+def sage_attn_fwd_fp4_dump(q4_codes, q4_scale, k4_codes, k4_scale, v4_codes, v4_scale, O, out_dtype, layout, B, Hq,
+                           Hkv, Nq, Nkv, d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream):
+    return _lib.sage_attn_fwd_fp4_dump(q4_codes, q4_scale, k4_codes, k4_scale, v4_codes, v4_scale, O, out_dtype, layout,
+                                       B, Hq, Hkv, Nq, Nkv, d, causal, sm_scale, sel, n_sel, s_dump, p_dump, stream)
 
 
 # ---------------------------------------------------------------- tensor helpers
@@ -583,6 +605,64 @@ def attn_fwd_qk4(qk4, v, causal=False, sm_scale=None, out_dtype=torch.float32, o
         sel, s_dump, p_dump = _check_dump(dump, Nkv, dev)
         fn = sage_attn_fwd_qk4_smooth_q_dump if smooth else sage_attn_fwd_qk4_dump
         _check(fn(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
+    return out
+
+
+def quantize_v4(V, layout="bhnd", stream=None):
+    """V in E2M1 with one E8M0 scale per channel and 32 tokens (MXFP4), for
+    attn_fwd_fp4.  Returns (v4_codes [B,H,Nt/64,d,32] bytes: per KV tile, d
+    channel rows of 64 codes, two per byte, low nibble first; v4_scale
+    [B,H,Nt/64,2,32,d/32] bytes: per tile, byte (g, m, c) for channel 32c + m
+    and tokens 32g ..); see ``v4_to_natural``."""
+    B, H, N, d = _bhnd(V, layout)
+    dev = V.device
+    kt = sage_kv_tile()
+    T = -(-N // kt)
+    v4_codes = torch.empty((B, H, T, d, kt // 2), dtype=torch.uint8, device=dev)
+    v4_scale = torch.empty((B, H, T, 2, 32, d // 32), dtype=torch.uint8, device=dev)
+    _check(sage_quantize_v4(_ptr(V), _DT.get(V.dtype, -1), _layout(layout), B, H, N, d, _ptr(v4_codes),
+                            _ptr(v4_scale), _stream(stream)))
+    return v4_codes, v4_scale
+
+
+def v4_to_natural(v4):
+    """(v4_codes, v4_scale) of quantize_v4 -> (codes [B,H,Nt,d] one per value,
+    scales [B,H,Nt/32,d]) token-major (Nt: tokens rounded up to 64)."""
+    codes, scale = v4
+    B, H, T, d, kb = codes.shape
+    lo, hi = codes & 0xF, codes >> 4
+    nib = torch.stack((lo, hi), dim=-1).reshape(B, H, T, d, 2 * kb)              # [.., d, 64 tokens]
+    nat = nib.permute(0, 1, 2, 4, 3).reshape(B, H, T * 2 * kb, d)
+    sc = scale.permute(0, 1, 2, 3, 5, 4).reshape(B, H, T, 2, d).reshape(B, H, 2 * T, d)   # channel 32c + m
+    return nat, sc
+
+
+def attn_fwd_fp4(qk4, v4, causal=False, sm_scale=None, out_dtype=torch.float32, out=None, layout="bhnd", stream=None,
+                 dump=None):
+    """FP4 attention: ``qk4`` from quantize_qk4 (without Q smoothing), ``v4``
+    from quantize_v4; the scores and P~V both on the FP4 matrix instructions."""
+    if "qm_codes" in qk4:
+        raise ValueError("attn_fwd_fp4 takes the plain 4-bit Q/K codes (no Q smoothing)")
+    B, Hq, _, h2 = qk4["q4_codes"].shape
+    d = 2 * h2
+    Hkv, Nkt = qk4["k4_codes"].shape[1], qk4["k4_codes"].shape[2]
+    Nq, Nkv = qk4["Nq"], qk4["Nkv"]
+    dev = qk4["q4_codes"].device
+    kt = sage_kv_tile()
+    v4_codes, v4_scale = v4
+    _expect(v4_codes, (B, Hkv, Nkt // kt, d, kt // 2), (torch.uint8,), dev, "v4_codes")
+    _expect(v4_scale, (B, Hkv, Nkt // kt, 2, 32, d // 32), (torch.uint8,), dev, "v4_scale")
+    if sm_scale is None:
+        sm_scale = default_sm_scale(d)
+    out = _out(out, B, Hq, Nq, d, out_dtype, layout, dev)
+    args = (_ptr(qk4["q4_codes"]), _ptr(qk4["q4_scale"]), _ptr(qk4["k4_codes"]), _ptr(qk4["k4_scale"]),
+            _ptr(v4_codes), _ptr(v4_scale), _ptr(out), _DT.get(out.dtype, -1), _layout(layout), B, Hq, Hkv, Nq, Nkv,
+            d, int(bool(causal)), float(sm_scale))
+    if dump is None:
+        _check(sage_attn_fwd_fp4(*args, _stream(stream)))
+    else:
+        sel, s_dump, p_dump = _check_dump(dump, Nkv, dev)
+        _check(sage_attn_fwd_fp4_dump(*args, _ptr(sel), sel.numel(), _ptr(s_dump), _ptr(p_dump), _stream(stream)))
     return out
 
 

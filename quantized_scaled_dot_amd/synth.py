@@ -44,7 +44,8 @@ class Workload:
     Nkv_: int = 0         # keys (0: N)
     decode: bool = False  # N new queries against a quantized cache of Nkv keys (split over the keys)
     qk4: bool = False     # 4-bit QK^T (E2M1, a power-of-two scale per 32 channels) instead of INT8
-    smooth_q: bool = False  # with qk4: Q smoothing (mean of each 32-query block, restored in FP8)
+    smooth_q: bool = False  # with qk4: Q smoothing (mean of each 32-query block, restored in INT8)
+    pv4: bool = False     # with qk4: P~V in FP4 too (E2M1 P~ and V with E8M0 scales per 32 keys / tokens)
     q_bias_var: float = 0.0   # variance of a per-(b, h, channel) bias added to every query
 
     @property
@@ -98,6 +99,9 @@ WORKLOADS = {
     # the video DiT shape with 4-bit QK^T
     "video-dit-32k-qk4": Workload("video-dit-32k-qk4", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0,
                                   _rsqrt32(128), qk4=True),
+    # the same with P~V in FP4 as well: all matrix work on the FP4 instructions
+    "video-dit-32k-fp4": Workload("video-dit-32k-fp4", 1, 24, 32768, 128, "bfloat16", False, 128, 64, 4.0,
+                                  _rsqrt32(128), qk4=True, pv4=True),
     # the same with a channel bias in Q too (variance 4, like K's), 4-bit QK^T with Q smoothing
     "video-dit-32k-qk4-qsmooth": Workload("video-dit-32k-qk4-qsmooth", 1, 24, 32768, 128, "bfloat16", False, 128,
                                           64, 4.0, _rsqrt32(128), qk4=True, smooth_q=True, q_bias_var=4.0),

@@ -19,7 +19,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _header_functions()
-    assert len(names) == 28 and tuple(names) == sage.SYMBOLS
+    assert len(names) == 31 and tuple(names) == sage.SYMBOLS
     lib = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -468,6 +468,17 @@ def _sample_rows(w, rng, n_rand=24):
 def test_full_size_workload(name):
     w = synth.WORKLOADS[name]
     Q, K, V = synth.make_inputs(w)
+    if w.pv4:
+        g = run_gpu_fp4(w, Q, K, V)
+        r, v4 = check_fp4_quant(w, g, Q, K, V)
+        rows = _sample_rows(w, np.random.default_rng(123))
+        O_ref = orc.attn_rows_fp4(r, *v4, w.causal, w.sm_scale, rows=rows)
+        O = g["O"].reshape(-1, w.d)
+        assert np.abs(O[rows] - O_ref).max() <= O_TOL
+        ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale,
+                                 rows=rows)
+        assert cosine(O[rows], ex) >= FP4_COS
+        return
     if w.qk4:
         g = run_gpu_qk4(w, Q, K, V)
         r = orc.quantize_qk4(synth.bits(Q), synth.bits(K), w.dtype_code, smooth_q=w.smooth_q)
@@ -801,6 +812,7 @@ QK4 = {
     "qk4s-no-bias-d128": (dict(base="video-dit-32k", H=2, N=640, smooth_q=True), "bhnd"),
 }
 QK4_COS = 0.98   # 4-bit scores: about three bits fewer than INT8
+FP4_COS = 0.96   # FP4 P~V as well: one mantissa bit for P~ and V (oracle on the video shape: 0.969)
 
 
 def unpack4(codes):
@@ -951,6 +963,128 @@ def test_qk4_smoothing_degenerate_cases():
     want = np.repeat(deq.mean(axis=2), zq.H // zq.Hkv, axis=1)              # per query head
     O = g["O"].reshape(zq.B, zq.H, zq.N, zq.d)
     assert np.abs(O - want[:, :, None, :]).max() <= 1e-5 * max(1.0, np.abs(want).max())
+
+
+# ------------------------------------------------------------------ FP4 attention (FP4 QK^T and FP4 P~V)
+FP4 = {
+    "fp4-noncausal-bf16-d128": (dict(base="video-dit-32k", H=2, N=768), "bhnd"),
+    "fp4-causal-gqa-d128": (dict(base="llm-prefill-4k-causal", B=1, H=8, Hkv_=2, N=512), "bnhd"),
+    "fp4-ragged-chunk-causal-d64": (dict(base="vit-2k-f16", B=1, H=4, Hkv_=2, N=200, Nkv_=333, causal=True), "bhnd"),
+    "fp4-ragged-noncausal-d64": (dict(base="vit-2k-f16", B=2, H=2, N=300), "bnhd"),
+    "fp4-outliers-causal": (dict(base="long-prefill-128k-causal", H=2, N=1024), "bhnd"),
+}
+
+
+def run_gpu_fp4(w, Q, K, V, layout="bhnd", dump_tiles=(), out_dtype=torch.float32):
+    sage = _sage()
+    dev = torch.device("cuda:0")
+    tok = layout == "bnhd"
+    Qd, Kd, Vd = ((t.transpose(1, 2) if tok else t).contiguous().to(dev) for t in (Q, K, V))
+    qk4 = sage.quantize_qk4(Qd, Kd, layout=layout)
+    v4 = sage.quantize_v4(Vd, layout=layout)
+    dump = None
+    if dump_tiles:
+        sel = torch.tensor(list(dump_tiles), dtype=torch.int32, device=dev)
+        s_d = torch.full((len(dump_tiles), 128, w.Nkv), S_SENTINEL, dtype=torch.int32, device=dev)
+        p_d = torch.full((len(dump_tiles), 128, w.Nkv), P_SENTINEL, dtype=torch.uint8, device=dev)
+        dump = (sel, s_d, p_d)
+    O = sage.attn_fwd_fp4(qk4, v4, causal=w.causal, sm_scale=w.sm_scale, out_dtype=out_dtype, layout=layout, dump=dump)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in qk4.items() if torch.is_tensor(v)}
+    vn, vsn = sage.v4_to_natural(v4)
+    res["v4_codes"], res["v4_scale"] = vn.cpu().numpy(), vsn.cpu().numpy()
+    res["O"] = (O.transpose(1, 2) if tok else O).float().cpu().numpy()
+    if dump:
+        res["s_dump"], res["p_dump"] = dump[1].cpu().numpy(), dump[2].cpu().numpy()
+    return res
+
+
+def check_fp4_quant(w, g, Q, K, V):
+    """Q/K codes as the 4-bit path; V codes and scales bit-exact, padding zero."""
+    r = orc.quantize_qk4(synth.bits(Q), synth.bits(K), w.dtype_code)
+    check_qk4_quant(w, g, r)
+    vc, vs = orc.quantize_v4(synth.bits(V), w.dtype_code)
+    nb = vs.shape[2]
+    assert np.array_equal(g["v4_codes"][:, :, :w.Nkv], vc), "v4 codes"
+    assert not g["v4_codes"][:, :, w.Nkv:].any(), "v4 padding"
+    assert np.array_equal(g["v4_scale"][:, :, :nb], vs), "v4 scales"
+    assert not g["v4_scale"][:, :, nb:].any(), "v4 padding scales"
+    return r, (vc, vs)
+
+
+@pytest.mark.parametrize("name", list(FP4))
+def test_fp4_against_the_oracle(name):
+    kw, layout = FP4[name]
+    kw = dict(kw)
+    w = synth.WORKLOADS[kw.pop("base")].with_(name=name, qk4=True, pv4=True, **kw)
+    Q, K, V = synth.make_inputs(w)
+    nqt = -(-w.N // 128)
+    tiles = sorted({0, nqt - 1, (w.B * w.H - 1) * nqt})
+    g = run_gpu_fp4(w, Q, K, V, layout, dump_tiles=tiles)
+    r, v4 = check_fp4_quant(w, g, Q, K, V)
+    O_ref, P_ref = orc.attn_rows_fp4(r, *v4, w.causal, w.sm_scale, want_p=True)
+    flips = 0
+    for k, tid in enumerate(tiles):
+        bh, qt = divmod(tid, nqt)
+        nr = min(128, w.N - qt * 128)
+        rows = bh * w.N + qt * 128 + np.arange(nr)
+        s_ref = orc.qk4_scores(r, rows)
+        s_got = g["s_dump"][k][:nr]
+        written = s_got != S_SENTINEL
+        i = qt * 128 + np.arange(nr)[:, None]
+        j = np.arange(w.Nkv)[None, :]
+        visible = (j <= i + (w.Nkv - w.N)) if w.causal else np.ones_like(written)
+        assert written[visible].all()
+        dev = np.abs(s_got.view(np.float32).astype(np.float64) - s_ref) / np.maximum(
+            np.abs(s_ref).max(axis=1, keepdims=True), 1e-30)
+        assert (dev[written] <= 2.0 ** -18).all(), f"score deviation {dev[written].max():.3g} of the row max"
+        # E2M1 codes of P~ (0..15; P~ >= 0, so 0..7): equal except one-step flips at rounding ties
+        flips += check_p_codes(g["p_dump"][k][:nr], P_ref[rows], visible)
+    O = g["O"].reshape(-1, w.d)
+    err = np.abs(O - O_ref)
+    ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale)
+    print(f"{name}: max |O - oracle| {err.max():.3g}, P^ flips {flips}, cosine vs fp64 {cosine(O, ex):.5f}")
+    assert err.max() <= O_TOL, f"max |O - oracle| = {err.max():.3g}"
+    assert cosine(O, ex) >= FP4_COS
+
+
+def test_fp4_q_zero_and_constant_v_closed_forms():
+    """Q = 0: every P~ is 2^8 and lands on the E2M1 value 4, so O is the plain
+    mean of the dequantized FP4 V rows (causal: of the visible ones).  V a
+    power of two per channel: O equals it up to the matrix core's windowed
+    inner sums (the P~V and the row-sum instructions truncate their block
+    sums independently; the oracle, summing exactly, gives it exactly)."""
+    sage = _sage()
+    for causal in (False, True):
+        w = synth.WORKLOADS["vit-2k-f16"].with_(B=1, H=4, Hkv_=2, N=70, Nkv_=200, causal=causal, qk4=True, pv4=True)
+        Q, K, V = synth.make_inputs(w)
+        Q = torch.zeros_like(Q)
+        g = run_gpu_fp4(w, Q, K, V)
+        vn = g["v4_codes"][:, :, :w.Nkv]
+        sc = np.repeat(g["v4_scale"], 32, axis=2)[:, :, :w.Nkv].astype(np.float64)
+        deq = orc.e2m1_decode(vn) * 2.0 ** (sc - 127)                          # [B, Hkv, Nkv, d]
+        O = g["O"].reshape(w.B, w.H, w.N, w.d)
+        for h in range(w.H):
+            for i in range(w.N):
+                last = i + w.Nkv - w.N if causal else w.Nkv - 1
+                want = deq[0, h // 2, :last + 1].mean(axis=0)
+                assert np.abs(O[0, h, i] - want).max() <= 2e-6 * max(1.0, np.abs(want).max()), (causal, h, i)
+        c = (2.0 ** np.random.default_rng(3).integers(-4, 4, w.d)).astype(np.float32)
+        Vc = torch.from_numpy(np.broadcast_to(c, V.shape).copy()).to(V.dtype)
+        Q2, K2, _ = synth.make_inputs(w)
+        g2 = run_gpu_fp4(w, Q2, K2, Vc)
+        rel = np.abs(g2["O"] / np.broadcast_to(c, g2["O"].shape) - 1.0).max()
+        assert rel <= 2.0 ** -20, (causal, rel)
+    del sage
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_fp4_output_dtypes_round_the_fp32_result(dt):
+    w = synth.WORKLOADS["llm-prefill-4k-causal"].with_(B=1, H=4, Hkv_=2, N=384, qk4=True, pv4=True)
+    Q, K, V = synth.make_inputs(w)
+    ref = torch.from_numpy(run_gpu_fp4(w, Q, K, V, "bnhd")["O"])
+    got = torch.from_numpy(run_gpu_fp4(w, Q, K, V, "bnhd", out_dtype=dt)["O"])
+    assert torch.equal(got, ref.to(dt).float())
 
 
 @pytest.mark.gpu
