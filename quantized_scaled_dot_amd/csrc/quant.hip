@@ -521,14 +521,26 @@ __global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ 
   const int nb = in.P / 32;
   const int blk = blockIdx.x % nb, bh = blockIdx.x / nb, c = threadIdx.x;
   const int n0 = 32 * blk, n = min(32, in.N - n0);
+  // the block's rows into LDS with 16-byte loads (32 rows x d/8 chunks, d threads)
+  constexpr int RW = D + 2;
+  __shared__ uint16_t rows[32 * RW];
+  const uint16_t* src = X + in.head(bh, D) + (size_t)max(n0, 0) * in.stride(D);
+#pragma unroll
+  for (int l = 0; l < 4; l++) {
+    const int ch = l * D + c, r = ch / (D / 8), c8 = ch % (D / 8);
+    v4i raw = {0, 0, 0, 0};
+    if (r < n) raw = *(const v4i*)(src + (size_t)r * in.stride(D) + 8 * c8);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      rows[r * RW + 8 * c8 + 2 * e] = (uint16_t)((unsigned)raw[e] & 0xFFFFu);
+      rows[r * RW + 8 * c8 + 2 * e + 1] = (uint16_t)((unsigned)raw[e] >> 16);
+    }
+  }
+  __syncthreads();
   float qm = 0.0f;
   if (n > 0) {
-    const uint16_t* src = X + in.head(bh, D) + (size_t)n0 * in.stride(D) + c;
     double sum = 0.0;
-    for (int i = 0; i < n; i++) {
-      const uint16_t h = src[(size_t)i * in.stride(D)];
-      sum += (double)load_h(h, is_bf16);
-    }
+    for (int i = 0; i < n; i++) sum += (double)load_h(rows[i * RW + c], is_bf16);   // ascending rows
     qm = (float)(sum / n);
   }
   float a = fabsf(qm);
@@ -549,54 +561,69 @@ __global__ __launch_bounds__(D) void q_mean_kernel(const uint16_t* __restrict__ 
   if (c == 0) qm_scale[r] = (uint8_t)(e + 127);
 }
 
-// FP4 V (MXFP4): one thread per (head, KV tile, channel): the tile's 64
-// tokens of the channel in two blocks of 32, each with the shared exponent
-// E = ilogb(max) - 2 clamped to [-127, 127] (an all-zero block: byte 0) and
-// the E2M1 codes of v / 2^E; tokens past N count as zero.  Lanes are
-// consecutive channels, so each token's loads are one contiguous row piece.
+// FP4 V (MXFP4): a workgroup of 256 threads takes 256 / (2 d) KV tiles (one
+// at d = 128, two at d = 64).  The tile's 64 token rows are read with
+// 16-byte loads into LDS (rows padded by 2 values), then thread pair 2c,
+// 2c + 1 takes channel c, each thread one block g of 32 tokens: the shared
+// exponent E = ilogb(max) - 2 clamped to [-127, 127] (an all-zero block: byte
+// 0) and the E2M1 codes of v / 2^E, written as the 16-byte half g of the
+// channel's 32-byte row (so a wave's stores are contiguous); tokens past N
+// count as zero.  Scales go to the per-tile array permuted for the
+// attention kernel's per-lane loads.
 template <int D>
 __global__ __launch_bounds__(256) void v4_quant_kernel(const uint16_t* __restrict__ V, int is_bf16, InRows in, int BH,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
+  constexpr int TPT = 2 * D;            // threads per tile
+  constexpr int NT = 256 / TPT;         // tiles per workgroup
+  constexpr int RW = D + 2;             // LDS row of one token (u16), padded
+  __shared__ uint16_t tileb[NT][kKTile * RW];
   const int nkt = in.P / kKTile;
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (long long)BH * nkt * D) return;
-  const int c = (int)(gid % D);
-  const long long rest = gid / D;
-  const int t = (int)(rest % nkt), bh = (int)(rest / nkt);
-  const uint16_t* src = V + in.head(bh, D) + c;
+  const int sub = (int)threadIdx.x / TPT, t_in = (int)threadIdx.x % TPT;
+  const long long tg = (long long)blockIdx.x * NT + sub;          // flat (head, tile)
+  const bool live = tg < (long long)BH * nkt;
+  const int t = live ? (int)(tg % nkt) : 0, bh = live ? (int)(tg / nkt) : 0;
+  const uint16_t* src = V + in.head(bh, D);
   const size_t stride = in.stride(D);
-  v4i packed[2];
-  unsigned sbyte[2];
+  // 64 rows x d values = 8 d chunks of 8 values; TPT = 2 d threads load 4 each
 #pragma unroll
-  for (int g = 0; g < 2; g++) {
-    float x[32];
-    float a = 0.0f;
+  for (int l = 0; l < 4; l++) {
+    const int ch = l * TPT + t_in;
+    const int row = ch / (D / 8), c8 = ch % (D / 8);
+    const int tok = t * kKTile + row;
+    v4i raw = {0, 0, 0, 0};
+    if (live && tok < in.N) raw = load16_in<true>(src + (size_t)tok * stride + 8 * c8);
+    uint16_t* dst = &tileb[sub][row * RW + 8 * c8];
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-      const int tok = t * kKTile + 32 * g + i;
-      x[i] = tok < in.N ? load_h(src[(size_t)tok * stride], is_bf16) : 0.0f;
-      a = fmaxf(a, fabsf(x[i]));
-    }
-    packed[g] = v4i{0, 0, 0, 0};
-    sbyte[g] = 0;
-    if (a != 0.0f) {
-      const int e = min(max(ilogbf(a) - 2, -127), 127);
-      sbyte[g] = (unsigned)(e + 127);
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        unsigned word = 0;
-#pragma unroll
-        for (int k = 0; k < 8; k++) word |= e2m1_code(ldexpf(x[8 * w + k], -e)) << (4 * k);
-        packed[g][w] = (int)word;
-      }
+    for (int e = 0; e < 4; e++) {
+      dst[2 * e] = (uint16_t)((unsigned)raw[e] & 0xFFFFu);
+      dst[2 * e + 1] = (uint16_t)((unsigned)raw[e] >> 16);
     }
   }
-  uint8_t* dst = codes + ((size_t)(bh * nkt + t) * D + c) * 32;
-  __builtin_nontemporal_store(packed[0], (v4i*)dst);
-  __builtin_nontemporal_store(packed[1], (v4i*)(dst + 16));
-  uint8_t* sp = scale + (size_t)(bh * nkt + t) * 64 * (D / 32);
-  sp[(c % 32) * (D / 32) + c / 32] = (uint8_t)sbyte[0];
-  sp[(32 + c % 32) * (D / 32) + c / 32] = (uint8_t)sbyte[1];
+  __syncthreads();
+  if (!live) return;
+  const int c = t_in >> 1, g = t_in & 1;
+  float x[32];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    x[i] = load_h(tileb[sub][(32 * g + i) * RW + c], is_bf16);
+    a = fmaxf(a, fabsf(x[i]));
+  }
+  v4i packed = {0, 0, 0, 0};
+  unsigned sbyte = 0;
+  if (a != 0.0f) {
+    const int e = min(max(ilogbf(a) - 2, -127), 127);
+    sbyte = (unsigned)(e + 127);
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      unsigned word = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) word |= e2m1_code(ldexpf(x[8 * w + k], -e)) << (4 * k);
+      packed[w] = (int)word;
+    }
+  }
+  __builtin_nontemporal_store(packed, (v4i*)(codes + ((size_t)(bh * nkt + t) * D + c) * 32 + 16 * g));
+  scale[(size_t)(bh * nkt + t) * 64 * (D / 32) + (32 * g + c % 32) * (D / 32) + c / 32] = (uint8_t)sbyte;
 }
 
 // ---------------------------------------------------------------------------
@@ -750,8 +777,9 @@ void launch_quantize_qk4(const Quant4Args& a, hipStream_t st) {
 void launch_quantize_v4(const QuantV4Args& a, hipStream_t st) {
   const InRows in{a.H, a.N, round_up(a.N, kKTile), a.nhd};
   const int BH = a.B * a.H;
-  const long long n = (long long)BH * (in.P / kKTile) * a.d;
-  const dim3 g((unsigned)((n + 255) / 256));
+  const long long tiles = (long long)BH * (in.P / kKTile);
+  const int nt = 256 / (2 * a.d);   // tiles per workgroup
+  const dim3 g((unsigned)((tiles + nt - 1) / nt));
   if (a.d == 128)
     hipLaunchKernelGGL(v4_quant_kernel<128>, g, dim3(256), 0, st, (const uint16_t*)a.V, a.is_bf16, in, BH, a.v4_codes,
                        a.v4_scale);
