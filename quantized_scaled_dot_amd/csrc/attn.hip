@@ -81,7 +81,8 @@ struct AttnK {
 
 // RAGGED: Nq or Nkv is not a multiple of 128 (masked partial last KV tile,
 // unstored padding rows, 1 to 4 masked steps at the end; at d = 64 it runs 2
-// workgroups per CU, where the 3 of the other d = 64 kernels would spill).
+// workgroups per CU, where the 3 of the other d = 64 kernels would spill;
+// so does the causal FP4 P~V kernel at d = 64).
 // Otherwise the masked steps are exactly the two causal diagonal tiles and
 // none at all without the mask.
 // FINEK: K blocks of 16 or 32 keys.  A lane's 32 keys of a tile are two runs
@@ -109,7 +110,8 @@ struct AttnK {
 // non-causal INT8 d = 128 kernel on whole 256-row query tiles, where one
 // workgroup then fills a CU and each K/V tile copy serves twice the rows.
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP, int NW = 4>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED ? 3 : 2) void attn_fwd_kernel(AttnK p) {
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED && !(QK4 == 3 && CAUSAL) ? 3 : 2) void
+attn_fwd_kernel(AttnK p) {
   static_assert(NW == 4 || (NW == 8 && D == 128 && !CAUSAL && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
   constexpr int QT = 32 * NW;   // query rows per workgroup
   constexpr bool QSM = QK4 == 2;

@@ -971,6 +971,7 @@ FP4 = {
     "fp4-causal-gqa-d128": (dict(base="llm-prefill-4k-causal", B=1, H=8, Hkv_=2, N=512), "bnhd"),
     "fp4-ragged-chunk-causal-d64": (dict(base="vit-2k-f16", B=1, H=4, Hkv_=2, N=200, Nkv_=333, causal=True), "bhnd"),
     "fp4-ragged-noncausal-d64": (dict(base="vit-2k-f16", B=2, H=2, N=300), "bnhd"),
+    "fp4-causal-d64": (dict(base="vit-2k-f16", B=1, H=4, N=512, causal=True), "bhnd"),
     "fp4-outliers-causal": (dict(base="long-prefill-128k-causal", H=2, N=1024), "bhnd"),
 }
 
