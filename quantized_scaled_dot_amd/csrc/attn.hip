@@ -106,11 +106,18 @@ struct AttnK {
 // integer products exactly, one fma per score turns that sum into the exact
 // fp32 term, and the FP4 products are added on top (the INT8 K tile is
 // staged next to the 4-bit one, rows of d + 16 bytes in the same MFMA order).
+// Workgroups per CU (launch bounds): 3 for the aligned d = 64 kernels (but
+// the causal FP4 one) and the aligned non-causal FP4 kernel at d = 128 (168
+// VGPRs, a few spilled; measured 4.7% faster than 2 at the video shape),
+// otherwise 2 (1 for NW = 8).
 // NW: waves per workgroup (query rows 32 NW).  4 everywhere; 8 for the
 // non-causal INT8 d = 128 kernel on whole 256-row query tiles, where one
 // workgroup then fills a CU and each K/V tile copy serves twice the rows.
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP, int NW = 4>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : D == 64 && !RAGGED && !(QK4 == 3 && CAUSAL) ? 3 : 2) void
+__global__ __launch_bounds__(64 * NW, NW == 8                                              ? 1
+                                       : D == 64 && !RAGGED && !(QK4 == 3 && CAUSAL)        ? 3
+                                       : QK4 == 3 && !CAUSAL && !RAGGED                     ? 3
+                                                                                            : 2) void
 attn_fwd_kernel(AttnK p) {
   static_assert(NW == 4 || (NW == 8 && D == 128 && !CAUSAL && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
   constexpr int QT = 32 * NW;   // query rows per workgroup

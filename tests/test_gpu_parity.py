@@ -557,6 +557,7 @@ MAX_LEN = {
     "max-len-causal-d128": dict(base="long-prefill-128k-causal", H=1, N=1 << 19),
     "max-len-ragged-d64": dict(base="vit-2k-f16", B=1, H=1, N=(1 << 19) - 37),
     "max-len-qk4": dict(base="video-dit-32k-qk4", H=1, N=1 << 19),
+    "max-len-fp4": dict(base="video-dit-32k-fp4", H=1, N=1 << 19),
     "max-len-decode": dict(base="decode-128k-gqa-4q", B=1, H=2, Hkv_=1, Nkv_=1 << 19),
 }
 
@@ -567,6 +568,17 @@ def test_maximum_length(name):
     kw = dict(MAX_LEN[name])
     w = synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw)
     Q, K, V = synth.make_inputs(w)
+    if w.pv4:
+        g = run_gpu_fp4(w, Q, K, V)
+        r, v4 = check_fp4_quant(w, g, Q, K, V)
+        rows = _sample_rows(w, np.random.default_rng(5), n_rand=16)
+        O_ref = orc.attn_rows_fp4(r, *v4, w.causal, w.sm_scale, rows=rows)
+        O = g["O"].reshape(-1, w.d)
+        assert np.abs(O[rows] - O_ref).max() <= O_TOL
+        ex = orc.exact_attention(Q.float().numpy(), K.float().numpy(), V.float().numpy(), w.causal, w.sm_scale,
+                                 rows=rows)
+        assert cosine(O[rows], ex) >= FP4_COS
+        return
     if w.qk4:
         g = run_gpu_qk4(w, Q, K, V)
         r = orc.quantize_qk4(synth.bits(Q), synth.bits(K), w.dtype_code, smooth_q=w.smooth_q)
