@@ -1103,9 +1103,10 @@ def test_fp4_output_dtypes_round_the_fp32_result(dt):
 @pytest.mark.gpu
 def test_graph_capture_replays_match_eager():
     """The calls allocate nothing, set no memory and never synchronize, so a
-    prefill step (quantize Q/K, quantize V, attention) and a decode step
-    (quantize the new queries, split-KV attention against a quantized cache)
-    can be captured in a HIP graph.  Every replay, with eager work and
+    prefill step (quantize Q/K, quantize V, attention; also with the fused
+    quantize call, in FP4, and with Q smoothing) and a decode step (quantize
+    the new queries, split-KV attention against a quantized cache) can be
+    captured in a HIP graph.  Every replay, with eager work and
     synchronizations in between, equals the eager result bit for bit."""
     sage = _sage()
     dev = torch.device("cuda:0")
@@ -1117,6 +1118,17 @@ def test_graph_capture_replays_match_eager():
         vq = sage.quantize_v(V)
         return sage.attn_fwd(qk, vq, causal=True, sm_scale=w.sm_scale, out_dtype=torch.float32)
 
+    def prefill_fused():   # the two quantize calls in one (three launches)
+        qk, vq = sage.quantize_qkv(Q, K, V, w.blk_q, w.blk_k)
+        return sage.attn_fwd(qk, vq, causal=True, sm_scale=w.sm_scale, out_dtype=torch.float32)
+
+    def prefill_fp4():     # FP4 QK^T and FP4 P~V
+        return sage.attn_fwd_fp4(sage.quantize_qk4(Q, K), sage.quantize_v4(V), causal=True, sm_scale=w.sm_scale)
+
+    def prefill_qk4s():    # 4-bit QK^T with Q smoothing
+        return sage.attn_fwd_qk4(sage.quantize_qk4(Q, K, smooth_q=True), sage.quantize_v(V), causal=True,
+                                 sm_scale=w.sm_scale)
+
     kc = sage.quantize_k(K)
     vq = sage.quantize_v(V)
     Qn = Q[:, :, -3:].contiguous()
@@ -1125,7 +1137,7 @@ def test_graph_capture_replays_match_eager():
         q = sage.quantize_q(Qn)
         return sage.attn_decode(q, kc, vq, causal=True, sm_scale=w.sm_scale, kv_chunk=128)
 
-    for step in (prefill, decode):
+    for step in (prefill, prefill_fused, prefill_fp4, prefill_qk4s, decode):
         ref = step().clone()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
