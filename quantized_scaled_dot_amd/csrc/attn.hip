@@ -688,12 +688,22 @@ attn_fwd_kernel(AttnK p) {
   const float* vs = p.v_scale + (size_t)bhkv * D;
   const size_t orow = p.nhd ? ((size_t)(bh / p.Hq) * Nq + row) * p.Hq + bh % p.Hq : (size_t)bh * Nq + row;
   const bool store = !RAGGED || row < Nq;
+  // every V scale of the lane's channels is loaded before the first store (the
+  // compiler may not move a load past a store to O), so the epilogue waits for
+  // one round trip instead of one per group of four channels
+  v4f vsc[PV4 ? 1 : CT][4];
+  if constexpr (!PV4) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) vsc[ct][q] = *(const v4f*)(vs + 32 * ct + 8 * q + 4 * lg);
+  }
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int c0 = 32 * ct + 8 * q + 4 * lg;   // O^T register 4q+e holds channel c0 + e
-      const v4f sc = PV4 ? v4f{1.0f, 1.0f, 1.0f, 1.0f} : *(const v4f*)(vs + c0);
+      const v4f sc = PV4 ? v4f{1.0f, 1.0f, 1.0f, 1.0f} : vsc[PV4 ? 0 : ct][q];
       v4f o;
 #pragma unroll
       for (int e = 0; e < 4; e++) o[e] = PV4 ? oacc[ct][4 * q + e] * inv : oacc[ct][4 * q + e] * (sc[e] * inv);

@@ -75,18 +75,22 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 // (The hardware f32->f16 conversion was measured to round exact ties away from
-// zero, so the rounding is done here on the bit pattern.)
+// zero, so the rounding is done here on the bit pattern.)  Every case is
+// computed and one is selected, without branches: per element the branchy form
+// compiled to three nested divergent branches.
 __device__ __forceinline__ uint32_t f16_bits_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7E00u;                  // NaN
-  if (a >= 0x477FF000u) return sign | 0x7C00u;                 // rounds to infinity
-  if (a >= 0x38800000u) {                                      // normal half: rebias, round 13 bits
-    const uint32_t m = a - 0x38000000u;
-    return sign | ((m + 0xFFFu + ((m >> 13) & 1u)) >> 13);
-  }
-  // subnormal half: |x| * 2^24 < 1024 is exact in fp32; rint rounds ties to even
-  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 16777216.0f);
+  // normal half: rebias, round off 13 bits
+  const uint32_t m = a - 0x38000000u;
+  const uint32_t nrm = (m + 0xFFFu + ((m >> 13) & 1u)) >> 13;
+  // subnormal half: |x| * 2^24 <= 1024 is exact in fp32; rint rounds ties to
+  // even (|x| clamped to 2^-14 so that the unused value stays in range)
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(min(a, 0x38800000u)) * 16777216.0f);
+  uint32_t r = a >= 0x38800000u ? nrm : sub;
+  r = a >= 0x477FF000u ? 0x7C00u : r;   // rounds to infinity
+  r = a > 0x7F800000u ? 0x7E00u : r;    // NaN
+  return sign | r;
 }
 
 // Exchange with the lane 32 apart (same query row, other half of the keys /
