@@ -111,15 +111,17 @@ struct AttnK {
 // VGPRs, a few spilled; measured 4.7% faster than 2 at the video shape),
 // otherwise 2 (1 for NW = 8).
 // NW: waves per workgroup (query rows 32 NW).  4 everywhere; 8 for the
-// non-causal INT8 d = 128 kernel on whole 256-row query tiles, where one
-// workgroup then fills a CU and each K/V tile copy serves twice the rows.
+// aligned INT8 d = 128 kernels on whole 256-row query tiles, where one
+// workgroup then fills a CU and each K/V tile copy serves twice the rows
+// (causal: only for long key ranges, since its four diagonal steps leave more
+// waves idle than the two of a 128-row workgroup).
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT, bool DUMP, int NW = 4>
 __global__ __launch_bounds__(64 * NW, NW == 8                                              ? 1
                                        : D == 64 && !RAGGED && !(QK4 == 3 && CAUSAL)        ? 3
                                        : QK4 == 3 && !CAUSAL && !RAGGED                     ? 3
                                                                                             : 2) void
 attn_fwd_kernel(AttnK p) {
-  static_assert(NW == 4 || (NW == 8 && D == 128 && !CAUSAL && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
+  static_assert(NW == 4 || (NW == 8 && D == 128 && !RAGGED && !DUMP && QK4 == 0), "wide tiles");
   constexpr int QT = 32 * NW;   // query rows per workgroup
   constexpr bool QSM = QK4 == 2;
   constexpr bool PV4 = QK4 == 3;               // FP4 P~V
@@ -670,6 +672,12 @@ attn_fwd_kernel(AttnK p) {
       if (t + 1 == ntiles) { t = ntiles; break; }
       tile_step(t + 1, sb0, sb1, sa0, sa1, std::true_type{}, I2{}, t + 2 < ntiles && !future(t + 2));
     }
+  } else if (CAUSAL && NW == 8) {   // the four diagonal tiles of 256 rows (scores of tile t are in sa)
+    for (; t < ntiles; t += 2) {
+      tile_step(t, sa0, sa1, sb0, sb1, std::true_type{}, I2{}, t + 1 < ntiles && !future(t + 1));
+      if (t + 1 == ntiles) { t = ntiles; break; }
+      tile_step(t + 1, sb0, sb1, sa0, sa1, std::true_type{}, I2{}, t + 2 < ntiles && !future(t + 2));
+    }
   } else if (CAUSAL) {   // the two diagonal tiles (q0 + off)/64 and the next (scores of tile t are in sa)
     tile_step(t, sa0, sa1, sb0, sb1, std::true_type{}, I2{}, !future(t + 1));
     tile_step(t + 1, sb0, sb1, sa0, sa1, std::true_type{}, I2{}, false);
@@ -716,7 +724,7 @@ attn_fwd_kernel(AttnK p) {
 // launcher only asks for them where that instance exists
 template <int D, bool CAUSAL, bool RAGGED, bool FINEK, int QK4, int OUT>
 static void launch5(const AttnK& k, int grid, bool dump, bool wide, hipStream_t st) {
-  if constexpr (D == 128 && !CAUSAL && !RAGGED && QK4 == 0) {
+  if constexpr (D == 128 && !RAGGED && QK4 == 0) {
     if (wide) {
       hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, RAGGED, FINEK, QK4, OUT, false, 8>), dim3(grid), dim3(512), 0,
                          st, k);
@@ -790,6 +798,9 @@ SAGE_PART_BODY(7, 64, false, true)
 #endif
 
 #if SAGE_ATTN_PART <= 0
+// average keys per query row (Nkv - Nq/2) from which causal runs 256-row workgroups
+constexpr int kWideCausalKeys = 16384;
+
 void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   AttnK k;
   k.q_codes = a.q_codes; k.q_scale = a.q_scale; k.k_codes = a.k_codes; k.k_scale = a.k_scale;
@@ -805,9 +816,12 @@ void launch_attn_fwd(const AttnArgs& a, bool dump, hipStream_t st) {
   k.qm_codes = a.qm_codes; k.qm_scale = a.qm_scale; k.k8_codes = a.k8_codes; k.k8_scale = a.k8_scale;
   k.v4_codes = a.v4_codes; k.v4_scale = a.v4_scale;
   const int variant = a.q4_codes ? (a.v4_codes ? 4 : a.qm_codes ? 3 : 2) : a.blk_k < kKTile ? 1 : 0;
-  // 256-row workgroups: non-causal INT8 at d = 128 on whole 256-row query tiles
-  // (not for the test dumps, which address 128-row tiles)
-  const bool wide = !dump && a.d == 128 && !a.causal && !ragged && variant <= 1 && a.Nq % 256 == 0;
+  // 256-row workgroups: INT8 at d = 128 on whole 256-row query tiles (not for
+  // the test dumps, which address 128-row tiles); causal only where a query
+  // row sees 16384 keys or more on average (Nkv - Nq/2): measured 0.8-2% faster
+  // at 30k-64k keys, 2-4% slower at 4k-8k, the same bits
+  const bool wide = !dump && a.d == 128 && !ragged && variant <= 1 && a.Nq % 256 == 0 &&
+                    (!a.causal || a.Nkv - a.Nq / 2 >= kWideCausalKeys);
   const int qtile = wide ? 256 : kQTile;
   k.nqt = (a.Nq + qtile - 1) / qtile;   // query tiles (workgroups) per head
   const int grid = a.B * a.Hq * k.nqt;

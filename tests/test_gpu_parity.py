@@ -264,14 +264,18 @@ def test_small_grouped_and_unequal_parity(name, layout):
     assert cosine(O, ex) >= 0.995
 
 
-# Non-causal INT8 at d = 128 on whole 256-row query tiles runs in 8-wave workgroups of 256 rows
-# (the dump instance always runs 128-row workgroups): the per-row arithmetic is the same, so O
-# must be bit-identical to the 128-row kernel's, and within 2e-3 of the oracle.
+# INT8 at d = 128 on whole 256-row query tiles runs in 8-wave workgroups of 256 rows: always
+# without the causal mask, and with it where a query row sees 16384 keys or more on average
+# (Nkv - Nq/2).  The dump instance always runs 128-row workgroups.  The per-row arithmetic is
+# the same (a wave skips the same tiles wholly after its rows), so O must be bit-identical to the
+# 128-row kernel's, and within 2e-3 of the oracle.
 WIDE = {
     "wide-noncausal-N768-blkq64": dict(base="video-dit-32k", B=1, H=2, N=768, blk_q=64),
     "wide-gqa-chunk-512-of-1024": dict(base="video-dit-32k", B=2, H=8, Hkv_=2, N=512, Nkv_=1024),
     "wide-fine-k16-N512": dict(base="video-dit-32k", B=1, H=3, N=512, blk_q=32, blk_k=16),
     "wide-mqa-N256-xcd": dict(base="video-dit-32k", B=1, H=64, Hkv_=8, N=256),
+    "wide-causal-chunk-256-of-16512": dict(base="long-prefill-128k-causal", B=1, H=2, N=256, Nkv_=16512),
+    "wide-causal-gqa-512-of-16640": dict(base="long-prefill-128k-causal", B=1, H=2, Hkv_=1, N=512, Nkv_=16640),
 }
 
 
@@ -281,7 +285,7 @@ def test_wide_workgroups_equal_the_128_row_kernel(name, layout):
     kw = dict(WIDE[name])
     w = synth.WORKLOADS[kw.pop("base")].with_(name=name, **kw)
     Q, K, V = synth.make_inputs(w)
-    assert w.d == 128 and not w.causal and w.N % 256 == 0 and w.Nkv % 128 == 0
+    assert w.d == 128 and w.N % 256 == 0 and w.Nkv % 128 == 0 and (not w.causal or w.Nkv - w.N // 2 >= 16384)
     nqt = -(-w.N // 128)
     g = run_gpu(w, Q, K, V, dump_tiles=(0,), layout=layout)     # the 128-row instance
     sage = _sage()
