@@ -69,30 +69,6 @@ __device__ __forceinline__ float load_h(uint16_t h, bool is_bf16) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// fp32 -> bf16 / fp16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-// (The hardware f32->f16 conversion was measured to round exact ties away from
-// zero, so the rounding is done here on the bit pattern.)  Every case is
-// computed and one is selected, without branches: per element the branchy form
-// compiled to three nested divergent branches.
-__device__ __forceinline__ uint32_t f16_bits_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
-  // normal half: rebias, round off 13 bits
-  const uint32_t m = a - 0x38000000u;
-  const uint32_t nrm = (m + 0xFFFu + ((m >> 13) & 1u)) >> 13;
-  // subnormal half: |x| * 2^24 <= 1024 is exact in fp32; rint rounds ties to
-  // even (|x| clamped to 2^-14 so that the unused value stays in range)
-  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(min(a, 0x38800000u)) * 16777216.0f);
-  uint32_t r = a >= 0x38800000u ? nrm : sub;
-  r = a >= 0x477FF000u ? 0x7C00u : r;   // rounds to infinity
-  r = a > 0x7F800000u ? 0x7E00u : r;    // NaN
-  return sign | r;
-}
-
 // Exchange with the lane 32 apart (same query row, other half of the keys /
 // channels): v_permlane32_swap returns {x[l], x[l^32]} in some order for every
 // lane, so a symmetric combination of the two results is the pair's combination.
@@ -128,21 +104,24 @@ __device__ __forceinline__ int k_lds_key(int rho) {
 template <int D> constexpr int kRowK = D + 16;
 constexpr int kRowV = kKTile + 16;
 
+// Four consecutive outputs: fp32, or bf16 / fp16 rounded to nearest even by
+// the packed hardware converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32: one
+// instruction per two values).  A check over every non-NaN fp32 input on the
+// MI355X found both equal to round-to-nearest-even on the bit pattern.
 template <int OUT>
 __device__ __forceinline__ void store4(void* O, size_t idx, v4f v) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
   if (OUT == 2) {
     *(v4f*)((float*)O + idx) = v;
   } else if (OUT == 1) {
-    unsigned u[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) u[e] = bf16_bits_rne(v[e]);
-    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    const h2 lo = __builtin_convertvector(f2{v[0], v[1]}, h2), hi = __builtin_convertvector(f2{v[2], v[3]}, h2);
+    const v2i w = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
     *(v2i*)((uint16_t*)O + idx) = w;
   } else {
-    unsigned u[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) u[e] = f16_bits_rne(v[e]);
-    v2i w = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 lo = __builtin_convertvector(f2{v[0], v[1]}, h2), hi = __builtin_convertvector(f2{v[2], v[3]}, h2);
+    const v2i w = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
     *(v2i*)((uint16_t*)O + idx) = w;
   }
 }
