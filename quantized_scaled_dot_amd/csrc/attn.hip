@@ -360,18 +360,28 @@ attn_fwd_kernel(AttnK p) {
     } else {
       a0 = kScoreBias16; a1 = kScoreBias16;   // int32 results read as fp32 give B + S exactly
     }
+    // QK4: this lane's 32 channels of k-step s are block 2s + lg.  With FP4
+    // P~V that is byte 2s of its scale words shifted by lg bytes, which the
+    // instruction selects (measured: 4% faster there); the other 4-bit kernels
+    // extract the byte on the VALU (selecting it cost them registers: 166 ->
+    // 170 VGPRs and the third wave of the plain 4-bit kernel, 5% slower)
+    const unsigned kw0 = PV4 ? ksw[0] >> (8 * lg) : 0u, kw1 = PV4 ? ksw[1] >> (8 * lg) : 0u;
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       const v4i k0 = *(const v4i*)(kb0 + 32 * s);
       const v4i k1 = *(const v4i*)(kb0 + 32 * RK + 32 * s);
       if constexpr (QK4) {
-        // this lane's 32 channels of the instruction are block 2s + lg
-        const int s0 = (int)((ksw[0] >> (8 * (2 * s + lg))) & 0xFFu), s1 = (int)((ksw[1] >> (8 * (2 * s + lg))) & 0xFFu);
         const v8i q8 = {qreg[s][0], qreg[s][1], qreg[s][2], qreg[s][3], 0, 0, 0, 0};
         const v8i a8 = {k0[0], k0[1], k0[2], k0[3], 0, 0, 0, 0};
         const v8i b8 = {k1[0], k1[1], k1[2], k1[3], 0, 0, 0, 0};
-        a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8, a0, 4, 4, 0, s0, 0, qsc[s]);
-        a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, q8, a1, 4, 4, 0, s1, 0, qsc[s]);
+        if constexpr (PV4) {
+          a0 = mfma_fp4_byte(2 * s, a8, q8, a0, kw0, qsc[s]);
+          a1 = mfma_fp4_byte(2 * s, b8, q8, a1, kw1, qsc[s]);
+        } else {
+          const int s0 = (int)((ksw[0] >> (8 * (2 * s + lg))) & 0xFFu), s1 = (int)((ksw[1] >> (8 * (2 * s + lg))) & 0xFFu);
+          a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8, a0, 4, 4, 0, s0, 0, qsc[s]);
+          a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, q8, a1, 4, 4, 0, s1, 0, qsc[s]);
+        }
       } else {
         a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qreg[s], a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qreg[s], a1, 0, 0, 0);
@@ -393,8 +403,7 @@ attn_fwd_kernel(AttnK p) {
       const v4i v0 = *(const v4i*)(vb);
       if constexpr (PV4) {
         const v8i av = {v0[0], v0[1], v0[2], v0[3], 0, 0, 0, 0};
-        oacc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[ct], 4, 4, 0,
-                                                                   (int)((vsw >> (8 * ct)) & 0xFFu), 0, pscale);
+        oacc[ct] = mfma_fp4_byte(ct, av, pb, oacc[ct], vsw, pscale);   // V scale: byte ct of vsw
       } else {
         const v4i v1 = *(const v4i*)(vb + 16);
         const v8i av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -571,7 +580,9 @@ attn_fwd_kernel(AttnK p) {
             // block: bytes 2(q%2), 2(q%2)+1 of dword 2h + q/2, low nibble first
             unsigned w;
             if (q % 2 == 0) {
-              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv4[0], pv4[1], pdiv, 0);
+              // (the first convert's "old" operand is a register that dies
+              // here: the four converts of a dword write all of its bytes)
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(pv4[0]), pv4[0], pv4[1], pdiv, 0);
               w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv4[2], pv4[3], pdiv, 1);
             } else {
               w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((unsigned)pb[2 * h + q / 2], pv4[0], pv4[1], pdiv, 2);

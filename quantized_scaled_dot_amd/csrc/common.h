@@ -36,6 +36,20 @@ constexpr v16i kScoreBias16 = {kScoreBiasBits, kScoreBiasBits, kScoreBiasBits, k
 // masked sentinels are compared before this is used, never converted).
 __device__ __forceinline__ int unbias_score(int x) { return (int)((unsigned)x - (unsigned)kScoreBiasBits); }
 
+// FP4 x FP4 scaled MFMA whose A scale is byte SEL of the word sa (the
+// instruction's operand byte select: no extraction on the VALU); B scale sb.
+template <int SEL>
+__device__ __forceinline__ v16f mfma_fp4_sel(const v8i& a, const v8i& b, const v16f& c, unsigned sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, SEL, (int)sa, 0, sb);
+}
+// the same with SEL picked by a value that is a constant after unrolling
+__device__ __forceinline__ v16f mfma_fp4_byte(int sel, const v8i& a, const v8i& b, const v16f& c, unsigned sa, int sb) {
+  return sel == 0 ? mfma_fp4_sel<0>(a, b, c, sa, sb)
+       : sel == 1 ? mfma_fp4_sel<1>(a, b, c, sa, sb)
+       : sel == 2 ? mfma_fp4_sel<2>(a, b, c, sa, sb)
+                  : mfma_fp4_sel<3>(a, b, c, sa, sb);
+}
+
 // Row sum of a wave's FP8 P~ codes on the matrix core.  pb is the B operand
 // of the 32x32x64 P~V instruction (lane l: query l%32, keys 32(l/32) ..
 // +31).  Read as the B operand of the 16x16x128 FP8 instruction, lane l is
