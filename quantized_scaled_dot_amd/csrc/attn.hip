@@ -143,6 +143,14 @@ attn_fwd_kernel(AttnK p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int li = lane & 31, lg = lane >> 5;
   const v8i ones16 = rowsum_ones_operand(lane, PV4);   // row sums of P^ (see rowsum_fp8)
+  // INT8 scores: the score bias held in 16 VGPRs for the whole kernel (an
+  // opaque value, so that it is not rebuilt from SGPRs with 8 moves per tile)
+  // and read as the C operand of each tile's first score MFMAs, wherever those
+  // registers fit without spills: not at d = 64 with three workgroups per CU,
+  // nor in the non-causal ragged d = 128 kernel (256 VGPRs already)
+  constexpr bool KEEPB = QK4 == 0 && (D == 128 ? CAUSAL || !RAGGED : RAGGED);
+  v16i kbias = kScoreBias16;
+  if constexpr (KEEPB) asm volatile("" : "+v"(kbias));
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs
   // on XCD b % 8).  Flat query head bh = b*Hq + h reads flat K/V head
   // bh / g (the g query heads of a K/V head are consecutive).  When the K/V
@@ -358,7 +366,7 @@ attn_fwd_kernel(AttnK p) {
     } else if constexpr (QK4) {
       a0 = SV{}; a1 = SV{};
     } else {
-      a0 = kScoreBias16; a1 = kScoreBias16;   // int32 results read as fp32 give B + S exactly
+      a0 = KEEPB ? kbias : kScoreBias16; a1 = a0;   // int32 results read as fp32 give B + S exactly
     }
     // QK4: this lane's 32 channels of k-step s are block 2s + lg.  With FP4
     // P~V that is byte 2s of its scale words shifted by lg bytes, which the
