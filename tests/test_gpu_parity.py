@@ -380,17 +380,18 @@ QKV_CASES = ["gqa4-causal-bf16-d128", "gqa2-xcd-f16-d64", "ragged-gqa-causal-130
              "fine-q32-k16-ragged-gqa-d64", "fine-k32-outliers-causal", "ragged-single-token-causal"]
 
 
-@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
-@pytest.mark.parametrize("name", QKV_CASES + ["llm-prefill-4k-causal", "video-dit-32k", "vit-2k-f16",
-                                              "long-prefill-128k-causal"])
+# the small shapes in both layouts, the full-size workloads in the head-major one
+QKV_FULL = ["llm-prefill-4k-causal", "video-dit-32k", "vit-2k-f16", "long-prefill-128k-causal"]
+
+
+@pytest.mark.parametrize("name,layout", [(n, l) for n in QKV_CASES for l in ("bhnd", "bnhd")] +
+                         [(n, "bhnd") for n in QKV_FULL])
 def test_fused_qkv_quantize_equals_the_two_calls(name, layout):
     """sage_quantize_qkv gives the codes, scales and K means of sage_quantize_qk + sage_quantize_v
     bit for bit (including the zero padding), on grouped, ragged and finer-block shapes and four
     full-size workloads (d = 64 and 128; 32768 and 131072 keys take the streaming loads in its
     first pass, 4096 and 2048 the cached ones)."""
     if name in synth.WORKLOADS:
-        if layout == "bnhd":
-            pytest.skip("the full-size workloads run in the head-major layout")
         w = synth.WORKLOADS[name]
     else:
         w = small_ex_workload(name)
