@@ -230,26 +230,56 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeK p, const floa
   if (f >= p.g * p.Nq) return;
   const int qi = f % p.Nq, bhq = bhkv * p.g + f / p.Nq;
   const size_t u0 = ((size_t)bhkv * p.R + rg) * p.nchunk;   // first unit of this row group
+  // The splits' states are loaded eight at a time, every load of a batch in
+  // flight before the first is used; the arithmetic keeps its order (the
+  // maximum first, then the fma chains in ascending split order).
+  static_assert(CPT == 4, "one 16-byte load of O_acc per split");
+  constexpr int NB = 8;
   float ms = -3.0e38f;
-  for (int c = 0; c < p.nchunk; c++) {
+  int c = 0;
+  for (; c + NB <= p.nchunk; c += NB) {
+    float mm[NB], ll[NB];
+#pragma unroll
+    for (int u = 0; u < NB; u++) {
+      const float* up = p.part + (u0 + c + u) * unit_floats<D>();
+      mm[u] = up[32 * D + row];
+      ll[u] = up[32 * D + 32 + row];
+    }
+#pragma unroll
+    for (int u = 0; u < NB; u++)
+      if (ll[u] > 0.0f) ms = fmaxf(ms, mm[u]);
+  }
+  for (; c < p.nchunk; c++) {
     const float* up = p.part + (u0 + c) * unit_floats<D>();
     if (up[32 * D + 32 + row] > 0.0f) ms = fmaxf(ms, up[32 * D + row]);
   }
   float L = 0.0f, o[CPT];
 #pragma unroll
   for (int e = 0; e < CPT; e++) o[e] = 0.0f;
-  for (int c = 0; c < p.nchunk; c++) {
-    const float* up = p.part + (u0 + c) * unit_floats<D>();
-    const float lc = up[32 * D + 32 + row];
-    if (!(lc > 0.0f)) continue;
-    const float w = __builtin_amdgcn_exp2f(up[32 * D + row] - ms);
+  auto add = [&](float lc, float mc, const v4f& x) {
+    if (!(lc > 0.0f)) return;
+    const float w = __builtin_amdgcn_exp2f(mc - ms);
     L = __builtin_fmaf(w, lc, L);
 #pragma unroll
-    for (int e = 0; e < CPT; e += 4) {
-      const v4f x = *(const v4f*)(up + (size_t)row * D + c0 + e);
+    for (int k = 0; k < 4; k++) o[k] = __builtin_fmaf(w, x[k], o[k]);
+  };
+  c = 0;
+  for (; c + NB <= p.nchunk; c += NB) {
+    float mm[NB], ll[NB];
+    v4f xx[NB];
 #pragma unroll
-      for (int k = 0; k < 4; k++) o[e + k] = __builtin_fmaf(w, x[k], o[e + k]);
+    for (int u = 0; u < NB; u++) {
+      const float* up = p.part + (u0 + c + u) * unit_floats<D>();
+      mm[u] = up[32 * D + row];
+      ll[u] = up[32 * D + 32 + row];
+      xx[u] = *(const v4f*)(up + (size_t)row * D + c0);   // in bounds; unused when the split has no key
     }
+#pragma unroll
+    for (int u = 0; u < NB; u++) add(ll[u], mm[u], xx[u]);
+  }
+  for (; c < p.nchunk; c++) {
+    const float* up = p.part + (u0 + c) * unit_floats<D>();
+    add(up[32 * D + 32 + row], up[32 * D + row], *(const v4f*)(up + (size_t)row * D + c0));
   }
   const float inv = 1.0f / L;
   const float* vs = v_scale + (size_t)bhkv * D;
